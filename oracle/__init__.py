@@ -1,0 +1,114 @@
+"""fp64 CPU oracle of the DeltaNet delta rule -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the HIP library
+(``deltanet_delta_rule_amd``) and imports nothing from it; the two meet only
+through the seeded input generator, which holds none of the method's
+arithmetic.
+
+Contents
+--------
+``delta_rule_ref``
+    The plain sequential recurrence in fp64 (C, ``ref_delta_rule.c``), the
+    definition every GPU result is judged against.  See that file's header for
+    the passages it follows.
+``chunk_algebra``
+    The chunkwise-parallel rearrangement of the same recurrence in fp64 NumPy,
+    step by step as the pages state it.  It is used only to pin the oracle and
+    the algebra the GPU kernels rely on; GPU parity is always judged against
+    ``delta_rule_ref``.
+
+Parity status: every function here is pinned by ``tests/test_oracle.py`` and
+``tests/test_chunk_algebra.py`` (equivalent update forms, closed forms,
+special cases, an exact-rational brute force and a hand-worked example).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ref_delta_rule.c")
+_LIB_PATH = os.path.join(_HERE, "libref_delta_rule.so")
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the C oracle with gcc (fp64, no FMA contraction) in place."""
+    cmd = [
+        "gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
+        "-shared", "-fPIC", "-pthread", _SRC, "-o", _LIB_PATH + ".tmp",
+    ]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    dp = ctypes.POINTER(ctypes.c_double)
+    i64 = ctypes.c_int64
+    lib.ref_delta_rule_f64.restype = ctypes.c_int
+    lib.ref_delta_rule_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp,
+                                       i64, i64, i64, i64, i64, ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def _as_f64(x) -> np.ndarray:
+    """Widen an array-like (NumPy or CPU torch tensor) to contiguous fp64."""
+    if hasattr(x, "detach"):  # torch tensor: widen on the torch side first
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def delta_rule_ref(q, k, v, beta, S0=None, nthreads: int = 1):
+    """Run the delta-rule recurrence in fp64 on the CPU.
+
+    Arguments are array-likes with the layouts q, k ``[B,T,H,Dk]``,
+    v ``[B,T,H,Dv]``, beta ``[B,T,H]`` and S0 ``[B,H,Dv,Dk]`` (or None for a
+    zero initial state).  They are widened to fp64 exactly (the caller passes
+    values already rounded to the dtype under test).
+
+    Returns ``(o, S_T)`` as fp64 NumPy arrays: o ``[B,T,H,Dv]`` and
+    S_T ``[B,H,Dv,Dk]``.
+    """
+    q, k, v, beta = (_as_f64(x) for x in (q, k, v, beta))
+    if q.ndim != 4 or k.shape != q.shape or v.ndim != 4 or beta.ndim != 3:
+        raise ValueError("expected q,k [B,T,H,Dk], v [B,T,H,Dv], beta [B,T,H]")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[3]
+    if v.shape[:3] != (B, T, H) or beta.shape != (B, T, H):
+        raise ValueError("inconsistent leading dimensions")
+    s0 = None
+    if S0 is not None:
+        s0 = _as_f64(S0)
+        if s0.shape != (B, H, Dv, Dk):
+            raise ValueError(f"S0 must be [B,H,Dv,Dk]={B, H, Dv, Dk}, got {s0.shape}")
+    o = np.zeros((B, T, H, Dv), dtype=np.float64)
+    st = np.zeros((B, H, Dv, Dk), dtype=np.float64)
+    rc = _load().ref_delta_rule_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                    _ptr(s0), _ptr(o), _ptr(st),
+                                    B, T, H, Dk, Dv, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle failed with code {rc}")
+    return o, st
+
+
+__all__ = ["build", "delta_rule_ref"]
