@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Throughput of the delta-rule forward on one MI355X.
+
+One step = one ``delta_rule_chunk_fwd`` over the 1.3B-scale layer shape
+(B=8, H=16, T=2048, d_k=d_v=128, chunk 64, bf16 inputs, fp32 state, final
+state returned) with inputs already resident in HBM.  W untimed warm-up
+steps, then K timed steps between two device synchronisations.  Prints ONE
+JSON line on stdout:
+
+  value        tokens/s = B*T*K / wall time of the K steps
+  roofline     the fused chunk kernel against HBM bandwidth (its roofline
+               bound: arithmetic intensity 170 flop/B is below the MI355X
+               ridge of ~315 flop/B), from the mean launch time measured with
+               HIP events on the launch stream; mfma_frac gives the same time
+               against the dense bf16 MFMA peak
+  cpu_baseline the fp64 CPU oracle on the host cores (reported, not a target)
+  parity       the timed run's outputs against that oracle run
+  decode       256 back-to-back single-token steps of the decode workload
+               (B=128, H=16, d=128), HBM bytes per step and tokens/s
+
+Options: --gpus N (only 1: this build targets one GPU), --steps K,
+--warmup W, --no-cpu-baseline, --no-decode, --copy-calib BYTES (also time a
+plain device copy of that size, for counter calibration runs).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("delta-rule fwd tokens/sec at H=16,d=128,T=2048; "
+          "% bf16 MFMA / HBM roofline")
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published (256 CU x 2.4 GHz x 4096)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_layer_1p3b_traffic.txt")
+KERNEL_SOURCES = ["deltanet_delta_rule_amd/csrc/chunk_fwd.hip",
+                  "deltanet_delta_rule_amd/csrc/dr_common.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def chunk_work(w):
+    """Algorithmic MFMA flops and HBM bytes of one chunk_fwd call.
+
+    flops per token-head: 2C(3Dk + 2Dv) + 6 Dk Dv (the products K K^T, Q K^T,
+    T K; T V, (QK^T.M) E; W S^T, Q S^T, E^T K of the chunk form with full
+    C x C tiles).  bytes: q, k, v, beta read and o written once in the input
+    dtype, S0 read and S_T written once in fp32."""
+    th = w.B * w.T * w.H
+    e = 2 if w.dtype == "bf16" else 4
+    flops = th * (2 * w.chunk * (3 * w.Dk + 2 * w.Dv) + 6 * w.Dk * w.Dv)
+    nbytes = th * e * (2 * w.Dk + w.Dv + 1) + th * e * w.Dv
+    nbytes += 4 * w.B * w.H * w.Dv * w.Dk * ((1 if w.s0_std > 0 else 0) + 1)
+    return flops, nbytes
+
+
+def decode_bytes(w):
+    """HBM bytes of one decode step: S read and written (fp32), q, k, v, beta
+    read and o written in the input dtype."""
+    e = 2 if w.dtype == "bf16" else 4
+    bh = w.B * w.H
+    return bh * (8 * w.Dv * w.Dk + e * (2 * w.Dk + w.Dv + 1) + e * w.Dv)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernel sources changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("kernel_source_sha256") != source_digest():
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def run_cpu_baseline(x, w, o_gpu, st_gpu):
+    """The fp64 oracle on the whole workload (all heads, full T), timed
+    around the oracle call only with inputs already widened to fp64."""
+    import numpy as np
+
+    from oracle import delta_rule_ref
+    q, k, v, beta = (x[n].double().numpy() for n in ("q", "k", "v", "beta"))
+    S0 = None if x["S0"] is None else x["S0"].double().numpy()
+    nt = cpu_threads()
+    t0 = time.perf_counter()
+    o_ref, s_ref = delta_rule_ref(q, k, v, beta, S0, nthreads=nt)
+    dt = time.perf_counter() - t0
+    og = o_gpu.double().cpu().numpy()
+    sg = st_gpu.double().cpu().numpy()
+    par = {
+        "o_rel_err": float(np.max(np.abs(og - o_ref)) / np.max(np.abs(o_ref))),
+        "S_T_rel_err": float(np.max(np.abs(sg - s_ref)) / np.max(np.abs(s_ref))),
+        "tol": 2e-2 if w.dtype == "bf16" else 1e-4,
+        "reference": "fp64 CPU oracle, whole workload",
+    }
+    base = {
+        "value": w.B * w.T / dt,
+        "unit": "tokens/s",
+        "cores": nt,
+        "kind": "oracle",
+        "sample": (f"whole {w.name} workload ({w.B * w.H} heads x {w.T} tokens), "
+                   f"{dt:.2f} s"),
+    }
+    return base, par
+
+
+def bench_decode(torch, dr, W, reps=3):
+    w = W.get("decode")
+    x = W.generate(w)
+    dev = torch.device("cuda:0")
+    d = {n: t.to(dev) for n, t in x.items()}
+    S = d["S0"].clone()
+    outs = [torch.empty((w.B, w.H, w.Dv), dtype=w.torch_dtype, device=dev)
+            for _ in range(w.T)]
+
+    def run():
+        for t in range(w.T):
+            dr.delta_rule_recurrent_step(d["q"][t], d["k"][t], d["v"][t], d["beta"][t], S,
+                                         o=outs[t])
+
+    run()  # warm-up
+    times = []
+    for _ in range(reps):
+        S.copy_(d["S0"])  # reset outside the timed region
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        run()
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e) / 1e3)
+    t = sorted(times)[len(times) // 2]
+    per_step = t / w.T
+    gbs = decode_bytes(w) / per_step / 1e9
+    return {
+        "workload": "decode B128 H16 d128, 256 steps, bf16 in, fp32 state",
+        "tokens_per_s": w.B * w.T / t,
+        "us_per_step": per_step * 1e6,
+        "hbm_gbs_algorithmic": gbs,
+        "hbm_frac": gbs / HBM_PEAK_GBS,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="layer_1p3b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0,
+                    help="also run a device copy of this many bytes (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the delta-rule kernels shard by "
+              "(batch, head) with no communication, and this build runs on a "
+              "single MI355X. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import deltanet_delta_rule_amd as dr
+    from deltanet_delta_rule_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = W.get(args.workload)
+    log(f"generating {w.name}: B{w.B} H{w.H} T{w.T} Dk{w.Dk} Dv{w.Dv} C{w.chunk} {w.dtype}")
+    x = W.generate(w)
+    d = {n: (None if t is None else t.to(dev)) for n, t in x.items()}
+    o = torch.empty((w.B, w.T, w.H, w.Dv), dtype=w.torch_dtype, device=dev)
+    st = torch.empty((w.B, w.H, w.Dv, w.Dk), dtype=torch.float32, device=dev)
+
+    def step():
+        dr.delta_rule_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["S0"], chunk=w.chunk,
+                                o=o, S_T=st)
+
+    if args.copy_calib:
+        n = args.copy_calib // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n * 4} bytes read, {n * 4} bytes written per copy")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()  # the kernel runs on this same (current) stream
+        step()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_s = sum(a.elapsed_time(b) for a, b in ev) / K / 1e3
+    log(f"{K} steps: {wall * 1e3 / K:.3f} ms/step wall, {launch_s * 1e6:.1f} us/launch (events)")
+
+    flops, nbytes = chunk_work(w)
+    achieved = nbytes / launch_s / 1e9
+    traffic = measured_traffic()
+    roof = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "kernel": "chunk_fwd_kernel<bf16, Dk=128, C=64, 4 waves>",
+        "algorithmic_bytes_per_launch": nbytes,
+        "mean_launch_us": round(launch_s * 1e6, 2),
+        "mfma_frac": round(flops / launch_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "algorithmic_flops_per_launch": flops,
+    }
+    out = {
+        "metric": METRIC,
+        "value": w.B * w.T * K / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "Dk": w.Dk,
+                   "Dv": w.Dv, "chunk": w.chunk, "state": "fp32",
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+    }
+    if not args.no_decode:
+        log("decode: 256 steps of B128 H16 d128")
+        out["decode"] = bench_decode(torch, dr, W)
+    if not args.no_cpu_baseline:
+        log("cpu baseline: fp64 oracle on the whole workload")
+        torch.cuda.synchronize()
+        out["cpu_baseline"], out["parity"] = run_cpu_baseline(x, w, o.cpu(), st.cpu())
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

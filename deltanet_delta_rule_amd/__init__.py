@@ -1,1 +1,186 @@
-"""MI355X-native DeltaNet delta-rule operator (HIP/gfx950)."""
+"""MI355X-native DeltaNet delta-rule operator.
+
+A thin ctypes binding over ``libdeltarule.so`` (HIP kernels for gfx950 behind
+the C ABI of ``include/deltarule.h``).  The functions below carry the C entry
+points' names and only marshal arguments: they check devices, dtypes, shapes
+and contiguity, allocate missing outputs with torch, and pass raw device
+pointers plus torch's current HIP stream.  Every step of the operator runs in
+the library's kernels; there is no CPU or PyTorch fallback.  If the library
+is not built, the first call raises.
+
+    o, S_T = delta_rule_chunk_fwd(q, k, v, beta, S0=None, chunk=64)
+    o      = delta_rule_recurrent_step(q, k, v, beta, S)   # S updated in place
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "delta_rule_chunk_fwd",
+    "delta_rule_recurrent_step",
+    "delta_rule_status_string",
+    "delta_rule_version",
+    "DeltaRuleError",
+    "LIB_PATH",
+    "load_library",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdeltarule.so")
+
+DR_OK, DR_ERR_INVALID_ARG, DR_ERR_UNSUPPORTED, DR_ERR_HIP = 0, 1, 2, 3
+DR_F32, DR_BF16 = 0, 1
+
+_lib = None
+
+
+class DeltaRuleError(RuntimeError):
+    """A HIP runtime failure reported by libdeltarule."""
+
+
+def load_library():
+    """Load libdeltarule.so (built in place by ``deltanet_delta_rule_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"libdeltarule.so is not built ({LIB_PATH}); run "
+            "`python -m deltanet_delta_rule_amd.build` first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.delta_rule_chunk_fwd.restype = i32
+    lib.delta_rule_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp,
+                                         i64, i64, i64, i64, i64, i64, i32, vp]
+    lib.delta_rule_recurrent_step.restype = i32
+    lib.delta_rule_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp,
+                                              i64, i64, i64, i64, i32, vp]
+    lib.delta_rule_status_string.restype = ctypes.c_char_p
+    lib.delta_rule_status_string.argtypes = [i32]
+    lib.delta_rule_last_hip_error.restype = i32
+    lib.delta_rule_last_hip_error.argtypes = []
+    lib.delta_rule_version.restype = i32
+    lib.delta_rule_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def delta_rule_status_string(status: int) -> str:
+    return load_library().delta_rule_status_string(int(status)).decode()
+
+
+def delta_rule_version() -> int:
+    return int(load_library().delta_rule_version())
+
+
+def _check(status: int) -> None:
+    if status == DR_OK:
+        return
+    msg = delta_rule_status_string(status)
+    if status == DR_ERR_HIP:
+        raise DeltaRuleError(f"{msg} (hipError {load_library().delta_rule_last_hip_error()})")
+    if status == DR_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise ValueError(msg)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return DR_F32
+    if t.dtype == torch.bfloat16:
+        return DR_BF16
+    raise ValueError(f"q/k/v/beta must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device, stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, shape, dtype, device):
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def delta_rule_chunk_fwd(q, k, v, beta, S0=None, *, chunk: int = 64,
+                         output_final_state: bool = True, o=None, S_T=None,
+                         stream=None):
+    """Chunkwise forward.  q, k ``[B,T,H,Dk]``; v ``[B,T,H,Dv]``; beta
+    ``[B,T,H]`` (float32 or bfloat16, all the same dtype, on one GPU);
+    S0 ``[B,H,Dv,Dk]`` float32 or None.  Returns ``(o, S_T)``; S_T is None
+    when ``output_final_state`` is False.  ``o`` / ``S_T`` may be passed in
+    (S_T may be S0 itself to carry the state in place)."""
+    torch = _torch()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("delta_rule_chunk_fwd needs GPU tensors")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    _dtype_code(q)
+    _need(q, "q", (B, T, H, Dk), dt, dev)
+    _need(k, "k", (B, T, H, Dk), dt, dev)
+    _need(v, "v", (B, T, H, Dv), dt, dev)
+    _need(beta, "beta", (B, T, H), dt, dev)
+    if S0 is not None:
+        _need(S0, "S0", (B, H, Dv, Dk), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=dt, device=dev)
+    else:
+        _need(o, "o", (B, T, H, Dv), dt, dev)
+    if output_final_state:
+        if S_T is None:
+            S_T = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+        else:
+            _need(S_T, "S_T", (B, H, Dv, Dk), torch.float32, dev)
+    else:
+        S_T = None
+    st = load_library().delta_rule_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T),
+        B, T, H, Dk, Dv, int(chunk), _dtype_code(q), _stream(dev, stream))
+    _check(st)
+    return o, S_T
+
+
+def delta_rule_recurrent_step(q, k, v, beta, S, *, o=None, stream=None):
+    """One decode token: q, k ``[B,H,Dk]``; v ``[B,H,Dv]``; beta ``[B,H]``;
+    S ``[B,H,Dv,Dk]`` float32, updated in place.  Returns o ``[B,H,Dv]``."""
+    torch = _torch()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("delta_rule_recurrent_step needs GPU tensors")
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    _dtype_code(q)
+    _need(q, "q", (B, H, Dk), dt, dev)
+    _need(k, "k", (B, H, Dk), dt, dev)
+    _need(v, "v", (B, H, Dv), dt, dev)
+    _need(beta, "beta", (B, H), dt, dev)
+    _need(S, "S", (B, H, Dv, Dk), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, H, Dv), dtype=dt, device=dev)
+    else:
+        _need(o, "o", (B, H, Dv), dt, dev)
+    st = load_library().delta_rule_recurrent_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S), _ptr(o),
+        B, H, Dk, Dv, _dtype_code(q), _stream(dev, stream))
+    _check(st)
+    return o

@@ -1,0 +1,142 @@
+// C ABI of libdeltarule: argument validation and dispatch to the HIP
+// launchers.  Every check happens on the host before any HIP call, so a
+// rejected call has enqueued nothing.  See include/deltarule.h for the
+// contract of each entry point.
+#include "deltarule.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dr_launch.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned_to(const void *p, int64_t n) {
+    return (reinterpret_cast<uintptr_t>(p) % static_cast<uintptr_t>(n)) == 0;
+}
+bool supported_dim(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool supported_chunk(int64_t c) { return c == 16 || c == 32 || c == 64; }
+
+struct Span {
+    const void *p;
+    int64_t bytes;
+};
+
+bool overlaps(Span a, Span b) {
+    if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + (uintptr_t)b.bytes && b0 < a0 + (uintptr_t)a.bytes;
+}
+
+// Product of non-negative factors, or -1 when it exceeds 2^62.
+int64_t mul_checked(std::initializer_list<int64_t> xs) {
+    int64_t r = 1;
+    for (int64_t x : xs) {
+        if (x != 0 && r > (int64_t(1) << 62) / x) return -1;
+        r *= x;
+    }
+    return r;
+}
+
+dr_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return DR_OK;
+    g_last_hip_error = static_cast<int>(e);
+    return DR_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+dr_status delta_rule_chunk_fwd(const void *q, const void *k, const void *v,
+                               const void *beta, const float *S0, void *o,
+                               float *S_T, int64_t B, int64_t T, int64_t H,
+                               int64_t Dk, int64_t Dv, int64_t chunk,
+                               dr_dtype dtype, void *stream) {
+    if (dtype != DR_F32 && dtype != DR_BF16) return DR_ERR_INVALID_ARG;
+    if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0 || chunk < 0) return DR_ERR_INVALID_ARG;
+    if (!supported_dim(Dk) || !supported_dim(Dv) || !supported_chunk(chunk))
+        return DR_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0) return DR_OK;  // empty batch: nothing to do
+
+    const int64_t esz = dtype == DR_BF16 ? 2 : 4;
+    const int64_t nqk = mul_checked({B, T, H, Dk}), nv = mul_checked({B, T, H, Dv});
+    const int64_t nb = mul_checked({B, T, H}), ns = mul_checked({B, H, Dv, Dk});
+    if (nqk < 0 || nv < 0 || nb < 0 || ns < 0) return DR_ERR_UNSUPPORTED;
+    // grid = B*H*(Dv/16) at most; sequence length and heads index in 32 bits
+    if (T > INT32_MAX || H > INT32_MAX || mul_checked({B, H, Dv / 16}) > INT32_MAX)
+        return DR_ERR_UNSUPPORTED;
+
+    if (T > 0 && (!q || !k || !v || !beta || !o)) return DR_ERR_INVALID_ARG;
+    // q, k and the states are read in 16-byte vectors; v, beta and o element-wise
+    const void *vec_ptrs[] = {q, k, S0, S_T};
+    for (const void *p : vec_ptrs)
+        if (p && !aligned16(p)) return DR_ERR_INVALID_ARG;
+    const void *elem_ptrs[] = {v, beta, o};
+    for (const void *p : elem_ptrs)
+        if (p && !aligned_to(p, esz)) return DR_ERR_INVALID_ARG;
+
+    const Span in[] = {{q, nqk * esz}, {k, nqk * esz}, {v, nv * esz}, {beta, nb * esz},
+                       {S0, ns * 4}};
+    const Span so{o, nv * esz}, sst{S_T, ns * 4};
+    for (const Span &s : in) {
+        if (T > 0 && overlaps(so, s)) return DR_ERR_INVALID_ARG;
+        // S_T may be exactly S0 (in-place carry); any other overlap is rejected
+        if (overlaps(sst, s) && !(s.p == S0 && S_T == S0)) return DR_ERR_INVALID_ARG;
+    }
+    if (T > 0 && overlaps(so, sst)) return DR_ERR_INVALID_ARG;
+
+    return hip_status(dr::launch_chunk_fwd(q, k, v, beta, S0, o, S_T, B, T, H, (int)Dk,
+                                           (int)Dv, (int)chunk, dtype == DR_BF16,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+dr_status delta_rule_recurrent_step(const void *q, const void *k,
+                                    const void *v, const void *beta, float *S,
+                                    void *o, int64_t B, int64_t H, int64_t Dk,
+                                    int64_t Dv, dr_dtype dtype, void *stream) {
+    if (dtype != DR_F32 && dtype != DR_BF16) return DR_ERR_INVALID_ARG;
+    if (B < 0 || H < 0 || Dk < 0 || Dv < 0) return DR_ERR_INVALID_ARG;
+    if (!supported_dim(Dk) || !supported_dim(Dv)) return DR_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0) return DR_OK;
+
+    const int64_t esz = dtype == DR_BF16 ? 2 : 4;
+    const int64_t bh = mul_checked({B, H});
+    const int64_t ns = mul_checked({B, H, Dv, Dk});
+    if (bh < 0 || ns < 0 || mul_checked({bh, Dv}) > INT32_MAX) return DR_ERR_UNSUPPORTED;
+
+    if (!q || !k || !v || !beta || !S || !o) return DR_ERR_INVALID_ARG;
+    // q, k and S are read in 16-byte vectors; v, beta and o element-wise
+    if (!aligned16(q) || !aligned16(k) || !aligned16(S)) return DR_ERR_INVALID_ARG;
+    if (!aligned_to(v, esz) || !aligned_to(beta, esz) || !aligned_to(o, esz))
+        return DR_ERR_INVALID_ARG;
+    const Span so{o, bh * Dv * esz}, ss{S, ns * 4};
+    const Span in[] = {{q, bh * Dk * esz}, {k, bh * Dk * esz}, {v, bh * Dv * esz},
+                       {beta, bh * esz}};
+    if (overlaps(so, ss)) return DR_ERR_INVALID_ARG;
+    for (const Span &s : in)
+        if (overlaps(so, s) || overlaps(ss, s)) return DR_ERR_INVALID_ARG;
+
+    return hip_status(dr::launch_recurrent_step(q, k, v, beta, S, o, bh, (int)Dk, (int)Dv,
+                                                dtype == DR_BF16,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+const char *delta_rule_status_string(dr_status status) {
+    switch (status) {
+    case DR_OK: return "DR_OK";
+    case DR_ERR_INVALID_ARG: return "DR_ERR_INVALID_ARG: invalid argument";
+    case DR_ERR_UNSUPPORTED: return "DR_ERR_UNSUPPORTED: unsupported size or shape";
+    case DR_ERR_HIP: return "DR_ERR_HIP: HIP runtime error (see delta_rule_last_hip_error)";
+    default: return "unknown dr_status";
+    }
+}
+
+int delta_rule_last_hip_error(void) { return g_last_hip_error; }
+
+int delta_rule_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,198 @@
+// Device-side building blocks shared by the delta-rule kernels (gfx950).
+//
+// Element types: `float` (fp32 inputs) or `__bf16` (bfloat16 inputs).  All
+// arithmetic accumulates in fp32; fp32 -> bf16 narrowing rounds to nearest
+// even (the hardware conversion).
+//
+// Matrix-core tiles.  Every product is built from 16x16 output tiles on the
+// MFMA units.  The lane layout of an output tile (the "D layout") is the one
+// all 16x16 MFMA shapes share on CDNA: lane l = 16*g + r (g = l/16, r = l%16)
+// holds D[4g + i][r] for i = 0..3.
+//
+// Operands are fed in one canonical k order.  For a contraction slab starting
+// at k0, lane (g, r) supplies the four k indices k0 + 4g + {0,1,2,3} of its
+// row r (A) or column r (B); a 32-wide slab adds k0 + 16 + 4g + {0,1,2,3}.
+// The hardware contracts lane (g, r)'s j-th A element with lane (g, n)'s j-th
+// B element, so any k permutation applied identically to A and B gives the
+// same sum -- and with this one, a D-layout tile stack whose rows run along k
+// is already a B operand (lane (g, r) holds rows 4g..4g+3 of each 16-row
+// tile).  Results computed with tokens along M can therefore feed the next
+// product over tokens straight from registers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dr {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+
+template <typename DT>
+__device__ __forceinline__ DT from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+// Operand fragments: 8 elements (32-wide slab) or 4 (16-wide slab) per lane.
+template <typename DT> struct Frag;
+template <> struct Frag<__bf16> {
+    typedef bf16x8 k32;
+    typedef bf16x4 k16;
+};
+struct f32x8_arr { float v[8]; };
+struct f32x4_arr { float v[4]; };
+template <> struct Frag<float> {
+    typedef f32x8_arr k32;
+    typedef f32x4_arr k16;
+};
+
+__device__ __forceinline__ void frag_set(bf16x8 &f, int i, float x) { f[i] = (__bf16)x; }
+__device__ __forceinline__ void frag_set(bf16x4 &f, int i, float x) { f[i] = (__bf16)x; }
+__device__ __forceinline__ void frag_set(f32x8_arr &f, int i, float x) { f.v[i] = x; }
+__device__ __forceinline__ void frag_set(f32x4_arr &f, int i, float x) { f.v[i] = x; }
+
+// acc += A * B over one 32-wide k slab.
+__device__ __forceinline__ void mma_k32(f32x4 &acc, const bf16x8 &a, const bf16x8 &b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma_k32(f32x4 &acc, const f32x8_arr &a, const f32x8_arr &b) {
+    // 16x16x4 fp32 MFMA: lane group g supplies hardware k = g.  Instruction j
+    // (j < 4) covers k0 + 4g + j, instruction 4 + j covers k0 + 16 + 4g + j.
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
+}
+// acc += A * B over one 16-wide k slab.
+__device__ __forceinline__ void mma_k16(f32x4 &acc, const bf16x4 &a, const bf16x4 &b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                    __builtin_bit_cast(i16x4, b),
+                                                    acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma_k16(f32x4 &acc, const f32x4_arr &a, const f32x4_arr &b) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
+}
+
+// Load 4 consecutive elements (an aligned quad) as floats.
+__device__ __forceinline__ void load4(const float *p, float (&x)[4]) {
+    const float4 t = *reinterpret_cast<const float4 *>(p);
+    x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+}
+__device__ __forceinline__ void load4(const __bf16 *p, float (&x)[4]) {
+    const bf16x4 t = *reinterpret_cast<const bf16x4 *>(p);
+    x[0] = (float)t[0]; x[1] = (float)t[1]; x[2] = (float)t[2]; x[3] = (float)t[3];
+}
+
+// Operand fragment of a row-major matrix M (leading dimension ld, elements of
+// type DT): lane (g, r) takes M[row0 + r][k0 + 4g + 0..3] (+ k0 + 16 + ...).
+// Serves as A (rows = m) or as B when B[k][n] = M[n][k] (rows = n).
+__device__ __forceinline__ void frag_rows(const __bf16 *M, int ld, int row0, int k0,
+                                          int lane, bf16x8 &f) {
+    const int g = lane >> 4, r = lane & 15;
+    const __bf16 *p = M + (row0 + r) * ld + k0 + 4 * g;
+    const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(p);
+    const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(p + 16);
+    f = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void frag_rows(const __bf16 *M, int ld, int row0, int k0,
+                                          int lane, bf16x4 &f) {
+    const int g = lane >> 4, r = lane & 15;
+    f = *reinterpret_cast<const bf16x4 *>(M + (row0 + r) * ld + k0 + 4 * g);
+}
+__device__ __forceinline__ void frag_rows(const float *M, int ld, int row0, int k0,
+                                          int lane, f32x8_arr &f) {
+    const int g = lane >> 4, r = lane & 15;
+    const float *p = M + (row0 + r) * ld + k0 + 4 * g;
+    const float4 lo = *reinterpret_cast<const float4 *>(p);
+    const float4 hi = *reinterpret_cast<const float4 *>(p + 16);
+    f.v[0] = lo.x; f.v[1] = lo.y; f.v[2] = lo.z; f.v[3] = lo.w;
+    f.v[4] = hi.x; f.v[5] = hi.y; f.v[6] = hi.z; f.v[7] = hi.w;
+}
+__device__ __forceinline__ void frag_rows(const float *M, int ld, int row0, int k0,
+                                          int lane, f32x4_arr &f) {
+    const int g = lane >> 4, r = lane & 15;
+    const float4 t = *reinterpret_cast<const float4 *>(M + (row0 + r) * ld + k0 + 4 * g);
+    f.v[0] = t.x; f.v[1] = t.y; f.v[2] = t.z; f.v[3] = t.w;
+}
+
+// Fragment of the transpose of a row-major matrix M over one 16-wide slab:
+// lane (g, r) takes M[k0 + 4g + j][col0 + r] for j = 0..3, i.e. column
+// col0 + r of M with k running down the rows.  For bf16 this is one LDS
+// transpose read (ds_read_b64_tr_b16): the 16 lanes of group g each address
+// one 8-byte piece of the 4 x 16 block M[k0+4g .. k0+4g+3][col0 .. col0+15]
+// (lane r: row r/4, columns 4(r%4)..4(r%4)+3) and the hardware hands lane r
+// column r of that block.  fp32 has no transpose read and gathers instead.
+__device__ __forceinline__ void frag_cols16(const __bf16 *M, int ld, int k0, int col0,
+                                            int lane, bf16x4 &f) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const int g = lane >> 4, r = lane & 15;
+    const __bf16 *p = M + (k0 + 4 * g + (r >> 2)) * ld + col0 + 4 * (r & 3);
+    f = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p));
+}
+__device__ __forceinline__ void frag_cols16(const float *M, int ld, int k0, int col0,
+                                            int lane, f32x4_arr &f) {
+    const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.v[j] = M[(k0 + 4 * g + j) * ld + col0 + r];
+}
+__device__ __forceinline__ void frag_cols32(const __bf16 *M, int ld, int k0, int col0,
+                                            int lane, bf16x8 &f) {
+    bf16x4 lo, hi;
+    frag_cols16(M, ld, k0, col0, lane, lo);
+    frag_cols16(M, ld, k0 + 16, col0, lane, hi);
+    f = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void frag_cols32(const float *M, int ld, int k0, int col0,
+                                            int lane, f32x8_arr &f) {
+    f32x4_arr lo, hi;
+    frag_cols16(M, ld, k0, col0, lane, lo);
+    frag_cols16(M, ld, k0 + 16, col0, lane, hi);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f.v[j] = lo.v[j];
+        f.v[4 + j] = hi.v[j];
+    }
+}
+
+// B operand from a stack of D-layout accumulator tiles whose rows run along
+// k: tile k0/16 (and k0/16 + 1 for a 32-wide slab), narrowed to DT.
+template <typename F>
+__device__ __forceinline__ void frag_from_acc32(const f32x4 &t0, const f32x4 &t1, F &f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        frag_set(f, i, t0[i]);
+        frag_set(f, 4 + i, t1[i]);
+    }
+}
+template <typename F>
+__device__ __forceinline__ void frag_from_acc16(const f32x4 &t0, F &f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) frag_set(f, i, t0[i]);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Workgroup barrier for hand-offs through LDS: waits for this wave's LDS
+// operations, then meets the other waves.  Unlike __syncthreads() it carries
+// no fence over global memory, so register prefetches and output stores stay
+// in flight across it.  The "memory" clobber keeps the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Orders this wave's LDS writes before its later LDS reads of data written by
+// other lanes of the same wave (no other wave involved, so no barrier).
+__device__ __forceinline__ void wave_lds_fence() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+}  // namespace dr

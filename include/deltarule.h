@@ -1,0 +1,144 @@
+/*
+ * libdeltarule -- the DeltaNet delta-rule operator on AMD Instinct MI355X
+ * (gfx950), behind a plain C ABI.
+ *
+ * The operator.  For every batch row b and head h independently, with a state
+ * S of d_v x d_k mapping key space to value space:
+ *
+ *     S_t = S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *         = S_{t-1} + beta_t (v_t - S_{t-1} k_t) k_t^T
+ *     o_t = S_t q_t                               (read after the write)
+ *
+ *   - houmin.site "infra/delta-net", section "DeltaNet 引入 Delta Rule":
+ *     both forms of the update and the read o_t = S_t q_t;
+ *   - hada.io digest "Tour d'horizon des variantes d'attention lineaire de la
+ *     famille DeltaNet", sections "DeltaNet : ecrire l'erreur de prediction
+ *     plutot que la valeur" and "Transition d'etat structuree";
+ *   - frankenstein-transformer docs, deltanet_attn.py, module docstring: the
+ *     same update with beta in (0,1) and L2-normalised keys.
+ *
+ * The operator does not normalise q or k, does not scale q and does not
+ * clamp beta: callers pass the features they want (the DeltaNet layer of fla,
+ * fla/layers/delta_net.py, feeds SiLU + L2-normalised q/k and may double beta
+ * into (0,2)).
+ *
+ * Common conventions
+ *   Layout   Contiguous row-major.  q, k: [B,T,H,Dk]; v, o: [B,T,H,Dv];
+ *            beta: [B,T,H] (one scalar per token and head);
+ *            states S0, S_T, S: [B,H,Dv,Dk], always fp32.
+ *            The decode entry point drops the T axis.
+ *   Dtype    DR_F32: q, k, v, beta, o are float.  DR_BF16: they are bfloat16
+ *            (raw 16-bit storage).  States are float in both cases.  All
+ *            accumulation is fp32.
+ *   Sizes    Dk and Dv in {16, 32, 64, 128}; chunk in {16, 32, 64};
+ *            B, H, T >= 0 (B or H zero: the call does nothing).  T and H
+ *            must fit in int32, and so must B*H*Dv/16.
+ *   Pointers Device pointers (hipMalloc'd or equivalent).  q, k and every
+ *            state pointer must be 16-byte aligned (they are read as 16-byte
+ *            vectors); v, beta and o need only their element alignment.
+ *            They are borrowed: the library never allocates, frees or keeps
+ *            them beyond the work queued on `stream`.
+ *   Stream   `stream` is a hipStream_t passed as void*; NULL is the default
+ *            stream.  Calls only enqueue work: they never synchronise the
+ *            device and never block on the GPU.
+ *   Errors   Every entry point returns a dr_status.  Arguments are validated
+ *            on the host before any HIP call; on DR_ERR_INVALID_ARG or
+ *            DR_ERR_UNSUPPORTED nothing was enqueued.  DR_ERR_HIP means a HIP
+ *            launch reported an error; the hipError_t value is then available
+ *            from delta_rule_last_hip_error() on the calling thread.
+ *   Threads  No global mutable state besides that thread-local error code:
+ *            concurrent calls on different streams are safe.  Calls on one
+ *            stream run in order.
+ */
+#ifndef DELTARULE_H
+#define DELTARULE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dr_status {
+    DR_OK = 0,
+    DR_ERR_INVALID_ARG = 1, /* null/misaligned pointer, negative size, bad enum */
+    DR_ERR_UNSUPPORTED = 2, /* valid request outside the supported size set */
+    DR_ERR_HIP = 3          /* a HIP runtime call failed; see last_hip_error */
+} dr_status;
+
+typedef enum dr_dtype {
+    DR_F32 = 0,
+    DR_BF16 = 1
+} dr_dtype;
+
+/*
+ * delta_rule_chunk_fwd -- training / prefill forward over whole sequences.
+ *
+ * Computes o[b,t,h,:] = S_t q_t for every token and, when S_T is not NULL,
+ * the final state S_T = S_T(b,h) after the last token.  The result is the
+ * token recurrence above; it is evaluated in the chunkwise-parallel form
+ * (paperlayer summary of arXiv:2406.06484, section 3 "Parallelizing DeltaNet
+ * Across the Sequence Dimension" and App. B.2 "UT transform derivation";
+ * hada.io digest, section "Chunkwise KDA : reorganiser la recurrence en
+ * multiplications matricielles"): per chunk of `chunk` tokens, a unit
+ * lower-triangular solve resolves the chunk's errors against its incoming
+ * state, then one set of matrix products writes the chunk's outputs and
+ * advances the state.
+ *
+ *   q, k    [B,T,H,Dk]  inputs, dtype `dtype`
+ *   v       [B,T,H,Dv]  input,  dtype `dtype`
+ *   beta    [B,T,H]     input,  dtype `dtype`; any finite value
+ *   S0      [B,H,Dv,Dk] fp32 initial state, or NULL for the zero state
+ *   o       [B,T,H,Dv]  output, dtype `dtype`; every element is written
+ *   S_T     [B,H,Dv,Dk] fp32 final state, or NULL to skip it.  S_T may be the
+ *                       same buffer as S0 (state carried in place); any other
+ *                       overlap between outputs and inputs is not allowed.
+ *   chunk   tokens per chunk (16, 32 or 64).  T need not be a multiple of it;
+ *           the last chunk is shorter.  The result does not depend on chunk
+ *           beyond rounding.
+ *
+ * T == 0 writes S_T = S0 (or zeros) and no o.
+ */
+dr_status delta_rule_chunk_fwd(const void *q, const void *k, const void *v,
+                               const void *beta, const float *S0, void *o,
+                               float *S_T, int64_t B, int64_t T, int64_t H,
+                               int64_t Dk, int64_t Dv, int64_t chunk,
+                               dr_dtype dtype, void *stream);
+
+/*
+ * delta_rule_recurrent_step -- one decode token per sequence, state in place.
+ *
+ * For every (b,h): reads S, applies the delta-rule write for the token
+ * (q,k,v,beta) and stores the new state back into S, then writes
+ * o = S_new q.  This is the token-serial schedule of the same recurrence
+ * (hada.io digest, section "Kernel Triton recurrent fusionne pour le
+ * decodage"; fla fla/layers/delta_net.py routes short inputs to its fused
+ * recurrent kernel); S is streamed through HBM once per call.
+ *
+ *   q, k    [B,H,Dk]     inputs, dtype `dtype`
+ *   v       [B,H,Dv]     input,  dtype `dtype`
+ *   beta    [B,H]        input,  dtype `dtype`
+ *   S       [B,H,Dv,Dk]  fp32 state, read and overwritten in place
+ *   o       [B,H,Dv]     output, dtype `dtype`; must not overlap S
+ */
+dr_status delta_rule_recurrent_step(const void *q, const void *k,
+                                    const void *v, const void *beta, float *S,
+                                    void *o, int64_t B, int64_t H, int64_t Dk,
+                                    int64_t Dv, dr_dtype dtype, void *stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *delta_rule_status_string(dr_status status);
+
+/* The hipError_t value of the last DR_ERR_HIP returned on this thread
+ * (0 if none). */
+int delta_rule_last_hip_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int delta_rule_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DELTARULE_H */

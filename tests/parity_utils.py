@@ -1,0 +1,65 @@
+"""Helpers shared by the GPU parity tests: run the HIP path and the fp64
+oracle on the same seeded inputs and measure the error the way the tolerance
+is stated -- max |gpu - ref| relative to max |ref| -- for o and the final
+state separately."""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import torch
+
+from oracle import delta_rule_ref
+
+# fp32 inputs: 1e-4; bf16 inputs: 2e-2 (fp32 state), both relative to max|ref|.
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+
+
+def threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def rel_err(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if ref.size == 0:
+        return 0.0
+    den = np.max(np.abs(ref))
+    if not np.all(np.isfinite(got)):
+        return float("inf")
+    return float(np.max(np.abs(got - ref)) / (den if den > 0 else 1.0))
+
+
+def to_np(t):
+    return t.detach().to("cpu").double().numpy()
+
+
+def oracle_heads(x, heads):
+    """Oracle on a subset of (b, h) pairs of a chunk workload's inputs.
+
+    Returns (o [T, n, Dv], S_T [n, Dv, Dk]) for the n pairs in `heads`, by
+    stacking the selected heads into one batch row (heads are independent).
+    """
+    sel = lambda t: np.stack([to_np(t[b, :, h]) for b, h in heads], axis=1)[None]
+    q, k, v = sel(x["q"]), sel(x["k"]), sel(x["v"])
+    beta = np.stack([to_np(x["beta"][b, :, h]) for b, h in heads], axis=1)[None]
+    S0 = None
+    if x["S0"] is not None:
+        S0 = np.stack([x["S0"][b, h].double().numpy() for b, h in heads])[None]
+    o, st = delta_rule_ref(q, k, v, beta, S0, nthreads=threads())
+    return o[0], st[0]
+
+
+def gather_heads(o_gpu, st_gpu, heads):
+    o = np.stack([to_np(o_gpu[b, :, h]) for b, h in heads], axis=1)
+    st = np.stack([to_np(st_gpu[b, h]) for b, h in heads])
+    return o, st
+
+
+def to_dev(x, device="cuda"):
+    return {n: (None if t is None else t.to(device)) for n, t in x.items()}

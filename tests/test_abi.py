@@ -1,0 +1,140 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function ``include/deltarule.h``
+declares, and reject bad arguments on the host before any HIP call.  Only
+rejected calls are made here: a call that passes validation would enqueue GPU
+work, which this suite never does.
+"""
+from __future__ import annotations
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import deltanet_delta_rule_amd as dr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# Fake device addresses: valid-looking and 16-byte aligned, far apart, never
+# dereferenced because every call below fails validation first.
+P = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(8)]
+MISALIGNED = ctypes.c_void_p(0x100000 * 9 + 4)   # element-aligned, not 16-byte
+ODD = ctypes.c_void_p(0x100000 * 9 + 1)          # not even element-aligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dr.LIB_PATH):
+        from deltanet_delta_rule_amd import build
+        build.build()
+    return dr.load_library()
+
+
+def _declared_functions():
+    names = set()
+    for path in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b([A-Za-z_]\w*)\s*\(", text):
+            name = m.group(1)
+            if name.startswith("delta_rule_"):
+                names.add(name)
+    return sorted(names)
+
+
+def test_header_declares_entry_points():
+    names = _declared_functions()
+    assert "delta_rule_chunk_fwd" in names
+    assert "delta_rule_recurrent_step" in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"libdeltarule.so does not export {name}"
+
+
+def test_status_strings_and_version(lib):
+    for code in range(4):
+        s = dr.delta_rule_status_string(code)
+        assert s.startswith("DR_")
+    assert "unknown" in dr.delta_rule_status_string(99)
+    assert dr.delta_rule_version() >= 100
+    assert lib.delta_rule_last_hip_error() == 0
+
+
+def _chunk(lib, q=P[0], k=P[1], v=P[2], beta=P[3], S0=None, o=P[4], S_T=P[5],
+           B=2, T=64, H=2, Dk=64, Dv=64, chunk=64, dtype=dr.DR_BF16):
+    return lib.delta_rule_chunk_fwd(q, k, v, beta, S0, o, S_T, B, T, H, Dk, Dv,
+                                    chunk, dtype, None)
+
+
+def _step(lib, q=P[0], k=P[1], v=P[2], beta=P[3], S=P[4], o=P[5], B=2, H=2,
+          Dk=64, Dv=64, dtype=dr.DR_BF16):
+    return lib.delta_rule_recurrent_step(q, k, v, beta, S, o, B, H, Dk, Dv,
+                                         dtype, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=-1), dict(T=-1), dict(H=-1), dict(chunk=-16), dict(dtype=7),
+    dict(q=None), dict(k=None), dict(v=None), dict(beta=None), dict(o=None),
+    dict(q=MISALIGNED), dict(k=MISALIGNED), dict(S0=MISALIGNED),
+    dict(S_T=MISALIGNED), dict(v=ODD), dict(beta=ODD), dict(o=ODD),
+    dict(o=P[0]),                    # output overlaps q
+    dict(S_T=P[1]),                  # final state overlaps k
+    dict(S0=P[6], S_T=P[4]),         # final state overlaps o
+])
+def test_chunk_rejects_invalid(lib, kw):
+    assert _chunk(lib, **kw) == dr.DR_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [
+    dict(Dk=48), dict(Dv=8), dict(Dk=256), dict(chunk=8), dict(chunk=128),
+    dict(chunk=48), dict(T=2 ** 31),
+])
+def test_chunk_rejects_unsupported(lib, kw):
+    assert _chunk(lib, **kw) == dr.DR_ERR_UNSUPPORTED
+
+
+def test_chunk_empty_batch_is_a_no_op(lib):
+    # B or H zero: nothing to do, no HIP call
+    assert _chunk(lib, B=0) == dr.DR_OK
+    assert _chunk(lib, H=0, q=None, k=None) == dr.DR_OK
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=-3), dict(dtype=2), dict(q=None), dict(S=None), dict(o=None),
+    dict(q=MISALIGNED), dict(S=MISALIGNED), dict(beta=ODD), dict(v=ODD),
+    dict(o=P[4]),                          # o overlaps S
+    dict(S=P[2]),                          # state overlaps v
+])
+def test_step_rejects_invalid(lib, kw):
+    assert _step(lib, **kw) == dr.DR_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(Dk=24), dict(Dv=512), dict(Dk=8)])
+def test_step_rejects_unsupported(lib, kw):
+    assert _step(lib, **kw) == dr.DR_ERR_UNSUPPORTED
+
+
+def test_step_empty_batch_is_a_no_op(lib):
+    assert _step(lib, B=0) == dr.DR_OK
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 4, 1, 16)
+    with pytest.raises(ValueError):
+        dr.delta_rule_chunk_fwd(x, x, x, x[..., 0])
+    with pytest.raises(ValueError):
+        dr.delta_rule_recurrent_step(x[:, 0], x[:, 0], x[:, 0], x[:, 0, :, 0],
+                                     torch.zeros(1, 1, 16, 16))
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(dr, "_lib", None)
+    monkeypatch.setattr(dr, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        dr.load_library()
