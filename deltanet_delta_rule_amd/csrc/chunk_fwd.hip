@@ -64,149 +64,168 @@ struct ChunkCfg {
     static constexpr int KSD = (DK % 32 == 0) ? 32 : 16;  // slab over d_k
     static constexpr int KSC = (C % 32 == 0) ? 32 : 16;   // slab over tokens
     static constexpr int PADE = 16 / (int)sizeof(DT);     // 16 bytes per row
-    static constexpr int LDK = DK + PADE;       // K, Q row stride
-    static constexpr int LDC = C + PADE;        // Ti, P (and K^T) row stride
-    static constexpr int LDA = C + 4;           // A row stride (fp32)
-    static constexpr int LDD = 16 + PADE;       // diagonal-inverse scratch stride
+    // Row strides.  Row-fragment reads (lane r reads row r) are free of LDS
+    // bank conflicts when the stride is 4*odd dwords; transpose reads (a lane
+    // group reads 4 rows x 32 bytes) when it is 8*odd dwords.
+    static constexpr int LDK = DK + PADE;       // K, Q (row fragments)
+    static constexpr int LDP = C + PADE;        // P (row fragments)
+    static constexpr int LDT = C + 2 * PADE;    // Ti^T (transpose reads)
+    static constexpr int LDA = C + 4;           // A (fp32)
+    static constexpr int LDD = 16 + PADE;       // diagonal-inverse scratch
     static constexpr int VEC = Vec16<DT>::N;    // elements per 16-byte load
     static constexpr int VPR = DK / VEC;        // 16-byte vectors per K row
     static constexpr int NTHR = 64 * NW;
     static constexpr int NPRE = (C * VPR + NTHR - 1) / NTHR;  // vectors/thread
     static constexpr int NTILE = NT * (NT + 1) / 2;          // lower 16x16 tiles
+    static constexpr int LDV = BV + 2 * PADE;   // V tile (transpose reads)
+    static constexpr int VPRV = BV / VEC;       // 16-byte vectors per V tile row
+    static constexpr int NPREV = (C * VPRV + NTHR - 1) / NTHR;  // V vectors/thread
 };
 
 template <bool K32, typename DT> struct SlabFrag;
 template <typename DT> struct SlabFrag<true, DT> { typedef typename Frag<DT>::k32 type; };
 template <typename DT> struct SlabFrag<false, DT> { typedef typename Frag<DT>::k16 type; };
 
-// acc += M[rows row0..row0+15, slab k0] * (B operand built from accumulator
-// tiles bt[k0/16], bt[k0/16 + 1]).
-template <typename DT, int KS>
-__device__ __forceinline__ void mma_rows_acc(f32x4 &acc, const DT *M, int ld, int row0,
-                                             int k0, int lane, const f32x4 *bt) {
-    typename SlabFrag<KS == 32, DT>::type fa, fb;
-    frag_rows(M, ld, row0, k0, lane, fa);
-    if constexpr (KS == 32) {
-        frag_from_acc32(bt[k0 / 16], bt[k0 / 16 + 1], fb);
-        mma_k32(acc, fa, fb);
-    } else {
-        frag_from_acc16(bt[k0 / 16], fb);
-        mma_k16(acc, fa, fb);
-    }
-}
-
-// acc += M^T[rows col0..col0+15, slab k0] * (B from accumulator tiles), where
-// M is row-major with k along its rows (the transpose is read from LDS).
-template <typename DT, int KS>
-__device__ __forceinline__ void mma_cols_acc(f32x4 &acc, const DT *M, int ld, int col0,
-                                             int k0, int lane, const f32x4 *bt) {
-    typename SlabFrag<KS == 32, DT>::type fa, fb;
-    if constexpr (KS == 32) {
-        frag_cols32(M, ld, k0, col0, lane, fa);
-        frag_from_acc32(bt[k0 / 16], bt[k0 / 16 + 1], fb);
-        mma_k32(acc, fa, fb);
-    } else {
-        frag_cols16(M, ld, k0, col0, lane, fa);
-        frag_from_acc16(bt[k0 / 16], fb);
-        mma_k16(acc, fa, fb);
-    }
-}
-
-// acc += M1[rows ra..ra+15, slab k0] * M2[rows rb..rb+15, slab k0]^T
-template <typename DT, int KS>
-__device__ __forceinline__ void mma_rows_rows(f32x4 &acc, const DT *M1, const DT *M2,
-                                              int ld, int ra, int rb, int k0, int lane) {
-    typename SlabFrag<KS == 32, DT>::type fa, fb;
-    frag_rows(M1, ld, ra, k0, lane, fa);
-    frag_rows(M2, ld, rb, k0, lane, fb);
-    if constexpr (KS == 32) mma_k32(acc, fa, fb);
-    else mma_k16(acc, fa, fb);
-}
-
-// Row and column of the jj-th lower tile (row-major order over ti >= tj).
-__device__ __forceinline__ void lower_tile(int jj, int &ti, int &tj) {
-    ti = 0;
-    while ((ti + 1) * (ti + 2) / 2 <= jj) ++ti;
-    tj = jj - ti * (ti + 1) / 2;
-}
-
 // ---------------------------------------------------------------------------
 // Per-chunk building blocks shared by both kernels.
 // ---------------------------------------------------------------------------
 
-// Gram tiles of one chunk, split over the waves (tile jobs w, w + NW, ...):
+// Gram tiles of one chunk:
 //   Af[i][j] = beta_i (K K^T)_ij for i > j, else 0      (fp32)
 //   Ps[i][j] = (Q K^T)_ij for i >= j, else 0             (DT)
-// Only lower tiles are written; upper tiles of Ps stay zero.
+// Each 16x16 tile (ti, tj) is computed transposed, D = K_tj X_ti^T (X = K or
+// Q), so lane (g, r) ends up with row 16ti + r, columns 16tj + 4g .. + 3: one
+// vector store per tile.  Work comes in row jobs: the A-row of tile row ti
+// goes to wave ti % NW and the P-row to wave (NT-1-ti) % NW, so with NW = NT
+// every wave computes NT+1 tiles.  A job loads all its operand fragments
+// before its first MFMA.  Upper tiles of Ps stay zero.
 template <typename DT, int DK, int C, int NW>
 __device__ __forceinline__ void gram_tiles(const DT *Ks, const DT *Qs, const float *betas,
                                            float *Af, DT *Ps, int wave, int lane) {
     typedef ChunkCfg<DT, DK, C, NW> G;
+    constexpr int NT = G::NT, KSD = G::KSD, NSD = DK / KSD;
+    typedef typename SlabFrag<KSD == 32, DT>::type FD;
     const int g = lane >> 4, r = lane & 15;
-    constexpr int NJ = (2 * G::NTILE + NW - 1) / NW;
 #pragma unroll
-    for (int s = 0; s < NJ; ++s) {
-        const int job = wave + s * NW;
-        if (job < 2 * G::NTILE) {
-            const bool isP = job >= G::NTILE;
-            int ti, tj;
-            lower_tile(isP ? job - G::NTILE : job, ti, tj);
-            f32x4 acc = zero4();
+    for (int ti = 0; ti < NT; ++ti) {
 #pragma unroll
-            for (int k0 = 0; k0 < DK; k0 += G::KSD)
-                mma_rows_rows<DT, G::KSD>(acc, isP ? Qs : Ks, Ks, G::LDK, 16 * ti, 16 * tj, k0,
-                                          lane);
+        for (int isP = 0; isP < 2; ++isP) {
+            const int owner = isP ? (NT - 1 - ti) % NW : ti % NW;
+            if (owner != wave) continue;
+            FD fx[NSD], fk[NT][NSD];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * ti + 4 * g + i, col = 16 * tj + r;
-                if (isP)
-                    Ps[row * G::LDC + col] = from_f32<DT>(row >= col ? acc[i] : 0.f);
-                else
-                    Af[row * G::LDA + col] = (row > col) ? betas[row] * acc[i] : 0.f;
+            for (int s = 0; s < NSD; ++s) frag_rows(isP ? Qs : Ks, G::LDK, 16 * ti, s * KSD, lane, fx[s]);
+#pragma unroll
+            for (int tj = 0; tj <= ti; ++tj)
+#pragma unroll
+                for (int s = 0; s < NSD; ++s)
+                    frag_rows(Ks, G::LDK, 16 * tj, s * KSD, lane, fk[tj][s]);
+            const int row = 16 * ti + r;
+            const float brow = betas[row];
+#pragma unroll
+            for (int tj = 0; tj <= ti; ++tj) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int s = 0; s < NSD; ++s) {
+                    if constexpr (KSD == 32) mma_k32(acc, fk[tj][s], fx[s]);
+                    else mma_k16(acc, fk[tj][s], fx[s]);
+                }
+                const int col = 16 * tj + 4 * g;  // columns col .. col+3 of row
+                if (isP) {
+                    typename Frag<DT>::k16 out;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) frag_set(out, e, row >= col + e ? acc[e] : 0.f);
+                    store_frag16(Ps + row * G::LDP + col, out);
+                } else {
+                    f32x4 out;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) out[e] = row > col + e ? brow * acc[e] : 0.f;
+                    *reinterpret_cast<f32x4 *>(Af + row * G::LDA + col) = out;
+                }
             }
         }
     }
 }
 
-// Ti = (I + A)^{-1} by blocks of 16, written into Ts (DT, row-major).
+// Ti = (I + A)^{-1} by blocks of 16, stored transposed: TsT[col][row] =
+// Ti[row][col] (Ti is unit lower-triangular, so TsT is upper-triangular; its
+// lower blocks stay zero).
 //  1. Every wave inverts all NT diagonal blocks (lane = 16*d + column, fp32
-//     forward substitution) into its private scratch Dw, stored transposed
-//     (row 16d + c of Dw is column c of block d).
-//  2. Wave w then fills the block columns j = w, w + NW, ...:
-//       Ti_jj from step 1, and for i > j
+//     forward substitution).  A lane's column of Ti_dd is a row of Ti^T, kept
+//     in the wave's private scratch Dw and, for the owning wave, in TsT.
+//  2. Wave w fills the block columns j = w, w + NW, ... of Ti: for i > j
 //       Ti_ij = -Ti_ii * sum_{k=j}^{i-1} A_ik Ti_kj,
 //     each block column needing only its own earlier blocks and the diagonal
 //     inverses, so no wave waits for another.
 template <typename DT, int DK, int C, int NW>
-__device__ __forceinline__ void tri_inverse(const float *Af, DT *Ts, DT *Dw, int wave,
+__device__ __forceinline__ void tri_inverse(const float *Af, DT *TsT, DT *Dw, int wave,
                                             int lane) {
     typedef ChunkCfg<DT, DK, C, NW> G;
-    constexpr int NT = G::NT, LDA = G::LDA, LDC = G::LDC, LDD = G::LDD;
+    constexpr int NT = G::NT, LDA = G::LDA, LDT = G::LDT, LDD = G::LDD;
     const int g = lane >> 4, r = lane & 15;
     const int d = lane >> 4, cc = lane & 15;
-    float x[16];
+    typename Frag<DT>::k16 xq[4];  // x as four quads, narrowed to DT
     if (lane < C) {
+        // Lane (d, cc) holds row cc of the diagonal block A_dd and solves for
+        // column cc of its inverse; A_dd[i][j] comes from lane i of the same
+        // 16-lane row through DPP, so the dependent chain has no LDS reads.
+        float a[16];
+        const float *arow = Af + (16 * d + cc) * LDA + 16 * d;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float s = (i == cc) ? 1.f : 0.f;
-            const float *arow = Af + (16 * d + i) * LDA + 16 * d;
-#pragma unroll
-            for (int j = 0; j < i; ++j) s -= arow[j] * x[j];
-            x[i] = s;
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 t = *reinterpret_cast<const float4 *>(arow + 4 * q4);
+            a[4 * q4] = t.x; a[4 * q4 + 1] = t.y; a[4 * q4 + 2] = t.z; a[4 * q4 + 3] = t.w;
         }
+        // Right-looking order: once x_j is final, the updates of all later
+        // partial sums are independent, so the dependent chain is one update
+        // per row rather than one per matrix entry.
+        float x[16], s[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            x[j] = ((j == cc) ? 1.f : 0.f) - s[j];
+#pragma unroll
+            for (int i = j + 1; i < 16; ++i) s[i] += row_bcast_at(a[j], i) * x[j];
+        }
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) frag_set(xq[q4], e, x[4 * q4 + e]);
         DT *drow = Dw + (16 * d + cc) * LDD;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) drow[i] = from_f32<DT>(x[i]);
+        for (int q4 = 0; q4 < 4; ++q4) store_frag16(drow + 4 * q4, xq[q4]);
     }
     wave_lds_fence();
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
         if (j % NW != wave) continue;
-        // diagonal block j: lanes of block j hold its columns
+        // diagonal block j: its lanes hold the rows of Ti_jj^T
         if (d == j) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                Ts[(16 * j + i) * LDC + 16 * j + cc] = from_f32<DT>(x[i]);
+            for (int q4 = 0; q4 < 4; ++q4)
+                store_frag16(TsT + (16 * j + cc) * LDT + 16 * j + 4 * q4, xq[q4]);
+        }
+        // all operands that do not depend on results of this block column
+        typename Frag<DT>::k16 fA[NT][NT], fTii[NT], fTjj;
+#pragma unroll
+        for (int i = j + 1; i < NT; ++i) {
+#pragma unroll
+            for (int kb = j; kb < i; ++kb) {
+                float a4[4];
+                load4(Af + (16 * i + r) * LDA + 16 * kb + 4 * g, a4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) frag_set(fA[i][kb], e, a4[e]);
+            }
+            // A = Ti_ii: lane (g, r) takes Ti_ii[r][4g + e] = Dw[16i + 4g + e][r]
+            frag_cols16(Dw, LDD, 16 * i, 0, lane, fTii[i]);
+        }
+        {
+            // B = Ti_jj: lane (g, r) takes Ti_jj[4g + e][r] = Dw row 16j + r
+            float b4[4];
+            load4(Dw + (16 * j + r) * LDD + 4 * g, b4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) frag_set(fTjj, e, b4[e]);
         }
         f32x4 Tcol[NT];
 #pragma unroll
@@ -214,79 +233,147 @@ __device__ __forceinline__ void tri_inverse(const float *Af, DT *Ts, DT *Dw, int
             f32x4 acc = zero4();
 #pragma unroll
             for (int kb = j; kb < i; ++kb) {
-                typename Frag<DT>::k16 fa, fb;
-                float a4[4];
-                load4(Af + (16 * i + r) * LDA + 16 * kb + 4 * g, a4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) frag_set(fa, e, a4[e]);
-                if (kb == j) {
-                    // B = Ti_jj: lane (g, r) takes Ti_jj[4g + e][r] = Dw row 16j + r
-                    float b4[4];
-                    load4(Dw + (16 * j + r) * LDD + 4 * g, b4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) frag_set(fb, e, b4[e]);
-                } else {
-                    frag_from_acc16(Tcol[kb], fb);
-                }
-                mma_k16(acc, fa, fb);
+                typename Frag<DT>::k16 fb;
+                if (kb == j) fb = fTjj;
+                else frag_from_acc16(Tcol[kb], fb);
+                mma_k16(acc, fA[i][kb], fb);
             }
-            // A = Ti_ii: lane (g, r) takes Ti_ii[r][4g + e] = Dw[16i + 4g + e][r]
-            typename Frag<DT>::k16 fa, fb;
-            frag_cols16(Dw, LDD, 16 * i, 0, lane, fa);
+            typename Frag<DT>::k16 fb;
             frag_from_acc16(acc, fb);
             f32x4 res = zero4();
-            mma_k16(res, fa, fb);
+            mma_k16(res, fTii[i], fb);
+            // lane (g, r) holds Ti[16i + 4g + e][16j + r] = TsT[16j + r][16i + 4g + e]
+            typename Frag<DT>::k16 out;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 Tcol[i][e] = -res[e];
-                Ts[(16 * i + 4 * g + e) * LDC + 16 * j + r] = from_f32<DT>(-res[e]);
+                frag_set(out, e, -res[e]);
             }
+            store_frag16(TsT + (16 * j + r) * LDT + 16 * i + 4 * g, out);
         }
     }
 }
 
 // State path of one chunk for this wave's 16 rows of S:
 //   X = K S^T, Y = Q S^T, R = diag(beta)(V - X), E = Ti R,
-//   O = Y + P E (stored for tokens < len), S^T += K^T E.
+//   S^T += K^T E, O = Y + P E (stored for tokens < len).
+// Operand fragments are loaded into registers ahead of their MFMAs: the Ti
+// and P rows first (they do not depend on the state), the K and Q slabs of
+// X and Y one slab ahead, the K^T fragments while X and Y run.
 template <typename DT, int DK, int C, int NW>
-__device__ __forceinline__ void state_path(const DT *Ks, const DT *Qs, const DT *Ts,
-                                           const DT *Ps, const float *betas,
-                                           const float (&vcur)[C / 16][4], f32x4 *Sacc,
-                                           DT *oh, int64_t tsv, int t0, int len, int lane) {
+__device__ __forceinline__ void state_path(const DT *Ks, const DT *Qs, const DT *Vs,
+                                           const DT *TsT, const DT *Ps, const float *betas,
+                                           f32x4 *Sacc, DT *oh, int64_t tsv, int t0, int len,
+                                           int wave, int lane) {
     typedef ChunkCfg<DT, DK, C, NW> G;
-    constexpr int NT = G::NT, ND = G::ND;
+    constexpr int NT = G::NT, ND = G::ND, KSD = G::KSD, KSC = G::KSC;
+    constexpr int NSD = DK / KSD, NSC = C / KSC;
+    typedef typename SlabFrag<KSD == 32, DT>::type FD;
+    typedef typename SlabFrag<KSC == 32, DT>::type FC;
     const int g = lane >> 4;
+
+    FC fT[NT][NSC], fP[NT][NSC];
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+        for (int s = 0; s < NSC; ++s)
+            if (s * KSC < 16 * (mt + 1)) {  // Ti and P are lower-triangular
+                // Ti row fragment = column fragment of Ti^T
+                if constexpr (KSC == 32) frag_cols32(TsT, G::LDT, s * KSC, 16 * mt, lane, fT[mt][s]);
+                else frag_cols16(TsT, G::LDT, s * KSC, 16 * mt, lane, fT[mt][s]);
+                frag_rows(Ps, G::LDP, 16 * mt, s * KSC, lane, fP[mt][s]);
+            }
+    float bcur[NT][4];
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bcur[mt][i] = betas[16 * mt + 4 * g + i];
+    // this wave's V columns in D layout: lane (g, r) takes V[16mt + 4g + j][16w + r]
+    typename Frag<DT>::k16 fv[NT];
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt) frag_cols16(Vs, G::LDV, 16 * mt, 16 * wave, lane, fv[mt]);
+
+    // X = K S^T, Y = Q S^T
     f32x4 X[NT], Y[NT];
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt) X[mt] = Y[mt] = zero4();
+    FD fk[2][NT], fq[2][NT];
 #pragma unroll
-    for (int k0 = 0; k0 < DK; k0 += G::KSD)
+    for (int mt = 0; mt < NT; ++mt) {
+        frag_rows(Ks, G::LDK, 16 * mt, 0, lane, fk[0][mt]);
+        frag_rows(Qs, G::LDK, 16 * mt, 0, lane, fq[0][mt]);
+    }
+#pragma unroll
+    for (int s = 0; s < NSD; ++s) {
+        const int cur = s & 1;
+        if (s + 1 < NSD) {
+#pragma unroll
+            for (int mt = 0; mt < NT; ++mt) {
+                frag_rows(Ks, G::LDK, 16 * mt, (s + 1) * KSD, lane, fk[cur ^ 1][mt]);
+                frag_rows(Qs, G::LDK, 16 * mt, (s + 1) * KSD, lane, fq[cur ^ 1][mt]);
+            }
+        }
+        FD fb;
+        if constexpr (KSD == 32) frag_from_acc32(Sacc[2 * s], Sacc[2 * s + 1], fb);
+        else frag_from_acc16(Sacc[s], fb);
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt) {
-            mma_rows_acc<DT, G::KSD>(X[mt], Ks, G::LDK, 16 * mt, k0, lane, Sacc);
-            mma_rows_acc<DT, G::KSD>(Y[mt], Qs, G::LDK, 16 * mt, k0, lane, Sacc);
+            if constexpr (KSD == 32) {
+                mma_k32(X[mt], fk[cur][mt], fb);
+                mma_k32(Y[mt], fq[cur][mt], fb);
+            } else {
+                mma_k16(X[mt], fk[cur][mt], fb);
+                mma_k16(Y[mt], fq[cur][mt], fb);
+            }
+        }
+    }
+    // K^T fragments for the state update (read through the transpose path)
+    FC fkt[ND][NSC];
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int s = 0; s < NSC; ++s) {
+            if constexpr (KSC == 32) frag_cols32(Ks, G::LDK, s * KSC, 16 * dt, lane, fkt[dt][s]);
+            else frag_cols16(Ks, G::LDK, s * KSC, 16 * dt, lane, fkt[dt][s]);
         }
     // R = diag(beta) (V - K S^T), in place in X
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            X[mt][i] = betas[16 * mt + 4 * g + i] * (vcur[mt][i] - X[mt][i]);
-    // E = Ti R  (Ti lower-triangular: slabs past the diagonal are zero)
+        for (int i = 0; i < 4; ++i) X[mt][i] = bcur[mt][i] * (frag_get(fv[mt], i) - X[mt][i]);
+    // E = Ti R  (slabs past the diagonal are zero and skipped)
     f32x4 E[NT];
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt) {
         E[mt] = zero4();
 #pragma unroll
-        for (int k0 = 0; k0 < 16 * (mt + 1); k0 += G::KSC)
-            mma_rows_acc<DT, G::KSC>(E[mt], Ts, G::LDC, 16 * mt, k0, lane, X);
+        for (int s = 0; s < NSC; ++s)
+            if (s * KSC < 16 * (mt + 1)) {
+                FC fb;
+                if constexpr (KSC == 32) {
+                    frag_from_acc32(X[2 * s], X[2 * s + 1], fb);
+                    mma_k32(E[mt], fT[mt][s], fb);
+                } else {
+                    frag_from_acc16(X[s], fb);
+                    mma_k16(E[mt], fT[mt][s], fb);
+                }
+            }
     }
-    // S^T += K^T E  (K^T read through the transpose path of the K tile)
+    // B operands built from E, shared by the state update and the output
+    FC fe[NSC];
+#pragma unroll
+    for (int s = 0; s < NSC; ++s) {
+        if constexpr (KSC == 32) frag_from_acc32(E[2 * s], E[2 * s + 1], fe[s]);
+        else frag_from_acc16(E[s], fe[s]);
+    }
+    // S^T += K^T E
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-        for (int k0 = 0; k0 < C; k0 += G::KSC)
-            mma_cols_acc<DT, G::KSC>(Sacc[dt], Ks, G::LDK, 16 * dt, k0, lane, E);
+        for (int s = 0; s < NSC; ++s) {
+            if constexpr (KSC == 32) mma_k32(Sacc[dt], fkt[dt][s], fe[s]);
+            else mma_k16(Sacc[dt], fkt[dt][s], fe[s]);
+        }
     // O = Q S^T + P E.  P E gets its own accumulator: Y comes from slabs
     // over d_k and P E from slabs over tokens, which can be different MFMA
     // shapes, and an accumulation chain must never switch shape (the compiler
@@ -296,12 +383,21 @@ __device__ __forceinline__ void state_path(const DT *Ks, const DT *Qs, const DT 
     for (int mt = 0; mt < NT; ++mt) {
         f32x4 PE = zero4();
 #pragma unroll
-        for (int k0 = 0; k0 < 16 * (mt + 1); k0 += G::KSC)
-            mma_rows_acc<DT, G::KSC>(PE, Ps, G::LDC, 16 * mt, k0, lane, E);
+        for (int s = 0; s < NSC; ++s)
+            if (s * KSC < 16 * (mt + 1)) {
+                if constexpr (KSC == 32) mma_k32(PE, fP[mt][s], fe[s]);
+                else mma_k16(PE, fP[mt][s], fe[s]);
+            }
+        if (len == C) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 16 * mt + 4 * g + i;
-            if (t < len) oh[(t0 + t) * tsv] = from_f32<DT>(Y[mt][i] + PE[i]);
+            for (int i = 0; i < 4; ++i)
+                oh[(t0 + 16 * mt + 4 * g + i) * tsv] = from_f32<DT>(Y[mt][i] + PE[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * mt + 4 * g + i;
+                if (t < len) oh[(t0 + t) * tsv] = from_f32<DT>(Y[mt][i] + PE[i]);
+            }
         }
     }
 }
@@ -334,21 +430,22 @@ __device__ __forceinline__ HeadPtrs<DT> head_ptrs(const DT *q, const DT *k, cons
     p.tsv = (int64_t)H * Dv;
     p.kh = k + ((int64_t)b * T * H + h) * DK;
     p.qh = q + ((int64_t)b * T * H + h) * DK;
-    p.vh = v + ((int64_t)b * T * H + h) * Dv + p.vcol;
+    p.vh = v + ((int64_t)b * T * H + h) * Dv + vt * 16 * NW;
     p.oh = o + ((int64_t)b * T * H + h) * Dv + p.vcol;
     p.bh = beta + (int64_t)b * T * H + h;
     p.sbase = ((int64_t)head * Dv + p.vcol) * DK;
     return p;
 }
 
-// Register staging of one chunk's K, Q and beta.  Loads are unconditional
-// (addresses clamped into the sequence) so that none sits in a branch that
-// would force an early wait; out-of-range tokens are zeroed when staged.
+// Register staging of one chunk's K, Q, V (this workgroup's value columns)
+// and beta.  Loads are unconditional (addresses clamped into the sequence) so
+// that none sits in a branch that would force an early wait; out-of-range
+// tokens are zeroed when staged.
 template <typename DT, int DK, int C, int NW>
-struct KQRegs {
+struct ChunkRegs {
     typedef ChunkCfg<DT, DK, C, NW> G;
     typedef typename Vec16<DT>::type vec_t;
-    vec_t k[G::NPRE], q[G::NPRE];
+    vec_t k[G::NPRE], q[G::NPRE], v[G::NPREV];
     DT b;
 
     __device__ __forceinline__ void load(const HeadPtrs<DT> &p, int T, int H, int t0, int tid) {
@@ -360,10 +457,17 @@ struct KQRegs {
             k[j] = *reinterpret_cast<const vec_t *>(p.kh + (t0 + t) * p.tsk + e0);
             q[j] = *reinterpret_cast<const vec_t *>(p.qh + (t0 + t) * p.tsk + e0);
         }
+#pragma unroll
+        for (int j = 0; j < G::NPREV; ++j) {
+            const int idx = min(tid + j * G::NTHR, C * G::VPRV - 1);
+            const int t = min(idx / G::VPRV, last), e0 = (idx % G::VPRV) * G::VEC;
+            v[j] = *reinterpret_cast<const vec_t *>(p.vh + (t0 + t) * p.tsv + e0);
+        }
         b = p.bh[(int64_t)(t0 + min(tid, last)) * H];
     }
     // Write into one LDS buffer set; tokens >= len become zeros.
-    __device__ __forceinline__ void stage(DT *Ks, DT *Qs, float *betas, int len, int tid) const {
+    __device__ __forceinline__ void stage(DT *Ks, DT *Qs, DT *Vs, float *betas, int len,
+                                          int tid) const {
 #pragma unroll
         for (int j = 0; j < G::NPRE; ++j) {
             const int idx = tid + j * G::NTHR;
@@ -373,29 +477,17 @@ struct KQRegs {
                 *reinterpret_cast<vec_t *>(Qs + t * G::LDK + e0) = (t < len) ? q[j] : vec_t{};
             }
         }
+#pragma unroll
+        for (int j = 0; j < G::NPREV; ++j) {
+            const int idx = tid + j * G::NTHR;
+            if (idx < C * G::VPRV) {
+                const int t = idx / G::VPRV, e0 = (idx % G::VPRV) * G::VEC;
+                *reinterpret_cast<vec_t *>(Vs + t * G::LDV + e0) = (t < len) ? v[j] : vec_t{};
+            }
+        }
         if (tid < C) betas[tid] = (tid < len) ? to_f32(b) : 0.f;
     }
 };
-
-// This lane's values of V for one chunk in D layout (token 16mt + 4g + i).
-template <typename DT, int C>
-__device__ __forceinline__ void load_v(const HeadPtrs<DT> &p, int T, int t0, int g,
-                                       DT (&dst)[C / 16][4]) {
-    const int last = min(C, T - t0) - 1;
-#pragma unroll
-    for (int mt = 0; mt < C / 16; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[mt][i] = p.vh[(t0 + min(16 * mt + 4 * g + i, last)) * p.tsv];
-}
-
-template <typename DT, int C>
-__device__ __forceinline__ void widen_v(const DT (&raw)[C / 16][4], int len, int g,
-                                        float (&dst)[C / 16][4]) {
-#pragma unroll
-    for (int mt = 0; mt < C / 16; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[mt][i] = (16 * mt + 4 * g + i < len) ? to_f32(raw[mt][i]) : 0.f;
-}
 
 // ---------------------------------------------------------------------------
 // Pipelined kernel
@@ -405,8 +497,9 @@ struct PipeSmem {
     typedef ChunkCfg<DT, DK, C, NW> G;
     DT Ks[2][C * G::LDK];          // K, token-major (double-buffered)
     DT Qs[2][C * G::LDK];          // Q, token-major
-    DT Ts[2][C * G::LDC];          // (I + A)^{-1}
-    DT Ps[2][C * G::LDC];          // Q K^T (.) M
+    DT Vs[2][C * G::LDV];          // V, this workgroup's value columns
+    DT TsT[2][C * G::LDT];         // ((I + A)^{-1})^T
+    DT Ps[2][C * G::LDP];          // Q K^T (.) M
     float Af[C * G::LDA];          // A = beta (K K^T) strictly lower, fp32
     float betas[2][C];
     DT Dw[NW][C * G::LDD];         // per-wave diagonal inverses (transposed)
@@ -418,7 +511,7 @@ constexpr bool pipelined_fits() {
 }
 
 template <typename DT, int DK, int C, int NW>
-__global__ __launch_bounds__(64 * NW) void chunk_fwd_pipelined_kernel(
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_fwd_pipelined_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const float *S0, DT *__restrict__ o, float *S_T,
     int T, int H, int Dv, int nvt) {
@@ -431,32 +524,33 @@ __global__ __launch_bounds__(64 * NW) void chunk_fwd_pipelined_kernel(
     const HeadPtrs<DT> p = head_ptrs<DT, DK, NW>(q, k, v, beta, o, T, H, Dv, nvt, wave, r);
 
     f32x4 Sacc[ND];
+    if (S0) {
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
-        Sacc[dt] = S0 ? *reinterpret_cast<const f32x4 *>(S0 + p.sbase + 16 * dt + 4 * g)
-                      : zero4();
+        for (int dt = 0; dt < ND; ++dt)
+            Sacc[dt] = *reinterpret_cast<const f32x4 *>(S0 + p.sbase + 16 * dt + 4 * g);
+    } else {
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) Sacc[dt] = zero4();
+    }
 
     const int N = (T + C - 1) / C;
     if (N > 0) {
-        // Upper blocks of Ts and Ps stay zero for the whole sequence.
-        for (int i = tid; i < 2 * C * G::LDC; i += G::NTHR) {
-            (&sm.Ts[0][0])[i] = from_f32<DT>(0.f);
-            (&sm.Ps[0][0])[i] = from_f32<DT>(0.f);
-        }
-        KQRegs<DT, DK, C, NW> kq;
-        DT vraw[NT][4], vnext[NT][4];
+        // Lower blocks of TsT and upper blocks of Ps stay zero for the whole
+        // sequence.
+        for (int i = tid; i < 2 * C * G::LDT; i += G::NTHR) (&sm.TsT[0][0])[i] = from_f32<DT>(0.f);
+        for (int i = tid; i < 2 * C * G::LDP; i += G::NTHR) (&sm.Ps[0][0])[i] = from_f32<DT>(0.f);
+        ChunkRegs<DT, DK, C, NW> rg;
         // prologue: chunks 0 and 1 staged, chunk 0 solved, chunk 2 in flight
-        kq.load(p, T, H, 0, tid);
-        load_v<DT, C>(p, T, 0, g, vraw);
-        kq.stage(sm.Ks[0], sm.Qs[0], sm.betas[0], min(C, T), tid);
+        rg.load(p, T, H, 0, tid);
+        rg.stage(sm.Ks[0], sm.Qs[0], sm.Vs[0], sm.betas[0], min(C, T), tid);
         const int c1 = min(1, N - 1);
-        kq.load(p, T, H, c1 * C, tid);
-        kq.stage(sm.Ks[1], sm.Qs[1], sm.betas[1], min(C, T - c1 * C), tid);
-        kq.load(p, T, H, min(2, N - 1) * C, tid);
+        rg.load(p, T, H, c1 * C, tid);
+        rg.stage(sm.Ks[1], sm.Qs[1], sm.Vs[1], sm.betas[1], min(C, T - c1 * C), tid);
+        rg.load(p, T, H, min(2, N - 1) * C, tid);
         lds_barrier();
         gram_tiles<DT, DK, C, NW>(sm.Ks[0], sm.Qs[0], sm.betas[0], sm.Af, sm.Ps[0], wave, lane);
         lds_barrier();
-        tri_inverse<DT, DK, C, NW>(sm.Af, sm.Ts[0], sm.Dw[wave], wave, lane);
+        tri_inverse<DT, DK, C, NW>(sm.Af, sm.TsT[0], sm.Dw[wave], wave, lane);
         lds_barrier();
 
         for (int c = 0; c < N; ++c) {
@@ -464,24 +558,17 @@ __global__ __launch_bounds__(64 * NW) void chunk_fwd_pipelined_kernel(
             const int t0 = c * C;
             const int len = min(C, T - t0);
             // ---- phase 1: state path of chunk c, Gram tiles of chunk c+1 ----
-            load_v<DT, C>(p, T, min(c + 1, N - 1) * C, g, vnext);
-            float vcur[NT][4];
-            widen_v<DT, C>(vraw, len, g, vcur);
-            state_path<DT, DK, C, NW>(sm.Ks[b], sm.Qs[b], sm.Ts[b], sm.Ps[b], sm.betas[b],
-                                      vcur, Sacc, p.oh, p.tsv, t0, len, lane);
+            state_path<DT, DK, C, NW>(sm.Ks[b], sm.Qs[b], sm.Vs[b], sm.TsT[b], sm.Ps[b],
+                                      sm.betas[b], Sacc, p.oh, p.tsv, t0, len, wave, lane);
             // (past the last chunk this works on stale buffers; never read)
             gram_tiles<DT, DK, C, NW>(sm.Ks[b1], sm.Qs[b1], sm.betas[b1], sm.Af, sm.Ps[b1],
                                       wave, lane);
             lds_barrier();
             // ---- phase 2: inverse of chunk c+1, staging of chunk c+2 ----
-            tri_inverse<DT, DK, C, NW>(sm.Af, sm.Ts[b1], sm.Dw[wave], wave, lane);
+            tri_inverse<DT, DK, C, NW>(sm.Af, sm.TsT[b1], sm.Dw[wave], wave, lane);
             const int c2 = min(c + 2, N - 1);
-            kq.stage(sm.Ks[b], sm.Qs[b], sm.betas[b], min(C, T - c2 * C), tid);
-            kq.load(p, T, H, min(c + 3, N - 1) * C, tid);
-#pragma unroll
-            for (int mt = 0; mt < NT; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) vraw[mt][i] = vnext[mt][i];
+            rg.stage(sm.Ks[b], sm.Qs[b], sm.Vs[b], sm.betas[b], min(C, T - c2 * C), tid);
+            rg.load(p, T, H, min(c + 3, N - 1) * C, tid);
             lds_barrier();
         }
     }
@@ -500,15 +587,16 @@ struct SerialSmem {
     typedef ChunkCfg<DT, DK, C, NW> G;
     DT Ks[C * G::LDK];
     DT Qs[C * G::LDK];
-    DT Ts[C * G::LDC];
-    DT Ps[C * G::LDC];
+    DT Vs[C * G::LDV];
+    DT TsT[C * G::LDT];
+    DT Ps[C * G::LDP];
     float Af[C * G::LDA];
     float betas[C];
     DT Dw[NW][C * G::LDD];
 };
 
 template <typename DT, int DK, int C, int NW>
-__global__ __launch_bounds__(64 * NW) void chunk_fwd_serial_kernel(
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_fwd_serial_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const float *S0, DT *__restrict__ o, float *S_T,
     int T, int H, int Dv, int nvt) {
@@ -521,37 +609,34 @@ __global__ __launch_bounds__(64 * NW) void chunk_fwd_serial_kernel(
     const HeadPtrs<DT> p = head_ptrs<DT, DK, NW>(q, k, v, beta, o, T, H, Dv, nvt, wave, r);
 
     f32x4 Sacc[ND];
+    if (S0) {
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
-        Sacc[dt] = S0 ? *reinterpret_cast<const f32x4 *>(S0 + p.sbase + 16 * dt + 4 * g)
-                      : zero4();
+        for (int dt = 0; dt < ND; ++dt)
+            Sacc[dt] = *reinterpret_cast<const f32x4 *>(S0 + p.sbase + 16 * dt + 4 * g);
+    } else {
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) Sacc[dt] = zero4();
+    }
 
     const int N = (T + C - 1) / C;
     if (N > 0) {
-        for (int i = tid; i < C * G::LDC; i += G::NTHR) {
-            sm.Ts[i] = from_f32<DT>(0.f);
-            sm.Ps[i] = from_f32<DT>(0.f);
-        }
-        KQRegs<DT, DK, C, NW> kq;
-        DT vraw[NT][4];
-        kq.load(p, T, H, 0, tid);
-        load_v<DT, C>(p, T, 0, g, vraw);
+        for (int i = tid; i < C * G::LDT; i += G::NTHR) sm.TsT[i] = from_f32<DT>(0.f);
+        for (int i = tid; i < C * G::LDP; i += G::NTHR) sm.Ps[i] = from_f32<DT>(0.f);
+        ChunkRegs<DT, DK, C, NW> rg;
+        rg.load(p, T, H, 0, tid);
         for (int c = 0; c < N; ++c) {
             const int t0 = c * C;
             const int len = min(C, T - t0);
             lds_barrier();
-            kq.stage(sm.Ks, sm.Qs, sm.betas, len, tid);
-            float vcur[NT][4];
-            widen_v<DT, C>(vraw, len, g, vcur);
+            rg.stage(sm.Ks, sm.Qs, sm.Vs, sm.betas, len, tid);
             lds_barrier();
-            kq.load(p, T, H, min(c + 1, N - 1) * C, tid);
-            load_v<DT, C>(p, T, min(c + 1, N - 1) * C, g, vraw);
+            rg.load(p, T, H, min(c + 1, N - 1) * C, tid);
             gram_tiles<DT, DK, C, NW>(sm.Ks, sm.Qs, sm.betas, sm.Af, sm.Ps, wave, lane);
             lds_barrier();
-            tri_inverse<DT, DK, C, NW>(sm.Af, sm.Ts, sm.Dw[wave], wave, lane);
+            tri_inverse<DT, DK, C, NW>(sm.Af, sm.TsT, sm.Dw[wave], wave, lane);
             lds_barrier();
-            state_path<DT, DK, C, NW>(sm.Ks, sm.Qs, sm.Ts, sm.Ps, sm.betas, vcur, Sacc, p.oh,
-                                      p.tsv, t0, len, lane);
+            state_path<DT, DK, C, NW>(sm.Ks, sm.Qs, sm.Vs, sm.TsT, sm.Ps, sm.betas, Sacc, p.oh,
+                                      p.tsv, t0, len, wave, lane);
         }
     }
     if (S_T) {

@@ -57,6 +57,8 @@ __device__ __forceinline__ void frag_set(bf16x8 &f, int i, float x) { f[i] = (__
 __device__ __forceinline__ void frag_set(bf16x4 &f, int i, float x) { f[i] = (__bf16)x; }
 __device__ __forceinline__ void frag_set(f32x8_arr &f, int i, float x) { f.v[i] = x; }
 __device__ __forceinline__ void frag_set(f32x4_arr &f, int i, float x) { f.v[i] = x; }
+__device__ __forceinline__ float frag_get(const bf16x4 &f, int i) { return (float)f[i]; }
+__device__ __forceinline__ float frag_get(const f32x4_arr &f, int i) { return f.v[i]; }
 
 // acc += A * B over one 32-wide k slab.
 __device__ __forceinline__ void mma_k32(f32x4 &acc, const bf16x8 &a, const bf16x8 &b) {
@@ -162,6 +164,14 @@ __device__ __forceinline__ void frag_cols32(const float *M, int ld, int k0, int 
     }
 }
 
+// Store a 4-element fragment to 4 consecutive elements (8 or 16 bytes).
+__device__ __forceinline__ void store_frag16(__bf16 *p, const bf16x4 &f) {
+    *reinterpret_cast<bf16x4 *>(p) = f;
+}
+__device__ __forceinline__ void store_frag16(float *p, const f32x4_arr &f) {
+    *reinterpret_cast<float4 *>(p) = make_float4(f.v[0], f.v[1], f.v[2], f.v[3]);
+}
+
 // B operand from a stack of D-layout accumulator tiles whose rows run along
 // k: tile k0/16 (and k0/16 + 1 for a 32-wide slab), narrowed to DT.
 template <typename F>
@@ -187,6 +197,33 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // memory accesses across it.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Value of x in lane N of this lane's 16-lane row (DPP row_newbcast).
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + N, 0xf, 0xf, true));
+}
+// Same with N known only after unrolling.
+__device__ __forceinline__ float row_bcast_at(float x, int n) {
+    switch (n) {
+    case 0: return row_bcast<0>(x);
+    case 1: return row_bcast<1>(x);
+    case 2: return row_bcast<2>(x);
+    case 3: return row_bcast<3>(x);
+    case 4: return row_bcast<4>(x);
+    case 5: return row_bcast<5>(x);
+    case 6: return row_bcast<6>(x);
+    case 7: return row_bcast<7>(x);
+    case 8: return row_bcast<8>(x);
+    case 9: return row_bcast<9>(x);
+    case 10: return row_bcast<10>(x);
+    case 11: return row_bcast<11>(x);
+    case 12: return row_bcast<12>(x);
+    case 13: return row_bcast<13>(x);
+    case 14: return row_bcast<14>(x);
+    default: return row_bcast<15>(x);
+    }
 }
 
 // Orders this wave's LDS writes before its later LDS reads of data written by
