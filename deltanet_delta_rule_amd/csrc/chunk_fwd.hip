@@ -64,13 +64,18 @@ struct ChunkCfg {
     static constexpr int KSD = (DK % 32 == 0) ? 32 : 16;  // slab over d_k
     static constexpr int KSC = (C % 32 == 0) ? 32 : 16;   // slab over tokens
     static constexpr int PADE = 16 / (int)sizeof(DT);     // 16 bytes per row
-    // Row strides.  Row-fragment reads (lane r reads row r) are free of LDS
-    // bank conflicts when the stride is 4*odd dwords; transpose reads (a lane
-    // group reads 4 rows x 32 bytes) when it is 8*odd dwords.
-    static constexpr int LDK = DK + PADE;       // K, Q (row fragments)
-    static constexpr int LDP = C + PADE;        // P (row fragments)
+    // LDS has 64 banks of 4 bytes.  A 16-byte read serves 16 lanes per pass
+    // (lanes 0-7 with 24-31, 8-15 with 16-23, and likewise in the upper
+    // half), an 8-byte read or transpose read 32 lanes per pass.  Strides of
+    // 8*odd dwords make both the 16-byte row-fragment reads (lane r reads row
+    // r) and the transpose reads (a 16-lane group reads 4 rows x 32 bytes)
+    // conflict-free.  The bf16 K and Q tiles are unpadded and swizzled
+    // instead (kq_off).
+    static constexpr bool SWZ = sizeof(DT) == 2 && DK >= 32;
+    static constexpr int LDK = SWZ ? DK : DK + PADE;   // K, Q
+    static constexpr int LDP = C + 2 * PADE;    // P (row fragments)
     static constexpr int LDT = C + 2 * PADE;    // Ti^T (transpose reads)
-    static constexpr int LDA = C + 4;           // A (fp32)
+    static constexpr int LDA = C + 8;           // A (fp32)
     static constexpr int LDD = 16 + PADE;       // diagonal-inverse scratch
     static constexpr int VEC = Vec16<DT>::N;    // elements per 16-byte load
     static constexpr int VPR = DK / VEC;        // 16-byte vectors per K row
@@ -82,9 +87,89 @@ struct ChunkCfg {
     static constexpr int NPREV = (C * VPRV + NTHR - 1) / NTHR;  // V vectors/thread
 };
 
+// Row swizzle of the bf16 K and Q tiles: 16-byte chunk c of row t is stored
+// at chunk c ^ kq_swz(t).  The masks make each pass of the three access
+// patterns of these tiles -- chunk-order row fragments, the transpose reads of
+// the state update (state_col order) and the 16-byte staging writes -- touch
+// every bank once.
+template <int NCH>
+__device__ __forceinline__ int kq_swz(int t) {
+    const int b0 = t & 1, b1 = (t >> 1) & 1, b2 = (t >> 2) & 1, b3 = (t >> 3) & 1;
+    if constexpr (NCH == 16) return b0 | (b1 << 2) | (b2 << 3) | (b3 << 1);
+    else if constexpr (NCH == 8) return b1 | (b2 << 2) | (b3 << 1);
+    else if constexpr (NCH == 4) return b2 | (b3 << 1);
+    else return 0;
+}
+
+// Element offset of K[t][e] (or Q[t][e]) in a chunk tile.
+template <typename DT, int DK, int C, int NW>
+__device__ __forceinline__ int kq_off(int t, int e) {
+    typedef ChunkCfg<DT, DK, C, NW> G;
+    if constexpr (G::SWZ) return t * G::LDK + (((e >> 3) ^ kq_swz<DK / 8>(t)) << 3) + (e & 7);
+    else return t * G::LDK + e;
+}
+
+// Column of token u in the P tile.  P rows are read in the canonical k order
+// over tokens (u = 32s + 4g + j and 32s + 16 + 4g + j for lane group g), so
+// those eight columns are stored next to each other: one 16-byte read.
+template <int KSC>
+__device__ __forceinline__ int p_col(int u) {
+    if constexpr (KSC == 32) return 32 * (u >> 5) + 8 * ((u >> 2) & 3) + 4 * ((u >> 4) & 1) + (u & 3);
+    else return u;
+}
+
 template <bool K32, typename DT> struct SlabFrag;
 template <typename DT> struct SlabFrag<true, DT> { typedef typename Frag<DT>::k32 type; };
 template <typename DT> struct SlabFrag<false, DT> { typedef typename Frag<DT>::k16 type; };
+
+// Row fragment of a K or Q tile over d_k in chunk order (16-byte reads).
+template <typename DT, int DK, int C, int NW, typename F>
+__device__ __forceinline__ void kq_rows(const DT *M, int row0, int k0, int lane, F &f) {
+    typedef ChunkCfg<DT, DK, C, NW> G;
+    const int g = lane >> 4, r = lane & 15;
+    load_chunk(M + kq_off<DT, DK, C, NW>(row0 + r, k0 + (G::KSD == 32 ? 8 : 4) * g), f);
+}
+
+// Row fragment of the P tile in canonical token order (see p_col).
+template <typename DT, int DK, int C, int NW, typename F>
+__device__ __forceinline__ void p_rows(const DT *Ps, int row0, int k0, int lane, F &f) {
+    typedef ChunkCfg<DT, DK, C, NW> G;
+    const int g = lane >> 4, r = lane & 15;
+    load_chunk(Ps + (row0 + r) * G::LDP + k0 + (G::KSC == 32 ? 8 : 4) * g, f);
+}
+
+// K^T fragment for state tile dt over the 16 tokens k0 .. k0 + 15: lane
+// (g, r) takes K[k0 + 4g + j][state_col(dt, r / 4) + r % 4], j = 0..3.  For
+// bf16 this is one transpose read: lane (g, r) fetches the 4 keys at
+// state_col(dt, r % 4) of token k0 + 4g + r / 4, and the hardware hands lane
+// r element r % 4 of lanes r / 4, 4 + r / 4, 8 + r / 4, 12 + r / 4.
+template <typename DT, int DK, int C, int NW>
+__device__ __forceinline__ void kt_frag16(const __bf16 *Ks, int k0, int dt, int lane, bf16x4 &f) {
+    typedef ChunkCfg<DT, DK, C, NW> G;
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const int g = lane >> 4, r = lane & 15;
+    const __bf16 *p = Ks + kq_off<DT, DK, C, NW>(k0 + 4 * g + (r >> 2), state_col<G::KSD>(dt, r & 3));
+    f = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p));
+}
+template <typename DT, int DK, int C, int NW>
+__device__ __forceinline__ void kt_frag16(const float *Ks, int k0, int dt, int lane, f32x4_arr &f) {
+    typedef ChunkCfg<DT, DK, C, NW> G;
+    const int g = lane >> 4, r = lane & 15;
+    const int col = state_col<G::KSD>(dt, r >> 2) + (r & 3);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.v[j] = Ks[kq_off<DT, DK, C, NW>(k0 + 4 * g + j, col)];
+}
+template <typename DT, int DK, int C, int NW, typename F8>
+__device__ __forceinline__ void kt_frag32(const DT *Ks, int k0, int dt, int lane, F8 &f) {
+    typename Frag<DT>::k16 lo, hi;
+    kt_frag16<DT, DK, C, NW>(Ks, k0, dt, lane, lo);
+    kt_frag16<DT, DK, C, NW>(Ks, k0 + 16, dt, lane, hi);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        frag_set(f, j, frag_get(lo, j));
+        frag_set(f, 4 + j, frag_get(hi, j));
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Per-chunk building blocks shared by both kernels.
@@ -114,12 +199,12 @@ __device__ __forceinline__ void gram_tiles(const DT *Ks, const DT *Qs, const flo
             if (owner != wave) continue;
             FD fx[NSD], fk[NT][NSD];
 #pragma unroll
-            for (int s = 0; s < NSD; ++s) frag_rows(isP ? Qs : Ks, G::LDK, 16 * ti, s * KSD, lane, fx[s]);
+            for (int s = 0; s < NSD; ++s) kq_rows<DT, DK, C, NW>(isP ? Qs : Ks, 16 * ti, s * KSD, lane, fx[s]);
 #pragma unroll
             for (int tj = 0; tj <= ti; ++tj)
 #pragma unroll
                 for (int s = 0; s < NSD; ++s)
-                    frag_rows(Ks, G::LDK, 16 * tj, s * KSD, lane, fk[tj][s]);
+                    kq_rows<DT, DK, C, NW>(Ks, 16 * tj, s * KSD, lane, fk[tj][s]);
             const int row = 16 * ti + r;
             const float brow = betas[row];
 #pragma unroll
@@ -135,7 +220,7 @@ __device__ __forceinline__ void gram_tiles(const DT *Ks, const DT *Qs, const flo
                     typename Frag<DT>::k16 out;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) frag_set(out, e, row >= col + e ? acc[e] : 0.f);
-                    store_frag16(Ps + row * G::LDP + col, out);
+                    store_frag16(Ps + row * G::LDP + p_col<G::KSC>(col), out);
                 } else {
                     f32x4 out;
 #pragma unroll
@@ -281,7 +366,7 @@ __device__ __forceinline__ void state_path(const DT *Ks, const DT *Qs, const DT 
                 // Ti row fragment = column fragment of Ti^T
                 if constexpr (KSC == 32) frag_cols32(TsT, G::LDT, s * KSC, 16 * mt, lane, fT[mt][s]);
                 else frag_cols16(TsT, G::LDT, s * KSC, 16 * mt, lane, fT[mt][s]);
-                frag_rows(Ps, G::LDP, 16 * mt, s * KSC, lane, fP[mt][s]);
+                p_rows<DT, DK, C, NW>(Ps, 16 * mt, s * KSC, lane, fP[mt][s]);
             }
     float bcur[NT][4];
 #pragma unroll
@@ -300,8 +385,8 @@ __device__ __forceinline__ void state_path(const DT *Ks, const DT *Qs, const DT 
     FD fk[2][NT], fq[2][NT];
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt) {
-        frag_rows(Ks, G::LDK, 16 * mt, 0, lane, fk[0][mt]);
-        frag_rows(Qs, G::LDK, 16 * mt, 0, lane, fq[0][mt]);
+        kq_rows<DT, DK, C, NW>(Ks, 16 * mt, 0, lane, fk[0][mt]);
+        kq_rows<DT, DK, C, NW>(Qs, 16 * mt, 0, lane, fq[0][mt]);
     }
 #pragma unroll
     for (int s = 0; s < NSD; ++s) {
@@ -309,12 +394,12 @@ __device__ __forceinline__ void state_path(const DT *Ks, const DT *Qs, const DT 
         if (s + 1 < NSD) {
 #pragma unroll
             for (int mt = 0; mt < NT; ++mt) {
-                frag_rows(Ks, G::LDK, 16 * mt, (s + 1) * KSD, lane, fk[cur ^ 1][mt]);
-                frag_rows(Qs, G::LDK, 16 * mt, (s + 1) * KSD, lane, fq[cur ^ 1][mt]);
+                kq_rows<DT, DK, C, NW>(Ks, 16 * mt, (s + 1) * KSD, lane, fk[cur ^ 1][mt]);
+                kq_rows<DT, DK, C, NW>(Qs, 16 * mt, (s + 1) * KSD, lane, fq[cur ^ 1][mt]);
             }
         }
         FD fb;
-        if constexpr (KSD == 32) frag_from_acc32(Sacc[2 * s], Sacc[2 * s + 1], fb);
+        if constexpr (KSD == 32) frag_from_state(Sacc[2 * s], Sacc[2 * s + 1], g, fb);
         else frag_from_acc16(Sacc[s], fb);
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt) {
@@ -333,8 +418,8 @@ __device__ __forceinline__ void state_path(const DT *Ks, const DT *Qs, const DT 
     for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
         for (int s = 0; s < NSC; ++s) {
-            if constexpr (KSC == 32) frag_cols32(Ks, G::LDK, s * KSC, 16 * dt, lane, fkt[dt][s]);
-            else frag_cols16(Ks, G::LDK, s * KSC, 16 * dt, lane, fkt[dt][s]);
+            if constexpr (KSC == 32) kt_frag32<DT, DK, C, NW>(Ks, s * KSC, dt, lane, fkt[dt][s]);
+            else kt_frag16<DT, DK, C, NW>(Ks, s * KSC, dt, lane, fkt[dt][s]);
         }
     // R = diag(beta) (V - K S^T), in place in X
 #pragma unroll
@@ -473,8 +558,9 @@ struct ChunkRegs {
             const int idx = tid + j * G::NTHR;
             if (idx < C * G::VPR) {
                 const int t = idx / G::VPR, e0 = (idx % G::VPR) * G::VEC;
-                *reinterpret_cast<vec_t *>(Ks + t * G::LDK + e0) = (t < len) ? k[j] : vec_t{};
-                *reinterpret_cast<vec_t *>(Qs + t * G::LDK + e0) = (t < len) ? q[j] : vec_t{};
+                const int off = kq_off<DT, DK, C, NW>(t, e0);
+                *reinterpret_cast<vec_t *>(Ks + off) = (t < len) ? k[j] : vec_t{};
+                *reinterpret_cast<vec_t *>(Qs + off) = (t < len) ? q[j] : vec_t{};
             }
         }
 #pragma unroll
@@ -527,7 +613,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     if (S0) {
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt)
-            Sacc[dt] = *reinterpret_cast<const f32x4 *>(S0 + p.sbase + 16 * dt + 4 * g);
+            Sacc[dt] = *reinterpret_cast<const f32x4 *>(S0 + p.sbase + state_col<G::KSD>(dt, g));
     } else {
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) Sacc[dt] = zero4();
@@ -575,7 +661,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     if (S_T) {
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt)
-            *reinterpret_cast<f32x4 *>(S_T + p.sbase + 16 * dt + 4 * g) = Sacc[dt];
+            *reinterpret_cast<f32x4 *>(S_T + p.sbase + state_col<G::KSD>(dt, g)) = Sacc[dt];
     }
 }
 
@@ -612,7 +698,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     if (S0) {
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt)
-            Sacc[dt] = *reinterpret_cast<const f32x4 *>(S0 + p.sbase + 16 * dt + 4 * g);
+            Sacc[dt] = *reinterpret_cast<const f32x4 *>(S0 + p.sbase + state_col<G::KSD>(dt, g));
     } else {
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) Sacc[dt] = zero4();
@@ -642,7 +728,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     if (S_T) {
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt)
-            *reinterpret_cast<f32x4 *>(S_T + p.sbase + 16 * dt + 4 * g) = Sacc[dt];
+            *reinterpret_cast<f32x4 *>(S_T + p.sbase + state_col<G::KSD>(dt, g)) = Sacc[dt];
     }
 }
 

@@ -164,6 +164,54 @@ __device__ __forceinline__ void frag_cols32(const float *M, int ld, int k0, int 
     }
 }
 
+// Fragments in chunk order: lane (g, r) supplies the eight consecutive k
+// indices k0 + 8g .. k0 + 8g + 7 (one 16-byte read for bf16).  Both operands
+// of a product must use the same order; a D-layout stack is turned into a
+// chunk-order operand by frag_from_state below.
+__device__ __forceinline__ void load_chunk(const __bf16 *p, bf16x8 &f) {
+    f = *reinterpret_cast<const bf16x8 *>(p);
+}
+__device__ __forceinline__ void load_chunk(const float *p, f32x8_arr &f) {
+    const float4 lo = *reinterpret_cast<const float4 *>(p);
+    const float4 hi = *reinterpret_cast<const float4 *>(p + 4);
+    f.v[0] = lo.x; f.v[1] = lo.y; f.v[2] = lo.z; f.v[3] = lo.w;
+    f.v[4] = hi.x; f.v[5] = hi.y; f.v[6] = hi.z; f.v[7] = hi.w;
+}
+__device__ __forceinline__ void load_chunk(const __bf16 *p, bf16x4 &f) {
+    f = *reinterpret_cast<const bf16x4 *>(p);
+}
+__device__ __forceinline__ void load_chunk(const float *p, f32x4_arr &f) {
+    const float4 t = *reinterpret_cast<const float4 *>(p);
+    f.v[0] = t.x; f.v[1] = t.y; f.v[2] = t.z; f.v[3] = t.w;
+}
+
+// Key order of the state tiles.  With 32-wide slabs over d_k, row 4g + i of
+// accumulator tile dt holds key index state_col<32>(dt, g) + i: tiles 2s and
+// 2s + 1 split the 8-key chunk 4s + g of slab s into halves, the lower half
+// going to tile 2s for even g and to tile 2s + 1 for odd g.  A product over
+// d_k then reads its other operand in chunk order (16 bytes per lane), and
+// the transpose read that feeds the state update fetches, per 16-lane row,
+// quads from alternating halves of four chunks -- which, with the row
+// swizzle of the key tile, spreads a read over all 64 LDS banks.  With
+// 16-wide slabs (d_k = 16) the order is the plain one.
+template <int KSD>
+__device__ __forceinline__ int state_col(int dt, int g) {
+    if constexpr (KSD == 32) return 8 * (4 * (dt >> 1) + g) + 4 * ((g & 1) ^ (dt & 1));
+    else return 16 * dt + 4 * g;
+}
+// B operand in chunk order from state tiles 2s, 2s + 1 (32-wide slab): lane
+// (g, r) needs keys 32s + 8g + 0..7, i.e. the tile holding the lower half
+// first (see state_col).
+template <typename F>
+__device__ __forceinline__ void frag_from_state(const f32x4 &t0, const f32x4 &t1, int g, F &f) {
+    const bool odd = g & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        frag_set(f, i, odd ? t1[i] : t0[i]);
+        frag_set(f, 4 + i, odd ? t0[i] : t1[i]);
+    }
+}
+
 // Store a 4-element fragment to 4 consecutive elements (8 or 16 bytes).
 __device__ __forceinline__ void store_frag16(__bf16 *p, const bf16x4 &f) {
     *reinterpret_cast<bf16x4 *>(p) = f;
