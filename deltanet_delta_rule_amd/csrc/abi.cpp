@@ -69,6 +69,10 @@ dr_status delta_rule_chunk_fwd(const void *q, const void *k, const void *v,
     // grid = B*H*(Dv/16) at most; sequence length and heads index in 32 bits
     if (T > INT32_MAX || H > INT32_MAX || mul_checked({B, H, Dv / 16}) > INT32_MAX)
         return DR_ERR_UNSUPPORTED;
+    // one chunk of one head (chunk tokens x H rows) is addressed with 32-bit
+    // byte offsets
+    const int64_t span = mul_checked({chunk, H, Dk > Dv ? Dk : Dv, esz});
+    if (span < 0 || span > INT32_MAX / 2) return DR_ERR_UNSUPPORTED;
 
     if (T > 0 && (!q || !k || !v || !beta || !o)) return DR_ERR_INVALID_ARG;
     // q, k and the states are read in 16-byte vectors; v, beta and o element-wise

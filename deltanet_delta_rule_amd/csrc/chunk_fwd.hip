@@ -342,14 +342,21 @@ __device__ __forceinline__ void tri_inverse(const float *Af, DT *TsT, DT *Dw, in
 // State path of one chunk for this wave's 16 rows of S:
 //   X = K S^T, Y = Q S^T, R = diag(beta)(V - X), E = Ti R,
 //   S^T += K^T E, O = Y + P E (stored for tokens < len).
+// Output rows of one chunk: a buffer resource over the chunk's valid tokens,
+// this lane's byte offset (its value column, rows 4g..) and the token stride.
+struct OutChunk {
+    __amdgpu_buffer_rsrc_t rsrc;
+    int voff, row_bytes;
+};
+
 // Operand fragments are loaded into registers ahead of their MFMAs: the Ti
 // and P rows first (they do not depend on the state), the K and Q slabs of
 // X and Y one slab ahead, the K^T fragments while X and Y run.
 template <typename DT, int DK, int C, int NW>
 __device__ __forceinline__ void state_path(const DT *Ks, const DT *Qs, const DT *Vs,
                                            const DT *TsT, const DT *Ps, const float *betas,
-                                           f32x4 *Sacc, DT *oh, int64_t tsv, int t0, int len,
-                                           int wave, int lane) {
+                                           f32x4 *Sacc, const OutChunk &out, int wave,
+                                           int lane) {
     typedef ChunkCfg<DT, DK, C, NW> G;
     constexpr int NT = G::NT, ND = G::ND, KSD = G::KSD, KSC = G::KSC;
     constexpr int NSD = DK / KSD, NSC = C / KSC;
@@ -473,17 +480,12 @@ __device__ __forceinline__ void state_path(const DT *Ks, const DT *Qs, const DT 
                 if constexpr (KSC == 32) mma_k32(PE, fP[mt][s], fe[s]);
                 else mma_k16(PE, fP[mt][s], fe[s]);
             }
-        if (len == C) {
+        // token 16mt + 4g + i of the chunk; stores past the chunk's last
+        // token fall outside the resource and are dropped
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                oh[(t0 + 16 * mt + 4 * g + i) * tsv] = from_f32<DT>(Y[mt][i] + PE[i]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * mt + 4 * g + i;
-                if (t < len) oh[(t0 + t) * tsv] = from_f32<DT>(Y[mt][i] + PE[i]);
-            }
-        }
+        for (int i = 0; i < 4; ++i)
+            buf_store_elem(from_f32<DT>(Y[mt][i] + PE[i]), out.rsrc, out.voff,
+                           (16 * mt + i) * out.row_bytes);
     }
 }
 
@@ -491,9 +493,10 @@ __device__ __forceinline__ void state_path(const DT *Ks, const DT *Qs, const DT 
 // an XCD-aware remap, and the base pointers of its head.
 template <typename DT>
 struct HeadPtrs {
-    const DT *kh, *qh, *vh, *bh;
-    DT *oh;
-    int64_t tsk, tsv, sbase;
+    const DT *kh, *qh, *vh, *bh;  // token 0 of the head (vh: first value column of the tile)
+    DT *oh;                       // token 0, column 0 of the head's output
+    int tsk, tsv, tsb;            // token strides in elements: H*d_k, H*d_v, H
+    int64_t sbase;
     int vcol;
 };
 
@@ -511,56 +514,73 @@ __device__ __forceinline__ HeadPtrs<DT> head_ptrs(const DT *q, const DT *k, cons
     const int b = head / H, h = head % H;
     HeadPtrs<DT> p;
     p.vcol = vt * 16 * NW + wave * 16 + r;
-    p.tsk = (int64_t)H * DK;
-    p.tsv = (int64_t)H * Dv;
+    p.tsk = H * DK;
+    p.tsv = H * Dv;
+    p.tsb = H;
     p.kh = k + ((int64_t)b * T * H + h) * DK;
     p.qh = q + ((int64_t)b * T * H + h) * DK;
     p.vh = v + ((int64_t)b * T * H + h) * Dv + vt * 16 * NW;
-    p.oh = o + ((int64_t)b * T * H + h) * Dv + p.vcol;
+    p.oh = o + ((int64_t)b * T * H + h) * Dv;
     p.bh = beta + (int64_t)b * T * H + h;
     p.sbase = ((int64_t)head * Dv + p.vcol) * DK;
     return p;
 }
 
 // Register staging of one chunk's K, Q, V (this workgroup's value columns)
-// and beta.  Loads are unconditional (addresses clamped into the sequence) so
-// that none sits in a branch that would force an early wait; out-of-range
-// tokens are zeroed when staged.
+// and beta.  Each tensor is read through a buffer resource that spans exactly
+// the chunk's valid tokens, so the tokens past the end of the sequence load as
+// zeros (beta = 0 leaves the state unchanged) without any masking, and every
+// lane's offsets within a chunk are constants computed once.
 template <typename DT, int DK, int C, int NW>
 struct ChunkRegs {
     typedef ChunkCfg<DT, DK, C, NW> G;
     typedef typename Vec16<DT>::type vec_t;
+    static constexpr int OUT = 0x7ffffff0;  // offset past any resource: loads 0
     vec_t k[G::NPRE], q[G::NPRE], v[G::NPREV];
     DT b;
+    int offk[G::NPRE], offv[G::NPREV], offb;
 
-    __device__ __forceinline__ void load(const HeadPtrs<DT> &p, int T, int H, int t0, int tid) {
-        const int last = min(C, T - t0) - 1;  // >= 0: the chunk holds a token
+    __device__ __forceinline__ void init(const HeadPtrs<DT> &p, int tid) {
 #pragma unroll
         for (int j = 0; j < G::NPRE; ++j) {
-            const int idx = min(tid + j * G::NTHR, C * G::VPR - 1);
-            const int t = min(idx / G::VPR, last), e0 = (idx % G::VPR) * G::VEC;
-            k[j] = *reinterpret_cast<const vec_t *>(p.kh + (t0 + t) * p.tsk + e0);
-            q[j] = *reinterpret_cast<const vec_t *>(p.qh + (t0 + t) * p.tsk + e0);
+            const int idx = tid + j * G::NTHR;
+            const int t = idx / G::VPR, e0 = (idx % G::VPR) * G::VEC;
+            offk[j] = idx < C * G::VPR ? (t * p.tsk + e0) * (int)sizeof(DT) : OUT;
         }
 #pragma unroll
         for (int j = 0; j < G::NPREV; ++j) {
-            const int idx = min(tid + j * G::NTHR, C * G::VPRV - 1);
-            const int t = min(idx / G::VPRV, last), e0 = (idx % G::VPRV) * G::VEC;
-            v[j] = *reinterpret_cast<const vec_t *>(p.vh + (t0 + t) * p.tsv + e0);
+            const int idx = tid + j * G::NTHR;
+            const int t = idx / G::VPRV, e0 = (idx % G::VPRV) * G::VEC;
+            offv[j] = idx < C * G::VPRV ? (t * p.tsv + e0) * (int)sizeof(DT) : OUT;
         }
-        b = p.bh[(int64_t)(t0 + min(tid, last)) * H];
+        offb = tid < C ? tid * p.tsb * (int)sizeof(DT) : OUT;
     }
-    // Write into one LDS buffer set; tokens >= len become zeros.
-    __device__ __forceinline__ void stage(DT *Ks, DT *Qs, DT *Vs, float *betas, int len,
-                                          int tid) const {
+    __device__ __forceinline__ void load(const HeadPtrs<DT> &p, int T, int t0) {
+        const int len = min(C, T - t0);
+        const int esz = (int)sizeof(DT);
+        const auto rk = make_rsrc(p.kh + (int64_t)t0 * p.tsk, len * p.tsk * esz);
+        const auto rq = make_rsrc(p.qh + (int64_t)t0 * p.tsk, len * p.tsk * esz);
+        const auto rv = make_rsrc(p.vh + (int64_t)t0 * p.tsv, len * p.tsv * esz);
+        const auto rb = make_rsrc(p.bh + (int64_t)t0 * p.tsb, len * p.tsb * esz);
+#pragma unroll
+        for (int j = 0; j < G::NPRE; ++j) {
+            k[j] = buf_load16<vec_t>(rk, offk[j]);
+            q[j] = buf_load16<vec_t>(rq, offk[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < G::NPREV; ++j) v[j] = buf_load16<vec_t>(rv, offv[j]);
+        b = buf_load_elem<DT>(rb, offb);
+    }
+    // Write into one LDS buffer set.
+    __device__ __forceinline__ void stage(DT *Ks, DT *Qs, DT *Vs, float *betas, int tid) const {
 #pragma unroll
         for (int j = 0; j < G::NPRE; ++j) {
             const int idx = tid + j * G::NTHR;
             if (idx < C * G::VPR) {
                 const int t = idx / G::VPR, e0 = (idx % G::VPR) * G::VEC;
                 const int off = kq_off<DT, DK, C, NW>(t, e0);
-                *reinterpret_cast<vec_t *>(Ks + off) = (t < len) ? k[j] : vec_t{};
-                *reinterpret_cast<vec_t *>(Qs + off) = (t < len) ? q[j] : vec_t{};
+                *reinterpret_cast<vec_t *>(Ks + off) = k[j];
+                *reinterpret_cast<vec_t *>(Qs + off) = q[j];
             }
         }
 #pragma unroll
@@ -568,10 +588,10 @@ struct ChunkRegs {
             const int idx = tid + j * G::NTHR;
             if (idx < C * G::VPRV) {
                 const int t = idx / G::VPRV, e0 = (idx % G::VPRV) * G::VEC;
-                *reinterpret_cast<vec_t *>(Vs + t * G::LDV + e0) = (t < len) ? v[j] : vec_t{};
+                *reinterpret_cast<vec_t *>(Vs + t * G::LDV + e0) = v[j];
             }
         }
-        if (tid < C) betas[tid] = (tid < len) ? to_f32(b) : 0.f;
+        if (tid < C) betas[tid] = to_f32(b);
     }
 };
 
@@ -626,13 +646,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
         for (int i = tid; i < 2 * C * G::LDT; i += G::NTHR) (&sm.TsT[0][0])[i] = from_f32<DT>(0.f);
         for (int i = tid; i < 2 * C * G::LDP; i += G::NTHR) (&sm.Ps[0][0])[i] = from_f32<DT>(0.f);
         ChunkRegs<DT, DK, C, NW> rg;
+        rg.init(p, tid);
+        OutChunk out;
+        out.voff = (4 * g * p.tsv + p.vcol) * (int)sizeof(DT);
+        out.row_bytes = p.tsv * (int)sizeof(DT);
         // prologue: chunks 0 and 1 staged, chunk 0 solved, chunk 2 in flight
-        rg.load(p, T, H, 0, tid);
-        rg.stage(sm.Ks[0], sm.Qs[0], sm.Vs[0], sm.betas[0], min(C, T), tid);
-        const int c1 = min(1, N - 1);
-        rg.load(p, T, H, c1 * C, tid);
-        rg.stage(sm.Ks[1], sm.Qs[1], sm.Vs[1], sm.betas[1], min(C, T - c1 * C), tid);
-        rg.load(p, T, H, min(2, N - 1) * C, tid);
+        rg.load(p, T, 0);
+        rg.stage(sm.Ks[0], sm.Qs[0], sm.Vs[0], sm.betas[0], tid);
+        rg.load(p, T, min(1, N - 1) * C);
+        rg.stage(sm.Ks[1], sm.Qs[1], sm.Vs[1], sm.betas[1], tid);
+        rg.load(p, T, min(2, N - 1) * C);
         lds_barrier();
         gram_tiles<DT, DK, C, NW>(sm.Ks[0], sm.Qs[0], sm.betas[0], sm.Af, sm.Ps[0], wave, lane);
         lds_barrier();
@@ -644,17 +667,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
             const int t0 = c * C;
             const int len = min(C, T - t0);
             // ---- phase 1: state path of chunk c, Gram tiles of chunk c+1 ----
+            out.rsrc = make_rsrc(p.oh + (int64_t)t0 * p.tsv, len * out.row_bytes);
             state_path<DT, DK, C, NW>(sm.Ks[b], sm.Qs[b], sm.Vs[b], sm.TsT[b], sm.Ps[b],
-                                      sm.betas[b], Sacc, p.oh, p.tsv, t0, len, wave, lane);
+                                      sm.betas[b], Sacc, out, wave, lane);
             // (past the last chunk this works on stale buffers; never read)
             gram_tiles<DT, DK, C, NW>(sm.Ks[b1], sm.Qs[b1], sm.betas[b1], sm.Af, sm.Ps[b1],
                                       wave, lane);
             lds_barrier();
             // ---- phase 2: inverse of chunk c+1, staging of chunk c+2 ----
             tri_inverse<DT, DK, C, NW>(sm.Af, sm.TsT[b1], sm.Dw[wave], wave, lane);
-            const int c2 = min(c + 2, N - 1);
-            rg.stage(sm.Ks[b], sm.Qs[b], sm.Vs[b], sm.betas[b], min(C, T - c2 * C), tid);
-            rg.load(p, T, H, min(c + 3, N - 1) * C, tid);
+            rg.stage(sm.Ks[b], sm.Qs[b], sm.Vs[b], sm.betas[b], tid);
+            rg.load(p, T, min(c + 3, N - 1) * C);
             lds_barrier();
         }
     }
@@ -709,20 +732,25 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
         for (int i = tid; i < C * G::LDT; i += G::NTHR) sm.TsT[i] = from_f32<DT>(0.f);
         for (int i = tid; i < C * G::LDP; i += G::NTHR) sm.Ps[i] = from_f32<DT>(0.f);
         ChunkRegs<DT, DK, C, NW> rg;
-        rg.load(p, T, H, 0, tid);
+        rg.init(p, tid);
+        OutChunk out;
+        out.voff = (4 * g * p.tsv + p.vcol) * (int)sizeof(DT);
+        out.row_bytes = p.tsv * (int)sizeof(DT);
+        rg.load(p, T, 0);
         for (int c = 0; c < N; ++c) {
             const int t0 = c * C;
             const int len = min(C, T - t0);
             lds_barrier();
-            rg.stage(sm.Ks, sm.Qs, sm.Vs, sm.betas, len, tid);
+            rg.stage(sm.Ks, sm.Qs, sm.Vs, sm.betas, tid);
             lds_barrier();
-            rg.load(p, T, H, min(c + 1, N - 1) * C, tid);
+            rg.load(p, T, min(c + 1, N - 1) * C);
             gram_tiles<DT, DK, C, NW>(sm.Ks, sm.Qs, sm.betas, sm.Af, sm.Ps, wave, lane);
             lds_barrier();
             tri_inverse<DT, DK, C, NW>(sm.Af, sm.TsT, sm.Dw[wave], wave, lane);
             lds_barrier();
-            state_path<DT, DK, C, NW>(sm.Ks, sm.Qs, sm.Vs, sm.TsT, sm.Ps, sm.betas, Sacc, p.oh,
-                                      p.tsv, t0, len, wave, lane);
+            out.rsrc = make_rsrc(p.oh + (int64_t)t0 * p.tsv, len * out.row_bytes);
+            state_path<DT, DK, C, NW>(sm.Ks, sm.Qs, sm.Vs, sm.TsT, sm.Ps, sm.betas, Sacc, out,
+                                      wave, lane);
         }
     }
     if (S_T) {

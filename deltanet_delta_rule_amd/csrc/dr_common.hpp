@@ -238,6 +238,38 @@ __device__ __forceinline__ void frag_from_acc16(const f32x4 &t0, F &f) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Raw buffer resource over `bytes` bytes from `base` (the 32-bit data format
+// word of gfx9 resources).  Accesses are range-checked against `bytes`: loads
+// past the end return zeros and stores past it are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes,
+                                             0x00020000);
+}
+template <typename V>
+__device__ __forceinline__ V buf_load16(__amdgpu_buffer_rsrc_t r, int voff) {
+    static_assert(sizeof(V) == 16, "16-byte vector");
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+template <typename DT>
+__device__ __forceinline__ DT buf_load_elem(__amdgpu_buffer_rsrc_t r, int voff);
+template <>
+__device__ __forceinline__ __bf16 buf_load_elem<__bf16>(__amdgpu_buffer_rsrc_t r, int voff) {
+    return __builtin_bit_cast(__bf16, __builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0));
+}
+template <>
+__device__ __forceinline__ float buf_load_elem<float>(__amdgpu_buffer_rsrc_t r, int voff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
+// Element store at voff (per lane) + soff (uniform).
+__device__ __forceinline__ void buf_store_elem(__bf16 x, __amdgpu_buffer_rsrc_t r, int voff,
+                                               int soff) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x), r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_store_elem(float x, __amdgpu_buffer_rsrc_t r, int voff,
+                                               int soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, voff, soff, 0);
+}
+
 // Workgroup barrier for hand-offs through LDS: waits for this wave's LDS
 // operations, then meets the other waves.  Unlike __syncthreads() it carries
 // no fence over global memory, so register prefetches and output stores stay

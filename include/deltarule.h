@@ -32,7 +32,10 @@
  *            accumulation is fp32.
  *   Sizes    Dk and Dv in {16, 32, 64, 128}; chunk in {16, 32, 64};
  *            B, H, T >= 0 (B or H zero: the call does nothing).  T and H
- *            must fit in int32, and so must B*H*Dv/16.
+ *            must fit in int32, and so must B*H*Dv/16.  For the chunked
+ *            entry point, chunk * H * max(Dk, Dv) * element size must not
+ *            exceed 2^30 bytes (one chunk of all heads is addressed with
+ *            32-bit offsets).
  *   Pointers Device pointers (hipMalloc'd or equivalent).  q, k and every
  *            state pointer must be 16-byte aligned (they are read as 16-byte
  *            vectors); v, beta and o need only their element alignment.

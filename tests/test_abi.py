@@ -93,6 +93,7 @@ def test_chunk_rejects_invalid(lib, kw):
 @pytest.mark.parametrize("kw", [
     dict(Dk=48), dict(Dv=8), dict(Dk=256), dict(chunk=8), dict(chunk=128),
     dict(chunk=48), dict(T=2 ** 31),
+    dict(B=1, H=2 ** 21, Dk=128, Dv=128),   # one chunk of all heads exceeds 2^30 bytes
 ])
 def test_chunk_rejects_unsupported(lib, kw):
     assert _chunk(lib, **kw) == dr.DR_ERR_UNSUPPORTED
