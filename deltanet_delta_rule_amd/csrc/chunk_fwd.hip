@@ -76,7 +76,6 @@ struct ChunkCfg {
     static constexpr int LDP = C + 2 * PADE;    // P (row fragments)
     static constexpr int LDT = C + 2 * PADE;    // Ti^T (transpose reads)
     static constexpr int LDA = C + 8;           // A (fp32)
-    static constexpr int LDD = 16 + PADE;       // diagonal-inverse scratch
     static constexpr int VEC = Vec16<DT>::N;    // elements per 16-byte load
     static constexpr int VPR = DK / VEC;        // 16-byte vectors per K row
     static constexpr int NTHR = 64 * NW;
@@ -232,109 +231,188 @@ __device__ __forceinline__ void gram_tiles(const DT *Ks, const DT *Qs, const flo
     }
 }
 
-// Ti = (I + A)^{-1} by blocks of 16, stored transposed: TsT[col][row] =
-// Ti[row][col] (Ti is unit lower-triangular, so TsT is upper-triangular; its
-// lower blocks stay zero).
-//  1. Every wave inverts all NT diagonal blocks (lane = 16*d + column, fp32
-//     forward substitution).  A lane's column of Ti_dd is a row of Ti^T, kept
-//     in the wave's private scratch Dw and, for the owning wave, in TsT.
-//  2. Wave w fills the block columns j = w, w + NW, ... of Ti: for i > j
-//       Ti_ij = -Ti_ii * sum_{k=j}^{i-1} A_ik Ti_kj,
-//     each block column needing only its own earlier blocks and the diagonal
-//     inverses, so no wave waits for another.
-template <typename DT, int DK, int C, int NW>
-__device__ __forceinline__ void tri_inverse(const float *Af, DT *TsT, DT *Dw, int wave,
-                                            int lane) {
-    typedef ChunkCfg<DT, DK, C, NW> G;
-    constexpr int NT = G::NT, LDA = G::LDA, LDT = G::LDT, LDD = G::LDD;
+// Ti = (I + A)^{-1}, stored transposed: TsT[col][row] = Ti[row][col] (Ti is
+// unit lower-triangular, so TsT is upper-triangular; its lower blocks stay
+// zero).  Blocked forward substitution by doubling: if T inverts the diagonal
+// blocks of size h of (I + A) and A_h holds the entries of A in the blocks of
+// size h just below them (rows in the upper half, columns in the lower half
+// of each diagonal block of size 2h), then T - T A_h T inverts the diagonal
+// blocks of size 2h, since (T A_h)^2 = 0.
+//  1. diag_inverse: the 4x4 diagonal blocks by substitution (VALU), then
+//     sizes 8 and 16 by doubling on the MFMA units.  A wave inverts the
+//     diagonal 16-blocks of the Gram row jobs it owns, right after computing
+//     them, so it reads back only its own A tiles.
+//  2. offdiag_inverse: sizes 32 and 64 by doubling over 16-blocks, after a
+//     barrier.  For a 64-token chunk the six new blocks are split into four
+//     self-contained jobs, each recomputing the size-32 blocks it needs.
+
+// A-operand rows of an Af tile (fp32 LDS) narrowed to DT: lane (g, r) takes
+// Af[row0 + r][col0 + 4g .. + 3].
+template <typename DT, int LDA>
+__device__ __forceinline__ void af_rows(const float *Af, int row0, int col0, int lane,
+                                        typename Frag<DT>::k16 &f) {
     const int g = lane >> 4, r = lane & 15;
-    const int d = lane >> 4, cc = lane & 15;
-    typename Frag<DT>::k16 xq[4];  // x as four quads, narrowed to DT
-    if (lane < C) {
-        // Lane (d, cc) holds row cc of the diagonal block A_dd and solves for
-        // column cc of its inverse; A_dd[i][j] comes from lane i of the same
-        // 16-lane row through DPP, so the dependent chain has no LDS reads.
-        float a[16];
-        const float *arow = Af + (16 * d + cc) * LDA + 16 * d;
+    float a4[4];
+    load4(Af + (row0 + r) * LDA + col0 + 4 * g, a4);
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 t = *reinterpret_cast<const float4 *>(arow + 4 * q4);
-            a[4 * q4] = t.x; a[4 * q4 + 1] = t.y; a[4 * q4 + 2] = t.z; a[4 * q4 + 3] = t.w;
-        }
-        // Right-looking order: once x_j is final, the updates of all later
-        // partial sums are independent, so the dependent chain is one update
-        // per row rather than one per matrix entry.
-        float x[16], s[16];
+    for (int e = 0; e < 4; ++e) frag_set(f, e, a4[e]);
+}
+
+template <typename DT, int DK, int C, int NW>
+__device__ __forceinline__ void diag_inverse(const float *Af, DT *TsT, int d, int lane) {
+    typedef ChunkCfg<DT, DK, C, NW> G;
+    typedef typename Frag<DT>::k16 F;
+    constexpr int LDA = G::LDA, LDT = G::LDT;
+    const int g = lane >> 4, r = lane & 15, c = r & 3;
+    const int o = 16 * d;
+    // Size 4: lane (g, r) with r / 4 == g takes 4x4 block g and solves for
+    // column c of its inverse (x) and for column c of the inverse of its
+    // transpose (y), i.e. row c of the inverse.  In D layout these are
+    // T[4g + i][r] and T^T[4g + i][r]; every other lane holds zeros.
+    float a1[4], a2[4], a3[4], ar[4];
+    load4(Af + (o + 4 * g + 1) * LDA + o + 4 * g, a1);
+    load4(Af + (o + 4 * g + 2) * LDA + o + 4 * g, a2);
+    load4(Af + (o + 4 * g + 3) * LDA + o + 4 * g, a3);
+    load4(Af + (o + r) * LDA + o + 4 * g, ar);  // A-operand row r, columns 4g..4g+3
+    const float e0 = c == 0 ? 1.f : 0.f, e1 = c == 1 ? 1.f : 0.f;
+    const float e2 = c == 2 ? 1.f : 0.f, e3 = c == 3 ? 1.f : 0.f;
+    const float x0 = e0, x1 = e1 - a1[0] * x0, x2 = e2 - a2[0] * x0 - a2[1] * x1;
+    const float x3 = e3 - a3[0] * x0 - a3[1] * x1 - a3[2] * x2;
+    const float y3 = e3, y2 = e2 - a3[2] * y3, y1 = e1 - a2[1] * y2 - a3[1] * y3;
+    const float y0 = e0 - a1[0] * y1 - a2[0] * y2 - a3[0] * y3;
+    const bool act = (r >> 2) == g;
+    f32x4 Tm = act ? f32x4{x0, x1, x2, x3} : zero4();
+    f32x4 Tt = act ? f32x4{y0, y1, y2, y3} : zero4();
+    // Sizes 8 and 16: M = A_h T, T <- T - T M and T^T <- T^T - M^T T^T.
+    // Operands: rows of T are the D layout of T^T and rows of M^T the D
+    // layout of M, so both products come straight from registers.
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = 0.f;
+    for (int lv = 0; lv < 2; ++lv) {
+        const int h = 4 << lv;
+        const bool keep = (r / (2 * h) == (4 * g) / (2 * h)) && (r % (2 * h) >= h) &&
+                          ((4 * g) % (2 * h) < h);
+        F fa, fT, fTt, fM;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            x[j] = ((j == cc) ? 1.f : 0.f) - s[j];
-#pragma unroll
-            for (int i = j + 1; i < 16; ++i) s[i] += row_bcast_at(a[j], i) * x[j];
-        }
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) frag_set(xq[q4], e, x[4 * q4 + e]);
-        DT *drow = Dw + (16 * d + cc) * LDD;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) store_frag16(drow + 4 * q4, xq[q4]);
+        for (int e = 0; e < 4; ++e) frag_set(fa, e, keep ? ar[e] : 0.f);
+        frag_from_acc16(Tm, fT);
+        frag_from_acc16(Tt, fTt);
+        f32x4 M = zero4(), P = zero4(), Pt = zero4();
+        mma_k16(M, fa, fT);
+        frag_from_acc16(M, fM);
+        mma_k16(P, fTt, fM);
+        mma_k16(Pt, fM, fTt);
+        Tm -= P;
+        Tt -= Pt;
     }
-    wave_lds_fence();
+    // lane (g, r) holds Ti[o + 4g + i][o + r] = TsT[o + r][o + 4g + i]
+    F out;
+    frag_from_acc16(Tm, out);
+    store_frag16(TsT + (o + r) * LDT + o + 4 * g, out);
+}
+
+template <typename DT, int DK, int C, int NW>
+__device__ __forceinline__ void offdiag_inverse(const float *Af, DT *TsT, int wave, int lane) {
+    typedef ChunkCfg<DT, DK, C, NW> G;
+    typedef typename Frag<DT>::k16 F;
+    constexpr int NT = G::NT, LDA = G::LDA, LDT = G::LDT;
+    const int g = lane >> 4, r = lane & 15;
+    // T_lj as B operand (lane (g, r): T_lj[4g + e][r] = TsT[16j + r][16l + 4g + e])
+    auto tB = [&](int l, int j, F &f) { load_chunk(TsT + (16 * j + r) * LDT + 16 * l + 4 * g, f); };
+    // rows of T_ik as A operand (lane (g, r): T_ik[r][4g + e] = TsT[16k + 4g + e][16i + r])
+    auto tA = [&](int i, int k, F &f) { frag_cols16(TsT, LDT, 16 * k, 16 * i, lane, f); };
+    auto aA = [&](int k, int l, F &f) { af_rows<DT, LDA>(Af, 16 * k, 16 * l, lane, f); };
+    auto store = [&](int i, int j, const f32x4 &D) {  // D = D layout of -T_ij
+        F out;
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-        if (j % NW != wave) continue;
-        // diagonal block j: its lanes hold the rows of Ti_jj^T
-        if (d == j) {
+        for (int e = 0; e < 4; ++e) frag_set(out, e, -D[e]);
+        store_frag16(TsT + (16 * j + r) * LDT + 16 * i + 4 * g, out);
+    };
+    if constexpr (NT == 2) {
+        if (wave != 0) return;
+        F fa, fb, ft, fn;
+        aA(1, 0, fa); tB(0, 0, fb); tA(1, 1, ft);
+        f32x4 N = zero4(), X = zero4();
+        mma_k16(N, fa, fb);
+        frag_from_acc16(N, fn);
+        mma_k16(X, ft, fn);
+        store(1, 0, X);
+    } else if constexpr (NT == 4) {
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                store_frag16(TsT + (16 * j + cc) * LDT + 16 * j + 4 * q4, xq[q4]);
-        }
-        // all operands that do not depend on results of this block column
-        typename Frag<DT>::k16 fA[NT][NT], fTii[NT], fTjj;
-#pragma unroll
-        for (int i = j + 1; i < NT; ++i) {
-#pragma unroll
-            for (int kb = j; kb < i; ++kb) {
-                float a4[4];
-                load4(Af + (16 * i + r) * LDA + 16 * kb + 4 * g, a4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) frag_set(fA[i][kb], e, a4[e]);
+        for (int job = 0; job < 4; ++job) {
+            if (job % NW != wave) continue;
+            // X10 = -T10 = T11 (A10 T00) and X32 = -T32 = T33 (A32 T22) with
+            // the D layout of X32^T (rows of X32 as an A operand)
+            const bool need10 = job == 0 || job == 3, need32 = job == 2 || job == 3;
+            F fT11, fT33, fT00, fT11b, fX10, fX32r;
+            f32x4 X10 = zero4(), X32 = zero4(), X32t = zero4();
+            tA(3, 3, fT33);
+            if (need10) {
+                F fa, fb, fn;
+                aA(1, 0, fa); tB(0, 0, fb); tA(1, 1, fT11);
+                f32x4 N = zero4();
+                mma_k16(N, fa, fb);
+                frag_from_acc16(N, fn);
+                mma_k16(X10, fT11, fn);
+                frag_from_acc16(X10, fX10);  // -T10 as B operand
+                fT00 = fb;
+                if (job == 0) store(1, 0, X10);
             }
-            // A = Ti_ii: lane (g, r) takes Ti_ii[r][4g + e] = Dw[16i + 4g + e][r]
-            frag_cols16(Dw, LDD, 16 * i, 0, lane, fTii[i]);
-        }
-        {
-            // B = Ti_jj: lane (g, r) takes Ti_jj[4g + e][r] = Dw row 16j + r
-            float b4[4];
-            load4(Dw + (16 * j + r) * LDD + 4 * g, b4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) frag_set(fTjj, e, b4[e]);
-        }
-        f32x4 Tcol[NT];
-#pragma unroll
-        for (int i = j + 1; i < NT; ++i) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kb = j; kb < i; ++kb) {
-                typename Frag<DT>::k16 fb;
-                if (kb == j) fb = fTjj;
-                else frag_from_acc16(Tcol[kb], fb);
-                mma_k16(acc, fA[i][kb], fb);
+            if (need32) {
+                F fa, fb, fn;
+                aA(3, 2, fa); tB(2, 2, fb);
+                f32x4 N = zero4();
+                mma_k16(N, fa, fb);
+                frag_from_acc16(N, fn);
+                mma_k16(X32, fT33, fn);
+                mma_k16(X32t, fn, fT33);
+                frag_from_acc16(X32t, fX32r);  // rows of -T32 as A operand
+                if (job == 2) store(3, 2, X32);
             }
-            typename Frag<DT>::k16 fb;
-            frag_from_acc16(acc, fb);
-            f32x4 res = zero4();
-            mma_k16(res, fTii[i], fb);
-            // lane (g, r) holds Ti[16i + 4g + e][16j + r] = TsT[16j + r][16i + 4g + e]
-            typename Frag<DT>::k16 out;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                Tcol[i][e] = -res[e];
-                frag_set(out, e, -res[e]);
+            if (job == 1 || job == 2) tB(1, 1, fT11b);
+            // M_k = sum_l A_kl T_lj for k = 2, 3; then T_ij = -sum_k T_ik M_k
+            if (job == 0 || job == 1) {  // T20, T21 = -T22 M_2
+                F fa, fm, fT22;
+                f32x4 M2 = zero4(), Y = zero4();
+                if (job == 0) {
+                    aA(2, 0, fa); mma_k16(M2, fa, fT00);
+                    // + A21 T10 = - A21 X10
+                    F fa1; aA(2, 1, fa1);
+                    f32x4 Mneg = zero4();
+                    mma_k16(Mneg, fa1, fX10);
+                    M2 -= Mneg;
+                } else {
+                    aA(2, 1, fa); mma_k16(M2, fa, fT11b);
+                }
+                frag_from_acc16(M2, fm);
+                tA(2, 2, fT22);
+                mma_k16(Y, fT22, fm);
+                store(2, job, Y);
+            } else {  // T31 (job 2), T30 (job 3) = -(T32 M_2 + T33 M_3)
+                F fa2, fa3, fm2, fm3;
+                f32x4 M2 = zero4(), M3 = zero4(), Y = zero4();
+                if (job == 2) {
+                    aA(2, 1, fa2); mma_k16(M2, fa2, fT11b);
+                    aA(3, 1, fa3); mma_k16(M3, fa3, fT11b);
+                } else {
+                    F fb0, fa21, fa31;
+                    aA(2, 0, fa2); aA(3, 0, fa3); aA(2, 1, fa21); aA(3, 1, fa31);
+                    mma_k16(M2, fa2, fT00);
+                    mma_k16(M3, fa3, fT00);
+                    f32x4 N2 = zero4(), N3 = zero4();  // A_k1 X10 = -A_k1 T10
+                    mma_k16(N2, fa21, fX10);
+                    mma_k16(N3, fa31, fX10);
+                    M2 -= N2;
+                    M3 -= N3;
+                }
+                frag_from_acc16(M2, fm2);
+                frag_from_acc16(M3, fm3);
+                // -T_i? = -(T32 M2 + T33 M3) = X32 M2 - T33 M3
+                f32x4 Y32 = zero4();
+                mma_k16(Y32, fX32r, fm2);
+                mma_k16(Y, fT33, fm3);
+                Y -= Y32;
+                store(3, job == 2 ? 1 : 0, Y);
             }
-            store_frag16(TsT + (16 * j + r) * LDT + 16 * i + 4 * g, out);
         }
     }
 }
@@ -608,7 +686,6 @@ struct PipeSmem {
     DT Ps[2][C * G::LDP];          // Q K^T (.) M
     float Af[C * G::LDA];          // A = beta (K K^T) strictly lower, fp32
     float betas[2][C];
-    DT Dw[NW][C * G::LDD];         // per-wave diagonal inverses (transposed)
 };
 
 template <typename DT, int DK, int C, int NW>
@@ -658,8 +735,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
         rg.load(p, T, min(2, N - 1) * C);
         lds_barrier();
         gram_tiles<DT, DK, C, NW>(sm.Ks[0], sm.Qs[0], sm.betas[0], sm.Af, sm.Ps[0], wave, lane);
+        wave_lds_fence();
+        for (int d = wave; d < NT; d += NW) diag_inverse<DT, DK, C, NW>(sm.Af, sm.TsT[0], d, lane);
         lds_barrier();
-        tri_inverse<DT, DK, C, NW>(sm.Af, sm.TsT[0], sm.Dw[wave], wave, lane);
+        offdiag_inverse<DT, DK, C, NW>(sm.Af, sm.TsT[0], wave, lane);
         lds_barrier();
 
         for (int c = 0; c < N; ++c) {
@@ -673,9 +752,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
             // (past the last chunk this works on stale buffers; never read)
             gram_tiles<DT, DK, C, NW>(sm.Ks[b1], sm.Qs[b1], sm.betas[b1], sm.Af, sm.Ps[b1],
                                       wave, lane);
+            wave_lds_fence();
+            for (int d = wave; d < NT; d += NW)
+                diag_inverse<DT, DK, C, NW>(sm.Af, sm.TsT[b1], d, lane);
             lds_barrier();
-            // ---- phase 2: inverse of chunk c+1, staging of chunk c+2 ----
-            tri_inverse<DT, DK, C, NW>(sm.Af, sm.TsT[b1], sm.Dw[wave], wave, lane);
+            // ---- phase 2: rest of the inverse of chunk c+1, staging of chunk c+2 ----
+            offdiag_inverse<DT, DK, C, NW>(sm.Af, sm.TsT[b1], wave, lane);
             rg.stage(sm.Ks[b], sm.Qs[b], sm.Vs[b], sm.betas[b], tid);
             rg.load(p, T, min(c + 3, N - 1) * C);
             lds_barrier();
@@ -701,7 +783,6 @@ struct SerialSmem {
     DT Ps[C * G::LDP];
     float Af[C * G::LDA];
     float betas[C];
-    DT Dw[NW][C * G::LDD];
 };
 
 template <typename DT, int DK, int C, int NW>
@@ -745,8 +826,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
             lds_barrier();
             rg.load(p, T, min(c + 1, N - 1) * C);
             gram_tiles<DT, DK, C, NW>(sm.Ks, sm.Qs, sm.betas, sm.Af, sm.Ps, wave, lane);
+            wave_lds_fence();
+            for (int d = wave; d < NT; d += NW) diag_inverse<DT, DK, C, NW>(sm.Af, sm.TsT, d, lane);
             lds_barrier();
-            tri_inverse<DT, DK, C, NW>(sm.Af, sm.TsT, sm.Dw[wave], wave, lane);
+            offdiag_inverse<DT, DK, C, NW>(sm.Af, sm.TsT, wave, lane);
             lds_barrier();
             out.rsrc = make_rsrc(p.oh + (int64_t)t0 * p.tsv, len * out.row_bytes);
             state_path<DT, DK, C, NW>(sm.Ks, sm.Qs, sm.Vs, sm.TsT, sm.Ps, sm.betas, Sacc, out,
