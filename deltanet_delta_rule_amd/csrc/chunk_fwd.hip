@@ -544,26 +544,28 @@ __device__ __forceinline__ void state_path(const DT *Ks, const DT *Qs, const DT 
             if constexpr (KSC == 32) mma_k32(Sacc[dt], fkt[dt][s], fe[s]);
             else mma_k16(Sacc[dt], fkt[dt][s], fe[s]);
         }
-    // O = Q S^T + P E.  P E gets its own accumulator: Y comes from slabs
-    // over d_k and P E from slabs over tokens, which can be different MFMA
-    // shapes, and an accumulation chain must never switch shape (the compiler
-    // issues such a dependent pair back to back and the second one reads a
-    // stale accumulator).
+    // O = Q S^T + P E.  When the slabs over d_k and over tokens have the same
+    // MFMA shape, P E accumulates onto Q S^T; otherwise it gets its own
+    // accumulator, since an accumulation chain must never switch shape (the
+    // compiler issues such a dependent pair back to back and the second one
+    // reads a stale accumulator).
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt) {
         f32x4 PE = zero4();
+        f32x4 &acc = (KSC == KSD) ? Y[mt] : PE;
 #pragma unroll
         for (int s = 0; s < NSC; ++s)
             if (s * KSC < 16 * (mt + 1)) {
-                if constexpr (KSC == 32) mma_k32(PE, fP[mt][s], fe[s]);
-                else mma_k16(PE, fP[mt][s], fe[s]);
+                if constexpr (KSC == 32) mma_k32(acc, fP[mt][s], fe[s]);
+                else mma_k16(acc, fP[mt][s], fe[s]);
             }
         // token 16mt + 4g + i of the chunk; stores past the chunk's last
         // token fall outside the resource and are dropped
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            buf_store_elem(from_f32<DT>(Y[mt][i] + PE[i]), out.rsrc, out.voff,
-                           (16 * mt + i) * out.row_bytes);
+        for (int i = 0; i < 4; ++i) {
+            const float oi = (KSC == KSD) ? Y[mt][i] : Y[mt][i] + PE[i];
+            buf_store_elem(from_f32<DT>(oi), out.rsrc, out.voff, (16 * mt + i) * out.row_bytes);
+        }
     }
 }
 
