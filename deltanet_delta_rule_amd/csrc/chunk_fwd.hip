@@ -158,15 +158,22 @@ __device__ __forceinline__ void kt_frag16(const float *Ks, int k0, int dt, int l
 #pragma unroll
     for (int j = 0; j < 4; ++j) f.v[j] = Ks[kq_off<DT, DK, C, NW>(k0 + 4 * g + j, col)];
 }
-template <typename DT, int DK, int C, int NW, typename F8>
-__device__ __forceinline__ void kt_frag32(const DT *Ks, int k0, int dt, int lane, F8 &f) {
-    typename Frag<DT>::k16 lo, hi;
+template <typename DT, int DK, int C, int NW>
+__device__ __forceinline__ void kt_frag32(const __bf16 *Ks, int k0, int dt, int lane, bf16x8 &f) {
+    bf16x4 lo, hi;
+    kt_frag16<DT, DK, C, NW>(Ks, k0, dt, lane, lo);
+    kt_frag16<DT, DK, C, NW>(Ks, k0 + 16, dt, lane, hi);
+    f = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+template <typename DT, int DK, int C, int NW>
+__device__ __forceinline__ void kt_frag32(const float *Ks, int k0, int dt, int lane, f32x8_arr &f) {
+    f32x4_arr lo, hi;
     kt_frag16<DT, DK, C, NW>(Ks, k0, dt, lane, lo);
     kt_frag16<DT, DK, C, NW>(Ks, k0 + 16, dt, lane, hi);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        frag_set(f, j, frag_get(lo, j));
-        frag_set(f, 4 + j, frag_get(hi, j));
+        f.v[j] = lo.v[j];
+        f.v[4 + j] = hi.v[j];
     }
 }
 
@@ -217,8 +224,10 @@ __device__ __forceinline__ void gram_tiles(const DT *Ks, const DT *Qs, const flo
                 const int col = 16 * tj + 4 * g;  // columns col .. col+3 of row
                 if (isP) {
                     typename Frag<DT>::k16 out;
+                    f32x4 m;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) frag_set(out, e, row >= col + e ? acc[e] : 0.f);
+                    for (int e = 0; e < 4; ++e) m[e] = row >= col + e ? acc[e] : 0.f;
+                    cvt4(m, out);
                     store_frag16(Ps + row * G::LDP + p_col<G::KSC>(col), out);
                 } else {
                     f32x4 out;
@@ -252,10 +261,15 @@ template <typename DT, int LDA>
 __device__ __forceinline__ void af_rows(const float *Af, int row0, int col0, int lane,
                                         typename Frag<DT>::k16 &f) {
     const int g = lane >> 4, r = lane & 15;
-    float a4[4];
-    load4(Af + (row0 + r) * LDA + col0 + 4 * g, a4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) frag_set(f, e, a4[e]);
+    cvt4(*reinterpret_cast<const f32x4 *>(Af + (row0 + r) * LDA + col0 + 4 * g), f);
+}
+
+// Fresh 16x16 product A * B (16-wide k).
+template <typename F>
+__device__ __forceinline__ f32x4 mm16(const F &a, const F &b) {
+    f32x4 acc = zero4();
+    mma_k16(acc, a, b);
+    return acc;
 }
 
 template <typename DT, int DK, int C, int NW>
@@ -292,8 +306,7 @@ __device__ __forceinline__ void diag_inverse(const float *Af, DT *TsT, int d, in
         const bool keep = (r / (2 * h) == (4 * g) / (2 * h)) && (r % (2 * h) >= h) &&
                           ((4 * g) % (2 * h) < h);
         F fa, fT, fTt, fM;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) frag_set(fa, e, keep ? ar[e] : 0.f);
+        cvt4(keep ? f32x4{ar[0], ar[1], ar[2], ar[3]} : zero4(), fa);
         frag_from_acc16(Tm, fT);
         frag_from_acc16(Tt, fTt);
         f32x4 M = zero4(), P = zero4(), Pt = zero4();
@@ -323,95 +336,77 @@ __device__ __forceinline__ void offdiag_inverse(const float *Af, DT *TsT, int wa
     auto aA = [&](int k, int l, F &f) { af_rows<DT, LDA>(Af, 16 * k, 16 * l, lane, f); };
     auto store = [&](int i, int j, const f32x4 &D) {  // D = D layout of -T_ij
         F out;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) frag_set(out, e, -D[e]);
+        cvt4(-D, out);
         store_frag16(TsT + (16 * j + r) * LDT + 16 * i + 4 * g, out);
     };
+    // Every job loads all of its operands before its first product (the
+    // scheduling barrier keeps the loads from sinking to their uses), then
+    // runs its chain of products.  X_ij denotes -T_ij.
     if constexpr (NT == 2) {
         if (wave != 0) return;
-        F fa, fb, ft, fn;
-        aA(1, 0, fa); tB(0, 0, fb); tA(1, 1, ft);
-        f32x4 N = zero4(), X = zero4();
-        mma_k16(N, fa, fb);
-        frag_from_acc16(N, fn);
-        mma_k16(X, ft, fn);
-        store(1, 0, X);
+        F a10, t00, t11r;
+        aA(1, 0, a10); tB(0, 0, t00); tA(1, 1, t11r);
+        __builtin_amdgcn_sched_barrier(0);
+        F n;
+        cvt4(mm16(a10, t00), n);
+        store(1, 0, mm16(t11r, n));                       // X10 = T11 A10 T00
     } else if constexpr (NT == 4) {
 #pragma unroll
         for (int job = 0; job < 4; ++job) {
             if (job % NW != wave) continue;
-            // X10 = -T10 = T11 (A10 T00) and X32 = -T32 = T33 (A32 T22) with
-            // the D layout of X32^T (rows of X32 as an A operand)
-            const bool need10 = job == 0 || job == 3, need32 = job == 2 || job == 3;
-            F fT11, fT33, fT00, fT11b, fX10, fX32r;
-            f32x4 X10 = zero4(), X32 = zero4(), X32t = zero4();
-            tA(3, 3, fT33);
-            if (need10) {
-                F fa, fb, fn;
-                aA(1, 0, fa); tB(0, 0, fb); tA(1, 1, fT11);
-                f32x4 N = zero4();
-                mma_k16(N, fa, fb);
-                frag_from_acc16(N, fn);
-                mma_k16(X10, fT11, fn);
-                frag_from_acc16(X10, fX10);  // -T10 as B operand
-                fT00 = fb;
-                if (job == 0) store(1, 0, X10);
-            }
-            if (need32) {
-                F fa, fb, fn;
-                aA(3, 2, fa); tB(2, 2, fb);
-                f32x4 N = zero4();
-                mma_k16(N, fa, fb);
-                frag_from_acc16(N, fn);
-                mma_k16(X32, fT33, fn);
-                mma_k16(X32t, fn, fT33);
-                frag_from_acc16(X32t, fX32r);  // rows of -T32 as A operand
-                if (job == 2) store(3, 2, X32);
-            }
-            if (job == 1 || job == 2) tB(1, 1, fT11b);
-            // M_k = sum_l A_kl T_lj for k = 2, 3; then T_ij = -sum_k T_ik M_k
-            if (job == 0 || job == 1) {  // T20, T21 = -T22 M_2
-                F fa, fm, fT22;
-                f32x4 M2 = zero4(), Y = zero4();
-                if (job == 0) {
-                    aA(2, 0, fa); mma_k16(M2, fa, fT00);
-                    // + A21 T10 = - A21 X10
-                    F fa1; aA(2, 1, fa1);
-                    f32x4 Mneg = zero4();
-                    mma_k16(Mneg, fa1, fX10);
-                    M2 -= Mneg;
-                } else {
-                    aA(2, 1, fa); mma_k16(M2, fa, fT11b);
-                }
-                frag_from_acc16(M2, fm);
-                tA(2, 2, fT22);
-                mma_k16(Y, fT22, fm);
-                store(2, job, Y);
-            } else {  // T31 (job 2), T30 (job 3) = -(T32 M_2 + T33 M_3)
-                F fa2, fa3, fm2, fm3;
-                f32x4 M2 = zero4(), M3 = zero4(), Y = zero4();
-                if (job == 2) {
-                    aA(2, 1, fa2); mma_k16(M2, fa2, fT11b);
-                    aA(3, 1, fa3); mma_k16(M3, fa3, fT11b);
-                } else {
-                    F fb0, fa21, fa31;
-                    aA(2, 0, fa2); aA(3, 0, fa3); aA(2, 1, fa21); aA(3, 1, fa31);
-                    mma_k16(M2, fa2, fT00);
-                    mma_k16(M3, fa3, fT00);
-                    f32x4 N2 = zero4(), N3 = zero4();  // A_k1 X10 = -A_k1 T10
-                    mma_k16(N2, fa21, fX10);
-                    mma_k16(N3, fa31, fX10);
-                    M2 -= N2;
-                    M3 -= N3;
-                }
-                frag_from_acc16(M2, fm2);
-                frag_from_acc16(M3, fm3);
-                // -T_i? = -(T32 M2 + T33 M3) = X32 M2 - T33 M3
-                f32x4 Y32 = zero4();
-                mma_k16(Y32, fX32r, fm2);
-                mma_k16(Y, fT33, fm3);
-                Y -= Y32;
-                store(3, job == 2 ? 1 : 0, Y);
+            if (job == 0) {  // T10, T20
+                F a10, a20, a21, t00, t11r, t22r;
+                aA(1, 0, a10); aA(2, 0, a20); aA(2, 1, a21);
+                tB(0, 0, t00); tA(1, 1, t11r); tA(2, 2, t22r);
+                __builtin_amdgcn_sched_barrier(0);
+                F n, t10, m2;
+                cvt4(mm16(a10, t00), n);
+                const f32x4 X10 = mm16(t11r, n);
+                store(1, 0, X10);
+                cvt4(-X10, t10);
+                f32x4 M2 = mm16(a20, t00);                // A20 T00 + A21 T10
+                mma_k16(M2, a21, t10);
+                cvt4(M2, m2);
+                store(2, 0, mm16(t22r, m2));              // X20 = T22 M2
+            } else if (job == 1) {  // T21
+                F a21, t11, t22r, m2;
+                aA(2, 1, a21); tB(1, 1, t11); tA(2, 2, t22r);
+                __builtin_amdgcn_sched_barrier(0);
+                cvt4(mm16(a21, t11), m2);                  // A21 T11
+                store(2, 1, mm16(t22r, m2));               // X21 = T22 M2
+            } else if (job == 2) {  // T32, T31
+                F a32, a21, a31, t22, t11, t33r;
+                aA(3, 2, a32); aA(2, 1, a21); aA(3, 1, a31);
+                tB(2, 2, t22); tB(1, 1, t11); tA(3, 3, t33r);
+                __builtin_amdgcn_sched_barrier(0);
+                F n, t32r, m2, m3;
+                cvt4(mm16(a32, t22), n);
+                store(3, 2, mm16(t33r, n));                // X32 = T33 A32 T22
+                cvt4(-mm16(n, t33r), t32r);                // rows of T32 (D layout of T32^T)
+                cvt4(mm16(a21, t11), m2);
+                cvt4(mm16(a31, t11), m3);
+                f32x4 Y = mm16(t32r, m2);                  // T32 M2 + T33 M3 = X31
+                mma_k16(Y, t33r, m3);
+                store(3, 1, Y);
+            } else {  // T30, recomputing T10 and T32
+                F a10, a32, a20, a21, a30, a31, t00, t22, t11r, t33r;
+                aA(1, 0, a10); aA(3, 2, a32); aA(2, 0, a20);
+                aA(2, 1, a21); aA(3, 0, a30); aA(3, 1, a31);
+                tB(0, 0, t00); tB(2, 2, t22); tA(1, 1, t11r); tA(3, 3, t33r);
+                __builtin_amdgcn_sched_barrier(0);
+                F n1, n3, t10, t32r, m2, m3;
+                cvt4(mm16(a10, t00), n1);
+                cvt4(mm16(a32, t22), n3);
+                cvt4(-mm16(t11r, n1), t10);               // T10
+                cvt4(-mm16(n3, t33r), t32r);               // rows of T32
+                f32x4 M2 = mm16(a20, t00), M3 = mm16(a30, t00);
+                mma_k16(M2, a21, t10);
+                mma_k16(M3, a31, t10);
+                cvt4(M2, m2);
+                cvt4(M3, m3);
+                f32x4 Y = mm16(t32r, m2);                  // T32 M2 + T33 M3 = X30
+                mma_k16(Y, t33r, m3);
+                store(3, 0, Y);
             }
         }
     }
@@ -704,7 +699,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     constexpr int NT = G::NT, ND = G::ND;
     __shared__ __attribute__((aligned(16))) PipeSmem<DT, DK, C, NW> sm;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
     const int g = lane >> 4, r = lane & 15;
     const HeadPtrs<DT> p = head_ptrs<DT, DK, NW>(q, k, v, beta, o, T, H, Dv, nvt, wave, r);
 
@@ -796,7 +792,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     constexpr int NT = G::NT, ND = G::ND;
     __shared__ __attribute__((aligned(16))) SerialSmem<DT, DK, C, NW> sm;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
     const int g = lane >> 4, r = lane & 15;
     const HeadPtrs<DT> p = head_ptrs<DT, DK, NW>(q, k, v, beta, o, T, H, Dv, nvt, wave, r);
 

@@ -202,13 +202,23 @@ __device__ __forceinline__ int state_col(int dt, int g) {
 // B operand in chunk order from state tiles 2s, 2s + 1 (32-wide slab): lane
 // (g, r) needs keys 32s + 8g + 0..7, i.e. the tile holding the lower half
 // first (see state_col).
-template <typename F>
-__device__ __forceinline__ void frag_from_state(const f32x4 &t0, const f32x4 &t1, int g, F &f) {
+__device__ __forceinline__ void frag_from_state(const f32x4 &t0, const f32x4 &t1, int g,
+                                                bf16x8 &f) {
+    // narrow first, then swap the packed halves (4 selects instead of 8)
+    typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+    const u32x2 a = __builtin_bit_cast(u32x2, __builtin_convertvector(t0, bf16x4));
+    const u32x2 b = __builtin_bit_cast(u32x2, __builtin_convertvector(t1, bf16x4));
+    const bool odd = g & 1;
+    const u32x2 lo = odd ? b : a, hi = odd ? a : b;
+    f = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3));
+}
+__device__ __forceinline__ void frag_from_state(const f32x4 &t0, const f32x4 &t1, int g,
+                                                f32x8_arr &f) {
     const bool odd = g & 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        frag_set(f, i, odd ? t1[i] : t0[i]);
-        frag_set(f, 4 + i, odd ? t0[i] : t1[i]);
+        f.v[i] = odd ? t1[i] : t0[i];
+        f.v[4 + i] = odd ? t0[i] : t1[i];
     }
 }
 
@@ -220,20 +230,47 @@ __device__ __forceinline__ void store_frag16(float *p, const f32x4_arr &f) {
     *reinterpret_cast<float4 *>(p) = make_float4(f.v[0], f.v[1], f.v[2], f.v[3]);
 }
 
+// Narrow four fp32 values to a 4-element fragment (bf16: two packed
+// conversions).
+__device__ __forceinline__ void cvt4(const f32x4 &x, bf16x4 &f) {
+    f = __builtin_convertvector(x, bf16x4);
+}
+__device__ __forceinline__ void cvt4(const f32x4 &x, f32x4_arr &f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.v[i] = x[i];
+}
+__device__ __forceinline__ void cvt8(const f32x4 &lo, const f32x4 &hi, bf16x8 &f) {
+    const bf16x4 a = __builtin_convertvector(lo, bf16x4), b = __builtin_convertvector(hi, bf16x4);
+    f = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void cvt8(const f32x4 &lo, const f32x4 &hi, f32x8_arr &f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f.v[i] = lo[i];
+        f.v[4 + i] = hi[i];
+    }
+}
+// Sign flip of a fragment.
+__device__ __forceinline__ bf16x4 neg(const bf16x4 &f) {
+    typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+    return __builtin_bit_cast(bf16x4, __builtin_bit_cast(u32x2, f) ^ 0x80008000u);
+}
+__device__ __forceinline__ f32x4_arr neg(const f32x4_arr &f) {
+    f32x4_arr r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.v[i] = -f.v[i];
+    return r;
+}
+
 // B operand from a stack of D-layout accumulator tiles whose rows run along
 // k: tile k0/16 (and k0/16 + 1 for a 32-wide slab), narrowed to DT.
 template <typename F>
 __device__ __forceinline__ void frag_from_acc32(const f32x4 &t0, const f32x4 &t1, F &f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        frag_set(f, i, t0[i]);
-        frag_set(f, 4 + i, t1[i]);
-    }
+    cvt8(t0, t1, f);
 }
 template <typename F>
 __device__ __forceinline__ void frag_from_acc16(const f32x4 &t0, F &f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) frag_set(f, i, t0[i]);
+    cvt4(t0, f);
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
