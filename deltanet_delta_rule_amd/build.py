@@ -22,10 +22,13 @@ SOURCES = ["abi.cpp", "chunk_fwd.hip", "recurrent_step.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-# Packed fp32 instructions are disabled for all device code.
+# Packed fp32 instructions are disabled for all device code.  MFMA results
+# are allocated in ordinary VGPRs (not the accumulator file), so the VALU
+# reads them without v_accvgpr copies.
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
