@@ -41,7 +41,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published (256 CU x 2.4 GHz x 4096)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_layer_1p3b_traffic.txt")
 KERNEL_SOURCES = ["deltanet_delta_rule_amd/csrc/chunk_fwd.hip",
-                  "deltanet_delta_rule_amd/csrc/dr_common.hpp"]
+                  "deltanet_delta_rule_amd/csrc/dr_common.hpp",
+                  "deltanet_delta_rule_amd/build.py"]  # compile flags
 
 
 def log(*a):
