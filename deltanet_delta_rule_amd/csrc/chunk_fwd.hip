@@ -2,40 +2,41 @@
 //
 // Math (per head; chunk c spans C tokens with incoming state S_c, d_v x d_k):
 //   A   = tril(diag(beta) K K^T, -1)                     chunk key couplings
-//   Ti  = (I + A)^{-1}                                    unit lower-triangular
-//   E   = Ti diag(beta) (V - K S_c^T)                     resolved errors
+//   R   = diag(beta) (V - K S_c^T)                       provisional errors
+//   E   = (I + A)^{-1} R                                 resolved errors
 //   O   = Q S_c^T + (Q K^T (.) M) E                       M incl. the diagonal
 //   S_{c+1} = S_c + E^T K
 // The pieces come from the paperlayer summary of arXiv:2406.06484 (section 3
 // "Parallelizing DeltaNet Across the Sequence Dimension": chunking, the
-// Householder/WY representation, forward substitution for the triangular
-// inverse; App. B.2 "UT transform derivation": T = (I + A)^{-1} diag(beta))
-// and the hada.io digest (section "Chunkwise KDA": provisional errors against
-// the incoming state, the unit lower-triangular solve that restores the causal
-// coupling, the end-of-chunk state as one product and the outputs with the
-// diagonal included; section "Pipeline Triton Chunkwise": 16-token diagonal
-// blocks solved first, then the off-diagonal blocks).  With D = I and no
-// output scale this is plain DeltaNet.  E = U - W S_c^T of the UT form; the
-// kernel applies Ti to the residual instead of forming W = T K and U = T V,
-// which skips the C x C x d_k product for W.
+// Householder/WY representation, forward substitution with the unit
+// lower-triangular matrix; App. B.2 "UT transform derivation": T = (I +
+// A)^{-1} diag(beta)) and the hada.io digest (section "Chunkwise KDA":
+// provisional errors against the incoming state, the unit lower-triangular
+// solve that restores the causal coupling, the end-of-chunk state as one
+// product and the outputs with the diagonal included; section "Pipeline
+// Triton Chunkwise": 16-token diagonal blocks solved first, then the blocks
+// below them).  With D = I and no output scale this is plain DeltaNet.  E is
+// U - W S_c^T of the UT form; the kernel solves for it from the residual
+// instead of forming W = T K and U = T V, which skips the C x C x d_k product
+// for W, and it does the solve by 16-token blocks: the diagonal blocks of
+// (I + A) are inverted once per chunk, and each block of E is one product
+// with its inverse after the blocks above it are subtracted.
 //
 // Work split.  One workgroup owns one (b, h) and a tile of BV = 16*NW value
 // rows of S and walks the chunks in order, so the state never leaves the chip.
-// Wave w owns 16 rows of S as fp32 MFMA accumulators (lane (g, r) holds
-// S[row r][16*dt + 4g + i]).  Rows of S evolve independently, so waves never
-// exchange state: every product on the state path (K S^T, Q S^T, Ti R, P E,
-// K^T E) runs inside one wave from registers, using the D-layout-as-B-operand
-// identity of dr_common.hpp; K^T fragments come from the token-major K tile
-// through the LDS transpose read.  The per-chunk work that does not depend on
-// the state -- the Gram tiles K K^T and Q K^T and the blocked triangular
-// inverse -- is shared by the waves through LDS.
+// A state wave owns 16 rows of S as fp32 MFMA accumulators (lane (g, r) holds
+// S[row r][state_col(dt, g) + i]).  Rows of S evolve independently, so waves
+// never exchange state: every product on the state path (K S^T, S Q^T, the
+// block substitution, E^T P^T, K^T E) runs inside one wave from registers,
+// using the D-layout-as-operand identity of dr_common.hpp; K^T fragments come
+// from the token-major K tile through the LDS transpose read.  The per-chunk
+// work that does not depend on the state -- the Gram tiles K K^T and Q K^T
+// and the inverses of the diagonal blocks of (I + A) -- is shared through LDS.
 //
 // Two kernels implement this:
-//  * chunk_fwd_pipelined_kernel (used whenever its buffers fit in LDS) runs a
-//    two-phase software pipeline with two barriers per chunk:
-//      phase 1: state path of chunk c  +  Gram tiles of chunk c+1
-//      phase 2: triangular inverse of chunk c+1  +  staging of chunk c+2
-//    with K, Q, Ti, P double-buffered and chunk c+3 loading into registers.
+//  * chunk_fwd_ws_kernel (used whenever its buffers fit in LDS) pairs each
+//    state wave with a preparation wave on the same SIMD, with one barrier
+//    per chunk;
 //  * chunk_fwd_serial_kernel runs the same steps one after the other on single
 //    buffers (fp32 inputs with large d_k * chunk, whose double buffers would
 //    exceed the 160 KiB of LDS).
@@ -74,13 +75,11 @@ struct ChunkCfg {
     static constexpr bool SWZ = sizeof(DT) == 2 && DK >= 32;
     static constexpr int LDK = SWZ ? DK : DK + PADE;   // K, Q
     static constexpr int LDP = C + 2 * PADE;    // P (row fragments)
-    static constexpr int LDT = C + 2 * PADE;    // Ti^T (transpose reads)
     static constexpr int LDA = C + 8;           // A (fp32)
     static constexpr int VEC = Vec16<DT>::N;    // elements per 16-byte load
     static constexpr int VPR = DK / VEC;        // 16-byte vectors per K row
     static constexpr int NTHR = 64 * NW;
     static constexpr int NPRE = (C * VPR + NTHR - 1) / NTHR;  // vectors/thread
-    static constexpr int NTILE = NT * (NT + 1) / 2;          // lower 16x16 tiles
     static constexpr int LDV = BV + 2 * PADE;   // V tile (transpose reads)
     static constexpr int VPRV = BV / VEC;       // 16-byte vectors per V tile row
     static constexpr int NPREV = (C * VPRV + NTHR - 1) / NTHR;  // V vectors/thread
@@ -178,48 +177,92 @@ __device__ __forceinline__ void kt_frag32(const float *Ks, int k0, int dt, int l
 }
 
 // ---------------------------------------------------------------------------
-// Per-chunk building blocks shared by both kernels.
+// Per-chunk building blocks
 // ---------------------------------------------------------------------------
 
-// Gram tiles of one chunk:
-//   Af[i][j] = beta_i (K K^T)_ij for i > j, else 0      (fp32)
-//   Ps[i][j] = (Q K^T)_ij for i >= j, else 0             (DT)
+// Fragment blocks.  A 16x16 matrix that some wave uses as a 16-wide MFMA
+// operand is kept in LDS "fragment-major": lane l's four elements at
+// 4l .. 4l+3, so writing and reading a block are both one linear 8-byte (bf16)
+// or 16-byte (fp32) access per lane.  Block (i, j) of the strictly lower
+// couplings, i > j, is block number i(i-1)/2 + j.
+constexpr int off_idx(int i, int j) { return i * (i - 1) / 2 + j; }
+constexpr int FRAG_ELEMS = 256;  // 64 lanes x 4 elements
+
+template <typename DT>
+__device__ __forceinline__ void store_fragblk(DT *base, int blk, int lane, const f32x4 &x) {
+    typename Frag<DT>::k16 f;
+    cvt4(x, f);
+    store_frag16(base + blk * FRAG_ELEMS + 4 * lane, f);
+}
+template <typename DT>
+__device__ __forceinline__ void load_fragblk(const DT *base, int blk, int lane,
+                                             typename Frag<DT>::k16 &f) {
+    load_chunk(base + blk * FRAG_ELEMS + 4 * lane, f);
+}
+
+// Gram tiles of one chunk, for the rows of the Gram jobs of wave W:
+//   A-row job ti:  A = beta_i (K K^T)_ij for i > j.  The diagonal tile goes to
+//                  Af (fp32, strictly lower, zeros elsewhere) for the
+//                  diagonal inverse; tiles left of it go to Ab as fragment
+//                  blocks of -A, the A operands of the block substitution.
+//   P-row job ti:  P = (Q K^T)_ij for i >= j into Ps (DT, masked).
 // Each 16x16 tile (ti, tj) is computed transposed, D = K_tj X_ti^T (X = K or
-// Q), so lane (g, r) ends up with row 16ti + r, columns 16tj + 4g .. + 3: one
-// vector store per tile.  Work comes in row jobs: the A-row of tile row ti
-// goes to wave ti % NW and the P-row to wave (NT-1-ti) % NW, so with NW = NT
-// every wave computes NT+1 tiles.  A job loads all its operand fragments
-// before its first MFMA.  Upper tiles of Ps stay zero.
-template <typename DT, int DK, int C, int NW>
-__device__ __forceinline__ void gram_tiles(const DT *Ks, const DT *Qs, const float *betas,
-                                           float *Af, DT *Ps, int wave, int lane) {
+// Q), so lane (g, r) ends up with row 16ti + r, columns 16tj + 4g .. + 3:
+// exactly the A-operand fragment of that tile.  The A-row of tile row ti goes
+// to wave ti % NW and the P-row to wave (NT-1-ti) % NW (with NW = NT every
+// wave computes NT+1 tiles).  The assignment is fixed at compile time per
+// wave; a wave loads every K tile its jobs touch once, plus the Q tiles of its
+// P rows, all before its first MFMA, and does its A rows first so that its
+// diagonal inverse can start early.
+template <int NT, int NW, int W>
+struct GramJobs {
+    static constexpr bool a_row(int ti) { return ti % NW == W; }
+    static constexpr bool p_row(int ti) { return (NT - 1 - ti) % NW == W; }
+    static constexpr int kmax() {
+        int m = -1;
+        for (int ti = 0; ti < NT; ++ti)
+            if (a_row(ti) || p_row(ti)) m = ti;
+        return m;
+    }
+};
+
+template <typename DT, int DK, int C, int NW, int W>
+__device__ __forceinline__ void gram_tiles_w(const DT *Ks, const DT *Qs, const float *betas,
+                                             float *Af, DT *Ab, DT *Ps, int lane) {
     typedef ChunkCfg<DT, DK, C, NW> G;
-    constexpr int NT = G::NT, KSD = G::KSD, NSD = DK / KSD;
+    typedef GramJobs<G::NT, NW, W> J;
+    constexpr int NT = G::NT, KSD = G::KSD, NSD = DK / KSD, KM = J::kmax();
     typedef typename SlabFrag<KSD == 32, DT>::type FD;
     const int g = lane >> 4, r = lane & 15;
+    FD fk[NT][NSD], fq[NT][NSD];
 #pragma unroll
-    for (int ti = 0; ti < NT; ++ti) {
+    for (int tj = 0; tj < NT; ++tj)
+        if (tj <= KM)
 #pragma unroll
-        for (int isP = 0; isP < 2; ++isP) {
-            const int owner = isP ? (NT - 1 - ti) % NW : ti % NW;
-            if (owner != wave) continue;
-            FD fx[NSD], fk[NT][NSD];
+            for (int s = 0; s < NSD; ++s) kq_rows<DT, DK, C, NW>(Ks, 16 * tj, s * KSD, lane, fk[tj][s]);
 #pragma unroll
-            for (int s = 0; s < NSD; ++s) kq_rows<DT, DK, C, NW>(isP ? Qs : Ks, 16 * ti, s * KSD, lane, fx[s]);
+    for (int ti = 0; ti < NT; ++ti)
+        if (J::p_row(ti))
 #pragma unroll
-            for (int tj = 0; tj <= ti; ++tj)
+            for (int s = 0; s < NSD; ++s) kq_rows<DT, DK, C, NW>(Qs, 16 * ti, s * KSD, lane, fq[ti][s]);
+    float brow[NT];
 #pragma unroll
-                for (int s = 0; s < NSD; ++s)
-                    kq_rows<DT, DK, C, NW>(Ks, 16 * tj, s * KSD, lane, fk[tj][s]);
+    for (int ti = 0; ti < NT; ++ti)
+        if (J::a_row(ti)) brow[ti] = betas[16 * ti + r];
+#pragma unroll
+    for (int isP = 0; isP < 2; ++isP)
+#pragma unroll
+        for (int ti = 0; ti < NT; ++ti) {
+            if (!(isP ? J::p_row(ti) : J::a_row(ti))) continue;
             const int row = 16 * ti + r;
-            const float brow = betas[row];
 #pragma unroll
             for (int tj = 0; tj <= ti; ++tj) {
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int s = 0; s < NSD; ++s) {
-                    if constexpr (KSD == 32) mma_k32(acc, fk[tj][s], fx[s]);
-                    else mma_k16(acc, fk[tj][s], fx[s]);
+                    const FD &x = isP ? fq[ti][s] : fk[ti][s];
+                    if constexpr (KSD == 32) mma_k32(acc, fk[tj][s], x);
+                    else mma_k16(acc, fk[tj][s], x);
                 }
                 const int col = 16 * tj + 4 * g;  // columns col .. col+3 of row
                 if (isP) {
@@ -229,42 +272,38 @@ __device__ __forceinline__ void gram_tiles(const DT *Ks, const DT *Qs, const flo
                     for (int e = 0; e < 4; ++e) m[e] = row >= col + e ? acc[e] : 0.f;
                     cvt4(m, out);
                     store_frag16(Ps + row * G::LDP + p_col<G::KSC>(col), out);
-                } else {
+                } else if (tj == ti) {
                     f32x4 out;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) out[e] = row > col + e ? brow * acc[e] : 0.f;
+                    for (int e = 0; e < 4; ++e) out[e] = row > col + e ? brow[ti] * acc[e] : 0.f;
                     *reinterpret_cast<f32x4 *>(Af + row * G::LDA + col) = out;
+                } else {
+                    store_fragblk(Ab, off_idx(ti, tj), lane, -brow[ti] * acc);
                 }
             }
         }
+}
+
+template <typename DT, int DK, int C, int NW>
+__device__ __forceinline__ void gram_tiles(const DT *Ks, const DT *Qs, const float *betas,
+                                           float *Af, DT *Ab, DT *Ps, int wave, int lane) {
+    switch (wave) {
+    case 0: gram_tiles_w<DT, DK, C, NW, 0>(Ks, Qs, betas, Af, Ab, Ps, lane); break;
+    case 1: if constexpr (NW > 1) gram_tiles_w<DT, DK, C, NW, 1>(Ks, Qs, betas, Af, Ab, Ps, lane); break;
+    case 2: if constexpr (NW > 2) gram_tiles_w<DT, DK, C, NW, 2>(Ks, Qs, betas, Af, Ab, Ps, lane); break;
+    default: if constexpr (NW > 3) gram_tiles_w<DT, DK, C, NW, 3>(Ks, Qs, betas, Af, Ab, Ps, lane); break;
     }
 }
 
-// Ti = (I + A)^{-1}, stored transposed: TsT[col][row] = Ti[row][col] (Ti is
-// unit lower-triangular, so TsT is upper-triangular; its lower blocks stay
-// zero).  Blocked forward substitution by doubling: if T inverts the diagonal
-// blocks of size h of (I + A) and A_h holds the entries of A in the blocks of
-// size h just below them (rows in the upper half, columns in the lower half
-// of each diagonal block of size 2h), then T - T A_h T inverts the diagonal
-// blocks of size 2h, since (T A_h)^2 = 0.
-//  1. diag_inverse: the 4x4 diagonal blocks by substitution (VALU), then
-//     sizes 8 and 16 by doubling on the MFMA units.  A wave inverts the
-//     diagonal 16-blocks of the Gram row jobs it owns, right after computing
-//     them, so it reads back only its own A tiles.
-//  2. offdiag_inverse: sizes 32 and 64 by doubling over 16-blocks, after a
-//     barrier.  For a 64-token chunk the six new blocks are split into four
-//     self-contained jobs, each recomputing the size-32 blocks it needs.
-
-// A-operand rows of an Af tile (fp32 LDS) narrowed to DT: lane (g, r) takes
-// Af[row0 + r][col0 + 4g .. + 3].
-template <typename DT, int LDA>
-__device__ __forceinline__ void af_rows(const float *Af, int row0, int col0, int lane,
-                                        typename Frag<DT>::k16 &f) {
-    const int g = lane >> 4, r = lane & 15;
-    cvt4(*reinterpret_cast<const f32x4 *>(Af + (row0 + r) * LDA + col0 + 4 * g), f);
-}
-
-// Fresh 16x16 product A * B (16-wide k).
+// Inverse T_dd = (I + A_dd)^{-1} of diagonal block d of the couplings (unit
+// lower-triangular).  Blocked forward substitution by doubling: if T inverts
+// the diagonal blocks of size h of (I + A) and A_h holds the entries of A in
+// the blocks of size h just below them (rows in the upper half, columns in
+// the lower half of each diagonal block of size 2h), then T - T A_h T
+// inverts the diagonal blocks of size 2h, since (T A_h)^2 = 0.  The 4x4
+// blocks are solved on the VALU, sizes 8 and 16 by that step on the MFMA
+// units.  The result goes to Tb as the fragment block of T_dd as an A
+// operand.
 template <typename F>
 __device__ __forceinline__ f32x4 mm16(const F &a, const F &b) {
     f32x4 acc = zero4();
@@ -273,10 +312,10 @@ __device__ __forceinline__ f32x4 mm16(const F &a, const F &b) {
 }
 
 template <typename DT, int DK, int C, int NW>
-__device__ __forceinline__ void diag_inverse(const float *Af, DT *TsT, int d, int lane) {
+__device__ __forceinline__ void diag_inverse(const float *Af, DT *Tb, int d, int lane) {
     typedef ChunkCfg<DT, DK, C, NW> G;
     typedef typename Frag<DT>::k16 F;
-    constexpr int LDA = G::LDA, LDT = G::LDT;
+    constexpr int LDA = G::LDA;
     const int g = lane >> 4, r = lane & 15, c = r & 3;
     const int o = 16 * d;
     // Size 4: lane (g, r) with r / 4 == g takes 4x4 block g and solves for
@@ -317,233 +356,198 @@ __device__ __forceinline__ void diag_inverse(const float *Af, DT *TsT, int d, in
         Tm -= P;
         Tt -= Pt;
     }
-    // lane (g, r) holds Ti[o + 4g + i][o + r] = TsT[o + r][o + 4g + i]
-    F out;
-    frag_from_acc16(Tm, out);
-    store_frag16(TsT + (o + r) * LDT + o + 4 * g, out);
+    // lane (g, r) holds T^T[4g + i][r] = T[r][4g + i]: row r, columns 4g ..
+    // 4g + 3, the A-operand fragment of T_dd
+    store_fragblk(Tb, d, lane, Tt);
 }
 
-template <typename DT, int DK, int C, int NW>
-__device__ __forceinline__ void offdiag_inverse(const float *Af, DT *TsT, int wave, int lane) {
-    typedef ChunkCfg<DT, DK, C, NW> G;
-    typedef typename Frag<DT>::k16 F;
-    constexpr int NT = G::NT, LDA = G::LDA, LDT = G::LDT;
-    const int g = lane >> 4, r = lane & 15;
-    // T_lj as B operand (lane (g, r): T_lj[4g + e][r] = TsT[16j + r][16l + 4g + e])
-    auto tB = [&](int l, int j, F &f) { load_chunk(TsT + (16 * j + r) * LDT + 16 * l + 4 * g, f); };
-    // rows of T_ik as A operand (lane (g, r): T_ik[r][4g + e] = TsT[16k + 4g + e][16i + r])
-    auto tA = [&](int i, int k, F &f) { frag_cols16(TsT, LDT, 16 * k, 16 * i, lane, f); };
-    auto aA = [&](int k, int l, F &f) { af_rows<DT, LDA>(Af, 16 * k, 16 * l, lane, f); };
-    auto store = [&](int i, int j, const f32x4 &D) {  // D = D layout of -T_ij
-        F out;
-        cvt4(-D, out);
-        store_frag16(TsT + (16 * j + r) * LDT + 16 * i + 4 * g, out);
-    };
-    // Every job loads all of its operands before its first product (the
-    // scheduling barrier keeps the loads from sinking to their uses), then
-    // runs its chain of products.  X_ij denotes -T_ij.
-    if constexpr (NT == 2) {
-        if (wave != 0) return;
-        F a10, t00, t11r;
-        aA(1, 0, a10); tB(0, 0, t00); tA(1, 1, t11r);
-        __builtin_amdgcn_sched_barrier(0);
-        F n;
-        cvt4(mm16(a10, t00), n);
-        store(1, 0, mm16(t11r, n));                       // X10 = T11 A10 T00
-    } else if constexpr (NT == 4) {
-#pragma unroll
-        for (int job = 0; job < 4; ++job) {
-            if (job % NW != wave) continue;
-            if (job == 0) {  // T10, T20
-                F a10, a20, a21, t00, t11r, t22r;
-                aA(1, 0, a10); aA(2, 0, a20); aA(2, 1, a21);
-                tB(0, 0, t00); tA(1, 1, t11r); tA(2, 2, t22r);
-                __builtin_amdgcn_sched_barrier(0);
-                F n, t10, m2;
-                cvt4(mm16(a10, t00), n);
-                const f32x4 X10 = mm16(t11r, n);
-                store(1, 0, X10);
-                cvt4(-X10, t10);
-                f32x4 M2 = mm16(a20, t00);                // A20 T00 + A21 T10
-                mma_k16(M2, a21, t10);
-                cvt4(M2, m2);
-                store(2, 0, mm16(t22r, m2));              // X20 = T22 M2
-            } else if (job == 1) {  // T21
-                F a21, t11, t22r, m2;
-                aA(2, 1, a21); tB(1, 1, t11); tA(2, 2, t22r);
-                __builtin_amdgcn_sched_barrier(0);
-                cvt4(mm16(a21, t11), m2);                  // A21 T11
-                store(2, 1, mm16(t22r, m2));               // X21 = T22 M2
-            } else if (job == 2) {  // T32, T31
-                F a32, a21, a31, t22, t11, t33r;
-                aA(3, 2, a32); aA(2, 1, a21); aA(3, 1, a31);
-                tB(2, 2, t22); tB(1, 1, t11); tA(3, 3, t33r);
-                __builtin_amdgcn_sched_barrier(0);
-                F n, t32r, m2, m3;
-                cvt4(mm16(a32, t22), n);
-                store(3, 2, mm16(t33r, n));                // X32 = T33 A32 T22
-                cvt4(-mm16(n, t33r), t32r);                // rows of T32 (D layout of T32^T)
-                cvt4(mm16(a21, t11), m2);
-                cvt4(mm16(a31, t11), m3);
-                f32x4 Y = mm16(t32r, m2);                  // T32 M2 + T33 M3 = X31
-                mma_k16(Y, t33r, m3);
-                store(3, 1, Y);
-            } else {  // T30, recomputing T10 and T32
-                F a10, a32, a20, a21, a30, a31, t00, t22, t11r, t33r;
-                aA(1, 0, a10); aA(3, 2, a32); aA(2, 0, a20);
-                aA(2, 1, a21); aA(3, 0, a30); aA(3, 1, a31);
-                tB(0, 0, t00); tB(2, 2, t22); tA(1, 1, t11r); tA(3, 3, t33r);
-                __builtin_amdgcn_sched_barrier(0);
-                F n1, n3, t10, t32r, m2, m3;
-                cvt4(mm16(a10, t00), n1);
-                cvt4(mm16(a32, t22), n3);
-                cvt4(-mm16(t11r, n1), t10);               // T10
-                cvt4(-mm16(n3, t33r), t32r);               // rows of T32
-                f32x4 M2 = mm16(a20, t00), M3 = mm16(a30, t00);
-                mma_k16(M2, a21, t10);
-                mma_k16(M3, a31, t10);
-                cvt4(M2, m2);
-                cvt4(M3, m3);
-                f32x4 Y = mm16(t32r, m2);                  // T32 M2 + T33 M3 = X30
-                mma_k16(Y, t33r, m3);
-                store(3, 0, Y);
-            }
-        }
-    }
-}
-
-// State path of one chunk for this wave's 16 rows of S:
-//   X = K S^T, Y = Q S^T, R = diag(beta)(V - X), E = Ti R,
-//   S^T += K^T E, O = Y + P E (stored for tokens < len).
 // Output rows of one chunk: a buffer resource over the chunk's valid tokens,
-// this lane's byte offset (its value column, rows 4g..) and the token stride.
+// this lane's byte offset (its token row r and value columns 4g ..) and the
+// token stride.
 struct OutChunk {
     __amdgpu_buffer_rsrc_t rsrc;
     int voff, row_bytes;
 };
 
-// Operand fragments are loaded into registers ahead of their MFMAs: the Ti
-// and P rows first (they do not depend on the state), the K and Q slabs of
-// X and Y one slab ahead, the K^T fragments while X and Y run.
+// Four consecutive output elements of one token row (8 bytes for bf16, 16 for
+// fp32); stores outside the resource are dropped by its range check.
+__device__ __forceinline__ void store_out4(const f32x4 &x, const OutChunk &out, int soff) {
+    bf16x4 f;
+    cvt4(x, f);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, f),
+                                          out.rsrc, out.voff, soff, 0);
+}
+__device__ __forceinline__ void store_out4_f32(const f32x4 &x, const OutChunk &out, int soff) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, x),
+                                           out.rsrc, out.voff, soff, 0);
+}
+
+// The state path of one chunk for this wave's 16 rows of S, in two halves so
+// that a pipeline can put the products over d_k of the next chunk right after
+// the state update of this one:
+//   state_xy:   X = K S^T (tokens x rows), Y = S Q^T (rows x tokens)
+//   state_rest: R = diag(beta)(V - X), E by block forward substitution,
+//               S^T += K^T E, O^T = Y + E^T P^T (stored for valid tokens)
+// Y and the output are computed transposed so that a lane holds four
+// consecutive value columns of one token, which it stores with one access.
 template <typename DT, int DK, int C, int NW>
-__device__ __forceinline__ void state_path(const DT *Ks, const DT *Qs, const DT *Vs,
-                                           const DT *TsT, const DT *Ps, const float *betas,
-                                           f32x4 *Sacc, const OutChunk &out, int wave,
-                                           int lane) {
+__device__ __forceinline__ void state_xy(const DT *Ks, const DT *Qs, const f32x4 *Sacc,
+                                         f32x4 *X, f32x4 *Y, int lane) {
     typedef ChunkCfg<DT, DK, C, NW> G;
-    constexpr int NT = G::NT, ND = G::ND, KSD = G::KSD, KSC = G::KSC;
-    constexpr int NSD = DK / KSD, NSC = C / KSC;
+    constexpr int NT = G::NT, KSD = G::KSD;
+    constexpr int NSD = DK / KSD;
     typedef typename SlabFrag<KSD == 32, DT>::type FD;
-    typedef typename SlabFrag<KSC == 32, DT>::type FC;
     const int g = lane >> 4;
-
-    FC fT[NT][NSC], fP[NT][NSC];
-#pragma unroll
-    for (int mt = 0; mt < NT; ++mt)
-#pragma unroll
-        for (int s = 0; s < NSC; ++s)
-            if (s * KSC < 16 * (mt + 1)) {  // Ti and P are lower-triangular
-                // Ti row fragment = column fragment of Ti^T
-                if constexpr (KSC == 32) frag_cols32(TsT, G::LDT, s * KSC, 16 * mt, lane, fT[mt][s]);
-                else frag_cols16(TsT, G::LDT, s * KSC, 16 * mt, lane, fT[mt][s]);
-                p_rows<DT, DK, C, NW>(Ps, 16 * mt, s * KSC, lane, fP[mt][s]);
-            }
-    float bcur[NT][4];
-#pragma unroll
-    for (int mt = 0; mt < NT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bcur[mt][i] = betas[16 * mt + 4 * g + i];
-    // this wave's V columns in D layout: lane (g, r) takes V[16mt + 4g + j][16w + r]
-    typename Frag<DT>::k16 fv[NT];
-#pragma unroll
-    for (int mt = 0; mt < NT; ++mt) frag_cols16(Vs, G::LDV, 16 * mt, 16 * wave, lane, fv[mt]);
-
-    // X = K S^T, Y = Q S^T
-    f32x4 X[NT], Y[NT];
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt) X[mt] = Y[mt] = zero4();
-    FD fk[2][NT], fq[2][NT];
+    // All operand fragments are loaded before the first MFMA when they fit in
+    // 128 VGPRs; otherwise they are double-buffered one slab ahead.
+    constexpr bool ALL = 2 * NSD * NT * sizeof(FD) <= 512;
+    constexpr int NB = ALL ? NSD : 2;
+    FD fk[NB][NT], fq[NB][NT];
 #pragma unroll
-    for (int mt = 0; mt < NT; ++mt) {
-        kq_rows<DT, DK, C, NW>(Ks, 16 * mt, 0, lane, fk[0][mt]);
-        kq_rows<DT, DK, C, NW>(Qs, 16 * mt, 0, lane, fq[0][mt]);
-    }
+    for (int s = 0; s < (ALL ? NSD : 1); ++s)
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) {
+            kq_rows<DT, DK, C, NW>(Ks, 16 * mt, s * KSD, lane, fk[s][mt]);
+            kq_rows<DT, DK, C, NW>(Qs, 16 * mt, s * KSD, lane, fq[s][mt]);
+        }
 #pragma unroll
     for (int s = 0; s < NSD; ++s) {
-        const int cur = s & 1;
-        if (s + 1 < NSD) {
+        const int cur = ALL ? s : (s & 1);
+        if (!ALL && s + 1 < NSD) {
 #pragma unroll
             for (int mt = 0; mt < NT; ++mt) {
                 kq_rows<DT, DK, C, NW>(Ks, 16 * mt, (s + 1) * KSD, lane, fk[cur ^ 1][mt]);
                 kq_rows<DT, DK, C, NW>(Qs, 16 * mt, (s + 1) * KSD, lane, fq[cur ^ 1][mt]);
             }
         }
-        FD fb;
+        FD fb;  // rows of S: B operand of X, A operand of Y
         if constexpr (KSD == 32) frag_from_state(Sacc[2 * s], Sacc[2 * s + 1], g, fb);
         else frag_from_acc16(Sacc[s], fb);
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt) {
             if constexpr (KSD == 32) {
                 mma_k32(X[mt], fk[cur][mt], fb);
-                mma_k32(Y[mt], fq[cur][mt], fb);
+                mma_k32(Y[mt], fb, fq[cur][mt]);
             } else {
                 mma_k16(X[mt], fk[cur][mt], fb);
-                mma_k16(Y[mt], fq[cur][mt], fb);
+                mma_k16(Y[mt], fb, fq[cur][mt]);
             }
         }
     }
-    // K^T fragments for the state update (read through the transpose path)
-    FC fkt[ND][NSC];
+}
+
+// Operands of state_rest that come from the chunk's K, V and beta tiles: the
+// K^T fragments of the state update, this wave's V columns in D layout and
+// the betas of its token rows.  Loading them ahead frees those tiles early.
+template <typename DT, int DK, int C, int NW>
+struct ChunkOperands {
+    typedef ChunkCfg<DT, DK, C, NW> G;
+    typedef typename SlabFrag<G::KSC == 32, DT>::type FC;
+    FC fkt[G::ND][C / G::KSC];
+    typename Frag<DT>::k16 fv[G::NT];
+    float bcur[G::NT][4];
+
+    __device__ __forceinline__ void load(const DT *Ks, const DT *Vs, const float *betas,
+                                         int vtile, int lane) {
+        constexpr int NT = G::NT, ND = G::ND, KSC = G::KSC, NSC = C / KSC;
+        const int g = lane >> 4;
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
+        for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-        for (int s = 0; s < NSC; ++s) {
-            if constexpr (KSC == 32) kt_frag32<DT, DK, C, NW>(Ks, s * KSC, dt, lane, fkt[dt][s]);
-            else kt_frag16<DT, DK, C, NW>(Ks, s * KSC, dt, lane, fkt[dt][s]);
+            for (int s = 0; s < NSC; ++s) {
+                if constexpr (KSC == 32) kt_frag32<DT, DK, C, NW>(Ks, s * KSC, dt, lane, fkt[dt][s]);
+                else kt_frag16<DT, DK, C, NW>(Ks, s * KSC, dt, lane, fkt[dt][s]);
+            }
+        // lane (g, r) takes V[16mt + 4g + j][16 vtile + r]
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) frag_cols16(Vs, G::LDV, 16 * mt, 16 * vtile, lane, fv[mt]);
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) {
+            const f32x4 b4 = *reinterpret_cast<const f32x4 *>(betas + 16 * mt + 4 * g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bcur[mt][i] = b4[i];
         }
+    }
+};
+
+// Two 16-wide fragments as one 32-wide fragment (k order of the 32-wide slab).
+__device__ __forceinline__ void cat16(const bf16x4 &a, const bf16x4 &b, bf16x8 &f) {
+    f = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void cat16(const f32x4_arr &a, const f32x4_arr &b, f32x8_arr &f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f.v[i] = a.v[i];
+        f.v[4 + i] = b.v[i];
+    }
+}
+
+// E solves (I + A) E = R block by block (16-token blocks i):
+//   E_i = T_ii (R_i - sum_{j<i} A_ij E_j),   T_ii = (I + A_ii)^{-1}
+// with T_ii from Tb and -A_ij from Ab as A operands, R_i and E_j as B
+// operands straight from their D layout (tokens along k).
+template <typename DT, int DK, int C, int NW>
+__device__ __forceinline__ void state_rest(const ChunkOperands<DT, DK, C, NW> &op,
+                                           const DT *Ab, const DT *Tb, const DT *Ps,
+                                           f32x4 *Sacc, f32x4 *X, f32x4 *Y,
+                                           const OutChunk &out, int lane) {
+    typedef ChunkCfg<DT, DK, C, NW> G;
+    constexpr int NT = G::NT, ND = G::ND, KSD = G::KSD, KSC = G::KSC;
+    constexpr int NSC = C / KSC, NOFF = NT * (NT - 1) / 2;
+    typedef typename SlabFrag<KSC == 32, DT>::type FC;
+    typedef typename Frag<DT>::k16 F16;
+
+    F16 ft[NT], fa[NOFF > 0 ? NOFF : 1];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) load_fragblk(Tb, i, lane, ft[i]);
+#pragma unroll
+    for (int i = 0; i < NOFF; ++i) load_fragblk(Ab, i, lane, fa[i]);
+    FC fP[NT][NSC];
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+        for (int s = 0; s < NSC; ++s)
+            if (s * KSC < 16 * (mt + 1))  // P is lower-triangular
+                p_rows<DT, DK, C, NW>(Ps, 16 * mt, s * KSC, lane, fP[mt][s]);
     // R = diag(beta) (V - K S^T), in place in X
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) X[mt][i] = bcur[mt][i] * (frag_get(fv[mt], i) - X[mt][i]);
-    // E = Ti R  (slabs past the diagonal are zero and skipped)
+        for (int i = 0; i < 4; ++i) X[mt][i] = op.bcur[mt][i] * (frag_get(op.fv[mt], i) - X[mt][i]);
+    // block forward substitution
     f32x4 E[NT];
+    F16 fe16[NT];
 #pragma unroll
-    for (int mt = 0; mt < NT; ++mt) {
-        E[mt] = zero4();
+    for (int i = 0; i < NT; ++i) {
 #pragma unroll
-        for (int s = 0; s < NSC; ++s)
-            if (s * KSC < 16 * (mt + 1)) {
-                FC fb;
-                if constexpr (KSC == 32) {
-                    frag_from_acc32(X[2 * s], X[2 * s + 1], fb);
-                    mma_k32(E[mt], fT[mt][s], fb);
-                } else {
-                    frag_from_acc16(X[s], fb);
-                    mma_k16(E[mt], fT[mt][s], fb);
-                }
-            }
+        for (int j = 0; j < i; ++j) mma_k16(X[i], fa[off_idx(i, j)], fe16[j]);
+        F16 fr;
+        frag_from_acc16(X[i], fr);
+        E[i] = mm16(ft[i], fr);
+        frag_from_acc16(E[i], fe16[i]);
     }
-    // B operands built from E, shared by the state update and the output
+    // B operands over 32-token slabs, shared by the state update and the output
     FC fe[NSC];
 #pragma unroll
     for (int s = 0; s < NSC; ++s) {
-        if constexpr (KSC == 32) frag_from_acc32(E[2 * s], E[2 * s + 1], fe[s]);
-        else frag_from_acc16(E[s], fe[s]);
+        if constexpr (KSC == 32) cat16(fe16[2 * s], fe16[2 * s + 1], fe[s]);
+        else fe[s] = fe16[s];
     }
     // S^T += K^T E
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
         for (int s = 0; s < NSC; ++s) {
-            if constexpr (KSC == 32) mma_k32(Sacc[dt], fkt[dt][s], fe[s]);
-            else mma_k16(Sacc[dt], fkt[dt][s], fe[s]);
+            if constexpr (KSC == 32) mma_k32(Sacc[dt], op.fkt[dt][s], fe[s]);
+            else mma_k16(Sacc[dt], op.fkt[dt][s], fe[s]);
         }
-    // O = Q S^T + P E.  When the slabs over d_k and over tokens have the same
-    // MFMA shape, P E accumulates onto Q S^T; otherwise it gets its own
-    // accumulator, since an accumulation chain must never switch shape (the
-    // compiler issues such a dependent pair back to back and the second one
-    // reads a stale accumulator).
+    // O^T = S Q^T + E^T P^T.  When the slabs over d_k and over tokens have the
+    // same MFMA shape, E^T P^T accumulates onto S Q^T; otherwise it gets its
+    // own accumulator, since an accumulation chain must never switch shape
+    // (the compiler issues such a dependent pair back to back and the second
+    // one reads a stale accumulator).
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt) {
         f32x4 PE = zero4();
@@ -551,17 +555,28 @@ __device__ __forceinline__ void state_path(const DT *Ks, const DT *Qs, const DT 
 #pragma unroll
         for (int s = 0; s < NSC; ++s)
             if (s * KSC < 16 * (mt + 1)) {
-                if constexpr (KSC == 32) mma_k32(acc, fP[mt][s], fe[s]);
-                else mma_k16(acc, fP[mt][s], fe[s]);
+                if constexpr (KSC == 32) mma_k32(acc, fe[s], fP[mt][s]);
+                else mma_k16(acc, fe[s], fP[mt][s]);
             }
-        // token 16mt + 4g + i of the chunk; stores past the chunk's last
-        // token fall outside the resource and are dropped
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float oi = (KSC == KSD) ? Y[mt][i] : Y[mt][i] + PE[i];
-            buf_store_elem(from_f32<DT>(oi), out.rsrc, out.voff, (16 * mt + i) * out.row_bytes);
-        }
+        // lane (g, r): token 16mt + r, value columns 4g .. 4g + 3
+        const f32x4 o4 = (KSC == KSD) ? Y[mt] : Y[mt] + PE;
+        if constexpr (sizeof(DT) == 2) store_out4(o4, out, 16 * mt * out.row_bytes);
+        else store_out4_f32(o4, out, 16 * mt * out.row_bytes);
     }
+}
+
+// Both halves back to back (single-buffered kernel).
+template <typename DT, int DK, int C, int NW>
+__device__ __forceinline__ void state_path(const DT *Ks, const DT *Qs, const DT *Vs,
+                                           const DT *Ab, const DT *Tb, const DT *Ps,
+                                           const float *betas, f32x4 *Sacc,
+                                           const OutChunk &out, int wave, int lane) {
+    typedef ChunkCfg<DT, DK, C, NW> G;
+    f32x4 X[G::NT], Y[G::NT];
+    state_xy<DT, DK, C, NW>(Ks, Qs, Sacc, X, Y, lane);
+    ChunkOperands<DT, DK, C, NW> op;
+    op.load(Ks, Vs, betas, wave, lane);
+    state_rest<DT, DK, C, NW>(op, Ab, Tb, Ps, Sacc, X, Y, out, lane);
 }
 
 // Common per-workgroup addressing: (b, h, value tile) of this workgroup with
@@ -670,18 +685,33 @@ struct ChunkRegs {
     }
 };
 
+// Byte offset of this lane's first output element within a chunk: token row
+// r, value columns 4g .. 4g + 3 of this wave's 16 columns.
+template <typename DT>
+__device__ __forceinline__ OutChunk out_chunk(const HeadPtrs<DT> &p, int g, int r) {
+    OutChunk out;
+    out.voff = (r * p.tsv + (p.vcol - r) + 4 * g) * (int)sizeof(DT);
+    out.row_bytes = p.tsv * (int)sizeof(DT);
+    return out;
+}
+
 // ---------------------------------------------------------------------------
-// Pipelined kernel
+// Warp-specialised kernel
 // ---------------------------------------------------------------------------
+// LDS of one workgroup: K, Q, V (this workgroup's value columns) and beta of
+// two chunks, and the per-chunk products the preparation waves hand to the
+// state waves, also for two chunks.
 template <typename DT, int DK, int C, int NW>
 struct PipeSmem {
     typedef ChunkCfg<DT, DK, C, NW> G;
-    DT Ks[2][C * G::LDK];          // K, token-major (double-buffered)
-    DT Qs[2][C * G::LDK];          // Q, token-major
-    DT Vs[2][C * G::LDV];          // V, this workgroup's value columns
-    DT TsT[2][C * G::LDT];         // ((I + A)^{-1})^T
-    DT Ps[2][C * G::LDP];          // Q K^T (.) M
-    float Af[C * G::LDA];          // A = beta (K K^T) strictly lower, fp32
+    static constexpr int NOFF = G::NT * (G::NT - 1) / 2;
+    DT Ks[2][C * G::LDK];                    // K, token-major
+    DT Qs[2][C * G::LDK];                    // Q, token-major
+    DT Vs[2][C * G::LDV];                    // V, this workgroup's value columns
+    DT Ps[2][C * G::LDP];                    // Q K^T (.) M
+    DT Ab[2][(NOFF > 0 ? NOFF : 1) * FRAG_ELEMS];  // -A_ij, i > j (fragment blocks)
+    DT Tb[2][G::NT * FRAG_ELEMS];            // T_ii = (I + A_ii)^{-1} (fragment blocks)
+    float Af[C * G::LDA];                    // diagonal tiles of A, fp32
     float betas[2][C];
 };
 
@@ -690,8 +720,25 @@ constexpr bool pipelined_fits() {
     return sizeof(PipeSmem<DT, DK, C, NW>) <= 160 * 1024;
 }
 
+// 2*NW waves: waves 0 .. NW-1 are state waves (wave w owns value rows
+// 16w .. 16w+15 of the workgroup's tile and keeps them in registers), waves
+// NW .. 2NW-1 are preparation waves (Gram tiles, diagonal inverses, staging
+// of the inputs).  Each SIMD runs one wave of each role, so the latency of one
+// role's LDS reads and MFMA chains hides behind the other's issue.  One
+// barrier per chunk; in the period of chunk c (b = c & 1, b1 = b ^ 1):
+//
+//   state: R, E, S^T += K^T E and the outputs of chunk c (X, Y and the K^T,
+//          V, beta operands already in registers; A, T and P blocks from
+//          buffers b); then the K^T, V, beta operands of chunk c+1 and
+//          X = K S^T, Y = S Q^T of chunk c+1 (K, Q, V, beta buffers b1)
+//   prep:  Gram tiles and diagonal inverses of chunk c+1 (K, Q, beta
+//          buffers b1 -> A, T, P buffers b1); chunk c+2 from registers into
+//          K, Q, V, beta buffers b; chunk c+3 loads into registers
+//
+// Within a period the state waves read only A, T, P buffers b and K, Q, V,
+// beta buffers b1, and the preparation waves write only the others.
 template <typename DT, int DK, int C, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_fwd_pipelined_kernel(
+__global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunk_fwd_ws_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const float *S0, DT *__restrict__ o, float *S_T,
     int T, int H, int Dv, int nvt) {
@@ -702,69 +749,86 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
     const int g = lane >> 4, r = lane & 15;
-    const HeadPtrs<DT> p = head_ptrs<DT, DK, NW>(q, k, v, beta, o, T, H, Dv, nvt, wave, r);
-
-    f32x4 Sacc[ND];
-    if (S0) {
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt)
-            Sacc[dt] = *reinterpret_cast<const f32x4 *>(S0 + p.sbase + state_col<G::KSD>(dt, g));
-    } else {
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt) Sacc[dt] = zero4();
-    }
-
     const int N = (T + C - 1) / C;
-    if (N > 0) {
-        // Lower blocks of TsT and upper blocks of Ps stay zero for the whole
-        // sequence.
-        for (int i = tid; i < 2 * C * G::LDT; i += G::NTHR) (&sm.TsT[0][0])[i] = from_f32<DT>(0.f);
-        for (int i = tid; i < 2 * C * G::LDP; i += G::NTHR) (&sm.Ps[0][0])[i] = from_f32<DT>(0.f);
-        ChunkRegs<DT, DK, C, NW> rg;
-        rg.init(p, tid);
-        OutChunk out;
-        out.voff = (4 * g * p.tsv + p.vcol) * (int)sizeof(DT);
-        out.row_bytes = p.tsv * (int)sizeof(DT);
-        // prologue: chunks 0 and 1 staged, chunk 0 solved, chunk 2 in flight
-        rg.load(p, T, 0);
-        rg.stage(sm.Ks[0], sm.Qs[0], sm.Vs[0], sm.betas[0], tid);
-        rg.load(p, T, min(1, N - 1) * C);
-        rg.stage(sm.Ks[1], sm.Qs[1], sm.Vs[1], sm.betas[1], tid);
-        rg.load(p, T, min(2, N - 1) * C);
-        lds_barrier();
-        gram_tiles<DT, DK, C, NW>(sm.Ks[0], sm.Qs[0], sm.betas[0], sm.Af, sm.Ps[0], wave, lane);
-        wave_lds_fence();
-        for (int d = wave; d < NT; d += NW) diag_inverse<DT, DK, C, NW>(sm.Af, sm.TsT[0], d, lane);
-        lds_barrier();
-        offdiag_inverse<DT, DK, C, NW>(sm.Af, sm.TsT[0], wave, lane);
-        lds_barrier();
 
+    if (wave < NW) {
+        // ------------------------------ state waves ------------------------------
+        const HeadPtrs<DT> p = head_ptrs<DT, DK, NW>(q, k, v, beta, o, T, H, Dv, nvt, wave, r);
+        f32x4 Sacc[ND], X[NT], Y[NT];
+        ChunkOperands<DT, DK, C, NW> op;
+        if (S0) {
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt)
+                Sacc[dt] = *reinterpret_cast<const f32x4 *>(S0 + p.sbase + state_col<G::KSD>(dt, g));
+        } else {
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt) Sacc[dt] = zero4();
+        }
+        OutChunk out = out_chunk(p, g, r);
+        lds_barrier();  // chunks 0 and 1 staged
+        if (N > 0) {
+            state_xy<DT, DK, C, NW>(sm.Ks[0], sm.Qs[0], Sacc, X, Y, lane);
+            op.load(sm.Ks[0], sm.Vs[0], sm.betas[0], wave, lane);
+        }
+        lds_barrier();  // Gram tiles and diagonal inverses of chunk 0
         for (int c = 0; c < N; ++c) {
             const int b = c & 1, b1 = b ^ 1;
             const int t0 = c * C;
             const int len = min(C, T - t0);
-            // ---- phase 1: state path of chunk c, Gram tiles of chunk c+1 ----
             out.rsrc = make_rsrc(p.oh + (int64_t)t0 * p.tsv, len * out.row_bytes);
-            state_path<DT, DK, C, NW>(sm.Ks[b], sm.Qs[b], sm.Vs[b], sm.TsT[b], sm.Ps[b],
-                                      sm.betas[b], Sacc, out, wave, lane);
-            // (past the last chunk this works on stale buffers; never read)
-            gram_tiles<DT, DK, C, NW>(sm.Ks[b1], sm.Qs[b1], sm.betas[b1], sm.Af, sm.Ps[b1],
-                                      wave, lane);
-            wave_lds_fence();
-            for (int d = wave; d < NT; d += NW)
-                diag_inverse<DT, DK, C, NW>(sm.Af, sm.TsT[b1], d, lane);
-            lds_barrier();
-            // ---- phase 2: rest of the inverse of chunk c+1, staging of chunk c+2 ----
-            offdiag_inverse<DT, DK, C, NW>(sm.Af, sm.TsT[b1], wave, lane);
-            rg.stage(sm.Ks[b], sm.Qs[b], sm.Vs[b], sm.betas[b], tid);
-            rg.load(p, T, min(c + 3, N - 1) * C);
+            state_rest<DT, DK, C, NW>(op, sm.Ab[b], sm.Tb[b], sm.Ps[b], Sacc, X, Y, out, lane);
+            if (c + 1 < N) {
+                op.load(sm.Ks[b1], sm.Vs[b1], sm.betas[b1], wave, lane);
+                state_xy<DT, DK, C, NW>(sm.Ks[b1], sm.Qs[b1], Sacc, X, Y, lane);
+            }
             lds_barrier();
         }
-    }
-    if (S_T) {
+        if (S_T) {
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt)
-            *reinterpret_cast<f32x4 *>(S_T + p.sbase + state_col<G::KSD>(dt, g)) = Sacc[dt];
+            for (int dt = 0; dt < ND; ++dt)
+                *reinterpret_cast<f32x4 *>(S_T + p.sbase + state_col<G::KSD>(dt, g)) = Sacc[dt];
+        }
+    } else {
+        // --------------------------- preparation waves ---------------------------
+        const int pw = wave - NW, ptid = tid - 64 * NW;
+        const HeadPtrs<DT> p = head_ptrs<DT, DK, NW>(q, k, v, beta, o, T, H, Dv, nvt, 0, r);
+        ChunkRegs<DT, DK, C, NW> rg;
+        rg.init(p, ptid);
+        // upper blocks of Ps stay zero for the whole sequence
+        for (int i = ptid; i < 2 * C * G::LDP; i += G::NTHR) (&sm.Ps[0][0])[i] = from_f32<DT>(0.f);
+        if (N > 0) {
+            // chunks 0 and 1 load concurrently; chunk 2 follows into the
+            // registers chunk 0 frees
+            ChunkRegs<DT, DK, C, NW> rg1 = rg;
+            rg.load(p, T, 0);
+            if (N > 1) rg1.load(p, T, C);
+            rg.stage(sm.Ks[0], sm.Qs[0], sm.Vs[0], sm.betas[0], ptid);
+            if (N > 2) rg.load(p, T, 2 * C);
+            if (N > 1) rg1.stage(sm.Ks[1], sm.Qs[1], sm.Vs[1], sm.betas[1], ptid);
+        }
+        lds_barrier();  // chunks 0 and 1 staged
+        if (N > 0) {
+            gram_tiles<DT, DK, C, NW>(sm.Ks[0], sm.Qs[0], sm.betas[0], sm.Af, sm.Ab[0], sm.Ps[0],
+                                      pw, lane);
+            wave_lds_fence();
+            for (int d = pw; d < NT; d += NW) diag_inverse<DT, DK, C, NW>(sm.Af, sm.Tb[0], d, lane);
+        }
+        lds_barrier();
+        for (int c = 0; c < N; ++c) {
+            const int b = c & 1, b1 = b ^ 1;
+            if (c + 1 < N) {
+                gram_tiles<DT, DK, C, NW>(sm.Ks[b1], sm.Qs[b1], sm.betas[b1], sm.Af, sm.Ab[b1],
+                                          sm.Ps[b1], pw, lane);
+                wave_lds_fence();
+                for (int d = pw; d < NT; d += NW)
+                    diag_inverse<DT, DK, C, NW>(sm.Af, sm.Tb[b1], d, lane);
+            }
+            if (c + 2 < N) {
+                rg.stage(sm.Ks[b], sm.Qs[b], sm.Vs[b], sm.betas[b], ptid);
+                if (c + 3 < N) rg.load(p, T, (c + 3) * C);
+            }
+            lds_barrier();
+        }
     }
 }
 
@@ -774,11 +838,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 template <typename DT, int DK, int C, int NW>
 struct SerialSmem {
     typedef ChunkCfg<DT, DK, C, NW> G;
+    static constexpr int NOFF = G::NT * (G::NT - 1) / 2;
     DT Ks[C * G::LDK];
     DT Qs[C * G::LDK];
     DT Vs[C * G::LDV];
-    DT TsT[C * G::LDT];
     DT Ps[C * G::LDP];
+    DT Ab[(NOFF > 0 ? NOFF : 1) * FRAG_ELEMS];
+    DT Tb[G::NT * FRAG_ELEMS];
     float Af[C * G::LDA];
     float betas[C];
 };
@@ -809,13 +875,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 
     const int N = (T + C - 1) / C;
     if (N > 0) {
-        for (int i = tid; i < C * G::LDT; i += G::NTHR) sm.TsT[i] = from_f32<DT>(0.f);
         for (int i = tid; i < C * G::LDP; i += G::NTHR) sm.Ps[i] = from_f32<DT>(0.f);
         ChunkRegs<DT, DK, C, NW> rg;
         rg.init(p, tid);
-        OutChunk out;
-        out.voff = (4 * g * p.tsv + p.vcol) * (int)sizeof(DT);
-        out.row_bytes = p.tsv * (int)sizeof(DT);
+        OutChunk out = out_chunk(p, g, r);
         rg.load(p, T, 0);
         for (int c = 0; c < N; ++c) {
             const int t0 = c * C;
@@ -824,15 +887,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
             rg.stage(sm.Ks, sm.Qs, sm.Vs, sm.betas, tid);
             lds_barrier();
             rg.load(p, T, min(c + 1, N - 1) * C);
-            gram_tiles<DT, DK, C, NW>(sm.Ks, sm.Qs, sm.betas, sm.Af, sm.Ps, wave, lane);
+            gram_tiles<DT, DK, C, NW>(sm.Ks, sm.Qs, sm.betas, sm.Af, sm.Ab, sm.Ps, wave, lane);
             wave_lds_fence();
-            for (int d = wave; d < NT; d += NW) diag_inverse<DT, DK, C, NW>(sm.Af, sm.TsT, d, lane);
-            lds_barrier();
-            offdiag_inverse<DT, DK, C, NW>(sm.Af, sm.TsT, wave, lane);
+            for (int d = wave; d < NT; d += NW) diag_inverse<DT, DK, C, NW>(sm.Af, sm.Tb, d, lane);
             lds_barrier();
             out.rsrc = make_rsrc(p.oh + (int64_t)t0 * p.tsv, len * out.row_bytes);
-            state_path<DT, DK, C, NW>(sm.Ks, sm.Qs, sm.Vs, sm.TsT, sm.Ps, sm.betas, Sacc, out,
-                                      wave, lane);
+            state_path<DT, DK, C, NW>(sm.Ks, sm.Qs, sm.Vs, sm.Ab, sm.Tb, sm.Ps, sm.betas, Sacc,
+                                      out, wave, lane);
         }
     }
     if (S_T) {
@@ -852,8 +913,8 @@ hipError_t launch_cfg(const void *q, const void *k, const void *v, const void *b
     const int nvt = Dv / (16 * NW);
     const int64_t grid = B * H * nvt;
     if constexpr (pipelined_fits<DT, DK, C, NW>()) {
-        hipLaunchKernelGGL((chunk_fwd_pipelined_kernel<DT, DK, C, NW>), dim3((unsigned)grid),
-                           dim3(64 * NW), 0, stream, static_cast<const DT *>(q),
+        hipLaunchKernelGGL((chunk_fwd_ws_kernel<DT, DK, C, NW>), dim3((unsigned)grid),
+                           dim3(128 * NW), 0, stream, static_cast<const DT *>(q),
                            static_cast<const DT *>(k), static_cast<const DT *>(v),
                            static_cast<const DT *>(beta), S0, static_cast<DT *>(o), S_T,
                            (int)T, (int)H, Dv, nvt);
