@@ -75,7 +75,6 @@ struct ChunkCfg {
     static constexpr bool SWZ = sizeof(DT) == 2 && DK >= 32;
     static constexpr int LDK = SWZ ? DK : DK + PADE;   // K, Q
     static constexpr int LDP = C + 2 * PADE;    // P (row fragments)
-    static constexpr int LDA = C + 8;           // A (fp32)
     static constexpr int VEC = Vec16<DT>::N;    // elements per 16-byte load
     static constexpr int VPR = DK / VEC;        // 16-byte vectors per K row
     static constexpr int NTHR = 64 * NW;
@@ -200,11 +199,66 @@ __device__ __forceinline__ void load_fragblk(const DT *base, int blk, int lane,
     load_chunk(base + blk * FRAG_ELEMS + 4 * lane, f);
 }
 
+// Inverse T_dd = (I + A_dd)^{-1} of a diagonal 16x16 block of the couplings
+// (unit lower-triangular), from the block in registers: lane (g, r) holds
+// A_dd[r][4g + e] (strictly lower, zero elsewhere), the A-operand fragment.
+// Blocked forward substitution by doubling: if T inverts the diagonal blocks
+// of size h of (I + A) and A_h holds the entries of A in the blocks of size h
+// just below them (rows in the lower half, columns in the upper half of each
+// diagonal block of size 2h), then T - T A_h T inverts the diagonal blocks of
+// size 2h, since (T A_h)^2 = 0.  Starting from T = I, four such steps (h = 1,
+// 2, 4, 8) on the MFMA units give the 16x16 inverse.  T is kept in D layout
+// both as T and as T^T: rows of T are the D layout of T^T and rows of M^T the
+// D layout of M, so every product comes straight from registers.  The result
+// goes to Tb as the fragment block of T_dd as an A operand.
+template <typename F>
+__device__ __forceinline__ f32x4 mm16(const F &a, const F &b) {
+    f32x4 acc = zero4();
+    mma_k16(acc, a, b);
+    return acc;
+}
+
+template <typename DT>
+__device__ __forceinline__ void diag_inverse(const f32x4 &a, const float *betas, DT *Tb, int d,
+                                             int lane) {
+    typedef typename Frag<DT>::k16 F;
+    const int g = lane >> 4, r = lane & 15;
+    f32x4 Tm, Tt;  // T[4g + i][r] and T^T[4g + i][r]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Tm[i] = Tt[i] = (4 * g + i == r) ? 1.f : 0.f;
+#pragma unroll
+    for (int lv = 0; lv < 4; ++lv) {
+        const int h = 1 << lv;
+        f32x4 ah;  // A_h: entry (r, 4g + e) of A
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int col = 4 * g + e;
+            const bool keep = (r / (2 * h) == col / (2 * h)) && (r % (2 * h) >= h) &&
+                              (col % (2 * h) < h);
+            ah[e] = keep ? a[e] : 0.f;
+        }
+        F fa, fT, fTt, fM;
+        cvt4(ah, fa);
+        frag_from_acc16(Tm, fT);
+        frag_from_acc16(Tt, fTt);
+        const f32x4 M = mm16(fa, fT);  // A_h T
+        frag_from_acc16(M, fM);
+        Tm -= mm16(fTt, fM);           // T M
+        Tt -= mm16(fM, fTt);           // M^T T^T
+    }
+    // lane (g, r) holds T^T[4g + i][r] = T[r][4g + i]: row r, columns 4g ..
+    // 4g + 3, the A-operand fragment of T_dd.  Stored as -T_dd diag(beta_d),
+    // the form the block substitution uses (state_rest).
+    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(betas + 16 * d + 4 * g);
+    store_fragblk(Tb, d, lane, -(Tt * b4));
+}
+
 // Gram tiles of one chunk, for the rows of the Gram jobs of wave W:
-//   A-row job ti:  A = beta_i (K K^T)_ij for i > j.  The diagonal tile goes to
-//                  Af (fp32, strictly lower, zeros elsewhere) for the
-//                  diagonal inverse; tiles left of it go to Ab as fragment
-//                  blocks of -A, the A operands of the block substitution.
+//   A-row job ti:  the K K^T tiles of row ti.  The diagonal tile, scaled
+//                  to A = tril(diag(beta) K K^T, -1), is inverted right away
+//                  from registers (diag_inverse, into Tb); the tiles left of
+//                  it go unscaled to Ab as fragment blocks G_ij = (K K^T)_ij,
+//                  the A operands of the block substitution.
 //   P-row job ti:  P = (Q K^T)_ij for i >= j into Ps (DT, masked).
 // Each 16x16 tile (ti, tj) is computed transposed, D = K_tj X_ti^T (X = K or
 // Q), so lane (g, r) ends up with row 16ti + r, columns 16tj + 4g .. + 3:
@@ -212,8 +266,8 @@ __device__ __forceinline__ void load_fragblk(const DT *base, int blk, int lane,
 // to wave ti % NW and the P-row to wave (NT-1-ti) % NW (with NW = NT every
 // wave computes NT+1 tiles).  The assignment is fixed at compile time per
 // wave; a wave loads every K tile its jobs touch once, plus the Q tiles of its
-// P rows, all before its first MFMA, and does its A rows first so that its
-// diagonal inverse can start early.
+// P rows, all before its first MFMA, and does its A rows first so that the
+// chain of its diagonal inverse overlaps the products of its P rows.
 template <int NT, int NW, int W>
 struct GramJobs {
     static constexpr bool a_row(int ti) { return ti % NW == W; }
@@ -226,139 +280,114 @@ struct GramJobs {
     }
 };
 
+template <int NT, int NW, int W>
+constexpr int n_prows() {
+    int n = 0;
+    for (int ti = 0; ti < NT; ++ti) n += GramJobs<NT, NW, W>::p_row(ti) ? 1 : 0;
+    return n;
+}
+
+// One Gram tile (ti, tj) from its operand fragments, written where its job
+// needs it.
+template <typename DT, int DK, int C, int NW, typename FD>
+__device__ __forceinline__ void gram_tile(const FD *fkj, const FD *fx, bool isP, int ti, int tj,
+                                          float brow, const float *betas, DT *Ab, DT *Tb, DT *Ps,
+                                          int lane) {
+    typedef ChunkCfg<DT, DK, C, NW> G;
+    constexpr int KSD = G::KSD, NSD = DK / KSD;
+    const int g = lane >> 4, r = lane & 15;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < NSD; ++s) {
+        if constexpr (KSD == 32) mma_k32(acc, fkj[s], fx[s]);
+        else mma_k16(acc, fkj[s], fx[s]);
+    }
+    const int row = 16 * ti + r;
+    const int col = 16 * tj + 4 * g;  // columns col .. col+3 of row
+    if (isP) {
+        typename Frag<DT>::k16 out;
+        f32x4 m;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m[e] = row >= col + e ? acc[e] : 0.f;
+        cvt4(m, out);
+        store_frag16(Ps + row * G::LDP + p_col<G::KSC>(col), out);
+    } else if (tj == ti) {
+        f32x4 a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = row > col + e ? brow * acc[e] : 0.f;
+        diag_inverse(a, betas, Tb, ti, lane);
+    } else {
+        store_fragblk(Ab, off_idx(ti, tj), lane, acc);
+    }
+}
+
+// When the fragments of all the wave's jobs fit in 96 VGPRs they are loaded
+// once, before the first MFMA; otherwise each job loads its own.
 template <typename DT, int DK, int C, int NW, int W>
 __device__ __forceinline__ void gram_tiles_w(const DT *Ks, const DT *Qs, const float *betas,
-                                             float *Af, DT *Ab, DT *Ps, int lane) {
+                                             DT *Ab, DT *Tb, DT *Ps, int lane) {
     typedef ChunkCfg<DT, DK, C, NW> G;
     typedef GramJobs<G::NT, NW, W> J;
     constexpr int NT = G::NT, KSD = G::KSD, NSD = DK / KSD, KM = J::kmax();
     typedef typename SlabFrag<KSD == 32, DT>::type FD;
-    const int g = lane >> 4, r = lane & 15;
-    FD fk[NT][NSD], fq[NT][NSD];
-#pragma unroll
-    for (int tj = 0; tj < NT; ++tj)
-        if (tj <= KM)
-#pragma unroll
-            for (int s = 0; s < NSD; ++s) kq_rows<DT, DK, C, NW>(Ks, 16 * tj, s * KSD, lane, fk[tj][s]);
-#pragma unroll
-    for (int ti = 0; ti < NT; ++ti)
-        if (J::p_row(ti))
-#pragma unroll
-            for (int s = 0; s < NSD; ++s) kq_rows<DT, DK, C, NW>(Qs, 16 * ti, s * KSD, lane, fq[ti][s]);
+    constexpr bool ALL = (KM + 1 + n_prows<NT, NW, W>()) * NSD * sizeof(FD) <= 384;
+    const int r = lane & 15;
     float brow[NT];
 #pragma unroll
     for (int ti = 0; ti < NT; ++ti)
         if (J::a_row(ti)) brow[ti] = betas[16 * ti + r];
+    if constexpr (ALL) {
+        FD fk[NT][NSD], fq[NT][NSD];
 #pragma unroll
-    for (int isP = 0; isP < 2; ++isP)
+        for (int tj = 0; tj < NT; ++tj)
+            if (tj <= KM)
 #pragma unroll
-        for (int ti = 0; ti < NT; ++ti) {
-            if (!(isP ? J::p_row(ti) : J::a_row(ti))) continue;
-            const int row = 16 * ti + r;
+                for (int s = 0; s < NSD; ++s) kq_rows<DT, DK, C, NW>(Ks, 16 * tj, s * KSD, lane, fk[tj][s]);
 #pragma unroll
-            for (int tj = 0; tj <= ti; ++tj) {
-                f32x4 acc = zero4();
+        for (int ti = 0; ti < NT; ++ti)
+            if (J::p_row(ti))
 #pragma unroll
-                for (int s = 0; s < NSD; ++s) {
-                    const FD &x = isP ? fq[ti][s] : fk[ti][s];
-                    if constexpr (KSD == 32) mma_k32(acc, fk[tj][s], x);
-                    else mma_k16(acc, fk[tj][s], x);
-                }
-                const int col = 16 * tj + 4 * g;  // columns col .. col+3 of row
-                if (isP) {
-                    typename Frag<DT>::k16 out;
-                    f32x4 m;
+                for (int s = 0; s < NSD; ++s) kq_rows<DT, DK, C, NW>(Qs, 16 * ti, s * KSD, lane, fq[ti][s]);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) m[e] = row >= col + e ? acc[e] : 0.f;
-                    cvt4(m, out);
-                    store_frag16(Ps + row * G::LDP + p_col<G::KSC>(col), out);
-                } else if (tj == ti) {
-                    f32x4 out;
+        for (int isP = 0; isP < 2; ++isP)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) out[e] = row > col + e ? brow[ti] * acc[e] : 0.f;
-                    *reinterpret_cast<f32x4 *>(Af + row * G::LDA + col) = out;
-                } else {
-                    store_fragblk(Ab, off_idx(ti, tj), lane, -brow[ti] * acc);
+            for (int ti = 0; ti < NT; ++ti) {
+                if (!(isP ? J::p_row(ti) : J::a_row(ti))) continue;
+#pragma unroll
+                for (int tj = 0; tj <= ti; ++tj)
+                    gram_tile<DT, DK, C, NW>(fk[tj], isP ? fq[ti] : fk[ti], isP, ti, tj,
+                                             isP ? 0.f : brow[ti], betas, Ab, Tb, Ps, lane);
+            }
+    } else {
+#pragma unroll
+        for (int isP = 0; isP < 2; ++isP)
+#pragma unroll
+            for (int ti = 0; ti < NT; ++ti) {
+                if (!(isP ? J::p_row(ti) : J::a_row(ti))) continue;
+                FD fx[NSD];
+#pragma unroll
+                for (int s = 0; s < NSD; ++s) kq_rows<DT, DK, C, NW>(isP ? Qs : Ks, 16 * ti, s * KSD, lane, fx[s]);
+#pragma unroll
+                for (int tj = 0; tj <= ti; ++tj) {
+                    FD fk[NSD];
+#pragma unroll
+                    for (int s = 0; s < NSD; ++s) kq_rows<DT, DK, C, NW>(Ks, 16 * tj, s * KSD, lane, fk[s]);
+                    gram_tile<DT, DK, C, NW>(fk, fx, isP, ti, tj, isP ? 0.f : brow[ti], betas,
+                                             Ab, Tb, Ps, lane);
                 }
             }
-        }
+    }
 }
 
 template <typename DT, int DK, int C, int NW>
 __device__ __forceinline__ void gram_tiles(const DT *Ks, const DT *Qs, const float *betas,
-                                           float *Af, DT *Ab, DT *Ps, int wave, int lane) {
+                                           DT *Ab, DT *Tb, DT *Ps, int wave, int lane) {
     switch (wave) {
-    case 0: gram_tiles_w<DT, DK, C, NW, 0>(Ks, Qs, betas, Af, Ab, Ps, lane); break;
-    case 1: if constexpr (NW > 1) gram_tiles_w<DT, DK, C, NW, 1>(Ks, Qs, betas, Af, Ab, Ps, lane); break;
-    case 2: if constexpr (NW > 2) gram_tiles_w<DT, DK, C, NW, 2>(Ks, Qs, betas, Af, Ab, Ps, lane); break;
-    default: if constexpr (NW > 3) gram_tiles_w<DT, DK, C, NW, 3>(Ks, Qs, betas, Af, Ab, Ps, lane); break;
+    case 0: gram_tiles_w<DT, DK, C, NW, 0>(Ks, Qs, betas, Ab, Tb, Ps, lane); break;
+    case 1: if constexpr (NW > 1) gram_tiles_w<DT, DK, C, NW, 1>(Ks, Qs, betas, Ab, Tb, Ps, lane); break;
+    case 2: if constexpr (NW > 2) gram_tiles_w<DT, DK, C, NW, 2>(Ks, Qs, betas, Ab, Tb, Ps, lane); break;
+    default: if constexpr (NW > 3) gram_tiles_w<DT, DK, C, NW, 3>(Ks, Qs, betas, Ab, Tb, Ps, lane); break;
     }
-}
-
-// Inverse T_dd = (I + A_dd)^{-1} of diagonal block d of the couplings (unit
-// lower-triangular).  Blocked forward substitution by doubling: if T inverts
-// the diagonal blocks of size h of (I + A) and A_h holds the entries of A in
-// the blocks of size h just below them (rows in the upper half, columns in
-// the lower half of each diagonal block of size 2h), then T - T A_h T
-// inverts the diagonal blocks of size 2h, since (T A_h)^2 = 0.  The 4x4
-// blocks are solved on the VALU, sizes 8 and 16 by that step on the MFMA
-// units.  The result goes to Tb as the fragment block of T_dd as an A
-// operand.
-template <typename F>
-__device__ __forceinline__ f32x4 mm16(const F &a, const F &b) {
-    f32x4 acc = zero4();
-    mma_k16(acc, a, b);
-    return acc;
-}
-
-template <typename DT, int DK, int C, int NW>
-__device__ __forceinline__ void diag_inverse(const float *Af, DT *Tb, int d, int lane) {
-    typedef ChunkCfg<DT, DK, C, NW> G;
-    typedef typename Frag<DT>::k16 F;
-    constexpr int LDA = G::LDA;
-    const int g = lane >> 4, r = lane & 15, c = r & 3;
-    const int o = 16 * d;
-    // Size 4: lane (g, r) with r / 4 == g takes 4x4 block g and solves for
-    // column c of its inverse (x) and for column c of the inverse of its
-    // transpose (y), i.e. row c of the inverse.  In D layout these are
-    // T[4g + i][r] and T^T[4g + i][r]; every other lane holds zeros.
-    float a1[4], a2[4], a3[4], ar[4];
-    load4(Af + (o + 4 * g + 1) * LDA + o + 4 * g, a1);
-    load4(Af + (o + 4 * g + 2) * LDA + o + 4 * g, a2);
-    load4(Af + (o + 4 * g + 3) * LDA + o + 4 * g, a3);
-    load4(Af + (o + r) * LDA + o + 4 * g, ar);  // A-operand row r, columns 4g..4g+3
-    const float e0 = c == 0 ? 1.f : 0.f, e1 = c == 1 ? 1.f : 0.f;
-    const float e2 = c == 2 ? 1.f : 0.f, e3 = c == 3 ? 1.f : 0.f;
-    const float x0 = e0, x1 = e1 - a1[0] * x0, x2 = e2 - a2[0] * x0 - a2[1] * x1;
-    const float x3 = e3 - a3[0] * x0 - a3[1] * x1 - a3[2] * x2;
-    const float y3 = e3, y2 = e2 - a3[2] * y3, y1 = e1 - a2[1] * y2 - a3[1] * y3;
-    const float y0 = e0 - a1[0] * y1 - a2[0] * y2 - a3[0] * y3;
-    const bool act = (r >> 2) == g;
-    f32x4 Tm = act ? f32x4{x0, x1, x2, x3} : zero4();
-    f32x4 Tt = act ? f32x4{y0, y1, y2, y3} : zero4();
-    // Sizes 8 and 16: M = A_h T, T <- T - T M and T^T <- T^T - M^T T^T.
-    // Operands: rows of T are the D layout of T^T and rows of M^T the D
-    // layout of M, so both products come straight from registers.
-#pragma unroll
-    for (int lv = 0; lv < 2; ++lv) {
-        const int h = 4 << lv;
-        const bool keep = (r / (2 * h) == (4 * g) / (2 * h)) && (r % (2 * h) >= h) &&
-                          ((4 * g) % (2 * h) < h);
-        F fa, fT, fTt, fM;
-        cvt4(keep ? f32x4{ar[0], ar[1], ar[2], ar[3]} : zero4(), fa);
-        frag_from_acc16(Tm, fT);
-        frag_from_acc16(Tt, fTt);
-        f32x4 M = zero4(), P = zero4(), Pt = zero4();
-        mma_k16(M, fa, fT);
-        frag_from_acc16(M, fM);
-        mma_k16(P, fTt, fM);
-        mma_k16(Pt, fM, fTt);
-        Tm -= P;
-        Tt -= Pt;
-    }
-    // lane (g, r) holds T^T[4g + i][r] = T[r][4g + i]: row r, columns 4g ..
-    // 4g + 3, the A-operand fragment of T_dd
-    store_fragblk(Tb, d, lane, Tt);
 }
 
 // Output rows of one chunk: a buffer resource over the chunk's valid tokens,
@@ -385,21 +414,27 @@ __device__ __forceinline__ void store_out4_f32(const f32x4 &x, const OutChunk &o
 // The state path of one chunk for this wave's 16 rows of S, in two halves so
 // that a pipeline can put the products over d_k of the next chunk right after
 // the state update of this one:
-//   state_xy:   X = K S^T (tokens x rows), Y = S Q^T (rows x tokens)
-//   state_rest: R = diag(beta)(V - X), E by block forward substitution,
-//               S^T += K^T E, O^T = Y + E^T P^T (stored for valid tokens)
+//   state_xy:   X = K S^T - V (tokens x rows), Y = S Q^T (rows x tokens)
+//   state_rest: E by block forward substitution, S^T += K^T E,
+//               O^T = Y + E^T P^T (stored for valid tokens)
 // Y and the output are computed transposed so that a lane holds four
 // consecutive value columns of one token, which it stores with one access.
 template <typename DT, int DK, int C, int NW>
 __device__ __forceinline__ void state_xy(const DT *Ks, const DT *Qs, const f32x4 *Sacc,
-                                         f32x4 *X, f32x4 *Y, int lane) {
+                                         const typename Frag<DT>::k16 *fv, f32x4 *X, f32x4 *Y,
+                                         int lane) {
     typedef ChunkCfg<DT, DK, C, NW> G;
     constexpr int NT = G::NT, KSD = G::KSD;
     constexpr int NSD = DK / KSD;
     typedef typename SlabFrag<KSD == 32, DT>::type FD;
     const int g = lane >> 4;
+    // X accumulates onto -V: X = K S^T - V
 #pragma unroll
-    for (int mt = 0; mt < NT; ++mt) X[mt] = Y[mt] = zero4();
+    for (int mt = 0; mt < NT; ++mt) {
+        Y[mt] = zero4();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) X[mt][i] = -frag_get(fv[mt], i);
+    }
     // All operand fragments are loaded before the first MFMA when they fit in
     // 128 VGPRs; otherwise they are double-buffered one slab ahead.
     constexpr bool ALL = 2 * NSD * NT * sizeof(FD) <= 512;
@@ -438,21 +473,18 @@ __device__ __forceinline__ void state_xy(const DT *Ks, const DT *Qs, const f32x4
     }
 }
 
-// Operands of state_rest that come from the chunk's K, V and beta tiles: the
-// K^T fragments of the state update, this wave's V columns in D layout and
-// the betas of its token rows.  Loading them ahead frees those tiles early.
+// Operands that come from the chunk's K and V tiles: the K^T fragments of the
+// state update and this wave's V columns in D layout.  Loading them ahead
+// frees those tiles early.
 template <typename DT, int DK, int C, int NW>
 struct ChunkOperands {
     typedef ChunkCfg<DT, DK, C, NW> G;
     typedef typename SlabFrag<G::KSC == 32, DT>::type FC;
     FC fkt[G::ND][C / G::KSC];
     typename Frag<DT>::k16 fv[G::NT];
-    float bcur[G::NT][4];
 
-    __device__ __forceinline__ void load(const DT *Ks, const DT *Vs, const float *betas,
-                                         int vtile, int lane) {
+    __device__ __forceinline__ void load(const DT *Ks, const DT *Vs, int vtile, int lane) {
         constexpr int NT = G::NT, ND = G::ND, KSC = G::KSC, NSC = C / KSC;
-        const int g = lane >> 4;
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
@@ -463,12 +495,6 @@ struct ChunkOperands {
         // lane (g, r) takes V[16mt + 4g + j][16 vtile + r]
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt) frag_cols16(Vs, G::LDV, 16 * mt, 16 * vtile, lane, fv[mt]);
-#pragma unroll
-        for (int mt = 0; mt < NT; ++mt) {
-            const f32x4 b4 = *reinterpret_cast<const f32x4 *>(betas + 16 * mt + 4 * g);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) bcur[mt][i] = b4[i];
-        }
     }
 };
 
@@ -484,10 +510,15 @@ __device__ __forceinline__ void cat16(const f32x4_arr &a, const f32x4_arr &b, f3
     }
 }
 
-// E solves (I + A) E = R block by block (16-token blocks i):
-//   E_i = T_ii (R_i - sum_{j<i} A_ij E_j),   T_ii = (I + A_ii)^{-1}
-// with T_ii from Tb and -A_ij from Ab as A operands, R_i and E_j as B
-// operands straight from their D layout (tokens along k).
+// E solves (I + A) E = R, R = diag(beta)(V - K S^T), block by block
+// (16-token blocks i).  With A_ij = diag(beta_i) G_ij, G = K K^T and
+// T_ii = (I + A_ii)^{-1}:
+//   E_i = T_ii diag(beta_i) (V_i - X_i - sum_{j<i} G_ij E_j)
+//       = (-T_ii diag(beta_i)) (X'_i + sum_{j<i} G_ij E_j),   X' = K S^T - V
+// so the products G_ij E_j accumulate onto X' in place and each block costs
+// one more product with the stored -T_ii diag(beta_i) (Tb); G_ij comes from
+// Ab.  X'_i and E_j enter as B operands straight from their D layout (tokens
+// along k).  No beta and no residual arithmetic remain on the state path.
 template <typename DT, int DK, int C, int NW>
 __device__ __forceinline__ void state_rest(const ChunkOperands<DT, DK, C, NW> &op,
                                            const DT *Ab, const DT *Tb, const DT *Ps,
@@ -511,11 +542,6 @@ __device__ __forceinline__ void state_rest(const ChunkOperands<DT, DK, C, NW> &o
         for (int s = 0; s < NSC; ++s)
             if (s * KSC < 16 * (mt + 1))  // P is lower-triangular
                 p_rows<DT, DK, C, NW>(Ps, 16 * mt, s * KSC, lane, fP[mt][s]);
-    // R = diag(beta) (V - K S^T), in place in X
-#pragma unroll
-    for (int mt = 0; mt < NT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) X[mt][i] = op.bcur[mt][i] * (frag_get(op.fv[mt], i) - X[mt][i]);
     // block forward substitution
     f32x4 E[NT];
     F16 fe16[NT];
@@ -573,9 +599,9 @@ __device__ __forceinline__ void state_path(const DT *Ks, const DT *Qs, const DT 
                                            const OutChunk &out, int wave, int lane) {
     typedef ChunkCfg<DT, DK, C, NW> G;
     f32x4 X[G::NT], Y[G::NT];
-    state_xy<DT, DK, C, NW>(Ks, Qs, Sacc, X, Y, lane);
     ChunkOperands<DT, DK, C, NW> op;
-    op.load(Ks, Vs, betas, wave, lane);
+    op.load(Ks, Vs, wave, lane);
+    state_xy<DT, DK, C, NW>(Ks, Qs, Sacc, op.fv, X, Y, lane);
     state_rest<DT, DK, C, NW>(op, Ab, Tb, Ps, Sacc, X, Y, out, lane);
 }
 
@@ -645,8 +671,10 @@ struct ChunkRegs {
         }
         offb = tid < C ? tid * p.tsb * (int)sizeof(DT) : OUT;
     }
+    // A chunk that starts at or past the end of the sequence gets empty
+    // resources: its loads return zeros and touch no memory.
     __device__ __forceinline__ void load(const HeadPtrs<DT> &p, int T, int t0) {
-        const int len = min(C, T - t0);
+        const int len = max(0, min(C, T - t0));
         const int esz = (int)sizeof(DT);
         const auto rk = make_rsrc(p.kh + (int64_t)t0 * p.tsk, len * p.tsk * esz);
         const auto rq = make_rsrc(p.qh + (int64_t)t0 * p.tsk, len * p.tsk * esz);
@@ -685,6 +713,12 @@ struct ChunkRegs {
     }
 };
 
+// Buffer index of a chunk period as a type, for loops unrolled by two.
+template <int B>
+struct Parity {
+    static constexpr int value = B;
+};
+
 // Byte offset of this lane's first output element within a chunk: token row
 // r, value columns 4g .. 4g + 3 of this wave's 16 columns.
 template <typename DT>
@@ -711,7 +745,6 @@ struct PipeSmem {
     DT Ps[2][C * G::LDP];                    // Q K^T (.) M
     DT Ab[2][(NOFF > 0 ? NOFF : 1) * FRAG_ELEMS];  // -A_ij, i > j (fragment blocks)
     DT Tb[2][G::NT * FRAG_ELEMS];            // T_ii = (I + A_ii)^{-1} (fragment blocks)
-    float Af[C * G::LDA];                    // diagonal tiles of A, fp32
     float betas[2][C];
 };
 
@@ -724,8 +757,9 @@ constexpr bool pipelined_fits() {
 // 16w .. 16w+15 of the workgroup's tile and keeps them in registers), waves
 // NW .. 2NW-1 are preparation waves (Gram tiles, diagonal inverses, staging
 // of the inputs).  Each SIMD runs one wave of each role, so the latency of one
-// role's LDS reads and MFMA chains hides behind the other's issue.  One
-// barrier per chunk; in the period of chunk c (b = c & 1, b1 = b ^ 1):
+// role's LDS reads and MFMA chains hides behind the other's issue (with NW
+// <= 2 the waves spread over distinct SIMDs and may use all their registers).
+// One barrier per chunk; in the period of chunk c (b = c & 1, b1 = b ^ 1):
 //
 //   state: R, E, S^T += K^T E and the outputs of chunk c (X, Y and the K^T,
 //          V, beta operands already in registers; A, T and P blocks from
@@ -738,7 +772,7 @@ constexpr bool pipelined_fits() {
 // Within a period the state waves read only A, T, P buffers b and K, Q, V,
 // beta buffers b1, and the preparation waves write only the others.
 template <typename DT, int DK, int C, int NW>
-__global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunk_fwd_ws_kernel(
+__global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4 + 1, NW / 4 + 1))) void chunk_fwd_ws_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const float *S0, DT *__restrict__ o, float *S_T,
     int T, int H, int Dv, int nvt) {
@@ -767,21 +801,26 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))
         OutChunk out = out_chunk(p, g, r);
         lds_barrier();  // chunks 0 and 1 staged
         if (N > 0) {
-            state_xy<DT, DK, C, NW>(sm.Ks[0], sm.Qs[0], Sacc, X, Y, lane);
-            op.load(sm.Ks[0], sm.Vs[0], sm.betas[0], wave, lane);
+            op.load(sm.Ks[0], sm.Vs[0], wave, lane);
+            state_xy<DT, DK, C, NW>(sm.Ks[0], sm.Qs[0], Sacc, op.fv, X, Y, lane);
         }
         lds_barrier();  // Gram tiles and diagonal inverses of chunk 0
-        for (int c = 0; c < N; ++c) {
-            const int b = c & 1, b1 = b ^ 1;
+        // the loop is unrolled by two so that the buffer index is a constant
+        auto period = [&](int c, auto parity) {
+            constexpr int b = decltype(parity)::value, b1 = b ^ 1;
             const int t0 = c * C;
             const int len = min(C, T - t0);
             out.rsrc = make_rsrc(p.oh + (int64_t)t0 * p.tsv, len * out.row_bytes);
             state_rest<DT, DK, C, NW>(op, sm.Ab[b], sm.Tb[b], sm.Ps[b], Sacc, X, Y, out, lane);
             if (c + 1 < N) {
-                op.load(sm.Ks[b1], sm.Vs[b1], sm.betas[b1], wave, lane);
-                state_xy<DT, DK, C, NW>(sm.Ks[b1], sm.Qs[b1], Sacc, X, Y, lane);
+                op.load(sm.Ks[b1], sm.Vs[b1], wave, lane);
+                state_xy<DT, DK, C, NW>(sm.Ks[b1], sm.Qs[b1], Sacc, op.fv, X, Y, lane);
             }
             lds_barrier();
+        };
+        for (int c = 0; c < N; c += 2) {
+            period(c, Parity<0>());
+            if (c + 1 < N) period(c + 1, Parity<1>());
         }
         if (S_T) {
 #pragma unroll
@@ -790,44 +829,42 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
     } else {
         // --------------------------- preparation waves ---------------------------
+        // Two register sets alternate: chunk m is loaded into set m & 1 two
+        // periods before it is staged, so its loads have two periods to land.
         const int pw = wave - NW, ptid = tid - 64 * NW;
         const HeadPtrs<DT> p = head_ptrs<DT, DK, NW>(q, k, v, beta, o, T, H, Dv, nvt, 0, r);
-        ChunkRegs<DT, DK, C, NW> rg;
-        rg.init(p, ptid);
+        ChunkRegs<DT, DK, C, NW> rga, rgb;
+        rga.init(p, ptid);
+        rgb = rga;
         // upper blocks of Ps stay zero for the whole sequence
         for (int i = ptid; i < 2 * C * G::LDP; i += G::NTHR) (&sm.Ps[0][0])[i] = from_f32<DT>(0.f);
-        if (N > 0) {
-            // chunks 0 and 1 load concurrently; chunk 2 follows into the
-            // registers chunk 0 frees
-            ChunkRegs<DT, DK, C, NW> rg1 = rg;
-            rg.load(p, T, 0);
-            if (N > 1) rg1.load(p, T, C);
-            rg.stage(sm.Ks[0], sm.Qs[0], sm.Vs[0], sm.betas[0], ptid);
-            if (N > 2) rg.load(p, T, 2 * C);
-            if (N > 1) rg1.stage(sm.Ks[1], sm.Qs[1], sm.Vs[1], sm.betas[1], ptid);
-        }
+        // Loads are issued unconditionally (chunks past the end load nothing),
+        // so the number of loads in flight is the same on every path and each
+        // wait for a register set covers only that set's loads.
+        rga.load(p, T, 0);
+        rgb.load(p, T, C);
+        if (N > 0) rga.stage(sm.Ks[0], sm.Qs[0], sm.Vs[0], sm.betas[0], ptid);
+        rga.load(p, T, 2 * C);
+        if (N > 1) rgb.stage(sm.Ks[1], sm.Qs[1], sm.Vs[1], sm.betas[1], ptid);
         lds_barrier();  // chunks 0 and 1 staged
-        if (N > 0) {
-            gram_tiles<DT, DK, C, NW>(sm.Ks[0], sm.Qs[0], sm.betas[0], sm.Af, sm.Ab[0], sm.Ps[0],
+        if (N > 0)
+            gram_tiles<DT, DK, C, NW>(sm.Ks[0], sm.Qs[0], sm.betas[0], sm.Ab[0], sm.Tb[0], sm.Ps[0],
                                       pw, lane);
-            wave_lds_fence();
-            for (int d = pw; d < NT; d += NW) diag_inverse<DT, DK, C, NW>(sm.Af, sm.Tb[0], d, lane);
-        }
         lds_barrier();
-        for (int c = 0; c < N; ++c) {
-            const int b = c & 1, b1 = b ^ 1;
-            if (c + 1 < N) {
-                gram_tiles<DT, DK, C, NW>(sm.Ks[b1], sm.Qs[b1], sm.betas[b1], sm.Af, sm.Ab[b1],
+        // period c: rcur holds chunk c+2, rnext receives chunk c+3
+        auto period = [&](int c, auto parity, ChunkRegs<DT, DK, C, NW> &rcur,
+                          ChunkRegs<DT, DK, C, NW> &rnext) {
+            constexpr int b = decltype(parity)::value, b1 = b ^ 1;
+            rnext.load(p, T, (c + 3) * C);
+            if (c + 1 < N)
+                gram_tiles<DT, DK, C, NW>(sm.Ks[b1], sm.Qs[b1], sm.betas[b1], sm.Ab[b1], sm.Tb[b1],
                                           sm.Ps[b1], pw, lane);
-                wave_lds_fence();
-                for (int d = pw; d < NT; d += NW)
-                    diag_inverse<DT, DK, C, NW>(sm.Af, sm.Tb[b1], d, lane);
-            }
-            if (c + 2 < N) {
-                rg.stage(sm.Ks[b], sm.Qs[b], sm.Vs[b], sm.betas[b], ptid);
-                if (c + 3 < N) rg.load(p, T, (c + 3) * C);
-            }
+            if (c + 2 < N) rcur.stage(sm.Ks[b], sm.Qs[b], sm.Vs[b], sm.betas[b], ptid);
             lds_barrier();
+        };
+        for (int c = 0; c < N; c += 2) {
+            period(c, Parity<0>(), rga, rgb);
+            if (c + 1 < N) period(c + 1, Parity<1>(), rgb, rga);
         }
     }
 }
@@ -845,7 +882,6 @@ struct SerialSmem {
     DT Ps[C * G::LDP];
     DT Ab[(NOFF > 0 ? NOFF : 1) * FRAG_ELEMS];
     DT Tb[G::NT * FRAG_ELEMS];
-    float Af[C * G::LDA];
     float betas[C];
 };
 
@@ -887,9 +923,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
             rg.stage(sm.Ks, sm.Qs, sm.Vs, sm.betas, tid);
             lds_barrier();
             rg.load(p, T, min(c + 1, N - 1) * C);
-            gram_tiles<DT, DK, C, NW>(sm.Ks, sm.Qs, sm.betas, sm.Af, sm.Ab, sm.Ps, wave, lane);
-            wave_lds_fence();
-            for (int d = wave; d < NT; d += NW) diag_inverse<DT, DK, C, NW>(sm.Af, sm.Tb, d, lane);
+            gram_tiles<DT, DK, C, NW>(sm.Ks, sm.Qs, sm.betas, sm.Ab, sm.Tb, sm.Ps, wave, lane);
             lds_barrier();
             out.rsrc = make_rsrc(p.oh + (int64_t)t0 * p.tsv, len * out.row_bytes);
             state_path<DT, DK, C, NW>(sm.Ks, sm.Qs, sm.Vs, sm.Ab, sm.Tb, sm.Ps, sm.betas, Sacc,

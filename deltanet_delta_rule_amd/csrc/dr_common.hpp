@@ -30,6 +30,20 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+
+// Two fp32 values narrowed to a packed bf16 pair (one v_cvt_pk_bf16_f32).
+// Narrowing whole 4-vectors at once lets the compiler scalarise into four
+// half-empty conversions and two permutes; pairs keep it to two instructions.
+__device__ __forceinline__ unsigned pk_bf16(float a, float b) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ u32x2 pk4_bf16(const f32x4 &x) {
+    return u32x2{pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3])};
+}
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
 
@@ -205,9 +219,8 @@ __device__ __forceinline__ int state_col(int dt, int g) {
 __device__ __forceinline__ void frag_from_state(const f32x4 &t0, const f32x4 &t1, int g,
                                                 bf16x8 &f) {
     // narrow first, then swap the packed halves (4 selects instead of 8)
-    typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
-    const u32x2 a = __builtin_bit_cast(u32x2, __builtin_convertvector(t0, bf16x4));
-    const u32x2 b = __builtin_bit_cast(u32x2, __builtin_convertvector(t1, bf16x4));
+    const u32x2 a = pk4_bf16(t0);
+    const u32x2 b = pk4_bf16(t1);
     const bool odd = g & 1;
     const u32x2 lo = odd ? b : a, hi = odd ? a : b;
     f = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3));
@@ -233,15 +246,15 @@ __device__ __forceinline__ void store_frag16(float *p, const f32x4_arr &f) {
 // Narrow four fp32 values to a 4-element fragment (bf16: two packed
 // conversions).
 __device__ __forceinline__ void cvt4(const f32x4 &x, bf16x4 &f) {
-    f = __builtin_convertvector(x, bf16x4);
+    f = __builtin_bit_cast(bf16x4, pk4_bf16(x));
 }
 __device__ __forceinline__ void cvt4(const f32x4 &x, f32x4_arr &f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) f.v[i] = x[i];
 }
 __device__ __forceinline__ void cvt8(const f32x4 &lo, const f32x4 &hi, bf16x8 &f) {
-    const bf16x4 a = __builtin_convertvector(lo, bf16x4), b = __builtin_convertvector(hi, bf16x4);
-    f = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    const u32x2 a = pk4_bf16(lo), b = pk4_bf16(hi);
+    f = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3));
 }
 __device__ __forceinline__ void cvt8(const f32x4 &lo, const f32x4 &hi, f32x8_arr &f) {
 #pragma unroll
@@ -252,7 +265,6 @@ __device__ __forceinline__ void cvt8(const f32x4 &lo, const f32x4 &hi, f32x8_arr
 }
 // Sign flip of a fragment.
 __device__ __forceinline__ bf16x4 neg(const bf16x4 &f) {
-    typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
     return __builtin_bit_cast(bf16x4, __builtin_bit_cast(u32x2, f) ^ 0x80008000u);
 }
 __device__ __forceinline__ f32x4_arr neg(const f32x4_arr &f) {
