@@ -483,8 +483,13 @@ struct ChunkOperands {
     FC fkt[G::ND][C / G::KSC];
     typename Frag<DT>::k16 fv[G::NT];
 
-    __device__ __forceinline__ void load(const DT *Ks, const DT *Vs, int vtile, int lane) {
-        constexpr int NT = G::NT, ND = G::ND, KSC = G::KSC, NSC = C / KSC;
+    // lane (g, r) takes V[16mt + 4g + j][16 vtile + r]
+    __device__ __forceinline__ void load_v(const DT *Vs, int vtile, int lane) {
+#pragma unroll
+        for (int mt = 0; mt < G::NT; ++mt) frag_cols16(Vs, G::LDV, 16 * mt, 16 * vtile, lane, fv[mt]);
+    }
+    __device__ __forceinline__ void load_kt(const DT *Ks, int lane) {
+        constexpr int ND = G::ND, KSC = G::KSC, NSC = C / KSC;
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
@@ -492,9 +497,6 @@ struct ChunkOperands {
                 if constexpr (KSC == 32) kt_frag32<DT, DK, C, NW>(Ks, s * KSC, dt, lane, fkt[dt][s]);
                 else kt_frag16<DT, DK, C, NW>(Ks, s * KSC, dt, lane, fkt[dt][s]);
             }
-        // lane (g, r) takes V[16mt + 4g + j][16 vtile + r]
-#pragma unroll
-        for (int mt = 0; mt < NT; ++mt) frag_cols16(Vs, G::LDV, 16 * mt, 16 * vtile, lane, fv[mt]);
     }
 };
 
@@ -600,8 +602,9 @@ __device__ __forceinline__ void state_path(const DT *Ks, const DT *Qs, const DT 
     typedef ChunkCfg<DT, DK, C, NW> G;
     f32x4 X[G::NT], Y[G::NT];
     ChunkOperands<DT, DK, C, NW> op;
-    op.load(Ks, Vs, wave, lane);
+    op.load_v(Vs, wave, lane);
     state_xy<DT, DK, C, NW>(Ks, Qs, Sacc, op.fv, X, Y, lane);
+    op.load_kt(Ks, lane);
     state_rest<DT, DK, C, NW>(op, Ab, Tb, Ps, Sacc, X, Y, out, lane);
 }
 
@@ -799,12 +802,13 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4
             for (int dt = 0; dt < ND; ++dt) Sacc[dt] = zero4();
         }
         OutChunk out = out_chunk(p, g, r);
-        lds_barrier();  // chunks 0 and 1 staged
+        lds_barrier();  // chunk 0 staged
         if (N > 0) {
-            op.load(sm.Ks[0], sm.Vs[0], wave, lane);
+            op.load_v(sm.Vs[0], wave, lane);
             state_xy<DT, DK, C, NW>(sm.Ks[0], sm.Qs[0], Sacc, op.fv, X, Y, lane);
+            op.load_kt(sm.Ks[0], lane);
         }
-        lds_barrier();  // Gram tiles and diagonal inverses of chunk 0
+        lds_barrier();  // Gram tiles of chunk 0 done, chunk 1 staged
         // the loop is unrolled by two so that the buffer index is a constant
         auto period = [&](int c, auto parity) {
             constexpr int b = decltype(parity)::value, b1 = b ^ 1;
@@ -813,8 +817,11 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4
             out.rsrc = make_rsrc(p.oh + (int64_t)t0 * p.tsv, len * out.row_bytes);
             state_rest<DT, DK, C, NW>(op, sm.Ab[b], sm.Tb[b], sm.Ps[b], Sacc, X, Y, out, lane);
             if (c + 1 < N) {
-                op.load(sm.Ks[b1], sm.Vs[b1], wave, lane);
+                // V first (X starts at -V); the K^T fragments of the next
+                // state update only after X and Y have used their operands
+                op.load_v(sm.Vs[b1], wave, lane);
                 state_xy<DT, DK, C, NW>(sm.Ks[b1], sm.Qs[b1], Sacc, op.fv, X, Y, lane);
+                op.load_kt(sm.Ks[b1], lane);
             }
             lds_barrier();
         };
@@ -845,12 +852,12 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4
         rgb.load(p, T, C);
         if (N > 0) rga.stage(sm.Ks[0], sm.Qs[0], sm.Vs[0], sm.betas[0], ptid);
         rga.load(p, T, 2 * C);
-        if (N > 1) rgb.stage(sm.Ks[1], sm.Qs[1], sm.Vs[1], sm.betas[1], ptid);
-        lds_barrier();  // chunks 0 and 1 staged
+        lds_barrier();  // chunk 0 staged
         if (N > 0)
             gram_tiles<DT, DK, C, NW>(sm.Ks[0], sm.Qs[0], sm.betas[0], sm.Ab[0], sm.Tb[0], sm.Ps[0],
                                       pw, lane);
-        lds_barrier();
+        if (N > 1) rgb.stage(sm.Ks[1], sm.Qs[1], sm.Vs[1], sm.betas[1], ptid);
+        lds_barrier();  // Gram tiles of chunk 0 done, chunk 1 staged
         // period c: rcur holds chunk c+2, rnext receives chunk c+3
         auto period = [&](int c, auto parity, ChunkRegs<DT, DK, C, NW> &rcur,
                           ChunkRegs<DT, DK, C, NW> &rnext) {
