@@ -716,7 +716,83 @@ struct ChunkRegs {
     }
 };
 
-// Buffer index of a chunk period as a type, for loops unrolled by two.
+// Direct global-to-LDS staging of one chunk's K, Q and V tiles (the LDS
+// form of a buffer load: 64 lanes x 16 bytes land at an LDS base + 16 lane,
+// for every lane, whatever the execution mask).  Instruction j of a tile
+// fills 16-byte units 64j .. 64j + 63 of the tile as it is laid out in LDS
+// (rows of LD elements, K and Q rows swizzled), so each lane's global offset
+// encodes the layout.  Tile buffers are rounded up to whole KiB; units in a
+// row's padding or past the tile load from past the resource (zeros), and a
+// chunk that ends early loads zeros for its missing tokens.  The K, Q, V
+// instructions of a chunk are dealt round-robin to the NW preparation waves;
+// wave W's share is fixed at compile time, so the number of loads it has in
+// flight is a constant.
+template <typename DT, int DK, int C, int NW, int W>
+struct DmaStage {
+    typedef ChunkCfg<DT, DK, C, NW> G;
+    static constexpr int ESZ = (int)sizeof(DT);
+    static constexpr int OUT = 0x7ffffff0;  // offset past any resource: loads 0
+    static constexpr int UPR_K = G::LDK * ESZ / 16, NU_K = C * UPR_K, NI_K = (NU_K + 63) / 64;
+    static constexpr int UPR_V = G::LDV * ESZ / 16, NU_V = C * UPR_V, NI_V = (NU_V + 63) / 64;
+    static constexpr int KTILE = NI_K * 1024 / ESZ, VTILE = NI_V * 1024 / ESZ;  // buffer sizes
+    static constexpr int NI = 2 * NI_K + NI_V;                // instructions per chunk: K, Q, V
+    static constexpr int NMINE = (NI - W + NW - 1) / NW;      // this wave's: j = W, W + NW, ...
+    static constexpr int NVMEM = NMINE + (W == 0 ? 1 : 0);    // plus the beta load (wave 0)
+    static_assert(G::LDK * ESZ % 16 == 0 && G::LDV * ESZ % 16 == 0, "16-byte units");
+    int off[NMINE > 0 ? NMINE : 1];
+    int offb;
+
+    __device__ __forceinline__ void init(const HeadPtrs<DT> &p, int lane) {
+#pragma unroll
+        for (int i = 0; i < NMINE; ++i) {
+            const int j = W + i * NW;
+            const bool isv = j >= 2 * NI_K;
+            const int jj = isv ? j - 2 * NI_K : (j < NI_K ? j : j - NI_K);
+            const int upr = isv ? UPR_V : UPR_K;
+            const int u = 64 * jj + lane;
+            const int t = u / upr, cu = u % upr;
+            const int ec = cu * (16 / ESZ);
+            const int data = isv ? G::BV : DK;
+            int e = ec;
+            if (!isv && G::SWZ) e = (cu ^ kq_swz<DK / 8>(t)) * 8;
+            off[i] = (t < C && ec < data) ? (t * (isv ? p.tsv : p.tsk) + e) * ESZ : OUT;
+        }
+        offb = lane < C ? lane * p.tsb * ESZ : OUT;
+    }
+    // Issue the loads of chunk m (tokens mC ..) into one K, Q, V buffer set;
+    // beta of that chunk goes to a register.
+    __device__ __forceinline__ void issue(const HeadPtrs<DT> &p, int T, int m, DT *Ks, DT *Qs,
+                                          DT *Vs, DT &b, int lane) const {
+        typedef __attribute__((address_space(3))) void lds_void;
+        const int t0 = m * C;
+        const int len = max(0, min(C, T - t0));
+        const auto rk = make_rsrc(p.kh + (int64_t)t0 * p.tsk, len * p.tsk * ESZ);
+        const auto rq = make_rsrc(p.qh + (int64_t)t0 * p.tsk, len * p.tsk * ESZ);
+        const auto rv = make_rsrc(p.vh + (int64_t)t0 * p.tsv, len * p.tsv * ESZ);
+#pragma unroll
+        for (int i = 0; i < NMINE; ++i) {
+            const int j = W + i * NW;
+            const bool isv = j >= 2 * NI_K, isq = !isv && j >= NI_K;
+            const int jj = isv ? j - 2 * NI_K : (isq ? j - NI_K : j);
+            DT *dst = (isv ? Vs : isq ? Qs : Ks) + jj * (1024 / ESZ);
+            const auto &rs = isv ? rv : isq ? rq : rk;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, off[i], 0, 0, 0);
+        }
+        if (W == 0) {
+            const auto rb = make_rsrc(p.bh + (int64_t)t0 * p.tsb, len * p.tsb * ESZ);
+            b = buf_load_elem<DT>(rb, offb);
+        }
+    }
+};
+
+// Wait until at most N of this wave's vector-memory operations are in flight
+// (the counter holds at most 63; a smaller count only waits longer).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N < 63 ? N : 63) : "memory");
+}
+
+// Buffer index of a chunk period as a type, for unrolled loops.
 template <int B>
 struct Parity {
     static constexpr int value = B;
@@ -736,19 +812,20 @@ __device__ __forceinline__ OutChunk out_chunk(const HeadPtrs<DT> &p, int g, int 
 // Warp-specialised kernel
 // ---------------------------------------------------------------------------
 // LDS of one workgroup: K, Q, V (this workgroup's value columns) and beta of
-// two chunks, and the per-chunk products the preparation waves hand to the
-// state waves, also for two chunks.
+// three chunks (one being consumed, two landing), and the per-chunk products
+// the preparation waves hand to the state waves for two chunks.
 template <typename DT, int DK, int C, int NW>
 struct PipeSmem {
     typedef ChunkCfg<DT, DK, C, NW> G;
+    typedef DmaStage<DT, DK, C, NW, 0> D;
     static constexpr int NOFF = G::NT * (G::NT - 1) / 2;
-    DT Ks[2][C * G::LDK];                    // K, token-major
-    DT Qs[2][C * G::LDK];                    // Q, token-major
-    DT Vs[2][C * G::LDV];                    // V, this workgroup's value columns
+    DT Ks[3][D::KTILE];                      // K, token-major (whole KiB)
+    DT Qs[3][D::KTILE];                      // Q, token-major
+    DT Vs[3][D::VTILE];                      // V, this workgroup's value columns
     DT Ps[2][C * G::LDP];                    // Q K^T (.) M
-    DT Ab[2][(NOFF > 0 ? NOFF : 1) * FRAG_ELEMS];  // -A_ij, i > j (fragment blocks)
-    DT Tb[2][G::NT * FRAG_ELEMS];            // T_ii = (I + A_ii)^{-1} (fragment blocks)
-    float betas[2][C];
+    DT Ab[2][(NOFF > 0 ? NOFF : 1) * FRAG_ELEMS];  // G_ij = (K K^T)_ij, i > j (fragment blocks)
+    DT Tb[2][G::NT * FRAG_ELEMS];            // -T_ii diag(beta_i) (fragment blocks)
+    float betas[3][C];
 };
 
 template <typename DT, int DK, int C, int NW>
@@ -756,24 +833,72 @@ constexpr bool pipelined_fits() {
     return sizeof(PipeSmem<DT, DK, C, NW>) <= 160 * 1024;
 }
 
+// Preparation wave W.  Chunk m's K, Q, V go to buffer set m % 3 by DMA issued
+// two periods before the period that reads them; its Gram tiles and diagonal
+// inverses go to buffers m & 1.  In the period of chunk c the wave issues the
+// loads of chunk c+3 (into the set chunk c has just vacated), computes the
+// Gram tiles and diagonal inverses of chunk c+1, waits for the loads of chunk
+// c+2 and publishes them at the barrier.
+template <typename DT, int DK, int C, int NW, int W>
+__device__ __forceinline__ void prep_role(PipeSmem<DT, DK, C, NW> &sm, const HeadPtrs<DT> &p,
+                                          int T, int N, int lane) {
+    typedef ChunkCfg<DT, DK, C, NW> G;
+    typedef DmaStage<DT, DK, C, NW, W> D;
+    D dma;
+    dma.init(p, lane);
+    const int ptid = 64 * W + lane;
+    // upper blocks of Ps stay zero for the whole sequence
+    for (int i = ptid; i < 2 * C * G::LDP; i += G::NTHR) (&sm.Ps[0][0])[i] = from_f32<DT>(0.f);
+    DT b0, b1, bq[2];  // beta of chunks in flight (bq[m & 1] holds chunk m + 2)
+    dma.issue(p, T, 0, sm.Ks[0], sm.Qs[0], sm.Vs[0], b0, lane);
+    dma.issue(p, T, 1, sm.Ks[1], sm.Qs[1], sm.Vs[1], b1, lane);
+    dma.issue(p, T, 2, sm.Ks[2], sm.Qs[2], sm.Vs[2], bq[0], lane);
+    wait_vmcnt<2 * D::NVMEM>();  // chunk 0 landed
+    if (W == 0 && lane < C) sm.betas[0][lane] = to_f32(b0);
+    lds_barrier();  // chunk 0 staged
+    if (N > 0)
+        gram_tiles_w<DT, DK, C, NW, W>(sm.Ks[0], sm.Qs[0], sm.betas[0], sm.Ab[0], sm.Tb[0], sm.Ps[0],
+                                       lane);
+    wait_vmcnt<D::NVMEM>();  // chunk 1 landed
+    if (W == 0 && lane < C) sm.betas[1][lane] = to_f32(b1);
+    lds_barrier();  // Gram tiles of chunk 0 done, chunk 1 staged
+    auto period = [&](int c, auto parity, DT &bcur, DT &bnext) {
+        constexpr int b1p = decltype(parity)::value ^ 1;
+        const int s0 = c % 3, s1 = (c + 1) % 3, s2 = (c + 2) % 3;
+        dma.issue(p, T, c + 3, sm.Ks[s0], sm.Qs[s0], sm.Vs[s0], bnext, lane);
+        if (c + 1 < N)
+            gram_tiles_w<DT, DK, C, NW, W>(sm.Ks[s1], sm.Qs[s1], sm.betas[s1], sm.Ab[b1p],
+                                           sm.Tb[b1p], sm.Ps[b1p], lane);
+        wait_vmcnt<D::NVMEM>();  // chunk c+2 landed
+        if (W == 0 && lane < C) sm.betas[s2][lane] = to_f32(bcur);
+        lds_barrier();
+    };
+    for (int c = 0; c < N; c += 2) {
+        period(c, Parity<0>(), bq[0], bq[1]);
+        if (c + 1 < N) period(c + 1, Parity<1>(), bq[1], bq[0]);
+    }
+    // the loads of the last chunks (past the sequence: nothing) drain here
+    wait_vmcnt<0>();
+}
+
 // 2*NW waves: waves 0 .. NW-1 are state waves (wave w owns value rows
 // 16w .. 16w+15 of the workgroup's tile and keeps them in registers), waves
-// NW .. 2NW-1 are preparation waves (Gram tiles, diagonal inverses, staging
-// of the inputs).  Each SIMD runs one wave of each role, so the latency of one
-// role's LDS reads and MFMA chains hides behind the other's issue (with NW
-// <= 2 the waves spread over distinct SIMDs and may use all their registers).
-// One barrier per chunk; in the period of chunk c (b = c & 1, b1 = b ^ 1):
+// NW .. 2NW-1 are preparation waves (input staging by DMA, Gram tiles,
+// diagonal inverses).  Each SIMD runs one wave of each role, so the latency
+// of one role's LDS reads and MFMA chains hides behind the other's issue
+// (with NW <= 2 the waves spread over distinct SIMDs and may use all their
+// registers).  One barrier per chunk; in the period of chunk c:
 //
-//   state: R, E, S^T += K^T E and the outputs of chunk c (X, Y and the K^T,
-//          V, beta operands already in registers; A, T and P blocks from
-//          buffers b); then the K^T, V, beta operands of chunk c+1 and
-//          X = K S^T, Y = S Q^T of chunk c+1 (K, Q, V, beta buffers b1)
-//   prep:  Gram tiles and diagonal inverses of chunk c+1 (K, Q, beta
-//          buffers b1 -> A, T, P buffers b1); chunk c+2 from registers into
-//          K, Q, V, beta buffers b; chunk c+3 loads into registers
+//   state: the block substitution, S^T += K^T E and the outputs of chunk c
+//          (X, Y and the K^T operands already in registers; A, T and P
+//          blocks from buffers c & 1); then V, X = K S^T - V, Y = S Q^T and
+//          the K^T operands of chunk c+1 (K, Q, V set (c+1) % 3)
+//   prep:  loads of chunk c+3 into set c % 3; Gram tiles and diagonal
+//          inverses of chunk c+1 (set (c+1) % 3 -> buffers (c+1) & 1); wait
+//          for chunk c+2 (set (c+2) % 3)
 //
-// Within a period the state waves read only A, T, P buffers b and K, Q, V,
-// beta buffers b1, and the preparation waves write only the others.
+// Within a period the state waves read only A, T, P buffers c & 1 and K, Q, V
+// set (c+1) % 3, and the preparation waves write only the others.
 template <typename DT, int DK, int C, int NW>
 __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4 + 1, NW / 4 + 1))) void chunk_fwd_ws_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
@@ -809,9 +934,11 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4
             op.load_kt(sm.Ks[0], lane);
         }
         lds_barrier();  // Gram tiles of chunk 0 done, chunk 1 staged
-        // the loop is unrolled by two so that the buffer index is a constant
-        auto period = [&](int c, auto parity) {
-            constexpr int b = decltype(parity)::value, b1 = b ^ 1;
+        // the loop is unrolled by three so that the K, Q, V set index is a
+        // constant (these tiles take most of the state waves' LDS reads)
+        auto period = [&](int c, auto set) {
+            constexpr int s1 = (decltype(set)::value + 1) % 3;  // set of chunk c+1
+            const int b = c & 1;
             const int t0 = c * C;
             const int len = min(C, T - t0);
             out.rsrc = make_rsrc(p.oh + (int64_t)t0 * p.tsv, len * out.row_bytes);
@@ -819,15 +946,16 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4
             if (c + 1 < N) {
                 // V first (X starts at -V); the K^T fragments of the next
                 // state update only after X and Y have used their operands
-                op.load_v(sm.Vs[b1], wave, lane);
-                state_xy<DT, DK, C, NW>(sm.Ks[b1], sm.Qs[b1], Sacc, op.fv, X, Y, lane);
-                op.load_kt(sm.Ks[b1], lane);
+                op.load_v(sm.Vs[s1], wave, lane);
+                state_xy<DT, DK, C, NW>(sm.Ks[s1], sm.Qs[s1], Sacc, op.fv, X, Y, lane);
+                op.load_kt(sm.Ks[s1], lane);
             }
             lds_barrier();
         };
-        for (int c = 0; c < N; c += 2) {
+        for (int c = 0; c < N; c += 3) {
             period(c, Parity<0>());
             if (c + 1 < N) period(c + 1, Parity<1>());
+            if (c + 2 < N) period(c + 2, Parity<2>());
         }
         if (S_T) {
 #pragma unroll
@@ -836,42 +964,13 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4
         }
     } else {
         // --------------------------- preparation waves ---------------------------
-        // Two register sets alternate: chunk m is loaded into set m & 1 two
-        // periods before it is staged, so its loads have two periods to land.
-        const int pw = wave - NW, ptid = tid - 64 * NW;
+        __builtin_amdgcn_s_setprio(3);
         const HeadPtrs<DT> p = head_ptrs<DT, DK, NW>(q, k, v, beta, o, T, H, Dv, nvt, 0, r);
-        ChunkRegs<DT, DK, C, NW> rga, rgb;
-        rga.init(p, ptid);
-        rgb = rga;
-        // upper blocks of Ps stay zero for the whole sequence
-        for (int i = ptid; i < 2 * C * G::LDP; i += G::NTHR) (&sm.Ps[0][0])[i] = from_f32<DT>(0.f);
-        // Loads are issued unconditionally (chunks past the end load nothing),
-        // so the number of loads in flight is the same on every path and each
-        // wait for a register set covers only that set's loads.
-        rga.load(p, T, 0);
-        rgb.load(p, T, C);
-        if (N > 0) rga.stage(sm.Ks[0], sm.Qs[0], sm.Vs[0], sm.betas[0], ptid);
-        rga.load(p, T, 2 * C);
-        lds_barrier();  // chunk 0 staged
-        if (N > 0)
-            gram_tiles<DT, DK, C, NW>(sm.Ks[0], sm.Qs[0], sm.betas[0], sm.Ab[0], sm.Tb[0], sm.Ps[0],
-                                      pw, lane);
-        if (N > 1) rgb.stage(sm.Ks[1], sm.Qs[1], sm.Vs[1], sm.betas[1], ptid);
-        lds_barrier();  // Gram tiles of chunk 0 done, chunk 1 staged
-        // period c: rcur holds chunk c+2, rnext receives chunk c+3
-        auto period = [&](int c, auto parity, ChunkRegs<DT, DK, C, NW> &rcur,
-                          ChunkRegs<DT, DK, C, NW> &rnext) {
-            constexpr int b = decltype(parity)::value, b1 = b ^ 1;
-            rnext.load(p, T, (c + 3) * C);
-            if (c + 1 < N)
-                gram_tiles<DT, DK, C, NW>(sm.Ks[b1], sm.Qs[b1], sm.betas[b1], sm.Ab[b1], sm.Tb[b1],
-                                          sm.Ps[b1], pw, lane);
-            if (c + 2 < N) rcur.stage(sm.Ks[b], sm.Qs[b], sm.Vs[b], sm.betas[b], ptid);
-            lds_barrier();
-        };
-        for (int c = 0; c < N; c += 2) {
-            period(c, Parity<0>(), rga, rgb);
-            if (c + 1 < N) period(c + 1, Parity<1>(), rgb, rga);
+        switch (wave - NW) {
+        case 0: prep_role<DT, DK, C, NW, 0>(sm, p, T, N, lane); break;
+        case 1: if constexpr (NW > 1) prep_role<DT, DK, C, NW, 1>(sm, p, T, N, lane); break;
+        case 2: if constexpr (NW > 2) prep_role<DT, DK, C, NW, 2>(sm, p, T, N, lane); break;
+        default: if constexpr (NW > 3) prep_role<DT, DK, C, NW, 3>(sm, p, T, N, lane); break;
         }
     }
 }
