@@ -250,7 +250,7 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": traffic,
-        "kernel": "chunk_fwd_pipelined_kernel<bf16, Dk=128, C=64, 4 waves>",
+        "kernel": "chunk_fwd_ws_kernel<bf16, Dk=128, C=64, NW=4> (4 state + 4 preparation waves)",
         "algorithmic_bytes_per_launch": nbytes,
         "mean_launch_us": round(launch_s * 1e6, 2),
         "mfma_frac": round(flops / launch_s / 1e12 / BF16_PEAK_TFLOPS, 4),
