@@ -829,7 +829,7 @@ struct PipeSmem {
 };
 
 template <typename DT, int DK, int C, int NW>
-constexpr bool pipelined_fits() {
+constexpr bool ws_fits() {
     return sizeof(PipeSmem<DT, DK, C, NW>) <= 160 * 1024;
 }
 
@@ -1052,7 +1052,7 @@ hipError_t launch_cfg(const void *q, const void *k, const void *v, const void *b
                       int64_t H, int Dv, hipStream_t stream) {
     const int nvt = Dv / (16 * NW);
     const int64_t grid = B * H * nvt;
-    if constexpr (pipelined_fits<DT, DK, C, NW>()) {
+    if constexpr (ws_fits<DT, DK, C, NW>()) {
         hipLaunchKernelGGL((chunk_fwd_ws_kernel<DT, DK, C, NW>), dim3((unsigned)grid),
                            dim3(128 * NW), 0, stream, static_cast<const DT *>(q),
                            static_cast<const DT *>(k), static_cast<const DT *>(v),
