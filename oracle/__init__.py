@@ -12,6 +12,9 @@ Contents
     The plain sequential recurrence in fp64 (C, ``ref_delta_rule.c``), the
     definition every GPU result is judged against.  See that file's header for
     the passages it follows.
+``gated_delta_rule_ref``
+    The same loop with a scalar forget gate alpha_t = exp(g_t) applied to the
+    whole state before each token's prediction (the gated variant).
 ``chunk_algebra``
     The chunkwise-parallel rearrangement of the same recurrence in fp64 NumPy,
     step by step as the pages state it.  It is used only to pin the oracle and
@@ -61,6 +64,9 @@ def _load():
     lib.ref_delta_rule_f64.restype = ctypes.c_int
     lib.ref_delta_rule_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp,
                                        i64, i64, i64, i64, i64, ctypes.c_int]
+    lib.ref_gated_delta_rule_f64.restype = ctypes.c_int
+    lib.ref_gated_delta_rule_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp,
+                                             i64, i64, i64, i64, i64, ctypes.c_int]
     _lib = lib
     return lib
 
@@ -78,17 +84,7 @@ def _ptr(a: np.ndarray | None):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
-def delta_rule_ref(q, k, v, beta, S0=None, nthreads: int = 1):
-    """Run the delta-rule recurrence in fp64 on the CPU.
-
-    Arguments are array-likes with the layouts q, k ``[B,T,H,Dk]``,
-    v ``[B,T,H,Dv]``, beta ``[B,T,H]`` and S0 ``[B,H,Dv,Dk]`` (or None for a
-    zero initial state).  They are widened to fp64 exactly (the caller passes
-    values already rounded to the dtype under test).
-
-    Returns ``(o, S_T)`` as fp64 NumPy arrays: o ``[B,T,H,Dv]`` and
-    S_T ``[B,H,Dv,Dk]``.
-    """
+def _check(q, k, v, beta, S0):
     q, k, v, beta = (_as_f64(x) for x in (q, k, v, beta))
     if q.ndim != 4 or k.shape != q.shape or v.ndim != 4 or beta.ndim != 3:
         raise ValueError("expected q,k [B,T,H,Dk], v [B,T,H,Dv], beta [B,T,H]")
@@ -101,6 +97,21 @@ def delta_rule_ref(q, k, v, beta, S0=None, nthreads: int = 1):
         s0 = _as_f64(S0)
         if s0.shape != (B, H, Dv, Dk):
             raise ValueError(f"S0 must be [B,H,Dv,Dk]={B, H, Dv, Dk}, got {s0.shape}")
+    return q, k, v, beta, s0, (B, T, H, Dk, Dv)
+
+
+def delta_rule_ref(q, k, v, beta, S0=None, nthreads: int = 1):
+    """Run the delta-rule recurrence in fp64 on the CPU.
+
+    Arguments are array-likes with the layouts q, k ``[B,T,H,Dk]``,
+    v ``[B,T,H,Dv]``, beta ``[B,T,H]`` and S0 ``[B,H,Dv,Dk]`` (or None for a
+    zero initial state).  They are widened to fp64 exactly (the caller passes
+    values already rounded to the dtype under test).
+
+    Returns ``(o, S_T)`` as fp64 NumPy arrays: o ``[B,T,H,Dv]`` and
+    S_T ``[B,H,Dv,Dk]``.
+    """
+    q, k, v, beta, s0, (B, T, H, Dk, Dv) = _check(q, k, v, beta, S0)
     o = np.zeros((B, T, H, Dv), dtype=np.float64)
     st = np.zeros((B, H, Dv, Dk), dtype=np.float64)
     rc = _load().ref_delta_rule_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(beta),
@@ -111,4 +122,24 @@ def delta_rule_ref(q, k, v, beta, S0=None, nthreads: int = 1):
     return o, st
 
 
-__all__ = ["build", "delta_rule_ref"]
+def gated_delta_rule_ref(q, k, v, beta, g, S0=None, nthreads: int = 1):
+    """The gated recurrence in fp64 on the CPU: before each token the whole
+    state is multiplied by alpha_t = exp(g_t), then the token is predicted,
+    corrected and written as in ``delta_rule_ref``.  g is ``[B,T,H]`` (the
+    natural log of the forget gate); the other arguments and the return value
+    are as in ``delta_rule_ref``."""
+    q, k, v, beta, s0, (B, T, H, Dk, Dv) = _check(q, k, v, beta, S0)
+    g = _as_f64(g)
+    if g.shape != (B, T, H):
+        raise ValueError(f"g must be [B,T,H]={B, T, H}, got {g.shape}")
+    o = np.zeros((B, T, H, Dv), dtype=np.float64)
+    st = np.zeros((B, H, Dv, Dk), dtype=np.float64)
+    rc = _load().ref_gated_delta_rule_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                                          _ptr(s0), _ptr(o), _ptr(st),
+                                          B, T, H, Dk, Dv, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle failed with code {rc}")
+    return o, st
+
+
+__all__ = ["build", "delta_rule_ref", "gated_delta_rule_ref"]

@@ -28,6 +28,18 @@ decay taken as the identity (plain DeltaNet) and no output scale:
 
 Every array here is per head: K, Q ``[L, Dk]``, V ``[L, Dv]``, beta ``[L]``,
 S ``[Dv, Dk]``.
+
+The gated functions take the same section with a scalar decay per token,
+D_i = alpha_i I, alpha_i = exp(g_i) (section "Gated DeltaNet : oublier
+d'abord l'etat entier" of the same digest for the recurrence): the cumulative
+decay from the chunk boundary to token i is gamma_i = exp(b_i) with b the
+in-chunk prefix sum of g (section "Pipeline Triton Chunkwise": differences of
+prefix sums of the log decay stand for D_{j+1:i} = gamma_i / gamma_j), so
+
+    e_bar_i = beta_i (v_i - gamma_i S_c k_i)
+    rho_ij  = beta_i (gamma_i / gamma_j) k_j^T k_i            (j < i)
+    S_{c+1} = gamma_last S_c + sum_j (gamma_last / gamma_j) e_j k_j^T
+    O_i     = gamma_i S_c q_i + sum_{j <= i} (gamma_i / gamma_j) (k_j^T q_i) e_j
 """
 from __future__ import annotations
 
@@ -89,6 +101,51 @@ def chunk_forward_head(Q, K, V, beta, S0=None, chunk=64):
     return O, S
 
 
+def gated_chunk_step(S, Q, K, V, beta, g):
+    """Advance one chunk of the gated recurrence from its incoming state S.
+
+    Returns (O_c, E_c, S_next); g is the chunk's log decay per token."""
+    S, Q, K, V, beta, g = (_f64(x) for x in (S, Q, K, V, beta, g))
+    L = K.shape[0]
+    b = np.cumsum(g)                       # log of the decay from the boundary
+    gam = np.exp(b)
+    ratio = np.exp(b[:, None] - b[None, :])  # gamma_i / gamma_j
+    # provisional errors against the decayed incoming state
+    E_bar = beta[:, None] * (V - gam[:, None] * (K @ S.T))
+    # causal coupling with the decay between the two tokens, strictly lower
+    R = np.tril(beta[:, None] * ratio * (K @ K.T), -1)
+    E = solve_triangular(np.eye(L) + R, E_bar, lower=True, unit_diagonal=True)
+    # end-of-chunk state: the incoming state decays through the whole chunk,
+    # each write only through the tokens after it
+    to_end = np.exp(b[-1] - b)
+    S_next = gam[-1] * S + (to_end[:, None] * E).T @ K
+    # outputs: decayed incoming state plus the decayed writes, diagonal included
+    A_qk = np.tril(ratio * (Q @ K.T))
+    O = gam[:, None] * (Q @ S.T) + A_qk @ E
+    return O, E, S_next
+
+
+def gated_chunk_forward(q, k, v, beta, g, S0=None, chunk=64):
+    """Gated chunkwise forward over the op layout (g [B,T,H]).  Returns
+    (o, S_T) in fp64."""
+    q, k, v, beta, g = (_f64(x) for x in (q, k, v, beta, g))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[3]
+    s0 = None if S0 is None else _f64(S0)
+    o = np.zeros((B, T, H, Dv))
+    st = np.zeros((B, H, Dv, Dk))
+    for bb in range(B):
+        for h in range(H):
+            S = np.zeros((Dv, Dk)) if s0 is None else s0[bb, h].copy()
+            for c0 in range(0, T, chunk):
+                sl = slice(c0, min(c0 + chunk, T))
+                o[bb, sl, h], _, S = gated_chunk_step(S, q[bb, sl, h], k[bb, sl, h],
+                                                      v[bb, sl, h], beta[bb, sl, h],
+                                                      g[bb, sl, h])
+            st[bb, h] = S
+    return o, st
+
+
 def chunk_forward(q, k, v, beta, S0=None, chunk=64):
     """Chunkwise forward over the op layout: q,k [B,T,H,Dk], v [B,T,H,Dv],
     beta [B,T,H], S0 [B,H,Dv,Dk] or None.  Returns (o, S_T) in fp64."""
@@ -106,4 +163,5 @@ def chunk_forward(q, k, v, beta, S0=None, chunk=64):
     return o, st
 
 
-__all__ = ["ut_transform", "chunk_step", "chunk_forward_head", "chunk_forward"]
+__all__ = ["ut_transform", "chunk_step", "chunk_forward_head", "chunk_forward",
+           "gated_chunk_step", "gated_chunk_forward"]

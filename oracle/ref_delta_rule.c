@@ -33,14 +33,32 @@
  *
  * Layouts (row-major, contiguous): q, k [B,T,H,Dk]; v, o [B,T,H,Dv];
  * beta [B,T,H]; S0, S_T [B,H,Dv,Dk].  S0 may be NULL (zero state).
+ *
+ * Gated variant (ref_gated_delta_rule_f64): one more input g [B,T,H], the
+ * natural log of a scalar forget gate alpha_t = exp(g_t).  Each token first
+ * decays the whole state, then predicts, corrects and writes:
+ *
+ *       S   = alpha_t S             forget (the whole matrix, one scalar)
+ *       p   = S k_t                 prediction from the decayed state
+ *       u   = beta_t (v_t - p)
+ *       S   = S + u k_t^T
+ *       o_t = S q_t
+ *
+ * Source: hada.io digest, section "Gated DeltaNet : oublier d'abord l'etat
+ * entier" (forget, predict, correct, write, in that order, with the decayed
+ * state used for the prediction); houmin.site "infra/delta-net", section
+ * "Gated DeltaNet" (S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t
+ * k_t^T).  alpha_t = exp(g_t) is evaluated with the C library's exp in fp64;
+ * g_t = 0 gives alpha_t = 1 exactly, i.e. the ungated recurrence bit for bit.
  */
+#include <math.h>
 #include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 typedef struct {
-    const double *q, *k, *v, *beta, *S0;
+    const double *q, *k, *v, *beta, *g, *S0;
     double *o, *S_T;
     int64_t B, T, H, Dk, Dv;
     int64_t next; /* next (b,h) pair to take; shared work counter */
@@ -65,7 +83,15 @@ static void one_head(const oracle_job *J, int64_t b, int64_t h, double *S, doubl
         const double bt = J->beta[row];
         double *ot = J->o + row * Dv;
 
-        /* u = beta_t (v_t - S k_t), with S the state before this token */
+        /* forget: S = alpha_t S (gated variant only) */
+        if (J->g) {
+            const double at = exp(J->g[row]);
+            for (int64_t i = 0; i < Dv * Dk; ++i)
+                S[i] = at * S[i];
+        }
+
+        /* u = beta_t (v_t - S k_t), with S the (decayed) state before this
+         * token's write */
         for (int64_t i = 0; i < Dv; ++i) {
             double p = 0.0;
             for (int64_t j = 0; j < Dk; ++j)
@@ -110,24 +136,16 @@ static void *worker(void *arg)
     return NULL;
 }
 
-/*
- * Runs the recurrence for every (b,h).  Work is split over `nthreads` POSIX
- * threads by (b,h) pair only; each pair is computed by one thread in token
- * order, so the result does not depend on the thread count.
- * Returns 0 on success, -1 on bad arguments, -2 on allocation or thread
- * failure.
- */
-int ref_delta_rule_f64(const double *q, const double *k, const double *v,
-                       const double *beta, const double *S0, double *o,
-                       double *S_T, int64_t B, int64_t T, int64_t H,
-                       int64_t Dk, int64_t Dv, int nthreads)
+static int run(const double *q, const double *k, const double *v, const double *beta,
+               const double *g, const double *S0, double *o, double *S_T, int64_t B,
+               int64_t T, int64_t H, int64_t Dk, int64_t Dv, int nthreads)
 {
     if (!q || !k || !v || !beta || !o || B < 0 || T < 0 || H < 0 || Dk < 1 ||
         Dv < 1)
         return -1;
     if (nthreads < 1)
         nthreads = 1;
-    oracle_job J = {q, k, v, beta, S0, o, S_T, B, T, H, Dk, Dv, 0, 0};
+    oracle_job J = {q, k, v, beta, g, S0, o, S_T, B, T, H, Dk, Dv, 0, 0};
     if (B * H == 0)
         return 0;
     if (nthreads > B * H)
@@ -147,4 +165,30 @@ int ref_delta_rule_f64(const double *q, const double *k, const double *v,
         pthread_join(tid[i], NULL);
     free(tid);
     return J.failed ? -2 : 0;
+}
+
+/*
+ * Runs the recurrence for every (b,h).  Work is split over `nthreads` POSIX
+ * threads by (b,h) pair only; each pair is computed by one thread in token
+ * order, so the result does not depend on the thread count.
+ * Returns 0 on success, -1 on bad arguments, -2 on allocation or thread
+ * failure.
+ */
+int ref_delta_rule_f64(const double *q, const double *k, const double *v,
+                       const double *beta, const double *S0, double *o,
+                       double *S_T, int64_t B, int64_t T, int64_t H,
+                       int64_t Dk, int64_t Dv, int nthreads)
+{
+    return run(q, k, v, beta, NULL, S0, o, S_T, B, T, H, Dk, Dv, nthreads);
+}
+
+/* The gated recurrence (g = log alpha, [B,T,H], required); otherwise as above. */
+int ref_gated_delta_rule_f64(const double *q, const double *k, const double *v,
+                             const double *beta, const double *g, const double *S0,
+                             double *o, double *S_T, int64_t B, int64_t T, int64_t H,
+                             int64_t Dk, int64_t Dv, int nthreads)
+{
+    if (!g)
+        return -1;
+    return run(q, k, v, beta, g, S0, o, S_T, B, T, H, Dk, Dv, nthreads);
 }
