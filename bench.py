@@ -17,9 +17,11 @@ JSON line on stdout:
   parity       the timed run's outputs against that oracle run
   decode       256 back-to-back single-token steps of the decode workload
                (B=128, H=16, d=128), HBM bytes per step and tokens/s
+  gated        the gated rule (per-token log forget gate) on the layer shape
+               (chunked forward) and on the decode workload
 
 Options: --gpus N (only 1: this build targets one GPU), --steps K,
---warmup W, --no-cpu-baseline, --no-decode, --copy-calib BYTES (also time a
+--warmup W, --no-cpu-baseline, --no-decode, --no-gated, --copy-calib BYTES (also time a
 plain device copy of that size, for counter calibration runs).
 """
 from __future__ import annotations
@@ -40,7 +42,8 @@ METRIC = ("delta-rule fwd tokens/sec at H=16,d=128,T=2048; "
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published (256 CU x 2.4 GHz x 4096)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_layer_1p3b_traffic.txt")
-KERNEL_SOURCES = ["deltanet_delta_rule_amd/csrc/chunk_fwd.hip",
+KERNEL_SOURCES = ["deltanet_delta_rule_amd/csrc/chunk_fwd.hpp",
+                  "deltanet_delta_rule_amd/csrc/chunk_fwd.hip",
                   "deltanet_delta_rule_amd/csrc/dr_common.hpp",
                   "deltanet_delta_rule_amd/build.py"]  # compile flags
 
@@ -60,16 +63,18 @@ def chunk_work(w):
     e = 2 if w.dtype == "bf16" else 4
     flops = th * (2 * w.chunk * (3 * w.Dk + 2 * w.Dv) + 6 * w.Dk * w.Dv)
     nbytes = th * e * (2 * w.Dk + w.Dv + 1) + th * e * w.Dv
+    nbytes += th * 4 if w.gate_amax > 0 else 0  # fp32 log gates
     nbytes += 4 * w.B * w.H * w.Dv * w.Dk * ((1 if w.s0_std > 0 else 0) + 1)
     return flops, nbytes
 
 
 def decode_bytes(w):
     """HBM bytes of one decode step: S read and written (fp32), q, k, v, beta
-    read and o written in the input dtype."""
+    read and o written in the input dtype, plus the fp32 log gate when gated."""
     e = 2 if w.dtype == "bf16" else 4
     bh = w.B * w.H
-    return bh * (8 * w.Dv * w.Dk + e * (2 * w.Dk + w.Dv + 1) + e * w.Dv)
+    return bh * (8 * w.Dv * w.Dk + e * (2 * w.Dk + w.Dv + 1) + e * w.Dv
+                 + (4 if w.gate_amax > 0 else 0))
 
 
 def source_digest():
@@ -138,19 +143,23 @@ def run_cpu_baseline(x, w, o_gpu, st_gpu):
     return base, par
 
 
-def bench_decode(torch, dr, W, reps=3):
-    w = W.get("decode")
+def bench_decode(torch, dr, W, reps=3, name="decode"):
+    w = W.get(name)
     x = W.generate(w)
     dev = torch.device("cuda:0")
-    d = {n: t.to(dev) for n, t in x.items()}
+    d = {n: (None if t is None else t.to(dev)) for n, t in x.items()}
     S = d["S0"].clone()
     outs = [torch.empty((w.B, w.H, w.Dv), dtype=w.torch_dtype, device=dev)
             for _ in range(w.T)]
 
     def run():
         for t in range(w.T):
-            dr.delta_rule_recurrent_step(d["q"][t], d["k"][t], d["v"][t], d["beta"][t], S,
-                                         o=outs[t])
+            if d["g"] is None:
+                dr.delta_rule_recurrent_step(d["q"][t], d["k"][t], d["v"][t], d["beta"][t], S,
+                                             o=outs[t])
+            else:
+                dr.gated_delta_rule_recurrent_step(d["q"][t], d["k"][t], d["v"][t],
+                                                   d["beta"][t], d["g"][t], S, o=outs[t])
 
     run()  # warm-up
     times = []
@@ -167,11 +176,48 @@ def bench_decode(torch, dr, W, reps=3):
     per_step = t / w.T
     gbs = decode_bytes(w) / per_step / 1e9
     return {
-        "workload": "decode B128 H16 d128, 256 steps, bf16 in, fp32 state",
+        "workload": (f"{w.name} B{w.B} H{w.H} d{w.Dk}, {w.T} steps, bf16 in, fp32 state"
+                     + (", log gates fp32" if w.gate_amax > 0 else "")),
         "tokens_per_s": w.B * w.T / t,
         "us_per_step": per_step * 1e6,
         "hbm_gbs_algorithmic": gbs,
         "hbm_frac": gbs / HBM_PEAK_GBS,
+    }
+
+
+def bench_gated_chunk(torch, dr, W, reps=20):
+    """The gated chunked forward on the layer shape (mean launch time with HIP
+    events on the launch stream)."""
+    w = W.get("gated_layer_1p3b")
+    x = W.generate(w)
+    dev = torch.device("cuda:0")
+    d = {n: (None if t is None else t.to(dev)) for n, t in x.items()}
+    o = torch.empty((w.B, w.T, w.H, w.Dv), dtype=w.torch_dtype, device=dev)
+    st = torch.empty((w.B, w.H, w.Dv, w.Dk), dtype=torch.float32, device=dev)
+
+    def step():
+        dr.gated_delta_rule_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["S0"],
+                                      chunk=w.chunk, o=o, S_T=st)
+
+    for _ in range(3):
+        step()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    launch_s = sum(a.elapsed_time(b) for a, b in ev) / reps / 1e3
+    flops, nbytes = chunk_work(w)
+    return {
+        "workload": (f"{w.name} B{w.B} H{w.H} T{w.T} d{w.Dk} chunk {w.chunk}, bf16 in, "
+                     "fp32 log gates and state"),
+        "tokens_per_s": w.B * w.T / launch_s,
+        "mean_launch_us": round(launch_s * 1e6, 2),
+        "hbm_frac": round(nbytes / launch_s / 1e9 / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(flops / launch_s / 1e12 / BF16_PEAK_TFLOPS, 4),
     }
 
 
@@ -183,6 +229,8 @@ def main():
     ap.add_argument("--workload", default="layer_1p3b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-gated", action="store_true",
+                    help="skip the gated-rule lines (chunked layer shape and decode)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="also run a device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -277,6 +325,11 @@ def main():
     if not args.no_decode:
         log("decode: 256 steps of B128 H16 d128")
         out["decode"] = bench_decode(torch, dr, W)
+    if not args.no_gated:
+        log("gated rule: layer shape chunked forward, then 256 decode steps")
+        out["gated"] = {"chunk": bench_gated_chunk(torch, dr, W)}
+        if not args.no_decode:
+            out["gated"]["decode"] = bench_decode(torch, dr, W, name="gated_decode")
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle on the whole workload")
         torch.cuda.synchronize()

@@ -10,6 +10,11 @@ is not built, the first call raises.
 
     o, S_T = delta_rule_chunk_fwd(q, k, v, beta, S0=None, chunk=64)
     o      = delta_rule_recurrent_step(q, k, v, beta, S)   # S updated in place
+
+and the gated rule (g = log of the per-token, per-head forget gate, fp32):
+
+    o, S_T = gated_delta_rule_chunk_fwd(q, k, v, beta, g, S0=None, chunk=64)
+    o      = gated_delta_rule_recurrent_step(q, k, v, beta, g, S)
 """
 from __future__ import annotations
 
@@ -19,6 +24,8 @@ import os
 __all__ = [
     "delta_rule_chunk_fwd",
     "delta_rule_recurrent_step",
+    "gated_delta_rule_chunk_fwd",
+    "gated_delta_rule_recurrent_step",
     "delta_rule_status_string",
     "delta_rule_version",
     "DeltaRuleError",
@@ -55,6 +62,12 @@ def load_library():
     lib.delta_rule_recurrent_step.restype = i32
     lib.delta_rule_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp,
                                               i64, i64, i64, i64, i32, vp]
+    lib.gated_delta_rule_chunk_fwd.restype = i32
+    lib.gated_delta_rule_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
+                                               i64, i64, i64, i64, i64, i64, i32, vp]
+    lib.gated_delta_rule_recurrent_step.restype = i32
+    lib.gated_delta_rule_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp,
+                                                    i64, i64, i64, i64, i32, vp]
     lib.delta_rule_status_string.restype = ctypes.c_char_p
     lib.delta_rule_status_string.argtypes = [i32]
     lib.delta_rule_last_hip_error.restype = i32
@@ -119,18 +132,11 @@ def _need(t, name, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def delta_rule_chunk_fwd(q, k, v, beta, S0=None, *, chunk: int = 64,
-                         output_final_state: bool = True, o=None, S_T=None,
-                         stream=None):
-    """Chunkwise forward.  q, k ``[B,T,H,Dk]``; v ``[B,T,H,Dv]``; beta
-    ``[B,T,H]`` (float32 or bfloat16, all the same dtype, on one GPU);
-    S0 ``[B,H,Dv,Dk]`` float32 or None.  Returns ``(o, S_T)``; S_T is None
-    when ``output_final_state`` is False.  ``o`` / ``S_T`` may be passed in
-    (S_T may be S0 itself to carry the state in place)."""
+def _chunk_call(entry, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, stream):
     torch = _torch()
     dev = q.device
     if dev.type != "cuda":
-        raise ValueError("delta_rule_chunk_fwd needs GPU tensors")
+        raise ValueError("the chunked forward needs GPU tensors")
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
     dt = q.dtype
@@ -139,6 +145,8 @@ def delta_rule_chunk_fwd(q, k, v, beta, S0=None, *, chunk: int = 64,
     _need(k, "k", (B, T, H, Dk), dt, dev)
     _need(v, "v", (B, T, H, Dv), dt, dev)
     _need(beta, "beta", (B, T, H), dt, dev)
+    if g is not None:
+        _need(g, "g", (B, T, H), torch.float32, dev)
     if S0 is not None:
         _need(S0, "S0", (B, H, Dv, Dk), torch.float32, dev)
     if o is None:
@@ -152,20 +160,42 @@ def delta_rule_chunk_fwd(q, k, v, beta, S0=None, *, chunk: int = 64,
             _need(S_T, "S_T", (B, H, Dv, Dk), torch.float32, dev)
     else:
         S_T = None
-    st = load_library().delta_rule_chunk_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T),
+    ptrs = [_ptr(q), _ptr(k), _ptr(v), _ptr(beta)]
+    if entry == "gated_delta_rule_chunk_fwd":
+        ptrs.append(_ptr(g))
+    st = getattr(load_library(), entry)(
+        *ptrs, _ptr(S0), _ptr(o), _ptr(S_T),
         B, T, H, Dk, Dv, int(chunk), _dtype_code(q), _stream(dev, stream))
     _check(st)
     return o, S_T
 
 
-def delta_rule_recurrent_step(q, k, v, beta, S, *, o=None, stream=None):
-    """One decode token: q, k ``[B,H,Dk]``; v ``[B,H,Dv]``; beta ``[B,H]``;
-    S ``[B,H,Dv,Dk]`` float32, updated in place.  Returns o ``[B,H,Dv]``."""
+def delta_rule_chunk_fwd(q, k, v, beta, S0=None, *, chunk: int = 64,
+                         output_final_state: bool = True, o=None, S_T=None,
+                         stream=None):
+    """Chunkwise forward.  q, k ``[B,T,H,Dk]``; v ``[B,T,H,Dv]``; beta
+    ``[B,T,H]`` (float32 or bfloat16, all the same dtype, on one GPU);
+    S0 ``[B,H,Dv,Dk]`` float32 or None.  Returns ``(o, S_T)``; S_T is None
+    when ``output_final_state`` is False.  ``o`` / ``S_T`` may be passed in
+    (S_T may be S0 itself to carry the state in place)."""
+    return _chunk_call("delta_rule_chunk_fwd", q, k, v, beta, None, S0, chunk,
+                       output_final_state, o, S_T, stream)
+
+
+def gated_delta_rule_chunk_fwd(q, k, v, beta, g, S0=None, *, chunk: int = 64,
+                               output_final_state: bool = True, o=None, S_T=None,
+                               stream=None):
+    """Chunkwise forward of the gated rule: as ``delta_rule_chunk_fwd`` plus
+    g ``[B,T,H]`` float32, the log of each token's forget gate (<= 0)."""
+    return _chunk_call("gated_delta_rule_chunk_fwd", q, k, v, beta, g, S0, chunk,
+                       output_final_state, o, S_T, stream)
+
+
+def _step_call(entry, q, k, v, beta, g, S, o, stream):
     torch = _torch()
     dev = q.device
     if dev.type != "cuda":
-        raise ValueError("delta_rule_recurrent_step needs GPU tensors")
+        raise ValueError("the decode step needs GPU tensors")
     B, H, Dk = q.shape
     Dv = v.shape[-1]
     dt = q.dtype
@@ -174,13 +204,29 @@ def delta_rule_recurrent_step(q, k, v, beta, S, *, o=None, stream=None):
     _need(k, "k", (B, H, Dk), dt, dev)
     _need(v, "v", (B, H, Dv), dt, dev)
     _need(beta, "beta", (B, H), dt, dev)
+    if g is not None:
+        _need(g, "g", (B, H), torch.float32, dev)
     _need(S, "S", (B, H, Dv, Dk), torch.float32, dev)
     if o is None:
         o = torch.empty((B, H, Dv), dtype=dt, device=dev)
     else:
         _need(o, "o", (B, H, Dv), dt, dev)
-    st = load_library().delta_rule_recurrent_step(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S), _ptr(o),
-        B, H, Dk, Dv, _dtype_code(q), _stream(dev, stream))
+    ptrs = [_ptr(q), _ptr(k), _ptr(v), _ptr(beta)]
+    if entry == "gated_delta_rule_recurrent_step":
+        ptrs.append(_ptr(g))
+    st = getattr(load_library(), entry)(
+        *ptrs, _ptr(S), _ptr(o), B, H, Dk, Dv, _dtype_code(q), _stream(dev, stream))
     _check(st)
     return o
+
+
+def delta_rule_recurrent_step(q, k, v, beta, S, *, o=None, stream=None):
+    """One decode token: q, k ``[B,H,Dk]``; v ``[B,H,Dv]``; beta ``[B,H]``;
+    S ``[B,H,Dv,Dk]`` float32, updated in place.  Returns o ``[B,H,Dv]``."""
+    return _step_call("delta_rule_recurrent_step", q, k, v, beta, None, S, o, stream)
+
+
+def gated_delta_rule_recurrent_step(q, k, v, beta, g, S, *, o=None, stream=None):
+    """One decode token of the gated rule: as ``delta_rule_recurrent_step``
+    plus g ``[B,H]`` float32, the log forget gate of this token."""
+    return _step_call("gated_delta_rule_recurrent_step", q, k, v, beta, g, S, o, stream)

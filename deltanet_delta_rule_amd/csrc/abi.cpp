@@ -47,15 +47,12 @@ dr_status hip_status(hipError_t e) {
     return DR_ERR_HIP;
 }
 
-}  // namespace
-
-extern "C" {
-
-dr_status delta_rule_chunk_fwd(const void *q, const void *k, const void *v,
-                               const void *beta, const float *S0, void *o,
-                               float *S_T, int64_t B, int64_t T, int64_t H,
-                               int64_t Dk, int64_t Dv, int64_t chunk,
-                               dr_dtype dtype, void *stream) {
+// Shared validation and dispatch of the chunked forward; g (log forget gate,
+// fp32 [B,T,H]) is nullptr for the plain rule and required for the gated one.
+dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *beta,
+                    const float *g, bool gated, const float *S0, void *o, float *S_T,
+                    int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t chunk,
+                    dr_dtype dtype, void *stream) {
     if (dtype != DR_F32 && dtype != DR_BF16) return DR_ERR_INVALID_ARG;
     if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0 || chunk < 0) return DR_ERR_INVALID_ARG;
     if (!supported_dim(Dk) || !supported_dim(Dv) || !supported_chunk(chunk))
@@ -75,6 +72,7 @@ dr_status delta_rule_chunk_fwd(const void *q, const void *k, const void *v,
     if (span < 0 || span > INT32_MAX / 2) return DR_ERR_UNSUPPORTED;
 
     if (T > 0 && (!q || !k || !v || !beta || !o)) return DR_ERR_INVALID_ARG;
+    if (gated && T > 0 && !g) return DR_ERR_INVALID_ARG;
     // q, k and the states are read in 16-byte vectors; v, beta and o element-wise
     const void *vec_ptrs[] = {q, k, S0, S_T};
     for (const void *p : vec_ptrs)
@@ -82,9 +80,10 @@ dr_status delta_rule_chunk_fwd(const void *q, const void *k, const void *v,
     const void *elem_ptrs[] = {v, beta, o};
     for (const void *p : elem_ptrs)
         if (p && !aligned_to(p, esz)) return DR_ERR_INVALID_ARG;
+    if (g && !aligned_to(g, 4)) return DR_ERR_INVALID_ARG;
 
     const Span in[] = {{q, nqk * esz}, {k, nqk * esz}, {v, nv * esz}, {beta, nb * esz},
-                       {S0, ns * 4}};
+                       {S0, ns * 4}, {gated ? g : nullptr, nb * 4}};
     const Span so{o, nv * esz}, sst{S_T, ns * 4};
     for (const Span &s : in) {
         if (T > 0 && overlaps(so, s)) return DR_ERR_INVALID_ARG;
@@ -93,15 +92,15 @@ dr_status delta_rule_chunk_fwd(const void *q, const void *k, const void *v,
     }
     if (T > 0 && overlaps(so, sst)) return DR_ERR_INVALID_ARG;
 
-    return hip_status(dr::launch_chunk_fwd(q, k, v, beta, S0, o, S_T, B, T, H, (int)Dk,
-                                           (int)Dv, (int)chunk, dtype == DR_BF16,
+    return hip_status(dr::launch_chunk_fwd(q, k, v, beta, gated ? g : nullptr, S0, o, S_T, B, T,
+                                           H, (int)Dk, (int)Dv, (int)chunk, dtype == DR_BF16,
                                            static_cast<hipStream_t>(stream)));
 }
 
-dr_status delta_rule_recurrent_step(const void *q, const void *k,
-                                    const void *v, const void *beta, float *S,
-                                    void *o, int64_t B, int64_t H, int64_t Dk,
-                                    int64_t Dv, dr_dtype dtype, void *stream) {
+// Shared validation and dispatch of the decode step; g (fp32 [B,H]) as above.
+dr_status recurrent_step(const void *q, const void *k, const void *v, const void *beta,
+                         const float *g, bool gated, float *S, void *o, int64_t B, int64_t H,
+                         int64_t Dk, int64_t Dv, dr_dtype dtype, void *stream) {
     if (dtype != DR_F32 && dtype != DR_BF16) return DR_ERR_INVALID_ARG;
     if (B < 0 || H < 0 || Dk < 0 || Dv < 0) return DR_ERR_INVALID_ARG;
     if (!supported_dim(Dk) || !supported_dim(Dv)) return DR_ERR_UNSUPPORTED;
@@ -113,20 +112,57 @@ dr_status delta_rule_recurrent_step(const void *q, const void *k,
     if (bh < 0 || ns < 0 || mul_checked({bh, Dv}) > INT32_MAX) return DR_ERR_UNSUPPORTED;
 
     if (!q || !k || !v || !beta || !S || !o) return DR_ERR_INVALID_ARG;
+    if (gated && !g) return DR_ERR_INVALID_ARG;
     // q, k and S are read in 16-byte vectors; v, beta and o element-wise
     if (!aligned16(q) || !aligned16(k) || !aligned16(S)) return DR_ERR_INVALID_ARG;
     if (!aligned_to(v, esz) || !aligned_to(beta, esz) || !aligned_to(o, esz))
         return DR_ERR_INVALID_ARG;
+    if (g && !aligned_to(g, 4)) return DR_ERR_INVALID_ARG;
     const Span so{o, bh * Dv * esz}, ss{S, ns * 4};
     const Span in[] = {{q, bh * Dk * esz}, {k, bh * Dk * esz}, {v, bh * Dv * esz},
-                       {beta, bh * esz}};
+                       {beta, bh * esz}, {gated ? g : nullptr, bh * 4}};
     if (overlaps(so, ss)) return DR_ERR_INVALID_ARG;
     for (const Span &s : in)
         if (overlaps(so, s) || overlaps(ss, s)) return DR_ERR_INVALID_ARG;
 
-    return hip_status(dr::launch_recurrent_step(q, k, v, beta, S, o, bh, (int)Dk, (int)Dv,
-                                                dtype == DR_BF16,
+    return hip_status(dr::launch_recurrent_step(q, k, v, beta, gated ? g : nullptr, S, o, bh,
+                                                (int)Dk, (int)Dv, dtype == DR_BF16,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+dr_status delta_rule_chunk_fwd(const void *q, const void *k, const void *v,
+                               const void *beta, const float *S0, void *o,
+                               float *S_T, int64_t B, int64_t T, int64_t H,
+                               int64_t Dk, int64_t Dv, int64_t chunk,
+                               dr_dtype dtype, void *stream) {
+    return chunk_fwd(q, k, v, beta, nullptr, false, S0, o, S_T, B, T, H, Dk, Dv, chunk, dtype,
+                     stream);
+}
+
+dr_status delta_rule_recurrent_step(const void *q, const void *k,
+                                    const void *v, const void *beta, float *S,
+                                    void *o, int64_t B, int64_t H, int64_t Dk,
+                                    int64_t Dv, dr_dtype dtype, void *stream) {
+    return recurrent_step(q, k, v, beta, nullptr, false, S, o, B, H, Dk, Dv, dtype, stream);
+}
+
+dr_status gated_delta_rule_chunk_fwd(const void *q, const void *k, const void *v,
+                                     const void *beta, const float *g, const float *S0,
+                                     void *o, float *S_T, int64_t B, int64_t T, int64_t H,
+                                     int64_t Dk, int64_t Dv, int64_t chunk, dr_dtype dtype,
+                                     void *stream) {
+    return chunk_fwd(q, k, v, beta, g, true, S0, o, S_T, B, T, H, Dk, Dv, chunk, dtype, stream);
+}
+
+dr_status gated_delta_rule_recurrent_step(const void *q, const void *k, const void *v,
+                                          const void *beta, const float *g, float *S, void *o,
+                                          int64_t B, int64_t H, int64_t Dk, int64_t Dv,
+                                          dr_dtype dtype, void *stream) {
+    return recurrent_step(q, k, v, beta, g, true, S, o, B, H, Dk, Dv, dtype, stream);
 }
 
 const char *delta_rule_status_string(dr_status status) {
@@ -141,6 +177,6 @@ const char *delta_rule_status_string(dr_status status) {
 
 int delta_rule_last_hip_error(void) { return g_last_hip_error; }
 
-int delta_rule_version(void) { return 100; }
+int delta_rule_version(void) { return 200; }
 
 }  // extern "C"

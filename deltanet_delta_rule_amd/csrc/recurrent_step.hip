@@ -42,11 +42,13 @@ __device__ __forceinline__ float row_sum(float x) {
     return x;
 }
 
-template <typename DT, int DK, int PASSES>
+// GATED: the whole row first decays by alpha = exp(g) of its (b, h), then the
+// token is predicted from the decayed row (forget before predict).
+template <typename DT, int DK, int PASSES, bool GATED>
 __global__ __launch_bounds__(256) void recurrent_step_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
-    const DT *__restrict__ beta, float *__restrict__ S, DT *__restrict__ o,
-    int Dv, int wg_per_head) {
+    const DT *__restrict__ beta, const float *__restrict__ g, float *__restrict__ S,
+    DT *__restrict__ o, int Dv, int wg_per_head) {
     constexpr int LPR = DK / 8;        // lanes per state row
     constexpr int RPP = 256 / LPR;     // rows per pass
     const int64_t head = blockIdx.x / wg_per_head;  // flattened b*H + h
@@ -58,6 +60,7 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
     load8(k + head * DK + 8 * sub, kf);
     load8(q + head * DK + 8 * sub, qf);
     const float b = to_f32(beta[head]);
+    const float a = GATED ? __expf(g[head]) : 1.f;
 
     float s[PASSES][8];
     float vr[PASSES];
@@ -67,6 +70,10 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
         row[p] = (part * PASSES + p) * RPP + rloc;
         if (row[p] < Dv) {
             load8(S + (head * Dv + row[p]) * DK + 8 * sub, s[p]);
+            if (GATED) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) s[p][i] *= a;
+            }
             vr[p] = to_f32(v[head * Dv + row[p]]);
         } else {
 #pragma unroll
@@ -99,29 +106,38 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
 
 template <typename DT, int DK>
 hipError_t launch_step(const void *q, const void *k, const void *v, const void *beta,
-                       float *S, void *o, int64_t BH, int Dv, hipStream_t stream) {
+                       const float *g, float *S, void *o, int64_t BH, int Dv,
+                       hipStream_t stream) {
     constexpr int LPR = DK / 8;
     constexpr int RPP = 256 / LPR;
     constexpr int PASSES = 2;
     const int rows_per_wg = RPP * PASSES;
     const int wg_per_head = (Dv + rows_per_wg - 1) / rows_per_wg;
     const int64_t grid = BH * wg_per_head;
-    hipLaunchKernelGGL((recurrent_step_kernel<DT, DK, PASSES>), dim3((unsigned)grid),
-                       dim3(256), 0, stream, static_cast<const DT *>(q),
-                       static_cast<const DT *>(k), static_cast<const DT *>(v),
-                       static_cast<const DT *>(beta), S, static_cast<DT *>(o), Dv,
-                       wg_per_head);
+    if (g)
+        hipLaunchKernelGGL((recurrent_step_kernel<DT, DK, PASSES, true>), dim3((unsigned)grid),
+                           dim3(256), 0, stream, static_cast<const DT *>(q),
+                           static_cast<const DT *>(k), static_cast<const DT *>(v),
+                           static_cast<const DT *>(beta), g, S, static_cast<DT *>(o), Dv,
+                           wg_per_head);
+    else
+        hipLaunchKernelGGL((recurrent_step_kernel<DT, DK, PASSES, false>), dim3((unsigned)grid),
+                           dim3(256), 0, stream, static_cast<const DT *>(q),
+                           static_cast<const DT *>(k), static_cast<const DT *>(v),
+                           static_cast<const DT *>(beta), g, S, static_cast<DT *>(o), Dv,
+                           wg_per_head);
     return hipGetLastError();
 }
 
 template <typename DT>
 hipError_t dispatch_dk(const void *q, const void *k, const void *v, const void *beta,
-                       float *S, void *o, int64_t BH, int Dk, int Dv, hipStream_t stream) {
+                       const float *g, float *S, void *o, int64_t BH, int Dk, int Dv,
+                       hipStream_t stream) {
     switch (Dk) {
-    case 16: return launch_step<DT, 16>(q, k, v, beta, S, o, BH, Dv, stream);
-    case 32: return launch_step<DT, 32>(q, k, v, beta, S, o, BH, Dv, stream);
-    case 64: return launch_step<DT, 64>(q, k, v, beta, S, o, BH, Dv, stream);
-    case 128: return launch_step<DT, 128>(q, k, v, beta, S, o, BH, Dv, stream);
+    case 16: return launch_step<DT, 16>(q, k, v, beta, g, S, o, BH, Dv, stream);
+    case 32: return launch_step<DT, 32>(q, k, v, beta, g, S, o, BH, Dv, stream);
+    case 64: return launch_step<DT, 64>(q, k, v, beta, g, S, o, BH, Dv, stream);
+    case 128: return launch_step<DT, 128>(q, k, v, beta, g, S, o, BH, Dv, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -129,10 +145,10 @@ hipError_t dispatch_dk(const void *q, const void *k, const void *v, const void *
 }  // namespace
 
 hipError_t launch_recurrent_step(const void *q, const void *k, const void *v,
-                                 const void *beta, float *S, void *o, int64_t BH,
-                                 int Dk, int Dv, bool bf16, hipStream_t stream) {
-    if (bf16) return dispatch_dk<__bf16>(q, k, v, beta, S, o, BH, Dk, Dv, stream);
-    return dispatch_dk<float>(q, k, v, beta, S, o, BH, Dk, Dv, stream);
+                                 const void *beta, const float *g, float *S, void *o,
+                                 int64_t BH, int Dk, int Dv, bool bf16, hipStream_t stream) {
+    if (bf16) return dispatch_dk<__bf16>(q, k, v, beta, g, S, o, BH, Dk, Dv, stream);
+    return dispatch_dk<float>(q, k, v, beta, g, S, o, BH, Dk, Dv, stream);
 }
 
 }  // namespace dr

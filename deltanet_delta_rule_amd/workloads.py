@@ -16,8 +16,14 @@ oracle can be fed from it.  Every tensor is drawn in fp32 on the CPU from a
   scalar per (token, head) (fla ``fla/layers/delta_net.py``: ``b_proj`` then
   ``sigmoid``, times 2 when ``allow_neg_eigval``);
 * S0: zero, or 0.02 * N(0,1) in fp32 where the workload carries a state in;
+* gated workloads (gate_amax > 0) then draw, per head, A ~ U(0, gate_amax)
+  and, per (token, head), a ~ N(0,1), and set the log forget gate
+  g = -A softplus(a + 1) (the gated layer of the houmin.site page,
+  "infra/delta-net", section "Gated DeltaNet": alpha = exp(-exp(A_log)
+  softplus(W_alpha x + dt_bias)) with A = exp(A_log) drawn from U(0,16) and
+  dt_bias = 1; a stands in for W_alpha x);
 * q, k, v, beta are then rounded once to the workload dtype (round to nearest
-  even); S0 stays fp32.
+  even); S0 and g stay fp32.
 
 Named workloads (sizes are the whole job on one GPU):
 
@@ -26,6 +32,8 @@ Named workloads (sizes are the whole job on one GPU):
 ``layer_1p3b``    B8 H16 T2048 d128, chunk 64, bf16 (hidden 2048, 16 heads)
 ``long_prefill``  B1 H16 T32768 d128, chunk 64, bf16, S0 != 0, beta in (0,2)
 ``decode``        B128 H16 d128, 256 single-token steps, bf16, S0 != 0
+``gated_layer_1p3b``  the layer_1p3b shape with the gated rule (A up to 16)
+``gated_decode``  the decode workload with the gated rule
 """
 from __future__ import annotations
 
@@ -51,6 +59,7 @@ class Workload:
     s0_std: float
     seed: int
     decode: bool = False
+    gate_amax: float = 0.0  # > 0: gated rule, per-head A ~ U(0, gate_amax)
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -76,6 +85,14 @@ WORKLOADS = {
     "decode": Workload("decode", B=128, H=16, T=256, Dk=128, Dv=128, chunk=1,
                        dtype="bf16", feature="l2", beta_scale=1.0,
                        s0_std=0.02, seed=BASE_SEED + 4, decode=True),
+    "gated_layer_1p3b": Workload("gated_layer_1p3b", B=8, H=16, T=2048, Dk=128,
+                                 Dv=128, chunk=64, dtype="bf16", feature="l2",
+                                 beta_scale=1.0, s0_std=0.0,
+                                 seed=BASE_SEED + 5, gate_amax=16.0),
+    "gated_decode": Workload("gated_decode", B=128, H=16, T=256, Dk=128,
+                             Dv=128, chunk=1, dtype="bf16", feature="l2",
+                             beta_scale=1.0, s0_std=0.02, seed=BASE_SEED + 6,
+                             decode=True, gate_amax=16.0),
 }
 
 
@@ -91,7 +108,8 @@ def generate(w: Workload) -> dict:
     """Draw one workload.  Returns CPU tensors:
 
     chunk workloads: q, k [B,T,H,Dk]; v [B,T,H,Dv]; beta [B,T,H] in the
-    workload dtype; S0 [B,H,Dv,Dk] fp32 or None.
+    workload dtype; S0 [B,H,Dv,Dk] fp32 or None; g [B,T,H] fp32 (gated
+    workloads) or None.
     decode workloads: the same with the leading two axes read as
     [steps, B] (q, k [steps,B,H,Dk] ...), i.e. step-major.
     """
@@ -107,6 +125,11 @@ def generate(w: Workload) -> dict:
                                     dtype=torch.float32)
     else:
         S0 = None
+    gl = None
+    if w.gate_amax > 0:
+        A = w.gate_amax * torch.rand(w.H, generator=g, dtype=torch.float32)
+        a = torch.randn(*lead, w.H, generator=g, dtype=torch.float32)
+        gl = (-A * torch.nn.functional.softplus(a + 1.0)).contiguous()
     q = _features(q_raw, w.feature)
     k = _features(k_raw, w.feature)
     beta = w.beta_scale * torch.sigmoid(beta_raw)
@@ -117,6 +140,7 @@ def generate(w: Workload) -> dict:
         "v": v.to(dt).contiguous(),
         "beta": beta.to(dt).contiguous(),
         "S0": S0,
+        "g": gl,
     }
     return out
 

@@ -130,6 +130,50 @@ dr_status delta_rule_recurrent_step(const void *q, const void *k,
                                     void *o, int64_t B, int64_t H, int64_t Dk,
                                     int64_t Dv, dr_dtype dtype, void *stream);
 
+/*
+ * gated_delta_rule_chunk_fwd -- the gated rule (scalar forget gate), chunked.
+ *
+ * Each token first multiplies the whole state by alpha_t = exp(g_t), then
+ * predicts from the decayed state, corrects and writes:
+ *
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = S_t q_t
+ *
+ * (houmin.site "infra/delta-net", section "Gated DeltaNet"; hada.io digest,
+ * section "Gated DeltaNet : oublier d'abord l'etat entier", which fixes the
+ * order forget, predict, correct, write).  Evaluated chunkwise with the decay
+ * carried as in-chunk prefix sums of g (hada.io digest, sections "Chunkwise
+ * KDA" with a scalar decay and "Pipeline Triton Chunkwise").
+ *
+ *   g       [B,T,H] fp32, the natural log of the forget gate, required when
+ *           T > 0 (4-byte aligned; must not overlap any output).  Values are
+ *           expected to be <= 0 (alpha in (0,1]); g = 0 everywhere gives
+ *           delta_rule_chunk_fwd's result up to rounding.  Within a chunk the
+ *           kernel forms exp of differences of prefix sums, so positive g
+ *           large enough to overflow fp32 over one chunk is not supported.
+ *   Every other argument, size, layout and error behaves as in
+ *   delta_rule_chunk_fwd.
+ */
+dr_status gated_delta_rule_chunk_fwd(const void *q, const void *k, const void *v,
+                                     const void *beta, const float *g, const float *S0,
+                                     void *o, float *S_T, int64_t B, int64_t T, int64_t H,
+                                     int64_t Dk, int64_t Dv, int64_t chunk, dr_dtype dtype,
+                                     void *stream);
+
+/*
+ * gated_delta_rule_recurrent_step -- one decode token of the gated rule per
+ * sequence, state in place: S <- exp(g) S, then the delta-rule write and
+ * o = S_new q as in delta_rule_recurrent_step.
+ *
+ *   g       [B,H] fp32, log forget gate of this token (required, 4-byte
+ *           aligned, not overlapping S or o).
+ *   Every other argument behaves as in delta_rule_recurrent_step.
+ */
+dr_status gated_delta_rule_recurrent_step(const void *q, const void *k, const void *v,
+                                          const void *beta, const float *g, float *S, void *o,
+                                          int64_t B, int64_t H, int64_t Dk, int64_t Dv,
+                                          dr_dtype dtype, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *delta_rule_status_string(dr_status status);
 
@@ -137,7 +181,8 @@ const char *delta_rule_status_string(dr_status status);
  * (0 if none). */
 int delta_rule_last_hip_error(void);
 
-/* Library version as major*10000 + minor*100 + patch. */
+/* Library version as major*10000 + minor*100 + patch (2.0.0: the gated
+ * entry points). */
 int delta_rule_version(void);
 
 #ifdef __cplusplus

@@ -9,7 +9,7 @@ import os
 import numpy as np
 import torch
 
-from oracle import delta_rule_ref
+from oracle import delta_rule_ref, gated_delta_rule_ref
 
 # fp32 inputs: 1e-4; bf16 inputs: 2e-2 (fp32 state), both relative to max|ref|.
 TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
@@ -40,19 +40,31 @@ def to_np(t):
 
 
 def oracle_heads(x, heads):
-    """Oracle on a subset of (b, h) pairs of a chunk workload's inputs.
+    """Oracle on a subset of (b, h) pairs of a chunk workload's inputs (the
+    gated oracle when the inputs carry log gates g).
 
     Returns (o [T, n, Dv], S_T [n, Dv, Dk]) for the n pairs in `heads`, by
     stacking the selected heads into one batch row (heads are independent).
     """
     sel = lambda t: np.stack([to_np(t[b, :, h]) for b, h in heads], axis=1)[None]
     q, k, v = sel(x["q"]), sel(x["k"]), sel(x["v"])
-    beta = np.stack([to_np(x["beta"][b, :, h]) for b, h in heads], axis=1)[None]
+    beta = sel(x["beta"])
     S0 = None
     if x["S0"] is not None:
         S0 = np.stack([x["S0"][b, h].double().numpy() for b, h in heads])[None]
-    o, st = delta_rule_ref(q, k, v, beta, S0, nthreads=threads())
+    if x.get("g") is not None:
+        o, st = gated_delta_rule_ref(q, k, v, beta, sel(x["g"]), S0, nthreads=threads())
+    else:
+        o, st = delta_rule_ref(q, k, v, beta, S0, nthreads=threads())
     return o[0], st[0]
+
+
+def oracle_all(x):
+    """Oracle on every head of a chunk workload's inputs (gated when g is set)."""
+    if x.get("g") is not None:
+        return gated_delta_rule_ref(x["q"], x["k"], x["v"], x["beta"], x["g"], x["S0"],
+                                    nthreads=threads())
+    return delta_rule_ref(x["q"], x["k"], x["v"], x["beta"], x["S0"], nthreads=threads())
 
 
 def gather_heads(o_gpu, st_gpu, heads):

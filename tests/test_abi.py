@@ -40,7 +40,7 @@ def _declared_functions():
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         for m in re.finditer(r"\b([A-Za-z_]\w*)\s*\(", text):
             name = m.group(1)
-            if name.startswith("delta_rule_"):
+            if name.startswith(("delta_rule_", "gated_delta_rule_")):
                 names.add(name)
     return sorted(names)
 
@@ -49,6 +49,8 @@ def test_header_declares_entry_points():
     names = _declared_functions()
     assert "delta_rule_chunk_fwd" in names
     assert "delta_rule_recurrent_step" in names
+    assert "gated_delta_rule_chunk_fwd" in names
+    assert "gated_delta_rule_recurrent_step" in names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -139,3 +141,60 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(dr, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         dr.load_library()
+
+
+# ------------------------------------------------------------- gated rule
+GP = ctypes.c_void_p(0x100000 * 7)   # the log gates, apart from every other buffer
+
+
+def _gchunk(lib, g=GP, q=P[0], k=P[1], v=P[2], beta=P[3], S0=None, o=P[4], S_T=P[5],
+            B=2, T=64, H=2, Dk=64, Dv=64, chunk=64, dtype=dr.DR_BF16):
+    return lib.gated_delta_rule_chunk_fwd(q, k, v, beta, g, S0, o, S_T, B, T, H, Dk, Dv,
+                                          chunk, dtype, None)
+
+
+def _gstep(lib, g=GP, q=P[0], k=P[1], v=P[2], beta=P[3], S=P[4], o=P[5], B=2, H=2,
+           Dk=64, Dv=64, dtype=dr.DR_BF16):
+    return lib.gated_delta_rule_recurrent_step(q, k, v, beta, g, S, o, B, H, Dk, Dv,
+                                               dtype, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(g=None),                    # the gate is required when T > 0
+    dict(g=ODD),                     # not 4-byte aligned
+    dict(g=P[4]),                    # gates overlap the output
+    dict(S_T=GP),                    # final state overlaps the gates
+    dict(B=-1), dict(q=None), dict(o=P[0]),
+])
+def test_gated_chunk_rejects_invalid(lib, kw):
+    assert _gchunk(lib, **kw) == dr.DR_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(Dk=48), dict(chunk=128), dict(Dv=8)])
+def test_gated_chunk_rejects_unsupported(lib, kw):
+    assert _gchunk(lib, **kw) == dr.DR_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [
+    dict(g=None), dict(g=ODD),
+    dict(g=P[4]),                    # gates overlap the state
+    dict(o=GP),                      # output overlaps the gates
+    dict(S=None), dict(q=MISALIGNED),
+])
+def test_gated_step_rejects_invalid(lib, kw):
+    assert _gstep(lib, **kw) == dr.DR_ERR_INVALID_ARG
+
+
+def test_gated_empty_batch_is_a_no_op(lib):
+    assert _gchunk(lib, B=0) == dr.DR_OK
+    assert _gstep(lib, H=0) == dr.DR_OK
+
+
+def test_gated_binding_checks_the_gate():
+    import torch
+    x = torch.zeros(1, 4, 1, 16)
+    with pytest.raises(ValueError):
+        dr.gated_delta_rule_chunk_fwd(x, x, x, x[..., 0], x[..., 0])
+    with pytest.raises(ValueError):
+        dr.gated_delta_rule_recurrent_step(x[:, 0], x[:, 0], x[:, 0], x[:, 0, :, 0],
+                                           x[:, 0, :, 0], torch.zeros(1, 1, 16, 16))
