@@ -15,6 +15,10 @@ and the gated rule (g = log of the per-token, per-head forget gate, fp32):
 
     o, S_T = gated_delta_rule_chunk_fwd(q, k, v, beta, g, S0=None, chunk=64)
     o      = gated_delta_rule_recurrent_step(q, k, v, beta, g, S)
+
+Both chunked calls also take ``scale=`` (output scale) and ``cu_seqlens=``
+(packed variable-length sequences in one batch row), which route them to
+``delta_rule_chunk_fwd_ex``.
 """
 from __future__ import annotations
 
@@ -41,6 +45,13 @@ DR_F32, DR_BF16 = 0, 1
 _lib = None
 
 
+class dr_chunk_opts(ctypes.Structure):
+    """``dr_chunk_opts`` of include/deltarule.h."""
+    _fields_ = [("g", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
+                ("num_seqs", ctypes.c_int64), ("scale", ctypes.c_float),
+                ("flags", ctypes.c_uint32)]
+
+
 class DeltaRuleError(RuntimeError):
     """A HIP runtime failure reported by libdeltarule."""
 
@@ -62,6 +73,10 @@ def load_library():
     lib.delta_rule_recurrent_step.restype = i32
     lib.delta_rule_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp,
                                               i64, i64, i64, i64, i32, vp]
+    lib.delta_rule_chunk_fwd_ex.restype = i32
+    lib.delta_rule_chunk_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp,
+                                            i64, i64, i64, i64, i64, i64,
+                                            ctypes.POINTER(dr_chunk_opts), i32, vp]
     lib.gated_delta_rule_chunk_fwd.restype = i32
     lib.gated_delta_rule_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                                                i64, i64, i64, i64, i64, i64, i32, vp]
@@ -132,7 +147,8 @@ def _need(t, name, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _chunk_call(entry, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, stream):
+def _chunk_call(gated, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, stream,
+                scale=None, cu_seqlens=None):
     torch = _torch()
     dev = q.device
     if dev.type != "cuda":
@@ -145,50 +161,74 @@ def _chunk_call(entry, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, 
     _need(k, "k", (B, T, H, Dk), dt, dev)
     _need(v, "v", (B, T, H, Dv), dt, dev)
     _need(beta, "beta", (B, T, H), dt, dev)
-    if g is not None:
+    if gated:
         _need(g, "g", (B, T, H), torch.float32, dev)
+    nseq = B
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError("packed sequences (cu_seqlens) need a batch of 1")
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+            raise ValueError("cu_seqlens must be a 1-D tensor of num_seqs + 1 offsets")
+        if cu_seqlens.dtype != torch.int32:
+            cu_seqlens = cu_seqlens.to(torch.int32)
+        nseq = cu_seqlens.numel() - 1
+        _need(cu_seqlens, "cu_seqlens", (nseq + 1,), torch.int32, dev)
     if S0 is not None:
-        _need(S0, "S0", (B, H, Dv, Dk), torch.float32, dev)
+        _need(S0, "S0", (nseq, H, Dv, Dk), torch.float32, dev)
     if o is None:
         o = torch.empty((B, T, H, Dv), dtype=dt, device=dev)
     else:
         _need(o, "o", (B, T, H, Dv), dt, dev)
     if output_final_state:
         if S_T is None:
-            S_T = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+            S_T = torch.empty((nseq, H, Dv, Dk), dtype=torch.float32, device=dev)
         else:
-            _need(S_T, "S_T", (B, H, Dv, Dk), torch.float32, dev)
+            _need(S_T, "S_T", (nseq, H, Dv, Dk), torch.float32, dev)
     else:
         S_T = None
-    ptrs = [_ptr(q), _ptr(k), _ptr(v), _ptr(beta)]
-    if entry == "gated_delta_rule_chunk_fwd":
-        ptrs.append(_ptr(g))
-    st = getattr(load_library(), entry)(
-        *ptrs, _ptr(S0), _ptr(o), _ptr(S_T),
-        B, T, H, Dk, Dv, int(chunk), _dtype_code(q), _stream(dev, stream))
+    lib = load_library()
+    common = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta))
+    tail = (B, T, H, Dk, Dv, int(chunk))
+    if scale is None and cu_seqlens is None:
+        if gated:
+            st = lib.gated_delta_rule_chunk_fwd(*common, _ptr(g), _ptr(S0), _ptr(o), _ptr(S_T),
+                                                *tail, _dtype_code(q), _stream(dev, stream))
+        else:
+            st = lib.delta_rule_chunk_fwd(*common, _ptr(S0), _ptr(o), _ptr(S_T), *tail,
+                                          _dtype_code(q), _stream(dev, stream))
+    else:
+        opts = dr_chunk_opts(g=g.data_ptr() if gated else None,
+                             cu_seqlens=None if cu_seqlens is None else cu_seqlens.data_ptr(),
+                             num_seqs=nseq if cu_seqlens is not None else 0,
+                             scale=1.0 if scale is None else float(scale), flags=0)
+        st = lib.delta_rule_chunk_fwd_ex(*common, _ptr(S0), _ptr(o), _ptr(S_T), *tail,
+                                         ctypes.byref(opts), _dtype_code(q),
+                                         _stream(dev, stream))
     _check(st)
     return o, S_T
 
 
 def delta_rule_chunk_fwd(q, k, v, beta, S0=None, *, chunk: int = 64,
                          output_final_state: bool = True, o=None, S_T=None,
-                         stream=None):
+                         scale=None, cu_seqlens=None, stream=None):
     """Chunkwise forward.  q, k ``[B,T,H,Dk]``; v ``[B,T,H,Dv]``; beta
     ``[B,T,H]`` (float32 or bfloat16, all the same dtype, on one GPU);
     S0 ``[B,H,Dv,Dk]`` float32 or None.  Returns ``(o, S_T)``; S_T is None
     when ``output_final_state`` is False.  ``o`` / ``S_T`` may be passed in
-    (S_T may be S0 itself to carry the state in place)."""
-    return _chunk_call("delta_rule_chunk_fwd", q, k, v, beta, None, S0, chunk,
-                       output_final_state, o, S_T, stream)
+    (S_T may be S0 itself to carry the state in place).  ``scale`` multiplies
+    the outputs; ``cu_seqlens`` (int32 ``[N+1]`` on the GPU, B = 1) packs N
+    sequences, whose states S0 / S_T are then ``[N,H,Dv,Dk]``."""
+    return _chunk_call(False, q, k, v, beta, None, S0, chunk, output_final_state, o, S_T,
+                       stream, scale, cu_seqlens)
 
 
 def gated_delta_rule_chunk_fwd(q, k, v, beta, g, S0=None, *, chunk: int = 64,
                                output_final_state: bool = True, o=None, S_T=None,
-                               stream=None):
+                               scale=None, cu_seqlens=None, stream=None):
     """Chunkwise forward of the gated rule: as ``delta_rule_chunk_fwd`` plus
     g ``[B,T,H]`` float32, the log of each token's forget gate (<= 0)."""
-    return _chunk_call("gated_delta_rule_chunk_fwd", q, k, v, beta, g, S0, chunk,
-                       output_final_state, o, S_T, stream)
+    return _chunk_call(True, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, stream,
+                       scale, cu_seqlens)
 
 
 def _step_call(entry, q, k, v, beta, g, S, o, stream):

@@ -47,24 +47,30 @@ dr_status hip_status(hipError_t e) {
     return DR_ERR_HIP;
 }
 
-// Shared validation and dispatch of the chunked forward; g (log forget gate,
-// fp32 [B,T,H]) is nullptr for the plain rule and required for the gated one.
+// Shared validation and dispatch of the chunked forward.  g (log forget
+// gate, fp32 [B,T,H]) is nullptr for the plain rule and required for the
+// gated one when T > 0; cu (int32 [nseq+1], nullable) packs nseq sequences
+// into the single batch row; scale multiplies the outputs.
 dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *beta,
                     const float *g, bool gated, const float *S0, void *o, float *S_T,
                     int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t chunk,
-                    dr_dtype dtype, void *stream) {
+                    const int32_t *cu, int64_t nseq, float scale, dr_dtype dtype,
+                    void *stream) {
     if (dtype != DR_F32 && dtype != DR_BF16) return DR_ERR_INVALID_ARG;
     if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0 || chunk < 0) return DR_ERR_INVALID_ARG;
+    if (cu && (B != 1 || nseq < 0 || !aligned_to(cu, 4))) return DR_ERR_INVALID_ARG;
+    if (!(scale == scale) || scale - scale != 0.f) return DR_ERR_INVALID_ARG;  // NaN or inf
     if (!supported_dim(Dk) || !supported_dim(Dv) || !supported_chunk(chunk))
         return DR_ERR_UNSUPPORTED;
-    if (B == 0 || H == 0) return DR_OK;  // empty batch: nothing to do
+    const int64_t ns_count = cu ? nseq : B;  // sequences (states)
+    if (ns_count == 0 || H == 0) return DR_OK;  // nothing to do
 
     const int64_t esz = dtype == DR_BF16 ? 2 : 4;
     const int64_t nqk = mul_checked({B, T, H, Dk}), nv = mul_checked({B, T, H, Dv});
-    const int64_t nb = mul_checked({B, T, H}), ns = mul_checked({B, H, Dv, Dk});
+    const int64_t nb = mul_checked({B, T, H}), ns = mul_checked({ns_count, H, Dv, Dk});
     if (nqk < 0 || nv < 0 || nb < 0 || ns < 0) return DR_ERR_UNSUPPORTED;
-    // grid = B*H*(Dv/16) at most; sequence length and heads index in 32 bits
-    if (T > INT32_MAX || H > INT32_MAX || mul_checked({B, H, Dv / 16}) > INT32_MAX)
+    // grid = sequences*H*(Dv/16) at most; sequence length and heads index in 32 bits
+    if (T > INT32_MAX || H > INT32_MAX || mul_checked({ns_count, H, Dv / 16}) > INT32_MAX)
         return DR_ERR_UNSUPPORTED;
     // one chunk of one head (chunk tokens x H rows) is addressed with 32-bit
     // byte offsets
@@ -82,8 +88,10 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
         if (p && !aligned_to(p, esz)) return DR_ERR_INVALID_ARG;
     if (g && !aligned_to(g, 4)) return DR_ERR_INVALID_ARG;
 
-    const Span in[] = {{q, nqk * esz}, {k, nqk * esz}, {v, nv * esz}, {beta, nb * esz},
-                       {S0, ns * 4}, {gated ? g : nullptr, nb * 4}};
+    const Span in[] = {{q, nqk * esz},        {k, nqk * esz},
+                       {v, nv * esz},         {beta, nb * esz},
+                       {S0, ns * 4},          {gated ? g : nullptr, nb * 4},
+                       {cu, (nseq + 1) * 4}};
     const Span so{o, nv * esz}, sst{S_T, ns * 4};
     for (const Span &s : in) {
         if (T > 0 && overlaps(so, s)) return DR_ERR_INVALID_ARG;
@@ -92,9 +100,11 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
     }
     if (T > 0 && overlaps(so, sst)) return DR_ERR_INVALID_ARG;
 
-    return hip_status(dr::launch_chunk_fwd(q, k, v, beta, gated ? g : nullptr, S0, o, S_T, B, T,
-                                           H, (int)Dk, (int)Dv, (int)chunk, dtype == DR_BF16,
-                                           static_cast<hipStream_t>(stream)));
+    dr::ChunkFwdArgs a{q,  k,        v,        beta, gated ? g : nullptr,
+                       S0, o,        S_T,      cu,   ns_count,
+                       T,  H,        (int)Dk,  (int)Dv, (int)chunk,
+                       scale};
+    return hip_status(dr::launch_chunk_fwd(a, dtype == DR_BF16, static_cast<hipStream_t>(stream)));
 }
 
 // Shared validation and dispatch of the decode step; g (fp32 [B,H]) as above.
@@ -139,8 +149,21 @@ dr_status delta_rule_chunk_fwd(const void *q, const void *k, const void *v,
                                float *S_T, int64_t B, int64_t T, int64_t H,
                                int64_t Dk, int64_t Dv, int64_t chunk,
                                dr_dtype dtype, void *stream) {
-    return chunk_fwd(q, k, v, beta, nullptr, false, S0, o, S_T, B, T, H, Dk, Dv, chunk, dtype,
-                     stream);
+    return chunk_fwd(q, k, v, beta, nullptr, false, S0, o, S_T, B, T, H, Dk, Dv, chunk, nullptr,
+                     0, 1.f, dtype, stream);
+}
+
+dr_status delta_rule_chunk_fwd_ex(const void *q, const void *k, const void *v,
+                                  const void *beta, const float *S0, void *o, float *S_T,
+                                  int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                  int64_t chunk, const dr_chunk_opts *opts, dr_dtype dtype,
+                                  void *stream) {
+    dr_chunk_opts d{};
+    d.scale = 1.f;
+    const dr_chunk_opts &x = opts ? *opts : d;
+    if (x.flags != 0) return DR_ERR_INVALID_ARG;  // no flags are defined
+    return chunk_fwd(q, k, v, beta, x.g, x.g != nullptr, S0, o, S_T, B, T, H, Dk, Dv, chunk,
+                     x.cu_seqlens, x.num_seqs, x.scale, dtype, stream);
 }
 
 dr_status delta_rule_recurrent_step(const void *q, const void *k,
@@ -155,7 +178,8 @@ dr_status gated_delta_rule_chunk_fwd(const void *q, const void *k, const void *v
                                      void *o, float *S_T, int64_t B, int64_t T, int64_t H,
                                      int64_t Dk, int64_t Dv, int64_t chunk, dr_dtype dtype,
                                      void *stream) {
-    return chunk_fwd(q, k, v, beta, g, true, S0, o, S_T, B, T, H, Dk, Dv, chunk, dtype, stream);
+    return chunk_fwd(q, k, v, beta, g, true, S0, o, S_T, B, T, H, Dk, Dv, chunk, nullptr, 0, 1.f,
+                     dtype, stream);
 }
 
 dr_status gated_delta_rule_recurrent_step(const void *q, const void *k, const void *v,
@@ -177,6 +201,6 @@ const char *delta_rule_status_string(dr_status status) {
 
 int delta_rule_last_hip_error(void) { return g_last_hip_error; }
 
-int delta_rule_version(void) { return 200; }
+int delta_rule_version(void) { return 20100; }
 
 }  // extern "C"

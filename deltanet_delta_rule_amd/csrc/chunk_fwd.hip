@@ -5,15 +5,8 @@
 
 namespace dr {
 
-hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v,
-                            const void *beta, const float *g, const float *S0, void *o,
-                            float *S_T, int64_t B, int64_t T, int64_t H, int Dk, int Dv,
-                            int chunk, bool bf16, hipStream_t stream) {
-    if (g)
-        return launch_chunk_fwd_gated(q, k, v, beta, g, S0, o, S_T, B, T, H, Dk, Dv, chunk, bf16,
-                                      stream);
-    return launch_rule<false>(q, k, v, beta, nullptr, S0, o, S_T, B, T, H, Dk, Dv, chunk, bf16,
-                              stream);
+hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, bool bf16, hipStream_t stream) {
+    return a.g ? launch_chunk_fwd_gated(a, bf16, stream) : launch_rule<false>(a, bf16, stream);
 }
 
 }  // namespace dr

@@ -465,13 +465,15 @@ __device__ __forceinline__ void gram_tiles(const DT *Ks, const DT *Qs, const flo
 struct OutChunk {
     __amdgpu_buffer_rsrc_t rsrc;
     int voff, row_bytes;
+    float scale;  // output scale (1: none)
 };
 
 // Four consecutive output elements of one token row (8 bytes for bf16, 16 for
-// fp32); stores outside the resource are dropped by its range check.
+// fp32), times the output scale; stores outside the resource are dropped by
+// its range check.
 __device__ __forceinline__ void store_out4(const f32x4 &x, const OutChunk &out, int soff) {
     bf16x4 f;
-    cvt4(x, f);
+    cvt4(x * out.scale, f);
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, f),
                                           out.rsrc, out.voff, soff, 0);
 }
@@ -482,7 +484,8 @@ __device__ __forceinline__ void store_out4(const f32x4 &x, const OutChunk &out, 
 // parity grid caught an output register rewritten right after such a store.
 // The whole offset therefore goes into the per-lane offset.
 __device__ __forceinline__ void store_out4_f32(const f32x4 &x, const OutChunk &out, int soff) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, x),
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned,
+                                                              x * out.scale),
                                            out.rsrc, out.voff + soff, 0, 0);
 }
 
@@ -737,15 +740,19 @@ struct HeadPtrs {
     const float *gh;              // token 0 of the head's log forget gate (gated rule)
     DT *oh;                       // token 0, column 0 of the head's output
     int tsk, tsv, tsb;            // token strides in elements: H*d_k, H*d_v, H
+    int T;                        // tokens of this sequence
     int64_t sbase;
     int vcol;
 };
 
+// Packed variable-length input (cu != nullptr): sequence b spans tokens
+// cu[b] .. cu[b+1] of the single batch row of T tokens; the bounds are
+// clamped into [0, T] so that no access leaves the buffers whatever cu holds.
 template <typename DT, int DK, int NW>
 __device__ __forceinline__ HeadPtrs<DT> head_ptrs(const DT *q, const DT *k, const DT *v,
                                                   const DT *beta, const float *gl, DT *o,
-                                                  int T, int H, int Dv, int nvt, int wave,
-                                                  int r) {
+                                                  const int *cu, int T, int H, int Dv, int nvt,
+                                                  int wave, int r) {
     // Consecutive workgroup ids are dispatched round-robin over the 8 XCDs
     // (each with its own L2).  Remap so that the value tiles of one head,
     // which read the same K and Q, run on the same XCD.
@@ -755,16 +762,24 @@ __device__ __forceinline__ HeadPtrs<DT> head_ptrs(const DT *q, const DT *k, cons
     const int head = wg / nvt, vt = wg % nvt;
     const int b = head / H, h = head % H;
     HeadPtrs<DT> p;
+    int64_t t0 = (int64_t)b * T;  // first token of the sequence in the token axis
+    p.T = T;
+    if (cu) {
+        const int lo = min(max(cu[b], 0), T);
+        const int hi = min(max(cu[b + 1], lo), T);
+        t0 = lo;
+        p.T = hi - lo;
+    }
     p.vcol = vt * 16 * NW + wave * 16 + r;
     p.tsk = H * DK;
     p.tsv = H * Dv;
     p.tsb = H;
-    p.kh = k + ((int64_t)b * T * H + h) * DK;
-    p.qh = q + ((int64_t)b * T * H + h) * DK;
-    p.vh = v + ((int64_t)b * T * H + h) * Dv + vt * 16 * NW;
-    p.oh = o + ((int64_t)b * T * H + h) * Dv;
-    p.bh = beta + (int64_t)b * T * H + h;
-    p.gh = gl ? gl + (int64_t)b * T * H + h : nullptr;
+    p.kh = k + (t0 * H + h) * DK;
+    p.qh = q + (t0 * H + h) * DK;
+    p.vh = v + (t0 * H + h) * Dv + vt * 16 * NW;
+    p.oh = o + (t0 * H + h) * Dv;
+    p.bh = beta + t0 * H + h;
+    p.gh = gl ? gl + t0 * H + h : nullptr;
     p.sbase = ((int64_t)head * Dv + p.vcol) * DK;
     return p;
 }
@@ -947,8 +962,9 @@ struct Parity {
 // Byte offset of this lane's first output element within a chunk: token row
 // r, value columns 4g .. 4g + 3 of this wave's 16 columns.
 template <typename DT>
-__device__ __forceinline__ OutChunk out_chunk(const HeadPtrs<DT> &p, int g, int r) {
+__device__ __forceinline__ OutChunk out_chunk(const HeadPtrs<DT> &p, float scale, int g, int r) {
     OutChunk out;
+    out.scale = scale;
     out.voff = (r * p.tsv + (p.vcol - r) + 4 * g) * (int)sizeof(DT);
     out.row_bytes = p.tsv * (int)sizeof(DT);
     return out;
@@ -1065,7 +1081,8 @@ template <typename DT, int DK, int C, int NW, bool GATED>
 __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4 + 1, NW / 4 + 1))) void chunk_fwd_ws_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const float *__restrict__ gl, const float *S0,
-    DT *__restrict__ o, float *S_T, int T, int H, int Dv, int nvt) {
+    DT *__restrict__ o, float *S_T, const int *__restrict__ cu, int T, int H, int Dv, int nvt,
+    float scale) {
     typedef ChunkCfg<DT, DK, C, NW> G;
     constexpr int NT = G::NT, ND = G::ND;
     __shared__ __attribute__((aligned(16))) PipeSmem<DT, DK, C, NW, GATED> sm;
@@ -1073,11 +1090,12 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
     const int g = lane >> 4, r = lane & 15;
-    const int N = (T + C - 1) / C;
 
     if (wave < NW) {
         // ------------------------------ state waves ------------------------------
-        const HeadPtrs<DT> p = head_ptrs<DT, DK, NW>(q, k, v, beta, gl, o, T, H, Dv, nvt, wave, r);
+        const HeadPtrs<DT> p =
+            head_ptrs<DT, DK, NW>(q, k, v, beta, gl, o, cu, T, H, Dv, nvt, wave, r);
+        const int N = (p.T + C - 1) / C;
         f32x4 Sacc[ND], X[NT], Y[NT];
         ChunkOperands<DT, DK, C, NW> op;
         if (S0) {
@@ -1088,7 +1106,7 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4
 #pragma unroll
             for (int dt = 0; dt < ND; ++dt) Sacc[dt] = zero4();
         }
-        OutChunk out = out_chunk(p, g, r);
+        OutChunk out = out_chunk(p, scale, g, r);
         lds_barrier();  // chunk 0 staged
         // X, Y and the K^T operands of the chunk in set s
         auto xy = [&](int s) {
@@ -1108,7 +1126,7 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4
             constexpr int s0 = decltype(set)::value, s1 = (s0 + 1) % 3;  // sets of chunks c, c+1
             const int b = c & 1;
             const int t0 = c * C;
-            const int len = min(C, T - t0);
+            const int len = min(C, p.T - t0);
             out.rsrc = make_rsrc(p.oh + (int64_t)t0 * p.tsv, len * out.row_bytes);
             state_rest<DT, DK, C, NW, GATED>(op, sm.Ab[b], sm.Tb[b], sm.Ps[b], sm.gate.at(s0),
                                              Sacc, X, Y, out, lane);
@@ -1130,12 +1148,14 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4
     } else {
         // --------------------------- preparation waves ---------------------------
         __builtin_amdgcn_s_setprio(3);
-        const HeadPtrs<DT> p = head_ptrs<DT, DK, NW>(q, k, v, beta, gl, o, T, H, Dv, nvt, 0, r);
+        const HeadPtrs<DT> p =
+            head_ptrs<DT, DK, NW>(q, k, v, beta, gl, o, cu, T, H, Dv, nvt, 0, r);
+        const int N = (p.T + C - 1) / C;
         switch (wave - NW) {
-        case 0: prep_role<DT, DK, C, NW, 0, GATED>(sm, p, T, N, lane); break;
-        case 1: if constexpr (NW > 1) prep_role<DT, DK, C, NW, 1, GATED>(sm, p, T, N, lane); break;
-        case 2: if constexpr (NW > 2) prep_role<DT, DK, C, NW, 2, GATED>(sm, p, T, N, lane); break;
-        default: if constexpr (NW > 3) prep_role<DT, DK, C, NW, 3, GATED>(sm, p, T, N, lane); break;
+        case 0: prep_role<DT, DK, C, NW, 0, GATED>(sm, p, p.T, N, lane); break;
+        case 1: if constexpr (NW > 1) prep_role<DT, DK, C, NW, 1, GATED>(sm, p, p.T, N, lane); break;
+        case 2: if constexpr (NW > 2) prep_role<DT, DK, C, NW, 2, GATED>(sm, p, p.T, N, lane); break;
+        default: if constexpr (NW > 3) prep_role<DT, DK, C, NW, 3, GATED>(sm, p, p.T, N, lane); break;
         }
     }
 }
@@ -1161,15 +1181,16 @@ template <typename DT, int DK, int C, int NW, bool GATED>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_fwd_serial_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const float *__restrict__ gl, const float *S0,
-    DT *__restrict__ o, float *S_T, int T, int H, int Dv, int nvt) {
+    DT *__restrict__ o, float *S_T, const int *__restrict__ cu, int T, int H, int Dv, int nvt,
+    float scale) {
     typedef ChunkCfg<DT, DK, C, NW> G;
-    constexpr int NT = G::NT, ND = G::ND;
+    constexpr int ND = G::ND;
     __shared__ __attribute__((aligned(16))) SerialSmem<DT, DK, C, NW, GATED> sm;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
     const int g = lane >> 4, r = lane & 15;
-    const HeadPtrs<DT> p = head_ptrs<DT, DK, NW>(q, k, v, beta, gl, o, T, H, Dv, nvt, wave, r);
+    const HeadPtrs<DT> p = head_ptrs<DT, DK, NW>(q, k, v, beta, gl, o, cu, T, H, Dv, nvt, wave, r);
 
     f32x4 Sacc[ND];
     if (S0) {
@@ -1181,20 +1202,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
         for (int dt = 0; dt < ND; ++dt) Sacc[dt] = zero4();
     }
 
-    const int N = (T + C - 1) / C;
+    const int N = (p.T + C - 1) / C;
     if (N > 0) {
         for (int i = tid; i < C * G::LDP; i += G::NTHR) sm.Ps[i] = from_f32<DT>(0.f);
         ChunkRegs<DT, DK, C, NW, GATED> rg;
         rg.init(p, tid);
-        OutChunk out = out_chunk(p, g, r);
-        rg.load(p, T, 0);
+        OutChunk out = out_chunk(p, scale, g, r);
+        rg.load(p, p.T, 0);
         for (int c = 0; c < N; ++c) {
             const int t0 = c * C;
-            const int len = min(C, T - t0);
+            const int len = min(C, p.T - t0);
             lds_barrier();
             rg.stage(sm.Ks, sm.Qs, sm.Vs, sm.betas, sm.gate.at(0), tid);
             lds_barrier();
-            rg.load(p, T, min(c + 1, N - 1) * C);
+            rg.load(p, p.T, min(c + 1, N - 1) * C);
             const float *bc = nullptr;
             if constexpr (GATED) bc = sm.gate.at(0)->bc;
             gram_tiles<DT, DK, C, NW, GATED>(sm.Ks, sm.Qs, sm.betas, bc, sm.Ab, sm.Tb, sm.Ps, wave,
@@ -1215,24 +1236,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 // ---------------------------------------------------------------------------
 // Host dispatch
 // ---------------------------------------------------------------------------
+// B in ChunkFwdArgs counts sequences (batch rows, or packed sequences when
+// cu is set); T is the token axis of each batch row.
 template <typename DT, int DK, int C, int NW, bool GATED>
-hipError_t launch_cfg(const void *q, const void *k, const void *v, const void *beta,
-                      const float *g, const float *S0, void *o, float *S_T, int64_t B,
-                      int64_t T, int64_t H, int Dv, hipStream_t stream) {
-    const int nvt = Dv / (16 * NW);
-    const int64_t grid = B * H * nvt;
+hipError_t launch_cfg(const ChunkFwdArgs &a, hipStream_t stream) {
+    const int nvt = a.Dv / (16 * NW);
+    const int64_t grid = a.B * a.H * nvt;
+    const DT *q = static_cast<const DT *>(a.q), *k = static_cast<const DT *>(a.k);
+    const DT *v = static_cast<const DT *>(a.v), *beta = static_cast<const DT *>(a.beta);
+    DT *o = static_cast<DT *>(a.o);
     if constexpr (ws_fits<DT, DK, C, NW, GATED>()) {
         hipLaunchKernelGGL((chunk_fwd_ws_kernel<DT, DK, C, NW, GATED>), dim3((unsigned)grid),
-                           dim3(128 * NW), 0, stream, static_cast<const DT *>(q),
-                           static_cast<const DT *>(k), static_cast<const DT *>(v),
-                           static_cast<const DT *>(beta), g, S0, static_cast<DT *>(o), S_T,
-                           (int)T, (int)H, Dv, nvt);
+                           dim3(128 * NW), 0, stream, q, k, v, beta, a.g, a.S0, o, a.S_T, a.cu,
+                           (int)a.T, (int)a.H, a.Dv, nvt, a.scale);
     } else {
         hipLaunchKernelGGL((chunk_fwd_serial_kernel<DT, DK, C, NW, GATED>), dim3((unsigned)grid),
-                           dim3(64 * NW), 0, stream, static_cast<const DT *>(q),
-                           static_cast<const DT *>(k), static_cast<const DT *>(v),
-                           static_cast<const DT *>(beta), g, S0, static_cast<DT *>(o), S_T,
-                           (int)T, (int)H, Dv, nvt);
+                           dim3(64 * NW), 0, stream, q, k, v, beta, a.g, a.S0, o, a.S_T, a.cu,
+                           (int)a.T, (int)a.H, a.Dv, nvt, a.scale);
     }
     return hipGetLastError();
 }
@@ -1248,59 +1268,44 @@ inline int pick_waves(int64_t /*BH*/, int Dv) {
 }
 
 template <typename DT, int DK, int C, bool GATED>
-hipError_t dispatch_nw(const void *q, const void *k, const void *v, const void *beta,
-                       const float *g, const float *S0, void *o, float *S_T, int64_t B,
-                       int64_t T, int64_t H, int Dv, hipStream_t stream) {
-    switch (pick_waves(B * H, Dv)) {
-    case 4: return launch_cfg<DT, DK, C, 4, GATED>(q, k, v, beta, g, S0, o, S_T, B, T, H, Dv, stream);
-    case 2: return launch_cfg<DT, DK, C, 2, GATED>(q, k, v, beta, g, S0, o, S_T, B, T, H, Dv, stream);
-    default: return launch_cfg<DT, DK, C, 1, GATED>(q, k, v, beta, g, S0, o, S_T, B, T, H, Dv, stream);
+hipError_t dispatch_nw(const ChunkFwdArgs &a, hipStream_t stream) {
+    switch (pick_waves(a.B * a.H, a.Dv)) {
+    case 4: return launch_cfg<DT, DK, C, 4, GATED>(a, stream);
+    case 2: return launch_cfg<DT, DK, C, 2, GATED>(a, stream);
+    default: return launch_cfg<DT, DK, C, 1, GATED>(a, stream);
     }
 }
 
 template <typename DT, int DK, bool GATED>
-hipError_t dispatch_c(const void *q, const void *k, const void *v, const void *beta,
-                      const float *g, const float *S0, void *o, float *S_T, int64_t B,
-                      int64_t T, int64_t H, int Dv, int chunk, hipStream_t stream) {
-    switch (chunk) {
-    case 16: return dispatch_nw<DT, DK, 16, GATED>(q, k, v, beta, g, S0, o, S_T, B, T, H, Dv, stream);
-    case 32: return dispatch_nw<DT, DK, 32, GATED>(q, k, v, beta, g, S0, o, S_T, B, T, H, Dv, stream);
-    case 64: return dispatch_nw<DT, DK, 64, GATED>(q, k, v, beta, g, S0, o, S_T, B, T, H, Dv, stream);
+hipError_t dispatch_c(const ChunkFwdArgs &a, hipStream_t stream) {
+    switch (a.chunk) {
+    case 16: return dispatch_nw<DT, DK, 16, GATED>(a, stream);
+    case 32: return dispatch_nw<DT, DK, 32, GATED>(a, stream);
+    case 64: return dispatch_nw<DT, DK, 64, GATED>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <typename DT, bool GATED>
-hipError_t dispatch_dk(const void *q, const void *k, const void *v, const void *beta,
-                       const float *g, const float *S0, void *o, float *S_T, int64_t B,
-                       int64_t T, int64_t H, int Dk, int Dv, int chunk, hipStream_t stream) {
-    switch (Dk) {
-    case 16: return dispatch_c<DT, 16, GATED>(q, k, v, beta, g, S0, o, S_T, B, T, H, Dv, chunk, stream);
-    case 32: return dispatch_c<DT, 32, GATED>(q, k, v, beta, g, S0, o, S_T, B, T, H, Dv, chunk, stream);
-    case 64: return dispatch_c<DT, 64, GATED>(q, k, v, beta, g, S0, o, S_T, B, T, H, Dv, chunk, stream);
-    case 128: return dispatch_c<DT, 128, GATED>(q, k, v, beta, g, S0, o, S_T, B, T, H, Dv, chunk, stream);
+hipError_t dispatch_dk(const ChunkFwdArgs &a, hipStream_t stream) {
+    switch (a.Dk) {
+    case 16: return dispatch_c<DT, 16, GATED>(a, stream);
+    case 32: return dispatch_c<DT, 32, GATED>(a, stream);
+    case 64: return dispatch_c<DT, 64, GATED>(a, stream);
+    case 128: return dispatch_c<DT, 128, GATED>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
 // Every kernel of one rule (plain or gated), both dtypes.
 template <bool GATED>
-hipError_t launch_rule(const void *q, const void *k, const void *v, const void *beta,
-                       const float *g, const float *S0, void *o, float *S_T, int64_t B,
-                       int64_t T, int64_t H, int Dk, int Dv, int chunk, bool bf16,
-                       hipStream_t stream) {
-    if (bf16)
-        return dispatch_dk<__bf16, GATED>(q, k, v, beta, g, S0, o, S_T, B, T, H, Dk, Dv, chunk,
-                                          stream);
-    return dispatch_dk<float, GATED>(q, k, v, beta, g, S0, o, S_T, B, T, H, Dk, Dv, chunk, stream);
+hipError_t launch_rule(const ChunkFwdArgs &a, bool bf16, hipStream_t stream) {
+    return bf16 ? dispatch_dk<__bf16, GATED>(a, stream) : dispatch_dk<float, GATED>(a, stream);
 }
 
 }  // namespace
 
 // The gated instantiations live in their own translation unit.
-hipError_t launch_chunk_fwd_gated(const void *q, const void *k, const void *v,
-                                  const void *beta, const float *g, const float *S0, void *o,
-                                  float *S_T, int64_t B, int64_t T, int64_t H, int Dk, int Dv,
-                                  int chunk, bool bf16, hipStream_t stream);
+hipError_t launch_chunk_fwd_gated(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
 
 }  // namespace dr

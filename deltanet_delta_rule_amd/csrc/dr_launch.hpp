@@ -8,12 +8,23 @@
 
 namespace dr {
 
-// Fused chunkwise forward (one workgroup per (b, h, value tile)).  g is the
-// log forget gate [B,T,H] (fp32) of the gated rule, or nullptr.
-hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v,
-                            const void *beta, const float *g, const float *S0, void *o,
-                            float *S_T, int64_t B, int64_t T, int64_t H, int Dk, int Dv,
-                            int chunk, bool bf16, hipStream_t stream);
+// Arguments of the fused chunkwise forward (one workgroup per (sequence,
+// head, value tile)).  g is the log forget gate [B,T,H] (fp32) of the gated
+// rule, or nullptr.  cu, when set, holds B+1 sequence offsets into the single
+// batch row of T tokens (packed variable-length input); scale multiplies the
+// outputs.
+struct ChunkFwdArgs {
+    const void *q, *k, *v, *beta;
+    const float *g, *S0;
+    void *o;
+    float *S_T;
+    const int *cu;
+    int64_t B, T, H;
+    int Dk, Dv, chunk;
+    float scale;
+};
+
+hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
 
 // Single-token decode step, state updated in place.  g is the log forget gate
 // [B,H] (fp32) of the gated rule, or nullptr.

@@ -110,6 +110,51 @@ dr_status delta_rule_chunk_fwd(const void *q, const void *k, const void *v,
                                dr_dtype dtype, void *stream);
 
 /*
+ * Options of delta_rule_chunk_fwd_ex (zero-initialise, then set scale = 1).
+ *
+ *   g           [B,T,H] fp32 log forget gate, or NULL.  Non-NULL selects the
+ *               gated rule of gated_delta_rule_chunk_fwd.
+ *   cu_seqlens  device int32 [num_seqs+1], or NULL.  Non-NULL packs num_seqs
+ *               variable-length sequences into one batch row (B must be 1):
+ *               sequence s is tokens cu_seqlens[s] .. cu_seqlens[s+1]-1 of
+ *               the T tokens, chunked from its own first token, with its own
+ *               initial and final state: S0 and S_T are then
+ *               [num_seqs,H,Dv,Dk].  Offsets should be non-decreasing from 0
+ *               to T; the kernels clamp them into [0, T] (an empty or
+ *               inverted range is an empty sequence) so that no access leaves
+ *               the buffers.  The array must not change while the call runs.
+ *               Tokens covered by no sequence get no output.  This is the
+ *               packed layout of fla's `cu_seqlens` (fla
+ *               fla/layers/delta_net.py, forward).
+ *   num_seqs    number of packed sequences (>= 0) when cu_seqlens != NULL.
+ *   scale       finite output scale: o = scale * S_t q_t (the same as
+ *               scaling q; the DeltaNet layer passes none, the gated layer
+ *               of houmin.site "infra/delta-net" divides q by sqrt(d_k)).
+ *   flags       must be 0.
+ */
+typedef struct dr_chunk_opts {
+    const float *g;
+    const int32_t *cu_seqlens;
+    int64_t num_seqs;
+    float scale;
+    uint32_t flags;
+} dr_chunk_opts;
+
+/*
+ * delta_rule_chunk_fwd_ex -- delta_rule_chunk_fwd with the options above
+ * (opts == NULL: none, i.e. exactly delta_rule_chunk_fwd).  Every other
+ * argument, size, layout and error behaves as in delta_rule_chunk_fwd; in
+ * addition DR_ERR_INVALID_ARG is returned for cu_seqlens with B != 1, a
+ * negative num_seqs, a misaligned cu_seqlens, cu_seqlens overlapping an
+ * output, a non-finite scale or unknown flags.
+ */
+dr_status delta_rule_chunk_fwd_ex(const void *q, const void *k, const void *v,
+                                  const void *beta, const float *S0, void *o, float *S_T,
+                                  int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                  int64_t chunk, const dr_chunk_opts *opts, dr_dtype dtype,
+                                  void *stream);
+
+/*
  * delta_rule_recurrent_step -- one decode token per sequence, state in place.
  *
  * For every (b,h): reads S, applies the delta-rule write for the token
@@ -182,7 +227,7 @@ const char *delta_rule_status_string(dr_status status);
 int delta_rule_last_hip_error(void);
 
 /* Library version as major*10000 + minor*100 + patch (2.0.0: the gated
- * entry points). */
+ * entry points; 2.1.0: delta_rule_chunk_fwd_ex). */
 int delta_rule_version(void);
 
 #ifdef __cplusplus

@@ -198,3 +198,52 @@ def test_gated_binding_checks_the_gate():
     with pytest.raises(ValueError):
         dr.gated_delta_rule_recurrent_step(x[:, 0], x[:, 0], x[:, 0], x[:, 0, :, 0],
                                            x[:, 0, :, 0], torch.zeros(1, 1, 16, 16))
+
+
+# ------------------------------------------------- extended chunked forward
+CU = ctypes.c_void_p(0x100000 * 8)   # sequence offsets, apart from every other buffer
+
+
+def _ex(lib, opts=None, q=P[0], k=P[1], v=P[2], beta=P[3], S0=None, o=P[4], S_T=P[5],
+        B=1, T=64, H=2, Dk=64, Dv=64, chunk=64, dtype=dr.DR_BF16):
+    return lib.delta_rule_chunk_fwd_ex(q, k, v, beta, S0, o, S_T, B, T, H, Dk, Dv, chunk,
+                                       None if opts is None else ctypes.byref(opts), dtype, None)
+
+
+def _opts(**kw):
+    o = dr.dr_chunk_opts(g=None, cu_seqlens=None, num_seqs=0, scale=1.0, flags=0)
+    for name, val in kw.items():
+        setattr(o, name, val)
+    return o
+
+
+def test_chunk_options_struct_layout():
+    # pointer, pointer, int64, float, uint32: 32 bytes with no padding between
+    assert ctypes.sizeof(dr.dr_chunk_opts) == 32
+    assert dr.dr_chunk_opts.scale.offset == 24 and dr.dr_chunk_opts.flags.offset == 28
+
+
+@pytest.mark.parametrize("kw, call", [
+    (dict(cu_seqlens=CU.value, num_seqs=3), dict(B=2)),          # packed needs B == 1
+    (dict(cu_seqlens=CU.value, num_seqs=-1), {}),                # negative count
+    (dict(cu_seqlens=ODD.value, num_seqs=2), {}),                # misaligned offsets
+    (dict(cu_seqlens=P[4].value, num_seqs=2), {}),               # offsets overlap o
+    (dict(cu_seqlens=CU.value, num_seqs=2), dict(S_T=CU)),       # S_T overlaps offsets
+    (dict(scale=float("nan")), {}),
+    (dict(scale=float("inf")), {}),
+    (dict(flags=1), {}),                                         # no flags are defined
+    (dict(g=ODD.value), {}),                                     # gate misaligned
+    (dict(g=P[4].value), {}),                                    # gate overlaps o
+])
+def test_chunk_ex_rejects_invalid(lib, kw, call):
+    assert _ex(lib, _opts(**kw), **call) == dr.DR_ERR_INVALID_ARG
+
+
+def test_chunk_ex_rejects_unsupported(lib):
+    assert _ex(lib, _opts(scale=0.5), Dk=48) == dr.DR_ERR_UNSUPPORTED
+    assert _ex(lib, None, chunk=128) == dr.DR_ERR_UNSUPPORTED
+
+
+def test_chunk_ex_no_sequences_is_a_no_op(lib):
+    assert _ex(lib, _opts(cu_seqlens=CU.value, num_seqs=0)) == dr.DR_OK
+    assert _ex(lib, _opts(scale=2.0), H=0) == dr.DR_OK
