@@ -19,6 +19,7 @@ JSON line on stdout:
                (B=128, H=16, d=128), HBM bytes per step and tokens/s
   gated        the gated rule (per-token log forget gate) on the layer shape
                (chunked forward) and on the decode workload
+  qk_l2norm    the layer shape with raw q, k normalised inside the kernel
 
 Options: --gpus N (only 1: this build targets one GPU), --steps K,
 --warmup W, --no-cpu-baseline, --no-decode, --no-gated, --copy-calib BYTES (also time a
@@ -185,10 +186,11 @@ def bench_decode(torch, dr, W, reps=3, name="decode"):
     }
 
 
-def bench_gated_chunk(torch, dr, W, reps=20):
-    """The gated chunked forward on the layer shape (mean launch time with HIP
-    events on the launch stream)."""
-    w = W.get("gated_layer_1p3b")
+def bench_gated_chunk(torch, dr, W, reps=20, name="gated_layer_1p3b", l2=False):
+    """A chunked-forward variant on the layer shape (mean launch time with HIP
+    events on the launch stream): the gated rule, or with l2 the plain rule
+    on raw q, k normalised inside the kernel."""
+    w = W.get(name, feature="raw") if l2 else W.get(name)
     x = W.generate(w)
     dev = torch.device("cuda:0")
     d = {n: (None if t is None else t.to(dev)) for n, t in x.items()}
@@ -196,8 +198,13 @@ def bench_gated_chunk(torch, dr, W, reps=20):
     st = torch.empty((w.B, w.H, w.Dv, w.Dk), dtype=torch.float32, device=dev)
 
     def step():
-        dr.gated_delta_rule_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["S0"],
-                                      chunk=w.chunk, o=o, S_T=st)
+        if d["g"] is None:
+            dr.delta_rule_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["S0"], chunk=w.chunk,
+                                    o=o, S_T=st, use_qk_l2norm_in_kernel=l2)
+        else:
+            dr.gated_delta_rule_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["S0"],
+                                          chunk=w.chunk, o=o, S_T=st,
+                                          use_qk_l2norm_in_kernel=l2)
 
     for _ in range(3):
         step()
@@ -213,7 +220,8 @@ def bench_gated_chunk(torch, dr, W, reps=20):
     flops, nbytes = chunk_work(w)
     return {
         "workload": (f"{w.name} B{w.B} H{w.H} T{w.T} d{w.Dk} chunk {w.chunk}, bf16 in, "
-                     "fp32 log gates and state"),
+                     + ("raw q, k normalised in the kernel, fp32 state" if l2 else
+                        "fp32 log gates and state")),
         "tokens_per_s": w.B * w.T / launch_s,
         "mean_launch_us": round(launch_s * 1e6, 2),
         "hbm_frac": round(nbytes / launch_s / 1e9 / HBM_PEAK_GBS, 4),
@@ -330,6 +338,8 @@ def main():
         out["gated"] = {"chunk": bench_gated_chunk(torch, dr, W)}
         if not args.no_decode:
             out["gated"]["decode"] = bench_decode(torch, dr, W, name="gated_decode")
+        log("in-kernel q/k L2 norm: layer shape chunked forward")
+        out["qk_l2norm"] = {"chunk": bench_gated_chunk(torch, dr, W, name="layer_1p3b", l2=True)}
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle on the whole workload")
         torch.cuda.synchronize()

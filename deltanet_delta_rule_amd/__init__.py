@@ -16,9 +16,9 @@ and the gated rule (g = log of the per-token, per-head forget gate, fp32):
     o, S_T = gated_delta_rule_chunk_fwd(q, k, v, beta, g, S0=None, chunk=64)
     o      = gated_delta_rule_recurrent_step(q, k, v, beta, g, S)
 
-Both chunked calls also take ``scale=`` (output scale) and ``cu_seqlens=``
-(packed variable-length sequences in one batch row), which route them to
-``delta_rule_chunk_fwd_ex``.
+Both chunked calls also take ``scale=`` (output scale), ``cu_seqlens=``
+(packed variable-length sequences in one batch row) and
+``use_qk_l2norm_in_kernel=``, which route them to ``delta_rule_chunk_fwd_ex``.
 """
 from __future__ import annotations
 
@@ -147,8 +147,11 @@ def _need(t, name, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+DR_QK_L2NORM = 1
+
+
 def _chunk_call(gated, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, stream,
-                scale=None, cu_seqlens=None):
+                scale=None, cu_seqlens=None, l2norm=False):
     torch = _torch()
     dev = q.device
     if dev.type != "cuda":
@@ -189,7 +192,7 @@ def _chunk_call(gated, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, 
     lib = load_library()
     common = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta))
     tail = (B, T, H, Dk, Dv, int(chunk))
-    if scale is None and cu_seqlens is None:
+    if scale is None and cu_seqlens is None and not l2norm:
         if gated:
             st = lib.gated_delta_rule_chunk_fwd(*common, _ptr(g), _ptr(S0), _ptr(o), _ptr(S_T),
                                                 *tail, _dtype_code(q), _stream(dev, stream))
@@ -200,7 +203,8 @@ def _chunk_call(gated, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, 
         opts = dr_chunk_opts(g=g.data_ptr() if gated else None,
                              cu_seqlens=None if cu_seqlens is None else cu_seqlens.data_ptr(),
                              num_seqs=nseq if cu_seqlens is not None else 0,
-                             scale=1.0 if scale is None else float(scale), flags=0)
+                             scale=1.0 if scale is None else float(scale),
+                             flags=DR_QK_L2NORM if l2norm else 0)
         st = lib.delta_rule_chunk_fwd_ex(*common, _ptr(S0), _ptr(o), _ptr(S_T), *tail,
                                          ctypes.byref(opts), _dtype_code(q),
                                          _stream(dev, stream))
@@ -210,25 +214,29 @@ def _chunk_call(gated, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, 
 
 def delta_rule_chunk_fwd(q, k, v, beta, S0=None, *, chunk: int = 64,
                          output_final_state: bool = True, o=None, S_T=None,
-                         scale=None, cu_seqlens=None, stream=None):
+                         scale=None, cu_seqlens=None, use_qk_l2norm_in_kernel=False,
+                         stream=None):
     """Chunkwise forward.  q, k ``[B,T,H,Dk]``; v ``[B,T,H,Dv]``; beta
     ``[B,T,H]`` (float32 or bfloat16, all the same dtype, on one GPU);
     S0 ``[B,H,Dv,Dk]`` float32 or None.  Returns ``(o, S_T)``; S_T is None
     when ``output_final_state`` is False.  ``o`` / ``S_T`` may be passed in
     (S_T may be S0 itself to carry the state in place).  ``scale`` multiplies
     the outputs; ``cu_seqlens`` (int32 ``[N+1]`` on the GPU, B = 1) packs N
-    sequences, whose states S0 / S_T are then ``[N,H,Dv,Dk]``."""
+    sequences, whose states S0 / S_T are then ``[N,H,Dv,Dk]``.
+    ``use_qk_l2norm_in_kernel`` normalises the rows of q and k inside the
+    kernel (x / sqrt(sum x^2 + 1e-6))."""
     return _chunk_call(False, q, k, v, beta, None, S0, chunk, output_final_state, o, S_T,
-                       stream, scale, cu_seqlens)
+                       stream, scale, cu_seqlens, use_qk_l2norm_in_kernel)
 
 
 def gated_delta_rule_chunk_fwd(q, k, v, beta, g, S0=None, *, chunk: int = 64,
                                output_final_state: bool = True, o=None, S_T=None,
-                               scale=None, cu_seqlens=None, stream=None):
+                               scale=None, cu_seqlens=None, use_qk_l2norm_in_kernel=False,
+                               stream=None):
     """Chunkwise forward of the gated rule: as ``delta_rule_chunk_fwd`` plus
     g ``[B,T,H]`` float32, the log of each token's forget gate (<= 0)."""
     return _chunk_call(True, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, stream,
-                       scale, cu_seqlens)
+                       scale, cu_seqlens, use_qk_l2norm_in_kernel)
 
 
 def _step_call(entry, q, k, v, beta, g, S, o, stream):

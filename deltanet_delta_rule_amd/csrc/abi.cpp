@@ -54,7 +54,7 @@ dr_status hip_status(hipError_t e) {
 dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *beta,
                     const float *g, bool gated, const float *S0, void *o, float *S_T,
                     int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t chunk,
-                    const int32_t *cu, int64_t nseq, float scale, dr_dtype dtype,
+                    const int32_t *cu, int64_t nseq, float scale, bool l2, dr_dtype dtype,
                     void *stream) {
     if (dtype != DR_F32 && dtype != DR_BF16) return DR_ERR_INVALID_ARG;
     if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0 || chunk < 0) return DR_ERR_INVALID_ARG;
@@ -103,7 +103,7 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
     dr::ChunkFwdArgs a{q,  k,        v,        beta, gated ? g : nullptr,
                        S0, o,        S_T,      cu,   ns_count,
                        T,  H,        (int)Dk,  (int)Dv, (int)chunk,
-                       scale};
+                       scale, l2};
     return hip_status(dr::launch_chunk_fwd(a, dtype == DR_BF16, static_cast<hipStream_t>(stream)));
 }
 
@@ -150,7 +150,7 @@ dr_status delta_rule_chunk_fwd(const void *q, const void *k, const void *v,
                                int64_t Dk, int64_t Dv, int64_t chunk,
                                dr_dtype dtype, void *stream) {
     return chunk_fwd(q, k, v, beta, nullptr, false, S0, o, S_T, B, T, H, Dk, Dv, chunk, nullptr,
-                     0, 1.f, dtype, stream);
+                     0, 1.f, false, dtype, stream);
 }
 
 dr_status delta_rule_chunk_fwd_ex(const void *q, const void *k, const void *v,
@@ -161,9 +161,10 @@ dr_status delta_rule_chunk_fwd_ex(const void *q, const void *k, const void *v,
     dr_chunk_opts d{};
     d.scale = 1.f;
     const dr_chunk_opts &x = opts ? *opts : d;
-    if (x.flags != 0) return DR_ERR_INVALID_ARG;  // no flags are defined
+    if (x.flags & ~uint32_t(DR_QK_L2NORM)) return DR_ERR_INVALID_ARG;  // unknown flags
     return chunk_fwd(q, k, v, beta, x.g, x.g != nullptr, S0, o, S_T, B, T, H, Dk, Dv, chunk,
-                     x.cu_seqlens, x.num_seqs, x.scale, dtype, stream);
+                     x.cu_seqlens, x.num_seqs, x.scale, (x.flags & DR_QK_L2NORM) != 0, dtype,
+                     stream);
 }
 
 dr_status delta_rule_recurrent_step(const void *q, const void *k,
@@ -179,7 +180,7 @@ dr_status gated_delta_rule_chunk_fwd(const void *q, const void *k, const void *v
                                      int64_t Dk, int64_t Dv, int64_t chunk, dr_dtype dtype,
                                      void *stream) {
     return chunk_fwd(q, k, v, beta, g, true, S0, o, S_T, B, T, H, Dk, Dv, chunk, nullptr, 0, 1.f,
-                     dtype, stream);
+                     false, dtype, stream);
 }
 
 dr_status gated_delta_rule_recurrent_step(const void *q, const void *k, const void *v,
@@ -201,6 +202,6 @@ const char *delta_rule_status_string(dr_status status) {
 
 int delta_rule_last_hip_error(void) { return g_last_hip_error; }
 
-int delta_rule_version(void) { return 20100; }
+int delta_rule_version(void) { return 20200; }
 
 }  // extern "C"

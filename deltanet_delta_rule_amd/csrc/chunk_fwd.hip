@@ -1,12 +1,14 @@
 // Chunked forward of the plain delta rule: the kernels of chunk_fwd.hpp
-// without the forget gate, and the entry that routes gated calls to
-// chunk_fwd_gated.hip.
+// without the forget gate or in-kernel normalisation, and the entry that
+// routes the other variants to their translation units.
 #include "chunk_fwd.hpp"
 
 namespace dr {
 
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, bool bf16, hipStream_t stream) {
-    return a.g ? launch_chunk_fwd_gated(a, bf16, stream) : launch_rule<false>(a, bf16, stream);
+    if (a.l2)
+        return a.g ? launch_chunk_fwd_gated_l2(a, bf16, stream) : launch_chunk_fwd_l2(a, bf16, stream);
+    return a.g ? launch_chunk_fwd_gated(a, bf16, stream) : launch_rule<false, false>(a, bf16, stream);
 }
 
 }  // namespace dr

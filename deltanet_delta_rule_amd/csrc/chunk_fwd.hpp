@@ -232,7 +232,7 @@ __device__ __forceinline__ f32x4 mm16(const F &a, const F &b) {
 }
 
 template <typename DT>
-__device__ __forceinline__ void diag_inverse(const f32x4 &a, const float *betas, DT *Tb, int d,
+__device__ __forceinline__ void diag_inverse(const f32x4 &a, const f32x4 &b4, DT *Tb, int d,
                                              int lane) {
     typedef typename Frag<DT>::k16 F;
     const int g = lane >> 4, r = lane & 15;
@@ -260,9 +260,9 @@ __device__ __forceinline__ void diag_inverse(const f32x4 &a, const float *betas,
         Tt -= mm16(fM, fTt);           // M^T T^T
     }
     // lane (g, r) holds T^T[4g + i][r] = T[r][4g + i]: row r, columns 4g ..
-    // 4g + 3, the A-operand fragment of T_dd.  Stored as -T_dd diag(beta_d),
-    // the form the block substitution uses (state_rest).
-    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(betas + 16 * d + 4 * g);
+    // 4g + 3, the A-operand fragment of T_dd.  Stored as -T_dd diag(beta_d)
+    // (b4: beta of columns 4g .. 4g + 3), the form the block substitution
+    // uses (state_rest).
     store_fragblk(Tb, d, lane, -(Tt * b4));
 }
 
@@ -308,6 +308,49 @@ struct GateSets<C, NS, false> {
     __device__ __forceinline__ GateLds<C> *at(int) { return nullptr; }
 };
 
+// In-kernel L2 normalisation of q and k (L2): per-token inverse norms
+// 1/sqrt(|x|^2 + eps), the l2norm of the gated layer on houmin.site
+// ("infra/delta-net", section "Gated DeltaNet", code).  |k_t|^2 is the
+// diagonal of the chunk's K K^T tiles and |q_t|^2 that of a Q Q^T product
+// per 16-token tile; the kernel never rewrites q or k but applies the norms
+// as row scalings:
+//   A      = diag(beta nk) G diag(nk) on the diagonal blocks (their inverses),
+//            raw G = K K^T off the diagonal,
+//   F_j    = diag(nk_j) E_j replaces E_j as the operand of every product,
+//   X_i    <- diag(nk_i) (K_i S^T + sum_{j<i} G_ij F_j) - V_i before the
+//            block product with -T_ii diag(beta_i),
+//   O      = diag(nq) (Q S^T + P F),   S^T += K^T F,
+// which is the chunk form on the normalised q and k.  Two buffers (chunk
+// parity), like the Gram products that carry them.
+constexpr float L2_EPS = 1e-6f;
+
+template <int C>
+struct alignas(16) NormLds {
+    float nk[C], nq[C];  // 1/|k_t|, 1/|q_t|
+};
+template <int C, int NS, bool L2>
+struct NormSets {
+    NormLds<C> s[NS];
+    __device__ __forceinline__ NormLds<C> *at(int i) { return &s[i]; }
+};
+template <int C, int NS>
+struct NormSets<C, NS, false> {
+    __device__ __forceinline__ NormLds<C> *at(int) { return nullptr; }
+};
+
+// Inverse norm of token 16 ti + r from a 16x16 Gram tile of a matrix with
+// itself (lane (g, r) holds entries (r, 4g + e)): lanes with 4g <= r < 4g + 4
+// hold the diagonal entry; the result is valid in those lanes only.
+__device__ __forceinline__ float diag_inv_norm(const f32x4 &acc, int lane, bool &own) {
+    const int g = lane >> 4, r = lane & 15, e0 = r - 4 * g;
+    float d = acc[0];
+    d = e0 == 1 ? acc[1] : d;
+    d = e0 == 2 ? acc[2] : d;
+    d = e0 == 3 ? acc[3] : d;
+    own = e0 >= 0 && e0 < 4;
+    return rsqrtf(d + L2_EPS);
+}
+
 // Gram tiles of one chunk, for the rows of the Gram jobs of wave W:
 //   A-row job ti:  the K K^T tiles of row ti.  The diagonal tile, scaled
 //                  to A = tril(diag(beta) K K^T, -1), is inverted right away
@@ -348,10 +391,10 @@ constexpr int n_prows() {
 // row and column tokens, exp(b_row - b_col) (bc: the chunk's prefix sums),
 // which turns K K^T into the decayed couplings and Q K^T into the decayed
 // reads of the pages' chunked form.
-template <typename DT, int DK, int C, int NW, bool GATED, typename FD>
+template <typename DT, int DK, int C, int NW, bool GATED, bool L2, typename FD>
 __device__ __forceinline__ void gram_tile(const FD *fkj, const FD *fx, bool isP, int ti, int tj,
                                           float brow, const float *betas, const float *bc,
-                                          DT *Ab, DT *Tb, DT *Ps, int lane) {
+                                          DT *Ab, DT *Tb, DT *Ps, NormLds<C> *nl, int lane) {
     typedef ChunkCfg<DT, DK, C, NW> G;
     constexpr int KSD = G::KSD, NSD = DK / KSD;
     const int g = lane >> 4, r = lane & 15;
@@ -380,19 +423,51 @@ __device__ __forceinline__ void gram_tile(const FD *fkj, const FD *fx, bool isP,
         store_frag16(Ps + row * G::LDP + p_col<G::KSC>(col), out);
     } else if (tj == ti) {
         f32x4 a;
+        const f32x4 b4 = *reinterpret_cast<const f32x4 *>(betas + col);
+        if constexpr (L2) {
+            // the diagonal of G gives |k|^2 of the tile's tokens (its decay
+            // factor is exactly 1); normalise the block on both sides
+            bool own;
+            const float nk = diag_inv_norm(acc, lane, own);
+            const float nr = __shfl(nk, 16 * (r >> 2) + r, 64);  // token row
+            f32x4 nc;                                              // tokens col + e
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a[e] = row > col + e ? brow * acc[e] : 0.f;
-        diag_inverse(a, betas, Tb, ti, lane);
+            for (int e = 0; e < 4; ++e) nc[e] = __shfl(nk, 20 * g + e, 64);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[e] = row > col + e ? brow * nr * nc[e] * acc[e] : 0.f;
+            if (own) nl->nk[row] = nk;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[e] = row > col + e ? brow * acc[e] : 0.f;
+        }
+        diag_inverse(a, b4, Tb, ti, lane);
     } else {
         store_fragblk(Ab, off_idx(ti, tj), lane, acc);
     }
 }
 
+// 1/|q| of the 16 tokens of tile ti from the diagonal of Q_ti Q_ti^T (L2).
+template <typename DT, int DK, int C, int NW, typename FD>
+__device__ __forceinline__ void q_norms(const FD *fq, int ti, NormLds<C> *nl, int lane) {
+    typedef ChunkCfg<DT, DK, C, NW> G;
+    constexpr int KSD = G::KSD, NSD = DK / KSD;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < NSD; ++s) {
+        if constexpr (KSD == 32) mma_k32(acc, fq[s], fq[s]);
+        else mma_k16(acc, fq[s], fq[s]);
+    }
+    bool own;
+    const float nq = diag_inv_norm(acc, lane, own);
+    if (own) nl->nq[16 * ti + (lane & 15)] = nq;
+}
+
 // When the fragments of all the wave's jobs fit in 96 VGPRs they are loaded
 // once, before the first MFMA; otherwise each job loads its own.
-template <typename DT, int DK, int C, int NW, int W, bool GATED>
+template <typename DT, int DK, int C, int NW, int W, bool GATED, bool L2>
 __device__ __forceinline__ void gram_tiles_w(const DT *Ks, const DT *Qs, const float *betas,
-                                             const float *bc, DT *Ab, DT *Tb, DT *Ps, int lane) {
+                                             const float *bc, DT *Ab, DT *Tb, DT *Ps,
+                                             NormLds<C> *nl, int lane) {
     typedef ChunkCfg<DT, DK, C, NW> G;
     typedef GramJobs<G::NT, NW, W> J;
     constexpr int NT = G::NT, KSD = G::KSD, NSD = DK / KSD, KM = J::kmax();
@@ -420,11 +495,13 @@ __device__ __forceinline__ void gram_tiles_w(const DT *Ks, const DT *Qs, const f
 #pragma unroll
             for (int ti = 0; ti < NT; ++ti) {
                 if (!(isP ? J::p_row(ti) : J::a_row(ti))) continue;
+                if constexpr (L2)
+                    if (isP) q_norms<DT, DK, C, NW>(fq[ti], ti, nl, lane);
 #pragma unroll
                 for (int tj = 0; tj <= ti; ++tj)
-                    gram_tile<DT, DK, C, NW, GATED>(fk[tj], isP ? fq[ti] : fk[ti], isP, ti, tj,
-                                                    isP ? 0.f : brow[ti], betas, bc, Ab, Tb, Ps,
-                                                    lane);
+                    gram_tile<DT, DK, C, NW, GATED, L2>(fk[tj], isP ? fq[ti] : fk[ti], isP, ti, tj,
+                                                        isP ? 0.f : brow[ti], betas, bc, Ab, Tb,
+                                                        Ps, nl, lane);
             }
     } else {
 #pragma unroll
@@ -435,27 +512,29 @@ __device__ __forceinline__ void gram_tiles_w(const DT *Ks, const DT *Qs, const f
                 FD fx[NSD];
 #pragma unroll
                 for (int s = 0; s < NSD; ++s) kq_rows<DT, DK, C, NW>(isP ? Qs : Ks, 16 * ti, s * KSD, lane, fx[s]);
+                if constexpr (L2)
+                    if (isP) q_norms<DT, DK, C, NW>(fx, ti, nl, lane);
 #pragma unroll
                 for (int tj = 0; tj <= ti; ++tj) {
                     FD fk[NSD];
 #pragma unroll
                     for (int s = 0; s < NSD; ++s) kq_rows<DT, DK, C, NW>(Ks, 16 * tj, s * KSD, lane, fk[s]);
-                    gram_tile<DT, DK, C, NW, GATED>(fk, fx, isP, ti, tj, isP ? 0.f : brow[ti],
-                                                    betas, bc, Ab, Tb, Ps, lane);
+                    gram_tile<DT, DK, C, NW, GATED, L2>(fk, fx, isP, ti, tj, isP ? 0.f : brow[ti],
+                                                        betas, bc, Ab, Tb, Ps, nl, lane);
                 }
             }
     }
 }
 
-template <typename DT, int DK, int C, int NW, bool GATED>
+template <typename DT, int DK, int C, int NW, bool GATED, bool L2>
 __device__ __forceinline__ void gram_tiles(const DT *Ks, const DT *Qs, const float *betas,
-                                           const float *bc, DT *Ab, DT *Tb, DT *Ps, int wave,
-                                           int lane) {
+                                           const float *bc, DT *Ab, DT *Tb, DT *Ps,
+                                           NormLds<C> *nl, int wave, int lane) {
     switch (wave) {
-    case 0: gram_tiles_w<DT, DK, C, NW, 0, GATED>(Ks, Qs, betas, bc, Ab, Tb, Ps, lane); break;
-    case 1: if constexpr (NW > 1) gram_tiles_w<DT, DK, C, NW, 1, GATED>(Ks, Qs, betas, bc, Ab, Tb, Ps, lane); break;
-    case 2: if constexpr (NW > 2) gram_tiles_w<DT, DK, C, NW, 2, GATED>(Ks, Qs, betas, bc, Ab, Tb, Ps, lane); break;
-    default: if constexpr (NW > 3) gram_tiles_w<DT, DK, C, NW, 3, GATED>(Ks, Qs, betas, bc, Ab, Tb, Ps, lane); break;
+    case 0: gram_tiles_w<DT, DK, C, NW, 0, GATED, L2>(Ks, Qs, betas, bc, Ab, Tb, Ps, nl, lane); break;
+    case 1: if constexpr (NW > 1) gram_tiles_w<DT, DK, C, NW, 1, GATED, L2>(Ks, Qs, betas, bc, Ab, Tb, Ps, nl, lane); break;
+    case 2: if constexpr (NW > 2) gram_tiles_w<DT, DK, C, NW, 2, GATED, L2>(Ks, Qs, betas, bc, Ab, Tb, Ps, nl, lane); break;
+    default: if constexpr (NW > 3) gram_tiles_w<DT, DK, C, NW, 3, GATED, L2>(Ks, Qs, betas, bc, Ab, Tb, Ps, nl, lane); break;
     }
 }
 
@@ -500,7 +579,7 @@ __device__ __forceinline__ void store_out4_f32(const f32x4 &x, const OutChunk &o
 // Gated rule: X starts at zero, and gate_xy applies the decays and -V after
 // the products (V is then loaded after them, which keeps its fragments out of
 // the products' live range).
-template <typename DT, int DK, int C, int NW, bool GATED>
+template <typename DT, int DK, int C, int NW, bool GATED, bool L2>
 __device__ __forceinline__ void state_xy(const DT *Ks, const DT *Qs, const f32x4 *Sacc,
                                          const typename Frag<DT>::k16 *fv, f32x4 *X, f32x4 *Y,
                                          int lane) {
@@ -514,7 +593,7 @@ __device__ __forceinline__ void state_xy(const DT *Ks, const DT *Qs, const f32x4
     for (int mt = 0; mt < NT; ++mt) {
         Y[mt] = zero4();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) X[mt][i] = GATED ? 0.f : -frag_get(fv[mt], i);
+        for (int i = 0; i < 4; ++i) X[mt][i] = (GATED || L2) ? 0.f : -frag_get(fv[mt], i);
     }
     // All operand fragments are loaded before the first MFMA when they fit in
     // 128 VGPRs; otherwise they are double-buffered one slab ahead.
@@ -556,7 +635,8 @@ __device__ __forceinline__ void state_xy(const DT *Ks, const DT *Qs, const f32x4
 
 // Gated rule (gam: the chunk's decay from its start): the incoming state is
 // read through the decay, X = diag(gam) K S^T - V and Y = S Q^T diag(gam).
-template <typename DT, int C, int NT>
+// With SUBV false (L2) the V term is left to the block substitution.
+template <typename DT, int C, int NT, bool SUBV>
 __device__ __forceinline__ void gate_xy(const typename Frag<DT>::k16 *fv, const float *gam,
                                         f32x4 *X, f32x4 *Y, int lane) {
     const int g = lane >> 4, r = lane & 15;
@@ -567,7 +647,7 @@ __device__ __forceinline__ void gate_xy(const typename Frag<DT>::k16 *fv, const 
         const float gy = gam[16 * mt + r];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            X[mt][i] = gx[i] * X[mt][i] - frag_get(fv[mt], i);
+            X[mt][i] = SUBV ? gx[i] * X[mt][i] - frag_get(fv[mt], i) : gx[i] * X[mt][i];
             Y[mt][i] *= gy;
         }
     }
@@ -626,11 +706,12 @@ __device__ __forceinline__ void cat16(const f32x4_arr &a, const f32x4_arr &b, f3
 // outputs are unchanged; the state update becomes
 //   S^T <- gam_last S^T + K^T diag(rto) E
 // with its own copy of the E fragments (the outputs need the unscaled E).
-template <typename DT, int DK, int C, int NW, bool GATED>
+template <typename DT, int DK, int C, int NW, bool GATED, bool L2>
 __device__ __forceinline__ void state_rest(const ChunkOperands<DT, DK, C, NW> &op,
                                            const DT *Ab, const DT *Tb, const DT *Ps,
-                                           const GateLds<C> *ga, f32x4 *Sacc, f32x4 *X,
-                                           f32x4 *Y, const OutChunk &out, int lane) {
+                                           const GateLds<C> *ga, const NormLds<C> *nl,
+                                           f32x4 *Sacc, f32x4 *X, f32x4 *Y, const OutChunk &out,
+                                           int lane) {
     typedef ChunkCfg<DT, DK, C, NW> G;
     constexpr int NT = G::NT, ND = G::ND, KSD = G::KSD, KSC = G::KSC;
     constexpr int NSC = C / KSC, NOFF = NT * (NT - 1) / 2;
@@ -656,12 +737,19 @@ __device__ __forceinline__ void state_rest(const ChunkOperands<DT, DK, C, NW> &o
     for (int i = 0; i < NT; ++i) {
 #pragma unroll
         for (int j = 0; j < i; ++j) mma_k16(X[i], fa[off_idx(i, j)], fe16[j]);
+        // rows of X[i] and E[i] are tokens 16i + 4g .. 16i + 4g + 3
+        f32x4 nk4;
+        if constexpr (L2) {
+            nk4 = *reinterpret_cast<const f32x4 *>(nl->nk + 16 * i + 4 * (lane >> 4));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) X[i][e] = nk4[e] * X[i][e] - frag_get(op.fv[i], e);
+        }
         F16 fr;
         frag_from_acc16(X[i], fr);
         E[i] = mm16(ft[i], fr);
+        if constexpr (L2) E[i] *= nk4;  // F_i, the operand form of E_i
         frag_from_acc16(E[i], fe16[i]);
         if constexpr (GATED) {
-            // rows of E[i] are tokens 16i + 4g .. 16i + 4g + 3
             const f32x4 rt = *reinterpret_cast<const f32x4 *>(ga->rto + 16 * i + 4 * (lane >> 4));
             frag_from_acc16(E[i] * rt, fs16[i]);
         }
@@ -707,29 +795,28 @@ __device__ __forceinline__ void state_rest(const ChunkOperands<DT, DK, C, NW> &o
                 else mma_k16(acc, fe[s], fP[mt][s]);
             }
         // lane (g, r): token 16mt + r, value columns 4g .. 4g + 3
-        const f32x4 o4 = (KSC == KSD) ? Y[mt] : Y[mt] + PE;
+        f32x4 o4 = (KSC == KSD) ? Y[mt] : Y[mt] + PE;
+        if constexpr (L2) o4 *= nl->nq[16 * mt + (lane & 15)];
         if constexpr (sizeof(DT) == 2) store_out4(o4, out, 16 * mt * out.row_bytes);
         else store_out4_f32(o4, out, 16 * mt * out.row_bytes);
     }
 }
 
 // Both halves back to back (single-buffered kernel).
-template <typename DT, int DK, int C, int NW, bool GATED>
+template <typename DT, int DK, int C, int NW, bool GATED, bool L2>
 __device__ __forceinline__ void state_path(const DT *Ks, const DT *Qs, const DT *Vs,
                                            const DT *Ab, const DT *Tb, const DT *Ps,
-                                           const GateLds<C> *ga, f32x4 *Sacc,
-                                           const OutChunk &out, int wave, int lane) {
+                                           const GateLds<C> *ga, const NormLds<C> *nl,
+                                           f32x4 *Sacc, const OutChunk &out, int wave, int lane) {
     typedef ChunkCfg<DT, DK, C, NW> G;
     f32x4 X[G::NT], Y[G::NT];
     ChunkOperands<DT, DK, C, NW> op;
-    if constexpr (!GATED) op.load_v(Vs, wave, lane);
-    state_xy<DT, DK, C, NW, GATED>(Ks, Qs, Sacc, op.fv, X, Y, lane);
-    if constexpr (GATED) {
-        op.load_v(Vs, wave, lane);
-        gate_xy<DT, C, G::NT>(op.fv, ga->gam, X, Y, lane);
-    }
+    if constexpr (!GATED && !L2) op.load_v(Vs, wave, lane);
+    state_xy<DT, DK, C, NW, GATED, L2>(Ks, Qs, Sacc, op.fv, X, Y, lane);
+    if constexpr (GATED || L2) op.load_v(Vs, wave, lane);
+    if constexpr (GATED) gate_xy<DT, C, G::NT, !L2>(op.fv, ga->gam, X, Y, lane);
     op.load_kt(Ks, lane);
-    state_rest<DT, DK, C, NW, GATED>(op, Ab, Tb, Ps, ga, Sacc, X, Y, out, lane);
+    state_rest<DT, DK, C, NW, GATED, L2>(op, Ab, Tb, Ps, ga, nl, Sacc, X, Y, out, lane);
 }
 
 // Common per-workgroup addressing: (b, h, value tile) of this workgroup with
@@ -976,7 +1063,7 @@ __device__ __forceinline__ OutChunk out_chunk(const HeadPtrs<DT> &p, float scale
 // LDS of one workgroup: K, Q, V (this workgroup's value columns) and beta of
 // three chunks (one being consumed, two landing), and the per-chunk products
 // the preparation waves hand to the state waves for two chunks.
-template <typename DT, int DK, int C, int NW, bool GATED>
+template <typename DT, int DK, int C, int NW, bool GATED, bool L2>
 struct PipeSmem {
     typedef ChunkCfg<DT, DK, C, NW> G;
     typedef DmaStage<DT, DK, C, NW, 0> D;
@@ -989,11 +1076,12 @@ struct PipeSmem {
     DT Tb[2][G::NT * FRAG_ELEMS];            // -T_ii diag(beta_i) (fragment blocks)
     float betas[3][C];
     GateSets<C, 3, GATED> gate;              // decays of the chunk in each K, Q, V set
+    NormSets<C, 2, L2> norm;                 // 1/|k|, 1/|q| (L2), buffers like Ab, Tb, Ps
 };
 
-template <typename DT, int DK, int C, int NW, bool GATED>
+template <typename DT, int DK, int C, int NW, bool GATED, bool L2>
 constexpr bool ws_fits() {
-    return sizeof(PipeSmem<DT, DK, C, NW, GATED>) <= 160 * 1024;
+    return sizeof(PipeSmem<DT, DK, C, NW, GATED, L2>) <= 160 * 1024;
 }
 
 // Preparation wave W.  Chunk m's K, Q, V go to buffer set m % 3 by DMA issued
@@ -1002,8 +1090,8 @@ constexpr bool ws_fits() {
 // loads of chunk c+3 (into the set chunk c has just vacated), computes the
 // Gram tiles and diagonal inverses of chunk c+1, waits for the loads of chunk
 // c+2 and publishes them at the barrier.
-template <typename DT, int DK, int C, int NW, int W, bool GATED>
-__device__ __forceinline__ void prep_role(PipeSmem<DT, DK, C, NW, GATED> &sm,
+template <typename DT, int DK, int C, int NW, int W, bool GATED, bool L2>
+__device__ __forceinline__ void prep_role(PipeSmem<DT, DK, C, NW, GATED, L2> &sm,
                                           const HeadPtrs<DT> &p, int T, int N, int lane) {
     typedef ChunkCfg<DT, DK, C, NW> G;
     typedef DmaStage<DT, DK, C, NW, W, GATED> D;
@@ -1032,8 +1120,9 @@ __device__ __forceinline__ void prep_role(PipeSmem<DT, DK, C, NW, GATED> &sm,
     publish(0, t0s);
     lds_barrier();  // chunk 0 staged
     if (N > 0)
-        gram_tiles_w<DT, DK, C, NW, W, GATED>(sm.Ks[0], sm.Qs[0], sm.betas[0], bc_of(0), sm.Ab[0],
-                                              sm.Tb[0], sm.Ps[0], lane);
+        gram_tiles_w<DT, DK, C, NW, W, GATED, L2>(sm.Ks[0], sm.Qs[0], sm.betas[0], bc_of(0),
+                                                  sm.Ab[0], sm.Tb[0], sm.Ps[0], sm.norm.at(0),
+                                                  lane);
     wait_vmcnt<D::NVMEM>();  // chunk 1 landed
     publish(1, t1s);
     lds_barrier();  // Gram tiles of chunk 0 done, chunk 1 staged
@@ -1042,8 +1131,9 @@ __device__ __forceinline__ void prep_role(PipeSmem<DT, DK, C, NW, GATED> &sm,
         const int s0 = c % 3, s1 = (c + 1) % 3, s2 = (c + 2) % 3;
         dma.issue(p, T, c + 3, sm.Ks[s0], sm.Qs[s0], sm.Vs[s0], tnext, lane);
         if (c + 1 < N)
-            gram_tiles_w<DT, DK, C, NW, W, GATED>(sm.Ks[s1], sm.Qs[s1], sm.betas[s1], bc_of(s1),
-                                                  sm.Ab[b1p], sm.Tb[b1p], sm.Ps[b1p], lane);
+            gram_tiles_w<DT, DK, C, NW, W, GATED, L2>(sm.Ks[s1], sm.Qs[s1], sm.betas[s1],
+                                                      bc_of(s1), sm.Ab[b1p], sm.Tb[b1p],
+                                                      sm.Ps[b1p], sm.norm.at(b1p), lane);
         wait_vmcnt<D::NVMEM>();  // chunk c+2 landed
         publish(s2, tcur);
         lds_barrier();
@@ -1077,7 +1167,7 @@ __device__ __forceinline__ void prep_role(PipeSmem<DT, DK, C, NW, GATED> &sm,
 //
 // Gated rule (GATED, gl = log gates [B,T,H]): wave 0 of the preparation waves
 // also loads each chunk's gates and publishes their decays with its betas.
-template <typename DT, int DK, int C, int NW, bool GATED>
+template <typename DT, int DK, int C, int NW, bool GATED, bool L2>
 __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4 + 1, NW / 4 + 1))) void chunk_fwd_ws_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const float *__restrict__ gl, const float *S0,
@@ -1085,7 +1175,7 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4
     float scale) {
     typedef ChunkCfg<DT, DK, C, NW> G;
     constexpr int NT = G::NT, ND = G::ND;
-    __shared__ __attribute__((aligned(16))) PipeSmem<DT, DK, C, NW, GATED> sm;
+    __shared__ __attribute__((aligned(16))) PipeSmem<DT, DK, C, NW, GATED, L2> sm;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
@@ -1109,13 +1199,12 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4
         OutChunk out = out_chunk(p, scale, g, r);
         lds_barrier();  // chunk 0 staged
         // X, Y and the K^T operands of the chunk in set s
+        // (L2: V stays in op.fv for the block substitution of that chunk)
         auto xy = [&](int s) {
-            if constexpr (!GATED) op.load_v(sm.Vs[s], wave, lane);
-            state_xy<DT, DK, C, NW, GATED>(sm.Ks[s], sm.Qs[s], Sacc, op.fv, X, Y, lane);
-            if constexpr (GATED) {
-                op.load_v(sm.Vs[s], wave, lane);
-                gate_xy<DT, C, NT>(op.fv, sm.gate.at(s)->gam, X, Y, lane);
-            }
+            if constexpr (!GATED && !L2) op.load_v(sm.Vs[s], wave, lane);
+            state_xy<DT, DK, C, NW, GATED, L2>(sm.Ks[s], sm.Qs[s], Sacc, op.fv, X, Y, lane);
+            if constexpr (GATED || L2) op.load_v(sm.Vs[s], wave, lane);
+            if constexpr (GATED) gate_xy<DT, C, NT, !L2>(op.fv, sm.gate.at(s)->gam, X, Y, lane);
             op.load_kt(sm.Ks[s], lane);
         };
         if (N > 0) xy(0);
@@ -1128,8 +1217,8 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4
             const int t0 = c * C;
             const int len = min(C, p.T - t0);
             out.rsrc = make_rsrc(p.oh + (int64_t)t0 * p.tsv, len * out.row_bytes);
-            state_rest<DT, DK, C, NW, GATED>(op, sm.Ab[b], sm.Tb[b], sm.Ps[b], sm.gate.at(s0),
-                                             Sacc, X, Y, out, lane);
+            state_rest<DT, DK, C, NW, GATED, L2>(op, sm.Ab[b], sm.Tb[b], sm.Ps[b], sm.gate.at(s0),
+                                                 sm.norm.at(b), Sacc, X, Y, out, lane);
             // V first (X starts at -V); the K^T fragments of the next state
             // update only after X and Y have used their operands
             if (c + 1 < N) xy(s1);
@@ -1152,10 +1241,10 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4
             head_ptrs<DT, DK, NW>(q, k, v, beta, gl, o, cu, T, H, Dv, nvt, 0, r);
         const int N = (p.T + C - 1) / C;
         switch (wave - NW) {
-        case 0: prep_role<DT, DK, C, NW, 0, GATED>(sm, p, p.T, N, lane); break;
-        case 1: if constexpr (NW > 1) prep_role<DT, DK, C, NW, 1, GATED>(sm, p, p.T, N, lane); break;
-        case 2: if constexpr (NW > 2) prep_role<DT, DK, C, NW, 2, GATED>(sm, p, p.T, N, lane); break;
-        default: if constexpr (NW > 3) prep_role<DT, DK, C, NW, 3, GATED>(sm, p, p.T, N, lane); break;
+        case 0: prep_role<DT, DK, C, NW, 0, GATED, L2>(sm, p, p.T, N, lane); break;
+        case 1: if constexpr (NW > 1) prep_role<DT, DK, C, NW, 1, GATED, L2>(sm, p, p.T, N, lane); break;
+        case 2: if constexpr (NW > 2) prep_role<DT, DK, C, NW, 2, GATED, L2>(sm, p, p.T, N, lane); break;
+        default: if constexpr (NW > 3) prep_role<DT, DK, C, NW, 3, GATED, L2>(sm, p, p.T, N, lane); break;
         }
     }
 }
@@ -1163,7 +1252,7 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4
 // ---------------------------------------------------------------------------
 // Serial kernel (single-buffered; for shapes whose double buffers do not fit)
 // ---------------------------------------------------------------------------
-template <typename DT, int DK, int C, int NW, bool GATED>
+template <typename DT, int DK, int C, int NW, bool GATED, bool L2>
 struct SerialSmem {
     typedef ChunkCfg<DT, DK, C, NW> G;
     static constexpr int NOFF = G::NT * (G::NT - 1) / 2;
@@ -1175,9 +1264,10 @@ struct SerialSmem {
     DT Tb[G::NT * FRAG_ELEMS];
     float betas[C];
     GateSets<C, 1, GATED> gate;
+    NormSets<C, 1, L2> norm;
 };
 
-template <typename DT, int DK, int C, int NW, bool GATED>
+template <typename DT, int DK, int C, int NW, bool GATED, bool L2>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_fwd_serial_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const float *__restrict__ gl, const float *S0,
@@ -1185,7 +1275,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     float scale) {
     typedef ChunkCfg<DT, DK, C, NW> G;
     constexpr int ND = G::ND;
-    __shared__ __attribute__((aligned(16))) SerialSmem<DT, DK, C, NW, GATED> sm;
+    __shared__ __attribute__((aligned(16))) SerialSmem<DT, DK, C, NW, GATED, L2> sm;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
@@ -1218,12 +1308,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
             rg.load(p, p.T, min(c + 1, N - 1) * C);
             const float *bc = nullptr;
             if constexpr (GATED) bc = sm.gate.at(0)->bc;
-            gram_tiles<DT, DK, C, NW, GATED>(sm.Ks, sm.Qs, sm.betas, bc, sm.Ab, sm.Tb, sm.Ps, wave,
-                                             lane);
+            gram_tiles<DT, DK, C, NW, GATED, L2>(sm.Ks, sm.Qs, sm.betas, bc, sm.Ab, sm.Tb, sm.Ps,
+                                                 sm.norm.at(0), wave, lane);
             lds_barrier();
             out.rsrc = make_rsrc(p.oh + (int64_t)t0 * p.tsv, len * out.row_bytes);
-            state_path<DT, DK, C, NW, GATED>(sm.Ks, sm.Qs, sm.Vs, sm.Ab, sm.Tb, sm.Ps,
-                                             sm.gate.at(0), Sacc, out, wave, lane);
+            state_path<DT, DK, C, NW, GATED, L2>(sm.Ks, sm.Qs, sm.Vs, sm.Ab, sm.Tb, sm.Ps,
+                                                 sm.gate.at(0), sm.norm.at(0), Sacc, out, wave,
+                                                 lane);
         }
     }
     if (S_T) {
@@ -1238,19 +1329,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 // ---------------------------------------------------------------------------
 // B in ChunkFwdArgs counts sequences (batch rows, or packed sequences when
 // cu is set); T is the token axis of each batch row.
-template <typename DT, int DK, int C, int NW, bool GATED>
+template <typename DT, int DK, int C, int NW, bool GATED, bool L2>
 hipError_t launch_cfg(const ChunkFwdArgs &a, hipStream_t stream) {
     const int nvt = a.Dv / (16 * NW);
     const int64_t grid = a.B * a.H * nvt;
     const DT *q = static_cast<const DT *>(a.q), *k = static_cast<const DT *>(a.k);
     const DT *v = static_cast<const DT *>(a.v), *beta = static_cast<const DT *>(a.beta);
     DT *o = static_cast<DT *>(a.o);
-    if constexpr (ws_fits<DT, DK, C, NW, GATED>()) {
-        hipLaunchKernelGGL((chunk_fwd_ws_kernel<DT, DK, C, NW, GATED>), dim3((unsigned)grid),
+    if constexpr (ws_fits<DT, DK, C, NW, GATED, L2>()) {
+        hipLaunchKernelGGL((chunk_fwd_ws_kernel<DT, DK, C, NW, GATED, L2>), dim3((unsigned)grid),
                            dim3(128 * NW), 0, stream, q, k, v, beta, a.g, a.S0, o, a.S_T, a.cu,
                            (int)a.T, (int)a.H, a.Dv, nvt, a.scale);
     } else {
-        hipLaunchKernelGGL((chunk_fwd_serial_kernel<DT, DK, C, NW, GATED>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((chunk_fwd_serial_kernel<DT, DK, C, NW, GATED, L2>), dim3((unsigned)grid),
                            dim3(64 * NW), 0, stream, q, k, v, beta, a.g, a.S0, o, a.S_T, a.cu,
                            (int)a.T, (int)a.H, a.Dv, nvt, a.scale);
     }
@@ -1267,45 +1358,48 @@ inline int pick_waves(int64_t /*BH*/, int Dv) {
     return 1;
 }
 
-template <typename DT, int DK, int C, bool GATED>
+template <typename DT, int DK, int C, bool GATED, bool L2>
 hipError_t dispatch_nw(const ChunkFwdArgs &a, hipStream_t stream) {
     switch (pick_waves(a.B * a.H, a.Dv)) {
-    case 4: return launch_cfg<DT, DK, C, 4, GATED>(a, stream);
-    case 2: return launch_cfg<DT, DK, C, 2, GATED>(a, stream);
-    default: return launch_cfg<DT, DK, C, 1, GATED>(a, stream);
+    case 4: return launch_cfg<DT, DK, C, 4, GATED, L2>(a, stream);
+    case 2: return launch_cfg<DT, DK, C, 2, GATED, L2>(a, stream);
+    default: return launch_cfg<DT, DK, C, 1, GATED, L2>(a, stream);
     }
 }
 
-template <typename DT, int DK, bool GATED>
+template <typename DT, int DK, bool GATED, bool L2>
 hipError_t dispatch_c(const ChunkFwdArgs &a, hipStream_t stream) {
     switch (a.chunk) {
-    case 16: return dispatch_nw<DT, DK, 16, GATED>(a, stream);
-    case 32: return dispatch_nw<DT, DK, 32, GATED>(a, stream);
-    case 64: return dispatch_nw<DT, DK, 64, GATED>(a, stream);
+    case 16: return dispatch_nw<DT, DK, 16, GATED, L2>(a, stream);
+    case 32: return dispatch_nw<DT, DK, 32, GATED, L2>(a, stream);
+    case 64: return dispatch_nw<DT, DK, 64, GATED, L2>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <typename DT, bool GATED>
+template <typename DT, bool GATED, bool L2>
 hipError_t dispatch_dk(const ChunkFwdArgs &a, hipStream_t stream) {
     switch (a.Dk) {
-    case 16: return dispatch_c<DT, 16, GATED>(a, stream);
-    case 32: return dispatch_c<DT, 32, GATED>(a, stream);
-    case 64: return dispatch_c<DT, 64, GATED>(a, stream);
-    case 128: return dispatch_c<DT, 128, GATED>(a, stream);
+    case 16: return dispatch_c<DT, 16, GATED, L2>(a, stream);
+    case 32: return dispatch_c<DT, 32, GATED, L2>(a, stream);
+    case 64: return dispatch_c<DT, 64, GATED, L2>(a, stream);
+    case 128: return dispatch_c<DT, 128, GATED, L2>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
 // Every kernel of one rule (plain or gated), both dtypes.
-template <bool GATED>
+template <bool GATED, bool L2>
 hipError_t launch_rule(const ChunkFwdArgs &a, bool bf16, hipStream_t stream) {
-    return bf16 ? dispatch_dk<__bf16, GATED>(a, stream) : dispatch_dk<float, GATED>(a, stream);
+    return bf16 ? dispatch_dk<__bf16, GATED, L2>(a, stream) : dispatch_dk<float, GATED, L2>(a, stream);
 }
 
 }  // namespace
 
-// The gated instantiations live in their own translation unit.
+// The gated and the L2-normalising instantiations live in translation units
+// of their own.
 hipError_t launch_chunk_fwd_gated(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
+hipError_t launch_chunk_fwd_l2(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
+hipError_t launch_chunk_fwd_gated_l2(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
 
 }  // namespace dr

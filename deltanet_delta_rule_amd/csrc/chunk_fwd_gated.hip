@@ -5,7 +5,7 @@
 namespace dr {
 
 hipError_t launch_chunk_fwd_gated(const ChunkFwdArgs &a, bool bf16, hipStream_t stream) {
-    return launch_rule<true>(a, bf16, stream);
+    return launch_rule<true, false>(a, bf16, stream);
 }
 
 }  // namespace dr

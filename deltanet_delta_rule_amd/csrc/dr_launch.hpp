@@ -12,7 +12,7 @@ namespace dr {
 // head, value tile)).  g is the log forget gate [B,T,H] (fp32) of the gated
 // rule, or nullptr.  cu, when set, holds B+1 sequence offsets into the single
 // batch row of T tokens (packed variable-length input); scale multiplies the
-// outputs.
+// outputs; l2 normalises the rows of q and k inside the kernel.
 struct ChunkFwdArgs {
     const void *q, *k, *v, *beta;
     const float *g, *S0;
@@ -22,6 +22,7 @@ struct ChunkFwdArgs {
     int64_t B, T, H;
     int Dk, Dv, chunk;
     float scale;
+    bool l2;
 };
 
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);

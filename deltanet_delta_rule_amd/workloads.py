@@ -7,8 +7,9 @@ oracle can be fed from it.  Every tensor is drawn in fp32 on the CPU from a
 
 * draw order: q_raw, k_raw, v, beta_raw, S0 (all standard normal);
 * q, k: L2-normalised along the head dimension (x / max(||x||, 1e-12)),
-  after a SiLU for the small-model workload; the operator itself never
-  normalises (the DeltaNet layer feeds it SiLU + L2-normalised keys and
+  after a SiLU for the small-model workload, or left raw (feature "raw") for
+  the tests of the kernel's own normalisation option; by default the operator
+  does not normalise (the DeltaNet layer feeds it SiLU + L2-normalised keys and
   queries: "Parallelizing Linear Transformers with the Delta Rule over Sequence
   Length", section 3 "DeltaNet transformer");
 * v: standard normal;
@@ -97,6 +98,8 @@ WORKLOADS = {
 
 
 def _features(x: torch.Tensor, feature: str) -> torch.Tensor:
+    if feature == "raw":
+        return x  # left for the kernel's own normalisation option
     if feature == "silu_l2":
         x = x * torch.sigmoid(x)
     elif feature != "l2":

@@ -109,6 +109,15 @@ dr_status delta_rule_chunk_fwd(const void *q, const void *k, const void *v,
                                int64_t Dk, int64_t Dv, int64_t chunk,
                                dr_dtype dtype, void *stream);
 
+/* Flags of dr_chunk_opts. */
+enum {
+    /* L2-normalise every token row of q and k inside the kernel:
+     * x / sqrt(sum x^2 + 1e-6) (the l2norm of the gated layer on houmin.site
+     * "infra/delta-net"; fla's use_qk_l2norm_in_kernel).  q and k are read as
+     * given and never written. */
+    DR_QK_L2NORM = 1u
+};
+
 /*
  * Options of delta_rule_chunk_fwd_ex (zero-initialise, then set scale = 1).
  *
@@ -130,7 +139,7 @@ dr_status delta_rule_chunk_fwd(const void *q, const void *k, const void *v,
  *   scale       finite output scale: o = scale * S_t q_t (the same as
  *               scaling q; the DeltaNet layer passes none, the gated layer
  *               of houmin.site "infra/delta-net" divides q by sqrt(d_k)).
- *   flags       must be 0.
+ *   flags       0 or DR_QK_L2NORM.
  */
 typedef struct dr_chunk_opts {
     const float *g;
@@ -146,7 +155,7 @@ typedef struct dr_chunk_opts {
  * argument, size, layout and error behaves as in delta_rule_chunk_fwd; in
  * addition DR_ERR_INVALID_ARG is returned for cu_seqlens with B != 1, a
  * negative num_seqs, a misaligned cu_seqlens, cu_seqlens overlapping an
- * output, a non-finite scale or unknown flags.
+ * output, a non-finite scale or unknown flag bits.
  */
 dr_status delta_rule_chunk_fwd_ex(const void *q, const void *k, const void *v,
                                   const void *beta, const float *S0, void *o, float *S_T,
@@ -227,7 +236,7 @@ const char *delta_rule_status_string(dr_status status);
 int delta_rule_last_hip_error(void);
 
 /* Library version as major*10000 + minor*100 + patch (2.0.0: the gated
- * entry points; 2.1.0: delta_rule_chunk_fwd_ex). */
+ * entry points; 2.1.0: delta_rule_chunk_fwd_ex; 2.2.0: DR_QK_L2NORM). */
 int delta_rule_version(void);
 
 #ifdef __cplusplus

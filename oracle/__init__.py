@@ -15,14 +15,17 @@ Contents
 ``gated_delta_rule_ref``
     The same loop with a scalar forget gate alpha_t = exp(g_t) applied to the
     whole state before each token's prediction (the gated variant).
+``l2norm_rows``
+    x / sqrt(sum x^2 + eps) along the last axis in fp64: the in-kernel
+    normalisation option applied to q and k before either oracle.
 ``chunk_algebra``
     The chunkwise-parallel rearrangement of the same recurrence in fp64 NumPy,
     step by step as the pages state it.  It is used only to pin the oracle and
     the algebra the GPU kernels rely on; GPU parity is always judged against
     ``delta_rule_ref``.
 
-Parity status: every function here is pinned by ``tests/test_oracle.py`` and
-``tests/test_chunk_algebra.py`` (equivalent update forms, closed forms,
+Parity status: every function here is pinned by ``tests/test_oracle.py``,
+``tests/test_gated_oracle.py`` and ``tests/test_chunk_algebra.py`` (equivalent update forms, closed forms,
 special cases, an exact-rational brute force and a hand-worked example).
 """
 from __future__ import annotations
@@ -142,4 +145,13 @@ def gated_delta_rule_ref(q, k, v, beta, g, S0=None, nthreads: int = 1):
     return o, st
 
 
-__all__ = ["build", "delta_rule_ref", "gated_delta_rule_ref"]
+def l2norm_rows(x, eps: float = 1e-6):
+    """Each row (last axis) of x divided by sqrt(sum of its squares + eps),
+    in fp64: the l2norm helper of the gated layer on houmin.site
+    ("infra/delta-net", section "Gated DeltaNet", code), which the DeltaNet
+    layer applies to q and k (fla/layers/delta_net.py, the l2 norm option)."""
+    x = _as_f64(x)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+__all__ = ["build", "delta_rule_ref", "gated_delta_rule_ref", "l2norm_rows"]

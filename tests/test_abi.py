@@ -231,7 +231,8 @@ def test_chunk_options_struct_layout():
     (dict(cu_seqlens=CU.value, num_seqs=2), dict(S_T=CU)),       # S_T overlaps offsets
     (dict(scale=float("nan")), {}),
     (dict(scale=float("inf")), {}),
-    (dict(flags=1), {}),                                         # no flags are defined
+    (dict(flags=2), {}),                                         # unknown flag bit
+    (dict(flags=0x80000001), {}),
     (dict(g=ODD.value), {}),                                     # gate misaligned
     (dict(g=P[4].value), {}),                                    # gate overlaps o
 ])

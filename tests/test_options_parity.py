@@ -127,3 +127,75 @@ def test_output_scale(gated, dtype):
     assert rel_err(to_np(o_s), scale * o_ref) <= tol
     # the scale is applied in fp32 before the output is rounded
     assert rel_err(to_np(o_s), scale * to_np(o_1)) <= (1e-6 if dtype == "f32" else 8e-3)
+
+
+# ------------------------------------------------ in-kernel q/k L2 norm
+def _l2_inputs(x):
+    from oracle import l2norm_rows
+    xs = dict(x)
+    xs["q"] = torch.from_numpy(l2norm_rows(x["q"]))
+    xs["k"] = torch.from_numpy(l2norm_rows(x["k"]))
+    return xs
+
+
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("dtype,Dk,Dv,chunk", [("bf16", 128, 128, 64), ("f32", 128, 64, 64),
+                                               ("f32", 16, 32, 16), ("bf16", 32, 128, 32),
+                                               ("bf16", 64, 64, 64)])
+def test_l2norm_in_kernel_matches_oracle(gated, dtype, Dk, Dv, chunk):
+    w = W.get("long_prefill", B=2, H=2, T=3 * chunk - 7, Dk=Dk, Dv=Dv, chunk=chunk, dtype=dtype,
+              feature="raw", gate_amax=0.5 if gated else 0.0, seed=6100 + Dk + Dv + chunk)
+    x = W.generate(w)
+    d = to_dev(x)
+    o, st = _call(d, gated, d["S0"], chunk=chunk, use_qk_l2norm_in_kernel=True)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_all(_l2_inputs(x))
+    tol = TOL[w.torch_dtype]
+    eo, es = rel_err(to_np(o), o_ref), rel_err(to_np(st), s_ref)
+    print(f"l2norm gated={gated} {dtype} Dk{Dk} Dv{Dv} C{chunk}: o {eo:.2e} S_T {es:.2e}",
+          flush=True)
+    assert eo <= tol and es <= tol
+
+
+def test_l2norm_full_layer_sampled_heads():
+    from tests.parity_utils import gather_heads, oracle_heads
+    w = W.get("layer_1p3b", feature="raw")
+    x = W.generate(w)
+    d = to_dev(x)
+    o, st = dr.delta_rule_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], None,
+                                    use_qk_l2norm_in_kernel=True)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (3, 9), (7, 15)]
+    o_ref, s_ref = oracle_heads(_l2_inputs(x), heads)
+    o_got, s_got = gather_heads(o, st, heads)
+    assert rel_err(o_got, o_ref) <= 2e-2 and rel_err(s_got, s_ref) <= 2e-2
+
+
+def test_l2norm_zero_rows_and_packed_sequences():
+    # zero q / k rows normalise to zero (nothing written, nothing read), and
+    # packed sequences still equal separate calls bit for bit
+    lengths = [70, 0, 129, 5]
+    w, x, S0, cu = _packed(lengths, True, "bf16")
+    x = dict(x)
+    x["q"] = 3.0 * x["q"].float()
+    x["k"] = 3.0 * x["k"].float()
+    x["k"][:, 10] = 0
+    x["q"][:, 11] = 0
+    x["q"], x["k"] = x["q"].to(torch.bfloat16), x["k"].to(torch.bfloat16)
+    d = to_dev(x)
+    S0d, cud = S0.cuda(), cu.cuda()
+    o, st = _call(d, True, S0d, cu_seqlens=cud, use_qk_l2norm_in_kernel=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(o[:, 11]) == 0
+    for s in range(len(lengths)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        sl = {n: (None if t is None else t[:, a:b].contiguous()) for n, t in d.items()}
+        o1, st1 = _call(sl, True, S0d[s:s + 1].contiguous(), use_qk_l2norm_in_kernel=True)
+        assert torch.equal(o[:, a:b], o1) and torch.equal(st[s:s + 1], st1)
+        if b > a:
+            xs = _l2_inputs({n: (None if t is None else t[:, a:b].contiguous())
+                             for n, t in x.items()})
+            xs["S0"] = S0[s:s + 1]
+            o_ref, s_ref = oracle_all(xs)
+            assert rel_err(to_np(o[:, a:b]), o_ref) <= 2e-2
+            assert rel_err(to_np(st[s:s + 1]), s_ref) <= 2e-2

@@ -385,3 +385,27 @@ def test_rejects_bad_shapes():
         delta_rule_ref(q, k[:, :-1], v, beta, S0)
     with pytest.raises(ValueError):
         delta_rule_ref(q, k, v, beta, S0[:, :, :-1])
+
+
+# ----------------------------------------------------------------- l2norm
+# houmin.site "infra/delta-net", Gated DeltaNet code: the l2norm helper
+# multiplies a row by 1/sqrt(sum of squares + 1e-6).
+def test_l2norm_rows_hand_values():
+    from oracle import l2norm_rows
+    x = np.array([[3.0, 4.0], [0.0, 0.0], [1e-4, 0.0]])
+    y = l2norm_rows(x)
+    assert np.allclose(y[0], np.array([3.0, 4.0]) / np.sqrt(25.0 + 1e-6), rtol=0, atol=1e-16)
+    assert np.array_equal(y[1], np.zeros(2))          # a zero row stays zero
+    # eps dominates tiny rows: 1e-4 / sqrt(1e-8 + 1e-6)
+    assert abs(y[2, 0] - 1e-4 / np.sqrt(1.01e-6)) < 1e-15
+
+
+def test_l2norm_rows_gives_unit_rows_and_keeps_direction():
+    from oracle import l2norm_rows
+    r = np.random.default_rng(11)
+    x = 3.0 * r.standard_normal((4, 5, 7))
+    y = l2norm_rows(x)
+    n2 = np.sum(x * x, axis=-1)
+    assert np.allclose(np.sum(y * y, axis=-1), n2 / (n2 + 1e-6), rtol=1e-14, atol=0)
+    cos = np.sum(x * y, axis=-1) / np.sqrt(n2 * np.sum(y * y, axis=-1))
+    assert np.allclose(cos, 1.0, rtol=0, atol=1e-14)
