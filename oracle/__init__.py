@@ -15,6 +15,10 @@ Contents
 ``gated_delta_rule_ref``
     The same loop with a scalar forget gate alpha_t = exp(g_t) applied to the
     whole state before each token's prediction (the gated variant).
+``delta_rule_bwd_ref``
+    Gradients with respect to q, k, v, beta, S0 (and g for the gated rule)
+    by the chain rule through the recurrence in reverse token order, in fp64
+    (C, ``ref_delta_rule_bwd.c``).
 ``l2norm_rows``
     x / sqrt(sum x^2 + eps) along the last axis in fp64: the in-kernel
     normalisation option applied to q and k before either oracle.
@@ -37,7 +41,7 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "ref_delta_rule.c")
+_SRC = [os.path.join(_HERE, "ref_delta_rule.c"), os.path.join(_HERE, "ref_delta_rule_bwd.c")]
 _LIB_PATH = os.path.join(_HERE, "libref_delta_rule.so")
 _lib = None
 
@@ -46,7 +50,7 @@ def build(verbose: bool = False) -> str:
     """Compile the C oracle with gcc (fp64, no FMA contraction) in place."""
     cmd = [
         "gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
-        "-shared", "-fPIC", "-pthread", _SRC, "-o", _LIB_PATH + ".tmp",
+        "-shared", "-fPIC", "-pthread", *_SRC, "-lm", "-o", _LIB_PATH + ".tmp",
     ]
     if verbose:
         print(" ".join(cmd))
@@ -67,6 +71,8 @@ def _load():
     lib.ref_delta_rule_f64.restype = ctypes.c_int
     lib.ref_delta_rule_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp,
                                        i64, i64, i64, i64, i64, ctypes.c_int]
+    lib.ref_delta_rule_bwd_f64.restype = ctypes.c_int
+    lib.ref_delta_rule_bwd_f64.argtypes = [dp] * 14 + [i64, i64, i64, i64, i64, ctypes.c_int]
     lib.ref_gated_delta_rule_f64.restype = ctypes.c_int
     lib.ref_gated_delta_rule_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp,
                                              i64, i64, i64, i64, i64, ctypes.c_int]
@@ -145,6 +151,41 @@ def gated_delta_rule_ref(q, k, v, beta, g, S0=None, nthreads: int = 1):
     return o, st
 
 
+def delta_rule_bwd_ref(q, k, v, beta, do, S0=None, dS_T=None, g=None, nthreads: int = 1):
+    """Gradients of L = sum <do, o> + <dS_T, S_T> through the recurrence in
+    fp64 on the CPU (``ref_delta_rule_bwd.c``: the chain rule through each
+    token in reverse order, with the forward states kept).  g (log forget
+    gate, [B,T,H]) selects the gated rule.  do is ``[B,T,H,Dv]``; dS_T is
+    ``[B,H,Dv,Dk]`` or None (zero).  Returns a dict with dq, dk, dv, dbeta,
+    dS0 and, for the gated rule, dg."""
+    q, k, v, beta, s0, (B, T, H, Dk, Dv) = _check(q, k, v, beta, S0)
+    do = _as_f64(do)
+    if do.shape != (B, T, H, Dv):
+        raise ValueError(f"do must be [B,T,H,Dv]={B, T, H, Dv}, got {do.shape}")
+    dst = None
+    if dS_T is not None:
+        dst = _as_f64(dS_T)
+        if dst.shape != (B, H, Dv, Dk):
+            raise ValueError(f"dS_T must be [B,H,Dv,Dk]={B, H, Dv, Dk}, got {dst.shape}")
+    gg = None
+    if g is not None:
+        gg = _as_f64(g)
+        if gg.shape != (B, T, H):
+            raise ValueError(f"g must be [B,T,H]={B, T, H}, got {gg.shape}")
+    out = {"dq": np.zeros((B, T, H, Dk)), "dk": np.zeros((B, T, H, Dk)),
+           "dv": np.zeros((B, T, H, Dv)), "dbeta": np.zeros((B, T, H)),
+           "dS0": np.zeros((B, H, Dv, Dk))}
+    if gg is not None:
+        out["dg"] = np.zeros((B, T, H))
+    rc = _load().ref_delta_rule_bwd_f64(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gg), _ptr(s0), _ptr(do), _ptr(dst),
+        _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
+        _ptr(out.get("dg")), _ptr(out["dS0"]), B, T, H, Dk, Dv, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle failed with code {rc}")
+    return out
+
+
 def l2norm_rows(x, eps: float = 1e-6):
     """Each row (last axis) of x divided by sqrt(sum of its squares + eps),
     in fp64: the l2norm helper of the gated layer on houmin.site
@@ -154,4 +195,5 @@ def l2norm_rows(x, eps: float = 1e-6):
     return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
 
 
-__all__ = ["build", "delta_rule_ref", "gated_delta_rule_ref", "l2norm_rows"]
+__all__ = ["build", "delta_rule_ref", "gated_delta_rule_ref", "delta_rule_bwd_ref",
+           "l2norm_rows"]
