@@ -52,6 +52,11 @@ class dr_chunk_opts(ctypes.Structure):
                 ("flags", ctypes.c_uint32)]
 
 
+class dr_step_opts(ctypes.Structure):
+    """``dr_step_opts`` of include/deltarule.h."""
+    _fields_ = [("g", ctypes.c_void_p), ("scale", ctypes.c_float), ("flags", ctypes.c_uint32)]
+
+
 class DeltaRuleError(RuntimeError):
     """A HIP runtime failure reported by libdeltarule."""
 
@@ -80,6 +85,9 @@ def load_library():
     lib.gated_delta_rule_chunk_fwd.restype = i32
     lib.gated_delta_rule_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                                                i64, i64, i64, i64, i64, i64, i32, vp]
+    lib.delta_rule_recurrent_step_ex.restype = i32
+    lib.delta_rule_recurrent_step_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                                 ctypes.POINTER(dr_step_opts), i32, vp]
     lib.gated_delta_rule_recurrent_step.restype = i32
     lib.gated_delta_rule_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp,
                                                     i64, i64, i64, i64, i32, vp]
@@ -239,7 +247,7 @@ def gated_delta_rule_chunk_fwd(q, k, v, beta, g, S0=None, *, chunk: int = 64,
                        scale, cu_seqlens, use_qk_l2norm_in_kernel)
 
 
-def _step_call(entry, q, k, v, beta, g, S, o, stream):
+def _step_call(gated, q, k, v, beta, g, S, o, stream, scale=None, l2norm=False):
     torch = _torch()
     dev = q.device
     if dev.type != "cuda":
@@ -252,29 +260,43 @@ def _step_call(entry, q, k, v, beta, g, S, o, stream):
     _need(k, "k", (B, H, Dk), dt, dev)
     _need(v, "v", (B, H, Dv), dt, dev)
     _need(beta, "beta", (B, H), dt, dev)
-    if g is not None:
+    if gated:
         _need(g, "g", (B, H), torch.float32, dev)
     _need(S, "S", (B, H, Dv, Dk), torch.float32, dev)
     if o is None:
         o = torch.empty((B, H, Dv), dtype=dt, device=dev)
     else:
         _need(o, "o", (B, H, Dv), dt, dev)
-    ptrs = [_ptr(q), _ptr(k), _ptr(v), _ptr(beta)]
-    if entry == "gated_delta_rule_recurrent_step":
-        ptrs.append(_ptr(g))
-    st = getattr(load_library(), entry)(
-        *ptrs, _ptr(S), _ptr(o), B, H, Dk, Dv, _dtype_code(q), _stream(dev, stream))
+    lib = load_library()
+    common = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta))
+    if scale is None and not l2norm:
+        if gated:
+            st = lib.gated_delta_rule_recurrent_step(*common, _ptr(g), _ptr(S), _ptr(o), B, H,
+                                                     Dk, Dv, _dtype_code(q), _stream(dev, stream))
+        else:
+            st = lib.delta_rule_recurrent_step(*common, _ptr(S), _ptr(o), B, H, Dk, Dv,
+                                               _dtype_code(q), _stream(dev, stream))
+    else:
+        opts = dr_step_opts(g=g.data_ptr() if gated else None,
+                            scale=1.0 if scale is None else float(scale),
+                            flags=DR_QK_L2NORM if l2norm else 0)
+        st = lib.delta_rule_recurrent_step_ex(*common, _ptr(S), _ptr(o), B, H, Dk, Dv,
+                                              ctypes.byref(opts), _dtype_code(q),
+                                              _stream(dev, stream))
     _check(st)
     return o
 
 
-def delta_rule_recurrent_step(q, k, v, beta, S, *, o=None, stream=None):
+def delta_rule_recurrent_step(q, k, v, beta, S, *, o=None, scale=None,
+                              use_qk_l2norm_in_kernel=False, stream=None):
     """One decode token: q, k ``[B,H,Dk]``; v ``[B,H,Dv]``; beta ``[B,H]``;
-    S ``[B,H,Dv,Dk]`` float32, updated in place.  Returns o ``[B,H,Dv]``."""
-    return _step_call("delta_rule_recurrent_step", q, k, v, beta, None, S, o, stream)
+    S ``[B,H,Dv,Dk]`` float32, updated in place.  Returns o ``[B,H,Dv]``.
+    ``scale`` and ``use_qk_l2norm_in_kernel`` as in the chunked forward."""
+    return _step_call(False, q, k, v, beta, None, S, o, stream, scale, use_qk_l2norm_in_kernel)
 
 
-def gated_delta_rule_recurrent_step(q, k, v, beta, g, S, *, o=None, stream=None):
+def gated_delta_rule_recurrent_step(q, k, v, beta, g, S, *, o=None, scale=None,
+                                    use_qk_l2norm_in_kernel=False, stream=None):
     """One decode token of the gated rule: as ``delta_rule_recurrent_step``
     plus g ``[B,H]`` float32, the log forget gate of this token."""
-    return _step_call("gated_delta_rule_recurrent_step", q, k, v, beta, g, S, o, stream)
+    return _step_call(True, q, k, v, beta, g, S, o, stream, scale, use_qk_l2norm_in_kernel)

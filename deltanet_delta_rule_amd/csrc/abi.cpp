@@ -110,9 +110,11 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
 // Shared validation and dispatch of the decode step; g (fp32 [B,H]) as above.
 dr_status recurrent_step(const void *q, const void *k, const void *v, const void *beta,
                          const float *g, bool gated, float *S, void *o, int64_t B, int64_t H,
-                         int64_t Dk, int64_t Dv, dr_dtype dtype, void *stream) {
+                         int64_t Dk, int64_t Dv, float scale, bool l2, dr_dtype dtype,
+                         void *stream) {
     if (dtype != DR_F32 && dtype != DR_BF16) return DR_ERR_INVALID_ARG;
     if (B < 0 || H < 0 || Dk < 0 || Dv < 0) return DR_ERR_INVALID_ARG;
+    if (!(scale == scale) || scale - scale != 0.f) return DR_ERR_INVALID_ARG;  // NaN or inf
     if (!supported_dim(Dk) || !supported_dim(Dv)) return DR_ERR_UNSUPPORTED;
     if (B == 0 || H == 0) return DR_OK;
 
@@ -135,9 +137,10 @@ dr_status recurrent_step(const void *q, const void *k, const void *v, const void
     for (const Span &s : in)
         if (overlaps(so, s) || overlaps(ss, s)) return DR_ERR_INVALID_ARG;
 
-    return hip_status(dr::launch_recurrent_step(q, k, v, beta, gated ? g : nullptr, S, o, bh,
-                                                (int)Dk, (int)Dv, dtype == DR_BF16,
-                                                static_cast<hipStream_t>(stream)));
+    const dr::StepArgs a{q, k, v, beta, gated ? g : nullptr, S, o, bh, (int)Dk, (int)Dv, scale,
+                         l2};
+    return hip_status(
+        dr::launch_recurrent_step(a, dtype == DR_BF16, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -171,7 +174,8 @@ dr_status delta_rule_recurrent_step(const void *q, const void *k,
                                     const void *v, const void *beta, float *S,
                                     void *o, int64_t B, int64_t H, int64_t Dk,
                                     int64_t Dv, dr_dtype dtype, void *stream) {
-    return recurrent_step(q, k, v, beta, nullptr, false, S, o, B, H, Dk, Dv, dtype, stream);
+    return recurrent_step(q, k, v, beta, nullptr, false, S, o, B, H, Dk, Dv, 1.f, false, dtype,
+                          stream);
 }
 
 dr_status gated_delta_rule_chunk_fwd(const void *q, const void *k, const void *v,
@@ -187,7 +191,19 @@ dr_status gated_delta_rule_recurrent_step(const void *q, const void *k, const vo
                                           const void *beta, const float *g, float *S, void *o,
                                           int64_t B, int64_t H, int64_t Dk, int64_t Dv,
                                           dr_dtype dtype, void *stream) {
-    return recurrent_step(q, k, v, beta, g, true, S, o, B, H, Dk, Dv, dtype, stream);
+    return recurrent_step(q, k, v, beta, g, true, S, o, B, H, Dk, Dv, 1.f, false, dtype, stream);
+}
+
+dr_status delta_rule_recurrent_step_ex(const void *q, const void *k, const void *v,
+                                       const void *beta, float *S, void *o, int64_t B,
+                                       int64_t H, int64_t Dk, int64_t Dv,
+                                       const dr_step_opts *opts, dr_dtype dtype, void *stream) {
+    dr_step_opts d{};
+    d.scale = 1.f;
+    const dr_step_opts &x = opts ? *opts : d;
+    if (x.flags & ~uint32_t(DR_QK_L2NORM)) return DR_ERR_INVALID_ARG;  // unknown flags
+    return recurrent_step(q, k, v, beta, x.g, x.g != nullptr, S, o, B, H, Dk, Dv, x.scale,
+                          (x.flags & DR_QK_L2NORM) != 0, dtype, stream);
 }
 
 const char *delta_rule_status_string(dr_status status) {
@@ -202,6 +218,6 @@ const char *delta_rule_status_string(dr_status status) {
 
 int delta_rule_last_hip_error(void) { return g_last_hip_error; }
 
-int delta_rule_version(void) { return 20200; }
+int delta_rule_version(void) { return 20300; }
 
 }  // extern "C"

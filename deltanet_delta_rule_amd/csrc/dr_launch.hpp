@@ -27,10 +27,20 @@ struct ChunkFwdArgs {
 
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
 
-// Single-token decode step, state updated in place.  g is the log forget gate
-// [B,H] (fp32) of the gated rule, or nullptr.
-hipError_t launch_recurrent_step(const void *q, const void *k, const void *v,
-                                 const void *beta, const float *g, float *S, void *o,
-                                 int64_t BH, int Dk, int Dv, bool bf16, hipStream_t stream);
+// Arguments of the single-token decode step (state updated in place).  g is
+// the log forget gate [B,H] (fp32) of the gated rule, or nullptr; scale
+// multiplies the outputs; l2 normalises q and k in the kernel.
+struct StepArgs {
+    const void *q, *k, *v, *beta;
+    const float *g;
+    float *S;
+    void *o;
+    int64_t BH;
+    int Dk, Dv;
+    float scale;
+    bool l2;
+};
+
+hipError_t launch_recurrent_step(const StepArgs &a, bool bf16, hipStream_t stream);
 
 }  // namespace dr

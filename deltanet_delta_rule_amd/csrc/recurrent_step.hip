@@ -44,11 +44,15 @@ __device__ __forceinline__ float row_sum(float x) {
 
 // GATED: the whole row first decays by alpha = exp(g) of its (b, h), then the
 // token is predicted from the decayed row (forget before predict).
-template <typename DT, int DK, int PASSES, bool GATED>
+// L2: q and k are divided by sqrt(|x|^2 + 1e-6) first (the l2norm of the
+// gated layer on houmin.site "infra/delta-net"); the row's lanes together
+// hold all of q and k, so the norms are two more lane reductions.
+// scale multiplies the output.
+template <typename DT, int DK, int PASSES, bool GATED, bool L2>
 __global__ __launch_bounds__(256) void recurrent_step_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const float *__restrict__ g, float *__restrict__ S,
-    DT *__restrict__ o, int Dv, int wg_per_head) {
+    DT *__restrict__ o, int Dv, int wg_per_head, float scale) {
     constexpr int LPR = DK / 8;        // lanes per state row
     constexpr int RPP = 256 / LPR;     // rows per pass
     const int64_t head = blockIdx.x / wg_per_head;  // flattened b*H + h
@@ -59,6 +63,20 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
     float kf[8], qf[8];
     load8(k + head * DK + 8 * sub, kf);
     load8(q + head * DK + 8 * sub, qf);
+    if constexpr (L2) {
+        float kk = 0.f, qq = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            kk += kf[i] * kf[i];
+            qq += qf[i] * qf[i];
+        }
+        const float nk = rsqrtf(row_sum<LPR>(kk) + 1e-6f), nq = rsqrtf(row_sum<LPR>(qq) + 1e-6f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            kf[i] *= nk;
+            qf[i] *= nq;
+        }
+    }
     const float b = to_f32(beta[head]);
     const float a = GATED ? __expf(g[head]) : 1.f;
 
@@ -99,56 +117,51 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
             float4 *dst = reinterpret_cast<float4 *>(S + (head * Dv + row[p]) * DK + 8 * sub);
             dst[0] = make_float4(s[p][0], s[p][1], s[p][2], s[p][3]);
             dst[1] = make_float4(s[p][4], s[p][5], s[p][6], s[p][7]);
-            if (sub == 0) o[head * Dv + row[p]] = from_f32<DT>(oq);
+            if (sub == 0) o[head * Dv + row[p]] = from_f32<DT>(oq * scale);
         }
     }
 }
 
-template <typename DT, int DK>
-hipError_t launch_step(const void *q, const void *k, const void *v, const void *beta,
-                       const float *g, float *S, void *o, int64_t BH, int Dv,
-                       hipStream_t stream) {
+template <typename DT, int DK, bool GATED, bool L2>
+hipError_t launch_step(const StepArgs &x, hipStream_t stream) {
     constexpr int LPR = DK / 8;
     constexpr int RPP = 256 / LPR;
     constexpr int PASSES = 2;
     const int rows_per_wg = RPP * PASSES;
-    const int wg_per_head = (Dv + rows_per_wg - 1) / rows_per_wg;
-    const int64_t grid = BH * wg_per_head;
-    if (g)
-        hipLaunchKernelGGL((recurrent_step_kernel<DT, DK, PASSES, true>), dim3((unsigned)grid),
-                           dim3(256), 0, stream, static_cast<const DT *>(q),
-                           static_cast<const DT *>(k), static_cast<const DT *>(v),
-                           static_cast<const DT *>(beta), g, S, static_cast<DT *>(o), Dv,
-                           wg_per_head);
-    else
-        hipLaunchKernelGGL((recurrent_step_kernel<DT, DK, PASSES, false>), dim3((unsigned)grid),
-                           dim3(256), 0, stream, static_cast<const DT *>(q),
-                           static_cast<const DT *>(k), static_cast<const DT *>(v),
-                           static_cast<const DT *>(beta), g, S, static_cast<DT *>(o), Dv,
-                           wg_per_head);
+    const int wg_per_head = (x.Dv + rows_per_wg - 1) / rows_per_wg;
+    const int64_t grid = x.BH * wg_per_head;
+    hipLaunchKernelGGL((recurrent_step_kernel<DT, DK, PASSES, GATED, L2>), dim3((unsigned)grid),
+                       dim3(256), 0, stream, static_cast<const DT *>(x.q),
+                       static_cast<const DT *>(x.k), static_cast<const DT *>(x.v),
+                       static_cast<const DT *>(x.beta), x.g, x.S, static_cast<DT *>(x.o), x.Dv,
+                       wg_per_head, x.scale);
     return hipGetLastError();
 }
 
+template <typename DT, int DK>
+hipError_t dispatch_opts(const StepArgs &x, hipStream_t stream) {
+    if (x.g)
+        return x.l2 ? launch_step<DT, DK, true, true>(x, stream)
+                    : launch_step<DT, DK, true, false>(x, stream);
+    return x.l2 ? launch_step<DT, DK, false, true>(x, stream)
+                : launch_step<DT, DK, false, false>(x, stream);
+}
+
 template <typename DT>
-hipError_t dispatch_dk(const void *q, const void *k, const void *v, const void *beta,
-                       const float *g, float *S, void *o, int64_t BH, int Dk, int Dv,
-                       hipStream_t stream) {
-    switch (Dk) {
-    case 16: return launch_step<DT, 16>(q, k, v, beta, g, S, o, BH, Dv, stream);
-    case 32: return launch_step<DT, 32>(q, k, v, beta, g, S, o, BH, Dv, stream);
-    case 64: return launch_step<DT, 64>(q, k, v, beta, g, S, o, BH, Dv, stream);
-    case 128: return launch_step<DT, 128>(q, k, v, beta, g, S, o, BH, Dv, stream);
+hipError_t dispatch_dk(const StepArgs &x, hipStream_t stream) {
+    switch (x.Dk) {
+    case 16: return dispatch_opts<DT, 16>(x, stream);
+    case 32: return dispatch_opts<DT, 32>(x, stream);
+    case 64: return dispatch_opts<DT, 64>(x, stream);
+    case 128: return dispatch_opts<DT, 128>(x, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_recurrent_step(const void *q, const void *k, const void *v,
-                                 const void *beta, const float *g, float *S, void *o,
-                                 int64_t BH, int Dk, int Dv, bool bf16, hipStream_t stream) {
-    if (bf16) return dispatch_dk<__bf16>(q, k, v, beta, g, S, o, BH, Dk, Dv, stream);
-    return dispatch_dk<float>(q, k, v, beta, g, S, o, BH, Dk, Dv, stream);
+hipError_t launch_recurrent_step(const StepArgs &x, bool bf16, hipStream_t stream) {
+    return bf16 ? dispatch_dk<__bf16>(x, stream) : dispatch_dk<float>(x, stream);
 }
 
 }  // namespace dr

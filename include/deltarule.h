@@ -228,6 +228,30 @@ dr_status gated_delta_rule_recurrent_step(const void *q, const void *k, const vo
                                           int64_t B, int64_t H, int64_t Dk, int64_t Dv,
                                           dr_dtype dtype, void *stream);
 
+/*
+ * Options of delta_rule_recurrent_step_ex (zero-initialise, then set
+ * scale = 1): g ([B,H] fp32 log forget gate, or NULL for the plain rule),
+ * scale (finite output scale) and flags (0 or DR_QK_L2NORM), with the
+ * meanings they have in dr_chunk_opts.
+ */
+typedef struct dr_step_opts {
+    const float *g;
+    float scale;
+    uint32_t flags;
+} dr_step_opts;
+
+/*
+ * delta_rule_recurrent_step_ex -- delta_rule_recurrent_step with the options
+ * above (opts == NULL: none).  Every other argument and error behaves as in
+ * delta_rule_recurrent_step (g as in gated_delta_rule_recurrent_step); in
+ * addition DR_ERR_INVALID_ARG is returned for a non-finite scale or unknown
+ * flag bits.
+ */
+dr_status delta_rule_recurrent_step_ex(const void *q, const void *k, const void *v,
+                                       const void *beta, float *S, void *o, int64_t B,
+                                       int64_t H, int64_t Dk, int64_t Dv,
+                                       const dr_step_opts *opts, dr_dtype dtype, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *delta_rule_status_string(dr_status status);
 
@@ -236,7 +260,8 @@ const char *delta_rule_status_string(dr_status status);
 int delta_rule_last_hip_error(void);
 
 /* Library version as major*10000 + minor*100 + patch (2.0.0: the gated
- * entry points; 2.1.0: delta_rule_chunk_fwd_ex; 2.2.0: DR_QK_L2NORM). */
+ * entry points; 2.1.0: delta_rule_chunk_fwd_ex; 2.2.0: DR_QK_L2NORM; 2.3.0:
+ * delta_rule_recurrent_step_ex). */
 int delta_rule_version(void);
 
 #ifdef __cplusplus

@@ -248,3 +248,34 @@ def test_chunk_ex_rejects_unsupported(lib):
 def test_chunk_ex_no_sequences_is_a_no_op(lib):
     assert _ex(lib, _opts(cu_seqlens=CU.value, num_seqs=0)) == dr.DR_OK
     assert _ex(lib, _opts(scale=2.0), H=0) == dr.DR_OK
+
+
+# ------------------------------------------------- extended decode step
+def _sx(lib, opts=None, q=P[0], k=P[1], v=P[2], beta=P[3], S=P[4], o=P[5], B=2, H=2,
+        Dk=64, Dv=64, dtype=dr.DR_BF16):
+    return lib.delta_rule_recurrent_step_ex(q, k, v, beta, S, o, B, H, Dk, Dv,
+                                            None if opts is None else ctypes.byref(opts),
+                                            dtype, None)
+
+
+def test_step_options_struct_layout():
+    assert ctypes.sizeof(dr.dr_step_opts) == 16
+    assert dr.dr_step_opts.scale.offset == 8 and dr.dr_step_opts.flags.offset == 12
+
+
+@pytest.mark.parametrize("kw, call", [
+    (dict(scale=float("nan")), {}), (dict(scale=float("-inf")), {}),
+    (dict(flags=4), {}), (dict(g=ODD.value), {}), (dict(g=P[4].value), {}),
+    (dict(scale=2.0), dict(S=None)), (dict(flags=1), dict(q=MISALIGNED)),
+])
+def test_step_ex_rejects_invalid(lib, kw, call):
+    o = dr.dr_step_opts(g=None, scale=1.0, flags=0)
+    for n, val in kw.items():
+        setattr(o, n, val)
+    assert _sx(lib, o, **call) == dr.DR_ERR_INVALID_ARG
+
+
+def test_step_ex_unsupported_and_empty(lib):
+    o = dr.dr_step_opts(g=None, scale=1.0, flags=1)
+    assert _sx(lib, o, Dk=24) == dr.DR_ERR_UNSUPPORTED
+    assert _sx(lib, o, B=0) == dr.DR_OK

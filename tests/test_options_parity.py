@@ -199,3 +199,59 @@ def test_l2norm_zero_rows_and_packed_sequences():
             o_ref, s_ref = oracle_all(xs)
             assert rel_err(to_np(o[:, a:b]), o_ref) <= 2e-2
             assert rel_err(to_np(st[s:s + 1]), s_ref) <= 2e-2
+
+
+# ------------------------------------------------------ decode-step options
+def _decode_opts_check(w, gated, **kw):
+    x = W.generate(w)
+    d = to_dev(x)
+    S = d["S0"].clone()
+    outs = []
+    for t in range(w.T):
+        if gated:
+            outs.append(dr.gated_delta_rule_recurrent_step(d["q"][t], d["k"][t], d["v"][t],
+                                                           d["beta"][t], d["g"][t], S, **kw))
+        else:
+            outs.append(dr.delta_rule_recurrent_step(d["q"][t], d["k"][t], d["v"][t],
+                                                     d["beta"][t], S, **kw))
+    torch.cuda.synchronize()
+    seq = {n: (None if t is None else (t.transpose(0, 1).contiguous() if n != "S0" else t))
+           for n, t in x.items()}
+    if kw.get("use_qk_l2norm_in_kernel"):
+        seq = _l2_inputs(seq)
+    o_ref, s_ref = oracle_all(seq)
+    o_ref = o_ref * (kw.get("scale") or 1.0)
+    tol = TOL[w.torch_dtype]
+    o_seq = torch.stack(outs).transpose(0, 1)
+    eo, es = rel_err(to_np(o_seq), o_ref), rel_err(to_np(S), s_ref)
+    print(f"decode opts {kw} gated={gated} Dk{w.Dk} {w.dtype}: o {eo:.2e} S {es:.2e}", flush=True)
+    assert eo <= tol and es <= tol
+
+
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("Dk,Dv", [(16, 16), (64, 128), (128, 128)])
+def test_decode_l2norm_and_scale(gated, dtype, Dk, Dv):
+    w = W.get("decode", B=3, H=2, T=10, Dk=Dk, Dv=Dv, dtype=dtype, feature="raw",
+              gate_amax=0.5 if gated else 0.0, seed=6300 + Dk + Dv)
+    _decode_opts_check(w, gated, use_qk_l2norm_in_kernel=True, scale=Dk ** -0.5)
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_decode_scale_only(gated):
+    w = W.get("decode", B=4, H=2, T=8, gate_amax=0.5 if gated else 0.0, seed=6400)
+    _decode_opts_check(w, gated, scale=0.25)
+
+
+def test_decode_l2norm_matches_chunk_l2norm():
+    w = W.get("long_prefill", B=2, H=3, T=40, feature="raw", gate_amax=0.5)
+    d = to_dev(W.generate(w))
+    o_c, s_c = dr.gated_delta_rule_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["S0"],
+                                             use_qk_l2norm_in_kernel=True)
+    S = d["S0"].clone()
+    col = lambda t, i: t[:, i].contiguous()
+    o_d = torch.stack([dr.gated_delta_rule_recurrent_step(
+        col(d["q"], t), col(d["k"], t), col(d["v"], t), col(d["beta"], t), col(d["g"], t), S,
+        use_qk_l2norm_in_kernel=True) for t in range(40)], dim=1)
+    assert rel_err(to_np(o_d), to_np(o_c)) <= 2e-2
+    assert rel_err(to_np(S), to_np(s_c)) <= 2e-2
