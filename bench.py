@@ -20,9 +20,12 @@ JSON line on stdout:
   gated        the gated rule (per-token log forget gate) on the layer shape
                (chunked forward) and on the decode workload
   qk_l2norm    the layer shape with raw q, k normalised inside the kernel
+  backward     delta_rule_chunk_bwd on the layer shape (checkpointing forward
+               and reverse pass), time per call and ratio to the forward launch
 
 Options: --gpus N (only 1: this build targets one GPU), --steps K,
---warmup W, --no-cpu-baseline, --no-decode, --no-gated, --copy-calib BYTES (also time a
+--warmup W, --no-cpu-baseline, --no-decode, --no-gated, --no-backward,
+--copy-calib BYTES (also time a
 plain device copy of that size, for counter calibration runs).
 """
 from __future__ import annotations
@@ -229,6 +232,48 @@ def bench_gated_chunk(torch, dr, W, reps=20, name="gated_layer_1p3b", l2=False):
     }
 
 
+def bench_backward(torch, dr, W, reps=10):
+    """delta_rule_chunk_bwd on the layer shape: the checkpointing forward pass
+    plus the reverse pass, with upstream gradients for o and S_T (mean time per
+    call with HIP events on the launch stream)."""
+    w = W.get("layer_1p3b")
+    x = W.generate(w)
+    dev = torch.device("cuda:0")
+    d = {n: (None if t is None else t.to(dev)) for n, t in x.items()}
+    gen = torch.Generator(device="cpu").manual_seed(11)
+    do = torch.randn(w.B, w.T, w.H, w.Dv, generator=gen).to(w.torch_dtype).to(dev)
+    dst = torch.randn(w.B, w.H, w.Dv, w.Dk, generator=gen).to(dev)
+    lib = dr.load_library()
+    code = dr.DR_BF16 if w.dtype == "bf16" else dr.DR_F32
+    ws = torch.empty(int(lib.delta_rule_chunk_bwd_workspace_bytes(w.B, w.T, w.H, w.Dk, w.Dv,
+                                                                  code)),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        dr.delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], do, d["S0"], dst,
+                                workspace=ws)
+
+    for _ in range(2):
+        step()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    t = sum(a.elapsed_time(b) for a, b in ev) / reps / 1e3
+    return {
+        "workload": (f"{w.name} B{w.B} H{w.H} T{w.T} d{w.Dk}, bf16 in, fp32 state; "
+                     "checkpointing forward + reverse pass (output allocation inside)"),
+        "tokens_per_s": w.B * w.T / t,
+        "mean_call_us": round(t * 1e6, 2),
+        "vs_forward_launch": None,
+        "workspace_bytes": int(ws.numel()),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,6 +282,8 @@ def main():
     ap.add_argument("--workload", default="layer_1p3b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward line")
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the gated-rule lines (chunked layer shape and decode)")
     ap.add_argument("--copy-calib", type=int, default=0,
@@ -340,6 +387,11 @@ def main():
             out["gated"]["decode"] = bench_decode(torch, dr, W, name="gated_decode")
         log("in-kernel q/k L2 norm: layer shape chunked forward")
         out["qk_l2norm"] = {"chunk": bench_gated_chunk(torch, dr, W, name="layer_1p3b", l2=True)}
+    if not args.no_backward:
+        log("backward: layer shape")
+        out["backward"] = bench_backward(torch, dr, W)
+        out["backward"]["vs_forward_launch"] = round(
+            out["backward"]["mean_call_us"] / roof["mean_launch_us"], 2)
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle on the whole workload")
         torch.cuda.synchronize()

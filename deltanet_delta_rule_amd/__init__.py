@@ -30,6 +30,7 @@ __all__ = [
     "delta_rule_recurrent_step",
     "gated_delta_rule_chunk_fwd",
     "gated_delta_rule_recurrent_step",
+    "delta_rule_chunk_bwd",
     "delta_rule_status_string",
     "delta_rule_version",
     "DeltaRuleError",
@@ -91,6 +92,11 @@ def load_library():
     lib.gated_delta_rule_recurrent_step.restype = i32
     lib.gated_delta_rule_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp,
                                                     i64, i64, i64, i64, i32, vp]
+    lib.delta_rule_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.delta_rule_chunk_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
+    lib.delta_rule_chunk_bwd.restype = i32
+    lib.delta_rule_chunk_bwd.argtypes = [vp] * 13 + [ctypes.c_size_t, i64, i64, i64, i64, i64,
+                                                     i32, vp]
     lib.delta_rule_status_string.restype = ctypes.c_char_p
     lib.delta_rule_status_string.argtypes = [i32]
     lib.delta_rule_last_hip_error.restype = i32
@@ -300,3 +306,47 @@ def gated_delta_rule_recurrent_step(q, k, v, beta, g, S, *, o=None, scale=None,
     """One decode token of the gated rule: as ``delta_rule_recurrent_step``
     plus g ``[B,H]`` float32, the log forget gate of this token."""
     return _step_call(True, q, k, v, beta, g, S, o, stream, scale, use_qk_l2norm_in_kernel)
+
+
+def delta_rule_chunk_bwd(q, k, v, beta, do, S0=None, dS_T=None, *, workspace=None,
+                         need_dS0=True, stream=None):
+    """Gradients of ``delta_rule_chunk_fwd`` (plain rule) for upstream
+    gradients ``do`` ``[B,T,H,Dv]`` (dtype of q) and ``dS_T`` ``[B,H,Dv,Dk]``
+    float32 or None.  Returns a dict with dq, dk, dv, dbeta (dtype of q) and
+    dS0 (float32, or None when ``need_dS0`` is False).  ``workspace`` (a
+    uint8 GPU tensor of at least ``delta_rule_chunk_bwd_workspace_bytes``
+    bytes) holds the forward checkpoints; it is allocated when not given."""
+    torch = _torch()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("the backward needs GPU tensors")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    code = _dtype_code(q)
+    _need(q, "q", (B, T, H, Dk), dt, dev)
+    _need(k, "k", (B, T, H, Dk), dt, dev)
+    _need(v, "v", (B, T, H, Dv), dt, dev)
+    _need(beta, "beta", (B, T, H), dt, dev)
+    _need(do, "do", (B, T, H, Dv), dt, dev)
+    if S0 is not None:
+        _need(S0, "S0", (B, H, Dv, Dk), torch.float32, dev)
+    if dS_T is not None:
+        _need(dS_T, "dS_T", (B, H, Dv, Dk), torch.float32, dev)
+    lib = load_library()
+    nbytes = int(lib.delta_rule_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, code))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace must be a GPU tensor of at least {nbytes} bytes")
+    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+           "dbeta": torch.empty_like(beta),
+           "dS0": torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+           if need_dS0 else None}
+    st = lib.delta_rule_chunk_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(do), _ptr(dS_T),
+        _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
+        _ptr(out["dS0"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        B, T, H, Dk, Dv, code, _stream(dev, stream))
+    _check(st)
+    return out

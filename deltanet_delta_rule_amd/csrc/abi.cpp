@@ -100,10 +100,10 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
     }
     if (T > 0 && overlaps(so, sst)) return DR_ERR_INVALID_ARG;
 
-    dr::ChunkFwdArgs a{q,  k,        v,        beta, gated ? g : nullptr,
-                       S0, o,        S_T,      cu,   ns_count,
-                       T,  H,        (int)Dk,  (int)Dv, (int)chunk,
-                       scale, l2};
+    dr::ChunkFwdArgs a{q,       k,        v,       beta,       gated ? g : nullptr,
+                       S0,      o,        S_T,     nullptr,    cu,
+                       ns_count, T,       H,       (int)Dk,    (int)Dv,
+                       (int)chunk, scale, l2};
     return hip_status(dr::launch_chunk_fwd(a, dtype == DR_BF16, static_cast<hipStream_t>(stream)));
 }
 
@@ -141,6 +141,66 @@ dr_status recurrent_step(const void *q, const void *k, const void *v, const void
                          l2};
     return hip_status(
         dr::launch_recurrent_step(a, dtype == DR_BF16, static_cast<hipStream_t>(stream)));
+}
+
+// Checkpoint workspace of the backward: every chunk's incoming state.
+int64_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, bool bf16) {
+    const int64_t cb = dr::chunk_bwd_chunk(bf16);
+    const int64_t N = (T + cb - 1) / cb;
+    return mul_checked({B, H, N, Dv, Dk, 4});
+}
+
+dr_status chunk_bwd(const void *q, const void *k, const void *v, const void *beta,
+                    const float *S0, const void *dout, const float *dS_T, void *dq, void *dk,
+                    void *dv, void *dbeta, float *dS0, void *ws, size_t ws_bytes, int64_t B,
+                    int64_t T, int64_t H, int64_t Dk, int64_t Dv, dr_dtype dtype, void *stream) {
+    if (dtype != DR_F32 && dtype != DR_BF16) return DR_ERR_INVALID_ARG;
+    if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0) return DR_ERR_INVALID_ARG;
+    if (!supported_dim(Dk) || !supported_dim(Dv)) return DR_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0) return DR_OK;
+    const bool bf16 = dtype == DR_BF16;
+    const int64_t esz = bf16 ? 2 : 4;
+    const int64_t nqk = mul_checked({B, T, H, Dk}), nv = mul_checked({B, T, H, Dv});
+    const int64_t nb = mul_checked({B, T, H}), ns = mul_checked({B, H, Dv, Dk});
+    const int64_t need = bwd_workspace_bytes(B, T, H, Dk, Dv, bf16);
+    if (nqk < 0 || nv < 0 || nb < 0 || ns < 0 || need < 0) return DR_ERR_UNSUPPORTED;
+    if (T > INT32_MAX || H > INT32_MAX || mul_checked({B, H}) > INT32_MAX) return DR_ERR_UNSUPPORTED;
+    const int64_t span = mul_checked({32, H, Dk > Dv ? Dk : Dv, esz});
+    if (span < 0 || span > INT32_MAX / 2) return DR_ERR_UNSUPPORTED;
+    if (T > 0 && (!q || !k || !v || !beta || !dout || !dq || !dk || !dv || !dbeta))
+        return DR_ERR_INVALID_ARG;
+    if (T > 0 && (!ws || (int64_t)ws_bytes < need)) return DR_ERR_INVALID_ARG;
+    const void *vec_ptrs[] = {q, k, S0, dS_T, dS0, ws};
+    for (const void *p : vec_ptrs)
+        if (p && !aligned16(p)) return DR_ERR_INVALID_ARG;
+    const void *elem_ptrs[] = {v, beta, dout, dq, dk, dv, dbeta};
+    for (const void *p : elem_ptrs)
+        if (p && !aligned_to(p, esz)) return DR_ERR_INVALID_ARG;
+    // outputs must not overlap any input or each other
+    const Span in[] = {{q, nqk * esz},  {k, nqk * esz},   {v, nv * esz},
+                       {beta, nb * esz}, {S0, ns * 4},    {dout, nv * esz},
+                       {dS_T, ns * 4}};
+    const Span out[] = {{dq, nqk * esz}, {dk, nqk * esz}, {dv, nv * esz},
+                        {dbeta, nb * esz}, {dS0, ns * 4}, {ws, need}};
+    for (const Span &o : out) {
+        for (const Span &s : in)
+            if (overlaps(o, s)) return DR_ERR_INVALID_ARG;
+        for (const Span &o2 : out)
+            if (&o2 != &o && overlaps(o, o2)) return DR_ERR_INVALID_ARG;
+    }
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    float *h = static_cast<float *>(ws);
+    if (T > 0) {
+        const dr::ChunkFwdArgs f{q,      k,       v,        beta,     nullptr, S0,
+                                 nullptr, nullptr, h,        nullptr,  B,       T,
+                                 H,      (int)Dk, (int)Dv,  dr::chunk_bwd_chunk(bf16),
+                                 1.f,    false};
+        const hipError_t e = dr::launch_chunk_fwd(f, bf16, st);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    const dr::ChunkBwdArgs a{q,  k,  v,  beta, dout, dS_T, h,       dq,      dk,
+                             dv, dbeta, dS0, B, T,    H,    (int)Dk, (int)Dv};
+    return hip_status(dr::launch_chunk_bwd(a, bf16, st));
 }
 
 }  // namespace
@@ -206,6 +266,24 @@ dr_status delta_rule_recurrent_step_ex(const void *q, const void *k, const void 
                           (x.flags & DR_QK_L2NORM) != 0, dtype, stream);
 }
 
+size_t delta_rule_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                            int64_t Dv, dr_dtype dtype) {
+    if (B < 0 || T < 0 || H < 0 || !supported_dim(Dk) || !supported_dim(Dv) ||
+        (dtype != DR_F32 && dtype != DR_BF16))
+        return 0;
+    const int64_t n = bwd_workspace_bytes(B, T, H, Dk, Dv, dtype == DR_BF16);
+    return n < 0 ? 0 : (size_t)n;
+}
+
+dr_status delta_rule_chunk_bwd(const void *q, const void *k, const void *v, const void *beta,
+                               const float *S0, const void *dout, const float *dS_T, void *dq,
+                               void *dk, void *dv, void *dbeta, float *dS0, void *workspace,
+                               size_t workspace_bytes, int64_t B, int64_t T, int64_t H,
+                               int64_t Dk, int64_t Dv, dr_dtype dtype, void *stream) {
+    return chunk_bwd(q, k, v, beta, S0, dout, dS_T, dq, dk, dv, dbeta, dS0, workspace,
+                     workspace_bytes, B, T, H, Dk, Dv, dtype, stream);
+}
+
 const char *delta_rule_status_string(dr_status status) {
     switch (status) {
     case DR_OK: return "DR_OK";
@@ -218,6 +296,6 @@ const char *delta_rule_status_string(dr_status status) {
 
 int delta_rule_last_hip_error(void) { return g_last_hip_error; }
 
-int delta_rule_version(void) { return 20300; }
+int delta_rule_version(void) { return 20400; }
 
 }  // extern "C"

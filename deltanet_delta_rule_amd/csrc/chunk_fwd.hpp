@@ -819,6 +819,15 @@ __device__ __forceinline__ void state_path(const DT *Ks, const DT *Qs, const DT 
     state_rest<DT, DK, C, NW, GATED, L2>(op, Ab, Tb, Ps, ga, nl, Sacc, X, Y, out, lane);
 }
 
+// A state tile row (this lane's row r, keys in state_col order) to row-major
+// memory at `row` (the row's first element).
+template <int KSD, int ND>
+__device__ __forceinline__ void store_state_row(float *row, const f32x4 *Sacc, int g) {
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+        *reinterpret_cast<f32x4 *>(row + state_col<KSD>(dt, g)) = Sacc[dt];
+}
+
 // Common per-workgroup addressing: (b, h, value tile) of this workgroup with
 // an XCD-aware remap, and the base pointers of its head.
 template <typename DT>
@@ -828,6 +837,7 @@ struct HeadPtrs {
     DT *oh;                       // token 0, column 0 of the head's output
     int tsk, tsv, tsb;            // token strides in elements: H*d_k, H*d_v, H
     int T;                        // tokens of this sequence
+    int64_t head;                 // sequence * H + head
     int64_t sbase;
     int vcol;
 };
@@ -867,6 +877,7 @@ __device__ __forceinline__ HeadPtrs<DT> head_ptrs(const DT *q, const DT *k, cons
     p.oh = o + (t0 * H + h) * Dv;
     p.bh = beta + t0 * H + h;
     p.gh = gl ? gl + t0 * H + h : nullptr;
+    p.head = head;
     p.sbase = ((int64_t)head * Dv + p.vcol) * DK;
     return p;
 }
@@ -1171,8 +1182,8 @@ template <typename DT, int DK, int C, int NW, bool GATED, bool L2>
 __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4 + 1, NW / 4 + 1))) void chunk_fwd_ws_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const float *__restrict__ gl, const float *S0,
-    DT *__restrict__ o, float *S_T, const int *__restrict__ cu, int T, int H, int Dv, int nvt,
-    float scale) {
+    DT *__restrict__ o, float *S_T, float *__restrict__ hs, const int *__restrict__ cu, int T,
+    int H, int Dv, int nvt, float scale) {
     typedef ChunkCfg<DT, DK, C, NW> G;
     constexpr int NT = G::NT, ND = G::ND;
     __shared__ __attribute__((aligned(16))) PipeSmem<DT, DK, C, NW, GATED, L2> sm;
@@ -1215,8 +1226,9 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4
             constexpr int s0 = decltype(set)::value, s1 = (s0 + 1) % 3;  // sets of chunks c, c+1
             const int b = c & 1;
             const int t0 = c * C;
-            const int len = min(C, p.T - t0);
+            const int len = o ? min(C, p.T - t0) : 0;
             out.rsrc = make_rsrc(p.oh + (int64_t)t0 * p.tsv, len * out.row_bytes);
+            if (hs) store_state_row<G::KSD, ND>(hs + ((p.head * N + c) * Dv + p.vcol) * DK, Sacc, g);
             state_rest<DT, DK, C, NW, GATED, L2>(op, sm.Ab[b], sm.Tb[b], sm.Ps[b], sm.gate.at(s0),
                                                  sm.norm.at(b), Sacc, X, Y, out, lane);
             // V first (X starts at -V); the K^T fragments of the next state
@@ -1271,8 +1283,8 @@ template <typename DT, int DK, int C, int NW, bool GATED, bool L2>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_fwd_serial_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const float *__restrict__ gl, const float *S0,
-    DT *__restrict__ o, float *S_T, const int *__restrict__ cu, int T, int H, int Dv, int nvt,
-    float scale) {
+    DT *__restrict__ o, float *S_T, float *__restrict__ hs, const int *__restrict__ cu, int T,
+    int H, int Dv, int nvt, float scale) {
     typedef ChunkCfg<DT, DK, C, NW> G;
     constexpr int ND = G::ND;
     __shared__ __attribute__((aligned(16))) SerialSmem<DT, DK, C, NW, GATED, L2> sm;
@@ -1301,7 +1313,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
         rg.load(p, p.T, 0);
         for (int c = 0; c < N; ++c) {
             const int t0 = c * C;
-            const int len = min(C, p.T - t0);
+            const int len = o ? min(C, p.T - t0) : 0;
+            if (hs) store_state_row<G::KSD, ND>(hs + ((p.head * N + c) * Dv + p.vcol) * DK, Sacc, g);
             lds_barrier();
             rg.stage(sm.Ks, sm.Qs, sm.Vs, sm.betas, sm.gate.at(0), tid);
             lds_barrier();
@@ -1338,11 +1351,11 @@ hipError_t launch_cfg(const ChunkFwdArgs &a, hipStream_t stream) {
     DT *o = static_cast<DT *>(a.o);
     if constexpr (ws_fits<DT, DK, C, NW, GATED, L2>()) {
         hipLaunchKernelGGL((chunk_fwd_ws_kernel<DT, DK, C, NW, GATED, L2>), dim3((unsigned)grid),
-                           dim3(128 * NW), 0, stream, q, k, v, beta, a.g, a.S0, o, a.S_T, a.cu,
+                           dim3(128 * NW), 0, stream, q, k, v, beta, a.g, a.S0, o, a.S_T, a.h, a.cu,
                            (int)a.T, (int)a.H, a.Dv, nvt, a.scale);
     } else {
         hipLaunchKernelGGL((chunk_fwd_serial_kernel<DT, DK, C, NW, GATED, L2>), dim3((unsigned)grid),
-                           dim3(64 * NW), 0, stream, q, k, v, beta, a.g, a.S0, o, a.S_T, a.cu,
+                           dim3(64 * NW), 0, stream, q, k, v, beta, a.g, a.S0, o, a.S_T, a.h, a.cu,
                            (int)a.T, (int)a.H, a.Dv, nvt, a.scale);
     }
     return hipGetLastError();

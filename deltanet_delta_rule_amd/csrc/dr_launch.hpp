@@ -12,12 +12,15 @@ namespace dr {
 // head, value tile)).  g is the log forget gate [B,T,H] (fp32) of the gated
 // rule, or nullptr.  cu, when set, holds B+1 sequence offsets into the single
 // batch row of T tokens (packed variable-length input); scale multiplies the
-// outputs; l2 normalises the rows of q and k inside the kernel.
+// outputs; l2 normalises the rows of q and k inside the kernel.  o may be
+// nullptr (no outputs written); h, when set, receives each chunk's incoming
+// state, [B,H,N,Dv,Dk] fp32 with N = ceil(T / chunk) (no packed sequences).
 struct ChunkFwdArgs {
     const void *q, *k, *v, *beta;
     const float *g, *S0;
     void *o;
     float *S_T;
+    float *h;
     const int *cu;
     int64_t B, T, H;
     int Dk, Dv, chunk;
@@ -26,6 +29,22 @@ struct ChunkFwdArgs {
 };
 
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
+
+// Arguments of the backward of the chunked forward (plain rule).  h holds the
+// checkpoints the forward kernel wrote with chunk = chunk_bwd_chunk(bf16);
+// dS_T and dS0 may be nullptr.
+struct ChunkBwdArgs {
+    const void *q, *k, *v, *beta, *dout;
+    const float *dS_T, *h;
+    void *dq, *dk, *dv, *dbeta;
+    float *dS0;
+    int64_t B, T, H;
+    int Dk, Dv;
+};
+
+hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, bool bf16, hipStream_t stream);
+// Tokens per chunk of the backward (and of its forward checkpoints).
+int chunk_bwd_chunk(bool bf16);
 
 // Arguments of the single-token decode step (state updated in place).  g is
 // the log forget gate [B,H] (fp32) of the gated rule, or nullptr; scale

@@ -252,6 +252,39 @@ dr_status delta_rule_recurrent_step_ex(const void *q, const void *k, const void 
                                        int64_t H, int64_t Dk, int64_t Dv,
                                        const dr_step_opts *opts, dr_dtype dtype, void *stream);
 
+/*
+ * delta_rule_chunk_bwd -- gradients of delta_rule_chunk_fwd (plain rule).
+ *
+ * For upstream gradients dout = dL/do ([B,T,H,Dv], dtype `dtype`) and
+ * dS_T = dL/dS_T ([B,H,Dv,Dk] fp32, or NULL for none), writes
+ * dq, dk [B,T,H,Dk], dv [B,T,H,Dv], dbeta [B,T,H] (dtype `dtype`) and, when
+ * dS0 is not NULL, dS0 = dL/dS0 [B,H,Dv,Dk] fp32.  The gradients are those of
+ * the token recurrence; they are computed chunkwise (the training strategy
+ * of the paperlayer summary of arXiv:2406.06484, section 3: the forward
+ * states of every chunk are kept and the chunk-internal quantities
+ * recomputed).  The call first reruns the forward pass to store each chunk's
+ * incoming state in `workspace`, then walks the chunks in reverse.
+ *
+ *   q, k, v, beta, S0   the forward inputs, as in delta_rule_chunk_fwd
+ *   workspace           device memory of at least
+ *                       delta_rule_chunk_bwd_workspace_bytes(B,T,H,Dk,Dv,dtype)
+ *                       bytes (16-byte aligned; contents on return: the
+ *                       forward checkpoints); may be NULL when T == 0
+ *   Outputs must not overlap the inputs, the workspace or each other.
+ * Sizes as delta_rule_chunk_fwd (Dk, Dv in {16,32,64,128}); the chunk length
+ * is chosen by the library (32 tokens for bf16, 16 for fp32).  Errors as
+ * delta_rule_chunk_fwd; a missing or too small workspace is
+ * DR_ERR_INVALID_ARG.
+ */
+size_t delta_rule_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                            int64_t Dv, dr_dtype dtype);
+
+dr_status delta_rule_chunk_bwd(const void *q, const void *k, const void *v, const void *beta,
+                               const float *S0, const void *dout, const float *dS_T, void *dq,
+                               void *dk, void *dv, void *dbeta, float *dS0, void *workspace,
+                               size_t workspace_bytes, int64_t B, int64_t T, int64_t H,
+                               int64_t Dk, int64_t Dv, dr_dtype dtype, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *delta_rule_status_string(dr_status status);
 
@@ -261,7 +294,7 @@ int delta_rule_last_hip_error(void);
 
 /* Library version as major*10000 + minor*100 + patch (2.0.0: the gated
  * entry points; 2.1.0: delta_rule_chunk_fwd_ex; 2.2.0: DR_QK_L2NORM; 2.3.0:
- * delta_rule_recurrent_step_ex). */
+ * delta_rule_recurrent_step_ex; 2.4.0: delta_rule_chunk_bwd). */
 int delta_rule_version(void);
 
 #ifdef __cplusplus

@@ -279,3 +279,37 @@ def test_step_ex_unsupported_and_empty(lib):
     o = dr.dr_step_opts(g=None, scale=1.0, flags=1)
     assert _sx(lib, o, Dk=24) == dr.DR_ERR_UNSUPPORTED
     assert _sx(lib, o, B=0) == dr.DR_OK
+
+
+# ---------------------------------------------------------------- backward
+def test_backward_workspace_size(lib):
+    f = lib.delta_rule_chunk_bwd_workspace_bytes
+    # bf16: 32-token chunks; fp32: 16-token chunks; one fp32 state per chunk and head
+    assert f(2, 100, 3, 64, 32, dr.DR_BF16) == 2 * 3 * 4 * 32 * 64 * 4
+    assert f(2, 100, 3, 64, 32, dr.DR_F32) == 2 * 3 * 7 * 32 * 64 * 4
+    assert f(1, 0, 1, 16, 16, dr.DR_BF16) == 0
+    assert f(1, 10, 1, 24, 16, dr.DR_BF16) == 0   # unsupported size
+    assert f(-1, 10, 1, 16, 16, dr.DR_BF16) == 0
+
+
+def _bwd(lib, ws=P[7], wsb=1 << 40, q=P[0], k=P[1], v=P[2], beta=P[3], dout=P[4], dq=P[5],
+         dk=P[6], dv=ctypes.c_void_p(0x100000 * 10), dbeta=ctypes.c_void_p(0x100000 * 11),
+         dS0=None, S0=None, dST=None, B=1, T=64, H=2, Dk=64, Dv=64, dtype=dr.DR_BF16):
+    return lib.delta_rule_chunk_bwd(q, k, v, beta, S0, dout, dST, dq, dk, dv, dbeta, dS0, ws,
+                                    wsb, B, T, H, Dk, Dv, dtype, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(ws=None), dict(wsb=16), dict(ws=MISALIGNED), dict(dout=None), dict(dq=None),
+    dict(dq=P[0]),                   # output overlaps q
+    dict(dk=P[5]),                   # two outputs overlap
+    dict(ws=P[4]),                   # workspace overlaps do
+    dict(dbeta=ODD), dict(B=-1), dict(dtype=5),
+])
+def test_backward_rejects_invalid(lib, kw):
+    assert _bwd(lib, **kw) == dr.DR_ERR_INVALID_ARG
+
+
+def test_backward_rejects_unsupported_and_empty(lib):
+    assert _bwd(lib, Dk=48) == dr.DR_ERR_UNSUPPORTED
+    assert _bwd(lib, B=0) == dr.DR_OK
