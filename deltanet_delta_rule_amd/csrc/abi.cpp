@@ -147,7 +147,7 @@ dr_status recurrent_step(const void *q, const void *k, const void *v, const void
 int64_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, bool bf16) {
     const int64_t cb = dr::chunk_bwd_chunk(bf16);
     const int64_t N = (T + cb - 1) / cb;
-    return mul_checked({B, H, N, Dv, Dk, 4});
+    return mul_checked({B, H, N, Dv, Dk, bf16 ? 2 : 4});
 }
 
 dr_status chunk_bwd(const void *q, const void *k, const void *v, const void *beta,
@@ -189,7 +189,7 @@ dr_status chunk_bwd(const void *q, const void *k, const void *v, const void *bet
             if (&o2 != &o && overlaps(o, o2)) return DR_ERR_INVALID_ARG;
     }
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    float *h = static_cast<float *>(ws);
+    void *h = ws;
     if (T > 0) {
         const dr::ChunkFwdArgs f{q,      k,       v,        beta,     nullptr, S0,
                                  nullptr, nullptr, h,        nullptr,  B,       T,

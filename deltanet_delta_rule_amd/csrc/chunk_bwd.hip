@@ -45,8 +45,14 @@ struct BwdCfg {
     static constexpr int PAD = 16 / (int)sizeof(DT);
     static constexpr int LDK = DK + PAD;          // K, Q rows (tokens x d_k)
     static constexpr int LDV = DV + PAD;          // V, dO, E, dV rows (tokens x d_v)
-    static constexpr int LDS_ = DV + PAD;         // S_c^T / dS^T rows (d_k x d_v)
+    static constexpr int LDS_ = DV + PAD;         // dS^T rows (d_k x d_v)
+    static constexpr int LDSK = DK + PAD;         // S_c rows (d_v x d_k)
     static constexpr int LDC = C + PAD;           // C x C matrices
+    // dS_{c+1}^T gets its own LDS buffer unless that overflows LDS (fp32 with
+    // d_k = d_v = 128); then it reuses the S_c^T buffer in a second pass.
+    static constexpr int BASE = (int)sizeof(DT) * (2 * C * LDK + 4 * C * LDV + DV * LDSK + 5 * C * LDC) +
+                                4 * C * (1 + NW);
+    static constexpr bool DBUF = BASE + (int)sizeof(DT) * DK * LDS_ + 256 <= 160 * 1024;
 };
 
 template <typename DT, int DK, int DV, int C>
@@ -55,7 +61,9 @@ struct BwdSmem {
     DT Ks[C * G::LDK], Qs[C * G::LDK];
     DT Vs[C * G::LDV], Os[C * G::LDV];            // V, dO
     DT Es[C * G::LDV], Rb[C * G::LDV];            // E, dV
-    DT Sb[DK * G::LDS_];                          // S_c^T, later dS_{c+1}^T
+    DT Sb[DV * G::LDSK];                          // S_c (rows: value index); second
+                                                  // pass without DBUF: dS_{c+1}
+    DT Db[G::DBUF ? DK * G::LDS_ : 8];            // dS_{c+1}^T (DBUF)
     DT Pm[C * G::LDC];                            // Q K^T (.) M
     DT Gl[C * G::LDC];                            // tril(K K^T, -1)
     DT Tm[C * G::LDC];                            // (I + A)^{-1}
@@ -80,38 +88,46 @@ __device__ __forceinline__ void mk(f32x4 &acc, const typename Frag<DT>::k16 &a,
 // 16x16 tile of A B with A row-major (rows m0.., k along the row) and B given
 // as B^T row-major (rows n0..): sum over k in [k0, k1).  D layout:
 // lane (g, r) holds (A B)[m0 + 4g + i][n0 + r].
-template <typename DT>
+// NK 16-wide steps from k0; every fragment is read before the first product
+// so that the LDS latency is paid once per tile.
+template <typename DT, int NK>
 __device__ __forceinline__ void tile_rr(f32x4 &acc, const DT *A, int lda, int m0, const DT *Bt,
-                                        int ldb, int n0, int k0, int k1, int lane) {
-    typename Frag<DT>::k16 fa, fb;
-    for (int k = k0; k < k1; k += 16) {
-        frag_rows(A, lda, m0, k, lane, fa);
-        frag_rows(Bt, ldb, n0, k, lane, fb);
-        mk<DT>(acc, fa, fb);
+                                        int ldb, int n0, int k0, int lane) {
+    typename Frag<DT>::k16 fa[NK], fb[NK];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+        frag_rows(A, lda, m0, k0 + 16 * i, lane, fa[i]);
+        frag_rows(Bt, ldb, n0, k0 + 16 * i, lane, fb[i]);
     }
+#pragma unroll
+    for (int i = 0; i < NK; ++i) mk<DT>(acc, fa[i], fb[i]);
 }
 // Same with B row-major (k along the rows of B: B[k][n]).
-template <typename DT>
+template <typename DT, int NK>
 __device__ __forceinline__ void tile_rc(f32x4 &acc, const DT *A, int lda, int m0, const DT *B,
-                                        int ldb, int n0, int k0, int k1, int lane) {
-    typename Frag<DT>::k16 fa, fb;
-    for (int k = k0; k < k1; k += 16) {
-        frag_rows(A, lda, m0, k, lane, fa);
-        frag_cols16(B, ldb, k, n0, lane, fb);
-        mk<DT>(acc, fa, fb);
+                                        int ldb, int n0, int k0, int lane) {
+    typename Frag<DT>::k16 fa[NK], fb[NK];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+        frag_rows(A, lda, m0, k0 + 16 * i, lane, fa[i]);
+        frag_cols16(B, ldb, k0 + 16 * i, n0, lane, fb[i]);
     }
+#pragma unroll
+    for (int i = 0; i < NK; ++i) mk<DT>(acc, fa[i], fb[i]);
 }
 // Same with A given transposed (A^T row-major: A[m][k] = At[k][m]) and B
 // row-major.
-template <typename DT>
+template <typename DT, int NK>
 __device__ __forceinline__ void tile_cc(f32x4 &acc, const DT *At, int lda, int m0, const DT *B,
-                                        int ldb, int n0, int k0, int k1, int lane) {
-    typename Frag<DT>::k16 fa, fb;
-    for (int k = k0; k < k1; k += 16) {
-        frag_cols16(At, lda, k, m0, lane, fa);
-        frag_cols16(B, ldb, k, n0, lane, fb);
-        mk<DT>(acc, fa, fb);
+                                        int ldb, int n0, int k0, int lane) {
+    typename Frag<DT>::k16 fa[NK], fb[NK];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+        frag_cols16(At, lda, k0 + 16 * i, m0, lane, fa[i]);
+        frag_cols16(B, ldb, k0 + 16 * i, n0, lane, fb[i]);
     }
+#pragma unroll
+    for (int i = 0; i < NK; ++i) mk<DT>(acc, fa[i], fb[i]);
 }
 
 // Store a D-layout tile (lane (g, r): rows 4g + i, column r) into a
@@ -159,36 +175,75 @@ __device__ __forceinline__ f32x4 inv_unit_lower(const f32x4 &a, const f32x4 &at,
     return dmul<DT>(t2t, I + a8);                             // ... (I + A^8)
 }
 
-// Cooperative copy of `rows` rows (valid < nvalid; the rest zero) of `cols`
-// elements from global (row stride gs elements) into LDS (row stride ld).
-template <typename DT>
-__device__ __forceinline__ void stage_rows(DT *dst, int ld, const DT *src, int64_t gs, int rows,
-                                           int nvalid, int cols, int tid, int nthr) {
-    const int per = cols / 4;  // groups of 4 elements
-    for (int i = tid; i < rows * per; i += nthr) {
-        const int t = i / per, e = (i % per) * 4;
-        DT x[4];
-        if (t < nvalid) {
+// 16 bytes of DT.
+template <typename DT> struct V16;
+template <> struct V16<__bf16> { typedef bf16x8 type; };
+template <> struct V16<float> { typedef f32x4 type; };
+
+// Register prefetch of one chunk's rows of a [tokens, cols] tile (row stride
+// gs elements in global memory, ld in LDS): 16-byte vectors dealt to the
+// threads; rows at or past the chunk's valid length load as zeros (buffer
+// resource range check).
+template <typename DT, int ROWS, int COLS, int NTHR>
+struct RowPrefetch {
+    typedef typename V16<DT>::type vec_t;
+    static constexpr int VPR = COLS * (int)sizeof(DT) / 16;   // vectors per row
+    static constexpr int NV = ROWS * VPR;
+    static constexpr int PER = (NV + NTHR - 1) / NTHR;
+    vec_t x[PER];
+    __device__ __forceinline__ void load(const DT *src, int64_t gs, int nvalid, int tid) {
+        const auto rs = make_rsrc(src, nvalid > 0 ? (int)((nvalid - 1) * gs + COLS) * (int)sizeof(DT) : 0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) x[j] = src[t * gs + e + j];
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) x[j] = from_f32<DT>(0.f);
+        for (int j = 0; j < PER; ++j) {
+            const int i = tid + j * NTHR;
+            const int t = i / VPR, e = (i % VPR) * (16 / (int)sizeof(DT));
+            const int off = (i < NV && t < nvalid) ? (int)((t * gs + e) * (int)sizeof(DT)) : 0x7ffffff0;
+            x[j] = buf_load16<vec_t>(rs, off);
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dst[t * ld + e + j] = x[j];
     }
-}
+    __device__ __forceinline__ void store(DT *dst, int ld, int tid) const {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int i = tid + j * NTHR;
+            if (i < NV) {
+                const int t = i / VPR, e = (i % VPR) * (16 / (int)sizeof(DT));
+                *reinterpret_cast<vec_t *>(dst + t * ld + e) = x[j];
+            }
+        }
+    }
+};
+
+// All per-chunk inputs of the backward, one chunk ahead: K, Q, V, dO, beta
+// and the chunk's incoming state S_c (row-major [d_v][d_k] checkpoint).
+template <typename DT, int DK, int DV, int C>
+struct ChunkPrefetch {
+    static constexpr int NTHR = 4 * DV;
+    RowPrefetch<DT, C, DK, NTHR> k, q;
+    RowPrefetch<DT, C, DV, NTHR> v, o;
+    RowPrefetch<DT, DV, DK, NTHR> s;
+    float b;
+    __device__ __forceinline__ void load(const DT *kk, const DT *qq, const DT *vv, const DT *oo,
+                                         const DT *bb, const DT *sc, int64_t tok0, int h, int H,
+                                         int len, int tid) {
+        const int64_t rk = (int64_t)H * DK, rv = (int64_t)H * DV;
+        k.load(kk + (tok0 * H + h) * DK, rk, len, tid);
+        q.load(qq + (tok0 * H + h) * DK, rk, len, tid);
+        v.load(vv + (tok0 * H + h) * DV, rv, len, tid);
+        o.load(oo + (tok0 * H + h) * DV, rv, len, tid);
+        s.load(sc, DK, DV, tid);
+        b = tid < len ? to_f32(bb[(tok0 + tid) * H + h]) : 0.f;
+    }
+};
 
 template <typename DT, int DK, int DV, int C>
 __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const DT *__restrict__ dout, const float *__restrict__ dST,
-    const float *__restrict__ hs, DT *__restrict__ dq, DT *__restrict__ dk, DT *__restrict__ dv,
+    const DT *__restrict__ hs, DT *__restrict__ dq, DT *__restrict__ dk, DT *__restrict__ dv,
     DT *__restrict__ dbeta, float *__restrict__ dS0, int T, int H) {
     typedef BwdCfg<DT, DK, DV, C> G;
-    constexpr int NW = G::NW, NT = G::NT, KT = G::KT;
-    constexpr int LDK = G::LDK, LDV = G::LDV, LDS_ = G::LDS_, LDC = G::LDC;
+    constexpr int NW = G::NW, NT = G::NT, KT = G::KT, VT = G::VT;
+    constexpr int LDK = G::LDK, LDV = G::LDV, LDS_ = G::LDS_, LDSK = G::LDSK, LDC = G::LDC;
     __shared__ __attribute__((aligned(16))) BwdSmem<DT, DK, DV, C> sm;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -199,7 +254,6 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
     const int b = (int)(head / H), h = (int)(head % H);
     const int N = (T + C - 1) / C;
     const int nthr = 64 * NW;
-    const int64_t rk = (int64_t)H * DK, rv = (int64_t)H * DV;  // token strides
 
     // upper tiles of the C x C matrices stay zero
     for (int i = tid; i < C * LDC; i += nthr) {
@@ -213,21 +267,29 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                     : zero4();
     }
 
+    // inputs of the next chunk to process travel in registers one chunk ahead
+    ChunkPrefetch<DT, DK, DV, C> pf;
+    if (N > 0) {
+        const int t0 = (N - 1) * C;
+        pf.load(k, q, v, dout, beta, hs + (head * N + N - 1) * DV * DK, (int64_t)b * T + t0, h, H,
+                min(C, T - t0), tid);
+    }
     for (int c = N - 1; c >= 0; --c) {
         const int t0 = c * C, len = min(C, T - t0);
         const int64_t tok0 = (int64_t)b * T + t0;
         __syncthreads();
         // ---------------------------------------------------------------- load
-        stage_rows(sm.Ks, LDK, k + (tok0 * H + h) * DK, rk, C, len, DK, tid, nthr);
-        stage_rows(sm.Qs, LDK, q + (tok0 * H + h) * DK, rk, C, len, DK, tid, nthr);
-        stage_rows(sm.Vs, LDV, v + (tok0 * H + h) * DV, rv, C, len, DV, tid, nthr);
-        stage_rows(sm.Os, LDV, dout + (tok0 * H + h) * DV, rv, C, len, DV, tid, nthr);
-        for (int t = tid; t < C; t += nthr) sm.betas[t] = t < len ? to_f32(beta[(tok0 + t) * H + h]) : 0.f;
-        // S_c^T of this wave's columns (tile s: S^T[16s + 4g + i][v0 + r])
-        f32x4 St[KT];
-        const float *hc = hs + ((head * N + c) * DV + v0 + r) * DK;
-#pragma unroll
-        for (int s = 0; s < KT; ++s) St[s] = *reinterpret_cast<const f32x4 *>(hc + 16 * s + 4 * g);
+        pf.k.store(sm.Ks, LDK, tid);
+        pf.q.store(sm.Qs, LDK, tid);
+        pf.v.store(sm.Vs, LDV, tid);
+        pf.o.store(sm.Os, LDV, tid);
+        pf.s.store(sm.Sb, LDSK, tid);
+        if (tid < C) sm.betas[tid] = pf.b;
+        if (c > 0) {
+            const int tp = (c - 1) * C;
+            pf.load(k, q, v, dout, beta, hs + (head * N + c - 1) * DV * DK, (int64_t)b * T + tp, h,
+                    H, min(C, T - tp), tid);
+        }
         __syncthreads();
 
         // ---------------------------------------------------- Gram and inverse
@@ -239,7 +301,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
             while (jj > ti) { jj -= ti + 1; ++ti; }
             const int tj = jj;
             f32x4 acc = zero4();
-            tile_rr(acc, isP ? sm.Qs : sm.Ks, LDK, 16 * ti, sm.Ks, LDK, 16 * tj, 0, DK, lane);
+            tile_rr<DT, KT>(acc, isP ? sm.Qs : sm.Ks, LDK, 16 * ti, sm.Ks, LDK, 16 * tj, 0, lane);
             if (isP) {
                 put_tile(sm.Pm, LDC, 16 * ti, 16 * tj, acc, lane, [](int x, int y) { return x >= y; });
             } else {
@@ -285,19 +347,18 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
         // ------------------------------------------- per-wave value columns
         f32x4 R[NT], E[NT], Z[NT];
         {
-            // R = V - K S_c^T
+            // R = V - K S_c^T (S_c rows of this wave's columns as B^T)
             typename Frag<DT>::k16 fs[KT];
 #pragma unroll
-            for (int s = 0; s < KT; ++s) cvt4(St[s], fs[s]);
+            for (int s = 0; s < KT; ++s) frag_rows(sm.Sb, LDSK, v0, 16 * s, lane, fs[s]);
 #pragma unroll
             for (int mt = 0; mt < NT; ++mt) {
                 f32x4 x = zero4();
-                typename Frag<DT>::k16 fk;
+                typename Frag<DT>::k16 fk[KT];
 #pragma unroll
-                for (int s = 0; s < KT; ++s) {
-                    frag_rows(sm.Ks, LDK, 16 * mt, 16 * s, lane, fk);
-                    mk<DT>(x, fk, fs[s]);
-                }
+                for (int s = 0; s < KT; ++s) frag_rows(sm.Ks, LDK, 16 * mt, 16 * s, lane, fk[s]);
+#pragma unroll
+                for (int s = 0; s < KT; ++s) mk<DT>(x, fk[s], fs[s]);
                 typename Frag<DT>::k16 fvv;
                 frag_cols16(sm.Vs, LDV, 16 * mt, v0, lane, fvv);
 #pragma unroll
@@ -337,11 +398,11 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                     frag_cols16(sm.Os, LDV, 16 * kt, v0, lane, fo);
                     mk<DT>(dE[mt], fa, fo);
                 }
+                typename Frag<DT>::k16 fks[KT];
 #pragma unroll
-                for (int s = 0; s < KT; ++s) {
-                    frag_rows(sm.Ks, LDK, 16 * mt, 16 * s, lane, fa);
-                    mk<DT>(dE[mt], fa, fd[s]);
-                }
+                for (int s = 0; s < KT; ++s) frag_rows(sm.Ks, LDK, 16 * mt, 16 * s, lane, fks[s]);
+#pragma unroll
+                for (int s = 0; s < KT; ++s) mk<DT>(dE[mt], fks[s], fd[s]);
             }
             typename Frag<DT>::k16 fde[NT];
 #pragma unroll
@@ -397,30 +458,41 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                 Z[mt] = dvv;  // keep dV
             }
         }
-        // dS update (keep dS_{c+1} for dK), and publish S_c^T for dQ, dK
-        f32x4 Dold[KT];
+        // publish S_c^T and dS_{c+1}^T (this wave's columns) for dQ, dK; then
+        // the dS update
+        f32x4 Dold[G::DBUF ? 1 : KT];
+        if constexpr (!G::DBUF) {
+#pragma unroll
+            for (int s2 = 0; s2 < KT; ++s2) Dold[s2] = Dt[s2];
+        }
         {
-            typename Frag<DT>::k16 fdv[NT];
+#pragma unroll
+            for (int s = 0; s < KT; ++s)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if constexpr (G::DBUF)
+                        sm.Db[(16 * s + 4 * g + i) * LDS_ + v0 + r] = from_f32<DT>(Dt[s][i]);
+                }
+            typename Frag<DT>::k16 fdv[NT], fo[NT];
 #pragma unroll
             for (int mt = 0; mt < NT; ++mt) {
                 f32x4 nz = -Z[mt];
                 cvt4(nz, fdv[mt]);
+                frag_cols16(sm.Os, LDV, 16 * mt, v0, lane, fo[mt]);
             }
 #pragma unroll
             for (int s = 0; s < KT; ++s) {
-                Dold[s] = Dt[s];
-                typename Frag<DT>::k16 fa, fo;
+                typename Frag<DT>::k16 fa[NT], fb[NT];
 #pragma unroll
                 for (int kt = 0; kt < NT; ++kt) {
-                    frag_cols16(sm.Qs, LDK, 16 * kt, 16 * s, lane, fa);
-                    frag_cols16(sm.Os, LDV, 16 * kt, v0, lane, fo);
-                    mk<DT>(Dt[s], fa, fo);
-                    frag_cols16(sm.Ks, LDK, 16 * kt, 16 * s, lane, fa);
-                    mk<DT>(Dt[s], fa, fdv[kt]);
+                    frag_cols16(sm.Qs, LDK, 16 * kt, 16 * s, lane, fa[kt]);
+                    frag_cols16(sm.Ks, LDK, 16 * kt, 16 * s, lane, fb[kt]);
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sm.Sb[(16 * s + 4 * g + i) * LDS_ + v0 + r] = from_f32<DT>(St[s][i]);
+                for (int kt = 0; kt < NT; ++kt) {
+                    mk<DT>(Dt[s], fa[kt], fo[kt]);
+                    mk<DT>(Dt[s], fb[kt], fdv[kt]);
+                }
             }
         }
         __syncthreads();
@@ -432,7 +504,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
             while (jj > ti) { jj -= ti + 1; ++ti; }
             const int tj = jj;
             f32x4 acc = zero4();
-            tile_rr(acc, isD ? sm.Os : sm.Rb, LDV, 16 * ti, sm.Es, LDV, 16 * tj, 0, DV, lane);
+            tile_rr<DT, VT>(acc, isD ? sm.Os : sm.Rb, LDV, 16 * ti, sm.Es, LDV, 16 * tj, 0, lane);
             if (isD) {
                 put_tile(sm.Dm, LDC, 16 * ti, 16 * tj, acc, lane, [](int x, int y) { return x >= y; });
             } else {
@@ -458,48 +530,63 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
 
         // ------------------------------------------------------- dQ and dK
         constexpr int NO = NT * KT;  // output tiles of each
-        f32x4 dKa[(NO + NW - 1) / NW];
+        constexpr int NU = (NO + NW - 1) / NW;
+        f32x4 dKa[G::DBUF ? 1 : NU];
 #pragma unroll
-        for (int u = 0; u < (NO + NW - 1) / NW; ++u) {
+        for (int u = 0; u < NU; ++u) {
             const int o = w + u * NW;
-            if (o >= NO) break;
-            const int mt = o / KT, j = o % KT;
-            // dQ = dO S_c + Dm K
-            f32x4 aq = zero4();
-            tile_rr(aq, sm.Os, LDV, 16 * mt, sm.Sb, LDS_, 16 * j, 0, DV, lane);
-            tile_rc(aq, sm.Dm, LDC, 16 * mt, sm.Ks, LDK, 16 * j, 0, 16 * (mt + 1), lane);
+            if (o < NO) {
+                const int mt = o / KT, j = o % KT;
+                // dQ = dO S_c + Dm K   (Dm is zero above the diagonal)
+                f32x4 aq = zero4();
+                tile_rc<DT, VT>(aq, sm.Os, LDV, 16 * mt, sm.Sb, LDSK, 16 * j, 0, lane);
+                tile_rc<DT, NT>(aq, sm.Dm, LDC, 16 * mt, sm.Ks, LDK, 16 * j, 0, lane);
+                // dK = -dV S_c + E dS_{c+1} + Gs K + Dm^T Q
+                f32x4 ak = zero4();
+                tile_rc<DT, VT>(ak, sm.Rb, LDV, 16 * mt, sm.Sb, LDSK, 16 * j, 0, lane);
+                ak = -ak;
+                if constexpr (G::DBUF)
+                    tile_rr<DT, VT>(ak, sm.Es, LDV, 16 * mt, sm.Db, LDS_, 16 * j, 0, lane);
+                tile_rc<DT, NT>(ak, sm.Gs, LDC, 16 * mt, sm.Ks, LDK, 16 * j, 0, lane);
+                tile_cc<DT, NT>(ak, sm.Dm, LDC, 16 * mt, sm.Qs, LDK, 16 * j, 0, lane);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * mt + 4 * g + i;
-                if (t < len) dq[((tok0 + t) * H + h) * DK + 16 * j + r] = from_f32<DT>(aq[i]);
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * mt + 4 * g + i;
+                    if (t < len) dq[((tok0 + t) * H + h) * DK + 16 * j + r] = from_f32<DT>(aq[i]);
+                }
+                if constexpr (G::DBUF) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = 16 * mt + 4 * g + i;
+                        if (t < len) dk[((tok0 + t) * H + h) * DK + 16 * j + r] = from_f32<DT>(ak[i]);
+                    }
+                } else {
+                    dKa[u] = ak;
+                }
             }
-            // dK (first part) = -dV S_c + Gs K + Dm^T Q
-            f32x4 ak = zero4();
-            tile_rr(ak, sm.Rb, LDV, 16 * mt, sm.Sb, LDS_, 16 * j, 0, DV, lane);
-            ak = -ak;
-            tile_rc(ak, sm.Gs, LDC, 16 * mt, sm.Ks, LDK, 16 * j, 0, C, lane);
-            tile_cc(ak, sm.Dm, LDC, 16 * mt, sm.Qs, LDK, 16 * j, 16 * mt, C, lane);
-            dKa[u] = ak;
         }
-        __syncthreads();
-        // dS_{c+1}^T into Sb, then dK += E dS_{c+1}
+        if constexpr (!G::DBUF) {
+            // second pass: dS_{c+1} replaces S_c, then dK += E dS_{c+1}
+            __syncthreads();
 #pragma unroll
-        for (int s = 0; s < KT; ++s)
+            for (int s2 = 0; s2 < KT; ++s2)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                sm.Sb[(16 * s + 4 * g + i) * LDS_ + v0 + r] = from_f32<DT>(Dold[s][i]);
-        __syncthreads();
+                for (int i = 0; i < 4; ++i)
+                    sm.Sb[(v0 + r) * LDSK + 16 * s2 + 4 * g + i] = from_f32<DT>(Dold[s2][i]);
+            __syncthreads();
 #pragma unroll
-        for (int u = 0; u < (NO + NW - 1) / NW; ++u) {
-            const int o = w + u * NW;
-            if (o >= NO) break;
-            const int mt = o / KT, j = o % KT;
-            f32x4 ak = dKa[u];
-            tile_rr(ak, sm.Es, LDV, 16 * mt, sm.Sb, LDS_, 16 * j, 0, DV, lane);
+            for (int u = 0; u < NU; ++u) {
+                const int o = w + u * NW;
+                if (o < NO) {
+                    const int mt = o / KT, j = o % KT;
+                    f32x4 ak = dKa[u];
+                    tile_rc<DT, VT>(ak, sm.Es, LDV, 16 * mt, sm.Sb, LDSK, 16 * j, 0, lane);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * mt + 4 * g + i;
-                if (t < len) dk[((tok0 + t) * H + h) * DK + 16 * j + r] = from_f32<DT>(ak[i]);
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = 16 * mt + 4 * g + i;
+                        if (t < len) dk[((tok0 + t) * H + h) * DK + 16 * j + r] = from_f32<DT>(ak[i]);
+                    }
+                }
             }
         }
     }
@@ -520,7 +607,7 @@ hipError_t launch_bwd_cfg(const ChunkBwdArgs &a, hipStream_t stream) {
                            dim3(DV * 4), 0, stream, static_cast<const DT *>(a.q),
                            static_cast<const DT *>(a.k), static_cast<const DT *>(a.v),
                            static_cast<const DT *>(a.beta), static_cast<const DT *>(a.dout),
-                           a.dS_T, a.h, static_cast<DT *>(a.dq), static_cast<DT *>(a.dk),
+                           a.dS_T, static_cast<const DT *>(a.h), static_cast<DT *>(a.dq), static_cast<DT *>(a.dk),
                            static_cast<DT *>(a.dv), static_cast<DT *>(a.dbeta), a.dS0,
                            (int)a.T, (int)a.H);
         return hipGetLastError();

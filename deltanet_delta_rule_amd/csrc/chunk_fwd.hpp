@@ -820,12 +820,18 @@ __device__ __forceinline__ void state_path(const DT *Ks, const DT *Qs, const DT 
 }
 
 // A state tile row (this lane's row r, keys in state_col order) to row-major
-// memory at `row` (the row's first element).
-template <int KSD, int ND>
-__device__ __forceinline__ void store_state_row(float *row, const f32x4 *Sacc, int g) {
+// memory at `row` (the row's first element), in DT (the checkpoints of the
+// backward, which uses them only as DT product operands).
+template <int KSD, int ND, typename DT>
+__device__ __forceinline__ void store_state_row(DT *row, const f32x4 *Sacc, int g) {
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
-        *reinterpret_cast<f32x4 *>(row + state_col<KSD>(dt, g)) = Sacc[dt];
+    for (int dt = 0; dt < ND; ++dt) {
+        if constexpr (sizeof(DT) == 4) {
+            *reinterpret_cast<f32x4 *>(row + state_col<KSD>(dt, g)) = Sacc[dt];
+        } else {
+            *reinterpret_cast<u32x2 *>(row + state_col<KSD>(dt, g)) = pk4_bf16(Sacc[dt]);
+        }
+    }
 }
 
 // Common per-workgroup addressing: (b, h, value tile) of this workgroup with
@@ -1182,7 +1188,7 @@ template <typename DT, int DK, int C, int NW, bool GATED, bool L2>
 __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4 + 1, NW / 4 + 1))) void chunk_fwd_ws_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const float *__restrict__ gl, const float *S0,
-    DT *__restrict__ o, float *S_T, float *__restrict__ hs, const int *__restrict__ cu, int T,
+    DT *__restrict__ o, float *S_T, DT *__restrict__ hs, const int *__restrict__ cu, int T,
     int H, int Dv, int nvt, float scale) {
     typedef ChunkCfg<DT, DK, C, NW> G;
     constexpr int NT = G::NT, ND = G::ND;
@@ -1283,7 +1289,7 @@ template <typename DT, int DK, int C, int NW, bool GATED, bool L2>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_fwd_serial_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const float *__restrict__ gl, const float *S0,
-    DT *__restrict__ o, float *S_T, float *__restrict__ hs, const int *__restrict__ cu, int T,
+    DT *__restrict__ o, float *S_T, DT *__restrict__ hs, const int *__restrict__ cu, int T,
     int H, int Dv, int nvt, float scale) {
     typedef ChunkCfg<DT, DK, C, NW> G;
     constexpr int ND = G::ND;
@@ -1351,11 +1357,13 @@ hipError_t launch_cfg(const ChunkFwdArgs &a, hipStream_t stream) {
     DT *o = static_cast<DT *>(a.o);
     if constexpr (ws_fits<DT, DK, C, NW, GATED, L2>()) {
         hipLaunchKernelGGL((chunk_fwd_ws_kernel<DT, DK, C, NW, GATED, L2>), dim3((unsigned)grid),
-                           dim3(128 * NW), 0, stream, q, k, v, beta, a.g, a.S0, o, a.S_T, a.h, a.cu,
+                           dim3(128 * NW), 0, stream, q, k, v, beta, a.g, a.S0, o, a.S_T,
+                           static_cast<DT *>(a.h), a.cu,
                            (int)a.T, (int)a.H, a.Dv, nvt, a.scale);
     } else {
         hipLaunchKernelGGL((chunk_fwd_serial_kernel<DT, DK, C, NW, GATED, L2>), dim3((unsigned)grid),
-                           dim3(64 * NW), 0, stream, q, k, v, beta, a.g, a.S0, o, a.S_T, a.h, a.cu,
+                           dim3(64 * NW), 0, stream, q, k, v, beta, a.g, a.S0, o, a.S_T,
+                           static_cast<DT *>(a.h), a.cu,
                            (int)a.T, (int)a.H, a.Dv, nvt, a.scale);
     }
     return hipGetLastError();

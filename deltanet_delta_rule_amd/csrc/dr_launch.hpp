@@ -14,13 +14,14 @@ namespace dr {
 // batch row of T tokens (packed variable-length input); scale multiplies the
 // outputs; l2 normalises the rows of q and k inside the kernel.  o may be
 // nullptr (no outputs written); h, when set, receives each chunk's incoming
-// state, [B,H,N,Dv,Dk] fp32 with N = ceil(T / chunk) (no packed sequences).
+// state, [B,H,N,Dv,Dk] in the input dtype with N = ceil(T / chunk) (no
+// packed sequences).
 struct ChunkFwdArgs {
     const void *q, *k, *v, *beta;
     const float *g, *S0;
     void *o;
     float *S_T;
-    float *h;
+    void *h;
     const int *cu;
     int64_t B, T, H;
     int Dk, Dv, chunk;
@@ -35,7 +36,8 @@ hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, bool bf16, hipStream_t stream
 // dS_T and dS0 may be nullptr.
 struct ChunkBwdArgs {
     const void *q, *k, *v, *beta, *dout;
-    const float *dS_T, *h;
+    const float *dS_T;
+    const void *h;
     void *dq, *dk, *dv, *dbeta;
     float *dS0;
     int64_t B, T, H;

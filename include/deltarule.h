@@ -263,7 +263,8 @@ dr_status delta_rule_recurrent_step_ex(const void *q, const void *k, const void 
  * of the paperlayer summary of arXiv:2406.06484, section 3: the forward
  * states of every chunk are kept and the chunk-internal quantities
  * recomputed).  The call first reruns the forward pass to store each chunk's
- * incoming state in `workspace`, then walks the chunks in reverse.
+ * incoming state in `workspace` (in `dtype`, the precision the backward's
+ * products use it in), then walks the chunks in reverse.
  *
  *   q, k, v, beta, S0   the forward inputs, as in delta_rule_chunk_fwd
  *   workspace           device memory of at least
