@@ -15,6 +15,9 @@ Contents
 ``gated_delta_rule_ref``
     The same loop with a scalar forget gate alpha_t = exp(g_t) applied to the
     whole state before each token's prediction (the gated variant).
+``kda_ref``
+    The per-key-channel decay variant (Kimi Delta Attention): column j of the
+    state decays by exp(gk_t[j]) before each token's prediction.
 ``delta_rule_bwd_ref``
     Gradients with respect to q, k, v, beta, S0 (and g for the gated rule)
     by the chain rule through the recurrence in reverse token order, in fp64
@@ -71,6 +74,9 @@ def _load():
     lib.ref_delta_rule_f64.restype = ctypes.c_int
     lib.ref_delta_rule_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp,
                                        i64, i64, i64, i64, i64, ctypes.c_int]
+    lib.ref_kda_f64.restype = ctypes.c_int
+    lib.ref_kda_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp,
+                                i64, i64, i64, i64, i64, ctypes.c_int]
     lib.ref_delta_rule_bwd_f64.restype = ctypes.c_int
     lib.ref_delta_rule_bwd_f64.argtypes = [dp] * 14 + [i64, i64, i64, i64, i64, ctypes.c_int]
     lib.ref_gated_delta_rule_f64.restype = ctypes.c_int
@@ -151,6 +157,25 @@ def gated_delta_rule_ref(q, k, v, beta, g, S0=None, nthreads: int = 1):
     return o, st
 
 
+def kda_ref(q, k, v, beta, gk, S0=None, nthreads: int = 1):
+    """The per-channel-decay recurrence (Kimi Delta Attention) in fp64 on the
+    CPU: before each token, column j of the state (key channel j) is
+    multiplied by exp(gk_t[j]), then the token is predicted, corrected and
+    written as in ``delta_rule_ref``.  gk is ``[B,T,H,Dk]``; the rest as
+    ``delta_rule_ref``."""
+    q, k, v, beta, s0, (B, T, H, Dk, Dv) = _check(q, k, v, beta, S0)
+    gk = _as_f64(gk)
+    if gk.shape != (B, T, H, Dk):
+        raise ValueError(f"gk must be [B,T,H,Dk]={B, T, H, Dk}, got {gk.shape}")
+    o = np.zeros((B, T, H, Dv), dtype=np.float64)
+    st = np.zeros((B, H, Dv, Dk), dtype=np.float64)
+    rc = _load().ref_kda_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gk), _ptr(s0),
+                             _ptr(o), _ptr(st), B, T, H, Dk, Dv, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle failed with code {rc}")
+    return o, st
+
+
 def delta_rule_bwd_ref(q, k, v, beta, do, S0=None, dS_T=None, g=None, nthreads: int = 1):
     """Gradients of L = sum <do, o> + <dS_T, S_T> through the recurrence in
     fp64 on the CPU (``ref_delta_rule_bwd.c``: the chain rule through each
@@ -195,5 +220,5 @@ def l2norm_rows(x, eps: float = 1e-6):
     return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
 
 
-__all__ = ["build", "delta_rule_ref", "gated_delta_rule_ref", "delta_rule_bwd_ref",
+__all__ = ["build", "delta_rule_ref", "gated_delta_rule_ref", "kda_ref", "delta_rule_bwd_ref",
            "l2norm_rows"]

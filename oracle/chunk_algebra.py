@@ -146,6 +146,50 @@ def gated_chunk_forward(q, k, v, beta, g, S0=None, chunk=64):
     return o, st
 
 
+def kda_chunk_step(S, Q, K, V, beta, gk):
+    """Advance one chunk of the per-channel-decay recurrence (KDA) from its
+    incoming state S, as the hada.io digest's section "Chunkwise KDA" states
+    it: cumulative per-channel decays from the chunk boundary, provisional
+    errors against the decayed incoming state, couplings
+    rho_ij = beta_i k_j^T D_{j+1:i} k_i, a unit lower-triangular solve, the
+    end-of-chunk state S D_{0:L-1} + E^T K_end and the outputs with the
+    diagonal included.  gk is the chunk's [L, Dk] log decay.  Returns
+    (O_c, E_c, S_next)."""
+    S, Q, K, V, beta, gk = (_f64(x) for x in (S, Q, K, V, beta, gk))
+    L = K.shape[0]
+    b = np.cumsum(gk, axis=0)                        # [L, Dk] log of D_{0:i}
+    dec = np.exp(b[:, None, :] - b[None, :, :])      # [i, j, d]: D_{j+1:i}
+    E_bar = beta[:, None] * (V - (K * np.exp(b)) @ S.T)
+    R = np.tril(beta[:, None] * np.einsum("jd,id,ijd->ij", K, K, dec), -1)
+    E = solve_triangular(np.eye(L) + R, E_bar, lower=True, unit_diagonal=True)
+    K_end = K * np.exp(b[-1][None, :] - b)           # keys decayed to the chunk end
+    S_next = S * np.exp(b[-1])[None, :] + E.T @ K_end
+    A_qk = np.tril(np.einsum("jd,id,ijd->ij", K, Q, dec))
+    O = (Q * np.exp(b)) @ S.T + A_qk @ E
+    return O, E, S_next
+
+
+def kda_chunk_forward(q, k, v, beta, gk, S0=None, chunk=64):
+    """KDA chunkwise forward over the op layout (gk [B,T,H,Dk]).  Returns
+    (o, S_T) in fp64."""
+    q, k, v, beta, gk = (_f64(x) for x in (q, k, v, beta, gk))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[3]
+    s0 = None if S0 is None else _f64(S0)
+    o = np.zeros((B, T, H, Dv))
+    st = np.zeros((B, H, Dv, Dk))
+    for bb in range(B):
+        for h in range(H):
+            S = np.zeros((Dv, Dk)) if s0 is None else s0[bb, h].copy()
+            for c0 in range(0, T, chunk):
+                sl = slice(c0, min(c0 + chunk, T))
+                o[bb, sl, h], _, S = kda_chunk_step(S, q[bb, sl, h], k[bb, sl, h],
+                                                    v[bb, sl, h], beta[bb, sl, h],
+                                                    gk[bb, sl, h])
+            st[bb, h] = S
+    return o, st
+
+
 def chunk_forward(q, k, v, beta, S0=None, chunk=64):
     """Chunkwise forward over the op layout: q,k [B,T,H,Dk], v [B,T,H,Dv],
     beta [B,T,H], S0 [B,H,Dv,Dk] or None.  Returns (o, S_T) in fp64."""

@@ -50,6 +50,19 @@
  * "Gated DeltaNet" (S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t
  * k_t^T).  alpha_t = exp(g_t) is evaluated with the C library's exp in fp64;
  * g_t = 0 gives alpha_t = 1 exactly, i.e. the ungated recurrence bit for bit.
+ *
+ * Per-channel variant (ref_kda_f64, Kimi Delta Attention): gk [B,T,H,Dk]
+ * holds the log decay of every key channel; the forget step scales column j
+ * of the state (key channel j) by exp(gk_t[j]):
+ *
+ *       S   = S Diag(exp(gk_t))     forget, per key channel
+ *       p   = S k_t ... as above
+ *
+ * Source: hada.io digest, section "Kimi Delta Attention : attenuation par
+ * canal" (decay S_{t-1} D_t with D_t = Diag(alpha_t), then predict, correct,
+ * write, read; the key channels are the columns of the state).  The read
+ * there also scales q by d_k^{-1/2}; here, as for the other rules, o = S q and
+ * callers pass the scale they want.
  */
 #include <math.h>
 #include <pthread.h>
@@ -58,7 +71,7 @@
 #include <string.h>
 
 typedef struct {
-    const double *q, *k, *v, *beta, *g, *S0;
+    const double *q, *k, *v, *beta, *g, *gk, *S0;
     double *o, *S_T;
     int64_t B, T, H, Dk, Dv;
     int64_t next; /* next (b,h) pair to take; shared work counter */
@@ -88,6 +101,13 @@ static void one_head(const oracle_job *J, int64_t b, int64_t h, double *S, doubl
             const double at = exp(J->g[row]);
             for (int64_t i = 0; i < Dv * Dk; ++i)
                 S[i] = at * S[i];
+        }
+        /* forget per key channel: column j of S times exp(gk_t[j]) (KDA) */
+        if (J->gk) {
+            const double *gt = J->gk + row * Dk;
+            for (int64_t i = 0; i < Dv; ++i)
+                for (int64_t j = 0; j < Dk; ++j)
+                    S[i * Dk + j] = exp(gt[j]) * S[i * Dk + j];
         }
 
         /* u = beta_t (v_t - S k_t), with S the (decayed) state before this
@@ -137,15 +157,15 @@ static void *worker(void *arg)
 }
 
 static int run(const double *q, const double *k, const double *v, const double *beta,
-               const double *g, const double *S0, double *o, double *S_T, int64_t B,
-               int64_t T, int64_t H, int64_t Dk, int64_t Dv, int nthreads)
+               const double *g, const double *gk, const double *S0, double *o, double *S_T,
+               int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int nthreads)
 {
     if (!q || !k || !v || !beta || !o || B < 0 || T < 0 || H < 0 || Dk < 1 ||
         Dv < 1)
         return -1;
     if (nthreads < 1)
         nthreads = 1;
-    oracle_job J = {q, k, v, beta, g, S0, o, S_T, B, T, H, Dk, Dv, 0, 0};
+    oracle_job J = {q, k, v, beta, g, gk, S0, o, S_T, B, T, H, Dk, Dv, 0, 0};
     if (B * H == 0)
         return 0;
     if (nthreads > B * H)
@@ -179,7 +199,7 @@ int ref_delta_rule_f64(const double *q, const double *k, const double *v,
                        double *S_T, int64_t B, int64_t T, int64_t H,
                        int64_t Dk, int64_t Dv, int nthreads)
 {
-    return run(q, k, v, beta, NULL, S0, o, S_T, B, T, H, Dk, Dv, nthreads);
+    return run(q, k, v, beta, NULL, NULL, S0, o, S_T, B, T, H, Dk, Dv, nthreads);
 }
 
 /* The gated recurrence (g = log alpha, [B,T,H], required); otherwise as above. */
@@ -190,5 +210,16 @@ int ref_gated_delta_rule_f64(const double *q, const double *k, const double *v,
 {
     if (!g)
         return -1;
-    return run(q, k, v, beta, g, S0, o, S_T, B, T, H, Dk, Dv, nthreads);
+    return run(q, k, v, beta, g, NULL, S0, o, S_T, B, T, H, Dk, Dv, nthreads);
+}
+
+/* The per-channel (KDA) recurrence (gk = log decay per key channel,
+ * [B,T,H,Dk], required); otherwise as above. */
+int ref_kda_f64(const double *q, const double *k, const double *v, const double *beta,
+                const double *gk, const double *S0, double *o, double *S_T, int64_t B,
+                int64_t T, int64_t H, int64_t Dk, int64_t Dv, int nthreads)
+{
+    if (!gk)
+        return -1;
+    return run(q, k, v, beta, NULL, gk, S0, o, S_T, B, T, H, Dk, Dv, nthreads);
 }

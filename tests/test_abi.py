@@ -284,8 +284,9 @@ def test_step_ex_unsupported_and_empty(lib):
 # ---------------------------------------------------------------- backward
 def test_backward_workspace_size(lib):
     f = lib.delta_rule_chunk_bwd_workspace_bytes
-    # bf16: 32-token chunks; fp32: 16-token chunks; one fp32 state per chunk and head
-    assert f(2, 100, 3, 64, 32, dr.DR_BF16) == 2 * 3 * 4 * 32 * 64 * 4
+    # bf16: 32-token chunks, bf16 states; fp32: 16-token chunks, fp32 states;
+    # one state per chunk and head
+    assert f(2, 100, 3, 64, 32, dr.DR_BF16) == 2 * 3 * 4 * 32 * 64 * 2
     assert f(2, 100, 3, 64, 32, dr.DR_F32) == 2 * 3 * 7 * 32 * 64 * 4
     assert f(1, 0, 1, 16, 16, dr.DR_BF16) == 0
     assert f(1, 10, 1, 24, 16, dr.DR_BF16) == 0   # unsupported size
