@@ -74,11 +74,12 @@ def chunk_work(w):
 
 def decode_bytes(w):
     """HBM bytes of one decode step: S read and written (fp32), q, k, v, beta
-    read and o written in the input dtype, plus the fp32 log gate when gated."""
+    read and o written in the input dtype, plus the fp32 log gate when gated
+    (one per head, or one per key channel with per-channel decay)."""
     e = 2 if w.dtype == "bf16" else 4
     bh = w.B * w.H
-    return bh * (8 * w.Dv * w.Dk + e * (2 * w.Dk + w.Dv + 1) + e * w.Dv
-                 + (4 if w.gate_amax > 0 else 0))
+    gate = 0 if w.gate_amax <= 0 else (4 * w.Dk if w.kda else 4)
+    return bh * (8 * w.Dv * w.Dk + e * (2 * w.Dk + w.Dv + 1) + e * w.Dv + gate)
 
 
 def source_digest():
@@ -158,7 +159,10 @@ def bench_decode(torch, dr, W, reps=3, name="decode"):
 
     def run():
         for t in range(w.T):
-            if d["g"] is None:
+            if d.get("gk") is not None:
+                dr.kda_recurrent_step(d["q"][t], d["k"][t], d["v"][t], d["beta"][t], d["gk"][t],
+                                      S, o=outs[t])
+            elif d["g"] is None:
                 dr.delta_rule_recurrent_step(d["q"][t], d["k"][t], d["v"][t], d["beta"][t], S,
                                              o=outs[t])
             else:
@@ -181,7 +185,8 @@ def bench_decode(torch, dr, W, reps=3, name="decode"):
     gbs = decode_bytes(w) / per_step / 1e9
     return {
         "workload": (f"{w.name} B{w.B} H{w.H} d{w.Dk}, {w.T} steps, bf16 in, fp32 state"
-                     + (", log gates fp32" if w.gate_amax > 0 else "")),
+                     + ("" if w.gate_amax <= 0 else
+                        ", per-channel log decay fp32" if w.kda else ", log gates fp32")),
         "tokens_per_s": w.B * w.T / t,
         "us_per_step": per_step * 1e6,
         "hbm_gbs_algorithmic": gbs,
@@ -385,6 +390,9 @@ def main():
         out["gated"] = {"chunk": bench_gated_chunk(torch, dr, W)}
         if not args.no_decode:
             out["gated"]["decode"] = bench_decode(torch, dr, W, name="gated_decode")
+        if not args.no_decode:
+            log("per-key-channel decay (KDA): 256 decode steps")
+            out["kda"] = {"decode": bench_decode(torch, dr, W, name="kda_decode")}
         log("in-kernel q/k L2 norm: layer shape chunked forward")
         out["qk_l2norm"] = {"chunk": bench_gated_chunk(torch, dr, W, name="layer_1p3b", l2=True)}
     if not args.no_backward:

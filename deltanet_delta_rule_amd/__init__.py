@@ -31,6 +31,7 @@ __all__ = [
     "gated_delta_rule_chunk_fwd",
     "gated_delta_rule_recurrent_step",
     "delta_rule_chunk_bwd",
+    "kda_recurrent_step",
     "delta_rule_status_string",
     "delta_rule_version",
     "DeltaRuleError",
@@ -55,7 +56,8 @@ class dr_chunk_opts(ctypes.Structure):
 
 class dr_step_opts(ctypes.Structure):
     """``dr_step_opts`` of include/deltarule.h."""
-    _fields_ = [("g", ctypes.c_void_p), ("scale", ctypes.c_float), ("flags", ctypes.c_uint32)]
+    _fields_ = [("g", ctypes.c_void_p), ("scale", ctypes.c_float), ("flags", ctypes.c_uint32),
+                ("gk", ctypes.c_void_p)]
 
 
 class DeltaRuleError(RuntimeError):
@@ -253,7 +255,7 @@ def gated_delta_rule_chunk_fwd(q, k, v, beta, g, S0=None, *, chunk: int = 64,
                        scale, cu_seqlens, use_qk_l2norm_in_kernel)
 
 
-def _step_call(gated, q, k, v, beta, g, S, o, stream, scale=None, l2norm=False):
+def _step_call(gated, q, k, v, beta, g, S, o, stream, scale=None, l2norm=False, gk=None):
     torch = _torch()
     dev = q.device
     if dev.type != "cuda":
@@ -268,6 +270,8 @@ def _step_call(gated, q, k, v, beta, g, S, o, stream, scale=None, l2norm=False):
     _need(beta, "beta", (B, H), dt, dev)
     if gated:
         _need(g, "g", (B, H), torch.float32, dev)
+    if gk is not None:
+        _need(gk, "gk", (B, H, Dk), torch.float32, dev)
     _need(S, "S", (B, H, Dv, Dk), torch.float32, dev)
     if o is None:
         o = torch.empty((B, H, Dv), dtype=dt, device=dev)
@@ -275,7 +279,7 @@ def _step_call(gated, q, k, v, beta, g, S, o, stream, scale=None, l2norm=False):
         _need(o, "o", (B, H, Dv), dt, dev)
     lib = load_library()
     common = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta))
-    if scale is None and not l2norm:
+    if scale is None and not l2norm and gk is None:
         if gated:
             st = lib.gated_delta_rule_recurrent_step(*common, _ptr(g), _ptr(S), _ptr(o), B, H,
                                                      Dk, Dv, _dtype_code(q), _stream(dev, stream))
@@ -285,7 +289,8 @@ def _step_call(gated, q, k, v, beta, g, S, o, stream, scale=None, l2norm=False):
     else:
         opts = dr_step_opts(g=g.data_ptr() if gated else None,
                             scale=1.0 if scale is None else float(scale),
-                            flags=DR_QK_L2NORM if l2norm else 0)
+                            flags=DR_QK_L2NORM if l2norm else 0,
+                            gk=None if gk is None else gk.data_ptr())
         st = lib.delta_rule_recurrent_step_ex(*common, _ptr(S), _ptr(o), B, H, Dk, Dv,
                                               ctypes.byref(opts), _dtype_code(q),
                                               _stream(dev, stream))
@@ -350,3 +355,13 @@ def delta_rule_chunk_bwd(q, k, v, beta, do, S0=None, dS_T=None, *, workspace=Non
         B, T, H, Dk, Dv, code, _stream(dev, stream))
     _check(st)
     return out
+
+
+def kda_recurrent_step(q, k, v, beta, gk, S, *, o=None, scale=None,
+                       use_qk_l2norm_in_kernel=False, stream=None):
+    """One decode token of Kimi Delta Attention: as
+    ``delta_rule_recurrent_step`` plus gk ``[B,H,Dk]`` float32, the log decay
+    of each key channel (column j of S is scaled by exp(gk[j]) before the
+    token)."""
+    return _step_call(False, q, k, v, beta, None, S, o, stream, scale, use_qk_l2norm_in_kernel,
+                      gk)

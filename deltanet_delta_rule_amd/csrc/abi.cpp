@@ -111,7 +111,7 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
 dr_status recurrent_step(const void *q, const void *k, const void *v, const void *beta,
                          const float *g, bool gated, float *S, void *o, int64_t B, int64_t H,
                          int64_t Dk, int64_t Dv, float scale, bool l2, dr_dtype dtype,
-                         void *stream) {
+                         void *stream, const float *gk = nullptr) {
     if (dtype != DR_F32 && dtype != DR_BF16) return DR_ERR_INVALID_ARG;
     if (B < 0 || H < 0 || Dk < 0 || Dv < 0) return DR_ERR_INVALID_ARG;
     if (!(scale == scale) || scale - scale != 0.f) return DR_ERR_INVALID_ARG;  // NaN or inf
@@ -125,6 +125,7 @@ dr_status recurrent_step(const void *q, const void *k, const void *v, const void
 
     if (!q || !k || !v || !beta || !S || !o) return DR_ERR_INVALID_ARG;
     if (gated && !g) return DR_ERR_INVALID_ARG;
+    if (gk && (gated || !aligned16(gk))) return DR_ERR_INVALID_ARG;  // one decay kind
     // q, k and S are read in 16-byte vectors; v, beta and o element-wise
     if (!aligned16(q) || !aligned16(k) || !aligned16(S)) return DR_ERR_INVALID_ARG;
     if (!aligned_to(v, esz) || !aligned_to(beta, esz) || !aligned_to(o, esz))
@@ -132,13 +133,14 @@ dr_status recurrent_step(const void *q, const void *k, const void *v, const void
     if (g && !aligned_to(g, 4)) return DR_ERR_INVALID_ARG;
     const Span so{o, bh * Dv * esz}, ss{S, ns * 4};
     const Span in[] = {{q, bh * Dk * esz}, {k, bh * Dk * esz}, {v, bh * Dv * esz},
-                       {beta, bh * esz}, {gated ? g : nullptr, bh * 4}};
+                       {beta, bh * esz}, {gated ? g : nullptr, bh * 4},
+                       {gk, bh * Dk * 4}};
     if (overlaps(so, ss)) return DR_ERR_INVALID_ARG;
     for (const Span &s : in)
         if (overlaps(so, s) || overlaps(ss, s)) return DR_ERR_INVALID_ARG;
 
-    const dr::StepArgs a{q, k, v, beta, gated ? g : nullptr, S, o, bh, (int)Dk, (int)Dv, scale,
-                         l2};
+    const dr::StepArgs a{q,  k,       v,       beta,  gated ? g : nullptr, S, o,
+                         bh, (int)Dk, (int)Dv, scale, l2,                  gk};
     return hip_status(
         dr::launch_recurrent_step(a, dtype == DR_BF16, static_cast<hipStream_t>(stream)));
 }
@@ -263,7 +265,7 @@ dr_status delta_rule_recurrent_step_ex(const void *q, const void *k, const void 
     const dr_step_opts &x = opts ? *opts : d;
     if (x.flags & ~uint32_t(DR_QK_L2NORM)) return DR_ERR_INVALID_ARG;  // unknown flags
     return recurrent_step(q, k, v, beta, x.g, x.g != nullptr, S, o, B, H, Dk, Dv, x.scale,
-                          (x.flags & DR_QK_L2NORM) != 0, dtype, stream);
+                          (x.flags & DR_QK_L2NORM) != 0, dtype, stream, x.gk);
 }
 
 size_t delta_rule_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk,
@@ -296,6 +298,6 @@ const char *delta_rule_status_string(dr_status status) {
 
 int delta_rule_last_hip_error(void) { return g_last_hip_error; }
 
-int delta_rule_version(void) { return 20400; }
+int delta_rule_version(void) { return 20500; }
 
 }  // extern "C"

@@ -50,7 +50,8 @@ int chunk_bwd_chunk(bool bf16);
 
 // Arguments of the single-token decode step (state updated in place).  g is
 // the log forget gate [B,H] (fp32) of the gated rule, or nullptr; scale
-// multiplies the outputs; l2 normalises q and k in the kernel.
+// multiplies the outputs; l2 normalises q and k in the kernel; gk, when set
+// (with g unset), is the per-key-channel log decay [B,H,Dk] (KDA).
 struct StepArgs {
     const void *q, *k, *v, *beta;
     const float *g;
@@ -60,6 +61,7 @@ struct StepArgs {
     int Dk, Dv;
     float scale;
     bool l2;
+    const float *gk;
 };
 
 hipError_t launch_recurrent_step(const StepArgs &a, bool bf16, hipStream_t stream);

@@ -48,7 +48,11 @@ __device__ __forceinline__ float row_sum(float x) {
 // gated layer on houmin.site "infra/delta-net"); the row's lanes together
 // hold all of q and k, so the norms are two more lane reductions.
 // scale multiplies the output.
-template <typename DT, int DK, int PASSES, bool GATED, bool L2>
+// KDA (Kimi Delta Attention, hada.io digest section "Kimi Delta Attention :
+// attenuation par canal"): g is the per-key-channel log decay [B,H,Dk] and
+// column j of the state decays by exp(g[j]); each lane holds 8 columns of a
+// row, so it applies its 8 factors.
+template <typename DT, int DK, int PASSES, bool GATED, bool L2, bool KDA = false>
 __global__ __launch_bounds__(256) void recurrent_step_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const float *__restrict__ g, float *__restrict__ S,
@@ -79,6 +83,12 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
     }
     const float b = to_f32(beta[head]);
     const float a = GATED ? __expf(g[head]) : 1.f;
+    float ak[8];
+    if constexpr (KDA) {
+        load8(g + head * DK + 8 * sub, ak);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ak[i] = __expf(ak[i]);
+    }
 
     float s[PASSES][8];
     float vr[PASSES];
@@ -91,6 +101,10 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
             if (GATED) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) s[p][i] *= a;
+            }
+            if constexpr (KDA) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) s[p][i] *= ak[i];
             }
             vr[p] = to_f32(v[head * Dv + row[p]]);
         } else {
@@ -122,7 +136,7 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
     }
 }
 
-template <typename DT, int DK, bool GATED, bool L2>
+template <typename DT, int DK, bool GATED, bool L2, bool KDA = false>
 hipError_t launch_step(const StepArgs &x, hipStream_t stream) {
     constexpr int LPR = DK / 8;
     constexpr int RPP = 256 / LPR;
@@ -130,16 +144,19 @@ hipError_t launch_step(const StepArgs &x, hipStream_t stream) {
     const int rows_per_wg = RPP * PASSES;
     const int wg_per_head = (x.Dv + rows_per_wg - 1) / rows_per_wg;
     const int64_t grid = x.BH * wg_per_head;
-    hipLaunchKernelGGL((recurrent_step_kernel<DT, DK, PASSES, GATED, L2>), dim3((unsigned)grid),
-                       dim3(256), 0, stream, static_cast<const DT *>(x.q),
+    hipLaunchKernelGGL((recurrent_step_kernel<DT, DK, PASSES, GATED, L2, KDA>),
+                       dim3((unsigned)grid), dim3(256), 0, stream, static_cast<const DT *>(x.q),
                        static_cast<const DT *>(x.k), static_cast<const DT *>(x.v),
-                       static_cast<const DT *>(x.beta), x.g, x.S, static_cast<DT *>(x.o), x.Dv,
-                       wg_per_head, x.scale);
+                       static_cast<const DT *>(x.beta), KDA ? x.gk : x.g, x.S,
+                       static_cast<DT *>(x.o), x.Dv, wg_per_head, x.scale);
     return hipGetLastError();
 }
 
 template <typename DT, int DK>
 hipError_t dispatch_opts(const StepArgs &x, hipStream_t stream) {
+    if (x.gk)
+        return x.l2 ? launch_step<DT, DK, false, true, true>(x, stream)
+                    : launch_step<DT, DK, false, false, true>(x, stream);
     if (x.g)
         return x.l2 ? launch_step<DT, DK, true, true>(x, stream)
                     : launch_step<DT, DK, true, false>(x, stream);

@@ -23,6 +23,10 @@ oracle can be fed from it.  Every tensor is drawn in fp32 on the CPU from a
   "infra/delta-net", section "Gated DeltaNet": alpha = exp(-exp(A_log)
   softplus(W_alpha x + dt_bias)) with A = exp(A_log) drawn from U(0,16) and
   dt_bias = 1; a stands in for W_alpha x);
+* KDA workloads (kda=True) draw a per (token, head, key channel) instead, so
+  the log decay gk = -A softplus(a + 1) is a vector over the key channels
+  (hada.io digest, section "Kimi Delta Attention : attenuation par canal":
+  the scalar gate becomes a diagonal over the key dimension);
 * q, k, v, beta are then rounded once to the workload dtype (round to nearest
   even); S0 and g stay fp32.
 
@@ -35,6 +39,7 @@ Named workloads (sizes are the whole job on one GPU):
 ``decode``        B128 H16 d128, 256 single-token steps, bf16, S0 != 0
 ``gated_layer_1p3b``  the layer_1p3b shape with the gated rule (A up to 16)
 ``gated_decode``  the decode workload with the gated rule
+``kda_decode``    the decode workload with per-key-channel decay (A up to 1)
 """
 from __future__ import annotations
 
@@ -61,6 +66,7 @@ class Workload:
     seed: int
     decode: bool = False
     gate_amax: float = 0.0  # > 0: gated rule, per-head A ~ U(0, gate_amax)
+    kda: bool = False       # with gate_amax > 0: one log decay per key channel
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -94,6 +100,10 @@ WORKLOADS = {
                              Dv=128, chunk=1, dtype="bf16", feature="l2",
                              beta_scale=1.0, s0_std=0.02, seed=BASE_SEED + 6,
                              decode=True, gate_amax=16.0),
+    "kda_decode": Workload("kda_decode", B=128, H=16, T=256, Dk=128,
+                           Dv=128, chunk=1, dtype="bf16", feature="l2",
+                           beta_scale=1.0, s0_std=0.02, seed=BASE_SEED + 7,
+                           decode=True, gate_amax=1.0, kda=True),
 }
 
 
@@ -112,7 +122,7 @@ def generate(w: Workload) -> dict:
 
     chunk workloads: q, k [B,T,H,Dk]; v [B,T,H,Dv]; beta [B,T,H] in the
     workload dtype; S0 [B,H,Dv,Dk] fp32 or None; g [B,T,H] fp32 (gated
-    workloads) or None.
+    workloads) or None; gk [B,T,H,Dk] fp32 (KDA workloads) or None.
     decode workloads: the same with the leading two axes read as
     [steps, B] (q, k [steps,B,H,Dk] ...), i.e. step-major.
     """
@@ -128,11 +138,15 @@ def generate(w: Workload) -> dict:
                                     dtype=torch.float32)
     else:
         S0 = None
-    gl = None
+    gl = gk = None
     if w.gate_amax > 0:
         A = w.gate_amax * torch.rand(w.H, generator=g, dtype=torch.float32)
-        a = torch.randn(*lead, w.H, generator=g, dtype=torch.float32)
-        gl = (-A * torch.nn.functional.softplus(a + 1.0)).contiguous()
+        if w.kda:
+            a = torch.randn(*lead, w.H, w.Dk, generator=g, dtype=torch.float32)
+            gk = (-A[:, None] * torch.nn.functional.softplus(a + 1.0)).contiguous()
+        else:
+            a = torch.randn(*lead, w.H, generator=g, dtype=torch.float32)
+            gl = (-A * torch.nn.functional.softplus(a + 1.0)).contiguous()
     q = _features(q_raw, w.feature)
     k = _features(k_raw, w.feature)
     beta = w.beta_scale * torch.sigmoid(beta_raw)
@@ -145,6 +159,8 @@ def generate(w: Workload) -> dict:
         "S0": S0,
         "g": gl,
     }
+    if gk is not None:
+        out["gk"] = gk
     return out
 
 

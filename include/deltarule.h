@@ -232,12 +232,17 @@ dr_status gated_delta_rule_recurrent_step(const void *q, const void *k, const vo
  * Options of delta_rule_recurrent_step_ex (zero-initialise, then set
  * scale = 1): g ([B,H] fp32 log forget gate, or NULL for the plain rule),
  * scale (finite output scale) and flags (0 or DR_QK_L2NORM), with the
- * meanings they have in dr_chunk_opts.
+ * meanings they have in dr_chunk_opts; gk ([B,H,Dk] fp32, 16-byte aligned,
+ * or NULL): the per-key-channel log decay of Kimi Delta Attention (hada.io
+ * digest, section "Kimi Delta Attention : attenuation par canal"): before
+ * the token, column j of S (key channel j) is multiplied by exp(gk[j]).
+ * g and gk are exclusive (both set: DR_ERR_INVALID_ARG).
  */
 typedef struct dr_step_opts {
     const float *g;
     float scale;
     uint32_t flags;
+    const float *gk;
 } dr_step_opts;
 
 /*
@@ -295,7 +300,8 @@ int delta_rule_last_hip_error(void);
 
 /* Library version as major*10000 + minor*100 + patch (2.0.0: the gated
  * entry points; 2.1.0: delta_rule_chunk_fwd_ex; 2.2.0: DR_QK_L2NORM; 2.3.0:
- * delta_rule_recurrent_step_ex; 2.4.0: delta_rule_chunk_bwd). */
+ * delta_rule_recurrent_step_ex; 2.4.0: delta_rule_chunk_bwd; 2.5.0: per-channel
+ * decay (gk) in dr_step_opts). */
 int delta_rule_version(void);
 
 #ifdef __cplusplus

@@ -9,7 +9,7 @@ import os
 import numpy as np
 import torch
 
-from oracle import delta_rule_ref, gated_delta_rule_ref
+from oracle import delta_rule_ref, gated_delta_rule_ref, kda_ref
 
 # fp32 inputs: 1e-4; bf16 inputs: 2e-2 (fp32 state), both relative to max|ref|.
 TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
@@ -41,7 +41,8 @@ def to_np(t):
 
 def oracle_heads(x, heads):
     """Oracle on a subset of (b, h) pairs of a chunk workload's inputs (the
-    gated oracle when the inputs carry log gates g).
+    gated oracle when the inputs carry log gates g, the KDA oracle when they
+    carry per-channel log decays gk).
 
     Returns (o [T, n, Dv], S_T [n, Dv, Dk]) for the n pairs in `heads`, by
     stacking the selected heads into one batch row (heads are independent).
@@ -52,7 +53,9 @@ def oracle_heads(x, heads):
     S0 = None
     if x["S0"] is not None:
         S0 = np.stack([x["S0"][b, h].double().numpy() for b, h in heads])[None]
-    if x.get("g") is not None:
+    if x.get("gk") is not None:
+        o, st = kda_ref(q, k, v, beta, sel(x["gk"]), S0, nthreads=threads())
+    elif x.get("g") is not None:
         o, st = gated_delta_rule_ref(q, k, v, beta, sel(x["g"]), S0, nthreads=threads())
     else:
         o, st = delta_rule_ref(q, k, v, beta, S0, nthreads=threads())
@@ -60,7 +63,10 @@ def oracle_heads(x, heads):
 
 
 def oracle_all(x):
-    """Oracle on every head of a chunk workload's inputs (gated when g is set)."""
+    """Oracle on every head of a chunk workload's inputs (gated when g is set,
+    KDA when gk is set)."""
+    if x.get("gk") is not None:
+        return kda_ref(x["q"], x["k"], x["v"], x["beta"], x["gk"], x["S0"], nthreads=threads())
     if x.get("g") is not None:
         return gated_delta_rule_ref(x["q"], x["k"], x["v"], x["beta"], x["g"], x["S0"],
                                     nthreads=threads())

@@ -259,24 +259,28 @@ def _sx(lib, opts=None, q=P[0], k=P[1], v=P[2], beta=P[3], S=P[4], o=P[5], B=2, 
 
 
 def test_step_options_struct_layout():
-    assert ctypes.sizeof(dr.dr_step_opts) == 16
+    assert ctypes.sizeof(dr.dr_step_opts) == 24
     assert dr.dr_step_opts.scale.offset == 8 and dr.dr_step_opts.flags.offset == 12
+    assert dr.dr_step_opts.gk.offset == 16
 
 
 @pytest.mark.parametrize("kw, call", [
     (dict(scale=float("nan")), {}), (dict(scale=float("-inf")), {}),
     (dict(flags=4), {}), (dict(g=ODD.value), {}), (dict(g=P[4].value), {}),
     (dict(scale=2.0), dict(S=None)), (dict(flags=1), dict(q=MISALIGNED)),
+    (dict(gk=MISALIGNED.value), {}),                       # per-channel decay misaligned
+    (dict(gk=P[4].value), {}),                             # overlaps S
+    (dict(gk=P[7].value, g=P[6].value), {}),               # both decay kinds
 ])
 def test_step_ex_rejects_invalid(lib, kw, call):
-    o = dr.dr_step_opts(g=None, scale=1.0, flags=0)
+    o = dr.dr_step_opts(g=None, scale=1.0, flags=0, gk=None)
     for n, val in kw.items():
         setattr(o, n, val)
     assert _sx(lib, o, **call) == dr.DR_ERR_INVALID_ARG
 
 
 def test_step_ex_unsupported_and_empty(lib):
-    o = dr.dr_step_opts(g=None, scale=1.0, flags=1)
+    o = dr.dr_step_opts(g=None, scale=1.0, flags=1, gk=None)
     assert _sx(lib, o, Dk=24) == dr.DR_ERR_UNSUPPORTED
     assert _sx(lib, o, B=0) == dr.DR_OK
 
