@@ -237,6 +237,37 @@ def bench_gated_chunk(torch, dr, W, reps=20, name="gated_layer_1p3b", l2=False):
     }
 
 
+def bench_kda_sequence(torch, dr, W, reps=5):
+    """kda_fwd (token-serial schedule) on the layer shape with per-channel
+    decay: mean call time with HIP events on the launch stream."""
+    w = W.get("layer_1p3b", gate_amax=1.0, kda=True)
+    x = W.generate(w)
+    dev = torch.device("cuda:0")
+    d = {n: (None if t is None else t.to(dev)) for n, t in x.items()}
+    o = torch.empty((w.B, w.T, w.H, w.Dv), dtype=w.torch_dtype, device=dev)
+    st = torch.empty((w.B, w.H, w.Dv, w.Dk), dtype=torch.float32, device=dev)
+
+    def step():
+        dr.kda_fwd(d["q"], d["k"], d["v"], d["beta"], d["gk"], None, o=o, S_T=st)
+
+    step()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    launch_s = sum(a.elapsed_time(b) for a, b in ev) / reps / 1e3
+    return {
+        "workload": (f"layer_1p3b B{w.B} H{w.H} T{w.T} d{w.Dk}, per-channel log decay fp32, "
+                     "token-serial schedule"),
+        "tokens_per_s": w.B * w.T / launch_s,
+        "mean_launch_us": round(launch_s * 1e6, 2),
+    }
+
+
 def bench_backward(torch, dr, W, reps=10):
     """delta_rule_chunk_bwd on the layer shape: the checkpointing forward pass
     plus the reverse pass, with upstream gradients for o and S_T (mean time per
@@ -393,6 +424,8 @@ def main():
         if not args.no_decode:
             log("per-key-channel decay (KDA): 256 decode steps")
             out["kda"] = {"decode": bench_decode(torch, dr, W, name="kda_decode")}
+        log("per-key-channel decay (KDA): layer shape sequence forward")
+        out.setdefault("kda", {})["sequence"] = bench_kda_sequence(torch, dr, W)
         log("in-kernel q/k L2 norm: layer shape chunked forward")
         out["qk_l2norm"] = {"chunk": bench_gated_chunk(torch, dr, W, name="layer_1p3b", l2=True)}
     if not args.no_backward:

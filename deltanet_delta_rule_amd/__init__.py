@@ -32,6 +32,8 @@ __all__ = [
     "gated_delta_rule_recurrent_step",
     "delta_rule_chunk_bwd",
     "kda_recurrent_step",
+    "kda_fwd",
+    "DR_FUSED_RECURRENT",
     "delta_rule_status_string",
     "delta_rule_version",
     "DeltaRuleError",
@@ -51,7 +53,7 @@ class dr_chunk_opts(ctypes.Structure):
     """``dr_chunk_opts`` of include/deltarule.h."""
     _fields_ = [("g", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
                 ("num_seqs", ctypes.c_int64), ("scale", ctypes.c_float),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("gk", ctypes.c_void_p)]
 
 
 class dr_step_opts(ctypes.Structure):
@@ -164,10 +166,11 @@ def _need(t, name, shape, dtype, device):
 
 
 DR_QK_L2NORM = 1
+DR_FUSED_RECURRENT = 2
 
 
 def _chunk_call(gated, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, stream,
-                scale=None, cu_seqlens=None, l2norm=False):
+                scale=None, cu_seqlens=None, l2norm=False, gk=None, recurrent=False):
     torch = _torch()
     dev = q.device
     if dev.type != "cuda":
@@ -182,6 +185,8 @@ def _chunk_call(gated, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, 
     _need(beta, "beta", (B, T, H), dt, dev)
     if gated:
         _need(g, "g", (B, T, H), torch.float32, dev)
+    if gk is not None:
+        _need(gk, "gk", (B, T, H, Dk), torch.float32, dev)
     nseq = B
     if cu_seqlens is not None:
         if B != 1:
@@ -208,7 +213,7 @@ def _chunk_call(gated, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, 
     lib = load_library()
     common = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta))
     tail = (B, T, H, Dk, Dv, int(chunk))
-    if scale is None and cu_seqlens is None and not l2norm:
+    if scale is None and cu_seqlens is None and not l2norm and gk is None and not recurrent:
         if gated:
             st = lib.gated_delta_rule_chunk_fwd(*common, _ptr(g), _ptr(S0), _ptr(o), _ptr(S_T),
                                                 *tail, _dtype_code(q), _stream(dev, stream))
@@ -220,7 +225,9 @@ def _chunk_call(gated, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, 
                              cu_seqlens=None if cu_seqlens is None else cu_seqlens.data_ptr(),
                              num_seqs=nseq if cu_seqlens is not None else 0,
                              scale=1.0 if scale is None else float(scale),
-                             flags=DR_QK_L2NORM if l2norm else 0)
+                             flags=(DR_QK_L2NORM if l2norm else 0)
+                             | (DR_FUSED_RECURRENT if recurrent else 0),
+                             gk=None if gk is None else gk.data_ptr())
         st = lib.delta_rule_chunk_fwd_ex(*common, _ptr(S0), _ptr(o), _ptr(S_T), *tail,
                                          ctypes.byref(opts), _dtype_code(q),
                                          _stream(dev, stream))
@@ -231,7 +238,7 @@ def _chunk_call(gated, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, 
 def delta_rule_chunk_fwd(q, k, v, beta, S0=None, *, chunk: int = 64,
                          output_final_state: bool = True, o=None, S_T=None,
                          scale=None, cu_seqlens=None, use_qk_l2norm_in_kernel=False,
-                         stream=None):
+                         fused_recurrent=False, stream=None):
     """Chunkwise forward.  q, k ``[B,T,H,Dk]``; v ``[B,T,H,Dv]``; beta
     ``[B,T,H]`` (float32 or bfloat16, all the same dtype, on one GPU);
     S0 ``[B,H,Dv,Dk]`` float32 or None.  Returns ``(o, S_T)``; S_T is None
@@ -240,19 +247,33 @@ def delta_rule_chunk_fwd(q, k, v, beta, S0=None, *, chunk: int = 64,
     the outputs; ``cu_seqlens`` (int32 ``[N+1]`` on the GPU, B = 1) packs N
     sequences, whose states S0 / S_T are then ``[N,H,Dv,Dk]``.
     ``use_qk_l2norm_in_kernel`` normalises the rows of q and k inside the
-    kernel (x / sqrt(sum x^2 + 1e-6))."""
+    kernel (x / sqrt(sum x^2 + 1e-6)).  ``fused_recurrent`` runs the
+    token-serial schedule instead of the chunked one (same results up to
+    rounding; for short sequences)."""
     return _chunk_call(False, q, k, v, beta, None, S0, chunk, output_final_state, o, S_T,
-                       stream, scale, cu_seqlens, use_qk_l2norm_in_kernel)
+                       stream, scale, cu_seqlens, use_qk_l2norm_in_kernel,
+                       recurrent=fused_recurrent)
 
 
 def gated_delta_rule_chunk_fwd(q, k, v, beta, g, S0=None, *, chunk: int = 64,
                                output_final_state: bool = True, o=None, S_T=None,
                                scale=None, cu_seqlens=None, use_qk_l2norm_in_kernel=False,
-                               stream=None):
+                               fused_recurrent=False, stream=None):
     """Chunkwise forward of the gated rule: as ``delta_rule_chunk_fwd`` plus
     g ``[B,T,H]`` float32, the log of each token's forget gate (<= 0)."""
     return _chunk_call(True, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, stream,
-                       scale, cu_seqlens, use_qk_l2norm_in_kernel)
+                       scale, cu_seqlens, use_qk_l2norm_in_kernel, recurrent=fused_recurrent)
+
+
+def kda_fwd(q, k, v, beta, gk, S0=None, *, output_final_state: bool = True, o=None, S_T=None,
+            scale=None, cu_seqlens=None, use_qk_l2norm_in_kernel=False, stream=None):
+    """Forward of Kimi Delta Attention over whole sequences: as
+    ``delta_rule_chunk_fwd`` plus gk ``[B,T,H,Dk]`` float32, the log decay
+    (<= 0) of each key channel at each token (column j of the state is
+    multiplied by exp(gk_t[j]) before token t).  Runs the token-serial
+    schedule."""
+    return _chunk_call(False, q, k, v, beta, None, S0, 64, output_final_state, o, S_T, stream,
+                       scale, cu_seqlens, use_qk_l2norm_in_kernel, gk=gk, recurrent=True)
 
 
 def _step_call(gated, q, k, v, beta, g, S, o, stream, scale=None, l2norm=False, gk=None):

@@ -55,7 +55,7 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
                     const float *g, bool gated, const float *S0, void *o, float *S_T,
                     int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t chunk,
                     const int32_t *cu, int64_t nseq, float scale, bool l2, dr_dtype dtype,
-                    void *stream) {
+                    void *stream, const float *gk = nullptr, bool recurrent = false) {
     if (dtype != DR_F32 && dtype != DR_BF16) return DR_ERR_INVALID_ARG;
     if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0 || chunk < 0) return DR_ERR_INVALID_ARG;
     if (cu && (B != 1 || nseq < 0 || !aligned_to(cu, 4))) return DR_ERR_INVALID_ARG;
@@ -79,8 +79,9 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
 
     if (T > 0 && (!q || !k || !v || !beta || !o)) return DR_ERR_INVALID_ARG;
     if (gated && T > 0 && !g) return DR_ERR_INVALID_ARG;
-    // q, k and the states are read in 16-byte vectors; v, beta and o element-wise
-    const void *vec_ptrs[] = {q, k, S0, S_T};
+    if (gk && gated) return DR_ERR_INVALID_ARG;  // one decay kind
+    // q, k, gk and the states are read in 16-byte vectors; v, beta and o element-wise
+    const void *vec_ptrs[] = {q, k, S0, S_T, gk};
     for (const void *p : vec_ptrs)
         if (p && !aligned16(p)) return DR_ERR_INVALID_ARG;
     const void *elem_ptrs[] = {v, beta, o};
@@ -91,7 +92,7 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
     const Span in[] = {{q, nqk * esz},        {k, nqk * esz},
                        {v, nv * esz},         {beta, nb * esz},
                        {S0, ns * 4},          {gated ? g : nullptr, nb * 4},
-                       {cu, (nseq + 1) * 4}};
+                       {cu, (nseq + 1) * 4},  {gk, nqk * 4}};
     const Span so{o, nv * esz}, sst{S_T, ns * 4};
     for (const Span &s : in) {
         if (T > 0 && overlaps(so, s)) return DR_ERR_INVALID_ARG;
@@ -103,7 +104,7 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
     dr::ChunkFwdArgs a{q,       k,        v,       beta,       gated ? g : nullptr,
                        S0,      o,        S_T,     nullptr,    cu,
                        ns_count, T,       H,       (int)Dk,    (int)Dv,
-                       (int)chunk, scale, l2};
+                       (int)chunk, scale, l2,     gk,       recurrent};
     return hip_status(dr::launch_chunk_fwd(a, dtype == DR_BF16, static_cast<hipStream_t>(stream)));
 }
 
@@ -226,10 +227,11 @@ dr_status delta_rule_chunk_fwd_ex(const void *q, const void *k, const void *v,
     dr_chunk_opts d{};
     d.scale = 1.f;
     const dr_chunk_opts &x = opts ? *opts : d;
-    if (x.flags & ~uint32_t(DR_QK_L2NORM)) return DR_ERR_INVALID_ARG;  // unknown flags
+    if (x.flags & ~uint32_t(DR_QK_L2NORM | DR_FUSED_RECURRENT))
+        return DR_ERR_INVALID_ARG;  // unknown flags
     return chunk_fwd(q, k, v, beta, x.g, x.g != nullptr, S0, o, S_T, B, T, H, Dk, Dv, chunk,
                      x.cu_seqlens, x.num_seqs, x.scale, (x.flags & DR_QK_L2NORM) != 0, dtype,
-                     stream);
+                     stream, x.gk, (x.flags & DR_FUSED_RECURRENT) != 0);
 }
 
 dr_status delta_rule_recurrent_step(const void *q, const void *k,
@@ -298,6 +300,6 @@ const char *delta_rule_status_string(dr_status status) {
 
 int delta_rule_last_hip_error(void) { return g_last_hip_error; }
 
-int delta_rule_version(void) { return 20500; }
+int delta_rule_version(void) { return 20600; }
 
 }  // extern "C"

@@ -6,6 +6,8 @@
 namespace dr {
 
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, bool bf16, hipStream_t stream) {
+    if (a.gk || a.recurrent)  // no checkpoints from the token-serial schedule
+        return a.h ? hipErrorInvalidValue : launch_fused_recurrent(a, bf16, stream);
     if (a.l2)
         return a.g ? launch_chunk_fwd_gated_l2(a, bf16, stream) : launch_chunk_fwd_l2(a, bf16, stream);
     return a.g ? launch_chunk_fwd_gated(a, bf16, stream) : launch_rule<false, false>(a, bf16, stream);

@@ -44,6 +44,28 @@ __device__ __forceinline__ u32x2 pk4_bf16(const f32x4 &x) {
     return u32x2{pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3])};
 }
 
+// x moved between lanes by one DPP pattern (a compile-time dpp_ctrl value).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N consecutive lanes (N = 2, 4, 8 or 16), every
+// lane of a group receiving the group's sum, on DPP row operations instead of
+// LDS permutes: quad permutes for lane xor 1 and xor 2, then the half-row
+// mirror (lane i and 7 - i of each 8) and the row mirror (i and 15 - i of
+// each 16).  Each step adds partial sums over two disjoint lane sets, so the
+// lanes of a group all end with the same value (additions commute).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group of 1..16 lanes");
+    if constexpr (N >= 2) x += dpp_move<0xB1>(x);   // quad_perm [1,0,3,2]
+    if constexpr (N >= 4) x += dpp_move<0x4E>(x);   // quad_perm [2,3,0,1]
+    if constexpr (N >= 8) x += dpp_move<0x141>(x);  // row_half_mirror
+    if constexpr (N >= 16) x += dpp_move<0x140>(x); // row_mirror
+    return x;
+}
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
 

@@ -15,7 +15,9 @@ namespace dr {
 // outputs; l2 normalises the rows of q and k inside the kernel.  o may be
 // nullptr (no outputs written); h, when set, receives each chunk's incoming
 // state, [B,H,N,Dv,Dk] in the input dtype with N = ceil(T / chunk) (no
-// packed sequences).
+// packed sequences).  gk, when set (with g unset), is the per-key-channel log
+// decay [B,T,H,Dk] (KDA); recurrent selects the token-serial schedule.  Both
+// run launch_fused_recurrent, which takes everything above except chunk and h.
 struct ChunkFwdArgs {
     const void *q, *k, *v, *beta;
     const float *g, *S0;
@@ -27,9 +29,12 @@ struct ChunkFwdArgs {
     int Dk, Dv, chunk;
     float scale;
     bool l2;
+    const float *gk = nullptr;
+    bool recurrent = false;
 };
 
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
+hipError_t launch_fused_recurrent(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
 
 // Arguments of the backward of the chunked forward (plain rule).  h holds the
 // checkpoints the forward kernel wrote with chunk = chunk_bwd_chunk(bf16);

@@ -37,9 +37,7 @@ __device__ __forceinline__ void load8(const __bf16 *p, float (&x)[8]) {
 // Sum over the LPR consecutive lanes that share a row (LPR a power of two).
 template <int LPR>
 __device__ __forceinline__ float row_sum(float x) {
-#pragma unroll
-    for (int m = LPR / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, LPR);
-    return x;
+    return group_sum<LPR>(x);
 }
 
 // GATED: the whole row first decays by alpha = exp(g) of its (b, h), then the

@@ -115,7 +115,14 @@ enum {
      * x / sqrt(sum x^2 + 1e-6) (the l2norm of the gated layer on houmin.site
      * "infra/delta-net"; fla's use_qk_l2norm_in_kernel).  q and k are read as
      * given and never written. */
-    DR_QK_L2NORM = 1u
+    DR_QK_L2NORM = 1u,
+    /* Run the token-serial ("fused recurrent") schedule: one pass over the
+     * tokens of each sequence with the state held on chip (hada.io digest,
+     * section "Kernel Triton recurrent fusionne pour le decodage").  Same
+     * results as the chunked schedule up to rounding; the chunk argument is
+     * validated but unused.  Suited to short sequences.  Always used for the
+     * per-channel decay (gk). */
+    DR_FUSED_RECURRENT = 2u
 };
 
 /*
@@ -139,7 +146,15 @@ enum {
  *   scale       finite output scale: o = scale * S_t q_t (the same as
  *               scaling q; the DeltaNet layer passes none, the gated layer
  *               of houmin.site "infra/delta-net" divides q by sqrt(d_k)).
- *   flags       0 or DR_QK_L2NORM.
+ *   flags       0 or a combination of DR_QK_L2NORM and DR_FUSED_RECURRENT.
+ *   gk          [B,T,H,Dk] fp32 (16-byte aligned) per-key-channel log decay,
+ *               or NULL.  Non-NULL selects Kimi Delta Attention (hada.io
+ *               digest, section "Kimi Delta Attention : attenuation par
+ *               canal"): before token t, column j of the state (key channel
+ *               j) is multiplied by exp(gk_t[j]), then the token is
+ *               predicted, corrected, written and read as in the plain rule.
+ *               Exclusive with g (both set: DR_ERR_INVALID_ARG).  Runs the
+ *               token-serial schedule (DR_FUSED_RECURRENT).
  */
 typedef struct dr_chunk_opts {
     const float *g;
@@ -147,6 +162,7 @@ typedef struct dr_chunk_opts {
     int64_t num_seqs;
     float scale;
     uint32_t flags;
+    const float *gk;
 } dr_chunk_opts;
 
 /*
@@ -301,7 +317,8 @@ int delta_rule_last_hip_error(void);
 /* Library version as major*10000 + minor*100 + patch (2.0.0: the gated
  * entry points; 2.1.0: delta_rule_chunk_fwd_ex; 2.2.0: DR_QK_L2NORM; 2.3.0:
  * delta_rule_recurrent_step_ex; 2.4.0: delta_rule_chunk_bwd; 2.5.0: per-channel
- * decay (gk) in dr_step_opts). */
+ * decay (gk) in dr_step_opts; 2.6.0: DR_FUSED_RECURRENT and gk in
+ * dr_chunk_opts). */
 int delta_rule_version(void);
 
 #ifdef __cplusplus

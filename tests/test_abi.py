@@ -211,16 +211,17 @@ def _ex(lib, opts=None, q=P[0], k=P[1], v=P[2], beta=P[3], S0=None, o=P[4], S_T=
 
 
 def _opts(**kw):
-    o = dr.dr_chunk_opts(g=None, cu_seqlens=None, num_seqs=0, scale=1.0, flags=0)
+    o = dr.dr_chunk_opts(g=None, cu_seqlens=None, num_seqs=0, scale=1.0, flags=0, gk=None)
     for name, val in kw.items():
         setattr(o, name, val)
     return o
 
 
 def test_chunk_options_struct_layout():
-    # pointer, pointer, int64, float, uint32: 32 bytes with no padding between
-    assert ctypes.sizeof(dr.dr_chunk_opts) == 32
+    # pointer, pointer, int64, float, uint32, pointer: 40 bytes, no padding
+    assert ctypes.sizeof(dr.dr_chunk_opts) == 40
     assert dr.dr_chunk_opts.scale.offset == 24 and dr.dr_chunk_opts.flags.offset == 28
+    assert dr.dr_chunk_opts.gk.offset == 32
 
 
 @pytest.mark.parametrize("kw, call", [
@@ -231,10 +232,14 @@ def test_chunk_options_struct_layout():
     (dict(cu_seqlens=CU.value, num_seqs=2), dict(S_T=CU)),       # S_T overlaps offsets
     (dict(scale=float("nan")), {}),
     (dict(scale=float("inf")), {}),
-    (dict(flags=2), {}),                                         # unknown flag bit
+    (dict(flags=4), {}),                                         # unknown flag bit
     (dict(flags=0x80000001), {}),
     (dict(g=ODD.value), {}),                                     # gate misaligned
     (dict(g=P[4].value), {}),                                    # gate overlaps o
+    (dict(gk=MISALIGNED.value), {}),                             # channel decay misaligned
+    (dict(gk=P[4].value), {}),                                   # channel decay overlaps o
+    (dict(gk=P[7].value, g=P[6].value), {}),                     # both decay kinds
+    (dict(gk=P[7].value, flags=3), dict(S_T=P[7])),              # S_T overlaps gk
 ])
 def test_chunk_ex_rejects_invalid(lib, kw, call):
     assert _ex(lib, _opts(**kw), **call) == dr.DR_ERR_INVALID_ARG
