@@ -237,9 +237,9 @@ def bench_gated_chunk(torch, dr, W, reps=20, name="gated_layer_1p3b", l2=False):
     }
 
 
-def bench_kda_sequence(torch, dr, W, reps=5):
-    """kda_fwd (token-serial schedule) on the layer shape with per-channel
-    decay: mean call time with HIP events on the launch stream."""
+def bench_kda_sequence(torch, dr, W, reps=10):
+    """kda_fwd (chunked kernel) on the layer shape with per-channel decay:
+    mean call time with HIP events on the launch stream."""
     w = W.get("layer_1p3b", gate_amax=1.0, kda=True)
     x = W.generate(w)
     dev = torch.device("cuda:0")
@@ -261,8 +261,8 @@ def bench_kda_sequence(torch, dr, W, reps=5):
     torch.cuda.synchronize()
     launch_s = sum(a.elapsed_time(b) for a, b in ev) / reps / 1e3
     return {
-        "workload": (f"layer_1p3b B{w.B} H{w.H} T{w.T} d{w.Dk}, per-channel log decay fp32, "
-                     "token-serial schedule"),
+        "workload": (f"layer_1p3b B{w.B} H{w.H} T{w.T} d{w.Dk} chunk 64, bf16 in, "
+                     "per-channel log decay fp32 (A up to 1), fp32 state"),
         "tokens_per_s": w.B * w.T / launch_s,
         "mean_launch_us": round(launch_s * 1e6, 2),
     }

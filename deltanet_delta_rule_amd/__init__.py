@@ -266,14 +266,19 @@ def gated_delta_rule_chunk_fwd(q, k, v, beta, g, S0=None, *, chunk: int = 64,
 
 
 def kda_fwd(q, k, v, beta, gk, S0=None, *, output_final_state: bool = True, o=None, S_T=None,
-            scale=None, cu_seqlens=None, use_qk_l2norm_in_kernel=False, stream=None):
+            scale=None, cu_seqlens=None, use_qk_l2norm_in_kernel=False, fused_recurrent=False,
+            stream=None):
     """Forward of Kimi Delta Attention over whole sequences: as
     ``delta_rule_chunk_fwd`` plus gk ``[B,T,H,Dk]`` float32, the log decay
     (<= 0) of each key channel at each token (column j of the state is
-    multiplied by exp(gk_t[j]) before token t).  Runs the token-serial
-    schedule."""
+    multiplied by exp(gk_t[j]) before token t).  bf16 inputs with Dk = 128 and
+    Dv a multiple of 64 run the chunked kernel (64-token chunks; accurate while
+    gk summed over any 8 consecutive tokens of a channel stays above -40, e.g.
+    gk >= -5); everything else, or ``fused_recurrent=True``, runs the
+    token-serial schedule, which has no such limit."""
     return _chunk_call(False, q, k, v, beta, None, S0, 64, output_final_state, o, S_T, stream,
-                       scale, cu_seqlens, use_qk_l2norm_in_kernel, gk=gk, recurrent=True)
+                       scale, cu_seqlens, use_qk_l2norm_in_kernel, gk=gk,
+                       recurrent=fused_recurrent)
 
 
 def _step_call(gated, q, k, v, beta, g, S, o, stream, scale=None, l2norm=False, gk=None):

@@ -6,6 +6,7 @@
 namespace dr {
 
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, bool bf16, hipStream_t stream) {
+    if (a.gk && !a.h && kda_chunk_supported(a, bf16)) return launch_kda_chunk(a, stream);
     if (a.gk || a.recurrent)  // no checkpoints from the token-serial schedule
         return a.h ? hipErrorInvalidValue : launch_fused_recurrent(a, bf16, stream);
     if (a.l2)

@@ -35,6 +35,10 @@ struct ChunkFwdArgs {
 
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
 hipError_t launch_fused_recurrent(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
+// Chunked KDA (per-channel decay): bf16, d_k = 128, d_v a multiple of 64, no
+// in-kernel L2 norm; other cases run the token-serial kernel.
+bool kda_chunk_supported(const ChunkFwdArgs &a, bool bf16);
+hipError_t launch_kda_chunk(const ChunkFwdArgs &a, hipStream_t stream);
 
 // Arguments of the backward of the chunked forward (plain rule).  h holds the
 // checkpoints the forward kernel wrote with chunk = chunk_bwd_chunk(bf16);

@@ -120,8 +120,8 @@ enum {
      * tokens of each sequence with the state held on chip (hada.io digest,
      * section "Kernel Triton recurrent fusionne pour le decodage").  Same
      * results as the chunked schedule up to rounding; the chunk argument is
-     * validated but unused.  Suited to short sequences.  Always used for the
-     * per-channel decay (gk). */
+     * validated but unused.  Suited to short sequences.  With the
+     * per-channel decay (gk) it is the path for any gk (see gk below). */
     DR_FUSED_RECURRENT = 2u
 };
 
@@ -153,8 +153,17 @@ enum {
  *               canal"): before token t, column j of the state (key channel
  *               j) is multiplied by exp(gk_t[j]), then the token is
  *               predicted, corrected, written and read as in the plain rule.
- *               Exclusive with g (both set: DR_ERR_INVALID_ARG).  Runs the
- *               token-serial schedule (DR_FUSED_RECURRENT).
+ *               Exclusive with g (both set: DR_ERR_INVALID_ARG).  bf16 inputs
+ *               with Dk = 128 and Dv a multiple of 64, without DR_QK_L2NORM
+ *               or DR_FUSED_RECURRENT, run the chunked kernel (64-token
+ *               chunks, same digest, "Chunkwise KDA"; the chunk argument is
+ *               validated but unused).  Its decay ratios are split around a
+ *               reference token per 16-token block, which keeps every factor
+ *               finite and accurate while the sum of gk over any 8
+ *               consecutive tokens of a channel stays above -40 (gk >= -5
+ *               per token guarantees it) and gk <= 0; outside that domain the
+ *               results lose accuracy (nothing overflows).  All other cases
+ *               run the token-serial schedule, exact for any gk.
  */
 typedef struct dr_chunk_opts {
     const float *g;

@@ -1,6 +1,6 @@
 """GPU parity of the token-serial schedule (``DR_FUSED_RECURRENT``:
-``fused_recurrent=True`` on the chunked entry points, and ``kda_fwd``, which
-always runs it) against the fp64 oracles.
+``fused_recurrent=True`` on the chunked entry points and on ``kda_fwd``)
+against the fp64 oracles.
 
 hada.io digest, section "Kernel Triton recurrent fusionne pour le decodage":
 each program owns a slab of one head's state and walks the tokens in order.
@@ -44,7 +44,8 @@ def _work(rule, **kw):
 
 def _run(d, rule, S0, **kw):
     if rule == "kda":
-        return dr.kda_fwd(d["q"], d["k"], d["v"], d["beta"], d["gk"], S0, **kw)
+        return dr.kda_fwd(d["q"], d["k"], d["v"], d["beta"], d["gk"], S0, fused_recurrent=True,
+                          **kw)
     if rule == "gated":
         return dr.gated_delta_rule_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], S0,
                                              fused_recurrent=True, **kw)
@@ -157,7 +158,7 @@ def test_kda_equal_channels_is_the_gated_rule():
     x = W.generate(w)
     d = to_dev(x)
     gk = d["g"][..., None].expand(-1, -1, -1, w.Dk).contiguous()
-    o_k, s_k = dr.kda_fwd(d["q"], d["k"], d["v"], d["beta"], gk, d["S0"])
+    o_k, s_k = dr.kda_fwd(d["q"], d["k"], d["v"], d["beta"], gk, d["S0"], fused_recurrent=True)
     o_g, s_g = _run(d, "gated", d["S0"])
     torch.testing.assert_close(o_k, o_g, rtol=0, atol=0)
     torch.testing.assert_close(s_k, s_g, rtol=0, atol=0)
@@ -198,13 +199,15 @@ def test_packed_gaps_untouched_and_in_place_state():
     S = 0.02 * torch.randn(3, 2, 128, 128, device="cuda")
     S_in = S.clone()
     o = torch.full_like(d["v"], float("nan"))
-    dr.kda_fwd(d["q"], d["k"], d["v"], d["beta"], d["gk"], S, cu_seqlens=cu, o=o, S_T=S)
+    dr.kda_fwd(d["q"], d["k"], d["v"], d["beta"], d["gk"], S, cu_seqlens=cu, o=o, S_T=S,
+               fused_recurrent=True)
     torch.cuda.synchronize()
     assert not torch.isnan(o[:, :60]).any()
     assert torch.isnan(o[:, 60:]).all()
     assert torch.equal(S[1], S_in[1])        # the inverted range is an empty sequence
     sl = {k: (None if t is None else t[:, 20:60].contiguous()) for k, t in d.items()}
-    o2, s2 = dr.kda_fwd(sl["q"], sl["k"], sl["v"], sl["beta"], sl["gk"], S_in[2:3].contiguous())
+    o2, s2 = dr.kda_fwd(sl["q"], sl["k"], sl["v"], sl["beta"], sl["gk"], S_in[2:3].contiguous(),
+                        fused_recurrent=True)
     assert torch.equal(S[2:3], s2)
 
 
@@ -217,7 +220,8 @@ def test_writes_every_output_and_nothing_else():
     sbuf = torch.full((n_s + 2 * G,), float("nan"), dtype=torch.float32, device="cuda")
     o = obuf[G:G + n_o].view(2, 53, 2, 128)
     st = sbuf[G:G + n_s].view(2, 2, 128, 128)
-    dr.kda_fwd(d["q"], d["k"], d["v"], d["beta"], d["gk"], d["S0"], o=o, S_T=st)
+    dr.kda_fwd(d["q"], d["k"], d["v"], d["beta"], d["gk"], d["S0"], o=o, S_T=st,
+               fused_recurrent=True)
     torch.cuda.synchronize()
     assert not torch.isnan(o).any() and not torch.isnan(st).any()
     assert torch.isnan(obuf[:G]).all() and torch.isnan(obuf[-G:]).all()
@@ -227,6 +231,6 @@ def test_writes_every_output_and_nothing_else():
 def test_empty_sequence_copies_state():
     w = _work("kda", H=3, T=0)
     d = to_dev(W.generate(w))
-    o, st = dr.kda_fwd(d["q"], d["k"], d["v"], d["beta"], d["gk"], d["S0"])
+    o, st = dr.kda_fwd(d["q"], d["k"], d["v"], d["beta"], d["gk"], d["S0"], fused_recurrent=True)
     assert o.shape == (1, 0, 3, 128)
     torch.testing.assert_close(st, d["S0"], rtol=0, atol=0)
