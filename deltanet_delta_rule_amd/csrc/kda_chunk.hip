@@ -47,7 +47,10 @@ constexpr int KDA_DK = 128;      // key channels
 constexpr int KDA_DVW = 64;      // value rows per workgroup
 constexpr int KDA_LD = 136;      // row pitch (bf16) of the token x channel tiles
 constexpr int KDA_LDV = 72;      // row pitch (bf16) of the value tile
-constexpr float KDA_EXP_MAX = 80.f;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float KDA_EXP2_MAX = 80.f * LOG2E;  // clamp of growing exponents (log2)
+
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Column operands of row block I start at row 8 I (I + 1) of KC: block I has
 // the 16 (I + 1) tokens 0 .. 16 I + 15.
@@ -83,43 +86,50 @@ __device__ __forceinline__ float hi_bf16(unsigned x) { return __uint_as_float(x 
 // Prefetched inputs of one chunk for one thread.
 struct KdaRegs {
     unsigned k[16], q[16];   // bf16 pairs: channels 2p, 2p + 1 of token 16J + s
-    float2 g[16];            // log decays of the same
+    u32x2 g[16];             // their log decays (fp32 pairs)
     uint4 v[2];              // 8 bf16 value entries each
-    __bf16 beta;
+    unsigned short beta;
 };
 
 struct KdaSeq {
     const __bf16 *q, *k, *v, *beta;
     const float *gk;
+    __bf16 *o;
     int64_t base;  // first token of the sequence in the flattened (batch, time) axis
     int H, h, Dv, vcol0, len;
     __device__ __forceinline__ int64_t row(int t) const { return (base + t) * H + h; }
 };
 
+// Loads of one chunk (tokens t0 .. t0 + 63 of the sequence) through buffer
+// resources that span exactly its valid tokens: offsets are constants per
+// lane and token, and tokens past the end of the sequence load as zeros
+// (k = q = v = 0, gk = 0, beta = 0 leave the state unchanged).
 __device__ __forceinline__ void kda_prefetch(KdaRegs &x, const KdaSeq &sq, int t0, int J,
                                              int p, int tid) {
+    const int nv = min(KDA_C, sq.len - t0);
+    const int64_t r0 = sq.row(t0);
+    const int sk = sq.H * KDA_DK * 2, sg = sq.H * KDA_DK * 4, sv = sq.H * sq.Dv * 2;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(sq.k + r0 * KDA_DK, nv * sk);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(sq.q + r0 * KDA_DK, nv * sk);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(sq.gk + r0 * KDA_DK, nv * sg);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(sq.v + r0 * sq.Dv + sq.vcol0, nv * sv);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(sq.beta + r0, nv * sq.H * 2);
+    // J is uniform over the wave: the token part of each offset goes in the
+    // scalar offset, the lane part (the channel pair) in the vector offset
+    const int Js = __builtin_amdgcn_readfirstlane(J);
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
-        const int t = t0 + 16 * J + s;
-        x.k[s] = x.q[s] = 0u;
-        x.g[s] = make_float2(0.f, 0.f);
-        if (t < sq.len) {  // uniform over the wave
-            const int64_t off = sq.row(t) * KDA_DK + 2 * p;
-            x.k[s] = *reinterpret_cast<const unsigned *>(sq.k + off);
-            x.q[s] = *reinterpret_cast<const unsigned *>(sq.q + off);
-            x.g[s] = *reinterpret_cast<const float2 *>(sq.gk + off);
-        }
+        const int tk = 16 * Js + s;
+        x.k[s] = __builtin_amdgcn_raw_buffer_load_b32(rk, 4 * p, tk * sk, 0);
+        x.q[s] = __builtin_amdgcn_raw_buffer_load_b32(rq, 4 * p, tk * sk, 0);
+        x.g[s] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, 8 * p, tk * sg, 0));
     }
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
         const int u = tid + 256 * n;
-        const int t = t0 + u / 8, c = 8 * (u % 8);
-        x.v[n] = make_uint4(0, 0, 0, 0);
-        if (t < sq.len)
-            x.v[n] = *reinterpret_cast<const uint4 *>(sq.v + sq.row(t) * sq.Dv + sq.vcol0 + c);
+        x.v[n] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, (u / 8) * sv + 16 * (u % 8), 0, 0));
     }
-    x.beta = __bf16(0.f);
-    if (tid < KDA_C && t0 + tid < sq.len) x.beta = sq.beta[sq.row(t0 + tid)];
+    x.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, min(tid, KDA_C - 1) * sq.H * 2, 0, 0);
 }
 
 __global__ __launch_bounds__(256) void kda_chunk_kernel(
@@ -128,9 +138,15 @@ __global__ __launch_bounds__(256) void kda_chunk_kernel(
     __bf16 *__restrict__ o, float *S_T, const int *__restrict__ cu, int T, int H, int Dv,
     float scale) {
     __shared__ KdaSmem sm;
+    // Consecutive workgroup ids go round-robin over the 8 XCDs (each with its
+    // own L2); remap so that the value slices of one head, which read the same
+    // k, q and gk and write the same o rows, run on the same XCD.
+    int wg = blockIdx.x;
+    const int nwg = gridDim.x;
+    if (nwg % 8 == 0) wg = (wg % 8) * (nwg / 8) + wg / 8;
     const int nvb = Dv / KDA_DVW;
-    const int vb = blockIdx.x % nvb;
-    const int64_t seqhead = blockIdx.x / nvb;
+    const int vb = wg % nvb;
+    const int64_t seqhead = wg / nvb;
     const int64_t n = seqhead / H;
     const int h = (int)(seqhead % H);
     int lo = 0, hi = T;
@@ -140,7 +156,7 @@ __global__ __launch_bounds__(256) void kda_chunk_kernel(
         hi = min(max(cu[n + 1], lo), T);
         batch = 0;
     }
-    const KdaSeq sq{q, k, v, beta, gk, batch * T + lo, H, h, Dv, vb * KDA_DVW, hi - lo};
+    const KdaSeq sq{q, k, v, beta, gk, o, batch * T + lo, H, h, Dv, vb * KDA_DVW, hi - lo};
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, r = lane & 15;
@@ -168,66 +184,79 @@ __global__ __launch_bounds__(256) void kda_chunk_kernel(
     for (int c = 0; c < nchunk; ++c) {
         const int t0 = c * KDA_C;
         const int J = wave;
-        // ---- 1. operands: in-block prefix sums of the two channels
+        // ---- 1. operands: in-block prefix sums of the two channels, in log2
+        // units (every exponential below is one exp2)
         float2 bl[16];
         {
             float2 acc = make_float2(0.f, 0.f);
 #pragma unroll
             for (int s = 0; s < 16; ++s) {
-                acc.x += x.g[s].x;
-                acc.y += x.g[s].y;
+                acc.x += __uint_as_float(x.g[s][0]) * LOG2E;
+                acc.y += __uint_as_float(x.g[s][1]) * LOG2E;
                 bl[s] = acc;
             }
         }
         *reinterpret_cast<float2 *>(&sm.tot[J][2 * p]) = bl[15];
         *reinterpret_cast<float2 *>(&sm.mid[J][2 * p]) = bl[7];
-        __syncthreads();
-        float2 offs[4], mI[4];
+        lds_barrier();
         {
+            float2 mI[4];
             float2 run = make_float2(0.f, 0.f);
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
-                offs[I] = run;
                 const float2 md = *reinterpret_cast<const float2 *>(&sm.mid[I][2 * p]);
                 mI[I] = make_float2(run.x + md.x, run.y + md.y);
                 const float2 tt = *reinterpret_cast<const float2 *>(&sm.tot[I][2 * p]);
                 run.x += tt.x;
                 run.y += tt.y;
             }
-            // run = b_last
+            // run = b_last (log2)
             if (J == 0) {
-                sm.gamC[2 * p] = __expf(run.x);
-                sm.gamC[2 * p + 1] = __expf(run.y);
+                sm.gamC[2 * p] = exp2_(run.x);
+                sm.gamC[2 * p + 1] = exp2_(run.y);
             }
-            const float2 off = offs[J], mJ = mI[J];
-            const float2 GJ = make_float2(__expf(mJ.x), __expf(mJ.y));
-            const float2 EJ = make_float2(__expf(run.x - mJ.x), __expf(run.y - mJ.y));
-            float2 F[4];
+            const float2 mJ = mI[J];
+            const float2 GJ = make_float2(exp2_(mJ.x), exp2_(mJ.y));            // Gamma at m_J
+            const float2 EJ = make_float2(exp2_(run.x - mJ.x), exp2_(run.y - mJ.y));
+            float2 F[4];  // exp(m_I - m_J) <= 1 for I > J
 #pragma unroll
             for (int I = 0; I < 4; ++I)
-                F[I] = make_float2(__expf(fminf(mI[I].x - mJ.x, 0.f)), __expf(fminf(mI[I].y - mJ.y, 0.f)));
+                F[I] = make_float2(exp2_(fminf(mI[I].x - mJ.x, 0.f)), exp2_(fminf(mI[I].y - mJ.y, 0.f)));
             const int col = 2 * p;
 #pragma unroll
             for (int s = 0; s < 16; ++s) {
                 const int t = 16 * J + s;
-                const float b0 = off.x + bl[s].x, b1 = off.y + bl[s].y;
-                const float e0 = __expf(fminf(b0 - mJ.x, KDA_EXP_MAX));
-                const float e1 = __expf(fminf(b1 - mJ.y, KDA_EXP_MAX));
-                const float i0 = __expf(fminf(mJ.x - b0, KDA_EXP_MAX));
-                const float i1 = __expf(fminf(mJ.y - b1, KDA_EXP_MAX));
+                // b_t - m_J is the in-block prefix difference: e grows for
+                // s < 7 (rows), ei for s > 7 (columns); only those are clamped
+                const float d0 = bl[s].x - bl[7].x, d1 = bl[s].y - bl[7].y;
+                float e0 = 1.f, e1 = 1.f, i0 = 1.f, i1 = 1.f;
+                if (s < 7) {
+                    e0 = exp2_(fminf(d0, KDA_EXP2_MAX));
+                    e1 = exp2_(fminf(d1, KDA_EXP2_MAX));
+                    i0 = exp2_(-d0);
+                    i1 = exp2_(-d1);
+                } else if (s > 7) {
+                    e0 = exp2_(d0);
+                    e1 = exp2_(d1);
+                    i0 = exp2_(fminf(-d0, KDA_EXP2_MAX));
+                    i1 = exp2_(fminf(-d1, KDA_EXP2_MAX));
+                }
                 const float k0 = lo_bf16(x.k[s]), k1 = hi_bf16(x.k[s]);
                 const float q0 = lo_bf16(x.q[s]), q1 = hi_bf16(x.q[s]);
+                const float g0 = e0 * GJ.x, g1 = e1 * GJ.y;      // Gamma_t
+                const float c0 = k0 * i0, c1 = k1 * i1;          // column operand, block J
                 const int o_t = t * KDA_LD + col;
                 *reinterpret_cast<unsigned *>(sm.KR + o_t) = pk2(k0 * e0, k1 * e1);
                 *reinterpret_cast<unsigned *>(sm.QR + o_t) = pk2(q0 * e0, q1 * e1);
-                *reinterpret_cast<unsigned *>(sm.KT + o_t) = pk2(k0 * e0 * GJ.x, k1 * e1 * GJ.y);
-                *reinterpret_cast<unsigned *>(sm.QT + o_t) = pk2(q0 * e0 * GJ.x, q1 * e1 * GJ.y);
-                *reinterpret_cast<unsigned *>(sm.KE + o_t) = pk2(k0 * i0 * EJ.x, k1 * i1 * EJ.y);
+                *reinterpret_cast<unsigned *>(sm.KT + o_t) = pk2(k0 * g0, k1 * g1);
+                *reinterpret_cast<unsigned *>(sm.QT + o_t) = pk2(q0 * g0, q1 * g1);
+                *reinterpret_cast<unsigned *>(sm.KE + o_t) = pk2(c0 * EJ.x, c1 * EJ.y);
+                *reinterpret_cast<unsigned *>(sm.KC + (kc_base(J) + t) * KDA_LD + col) = pk2(c0, c1);
 #pragma unroll
                 for (int I = 0; I < 4; ++I)
-                    if (I >= J)
+                    if (I > J)
                         *reinterpret_cast<unsigned *>(sm.KC + (kc_base(I) + t) * KDA_LD + col) =
-                            pk2(k0 * i0 * F[I].x, k1 * i1 * F[I].y);
+                            pk2(c0 * F[I].x, c1 * F[I].y);
             }
         }
 #pragma unroll
@@ -235,9 +264,9 @@ __global__ __launch_bounds__(256) void kda_chunk_kernel(
             const int u = tid + 256 * nn;
             *reinterpret_cast<uint4 *>(sm.V + (u / 8) * KDA_LDV + 8 * (u % 8)) = x.v[nn];
         }
-        if (tid < KDA_C) sm.beta[tid] = (float)x.beta;
+        if (tid < KDA_C) sm.beta[tid] = (float)__builtin_bit_cast(__bf16, x.beta);
         if (c + 1 < nchunk) kda_prefetch(x, sq, t0 + KDA_C, wave, p, tid);
-        __syncthreads();
+        lds_barrier();
 
         // ---- 2. G and P blocks, diagonal inverses
         for (int pp = wave; pp < 10; pp += 4) {
@@ -270,7 +299,7 @@ __global__ __launch_bounds__(256) void kda_chunk_kernel(
                 store_fragblk(sm.Pb, pp, lane, aP);
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- 3. state path on this wave's 16 value rows
         {
@@ -307,7 +336,11 @@ __global__ __launch_bounds__(256) void kda_chunk_kernel(
                 E[I] = zero4();
                 mma_k16(E[I], ft, fy);
             }
-            // O_I += sum_{J<=I} P_IJ E_J, then out
+            // O_I += sum_{J<=I} P_IJ E_J, then out (stores past the sequence's
+            // end fall outside the resource and are dropped)
+            const int so = H * Dv * 2;
+            const __amdgpu_buffer_rsrc_t ro =
+                make_rsrc(sq.o + sq.row(t0) * Dv, min(KDA_C, sq.len - t0) * so);
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
 #pragma unroll
@@ -318,10 +351,8 @@ __global__ __launch_bounds__(256) void kda_chunk_kernel(
                     mma_k16(O[I], fa, fe);
                 }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = t0 + 16 * I + 4 * g + e;
-                    if (t < sq.len) o[sq.row(t) * Dv + drow] = (__bf16)(scale * O[I][e]);
-                }
+                for (int e = 0; e < 4; ++e)
+                    buf_store_elem((__bf16)(scale * O[I][e]), ro, (16 * I + 4 * g + e) * so + 2 * drow, 0);
             }
             // S <- S diag(Gamma_last) + (E^T KE)^T, slab by slab
             bf16x8 fE[2];
@@ -359,9 +390,13 @@ __global__ __launch_bounds__(256) void kda_chunk_kernel(
 }  // namespace
 
 bool kda_chunk_supported(const ChunkFwdArgs &a, bool bf16) {
-    // v is read in 16-byte vectors here (the ABI only guarantees element alignment)
+    // v is read in 16-byte vectors here (the ABI only guarantees element
+    // alignment), and one chunk of one head's rows of every input must be
+    // addressable with 32-bit byte offsets
+    const int64_t span = int64_t(KDA_C) * a.H * (a.Dv > 2 * KDA_DK ? 2 * a.Dv : 4 * KDA_DK);
     return bf16 && a.gk && !a.g && !a.l2 && !a.recurrent && a.Dk == KDA_DK &&
-           a.Dv % KDA_DVW == 0 && (reinterpret_cast<uintptr_t>(a.v) & 15) == 0;
+           a.Dv % KDA_DVW == 0 && (reinterpret_cast<uintptr_t>(a.v) & 15) == 0 &&
+           span < INT32_MAX;
 }
 
 hipError_t launch_kda_chunk(const ChunkFwdArgs &a, hipStream_t stream) {
