@@ -286,7 +286,7 @@ __global__ __launch_bounds__(256) void fused_recurrent_kernel(
         stage_load<DT, DK, DECAY>(st, q, k, v, beta, g, sr, 0, min(C::TB, len), row0, Dv);
         stage_store<DT, DK, DECAY>(st, smem);
     }
-    __syncthreads();
+    lds_barrier();
     for (int j = 0; j < nblk; ++j) {
         const int t0 = j * C::TB;
         const int nt = min(C::TB, len - t0);
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256) void fused_recurrent_kernel(
             fr_token<DK, DECAY, L2>(tb, s, sub, live, o + sr.row(t0 + i + 1) * Dv + row, scale);
         }
         if (more) stage_store<DT, DK, DECAY>(st, smem + ((j + 1) & 1) * C::BUF);
-        __syncthreads();
+        lds_barrier();
     }
     if (S_T && live) {
         float4 *dst = reinterpret_cast<float4 *>(S_T + srow);
