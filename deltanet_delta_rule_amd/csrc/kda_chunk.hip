@@ -24,18 +24,24 @@
 // should stay above -40 (per-token gk >= -5 guarantees it); the growing
 // exponents are clamped at 80 so that nothing overflows outside it.
 //
-// Work split.  One workgroup of four waves owns one (sequence, head) and a
-// slice of 64 value rows of S (wave w: rows 16w .. 16w + 15 of the slice, all
-// d_k columns, fp32 in registers in the canonical k order of the matrix-core
-// operands), and walks the chunks in order.  Per chunk:
-//   1. wave J (token block J) and lane p (key channels 2p, 2p + 1) turn the
-//      prefetched k, q and gk of its 16 tokens into the scaled operands in
-//      LDS (prefix sums, with block totals exchanged through LDS);
-//   2. the ten block pairs (I, J <= I) of G and P are shared out over the
-//      waves; diagonal blocks are inverted right away;
-//   3. each wave runs the state path on its 16 value rows: X = (K.Gamma)
-//      S^T, the block substitution for E, O, and the state update.
-// The next chunk's inputs are loaded into registers while steps 2 and 3 run.
+// Work split.  One workgroup of eight waves owns one (sequence, head) and a
+// slice of 64 value rows of S, and walks the chunks in order.  Per chunk:
+//   1. wave w (tokens 8w .. 8w + 7) and lane p (key channels 2p, 2p + 1)
+//      turn the prefetched k, q and gk of its tokens into the scaled
+//      operands in LDS (prefix sums, with half-block sums exchanged through
+//      LDS);
+//   2. the ten 16-token block pairs (I, J <= I) of G and P are shared out over
+//      the waves; diagonal blocks are inverted right away;
+//   3. waves 0-3 (the solvers) each take 16 value rows: X = (K.Gamma) S^T and
+//      the block substitution for E, which they hand to waves 4-7 through
+//      LDS; waves 4-7 (the readers) meanwhile form (Q.Gamma) S^T for the same
+//      rows, then add P E and store O.  Both keep the rows of S in registers
+//      (fp32, the canonical k order of the matrix-core operands) and apply
+//      the same state update from the same bf16 E, so their copies stay
+//      identical.
+// Two waves per SIMD let one wave's exponentials and LDS traffic overlap the
+// other's matrix-core work.  The next chunk's inputs are loaded into
+// registers while steps 2 and 3 run.
 #include "chunk_fwd.hpp"
 
 namespace dr {
@@ -46,7 +52,6 @@ constexpr int KDA_C = 64;        // tokens per chunk
 constexpr int KDA_DK = 128;      // key channels
 constexpr int KDA_DVW = 64;      // value rows per workgroup
 constexpr int KDA_LD = 136;      // row pitch (bf16) of the token x channel tiles
-constexpr int KDA_LDV = 72;      // row pitch (bf16) of the value tile
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float KDA_EXP2_MAX = 80.f * LOG2E;  // clamp of growing exponents (log2)
 
@@ -63,14 +68,13 @@ struct alignas(16) KdaSmem {
     __bf16 KT[KDA_C * KDA_LD];        // k_t Gamma_t               (X)
     __bf16 QT[KDA_C * KDA_LD];        // q_t Gamma_t               (O)
     __bf16 KE[KDA_C * KDA_LD];        // k_t exp(b_last - b_t)     (state update)
-    __bf16 V[KDA_C * KDA_LDV];        // this workgroup's 64 value columns
     __bf16 Gb[6 * FRAG_ELEMS];        // G blocks below the diagonal
     __bf16 Tb[4 * FRAG_ELEMS];        // -T_II diag(beta_I), T_II = (I + diag(beta) G_II)^{-1}
     __bf16 Pb[10 * FRAG_ELEMS];       // P blocks on and below the diagonal
     float beta[KDA_C];
     float gamC[KDA_DK];               // Gamma_last per channel
-    float tot[4][KDA_DK];             // block sums of gk
-    float mid[4][KDA_DK];             // in-block prefix sum at the 8th token
+    float htot[8][KDA_DK];            // sums of gk over each 8-token half block (log2)
+    __bf16 Ex[4][4 * FRAG_ELEMS];     // E of each solver wave, as B-operand fragments
 };
 
 // Block pair p = I (I + 1) / 2 + J of the ten (I, J <= I).
@@ -85,9 +89,8 @@ __device__ __forceinline__ float hi_bf16(unsigned x) { return __uint_as_float(x 
 
 // Prefetched inputs of one chunk for one thread.
 struct KdaRegs {
-    unsigned k[16], q[16];   // bf16 pairs: channels 2p, 2p + 1 of token 16J + s
-    u32x2 g[16];             // their log decays (fp32 pairs)
-    uint4 v[2];              // 8 bf16 value entries each
+    unsigned k[8], q[8];     // bf16 pairs: channels 2p, 2p + 1 of token 8w + s
+    u32x2 g[8];              // their log decays (fp32 pairs)
     unsigned short beta;
 };
 
@@ -103,36 +106,44 @@ struct KdaSeq {
 // Loads of one chunk (tokens t0 .. t0 + 63 of the sequence) through buffer
 // resources that span exactly its valid tokens: offsets are constants per
 // lane and token, and tokens past the end of the sequence load as zeros
-// (k = q = v = 0, gk = 0, beta = 0 leave the state unchanged).
-__device__ __forceinline__ void kda_prefetch(KdaRegs &x, const KdaSeq &sq, int t0, int J,
+// (k = q = v = 0, gk = 0, beta = 0 leave the state unchanged).  The token part
+// of each offset is wave-uniform and goes in the scalar offset.
+__device__ __forceinline__ void kda_prefetch(KdaRegs &x, const KdaSeq &sq, int t0, int w,
                                              int p, int tid) {
     const int nv = min(KDA_C, sq.len - t0);
     const int64_t r0 = sq.row(t0);
-    const int sk = sq.H * KDA_DK * 2, sg = sq.H * KDA_DK * 4, sv = sq.H * sq.Dv * 2;
+    const int sk = sq.H * KDA_DK * 2, sg = sq.H * KDA_DK * 4;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(sq.k + r0 * KDA_DK, nv * sk);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(sq.q + r0 * KDA_DK, nv * sk);
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(sq.gk + r0 * KDA_DK, nv * sg);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(sq.v + r0 * sq.Dv + sq.vcol0, nv * sv);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(sq.beta + r0, nv * sq.H * 2);
-    // J is uniform over the wave: the token part of each offset goes in the
-    // scalar offset, the lane part (the channel pair) in the vector offset
-    const int Js = __builtin_amdgcn_readfirstlane(J);
+    const int ws = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-        const int tk = 16 * Js + s;
+    for (int s = 0; s < 8; ++s) {
+        const int tk = 8 * ws + s;
         x.k[s] = __builtin_amdgcn_raw_buffer_load_b32(rk, 4 * p, tk * sk, 0);
         x.q[s] = __builtin_amdgcn_raw_buffer_load_b32(rq, 4 * p, tk * sk, 0);
         x.g[s] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, 8 * p, tk * sg, 0));
     }
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-        const int u = tid + 256 * n;
-        x.v[n] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, (u / 8) * sv + 16 * (u % 8), 0, 0));
-    }
     x.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, min(tid, KDA_C - 1) * sq.H * 2, 0, 0);
 }
 
-__global__ __launch_bounds__(256) void kda_chunk_kernel(
+// The value entries a solver lane needs, in the D layout of its X tiles:
+// v[t0 + 16 I + 4 g + e][vcol] for I, e = 0..3.
+__device__ __forceinline__ void kda_prefetch_v(unsigned short (&vr)[16], const KdaSeq &sq,
+                                               int t0, int g, int vcol) {
+    const int nv = min(KDA_C, sq.len - t0);
+    const int sv = sq.H * sq.Dv * 2;
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(sq.v + sq.row(t0) * sq.Dv, nv * sv);
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            vr[4 * I + e] = __builtin_amdgcn_raw_buffer_load_b16(
+                rv, (4 * g) * sv + 2 * vcol, (16 * I + e) * sv, 0);
+}
+
+__global__ __launch_bounds__(512) void kda_chunk_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const __bf16 *__restrict__ beta, const float *__restrict__ gk, const float *S0,
     __bf16 *__restrict__ o, float *S_T, const int *__restrict__ cu, int T, int H, int Dv,
@@ -160,9 +171,11 @@ __global__ __launch_bounds__(256) void kda_chunk_kernel(
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, r = lane & 15;
-    const int p = lane;                       // channel pair of the operand step
-    const int drow = vb * KDA_DVW + 16 * wave + r;  // this lane's state row
-    const int64_t srow = (seqhead * Dv + drow) * KDA_DK;
+    const int p = lane;                      // channel pair of the operand step
+    const bool solver = wave < 4;
+    const int vt = wave & 3;                 // value tile of the state step
+    const int vcol = vb * KDA_DVW + 16 * vt + r;   // this lane's state row
+    const int64_t srow = (seqhead * Dv + vcol) * KDA_DK;
 
     // state: slab s (channels 32 s ..), half 0: 32 s + 4 g + e, half 1: + 16
     f32x4 S[4][2];
@@ -179,39 +192,43 @@ __global__ __launch_bounds__(256) void kda_chunk_kernel(
 
     const int nchunk = (sq.len + KDA_C - 1) / KDA_C;
     KdaRegs x;
-    if (nchunk > 0) kda_prefetch(x, sq, 0, wave, p, tid);
+    unsigned short vr[16];
+    if (nchunk > 0) {
+        kda_prefetch(x, sq, 0, wave, p, tid);
+        if (solver) kda_prefetch_v(vr, sq, 0, g, vcol);
+    }
 
+    const int J = wave >> 1, hf = wave & 1;  // token block and half of the operand step
     for (int c = 0; c < nchunk; ++c) {
         const int t0 = c * KDA_C;
-        const int J = wave;
-        // ---- 1. operands: in-block prefix sums of the two channels, in log2
-        // units (every exponential below is one exp2)
-        float2 bl[16];
+        // ---- 1. operands: prefix sums of the two channels over this wave's
+        // 8 tokens, in log2 units (every exponential below is one exp2)
+        float2 bl[8];
         {
             float2 acc = make_float2(0.f, 0.f);
 #pragma unroll
-            for (int s = 0; s < 16; ++s) {
+            for (int s = 0; s < 8; ++s) {
                 acc.x += __uint_as_float(x.g[s][0]) * LOG2E;
                 acc.y += __uint_as_float(x.g[s][1]) * LOG2E;
                 bl[s] = acc;
             }
         }
-        *reinterpret_cast<float2 *>(&sm.tot[J][2 * p]) = bl[15];
-        *reinterpret_cast<float2 *>(&sm.mid[J][2 * p]) = bl[7];
+        *reinterpret_cast<float2 *>(&sm.htot[wave][2 * p]) = bl[7];
         lds_barrier();
         {
+            // m_I: prefix sum at the 8th token of block I = the end of its
+            // first half; run: the prefix sum before block I, then b_last
             float2 mI[4];
             float2 run = make_float2(0.f, 0.f);
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
-                const float2 md = *reinterpret_cast<const float2 *>(&sm.mid[I][2 * p]);
-                mI[I] = make_float2(run.x + md.x, run.y + md.y);
-                const float2 tt = *reinterpret_cast<const float2 *>(&sm.tot[I][2 * p]);
-                run.x += tt.x;
-                run.y += tt.y;
+                const float2 h0 = *reinterpret_cast<const float2 *>(&sm.htot[2 * I][2 * p]);
+                const float2 h1 = *reinterpret_cast<const float2 *>(&sm.htot[2 * I + 1][2 * p]);
+                mI[I] = make_float2(run.x + h0.x, run.y + h0.y);
+                run.x += h0.x + h1.x;
+                run.y += h0.y + h1.y;
             }
-            // run = b_last (log2)
-            if (J == 0) {
+            if (wave == 0) {
                 sm.gamC[2 * p] = exp2_(run.x);
                 sm.gamC[2 * p + 1] = exp2_(run.y);
             }
@@ -224,18 +241,20 @@ __global__ __launch_bounds__(256) void kda_chunk_kernel(
                 F[I] = make_float2(exp2_(fminf(mI[I].x - mJ.x, 0.f)), exp2_(fminf(mI[I].y - mJ.y, 0.f)));
             const int col = 2 * p;
 #pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                const int t = 16 * J + s;
-                // b_t - m_J is the in-block prefix difference: e grows for
-                // s < 7 (rows), ei for s > 7 (columns); only those are clamped
-                const float d0 = bl[s].x - bl[7].x, d1 = bl[s].y - bl[7].y;
-                float e0 = 1.f, e1 = 1.f, i0 = 1.f, i1 = 1.f;
-                if (s < 7) {
+            for (int s = 0; s < 8; ++s) {
+                const int t = 16 * J + 8 * hf + s;
+                // b_t - m_J: the first half's own prefix difference (>= 0,
+                // rows grow), or the second half's own prefix sum (<= 0,
+                // columns grow); only the growing side is clamped
+                float e0, e1, i0, i1;
+                if (hf == 0) {
+                    const float d0 = bl[s].x - bl[7].x, d1 = bl[s].y - bl[7].y;
                     e0 = exp2_(fminf(d0, KDA_EXP2_MAX));
                     e1 = exp2_(fminf(d1, KDA_EXP2_MAX));
                     i0 = exp2_(-d0);
                     i1 = exp2_(-d1);
-                } else if (s > 7) {
+                } else {
+                    const float d0 = bl[s].x, d1 = bl[s].y;
                     e0 = exp2_(d0);
                     e1 = exp2_(d1);
                     i0 = exp2_(fminf(-d0, KDA_EXP2_MAX));
@@ -259,17 +278,12 @@ __global__ __launch_bounds__(256) void kda_chunk_kernel(
                             pk2(c0 * F[I].x, c1 * F[I].y);
             }
         }
-#pragma unroll
-        for (int nn = 0; nn < 2; ++nn) {
-            const int u = tid + 256 * nn;
-            *reinterpret_cast<uint4 *>(sm.V + (u / 8) * KDA_LDV + 8 * (u % 8)) = x.v[nn];
-        }
         if (tid < KDA_C) sm.beta[tid] = (float)__builtin_bit_cast(__bf16, x.beta);
         if (c + 1 < nchunk) kda_prefetch(x, sq, t0 + KDA_C, wave, p, tid);
         lds_barrier();
 
         // ---- 2. G and P blocks, diagonal inverses
-        for (int pp = wave; pp < 10; pp += 4) {
+        for (int pp = wave; pp < 10; pp += 8) {
             int I, Jb;
             pair_ij(pp, I, Jb);
             f32x4 aG = zero4(), aP = zero4();
@@ -301,63 +315,86 @@ __global__ __launch_bounds__(256) void kda_chunk_kernel(
         }
         lds_barrier();
 
-        // ---- 3. state path on this wave's 16 value rows
+        // ---- 3. state path on 16 value rows
         {
             bf16x8 fS[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) cvt8(S[s][0], S[s][1], fS[s]);
-            f32x4 E[4], O[4];
+            bf16x4 fE[4];  // E_I as B-operand fragments (lane (g, r): E_I[4g + e][r])
+            if (solver) {
+                // all four X tiles first (independent), then the serial solve
+                f32x4 E[4], Xs[4];
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                f32x4 X = zero4();
-                O[I] = zero4();
+                for (int I = 0; I < 4; ++I) Xs[I] = zero4();
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    bf16x8 fk, fq;
-                    frag_rows(sm.KT, KDA_LD, 16 * I, 32 * s, lane, fk);
-                    frag_rows(sm.QT, KDA_LD, 16 * I, 32 * s, lane, fq);
-                    mma_k32(X, fk, fS[s]);
-                    mma_k32(O[I], fq, fS[s]);
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int I = 0; I < 4; ++I) {
+                        bf16x8 fk;
+                        frag_rows(sm.KT, KDA_LD, 16 * I, 32 * s, lane, fk);
+                        mma_k32(Xs[I], fk, fS[s]);
+                    }
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    f32x4 X = Xs[I];
+                    // Y = X - V + sum_{J<I} G_IJ E_J;  E_I = (-T_II diag(beta_I)) Y
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        X[e] -= (float)__builtin_bit_cast(__bf16, vr[4 * I + e]);
+#pragma unroll
+                    for (int Jb = 0; Jb < I; ++Jb) {
+                        bf16x4 fa;
+                        load_fragblk(sm.Gb, off_idx(I, Jb), lane, fa);
+                        mma_k16(X, fa, fE[Jb]);
+                    }
+                    bf16x4 ft, fy;
+                    load_fragblk(sm.Tb, I, lane, ft);
+                    frag_from_acc16(X, fy);
+                    E[I] = zero4();
+                    mma_k16(E[I], ft, fy);
+                    frag_from_acc16(E[I], fE[I]);
+                    store_frag16(sm.Ex[vt] + I * FRAG_ELEMS + 4 * lane, fE[I]);
                 }
-                // Y = X - V + sum_{J<I} G_IJ E_J;  E_I = (-T_II diag(beta_I)) Y
+                if (c + 1 < nchunk) kda_prefetch_v(vr, sq, t0 + KDA_C, g, vcol);
+                lds_barrier();
+            } else {
+                f32x4 O[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    X[e] -= (float)sm.V[(16 * I + 4 * g + e) * KDA_LDV + 16 * wave + r];
+                for (int I = 0; I < 4; ++I) O[I] = zero4();
 #pragma unroll
-                for (int Jb = 0; Jb < I; ++Jb) {
-                    bf16x4 fa, fe;
-                    load_fragblk(sm.Gb, off_idx(I, Jb), lane, fa);
-                    frag_from_acc16(E[Jb], fe);
-                    mma_k16(X, fa, fe);
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int I = 0; I < 4; ++I) {
+                        bf16x8 fq;
+                        frag_rows(sm.QT, KDA_LD, 16 * I, 32 * s, lane, fq);
+                        mma_k32(O[I], fq, fS[s]);
+                    }
+                lds_barrier();
+#pragma unroll
+                for (int I = 0; I < 4; ++I) load_chunk(sm.Ex[vt] + I * FRAG_ELEMS + 4 * lane, fE[I]);
+                // O_I += sum_{J<=I} P_IJ E_J, then out (stores past the
+                // sequence's end fall outside the resource and are dropped)
+                const int so = H * Dv * 2;
+                const __amdgpu_buffer_rsrc_t ro =
+                    make_rsrc(sq.o + sq.row(t0) * Dv, min(KDA_C, sq.len - t0) * so);
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+#pragma unroll
+                    for (int Jb = 0; Jb <= I; ++Jb) {
+                        bf16x4 fa;
+                        load_fragblk(sm.Pb, I * (I + 1) / 2 + Jb, lane, fa);
+                        mma_k16(O[I], fa, fE[Jb]);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        buf_store_elem((__bf16)(scale * O[I][e]), ro,
+                                       (16 * I + 4 * g + e) * so + 2 * vcol, 0);
                 }
-                bf16x4 ft, fy;
-                load_fragblk(sm.Tb, I, lane, ft);
-                frag_from_acc16(X, fy);
-                E[I] = zero4();
-                mma_k16(E[I], ft, fy);
             }
-            // O_I += sum_{J<=I} P_IJ E_J, then out (stores past the sequence's
-            // end fall outside the resource and are dropped)
-            const int so = H * Dv * 2;
-            const __amdgpu_buffer_rsrc_t ro =
-                make_rsrc(sq.o + sq.row(t0) * Dv, min(KDA_C, sq.len - t0) * so);
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
-#pragma unroll
-                for (int Jb = 0; Jb <= I; ++Jb) {
-                    bf16x4 fa, fe;
-                    load_fragblk(sm.Pb, I * (I + 1) / 2 + Jb, lane, fa);
-                    frag_from_acc16(E[Jb], fe);
-                    mma_k16(O[I], fa, fe);
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    buf_store_elem((__bf16)(scale * O[I][e]), ro, (16 * I + 4 * g + e) * so + 2 * drow, 0);
-            }
-            // S <- S diag(Gamma_last) + (E^T KE)^T, slab by slab
-            bf16x8 fE[2];
-            cvt8(E[0], E[1], fE[0]);
-            cvt8(E[2], E[3], fE[1]);
+            // S <- S diag(Gamma_last) + (E^T KE)^T, slab by slab (both copies)
+            bf16x8 fE32[2];
+            fE32[0] = __builtin_shufflevector(fE[0], fE[1], 0, 1, 2, 3, 4, 5, 6, 7);
+            fE32[1] = __builtin_shufflevector(fE[2], fE[3], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -367,17 +404,17 @@ __global__ __launch_bounds__(256) void kda_chunk_kernel(
                     for (int u = 0; u < 2; ++u) {
                         bf16x8 fa;
                         frag_cols32(sm.KE, KDA_LD, 32 * u, 32 * s + 16 * hh, lane, fa);
-                        mma_k32(d, fa, fE[u]);
+                        mma_k32(d, fa, fE32[u]);
                     }
                     const f32x4 gc = *reinterpret_cast<const f32x4 *>(sm.gamC + 32 * s + 16 * hh + 4 * g);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) S[s][hh][e] = S[s][hh][e] * gc[e] + d[e];
                 }
         }
-        // the next chunk's first LDS writes (block sums) touch only tot and
-        // mid, which nobody reads after the barrier above
+        // the next chunk's first LDS writes (half-block sums) touch only htot,
+        // which nobody reads after the first barrier of this chunk
     }
-    if (S_T) {
+    if (S_T && solver) {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -402,7 +439,7 @@ bool kda_chunk_supported(const ChunkFwdArgs &a, bool bf16) {
 hipError_t launch_kda_chunk(const ChunkFwdArgs &a, hipStream_t stream) {
     if (a.B == 0 || a.H == 0) return hipSuccess;
     const int64_t grid = a.B * a.H * (a.Dv / KDA_DVW);
-    hipLaunchKernelGGL(kda_chunk_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+    hipLaunchKernelGGL(kda_chunk_kernel, dim3((unsigned)grid), dim3(512), 0, stream,
                        static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k),
                        static_cast<const __bf16 *>(a.v), static_cast<const __bf16 *>(a.beta),
                        a.gk, a.S0, static_cast<__bf16 *>(a.o), a.S_T, a.cu, (int)a.T, (int)a.H,
