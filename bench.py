@@ -261,7 +261,7 @@ def bench_kda_sequence(torch, dr, W, reps=10):
     torch.cuda.synchronize()
     launch_s = sum(a.elapsed_time(b) for a, b in ev) / reps / 1e3
     return {
-        "workload": (f"layer_1p3b B{w.B} H{w.H} T{w.T} d{w.Dk} chunk 64, bf16 in, "
+        "workload": (f"layer_1p3b B{w.B} H{w.H} T{w.T} d{w.Dk} chunk 32, bf16 in, "
                      "per-channel log decay fp32 (A up to 1), fp32 state"),
         "tokens_per_s": w.B * w.T / launch_s,
         "mean_launch_us": round(launch_s * 1e6, 2),

@@ -1,5 +1,5 @@
 // Chunked forward of Kimi Delta Attention (per-key-channel decay), bf16
-// inputs, d_k = 128, chunks of 64 tokens (gfx950).
+// inputs, d_k = 128, chunks of 32 tokens (gfx950).
 //
 // hada.io digest, sections "Chunkwise KDA" and "Pipeline Triton Chunkwise".
 // With b_t the in-chunk prefix sums of the log decays gk (a vector over the
@@ -12,7 +12,7 @@
 // which is the recurrence token by token (decay, predict, correct, write,
 // read).  The same block substitution as the scalar-decay kernels resolves E:
 // the diagonal 16-token blocks of (I + diag(beta) G) are inverted on the
-// matrix cores, the blocks below them are products.
+// matrix cores, the block below them is a product.
 //
 // The decay ratio exp(b_i - b_j) lives inside the contraction over key
 // channels, so it cannot be applied to a finished Gram tile.  It is split
@@ -24,31 +24,13 @@
 // should stay above -40 (per-token gk >= -5 guarantees it); the growing
 // exponents are clamped at 80 so that nothing overflows outside it.
 //
-// Work split.  One workgroup of eight waves owns one (sequence, head) and a
-// slice of 64 value rows of S, and walks the chunks in order.  Per chunk:
-//   1. wave w (tokens 8w .. 8w + 7) and lane p (key channels 2p, 2p + 1)
-//      turn the prefetched k, q and gk of its tokens into the scaled
-//      operands in LDS (prefix sums, with half-block sums exchanged through
-//      LDS);
-//   2. the ten 16-token block pairs (I, J <= I) of G and P are shared out over
-//      the waves; diagonal blocks are inverted right away;
-//   3. waves 0-3 (the solvers) each take 16 value rows: X = (K.Gamma) S^T and
-//      the block substitution for E, which they hand to waves 4-7 through
-//      LDS; waves 4-7 (the readers) meanwhile form (Q.Gamma) S^T for the same
-//      rows, then add P E and store O.  Both keep the rows of S in registers
-//      (fp32, the canonical k order of the matrix-core operands) and apply
-//      the same state update from the same bf16 E, so their copies stay
-//      identical.
-// Two waves per SIMD let one wave's exponentials and LDS traffic overlap the
-// other's matrix-core work.  The next chunk's inputs are loaded into
-// registers while steps 2 and 3 run.
+// Work split: see kda_pipe_kernel.
 #include "chunk_fwd.hpp"
 
 namespace dr {
 
 namespace {
 
-constexpr int KDA_C = 64;        // tokens per chunk
 constexpr int KDA_DK = 128;      // key channels
 constexpr int KDA_DVW = 64;      // value rows per workgroup
 constexpr int KDA_LD = 136;      // row pitch (bf16) of the token x channel tiles
@@ -61,23 +43,7 @@ __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(
 // the 16 (I + 1) tokens 0 .. 16 I + 15.
 constexpr int kc_base(int I) { return 8 * I * (I + 1); }
 
-struct alignas(16) KdaSmem {
-    __bf16 KR[KDA_C * KDA_LD];        // k_i exp(b_i - m_I)        (Gram rows)
-    __bf16 QR[KDA_C * KDA_LD];        // q_i exp(b_i - m_I)        (P rows)
-    __bf16 KC[160 * KDA_LD];          // k_j exp(m_I - b_j), per row block I
-    __bf16 KT[KDA_C * KDA_LD];        // k_t Gamma_t               (X)
-    __bf16 QT[KDA_C * KDA_LD];        // q_t Gamma_t               (O)
-    __bf16 KE[KDA_C * KDA_LD];        // k_t exp(b_last - b_t)     (state update)
-    __bf16 Gb[6 * FRAG_ELEMS];        // G blocks below the diagonal
-    __bf16 Tb[4 * FRAG_ELEMS];        // -T_II diag(beta_I), T_II = (I + diag(beta) G_II)^{-1}
-    __bf16 Pb[10 * FRAG_ELEMS];       // P blocks on and below the diagonal
-    float beta[KDA_C];
-    float gamC[KDA_DK];               // Gamma_last per channel
-    float htot[8][KDA_DK];            // sums of gk over each 8-token half block (log2)
-    __bf16 Ex[4][4 * FRAG_ELEMS];     // E of each solver wave, as B-operand fragments
-};
-
-// Block pair p = I (I + 1) / 2 + J of the ten (I, J <= I).
+// Block pair p = I (I + 1) / 2 + J of the pairs (I, J <= I).
 __device__ __forceinline__ void pair_ij(int p, int &I, int &J) {
     I = p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0;
     J = p - I * (I + 1) / 2;
@@ -103,14 +69,50 @@ struct KdaSeq {
     __device__ __forceinline__ int64_t row(int t) const { return (base + t) * H + h; }
 };
 
-// Loads of one chunk (tokens t0 .. t0 + 63 of the sequence) through buffer
-// resources that span exactly its valid tokens: offsets are constants per
-// lane and token, and tokens past the end of the sequence load as zeros
-// (k = q = v = 0, gk = 0, beta = 0 leave the state unchanged).  The token part
-// of each offset is wave-uniform and goes in the scalar offset.
-__device__ __forceinline__ void kda_prefetch(KdaRegs &x, const KdaSeq &sq, int t0, int w,
-                                             int p, int tid) {
-    const int nv = min(KDA_C, sq.len - t0);
+// ---------------------------------------------------------------------------
+// Work split.  One workgroup of eight waves owns one (sequence, head) and a
+// slice of 64 value rows of S (wave 4 + i: rows 16i .. 16i + 15, fp32 in
+// registers in the canonical k order of the matrix-core operands), walks the
+// 32-token chunks in order, and is pipelined: waves 0-3 (preparation) build the
+// operands and the G / P blocks of chunk c + 1 while waves 4-7 (state) run
+// the state path of chunk c on 16 value rows each, so the exponentials and
+// LDS writes of one overlap the matrix-core work of the other.  What the
+// state waves read (K.Gamma, Q.Gamma, KE, the blocks, Gamma_last) is double
+// buffered by chunk parity; at 32 tokens everything fits in LDS.  Each step
+// has three segments separated by workgroup barriers:
+//   1. preparation: prefix sums of its 8 tokens and the operands that need
+//      only in-block differences;  state: X and (Q.Gamma) S^T
+//   2. preparation: the operands that need the other waves' sums;  state:
+//      block substitution, P E, outputs
+//   3. preparation: G and P blocks, inverses;  state: state update
+// Step -1 prepares chunk 0 only; the last step only runs the state path.
+// ---------------------------------------------------------------------------
+constexpr int KP_C = 32;
+
+struct alignas(16) KdaPipeBuf {
+    __bf16 KT[KP_C * KDA_LD];        // k_t Gamma_t
+    __bf16 QT[KP_C * KDA_LD];        // q_t Gamma_t
+    __bf16 KE[KP_C * KDA_LD];        // k_t exp(b_last - b_t)
+    __bf16 Gb[1 * FRAG_ELEMS];       // G_10
+    __bf16 Tb[2 * FRAG_ELEMS];       // -T_II diag(beta_I)
+    __bf16 Pb[3 * FRAG_ELEMS];       // P_00, P_10, P_11
+    float gamC[KDA_DK];              // Gamma_last
+};
+
+struct alignas(16) KdaPipeSmem {
+    __bf16 KR[KP_C * KDA_LD];        // k_i exp(b_i - m_I)
+    __bf16 QR[KP_C * KDA_LD];        // q_i exp(b_i - m_I)
+    __bf16 KC[48 * KDA_LD];          // k_j exp(m_I - b_j): I = 0 rows 0..15, I = 1 rows 16..47
+    KdaPipeBuf buf[2];
+    float beta[KP_C];
+    float htot[4][KDA_DK];           // sums of gk over each 8-token quarter (log2)
+};
+
+// Raw k, q, gk of tokens 8w .. 8w + 7 and beta of token tid (< 32) of the
+// 32-token chunk at t0, zeros past the sequence's end.
+__device__ __forceinline__ void kp_prefetch(KdaRegs &x, const KdaSeq &sq, int t0, int w, int p,
+                                            int tid) {
+    const int nv = min(KP_C, sq.len - t0);
     const int64_t r0 = sq.row(t0);
     const int sk = sq.H * KDA_DK * 2, sg = sq.H * KDA_DK * 4;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(sq.k + r0 * KDA_DK, nv * sk);
@@ -125,36 +127,32 @@ __device__ __forceinline__ void kda_prefetch(KdaRegs &x, const KdaSeq &sq, int t
         x.q[s] = __builtin_amdgcn_raw_buffer_load_b32(rq, 4 * p, tk * sk, 0);
         x.g[s] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, 8 * p, tk * sg, 0));
     }
-    x.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, min(tid, KDA_C - 1) * sq.H * 2, 0, 0);
+    x.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, min(tid, KP_C - 1) * sq.H * 2, 0, 0);
 }
 
-// The value entries a solver lane needs, in the D layout of its X tiles:
-// v[t0 + 16 I + 4 g + e][vcol] for I, e = 0..3.
-__device__ __forceinline__ void kda_prefetch_v(unsigned short (&vr)[16], const KdaSeq &sq,
-                                               int t0, int g, int vcol) {
-    const int nv = min(KDA_C, sq.len - t0);
+// v[t0 + 16 I + 4 g + e][vcol] for I < 2, e < 4 (the D layout of X).
+__device__ __forceinline__ void kp_prefetch_v(unsigned short (&vr)[8], const KdaSeq &sq, int t0,
+                                              int g, int vcol) {
+    const int nv = min(KP_C, sq.len - t0);
     const int sv = sq.H * sq.Dv * 2;
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(sq.v + sq.row(t0) * sq.Dv, nv * sv);
 #pragma unroll
-    for (int I = 0; I < 4; ++I)
+    for (int I = 0; I < 2; ++I)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             vr[4 * I + e] = __builtin_amdgcn_raw_buffer_load_b16(
                 rv, (4 * g) * sv + 2 * vcol, (16 * I + e) * sv, 0);
 }
 
-__global__ __launch_bounds__(512) void kda_chunk_kernel(
+__global__ __launch_bounds__(512) void kda_pipe_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const __bf16 *__restrict__ beta, const float *__restrict__ gk, const float *S0,
     __bf16 *__restrict__ o, float *S_T, const int *__restrict__ cu, int T, int H, int Dv,
     float scale) {
-    __shared__ KdaSmem sm;
-    // Consecutive workgroup ids go round-robin over the 8 XCDs (each with its
-    // own L2); remap so that the value slices of one head, which read the same
-    // k, q and gk and write the same o rows, run on the same XCD.
+    __shared__ KdaPipeSmem sm;
     int wg = blockIdx.x;
     const int nwg = gridDim.x;
-    if (nwg % 8 == 0) wg = (wg % 8) * (nwg / 8) + wg / 8;
+    if (nwg % 8 == 0) wg = (wg % 8) * (nwg / 8) + wg / 8;  // value slices of a head on one XCD
     const int nvb = Dv / KDA_DVW;
     const int vb = wg % nvb;
     const int64_t seqhead = wg / nvb;
@@ -171,40 +169,46 @@ __global__ __launch_bounds__(512) void kda_chunk_kernel(
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, r = lane & 15;
-    const int p = lane;                      // channel pair of the operand step
-    const bool solver = wave < 4;
-    const int vt = wave & 3;                 // value tile of the state step
-    const int vcol = vb * KDA_DVW + 16 * vt + r;   // this lane's state row
+    const int p = lane;                       // channel pair of the operand step
+    const bool prep = wave < 4;
+    const int vt = wave & 3;                  // value tile of a state wave
+    const int vcol = vb * KDA_DVW + 16 * vt + r;
     const int64_t srow = (seqhead * Dv + vcol) * KDA_DK;
+    const int J = (wave & 3) >> 1, hf = wave & 1;  // token block and half (preparation)
 
-    // state: slab s (channels 32 s ..), half 0: 32 s + 4 g + e, half 1: + 16
     f32x4 S[4][2];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             S[s][hh] = zero4();
-            if (S0) {
+            if (S0 && !prep) {
                 const float4 x = *reinterpret_cast<const float4 *>(S0 + srow + 32 * s + 16 * hh + 4 * g);
                 S[s][hh] = f32x4{x.x, x.y, x.z, x.w};
             }
         }
 
-    const int nchunk = (sq.len + KDA_C - 1) / KDA_C;
+    const int nchunk = (sq.len + KP_C - 1) / KP_C;
     KdaRegs x;
-    unsigned short vr[16];
+    unsigned short vr[8];
     if (nchunk > 0) {
-        kda_prefetch(x, sq, 0, wave, p, tid);
-        if (solver) kda_prefetch_v(vr, sq, 0, g, vcol);
+        if (prep) kp_prefetch(x, sq, 0, wave, p, tid);
+        else kp_prefetch_v(vr, sq, 0, g, vcol);
     }
 
-    const int J = wave >> 1, hf = wave & 1;  // token block and half of the operand step
-    for (int c = 0; c < nchunk; ++c) {
-        const int t0 = c * KDA_C;
-        // ---- 1. operands: prefix sums of the two channels over this wave's
-        // 8 tokens, in log2 units (every exponential below is one exp2)
+    for (int it = -1; it < nchunk; ++it) {
+        const bool pw = prep && it + 1 < nchunk;   // prepare chunk it + 1
+        const bool sw = !prep && it >= 0;          // state path of chunk it
+        const int tp = (it + 1) * KP_C, ts = it * KP_C;
+        KdaPipeBuf &bp = sm.buf[(it + 1) & 1];
+        KdaPipeBuf &bs = sm.buf[it & 1];
+
+        // ---- segment 1
         float2 bl[8];
-        {
+        float2 ef[8], ifc[8];  // exp(b_t - m_J) and exp(m_J - b_t) of the two channels
+        bf16x8 fS[4];
+        f32x4 Xs[2], O[2];
+        if (pw) {
             float2 acc = make_float2(0.f, 0.f);
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
@@ -212,16 +216,59 @@ __global__ __launch_bounds__(512) void kda_chunk_kernel(
                 acc.y += __uint_as_float(x.g[s][1]) * LOG2E;
                 bl[s] = acc;
             }
+            *reinterpret_cast<float2 *>(&sm.htot[wave][2 * p]) = bl[7];
+            // everything that needs only in-block differences: b_t - m_J is
+            // the first half's own prefix difference (>= 0, rows grow) or
+            // the second half's own prefix sum (<= 0, columns grow); only the
+            // growing side is clamped.  Rows k e, q e and the block's own
+            // columns k i go to LDS now.
+            const int col = 2 * p;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const int t = 16 * J + 8 * hf + s;
+                if (hf == 0) {
+                    const float d0 = bl[s].x - bl[7].x, d1 = bl[s].y - bl[7].y;
+                    ef[s] = make_float2(exp2_(fminf(d0, KDA_EXP2_MAX)), exp2_(fminf(d1, KDA_EXP2_MAX)));
+                    ifc[s] = make_float2(exp2_(-d0), exp2_(-d1));
+                } else {
+                    const float d0 = bl[s].x, d1 = bl[s].y;
+                    ef[s] = make_float2(exp2_(d0), exp2_(d1));
+                    ifc[s] = make_float2(exp2_(fminf(-d0, KDA_EXP2_MAX)), exp2_(fminf(-d1, KDA_EXP2_MAX)));
+                }
+                const float k0 = lo_bf16(x.k[s]), k1 = hi_bf16(x.k[s]);
+                const float q0 = lo_bf16(x.q[s]), q1 = hi_bf16(x.q[s]);
+                const int o_t = t * KDA_LD + col;
+                *reinterpret_cast<unsigned *>(sm.KR + o_t) = pk2(k0 * ef[s].x, k1 * ef[s].y);
+                *reinterpret_cast<unsigned *>(sm.QR + o_t) = pk2(q0 * ef[s].x, q1 * ef[s].y);
+                *reinterpret_cast<unsigned *>(sm.KC + (kc_base(J) + t) * KDA_LD + col) =
+                    pk2(k0 * ifc[s].x, k1 * ifc[s].y);
+            }
         }
-        *reinterpret_cast<float2 *>(&sm.htot[wave][2 * p]) = bl[7];
+        if (sw) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) cvt8(S[s][0], S[s][1], fS[s]);
+#pragma unroll
+            for (int I = 0; I < 2; ++I) Xs[I] = O[I] = zero4();
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int I = 0; I < 2; ++I) {
+                    bf16x8 fk, fq;
+                    frag_rows(bs.KT, KDA_LD, 16 * I, 32 * s, lane, fk);
+                    frag_rows(bs.QT, KDA_LD, 16 * I, 32 * s, lane, fq);
+                    mma_k32(Xs[I], fk, fS[s]);
+                    mma_k32(O[I], fq, fS[s]);
+                }
+        }
         lds_barrier();
-        {
-            // m_I: prefix sum at the 8th token of block I = the end of its
-            // first half; run: the prefix sum before block I, then b_last
-            float2 mI[4];
+
+        // ---- segment 2
+        bf16x4 fE[2];
+        if (pw) {
+            float2 mI[2];
             float2 run = make_float2(0.f, 0.f);
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
+            for (int I = 0; I < 2; ++I) {
                 const float2 h0 = *reinterpret_cast<const float2 *>(&sm.htot[2 * I][2 * p]);
                 const float2 h1 = *reinterpret_cast<const float2 *>(&sm.htot[2 * I + 1][2 * p]);
                 mI[I] = make_float2(run.x + h0.x, run.y + h0.y);
@@ -229,63 +276,76 @@ __global__ __launch_bounds__(512) void kda_chunk_kernel(
                 run.y += h0.y + h1.y;
             }
             if (wave == 0) {
-                sm.gamC[2 * p] = exp2_(run.x);
-                sm.gamC[2 * p + 1] = exp2_(run.y);
+                bp.gamC[2 * p] = exp2_(run.x);
+                bp.gamC[2 * p + 1] = exp2_(run.y);
             }
             const float2 mJ = mI[J];
-            const float2 GJ = make_float2(exp2_(mJ.x), exp2_(mJ.y));            // Gamma at m_J
+            const float2 GJ = make_float2(exp2_(mJ.x), exp2_(mJ.y));
             const float2 EJ = make_float2(exp2_(run.x - mJ.x), exp2_(run.y - mJ.y));
-            float2 F[4];  // exp(m_I - m_J) <= 1 for I > J
-#pragma unroll
-            for (int I = 0; I < 4; ++I)
-                F[I] = make_float2(exp2_(fminf(mI[I].x - mJ.x, 0.f)), exp2_(fminf(mI[I].y - mJ.y, 0.f)));
+            const float2 F1 = make_float2(exp2_(fminf(mI[1].x - mJ.x, 0.f)), exp2_(fminf(mI[1].y - mJ.y, 0.f)));
             const int col = 2 * p;
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 const int t = 16 * J + 8 * hf + s;
-                // b_t - m_J: the first half's own prefix difference (>= 0,
-                // rows grow), or the second half's own prefix sum (<= 0,
-                // columns grow); only the growing side is clamped
-                float e0, e1, i0, i1;
-                if (hf == 0) {
-                    const float d0 = bl[s].x - bl[7].x, d1 = bl[s].y - bl[7].y;
-                    e0 = exp2_(fminf(d0, KDA_EXP2_MAX));
-                    e1 = exp2_(fminf(d1, KDA_EXP2_MAX));
-                    i0 = exp2_(-d0);
-                    i1 = exp2_(-d1);
-                } else {
-                    const float d0 = bl[s].x, d1 = bl[s].y;
-                    e0 = exp2_(d0);
-                    e1 = exp2_(d1);
-                    i0 = exp2_(fminf(-d0, KDA_EXP2_MAX));
-                    i1 = exp2_(fminf(-d1, KDA_EXP2_MAX));
-                }
                 const float k0 = lo_bf16(x.k[s]), k1 = hi_bf16(x.k[s]);
                 const float q0 = lo_bf16(x.q[s]), q1 = hi_bf16(x.q[s]);
-                const float g0 = e0 * GJ.x, g1 = e1 * GJ.y;      // Gamma_t
-                const float c0 = k0 * i0, c1 = k1 * i1;          // column operand, block J
+                const float g0 = ef[s].x * GJ.x, g1 = ef[s].y * GJ.y;   // Gamma_t
+                const float c0 = k0 * ifc[s].x, c1 = k1 * ifc[s].y;     // column operand, block J
                 const int o_t = t * KDA_LD + col;
-                *reinterpret_cast<unsigned *>(sm.KR + o_t) = pk2(k0 * e0, k1 * e1);
-                *reinterpret_cast<unsigned *>(sm.QR + o_t) = pk2(q0 * e0, q1 * e1);
-                *reinterpret_cast<unsigned *>(sm.KT + o_t) = pk2(k0 * g0, k1 * g1);
-                *reinterpret_cast<unsigned *>(sm.QT + o_t) = pk2(q0 * g0, q1 * g1);
-                *reinterpret_cast<unsigned *>(sm.KE + o_t) = pk2(c0 * EJ.x, c1 * EJ.y);
-                *reinterpret_cast<unsigned *>(sm.KC + (kc_base(J) + t) * KDA_LD + col) = pk2(c0, c1);
+                *reinterpret_cast<unsigned *>(bp.KT + o_t) = pk2(k0 * g0, k1 * g1);
+                *reinterpret_cast<unsigned *>(bp.QT + o_t) = pk2(q0 * g0, q1 * g1);
+                *reinterpret_cast<unsigned *>(bp.KE + o_t) = pk2(c0 * EJ.x, c1 * EJ.y);
+                if (J == 0)
+                    *reinterpret_cast<unsigned *>(sm.KC + (kc_base(1) + t) * KDA_LD + col) =
+                        pk2(c0 * F1.x, c1 * F1.y);
+            }
+            if (tid < KP_C) sm.beta[tid] = (float)__builtin_bit_cast(__bf16, x.beta);
+            if (it + 2 < nchunk) kp_prefetch(x, sq, tp + KP_C, wave, p, tid);
+        }
+        if (sw) {
+            f32x4 E[2];
 #pragma unroll
-                for (int I = 0; I < 4; ++I)
-                    if (I > J)
-                        *reinterpret_cast<unsigned *>(sm.KC + (kc_base(I) + t) * KDA_LD + col) =
-                            pk2(c0 * F[I].x, c1 * F[I].y);
+            for (int I = 0; I < 2; ++I) {
+                f32x4 X = Xs[I];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    X[e] -= (float)__builtin_bit_cast(__bf16, vr[4 * I + e]);
+                if (I == 1) {
+                    bf16x4 fa;
+                    load_fragblk(bs.Gb, 0, lane, fa);
+                    mma_k16(X, fa, fE[0]);
+                }
+                bf16x4 ft, fy;
+                load_fragblk(bs.Tb, I, lane, ft);
+                frag_from_acc16(X, fy);
+                E[I] = zero4();
+                mma_k16(E[I], ft, fy);
+                frag_from_acc16(E[I], fE[I]);
+            }
+            if (it + 1 < nchunk) kp_prefetch_v(vr, sq, ts + KP_C, g, vcol);
+            const int so = H * Dv * 2;
+            const __amdgpu_buffer_rsrc_t ro =
+                make_rsrc(sq.o + sq.row(ts) * Dv, min(KP_C, sq.len - ts) * so);
+#pragma unroll
+            for (int I = 0; I < 2; ++I) {
+#pragma unroll
+                for (int Jb = 0; Jb <= I; ++Jb) {
+                    bf16x4 fa;
+                    load_fragblk(bs.Pb, I * (I + 1) / 2 + Jb, lane, fa);
+                    mma_k16(O[I], fa, fE[Jb]);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    buf_store_elem((__bf16)(scale * O[I][e]), ro,
+                                   (16 * I + 4 * g + e) * so + 2 * vcol, 0);
             }
         }
-        if (tid < KDA_C) sm.beta[tid] = (float)__builtin_bit_cast(__bf16, x.beta);
-        if (c + 1 < nchunk) kda_prefetch(x, sq, t0 + KDA_C, wave, p, tid);
         lds_barrier();
 
-        // ---- 2. G and P blocks, diagonal inverses
-        for (int pp = wave; pp < 10; pp += 8) {
+        // ---- segment 3
+        if (pw && wave < 3) {
             int I, Jb;
-            pair_ij(pp, I, Jb);
+            pair_ij(wave, I, Jb);
             f32x4 aG = zero4(), aP = zero4();
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -296,7 +356,6 @@ __global__ __launch_bounds__(512) void kda_chunk_kernel(
                 mma_k32(aG, fc, fk);
                 mma_k32(aP, fc, fq);
             }
-            // lane (g, r) holds G[16 I + r][16 Jb + 4 g + e] (and P alike)
             if (I == Jb) {
                 const float br = sm.beta[16 * I + r];
                 f32x4 a, pm;
@@ -306,115 +365,31 @@ __global__ __launch_bounds__(512) void kda_chunk_kernel(
                     pm[e] = r >= 4 * g + e ? aP[e] : 0.f;
                 }
                 const f32x4 b4 = *reinterpret_cast<const f32x4 *>(sm.beta + 16 * I + 4 * g);
-                diag_inverse(a, b4, sm.Tb, I, lane);
-                store_fragblk(sm.Pb, pp, lane, pm);
+                diag_inverse(a, b4, bp.Tb, I, lane);
+                store_fragblk(bp.Pb, wave, lane, pm);
             } else {
-                store_fragblk(sm.Gb, off_idx(I, Jb), lane, aG);
-                store_fragblk(sm.Pb, pp, lane, aP);
+                store_fragblk(bp.Gb, 0, lane, aG);
+                store_fragblk(bp.Pb, wave, lane, aP);
             }
         }
-        lds_barrier();
-
-        // ---- 3. state path on 16 value rows
-        {
-            bf16x8 fS[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) cvt8(S[s][0], S[s][1], fS[s]);
-            bf16x4 fE[4];  // E_I as B-operand fragments (lane (g, r): E_I[4g + e][r])
-            if (solver) {
-                // all four X tiles first (independent), then the serial solve
-                f32x4 E[4], Xs[4];
-#pragma unroll
-                for (int I = 0; I < 4; ++I) Xs[I] = zero4();
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-#pragma unroll
-                    for (int I = 0; I < 4; ++I) {
-                        bf16x8 fk;
-                        frag_rows(sm.KT, KDA_LD, 16 * I, 32 * s, lane, fk);
-                        mma_k32(Xs[I], fk, fS[s]);
-                    }
-#pragma unroll
-                for (int I = 0; I < 4; ++I) {
-                    f32x4 X = Xs[I];
-                    // Y = X - V + sum_{J<I} G_IJ E_J;  E_I = (-T_II diag(beta_I)) Y
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        X[e] -= (float)__builtin_bit_cast(__bf16, vr[4 * I + e]);
-#pragma unroll
-                    for (int Jb = 0; Jb < I; ++Jb) {
-                        bf16x4 fa;
-                        load_fragblk(sm.Gb, off_idx(I, Jb), lane, fa);
-                        mma_k16(X, fa, fE[Jb]);
-                    }
-                    bf16x4 ft, fy;
-                    load_fragblk(sm.Tb, I, lane, ft);
-                    frag_from_acc16(X, fy);
-                    E[I] = zero4();
-                    mma_k16(E[I], ft, fy);
-                    frag_from_acc16(E[I], fE[I]);
-                    store_frag16(sm.Ex[vt] + I * FRAG_ELEMS + 4 * lane, fE[I]);
-                }
-                if (c + 1 < nchunk) kda_prefetch_v(vr, sq, t0 + KDA_C, g, vcol);
-                lds_barrier();
-            } else {
-                f32x4 O[4];
-#pragma unroll
-                for (int I = 0; I < 4; ++I) O[I] = zero4();
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-#pragma unroll
-                    for (int I = 0; I < 4; ++I) {
-                        bf16x8 fq;
-                        frag_rows(sm.QT, KDA_LD, 16 * I, 32 * s, lane, fq);
-                        mma_k32(O[I], fq, fS[s]);
-                    }
-                lds_barrier();
-#pragma unroll
-                for (int I = 0; I < 4; ++I) load_chunk(sm.Ex[vt] + I * FRAG_ELEMS + 4 * lane, fE[I]);
-                // O_I += sum_{J<=I} P_IJ E_J, then out (stores past the
-                // sequence's end fall outside the resource and are dropped)
-                const int so = H * Dv * 2;
-                const __amdgpu_buffer_rsrc_t ro =
-                    make_rsrc(sq.o + sq.row(t0) * Dv, min(KDA_C, sq.len - t0) * so);
-#pragma unroll
-                for (int I = 0; I < 4; ++I) {
-#pragma unroll
-                    for (int Jb = 0; Jb <= I; ++Jb) {
-                        bf16x4 fa;
-                        load_fragblk(sm.Pb, I * (I + 1) / 2 + Jb, lane, fa);
-                        mma_k16(O[I], fa, fE[Jb]);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        buf_store_elem((__bf16)(scale * O[I][e]), ro,
-                                       (16 * I + 4 * g + e) * so + 2 * vcol, 0);
-                }
-            }
-            // S <- S diag(Gamma_last) + (E^T KE)^T, slab by slab (both copies)
-            bf16x8 fE32[2];
-            fE32[0] = __builtin_shufflevector(fE[0], fE[1], 0, 1, 2, 3, 4, 5, 6, 7);
-            fE32[1] = __builtin_shufflevector(fE[2], fE[3], 0, 1, 2, 3, 4, 5, 6, 7);
+        if (sw) {
+            const bf16x8 fE32 = __builtin_shufflevector(fE[0], fE[1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     f32x4 d = zero4();
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        bf16x8 fa;
-                        frag_cols32(sm.KE, KDA_LD, 32 * u, 32 * s + 16 * hh, lane, fa);
-                        mma_k32(d, fa, fE32[u]);
-                    }
-                    const f32x4 gc = *reinterpret_cast<const f32x4 *>(sm.gamC + 32 * s + 16 * hh + 4 * g);
+                    bf16x8 fa;
+                    frag_cols32(bs.KE, KDA_LD, 0, 32 * s + 16 * hh, lane, fa);
+                    mma_k32(d, fa, fE32);
+                    const f32x4 gc = *reinterpret_cast<const f32x4 *>(bs.gamC + 32 * s + 16 * hh + 4 * g);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) S[s][hh][e] = S[s][hh][e] * gc[e] + d[e];
                 }
         }
-        // the next chunk's first LDS writes (half-block sums) touch only htot,
-        // which nobody reads after the first barrier of this chunk
+        lds_barrier();
     }
-    if (S_T && solver) {
+    if (S_T && !prep) {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -427,19 +402,17 @@ __global__ __launch_bounds__(512) void kda_chunk_kernel(
 }  // namespace
 
 bool kda_chunk_supported(const ChunkFwdArgs &a, bool bf16) {
-    // v is read in 16-byte vectors here (the ABI only guarantees element
-    // alignment), and one chunk of one head's rows of every input must be
-    // addressable with 32-bit byte offsets
-    const int64_t span = int64_t(KDA_C) * a.H * (a.Dv > 2 * KDA_DK ? 2 * a.Dv : 4 * KDA_DK);
+    // one chunk of one head's rows of every input must be addressable with
+    // 32-bit byte offsets
+    const int64_t span = int64_t(KP_C) * a.H * (a.Dv > 2 * KDA_DK ? 2 * a.Dv : 4 * KDA_DK);
     return bf16 && a.gk && !a.g && !a.l2 && !a.recurrent && a.Dk == KDA_DK &&
-           a.Dv % KDA_DVW == 0 && (reinterpret_cast<uintptr_t>(a.v) & 15) == 0 &&
-           span < INT32_MAX;
+           a.Dv % KDA_DVW == 0 && span < INT32_MAX;
 }
 
 hipError_t launch_kda_chunk(const ChunkFwdArgs &a, hipStream_t stream) {
     if (a.B == 0 || a.H == 0) return hipSuccess;
     const int64_t grid = a.B * a.H * (a.Dv / KDA_DVW);
-    hipLaunchKernelGGL(kda_chunk_kernel, dim3((unsigned)grid), dim3(512), 0, stream,
+    hipLaunchKernelGGL(kda_pipe_kernel, dim3((unsigned)grid), dim3(512), 0, stream,
                        static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k),
                        static_cast<const __bf16 *>(a.v), static_cast<const __bf16 *>(a.beta),
                        a.gk, a.S0, static_cast<__bf16 *>(a.o), a.S_T, a.cu, (int)a.T, (int)a.H,

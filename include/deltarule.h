@@ -155,7 +155,7 @@ enum {
  *               predicted, corrected, written and read as in the plain rule.
  *               Exclusive with g (both set: DR_ERR_INVALID_ARG).  bf16 inputs
  *               with Dk = 128 and Dv a multiple of 64, without DR_QK_L2NORM
- *               or DR_FUSED_RECURRENT, run the chunked kernel (64-token
+ *               or DR_FUSED_RECURRENT, run the chunked kernel (32-token
  *               chunks, same digest, "Chunkwise KDA"; the chunk argument is
  *               validated but unused).  Its decay ratios are split around a
  *               reference token per 16-token block, which keeps every factor
