@@ -35,8 +35,8 @@ struct ChunkFwdArgs {
 
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
 hipError_t launch_fused_recurrent(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
-// Chunked KDA (per-channel decay): bf16, d_k = 128, d_v a multiple of 64, no
-// in-kernel L2 norm; other cases run the token-serial kernel.
+// Chunked KDA (per-channel decay): bf16, d_k = 128, d_v a multiple of 64;
+// other cases run the token-serial kernel.
 bool kda_chunk_supported(const ChunkFwdArgs &a, bool bf16);
 hipError_t launch_kda_chunk(const ChunkFwdArgs &a, hipStream_t stream);
 

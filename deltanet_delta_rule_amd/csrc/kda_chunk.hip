@@ -50,6 +50,14 @@ __device__ __forceinline__ void pair_ij(int p, int &I, int &J) {
 }
 
 __device__ __forceinline__ unsigned pk2(float a, float b) { return pk_bf16(a, b); }
+
+// Sum over the 64 lanes of the wave, every lane receiving it.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = group_sum<16>(v);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
 __device__ __forceinline__ float lo_bf16(unsigned x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float hi_bf16(unsigned x) { return __uint_as_float(x & 0xffff0000u); }
 
@@ -144,6 +152,10 @@ __device__ __forceinline__ void kp_prefetch_v(unsigned short (&vr)[8], const Kda
                 rv, (4 * g) * sv + 2 * vcol, (16 * I + e) * sv, 0);
 }
 
+// L2: q and k rows are divided by sqrt(|x|^2 + 1e-6) first (the l2norm of the
+// gated layer on houmin.site "infra/delta-net"); a preparation lane holds two
+// channels of each of its tokens, so a token's norm is one wave-wide sum.
+template <bool L2>
 __global__ __launch_bounds__(512) void kda_pipe_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const __bf16 *__restrict__ beta, const float *__restrict__ gk, const float *S0,
@@ -206,6 +218,7 @@ __global__ __launch_bounds__(512) void kda_pipe_kernel(
         // ---- segment 1
         float2 bl[8];
         float2 ef[8], ifc[8];  // exp(b_t - m_J) and exp(m_J - b_t) of the two channels
+        float nk[8], nq[8];    // inverse norms of k_t and q_t (1 without L2)
         bf16x8 fS[4];
         f32x4 Xs[2], O[2];
         if (pw) {
@@ -217,6 +230,16 @@ __global__ __launch_bounds__(512) void kda_pipe_kernel(
                 bl[s] = acc;
             }
             *reinterpret_cast<float2 *>(&sm.htot[wave][2 * p]) = bl[7];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                nk[s] = nq[s] = 1.f;
+                if constexpr (L2) {
+                    const float k0 = lo_bf16(x.k[s]), k1 = hi_bf16(x.k[s]);
+                    const float q0 = lo_bf16(x.q[s]), q1 = hi_bf16(x.q[s]);
+                    nk[s] = rsqrtf(wave_sum(k0 * k0 + k1 * k1) + 1e-6f);
+                    nq[s] = rsqrtf(wave_sum(q0 * q0 + q1 * q1) + 1e-6f);
+                }
+            }
             // everything that needs only in-block differences: b_t - m_J is
             // the first half's own prefix difference (>= 0, rows grow) or
             // the second half's own prefix sum (<= 0, columns grow); only the
@@ -235,8 +258,8 @@ __global__ __launch_bounds__(512) void kda_pipe_kernel(
                     ef[s] = make_float2(exp2_(d0), exp2_(d1));
                     ifc[s] = make_float2(exp2_(fminf(-d0, KDA_EXP2_MAX)), exp2_(fminf(-d1, KDA_EXP2_MAX)));
                 }
-                const float k0 = lo_bf16(x.k[s]), k1 = hi_bf16(x.k[s]);
-                const float q0 = lo_bf16(x.q[s]), q1 = hi_bf16(x.q[s]);
+                const float k0 = lo_bf16(x.k[s]) * nk[s], k1 = hi_bf16(x.k[s]) * nk[s];
+                const float q0 = lo_bf16(x.q[s]) * nq[s], q1 = hi_bf16(x.q[s]) * nq[s];
                 const int o_t = t * KDA_LD + col;
                 *reinterpret_cast<unsigned *>(sm.KR + o_t) = pk2(k0 * ef[s].x, k1 * ef[s].y);
                 *reinterpret_cast<unsigned *>(sm.QR + o_t) = pk2(q0 * ef[s].x, q1 * ef[s].y);
@@ -287,8 +310,8 @@ __global__ __launch_bounds__(512) void kda_pipe_kernel(
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 const int t = 16 * J + 8 * hf + s;
-                const float k0 = lo_bf16(x.k[s]), k1 = hi_bf16(x.k[s]);
-                const float q0 = lo_bf16(x.q[s]), q1 = hi_bf16(x.q[s]);
+                const float k0 = lo_bf16(x.k[s]) * nk[s], k1 = hi_bf16(x.k[s]) * nk[s];
+                const float q0 = lo_bf16(x.q[s]) * nq[s], q1 = hi_bf16(x.q[s]) * nq[s];
                 const float g0 = ef[s].x * GJ.x, g1 = ef[s].y * GJ.y;   // Gamma_t
                 const float c0 = k0 * ifc[s].x, c1 = k1 * ifc[s].y;     // column operand, block J
                 const int o_t = t * KDA_LD + col;
@@ -405,14 +428,15 @@ bool kda_chunk_supported(const ChunkFwdArgs &a, bool bf16) {
     // one chunk of one head's rows of every input must be addressable with
     // 32-bit byte offsets
     const int64_t span = int64_t(KP_C) * a.H * (a.Dv > 2 * KDA_DK ? 2 * a.Dv : 4 * KDA_DK);
-    return bf16 && a.gk && !a.g && !a.l2 && !a.recurrent && a.Dk == KDA_DK &&
+    return bf16 && a.gk && !a.g && !a.recurrent && a.Dk == KDA_DK &&
            a.Dv % KDA_DVW == 0 && span < INT32_MAX;
 }
 
 hipError_t launch_kda_chunk(const ChunkFwdArgs &a, hipStream_t stream) {
     if (a.B == 0 || a.H == 0) return hipSuccess;
     const int64_t grid = a.B * a.H * (a.Dv / KDA_DVW);
-    hipLaunchKernelGGL(kda_pipe_kernel, dim3((unsigned)grid), dim3(512), 0, stream,
+    auto kern = a.l2 ? kda_pipe_kernel<true> : kda_pipe_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), 0, stream,
                        static_cast<const __bf16 *>(a.q), static_cast<const __bf16 *>(a.k),
                        static_cast<const __bf16 *>(a.v), static_cast<const __bf16 *>(a.beta),
                        a.gk, a.S0, static_cast<__bf16 *>(a.o), a.S_T, a.cu, (int)a.T, (int)a.H,

@@ -154,8 +154,8 @@ enum {
  *               j) is multiplied by exp(gk_t[j]), then the token is
  *               predicted, corrected, written and read as in the plain rule.
  *               Exclusive with g (both set: DR_ERR_INVALID_ARG).  bf16 inputs
- *               with Dk = 128 and Dv a multiple of 64, without DR_QK_L2NORM
- *               or DR_FUSED_RECURRENT, run the chunked kernel (32-token
+ *               with Dk = 128 and Dv a multiple of 64, without
+ *               DR_FUSED_RECURRENT, run the chunked kernel (32-token
  *               chunks, same digest, "Chunkwise KDA"; the chunk argument is
  *               validated but unused).  Its decay ratios are split around a
  *               reference token per 16-token block, which keeps every factor

@@ -119,6 +119,27 @@ def test_matches_token_serial_schedule():
     assert rel_err(to_np(s_c), to_np(s_r)) <= 2e-2
 
 
+def test_in_kernel_l2norm():
+    # raw q, k normalised inside the kernel, against the oracle on the
+    # normalised rows and against the token-serial kernel's own L2 option
+    from oracle import l2norm_rows
+    w = _kda("layer_1p3b", B=2, H=2, T=100, feature="raw", seed=10750)
+    x = W.generate(w)
+    d = to_dev(x)
+    o, st = dr.kda_fwd(d["q"], d["k"], d["v"], d["beta"], d["gk"], None,
+                       use_qk_l2norm_in_kernel=True)
+    xn = dict(x)
+    for n in ("q", "k"):
+        xn[n] = torch.from_numpy(l2norm_rows(x[n].double().numpy()))
+    o_ref, s_ref = oracle_all(xn)
+    assert rel_err(to_np(o), o_ref) <= 2e-2
+    assert rel_err(to_np(st), s_ref) <= 2e-2
+    o_r, s_r = dr.kda_fwd(d["q"], d["k"], d["v"], d["beta"], d["gk"], None,
+                          use_qk_l2norm_in_kernel=True, fused_recurrent=True)
+    assert rel_err(to_np(o), to_np(o_r)) <= 2e-2
+    assert rel_err(to_np(st), to_np(s_r)) <= 2e-2
+
+
 def test_output_scale_and_no_initial_state():
     w = _kda("layer_1p3b", B=2, H=2, T=90, seed=10700)
     x = W.generate(w)
