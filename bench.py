@@ -67,7 +67,8 @@ def chunk_work(w):
     e = 2 if w.dtype == "bf16" else 4
     flops = th * (2 * w.chunk * (3 * w.Dk + 2 * w.Dv) + 6 * w.Dk * w.Dv)
     nbytes = th * e * (2 * w.Dk + w.Dv + 1) + th * e * w.Dv
-    nbytes += th * 4 if w.gate_amax > 0 else 0  # fp32 log gates
+    if w.gate_amax > 0:  # fp32 log gates: one per token-head, or per key channel
+        nbytes += th * 4 * (w.Dk if w.kda else 1)
     nbytes += 4 * w.B * w.H * w.Dv * w.Dk * ((1 if w.s0_std > 0 else 0) + 1)
     return flops, nbytes
 
@@ -240,7 +241,7 @@ def bench_gated_chunk(torch, dr, W, reps=20, name="gated_layer_1p3b", l2=False):
 def bench_kda_sequence(torch, dr, W, reps=10):
     """kda_fwd (chunked kernel) on the layer shape with per-channel decay:
     mean call time with HIP events on the launch stream."""
-    w = W.get("layer_1p3b", gate_amax=1.0, kda=True)
+    w = W.get("layer_1p3b", gate_amax=1.0, kda=True, chunk=32)
     x = W.generate(w)
     dev = torch.device("cuda:0")
     d = {n: (None if t is None else t.to(dev)) for n, t in x.items()}
@@ -260,11 +261,14 @@ def bench_kda_sequence(torch, dr, W, reps=10):
         b.record()
     torch.cuda.synchronize()
     launch_s = sum(a.elapsed_time(b) for a, b in ev) / reps / 1e3
+    flops, nbytes = chunk_work(w)
     return {
-        "workload": (f"layer_1p3b B{w.B} H{w.H} T{w.T} d{w.Dk} chunk 32, bf16 in, "
+        "workload": (f"layer_1p3b B{w.B} H{w.H} T{w.T} d{w.Dk} chunk {w.chunk}, bf16 in, "
                      "per-channel log decay fp32 (A up to 1), fp32 state"),
         "tokens_per_s": w.B * w.T / launch_s,
         "mean_launch_us": round(launch_s * 1e6, 2),
+        "hbm_frac": round(nbytes / launch_s / 1e9 / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(flops / launch_s / 1e12 / BF16_PEAK_TFLOPS, 4),
     }
 
 
