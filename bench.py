@@ -272,6 +272,48 @@ def bench_kda_sequence(torch, dr, W, reps=10):
     }
 
 
+def bench_long_prefill(torch, dr, W, reps=5):
+    """delta_rule_chunk_fwd on the long-prefill config (B1 H16 T32768, beta in
+    (0,2), S0 != 0): the segment-parallel schedule the binding picks for it,
+    and the plain schedule (workspace=False) for comparison; mean call time
+    with HIP events on the launch stream (the workspace is allocated before
+    timing)."""
+    w = W.get("long_prefill")
+    x = W.generate(w)
+    dev = torch.device("cuda:0")
+    d = {n: (None if t is None else t.to(dev)) for n, t in x.items()}
+    o = torch.empty((w.B, w.T, w.H, w.Dv), dtype=w.torch_dtype, device=dev)
+    st = torch.empty((w.B, w.H, w.Dv, w.Dk), dtype=torch.float32, device=dev)
+    need = dr.chunk_fwd_workspace_bytes(w.B, w.T, w.H, w.Dk, w.Dv, w.chunk)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def timed(workspace):
+        def step():
+            dr.delta_rule_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["S0"], chunk=w.chunk,
+                                    o=o, S_T=st, workspace=workspace)
+        step()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(reps):
+            step()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps / 1e3
+
+    t_seg, t_plain = timed(ws if need > 0 else False), timed(False)
+    _, nbytes = chunk_work(w)
+    return {
+        "workload": (f"long_prefill B{w.B} H{w.H} T{w.T} d{w.Dk} chunk {w.chunk}, bf16 in, "
+                     "beta in (0,2), S0 != 0, fp32 state"),
+        "tokens_per_s": w.B * w.T / t_seg,
+        "mean_call_us": round(t_seg * 1e6, 2),
+        "workspace_bytes": need,
+        "plain_schedule_us": round(t_plain * 1e6, 2),
+        "hbm_frac_algorithmic": round(nbytes / t_seg / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+
 def bench_backward(torch, dr, W, reps=10):
     """delta_rule_chunk_bwd on the layer shape: the checkpointing forward pass
     plus the reverse pass, with upstream gradients for o and S_T (mean time per
@@ -432,6 +474,8 @@ def main():
         out.setdefault("kda", {})["sequence"] = bench_kda_sequence(torch, dr, W)
         log("in-kernel q/k L2 norm: layer shape chunked forward")
         out["qk_l2norm"] = {"chunk": bench_gated_chunk(torch, dr, W, name="layer_1p3b", l2=True)}
+    log("long prefill: B1 H16 T32768, segment-parallel schedule")
+    out["long_prefill"] = bench_long_prefill(torch, dr, W)
     if not args.no_backward:
         log("backward: layer shape")
         out["backward"] = bench_backward(torch, dr, W)

@@ -34,6 +34,7 @@ __all__ = [
     "kda_recurrent_step",
     "kda_fwd",
     "DR_FUSED_RECURRENT",
+    "chunk_fwd_workspace_bytes",
     "delta_rule_status_string",
     "delta_rule_version",
     "DeltaRuleError",
@@ -53,7 +54,8 @@ class dr_chunk_opts(ctypes.Structure):
     """``dr_chunk_opts`` of include/deltarule.h."""
     _fields_ = [("g", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
                 ("num_seqs", ctypes.c_int64), ("scale", ctypes.c_float),
-                ("flags", ctypes.c_uint32), ("gk", ctypes.c_void_p)]
+                ("flags", ctypes.c_uint32), ("gk", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64)]
 
 
 class dr_step_opts(ctypes.Structure):
@@ -96,6 +98,8 @@ def load_library():
     lib.gated_delta_rule_recurrent_step.restype = i32
     lib.gated_delta_rule_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp,
                                                     i64, i64, i64, i64, i32, vp]
+    lib.delta_rule_chunk_fwd_workspace_bytes.restype = i64
+    lib.delta_rule_chunk_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i32]
     lib.delta_rule_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.delta_rule_chunk_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
     lib.delta_rule_chunk_bwd.restype = i32
@@ -169,8 +173,18 @@ DR_QK_L2NORM = 1
 DR_FUSED_RECURRENT = 2
 
 
+def chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk=64, dtype=None):
+    """Bytes of device workspace the segment-parallel schedule of the chunked
+    forward needs for this shape, or 0 when the plain schedule already fills
+    the GPU (``delta_rule_chunk_fwd_workspace_bytes``)."""
+    torch = _torch()
+    code = DR_F32 if dtype == torch.float32 else DR_BF16
+    return int(load_library().delta_rule_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, code))
+
+
 def _chunk_call(gated, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, stream,
-                scale=None, cu_seqlens=None, l2norm=False, gk=None, recurrent=False):
+                scale=None, cu_seqlens=None, l2norm=False, gk=None, recurrent=False,
+                workspace=None):
     torch = _torch()
     dev = q.device
     if dev.type != "cuda":
@@ -213,7 +227,22 @@ def _chunk_call(gated, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, 
     lib = load_library()
     common = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta))
     tail = (B, T, H, Dk, Dv, int(chunk))
-    if scale is None and cu_seqlens is None and not l2norm and gk is None and not recurrent:
+    # segment-parallel schedule for sequences too few to fill the GPU:
+    # workspace=None allocates it when the library asks for one, False never
+    ws_ptr, ws_bytes = None, 0
+    if (workspace is not False and cu_seqlens is None and gk is None and not recurrent
+            and T > 0):
+        if workspace is None:
+            need = lib.delta_rule_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, int(chunk),
+                                                            _dtype_code(q))
+            if need > 0:
+                workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        if workspace is not None and workspace is not False:
+            if workspace.device != dev or not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous tensor on the inputs' GPU")
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if (scale is None and cu_seqlens is None and not l2norm and gk is None and not recurrent
+            and ws_ptr is None):
         if gated:
             st = lib.gated_delta_rule_chunk_fwd(*common, _ptr(g), _ptr(S0), _ptr(o), _ptr(S_T),
                                                 *tail, _dtype_code(q), _stream(dev, stream))
@@ -227,7 +256,8 @@ def _chunk_call(gated, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, 
                              scale=1.0 if scale is None else float(scale),
                              flags=(DR_QK_L2NORM if l2norm else 0)
                              | (DR_FUSED_RECURRENT if recurrent else 0),
-                             gk=None if gk is None else gk.data_ptr())
+                             gk=None if gk is None else gk.data_ptr(),
+                             workspace=ws_ptr, workspace_bytes=ws_bytes)
         st = lib.delta_rule_chunk_fwd_ex(*common, _ptr(S0), _ptr(o), _ptr(S_T), *tail,
                                          ctypes.byref(opts), _dtype_code(q),
                                          _stream(dev, stream))
@@ -238,7 +268,7 @@ def _chunk_call(gated, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, 
 def delta_rule_chunk_fwd(q, k, v, beta, S0=None, *, chunk: int = 64,
                          output_final_state: bool = True, o=None, S_T=None,
                          scale=None, cu_seqlens=None, use_qk_l2norm_in_kernel=False,
-                         fused_recurrent=False, stream=None):
+                         fused_recurrent=False, workspace=None, stream=None):
     """Chunkwise forward.  q, k ``[B,T,H,Dk]``; v ``[B,T,H,Dv]``; beta
     ``[B,T,H]`` (float32 or bfloat16, all the same dtype, on one GPU);
     S0 ``[B,H,Dv,Dk]`` float32 or None.  Returns ``(o, S_T)``; S_T is None
@@ -249,20 +279,23 @@ def delta_rule_chunk_fwd(q, k, v, beta, S0=None, *, chunk: int = 64,
     ``use_qk_l2norm_in_kernel`` normalises the rows of q and k inside the
     kernel (x / sqrt(sum x^2 + 1e-6)).  ``fused_recurrent`` runs the
     token-serial schedule instead of the chunked one (same results up to
-    rounding; for short sequences)."""
+    rounding; for short sequences).  When the sequences are too few to fill
+    the GPU, a device ``workspace`` (allocated here when None; pass False to
+    disable) lets the library run the segment-parallel schedule."""
     return _chunk_call(False, q, k, v, beta, None, S0, chunk, output_final_state, o, S_T,
                        stream, scale, cu_seqlens, use_qk_l2norm_in_kernel,
-                       recurrent=fused_recurrent)
+                       recurrent=fused_recurrent, workspace=workspace)
 
 
 def gated_delta_rule_chunk_fwd(q, k, v, beta, g, S0=None, *, chunk: int = 64,
                                output_final_state: bool = True, o=None, S_T=None,
                                scale=None, cu_seqlens=None, use_qk_l2norm_in_kernel=False,
-                               fused_recurrent=False, stream=None):
+                               fused_recurrent=False, workspace=None, stream=None):
     """Chunkwise forward of the gated rule: as ``delta_rule_chunk_fwd`` plus
     g ``[B,T,H]`` float32, the log of each token's forget gate (<= 0)."""
     return _chunk_call(True, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, stream,
-                       scale, cu_seqlens, use_qk_l2norm_in_kernel, recurrent=fused_recurrent)
+                       scale, cu_seqlens, use_qk_l2norm_in_kernel, recurrent=fused_recurrent,
+                       workspace=workspace)
 
 
 def kda_fwd(q, k, v, beta, gk, S0=None, *, output_final_state: bool = True, o=None, S_T=None,

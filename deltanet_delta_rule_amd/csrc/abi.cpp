@@ -55,7 +55,8 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
                     const float *g, bool gated, const float *S0, void *o, float *S_T,
                     int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t chunk,
                     const int32_t *cu, int64_t nseq, float scale, bool l2, dr_dtype dtype,
-                    void *stream, const float *gk = nullptr, bool recurrent = false) {
+                    void *stream, const float *gk = nullptr, bool recurrent = false,
+                    void *ws = nullptr, int64_t ws_bytes = 0) {
     if (dtype != DR_F32 && dtype != DR_BF16) return DR_ERR_INVALID_ARG;
     if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0 || chunk < 0) return DR_ERR_INVALID_ARG;
     if (cu && (B != 1 || nseq < 0 || !aligned_to(cu, 4))) return DR_ERR_INVALID_ARG;
@@ -80,6 +81,7 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
     if (T > 0 && (!q || !k || !v || !beta || !o)) return DR_ERR_INVALID_ARG;
     if (gated && T > 0 && !g) return DR_ERR_INVALID_ARG;
     if (gk && gated) return DR_ERR_INVALID_ARG;  // one decay kind
+    if (ws && (ws_bytes < 0 || !aligned16(ws))) return DR_ERR_INVALID_ARG;
     // q, k, gk and the states are read in 16-byte vectors; v, beta and o element-wise
     const void *vec_ptrs[] = {q, k, S0, S_T, gk};
     for (const void *p : vec_ptrs)
@@ -92,7 +94,8 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
     const Span in[] = {{q, nqk * esz},        {k, nqk * esz},
                        {v, nv * esz},         {beta, nb * esz},
                        {S0, ns * 4},          {gated ? g : nullptr, nb * 4},
-                       {cu, (nseq + 1) * 4},  {gk, nqk * 4}};
+                       {cu, (nseq + 1) * 4},  {gk, nqk * 4},
+                       {ws, ws ? ws_bytes : 0}};
     const Span so{o, nv * esz}, sst{S_T, ns * 4};
     for (const Span &s : in) {
         if (T > 0 && overlaps(so, s)) return DR_ERR_INVALID_ARG;
@@ -100,11 +103,21 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
         if (overlaps(sst, s) && !(s.p == S0 && S_T == S0)) return DR_ERR_INVALID_ARG;
     }
     if (T > 0 && overlaps(so, sst)) return DR_ERR_INVALID_ARG;
+    if (ws && (overlaps(so, {ws, ws_bytes}) || overlaps(sst, {ws, ws_bytes})))
+        return DR_ERR_INVALID_ARG;
 
     dr::ChunkFwdArgs a{q,       k,        v,       beta,       gated ? g : nullptr,
                        S0,      o,        S_T,     nullptr,    cu,
                        ns_count, T,       H,       (int)Dk,    (int)Dv,
                        (int)chunk, scale, l2,     gk,       recurrent};
+    // one long sequence per head: the segment-parallel schedule, when the
+    // caller gave it a large enough workspace
+    if (ws && !cu && !gk && !recurrent) {
+        const dr::SegPlan pl = dr::seg_plan(B, T, H, (int)Dk, (int)Dv, (int)chunk);
+        if (pl.P > 0 && ws_bytes >= pl.bytes)
+            return hip_status(dr::launch_chunk_fwd_segmented(
+                a, pl, ws, dtype == DR_BF16, static_cast<hipStream_t>(stream)));
+    }
     return hip_status(dr::launch_chunk_fwd(a, dtype == DR_BF16, static_cast<hipStream_t>(stream)));
 }
 
@@ -219,6 +232,15 @@ dr_status delta_rule_chunk_fwd(const void *q, const void *k, const void *v,
                      0, 1.f, false, dtype, stream);
 }
 
+int64_t delta_rule_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                             int64_t Dv, int64_t chunk, dr_dtype dtype) {
+    if (dtype != DR_F32 && dtype != DR_BF16) return -1;
+    if (B < 0 || T < 0 || H < 0 || !supported_dim(Dk) || !supported_dim(Dv) ||
+        !supported_chunk(chunk))
+        return -1;
+    return dr::seg_plan(B, T, H, (int)Dk, (int)Dv, (int)chunk).bytes;
+}
+
 dr_status delta_rule_chunk_fwd_ex(const void *q, const void *k, const void *v,
                                   const void *beta, const float *S0, void *o, float *S_T,
                                   int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
@@ -231,7 +253,8 @@ dr_status delta_rule_chunk_fwd_ex(const void *q, const void *k, const void *v,
         return DR_ERR_INVALID_ARG;  // unknown flags
     return chunk_fwd(q, k, v, beta, x.g, x.g != nullptr, S0, o, S_T, B, T, H, Dk, Dv, chunk,
                      x.cu_seqlens, x.num_seqs, x.scale, (x.flags & DR_QK_L2NORM) != 0, dtype,
-                     stream, x.gk, (x.flags & DR_FUSED_RECURRENT) != 0);
+                     stream, x.gk, (x.flags & DR_FUSED_RECURRENT) != 0, x.workspace,
+                     x.workspace_bytes);
 }
 
 dr_status delta_rule_recurrent_step(const void *q, const void *k,
@@ -300,6 +323,6 @@ const char *delta_rule_status_string(dr_status status) {
 
 int delta_rule_last_hip_error(void) { return g_last_hip_error; }
 
-int delta_rule_version(void) { return 20600; }
+int delta_rule_version(void) { return 20700; }
 
 }  // extern "C"

@@ -846,6 +846,7 @@ struct HeadPtrs {
     int64_t head;                 // sequence * H + head
     int64_t sbase;
     int vcol;
+    bool vz;                      // v == nullptr: every value loads as zero
 };
 
 // Packed variable-length input (cu != nullptr): sequence b spans tokens
@@ -885,6 +886,7 @@ __device__ __forceinline__ HeadPtrs<DT> head_ptrs(const DT *q, const DT *k, cons
     p.gh = gl ? gl + t0 * H + h : nullptr;
     p.head = head;
     p.sbase = ((int64_t)head * Dv + p.vcol) * DK;
+    p.vz = v == nullptr;
     return p;
 }
 
@@ -926,7 +928,7 @@ struct ChunkRegs {
         const int esz = (int)sizeof(DT);
         const auto rk = make_rsrc(p.kh + (int64_t)t0 * p.tsk, len * p.tsk * esz);
         const auto rq = make_rsrc(p.qh + (int64_t)t0 * p.tsk, len * p.tsk * esz);
-        const auto rv = make_rsrc(p.vh + (int64_t)t0 * p.tsv, len * p.tsv * esz);
+        const auto rv = make_rsrc(p.vh + (int64_t)t0 * p.tsv, p.vz ? 0 : len * p.tsv * esz);
         const auto rb = make_rsrc(p.bh + (int64_t)t0 * p.tsb, len * p.tsb * esz);
 #pragma unroll
         for (int j = 0; j < G::NPRE; ++j) {
@@ -1028,7 +1030,7 @@ struct DmaStage {
         const int len = max(0, min(C, T - t0));
         const auto rk = make_rsrc(p.kh + (int64_t)t0 * p.tsk, len * p.tsk * ESZ);
         const auto rq = make_rsrc(p.qh + (int64_t)t0 * p.tsk, len * p.tsk * ESZ);
-        const auto rv = make_rsrc(p.vh + (int64_t)t0 * p.tsv, len * p.tsv * ESZ);
+        const auto rv = make_rsrc(p.vh + (int64_t)t0 * p.tsv, p.vz ? 0 : len * p.tsv * ESZ);
 #pragma unroll
         for (int i = 0; i < NMINE; ++i) {
             const int j = W + i * NW;

@@ -35,6 +35,17 @@ struct ChunkFwdArgs {
 
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
 hipError_t launch_fused_recurrent(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
+// Segment-parallel schedule of the chunked forward (plain or gated rule, no
+// packed sequences): P segments of L tokens (a multiple of the chunk), and
+// the workspace it needs; P = 0 when the plain schedule fills the GPU anyway.
+struct SegPlan {
+    int P, L;
+    int64_t bytes;
+};
+SegPlan seg_plan(int64_t B, int64_t T, int64_t H, int Dk, int Dv, int chunk);
+hipError_t launch_chunk_fwd_segmented(const ChunkFwdArgs &a, const SegPlan &pl, void *ws,
+                                      bool bf16, hipStream_t stream);
+
 // Chunked KDA (per-channel decay): bf16, d_k = 128, d_v a multiple of 64;
 // other cases run the token-serial kernel.
 bool kda_chunk_supported(const ChunkFwdArgs &a, bool bf16);

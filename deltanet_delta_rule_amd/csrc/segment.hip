@@ -1,0 +1,194 @@
+// Segment-parallel schedule of the chunked forward for sequences too few to
+// fill the GPU (one long prefill: B = 1, H = 16 gives the chunk kernel 32
+// workgroups for 256 CUs).
+//
+// The map from a segment's incoming state to its outgoing state is affine:
+// every token applies S <- S A_t + beta_t v_t k_t^T with A_t = alpha_t (I -
+// beta_t k_t k_t^T) (alpha_t = 1 for the plain rule), so over a segment
+//   S_out = S_in M + H,   M = A_first ... A_last,   H = S_out from S_in = 0
+// (hada.io digest, sections "Chunkwise KDA" and "Transition diagonale-bas
+// rang": the state update is a product of transitions plus rank-one writes;
+// the composition of segments follows from it).  The sequence is cut into P
+// segments of whole chunks and, with the existing chunk kernel on the
+// segments as packed sequences:
+//   1. H_p: each segment from a zero state, no outputs;
+//   2. M_p: each segment with v = 0 from S = I (d_k value rows), no outputs;
+//   3. a short chain per (sequence, head, 16 state rows):
+//      S_in(p) = S_in(p-1) M_{p-1} + H_{p-1} in fp32, which also gives S_T;
+//   4. each segment from its true S_in, writing the outputs.
+// Steps 1, 2 and 4 run P times as many workgroups as the plain schedule; the
+// total work is about three plain passes, and a chunk step costs more when
+// the whole GPU shares HBM (~2.4 us against ~1.7 us for a few workgroups at
+// d = 128), so the schedule is used only with at least six segments of at
+// least sixteen chunks each (measured: B1 H16 T32768 with 8 segments runs in
+// 0.59x the time of the plain schedule; B4 H8 T2048 with 8 segments of 4
+// chunks in 1.45x).
+#include <algorithm>
+
+#include "dr_common.hpp"
+#include "dr_launch.hpp"
+
+namespace dr {
+
+namespace {
+
+constexpr int SEG_CUS = 256;      // compute units of one MI355X
+constexpr int SEG_MIN = 6;        // fewest segments worth three passes
+constexpr int SEG_MIN_CHUNKS = 16;  // shortest segment, in chunks
+
+// Identity initial state of the M pass and the segment offsets (one packed
+// row of B * T tokens; segment p of sequence b covers tokens b T + p L ..
+// b T + min((p + 1) L, T)).
+__global__ __launch_bounds__(256) void seg_init_kernel(float *M, int *cu, int64_t nmat, int Dk,
+                                                       int B, int P, int T, int L) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t per = (int64_t)Dk * Dk;
+    if (i < nmat * per) {
+        const int64_t e = i % per;
+        M[i] = (e / Dk == e % Dk) ? 1.f : 0.f;
+    }
+    if (i <= (int64_t)B * P) {
+        const int b = (int)(i / P), p = (int)(i % P);
+        cu[i] = i == (int64_t)B * P ? B * T : b * T + min(p * L, T);
+    }
+}
+
+// The chain over segments for 16 state rows of one (sequence, head): lane
+// group (row i, columns j0 .. j0 + CK - 1) keeps its part of S in registers;
+// S and each M_p are staged in LDS.  Hs holds H_p on entry and S_in(p) on
+// exit (each workgroup touches only its own rows).
+template <int DK>
+__global__ __launch_bounds__(256) void seg_chain_kernel(float *Hs, const float *M,
+                                                        const float *S0, float *S_T, int P,
+                                                        int H, int Dv) {
+    constexpr int CK = DK / 16;  // columns per lane
+    __shared__ __attribute__((aligned(16))) float Ms[DK * DK];
+    __shared__ __attribute__((aligned(16))) float Ss[16 * DK];
+    const int nrt = Dv / 16;
+    const int rt = blockIdx.x % nrt;
+    const int64_t bh = blockIdx.x / nrt;  // b * H + h
+    const int64_t b = bh / H, h = bh % H;
+    const int tid = threadIdx.x, i = tid / 16, j0 = (tid % 16) * CK;
+    const int row = rt * 16 + i;
+
+    float s[CK];
+#pragma unroll
+    for (int c = 0; c < CK; ++c)
+        s[c] = S0 ? S0[(bh * Dv + row) * DK + j0 + c] : 0.f;
+#pragma unroll
+    for (int c = 0; c < CK; ++c) Ss[i * DK + j0 + c] = s[c];
+    for (int p = 0; p < P; ++p) {
+        const int64_t seg = b * P + p;
+        float *hp = Hs + ((seg * H + h) * Dv + row) * DK + j0;
+        const float *mp = M + (seg * H + h) * DK * DK;
+        float hv[CK];
+#pragma unroll
+        for (int c = 0; c < CK; ++c) {
+            hv[c] = hp[c];
+            hp[c] = s[c];  // S_in of segment p
+        }
+        for (int e = tid; e < DK * DK / 4; e += 256)
+            reinterpret_cast<float4 *>(Ms)[e] = reinterpret_cast<const float4 *>(mp)[e];
+        __syncthreads();
+        float acc[CK];
+#pragma unroll
+        for (int c = 0; c < CK; ++c) acc[c] = hv[c];
+        for (int k = 0; k < DK; ++k) {
+            const float sk = Ss[i * DK + k];
+#pragma unroll
+            for (int c = 0; c < CK; ++c) acc[c] += sk * Ms[k * DK + j0 + c];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < CK; ++c) {
+            s[c] = acc[c];
+            Ss[i * DK + j0 + c] = acc[c];
+        }
+    }
+    if (S_T) {
+#pragma unroll
+        for (int c = 0; c < CK; ++c) S_T[(bh * Dv + row) * DK + j0 + c] = s[c];
+    }
+}
+
+template <int DK>
+hipError_t launch_chain(float *Hs, const float *M, const float *S0, float *S_T, int64_t B, int P,
+                        int64_t H, int Dv, hipStream_t stream) {
+    const int64_t grid = B * H * (Dv / 16);
+    hipLaunchKernelGGL((seg_chain_kernel<DK>), dim3((unsigned)grid), dim3(256), 0, stream, Hs,
+                       M, S0, S_T, P, (int)H, Dv);
+    return hipGetLastError();
+}
+
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+SegPlan seg_plan(int64_t B, int64_t T, int64_t H, int Dk, int Dv, int chunk) {
+    SegPlan pl{0, 0, 0};
+    if (B <= 0 || T <= 0 || H <= 0 || chunk <= 0 || B * T > INT32_MAX) return pl;
+    const int64_t units = B * H * std::max(1, Dv / 64);  // workgroups of the plain schedule
+    int64_t P = std::min<int64_t>(SEG_CUS / std::max<int64_t>(units, 1),
+                                  T / (SEG_MIN_CHUNKS * chunk));
+    if (P < SEG_MIN) return pl;
+    const int64_t L = ((T + P - 1) / P + chunk - 1) / chunk * chunk;
+    P = (T + L - 1) / L;
+    if (P < SEG_MIN) return pl;
+    pl.P = (int)P;
+    pl.L = (int)L;
+    const int64_t nseg = B * P;
+    pl.bytes = align256(nseg * H * (int64_t)Dv * Dk * 4) +     // H_p, then S_in(p)
+               align256(nseg * H * (int64_t)Dk * Dk * 4) +     // M_p
+               align256((nseg + 1) * 4);                        // segment offsets
+    return pl;
+}
+
+hipError_t launch_chunk_fwd_segmented(const ChunkFwdArgs &a, const SegPlan &pl, void *ws,
+                                      bool bf16, hipStream_t stream) {
+    const int64_t nseg = a.B * pl.P;
+    char *base = static_cast<char *>(ws);
+    float *Hs = reinterpret_cast<float *>(base);
+    float *M = reinterpret_cast<float *>(base + align256(nseg * a.H * (int64_t)a.Dv * a.Dk * 4));
+    int *cu = reinterpret_cast<int *>(reinterpret_cast<char *>(M) +
+                                      align256(nseg * a.H * (int64_t)a.Dk * a.Dk * 4));
+    const int64_t nmat = nseg * a.H;
+    const int64_t n_init = std::max<int64_t>(nmat * a.Dk * a.Dk, nseg + 1);
+    hipLaunchKernelGGL(seg_init_kernel, dim3((unsigned)((n_init + 255) / 256)), dim3(256), 0,
+                       stream, M, cu, nmat, a.Dk, (int)a.B, pl.P, (int)a.T, pl.L);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    ChunkFwdArgs s = a;  // the segments as packed sequences of one row of B*T tokens
+    s.cu = cu;
+    s.B = nseg;
+    s.T = a.B * a.T;
+    s.h = nullptr;
+    // 1. H_p from zero states, no outputs
+    s.S0 = nullptr;
+    s.o = nullptr;
+    s.S_T = Hs;
+    if ((e = launch_chunk_fwd(s, bf16, stream)) != hipSuccess) return e;
+    // 2. M_p: v = 0, S = I in place, d_k value rows
+    ChunkFwdArgs m = s;
+    m.v = nullptr;
+    m.Dv = a.Dk;
+    m.S0 = M;
+    m.S_T = M;
+    if ((e = launch_chunk_fwd(m, bf16, stream)) != hipSuccess) return e;
+    // 3. the chain: S_in(p) into Hs, and the final state
+    switch (a.Dk) {
+    case 16: e = launch_chain<16>(Hs, M, a.S0, a.S_T, a.B, pl.P, a.H, a.Dv, stream); break;
+    case 32: e = launch_chain<32>(Hs, M, a.S0, a.S_T, a.B, pl.P, a.H, a.Dv, stream); break;
+    case 64: e = launch_chain<64>(Hs, M, a.S0, a.S_T, a.B, pl.P, a.H, a.Dv, stream); break;
+    case 128: e = launch_chain<128>(Hs, M, a.S0, a.S_T, a.B, pl.P, a.H, a.Dv, stream); break;
+    default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    // 4. outputs from the true incoming states
+    s.S0 = Hs;
+    s.S_T = nullptr;
+    s.o = a.o;
+    return launch_chunk_fwd(s, bf16, stream);
+}
+
+}  // namespace dr

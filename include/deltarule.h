@@ -164,6 +164,21 @@ enum {
  *               per token guarantees it) and gk <= 0; outside that domain the
  *               results lose accuracy (nothing overflows).  All other cases
  *               run the token-serial schedule, exact for any gk.
+ *   workspace, workspace_bytes
+ *               device scratch (16-byte aligned, not overlapping any argument)
+ *               for the segment-parallel schedule, or NULL.  When the
+ *               sequences are too few to fill the GPU (say B = 1, H = 16,
+ *               T = 32768), the plain and gated rules without cu_seqlens cut
+ *               each sequence into P segments of whole chunks, run them in
+ *               parallel from zero states and (with v = 0) from S = I to get
+ *               each segment's affine state map S_out = S_in M + H, chain the
+ *               maps in fp32, and run the segments again from their true
+ *               incoming states for the outputs (about three passes of work
+ *               on P times as many workgroups).  Used only when
+ *               workspace_bytes >= delta_rule_chunk_fwd_workspace_bytes(...)
+ *               > 0; otherwise the plain schedule runs and the workspace is
+ *               not touched.  Results agree with the plain schedule up to
+ *               rounding.
  */
 typedef struct dr_chunk_opts {
     const float *g;
@@ -172,7 +187,18 @@ typedef struct dr_chunk_opts {
     float scale;
     uint32_t flags;
     const float *gk;
+    void *workspace;
+    int64_t workspace_bytes;
 } dr_chunk_opts;
+
+/*
+ * Bytes of workspace for the segment-parallel schedule of
+ * delta_rule_chunk_fwd_ex on this shape (B sequences of T tokens), or 0 when
+ * the plain schedule already fills the GPU (the schedule is then never used);
+ * -1 for an unsupported dtype, dimension or chunk.  Pure host arithmetic.
+ */
+int64_t delta_rule_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk,
+                                             int64_t Dv, int64_t chunk, dr_dtype dtype);
 
 /*
  * delta_rule_chunk_fwd_ex -- delta_rule_chunk_fwd with the options above
@@ -327,7 +353,8 @@ int delta_rule_last_hip_error(void);
  * entry points; 2.1.0: delta_rule_chunk_fwd_ex; 2.2.0: DR_QK_L2NORM; 2.3.0:
  * delta_rule_recurrent_step_ex; 2.4.0: delta_rule_chunk_bwd; 2.5.0: per-channel
  * decay (gk) in dr_step_opts; 2.6.0: DR_FUSED_RECURRENT and gk in
- * dr_chunk_opts). */
+ * dr_chunk_opts; 2.7.0: the segment-parallel schedule's workspace in
+ * dr_chunk_opts and delta_rule_chunk_fwd_workspace_bytes). */
 int delta_rule_version(void);
 
 #ifdef __cplusplus

@@ -211,17 +211,20 @@ def _ex(lib, opts=None, q=P[0], k=P[1], v=P[2], beta=P[3], S0=None, o=P[4], S_T=
 
 
 def _opts(**kw):
-    o = dr.dr_chunk_opts(g=None, cu_seqlens=None, num_seqs=0, scale=1.0, flags=0, gk=None)
+    o = dr.dr_chunk_opts(g=None, cu_seqlens=None, num_seqs=0, scale=1.0, flags=0, gk=None,
+                         workspace=None, workspace_bytes=0)
     for name, val in kw.items():
         setattr(o, name, val)
     return o
 
 
 def test_chunk_options_struct_layout():
-    # pointer, pointer, int64, float, uint32, pointer: 40 bytes, no padding
-    assert ctypes.sizeof(dr.dr_chunk_opts) == 40
+    # pointer, pointer, int64, float, uint32, pointer, pointer, int64: 56 bytes
+    assert ctypes.sizeof(dr.dr_chunk_opts) == 56
     assert dr.dr_chunk_opts.scale.offset == 24 and dr.dr_chunk_opts.flags.offset == 28
     assert dr.dr_chunk_opts.gk.offset == 32
+    assert dr.dr_chunk_opts.workspace.offset == 40
+    assert dr.dr_chunk_opts.workspace_bytes.offset == 48
 
 
 @pytest.mark.parametrize("kw, call", [
@@ -240,6 +243,9 @@ def test_chunk_options_struct_layout():
     (dict(gk=P[4].value), {}),                                   # channel decay overlaps o
     (dict(gk=P[7].value, g=P[6].value), {}),                     # both decay kinds
     (dict(gk=P[7].value, flags=3), dict(S_T=P[7])),              # S_T overlaps gk
+    (dict(workspace=MISALIGNED.value, workspace_bytes=1 << 20), {}),   # workspace misaligned
+    (dict(workspace=P[4].value, workspace_bytes=1 << 20), {}),         # workspace overlaps o
+    (dict(workspace=P[7].value, workspace_bytes=-1), {}),              # negative size
 ])
 def test_chunk_ex_rejects_invalid(lib, kw, call):
     assert _ex(lib, _opts(**kw), **call) == dr.DR_ERR_INVALID_ARG
@@ -323,3 +329,25 @@ def test_backward_rejects_invalid(lib, kw):
 def test_backward_rejects_unsupported_and_empty(lib):
     assert _bwd(lib, Dk=48) == dr.DR_ERR_UNSUPPORTED
     assert _bwd(lib, B=0) == dr.DR_OK
+
+
+# ------------------------------------------- segment-parallel workspace size
+def test_chunk_fwd_workspace_bytes(lib):
+    f = lib.delta_rule_chunk_fwd_workspace_bytes
+    f.restype = ctypes.c_int64
+    f.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int]
+    # one long prefill (B1 H16 T32768 d128): 8 segments of 4096 tokens;
+    # H_p / S_in and M_p in fp32 plus the offsets
+    seg = 8 * 16 * 128 * 128 * 4
+    assert f(1, 32768, 16, 128, 128, 64, dr.DR_BF16) == 2 * seg + 256
+    # the 1.3B layer shape fills the GPU with the plain schedule
+    assert f(8, 2048, 16, 128, 128, 64, dr.DR_BF16) == 0
+    # too short to cut into six segments of sixteen chunks
+    assert f(1, 6000, 2, 128, 128, 64, dr.DR_BF16) == 0
+    # a batch of small sequences: more segments would not pay for three passes
+    assert f(4, 2048, 8, 64, 64, 64, dr.DR_BF16) == 0
+    assert f(1, 0, 16, 128, 128, 64, dr.DR_BF16) == 0
+    # invalid arguments
+    assert f(1, 32768, 16, 48, 128, 64, dr.DR_BF16) == -1
+    assert f(1, 32768, 16, 128, 128, 100, dr.DR_BF16) == -1
+    assert f(1, 32768, 16, 128, 128, 64, 7) == -1
