@@ -8,7 +8,8 @@
 //   S_out = S_in M + H,   M = A_first ... A_last,   H = S_out from S_in = 0
 // (hada.io digest, sections "Chunkwise KDA" and "Transition diagonale-bas
 // rang": the state update is a product of transitions plus rank-one writes;
-// the composition of segments follows from it).  The sequence is cut into P
+// paperlayer summary of arXiv:2406.06484, section 5: associative
+// matrix-valued state updates; the composition of segments follows).  The sequence is cut into P
 // segments of whole chunks and, with the existing chunk kernel on the
 // segments as packed sequences:
 //   1. H_p: each segment from a zero state, no outputs;
