@@ -22,9 +22,14 @@ JSON line on stdout:
   qk_l2norm    the layer shape with raw q, k normalised inside the kernel
   backward     delta_rule_chunk_bwd on the layer shape (checkpointing forward
                and reverse pass), time per call and ratio to the forward launch
+  kda          per-key-channel decay: decode steps and the chunked forward
+  long_prefill the long-prefill config (B1 H16 T32768) through the
+               segment-parallel schedule, with the plain schedule beside it
 
 Options: --gpus N (only 1: this build targets one GPU), --steps K,
 --warmup W, --no-cpu-baseline, --no-decode, --no-gated, --no-backward,
+--no-long-prefill (its segment passes launch the benchmark's kernel on
+other shapes; counter and trace runs of the benchmark line skip it),
 --copy-calib BYTES (also time a
 plain device copy of that size, for counter calibration runs).
 """
@@ -366,6 +371,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward line")
+    ap.add_argument("--no-long-prefill", action="store_true",
+                    help="skip the long-prefill line")
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the gated-rule lines (chunked layer shape and decode)")
     ap.add_argument("--copy-calib", type=int, default=0,
@@ -474,8 +481,9 @@ def main():
         out.setdefault("kda", {})["sequence"] = bench_kda_sequence(torch, dr, W)
         log("in-kernel q/k L2 norm: layer shape chunked forward")
         out["qk_l2norm"] = {"chunk": bench_gated_chunk(torch, dr, W, name="layer_1p3b", l2=True)}
-    log("long prefill: B1 H16 T32768, segment-parallel schedule")
-    out["long_prefill"] = bench_long_prefill(torch, dr, W)
+    if not args.no_long_prefill:
+        log("long prefill: B1 H16 T32768, segment-parallel schedule")
+        out["long_prefill"] = bench_long_prefill(torch, dr, W)
     if not args.no_backward:
         log("backward: layer shape")
         out["backward"] = bench_backward(torch, dr, W)

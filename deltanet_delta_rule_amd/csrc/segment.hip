@@ -37,16 +37,18 @@ constexpr int SEG_CUS = 256;      // compute units of one MI355X
 constexpr int SEG_MIN = 6;        // fewest segments worth three passes
 constexpr int SEG_MIN_CHUNKS = 16;  // shortest segment, in chunks
 
-// Identity initial state of the M pass and the segment offsets (one packed
-// row of B * T tokens; segment p of sequence b covers tokens b T + p L ..
-// b T + min((p + 1) L, T)).
+// Identity initial state of the M pass (one float4 per thread) and the
+// segment offsets (one packed row of B * T tokens; segment p of sequence b
+// covers tokens b T + p L .. b T + min((p + 1) L, T)).
 __global__ __launch_bounds__(256) void seg_init_kernel(float *M, int *cu, int64_t nmat, int Dk,
                                                        int B, int P, int T, int L) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t per = (int64_t)Dk * Dk;
-    if (i < nmat * per) {
-        const int64_t e = i % per;
-        M[i] = (e / Dk == e % Dk) ? 1.f : 0.f;
+    if (i < nmat * per / 4) {
+        const int64_t e = (i * 4) % per;
+        const int64_t r = e / Dk, c = e % Dk;  // four consecutive columns of row r
+        reinterpret_cast<float4 *>(M)[i] = make_float4(r == c ? 1.f : 0.f, r == c + 1 ? 1.f : 0.f,
+                                                       r == c + 2 ? 1.f : 0.f, r == c + 3 ? 1.f : 0.f);
     }
     if (i <= (int64_t)B * P) {
         const int b = (int)(i / P), p = (int)(i % P);
@@ -54,61 +56,128 @@ __global__ __launch_bounds__(256) void seg_init_kernel(float *M, int *cu, int64_
     }
 }
 
-// The chain over segments for 16 state rows of one (sequence, head): lane
-// group (row i, columns j0 .. j0 + CK - 1) keeps its part of S in registers;
-// S and each M_p are staged in LDS.  Hs holds H_p on entry and S_in(p) on
-// exit (each workgroup touches only its own rows).
+// The chain over segments for 16 state rows of one (sequence, head), on the
+// fp32 matrix cores: wave w computes the output columns 16 (w + 4 j) .. of
+// S M_p (16 x 16 tiles, D layout: lane (g, r) holds rows 4g .. 4g + 3 of
+// column r), contracting over d_k four keys at a time with S and M_p staged
+// in LDS.  Hs holds H_p on entry and S_in(p) on exit (each workgroup touches
+// only its own rows).
 template <int DK>
 __global__ __launch_bounds__(256) void seg_chain_kernel(float *Hs, const float *M,
                                                         const float *S0, float *S_T, int P,
                                                         int H, int Dv) {
-    constexpr int CK = DK / 16;  // columns per lane
-    __shared__ __attribute__((aligned(16))) float Ms[DK * DK];
-    __shared__ __attribute__((aligned(16))) float Ss[16 * DK];
+    constexpr int NT = DK / 16;                 // output tiles per row block
+    constexpr int TPW = (NT + 3) / 4;           // tiles per wave
+    constexpr int LDSS = DK + 4;                // S row pitch (floats)
+    constexpr int LDM = DK + 16;                // M row pitch: lane groups on distinct banks
+    __shared__ __attribute__((aligned(16))) float Ms[DK * LDM];
+    __shared__ __attribute__((aligned(16))) float Ss[16 * LDSS];
     const int nrt = Dv / 16;
     const int rt = blockIdx.x % nrt;
     const int64_t bh = blockIdx.x / nrt;  // b * H + h
     const int64_t b = bh / H, h = bh % H;
-    const int tid = threadIdx.x, i = tid / 16, j0 = (tid % 16) * CK;
-    const int row = rt * 16 + i;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int g = lane >> 4, r = lane & 15;
+    const int row0 = rt * 16;
 
-    float s[CK];
+    constexpr int NMV = DK * DK / 4 / 256 > 0 ? DK * DK / 4 / 256 : 1;  // float4 of M per thread
+    const int nmv = DK * DK / 4;
+
+    // S in D layout: tile j of this wave (if any), lane (g, r): rows 4g + e,
+    // column 16 n + r with n = wave + 4 j
+    f32x4 s[TPW];
 #pragma unroll
-    for (int c = 0; c < CK; ++c)
-        s[c] = S0 ? S0[(bh * Dv + row) * DK + j0 + c] : 0.f;
+    for (int j = 0; j < TPW; ++j) {
+        const int n = wave + 4 * j;
 #pragma unroll
-    for (int c = 0; c < CK; ++c) Ss[i * DK + j0 + c] = s[c];
+        for (int e = 0; e < 4; ++e) {
+            const int row = row0 + 4 * g + e;
+            s[j][e] = (n < NT && S0) ? S0[(bh * Dv + row) * DK + 16 * n + r] : 0.f;
+            if (n < NT) Ss[(4 * g + e) * LDSS + 16 * n + r] = s[j][e];
+        }
+    }
+    // M_p and this lane's H_p entries travel in registers one step ahead
+    float4 mreg[NMV];
+    f32x4 hreg[TPW];
+    auto fetch = [&](int p) {
+        const int64_t seg = b * P + p;
+        const float4 *mp = reinterpret_cast<const float4 *>(M + (seg * H + h) * DK * DK);
+#pragma unroll
+        for (int u = 0; u < NMV; ++u) {
+            const int e = tid + 256 * u;
+            mreg[u] = e < nmv ? mp[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        const float *hp = Hs + ((seg * H + h) * Dv + row0) * DK;
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int n = wave + 4 * j;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hreg[j][e] = n < NT ? hp[(4 * g + e) * DK + 16 * n + r] : 0.f;
+        }
+    };
+    if (P > 0) fetch(0);
     for (int p = 0; p < P; ++p) {
         const int64_t seg = b * P + p;
-        float *hp = Hs + ((seg * H + h) * Dv + row) * DK + j0;
-        const float *mp = M + (seg * H + h) * DK * DK;
-        float hv[CK];
+        float *hp = Hs + ((seg * H + h) * Dv + row0) * DK;
+        // M_p into LDS, S_in(p) over H_p, accumulators start at H_p
 #pragma unroll
-        for (int c = 0; c < CK; ++c) {
-            hv[c] = hp[c];
-            hp[c] = s[c];  // S_in of segment p
+        for (int u = 0; u < NMV; ++u) {
+            const int e = tid + 256 * u;
+            if (e < nmv) {
+                const int row = 4 * e / DK, col = 4 * e % DK;
+                *reinterpret_cast<float4 *>(Ms + row * LDM + col) = mreg[u];
+            }
         }
-        for (int e = tid; e < DK * DK / 4; e += 256)
-            reinterpret_cast<float4 *>(Ms)[e] = reinterpret_cast<const float4 *>(mp)[e];
+        f32x4 acc[TPW][2];
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int n = wave + 4 * j;
+            acc[j][0] = hreg[j];
+            acc[j][1] = zero4();
+            if (n < NT) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hp[(4 * g + e) * DK + 16 * n + r] = s[j][e];
+            }
+        }
         __syncthreads();
-        float acc[CK];
+        if (p + 1 < P) fetch(p + 1);
+        // acc += S M_p: A = S rows (lane (g, r): S[r][k0 + g]), B = M_p
+        // (lane (g, r): M[k0 + g][16 n + r]); two chains per tile
+#pragma unroll 4
+        for (int k0 = 0; k0 < DK; k0 += 8) {
+            const float a0 = Ss[r * LDSS + k0 + g], a1 = Ss[r * LDSS + k0 + 4 + g];
 #pragma unroll
-        for (int c = 0; c < CK; ++c) acc[c] = hv[c];
-        for (int k = 0; k < DK; ++k) {
-            const float sk = Ss[i * DK + k];
-#pragma unroll
-            for (int c = 0; c < CK; ++c) acc[c] += sk * Ms[k * DK + j0 + c];
+            for (int j = 0; j < TPW; ++j) {
+                const int n = wave + 4 * j;
+                if (n < NT) {
+                    acc[j][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                        a0, Ms[(k0 + g) * LDM + 16 * n + r], acc[j][0], 0, 0, 0);
+                    acc[j][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                        a1, Ms[(k0 + 4 + g) * LDM + 16 * n + r], acc[j][1], 0, 0, 0);
+                }
+            }
         }
         __syncthreads();
 #pragma unroll
-        for (int c = 0; c < CK; ++c) {
-            s[c] = acc[c];
-            Ss[i * DK + j0 + c] = acc[c];
+        for (int j = 0; j < TPW; ++j) {
+            const int n = wave + 4 * j;
+            s[j] = acc[j][0] + acc[j][1];
+            if (n < NT) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Ss[(4 * g + e) * LDSS + 16 * n + r] = s[j][e];
+            }
         }
     }
     if (S_T) {
 #pragma unroll
-        for (int c = 0; c < CK; ++c) S_T[(bh * Dv + row) * DK + j0 + c] = s[c];
+        for (int j = 0; j < TPW; ++j) {
+            const int n = wave + 4 * j;
+            if (n < NT) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    S_T[(bh * Dv + row0 + 4 * g + e) * DK + 16 * n + r] = s[j][e];
+            }
+        }
     }
 }
 
@@ -153,7 +222,7 @@ hipError_t launch_chunk_fwd_segmented(const ChunkFwdArgs &a, const SegPlan &pl, 
     int *cu = reinterpret_cast<int *>(reinterpret_cast<char *>(M) +
                                       align256(nseg * a.H * (int64_t)a.Dk * a.Dk * 4));
     const int64_t nmat = nseg * a.H;
-    const int64_t n_init = std::max<int64_t>(nmat * a.Dk * a.Dk, nseg + 1);
+    const int64_t n_init = std::max<int64_t>(nmat * a.Dk * a.Dk / 4, nseg + 1);
     hipLaunchKernelGGL(seg_init_kernel, dim3((unsigned)((n_init + 255) / 256)), dim3(256), 0,
                        stream, M, cu, nmat, a.Dk, (int)a.B, pl.P, (int)a.T, pl.L);
     hipError_t e = hipGetLastError();
