@@ -230,8 +230,7 @@ def _chunk_call(gated, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, 
     # segment-parallel schedule for sequences too few to fill the GPU:
     # workspace=None allocates it when the library asks for one, False never
     ws_ptr, ws_bytes = None, 0
-    if (workspace is not False and cu_seqlens is None and gk is None and not recurrent
-            and T > 0):
+    if workspace is not False and cu_seqlens is None and not recurrent and T > 0:
         if workspace is None:
             need = lib.delta_rule_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, int(chunk),
                                                             _dtype_code(q))
@@ -300,7 +299,7 @@ def gated_delta_rule_chunk_fwd(q, k, v, beta, g, S0=None, *, chunk: int = 64,
 
 def kda_fwd(q, k, v, beta, gk, S0=None, *, output_final_state: bool = True, o=None, S_T=None,
             scale=None, cu_seqlens=None, use_qk_l2norm_in_kernel=False, fused_recurrent=False,
-            stream=None):
+            workspace=None, stream=None):
     """Forward of Kimi Delta Attention over whole sequences: as
     ``delta_rule_chunk_fwd`` plus gk ``[B,T,H,Dk]`` float32, the log decay
     (<= 0) of each key channel at each token (column j of the state is
@@ -308,10 +307,12 @@ def kda_fwd(q, k, v, beta, gk, S0=None, *, output_final_state: bool = True, o=No
     Dv a multiple of 64 run the chunked kernel (32-token chunks; accurate while
     gk summed over any 8 consecutive tokens of a channel stays above -40, e.g.
     gk >= -5); everything else, or ``fused_recurrent=True``, runs the
-    token-serial schedule, which has no such limit."""
+    token-serial schedule, which has no such limit.  Long sequences that do
+    not fill the GPU run the chunked kernel segment-parallel (``workspace``
+    as in ``delta_rule_chunk_fwd``)."""
     return _chunk_call(False, q, k, v, beta, None, S0, 64, output_final_state, o, S_T, stream,
                        scale, cu_seqlens, use_qk_l2norm_in_kernel, gk=gk,
-                       recurrent=fused_recurrent)
+                       recurrent=fused_recurrent, workspace=workspace)
 
 
 def _step_call(gated, q, k, v, beta, g, S, o, stream, scale=None, l2norm=False, gk=None):

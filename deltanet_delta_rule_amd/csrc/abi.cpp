@@ -112,7 +112,7 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
                        (int)chunk, scale, l2,     gk,       recurrent};
     // one long sequence per head: the segment-parallel schedule, when the
     // caller gave it a large enough workspace
-    if (ws && !cu && !gk && !recurrent) {
+    if (ws && !cu && !recurrent && (!gk || dr::kda_chunk_supported(a, dtype == DR_BF16))) {
         const dr::SegPlan pl = dr::seg_plan(B, T, H, (int)Dk, (int)Dv, (int)chunk);
         if (pl.P > 0 && ws_bytes >= pl.bytes)
             return hip_status(dr::launch_chunk_fwd_segmented(

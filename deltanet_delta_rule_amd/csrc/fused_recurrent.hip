@@ -229,7 +229,7 @@ __device__ __forceinline__ void fr_token(FrTok<DECAY> &t, float (&s)[8], int sub
         oq += s[e] * t.q[e];
     }
     oq = row_sum<LPR>(oq);                 // read after the write
-    if (live && sub == 0) *o_row = from_f32<DT>(oq * scale);
+    if (live && sub == 0 && o_row) *o_row = from_f32<DT>(oq * scale);
 }
 
 // Grid: (sequence, head, row slab) flattened, slab fastest.  cu (packed
@@ -301,10 +301,10 @@ __global__ __launch_bounds__(256) void fused_recurrent_kernel(
         tok_load<DT, DK, DECAY>(buf, 0, sub, rloc, ta);
         for (int i = 0; i < nt; i += 2) {
             tok_load<DT, DK, DECAY>(buf, min(i + 1, C::TB - 1), sub, rloc, tb);
-            fr_token<DK, DECAY, L2>(ta, s, sub, live, o + sr.row(t0 + i) * Dv + row, scale);
+            fr_token<DK, DECAY, L2>(ta, s, sub, live, o ? o + sr.row(t0 + i) * Dv + row : nullptr, scale);
             if (i + 1 >= nt) break;
             tok_load<DT, DK, DECAY>(buf, min(i + 2, C::TB - 1), sub, rloc, ta);
-            fr_token<DK, DECAY, L2>(tb, s, sub, live, o + sr.row(t0 + i + 1) * Dv + row, scale);
+            fr_token<DK, DECAY, L2>(tb, s, sub, live, o ? o + sr.row(t0 + i + 1) * Dv + row : nullptr, scale);
         }
         if (more) stage_store<DT, DK, DECAY>(st, smem + ((j + 1) & 1) * C::BUF);
         lds_barrier();

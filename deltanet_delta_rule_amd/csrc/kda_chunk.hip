@@ -138,12 +138,13 @@ __device__ __forceinline__ void kp_prefetch(KdaRegs &x, const KdaSeq &sq, int t0
     x.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, min(tid, KP_C - 1) * sq.H * 2, 0, 0);
 }
 
-// v[t0 + 16 I + 4 g + e][vcol] for I < 2, e < 4 (the D layout of X).
+// v[t0 + 16 I + 4 g + e][vcol] for I < 2, e < 4 (the D layout of X); v ==
+// nullptr loads zeros.
 __device__ __forceinline__ void kp_prefetch_v(unsigned short (&vr)[8], const KdaSeq &sq, int t0,
                                               int g, int vcol) {
     const int nv = min(KP_C, sq.len - t0);
     const int sv = sq.H * sq.Dv * 2;
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(sq.v + sq.row(t0) * sq.Dv, nv * sv);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(sq.v + sq.row(t0) * sq.Dv, sq.v ? nv * sv : 0);
 #pragma unroll
     for (int I = 0; I < 2; ++I)
 #pragma unroll
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(512) void kda_pipe_kernel(
             if (it + 1 < nchunk) kp_prefetch_v(vr, sq, ts + KP_C, g, vcol);
             const int so = H * Dv * 2;
             const __amdgpu_buffer_rsrc_t ro =
-                make_rsrc(sq.o + sq.row(ts) * Dv, min(KP_C, sq.len - ts) * so);
+                make_rsrc(sq.o + sq.row(ts) * Dv, sq.o ? min(KP_C, sq.len - ts) * so : 0);
 #pragma unroll
             for (int I = 0; I < 2; ++I) {
 #pragma unroll

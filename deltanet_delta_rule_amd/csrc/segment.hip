@@ -3,8 +3,9 @@
 // workgroups for 256 CUs).
 //
 // The map from a segment's incoming state to its outgoing state is affine:
-// every token applies S <- S A_t + beta_t v_t k_t^T with A_t = alpha_t (I -
-// beta_t k_t k_t^T) (alpha_t = 1 for the plain rule), so over a segment
+// every token applies S <- S A_t + beta_t v_t k_t^T with A_t = D_t (I -
+// beta_t k_t k_t^T) (D_t = I for the plain rule, alpha_t I for the gated one,
+// diag(exp(gk_t)) for KDA), so over a segment
 //   S_out = S_in M + H,   M = A_first ... A_last,   H = S_out from S_in = 0
 // (hada.io digest, sections "Chunkwise KDA" and "Transition diagonale-bas
 // rang": the state update is a product of transitions plus rank-one writes;

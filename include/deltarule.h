@@ -168,7 +168,8 @@ enum {
  *               device scratch (16-byte aligned, not overlapping any argument)
  *               for the segment-parallel schedule, or NULL.  When the
  *               sequences are too few to fill the GPU (say B = 1, H = 16,
- *               T = 32768), the plain and gated rules without cu_seqlens cut
+ *               T = 32768), the plain and gated rules and the chunked KDA
+ *               kernel (not the token-serial schedule), without cu_seqlens, cut
  *               each sequence into P segments of whole chunks, run them in
  *               parallel from zero states and (with v = 0) from S = I to get
  *               each segment's affine state map S_out = S_in M + H, chain the

@@ -119,6 +119,25 @@ def test_long_prefill_full_size_sampled_heads():
     assert eo <= 2e-2 and es <= 2e-2
 
 
+def test_kda_long_sequence():
+    # per-key-channel decay: the chunked KDA kernel on the segments
+    w = W.get("long_prefill", H=2, T=6700, gate_amax=1.0, kda=True, seed=12700)
+    x = W.generate(w)
+    d = to_dev(x)
+    need = dr.chunk_fwd_workspace_bytes(w.B, w.T, w.H, w.Dk, w.Dv, 64)
+    assert need > 0
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    o, st = dr.kda_fwd(d["q"], d["k"], d["v"], d["beta"], d["gk"], d["S0"], workspace=ws)
+    torch.cuda.synchronize()
+    assert not torch.isnan(ws[:16]).any()
+    o_p, st_p = dr.kda_fwd(d["q"], d["k"], d["v"], d["beta"], d["gk"], d["S0"], workspace=False)
+    o_ref, s_ref = oracle_all(x)
+    eo, es = rel_err(to_np(o), o_ref), rel_err(to_np(st), s_ref)
+    print(f"segments kda T{w.T}: o err {eo:.3e} S_T err {es:.3e}", flush=True)
+    assert eo <= 2e-2 and es <= 2e-2
+    assert rel_err(to_np(o), to_np(o_p)) <= 2e-2 and rel_err(to_np(st), to_np(st_p)) <= 2e-2
+
+
 def test_small_workspace_falls_back_to_the_plain_schedule():
     w = W.get("long_prefill", H=2, T=6600, seed=12600)
     d = to_dev(W.generate(w))
