@@ -26,11 +26,22 @@
 // rows of dS (kept transposed, d_k x 16, as fp32 MFMA accumulators for the
 // whole sequence).  The state S_c of each chunk comes from checkpoints the
 // forward kernel writes.  Products that sum over all value columns (dO E^T,
-// dV E^T, dQ, dK) run after the waves have published their slices in LDS,
-// with output tiles dealt round-robin to the waves.  Chunks are 32 tokens for
-// bf16 and 16 for fp32 (LDS capacity), which the forward checkpoints follow.
+// dV E^T, dQ, dK) run after the waves have published their slices in LDS:
+// the C x C tiles dealt round-robin to the waves, dQ and dK by key tile.
+// Chunks are 32 tokens for bf16 and 16 for fp32 (LDS capacity), which the
+// forward checkpoints follow.
+//
+// Memory traffic.  The next chunk's inputs travel in registers, loaded in
+// three parts at three phases of the current chunk (S_c, then K and Q, then
+// V, dO and beta), and the outputs are written at the start of the last
+// phase (dV from its LDS copy and dQ, dK of the previous chunk from
+// registers, all as vectors): the last phase is bound by LDS reads and leaves
+// the vector memory path free, while a burst of loads just before a barrier
+// had every wave waiting for the slowest one to issue its share.
 #include "dr_common.hpp"
 #include "dr_launch.hpp"
+
+#include <type_traits>
 
 namespace dr {
 
@@ -78,11 +89,44 @@ constexpr bool bwd_fits() {
     return sizeof(BwdSmem<DT, DK, DV, C>) <= 160 * 1024;
 }
 
+// Four consecutive elements of DT to global memory through a buffer resource
+// (dropped past its range).
+__device__ __forceinline__ void store4(const bf16x4 &f, __amdgpu_buffer_rsrc_t r, int voff) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, f), r, voff, 0, 0);
+}
+__device__ __forceinline__ void store4(const f32x4_arr &f, __amdgpu_buffer_rsrc_t r, int voff) {
+    typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f), r, voff, 0, 0);
+}
+
 // One 16x16x16 product step on 16-wide fragments of DT.
 template <typename DT>
 __device__ __forceinline__ void mk(f32x4 &acc, const typename Frag<DT>::k16 &a,
                                    const typename Frag<DT>::k16 &b) {
     mma_k16(acc, a, b);
+}
+
+// acc += sum_i A_i B_i over N 16-wide slabs (fragments fa[i], fb[i]).  For
+// bf16 two consecutive slabs go through one 16x16x32 product: a 32-wide
+// fragment is two 16-wide ones side by side, and A and B take the same k
+// order.  An odd last slab is paired with zeros, so that every product of an
+// accumulation chain has the same shape (a dependent 16x16x16 product right
+// after a 16x16x32 one on the same accumulator would read a stale value).
+template <typename DT, int N>
+__device__ __forceinline__ void mk_n(f32x4 &acc, const typename Frag<DT>::k16 *fa,
+                                     const typename Frag<DT>::k16 *fb) {
+    if constexpr (std::is_same<DT, __bf16>::value) {
+#pragma unroll
+        for (int i = 0; i < N; i += 2) {
+            const bf16x4 z = {};
+            const bf16x4 a1 = i + 1 < N ? fa[i + 1] : z, b1 = i + 1 < N ? fb[i + 1] : z;
+            mma_k32(acc, __builtin_shufflevector(fa[i], a1, 0, 1, 2, 3, 4, 5, 6, 7),
+                    __builtin_shufflevector(fb[i], b1, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) mk<DT>(acc, fa[i], fb[i]);
+    }
 }
 
 // 16x16 tile of A B with A row-major (rows m0.., k along the row) and B given
@@ -99,8 +143,7 @@ __device__ __forceinline__ void tile_rr(f32x4 &acc, const DT *A, int lda, int m0
         frag_rows(A, lda, m0, k0 + 16 * i, lane, fa[i]);
         frag_rows(Bt, ldb, n0, k0 + 16 * i, lane, fb[i]);
     }
-#pragma unroll
-    for (int i = 0; i < NK; ++i) mk<DT>(acc, fa[i], fb[i]);
+    mk_n<DT, NK>(acc, fa, fb);
 }
 // Same with B row-major (k along the rows of B: B[k][n]).
 template <typename DT, int NK>
@@ -112,8 +155,7 @@ __device__ __forceinline__ void tile_rc(f32x4 &acc, const DT *A, int lda, int m0
         frag_rows(A, lda, m0, k0 + 16 * i, lane, fa[i]);
         frag_cols16(B, ldb, k0 + 16 * i, n0, lane, fb[i]);
     }
-#pragma unroll
-    for (int i = 0; i < NK; ++i) mk<DT>(acc, fa[i], fb[i]);
+    mk_n<DT, NK>(acc, fa, fb);
 }
 // Same with A given transposed (A^T row-major: A[m][k] = At[k][m]) and B
 // row-major.
@@ -126,8 +168,7 @@ __device__ __forceinline__ void tile_cc(f32x4 &acc, const DT *At, int lda, int m
         frag_cols16(At, lda, k0 + 16 * i, m0, lane, fa[i]);
         frag_cols16(B, ldb, k0 + 16 * i, n0, lane, fb[i]);
     }
-#pragma unroll
-    for (int i = 0; i < NK; ++i) mk<DT>(acc, fa[i], fb[i]);
+    mk_n<DT, NK>(acc, fa, fb);
 }
 
 // Store a D-layout tile (lane (g, r): rows 4g + i, column r) into a
@@ -201,11 +242,14 @@ struct RowPrefetch {
             x[j] = buf_load16<vec_t>(rs, off);
         }
     }
+    // Unguarded where the vectors divide evenly over the threads: a store
+    // skipped on some path leaves its registers' loads pending there, and the
+    // next load into them would then wait for every load in flight.
     __device__ __forceinline__ void store(DT *dst, int ld, int tid) const {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const int i = tid + j * NTHR;
-            if (i < NV) {
+            if (NV % NTHR == 0 || i < NV) {
                 const int t = i / VPR, e = (i % VPR) * (16 / (int)sizeof(DT));
                 *reinterpret_cast<vec_t *>(dst + t * ld + e) = x[j];
             }
@@ -221,19 +265,60 @@ struct ChunkPrefetch {
     RowPrefetch<DT, C, DK, NTHR> k, q;
     RowPrefetch<DT, C, DV, NTHR> v, o;
     RowPrefetch<DT, DV, DK, NTHR> s;
-    float b;
+    DT b;   // beta of token tid (zero past the chunk's valid length)
+    // Part 0: S_c; part 1: K and Q; part 2: V, dO and beta (issued at three
+    // points of a chunk, so that no single point floods the vector memory
+    // path).
+    template <int P>
+    __device__ __forceinline__ void load_part(const DT *kk, const DT *qq, const DT *vv,
+                                              const DT *oo, const DT *bb, const DT *sc,
+                                              int64_t tok0, int h, int H, int len, int tid) {
+        const int64_t rk = (int64_t)H * DK, rv = (int64_t)H * DV;
+        if constexpr (P == 0) s.load(sc, DK, DV, tid);
+        if constexpr (P == 1) {
+            k.load(kk + (tok0 * H + h) * DK, rk, len, tid);
+            q.load(qq + (tok0 * H + h) * DK, rk, len, tid);
+        }
+        if constexpr (P == 2) {
+            v.load(vv + (tok0 * H + h) * DV, rv, len, tid);
+            o.load(oo + (tok0 * H + h) * DV, rv, len, tid);
+            // through a range-checked resource like the tiles, so that nothing
+            // waits for this load before the chunk's LDS stores
+            const auto rb = make_rsrc(bb + tok0 * H + h, len > 0 ? ((len - 1) * H + 1) * (int)sizeof(DT) : 0);
+            b = buf_load_elem<DT>(rb, tid < len ? tid * H * (int)sizeof(DT) : 0x7ffffff0);
+        }
+    }
     __device__ __forceinline__ void load(const DT *kk, const DT *qq, const DT *vv, const DT *oo,
                                          const DT *bb, const DT *sc, int64_t tok0, int h, int H,
                                          int len, int tid) {
-        const int64_t rk = (int64_t)H * DK, rv = (int64_t)H * DV;
-        k.load(kk + (tok0 * H + h) * DK, rk, len, tid);
-        q.load(qq + (tok0 * H + h) * DK, rk, len, tid);
-        v.load(vv + (tok0 * H + h) * DV, rv, len, tid);
-        o.load(oo + (tok0 * H + h) * DV, rv, len, tid);
-        s.load(sc, DK, DV, tid);
-        b = tid < len ? to_f32(bb[(tok0 + tid) * H + h]) : 0.f;
+        load_part<0>(kk, qq, vv, oo, bb, sc, tok0, h, H, len, tid);
+        load_part<1>(kk, qq, vv, oo, bb, sc, tok0, h, H, len, tid);
+        load_part<2>(kk, qq, vv, oo, bb, sc, tok0, h, H, len, tid);
     }
 };
+
+// Rows [0, nvalid) of a [ROWS, COLS] LDS tile (row stride ld) to global rows
+// of stride gs elements, 16 bytes per store; rows past nvalid are dropped by
+// the buffer resource's range check.
+template <typename DT, int ROWS, int COLS, int NTHR>
+__device__ __forceinline__ void store_rows(DT *dst, int64_t gs, int nvalid, const DT *src, int ld,
+                                           int tid) {
+    typedef typename V16<DT>::type vec_t;
+    typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+    constexpr int VPR = COLS * (int)sizeof(DT) / 16;
+    constexpr int NV = ROWS * VPR;
+    const auto rs = make_rsrc(dst, (int)((nvalid - 1) * gs + COLS) * (int)sizeof(DT));
+#pragma unroll
+    for (int j = 0; j < (NV + NTHR - 1) / NTHR; ++j) {
+        const int i = tid + j * NTHR;
+        if (NV % NTHR == 0 || i < NV) {
+            const int t = i / VPR, e = (i % VPR) * (16 / (int)sizeof(DT));
+            const vec_t x = *reinterpret_cast<const vec_t *>(src + t * ld + e);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs,
+                                                   (int)((t * gs + e) * (int)sizeof(DT)), 0, 0);
+        }
+    }
+}
 
 template <typename DT, int DK, int DV, int C>
 __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
@@ -266,17 +351,66 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
         Dt[s] = dST ? *reinterpret_cast<const f32x4 *>(dST + (head * DV + v0 + r) * DK + 16 * s + 4 * g)
                     : zero4();
     }
+    // The in-loop code must not see these loads as pending (it would wait for
+    // every memory operation in flight at their first use, in every chunk).
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+    // Output tiles (mt, j) of dQ and dK: token tile mt, key tile j.  With
+    // NW <= KT wave w takes key tiles j = w, w + NW, ... for every token tile;
+    // with more waves than key tiles, key tile w % KT and token tiles w / KT,
+    // w / KT + NW / KT, ...
+    constexpr int NJW = NW <= KT ? KT / NW : 1;   // key tiles per wave
+    constexpr int MS = NW <= KT ? 1 : NW / KT;    // token tile stride
+    constexpr int NMU = (NT + MS - 1) / MS;       // token tiles per wave (at most)
+    const int mt0 = NW <= KT ? 0 : w / KT;
+    // dQ and dK tiles are computed transposed (operands swapped), so that a
+    // lane holds four consecutive keys of one token and stores them at once.
+    // Where a wave has at most two tiles of each, they are held in registers
+    // and stored in the next chunk, after the loads of the chunk after it
+    // have been issued: a store issued just before the wait for those loads
+    // at the top of a chunk would be waited for with them (the wait covers
+    // every memory operation issued before the last load).
+    constexpr bool DEFER = NJW * NMU <= 2;
+    typedef typename Frag<DT>::k16 out4;
+    out4 pq[DEFER ? NJW * NMU : 1], pk[DEFER ? NJW * NMU : 1];
+    const int64_t rowq = (int64_t)H * DK;
+    auto chunk_rsrc = [&](DT *base, int cc, int64_t row, int cols) {
+        const int ft0 = cc * C, flen = min(C, T - ft0);
+        return make_rsrc(base + (((int64_t)b * T + ft0) * H + h) * cols,
+                         (int)((flen - 1) * row + cols) * (int)sizeof(DT));
+    };
+    auto flush = [&](int cc) {
+        if constexpr (DEFER) {
+            const auto rq = chunk_rsrc(dq, cc, rowq, DK), rk = chunk_rsrc(dk, cc, rowq, DK);
+#pragma unroll
+            for (int jj = 0; jj < NJW; ++jj)
+#pragma unroll
+                for (int u = 0; u < NMU; ++u) {
+                    const int mt = mt0 + u * MS, j = NW <= KT ? w + jj * NW : w % KT;
+                    if (mt < NT) {
+                        const int voff = ((16 * mt + r) * (int)rowq + 16 * j + 4 * g) * (int)sizeof(DT);
+                        store4(pq[jj * NMU + u], rq, voff);
+                        store4(pk[jj * NMU + u], rk, voff);
+                    }
+                }
+        }
+    };
 
     // inputs of the next chunk to process travel in registers one chunk ahead
     ChunkPrefetch<DT, DK, DV, C> pf;
+    auto prefetch = [&](auto part, int cn) {
+        const int tp = cn * C;
+        pf.template load_part<decltype(part)::value>(k, q, v, dout, beta, hs + (head * N + cn) * DV * DK,
+                                                     (int64_t)b * T + tp, h, H, min(C, T - tp), tid);
+    };
     if (N > 0) {
         const int t0 = (N - 1) * C;
         pf.load(k, q, v, dout, beta, hs + (head * N + N - 1) * DV * DK, (int64_t)b * T + t0, h, H,
                 min(C, T - t0), tid);
     }
     for (int c = N - 1; c >= 0; --c) {
-        const int t0 = c * C, len = min(C, T - t0);
-        const int64_t tok0 = (int64_t)b * T + t0;
+        const int len = min(C, T - c * C);
+        const int64_t tok0 = (int64_t)b * T + c * C;
         __syncthreads();
         // ---------------------------------------------------------------- load
         pf.k.store(sm.Ks, LDK, tid);
@@ -284,15 +418,14 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
         pf.v.store(sm.Vs, LDV, tid);
         pf.o.store(sm.Os, LDV, tid);
         pf.s.store(sm.Sb, LDSK, tid);
-        if (tid < C) sm.betas[tid] = pf.b;
-        if (c > 0) {
-            const int tp = (c - 1) * C;
-            pf.load(k, q, v, dout, beta, hs + (head * N + c - 1) * DV * DK, (int64_t)b * T + tp, h,
-                    H, min(C, T - tp), tid);
+        {
+            const float bt = to_f32(pf.b);  // converted by every lane (see RowPrefetch::store)
+            if (tid < C) sm.betas[tid] = bt;
         }
         __syncthreads();
 
         // ---------------------------------------------------- Gram and inverse
+        if (c > 0) prefetch(std::integral_constant<int, 0>(), c - 1);
         // jobs: lower tiles (ti >= tj) of G = K K^T and P = Q K^T
         constexpr int NJ = NT * (NT + 1) / 2;
         for (int j = w; j < 2 * NJ; j += NW) {
@@ -345,6 +478,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
         }
 
         // ------------------------------------------- per-wave value columns
+        if (c > 0) prefetch(std::integral_constant<int, 1>(), c - 1);
         f32x4 R[NT], E[NT], Z[NT];
         {
             // R = V - K S_c^T (S_c rows of this wave's columns as B^T)
@@ -357,8 +491,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                 typename Frag<DT>::k16 fk[KT];
 #pragma unroll
                 for (int s = 0; s < KT; ++s) frag_rows(sm.Ks, LDK, 16 * mt, 16 * s, lane, fk[s]);
-#pragma unroll
-                for (int s = 0; s < KT; ++s) mk<DT>(x, fk[s], fs[s]);
+                mk_n<DT, KT>(x, fk, fs);
                 typename Frag<DT>::k16 fvv;
                 frag_cols16(sm.Vs, LDV, 16 * mt, v0, lane, fvv);
 #pragma unroll
@@ -391,18 +524,22 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
 #pragma unroll
             for (int mt = 0; mt < NT; ++mt) {
                 dE[mt] = zero4();
-                typename Frag<DT>::k16 fa, fo;
+                // P^T is zero above the diagonal: slabs kt < mt are zeros
+                typename Frag<DT>::k16 fa[NT], fo[NT];
 #pragma unroll
-                for (int kt = mt; kt < NT; ++kt) {
-                    frag_cols16(sm.Pm, LDC, 16 * kt, 16 * mt, lane, fa);
-                    frag_cols16(sm.Os, LDV, 16 * kt, v0, lane, fo);
-                    mk<DT>(dE[mt], fa, fo);
+                for (int kt = 0; kt < NT; ++kt) {
+                    if (kt >= mt) {
+                        frag_cols16(sm.Pm, LDC, 16 * kt, 16 * mt, lane, fa[kt]);
+                        frag_cols16(sm.Os, LDV, 16 * kt, v0, lane, fo[kt]);
+                    } else {
+                        fa[kt] = fo[kt] = typename Frag<DT>::k16{};
+                    }
                 }
+                mk_n<DT, NT>(dE[mt], fa, fo);
                 typename Frag<DT>::k16 fks[KT];
 #pragma unroll
                 for (int s = 0; s < KT; ++s) frag_rows(sm.Ks, LDK, 16 * mt, 16 * s, lane, fks[s]);
-#pragma unroll
-                for (int s = 0; s < KT; ++s) mk<DT>(dE[mt], fks[s], fd[s]);
+                mk_n<DT, KT>(dE[mt], fks, fd);
             }
             typename Frag<DT>::k16 fde[NT];
 #pragma unroll
@@ -436,11 +573,8 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float y = R[mt][i] - ge[i];
-                    float p = Z[mt][i] * y;
                     // sum over the 16 value columns of this wave (lanes r)
-#pragma unroll
-                    for (int m = 8; m >= 1; m >>= 1) p += __shfl_xor(p, m, 16);
-                    zy[i] = p;
+                    zy[i] = group_sum<16>(Z[mt][i] * y);
                 }
                 if (r == 0) {
 #pragma unroll
@@ -453,7 +587,6 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                     dvv[i] = sm.betas[t] * Z[mt][i];
                     sm.Es[t * LDV + v0 + r] = from_f32<DT>(E[mt][i]);
                     sm.Rb[t * LDV + v0 + r] = from_f32<DT>(dvv[i]);
-                    if (t < len) dv[((tok0 + t) * H + h) * DV + v0 + r] = from_f32<DT>(dvv[i]);
                 }
                 Z[mt] = dvv;  // keep dV
             }
@@ -488,11 +621,8 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                     frag_cols16(sm.Qs, LDK, 16 * kt, 16 * s, lane, fa[kt]);
                     frag_cols16(sm.Ks, LDK, 16 * kt, 16 * s, lane, fb[kt]);
                 }
-#pragma unroll
-                for (int kt = 0; kt < NT; ++kt) {
-                    mk<DT>(Dt[s], fa[kt], fo[kt]);
-                    mk<DT>(Dt[s], fb[kt], fdv[kt]);
-                }
+                mk_n<DT, NT>(Dt[s], fa, fo);
+                mk_n<DT, NT>(Dt[s], fb, fdv);
             }
         }
         __syncthreads();
@@ -521,47 +651,87 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
             }
         }
         for (int t = tid; t < len; t += nthr) {
-            float s = 0.f;
+            float sb = 0.f;
 #pragma unroll
-            for (int ww = 0; ww < NW; ++ww) s += sm.dbp[ww][t];
-            dbeta[(tok0 + t) * H + h] = from_f32<DT>(s);
+            for (int ww = 0; ww < NW; ++ww) sb += sm.dbp[ww][t];
+            dbeta[(tok0 + t) * H + h] = from_f32<DT>(sb);
         }
         __syncthreads();
 
         // ------------------------------------------------------- dQ and dK
-        constexpr int NO = NT * KT;  // output tiles of each
-        constexpr int NU = (NO + NW - 1) / NW;
-        f32x4 dKa[G::DBUF ? 1 : NU];
+        if (c > 0) prefetch(std::integral_constant<int, 2>(), c - 1);
+        if (c + 1 < N) flush(c + 1);
+        // dV of all value columns, from its LDS copy, 16 bytes per store
+        store_rows<DT, C, DV, 64 * NW>(dv + (tok0 * H + h) * DV, (int64_t)H * DV, len, sm.Rb, LDV, tid);
+        // The operands along d_k (columns of S_c, K and Q, rows of
+        // dS_{c+1}^T) are read once per key tile and serve all of the wave's
+        // token tiles.
+        f32x4 dKa[G::DBUF ? 1 : NJW * NMU];
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int o = w + u * NW;
-            if (o < NO) {
-                const int mt = o / KT, j = o % KT;
-                // dQ = dO S_c + Dm K   (Dm is zero above the diagonal)
-                f32x4 aq = zero4();
-                tile_rc<DT, VT>(aq, sm.Os, LDV, 16 * mt, sm.Sb, LDSK, 16 * j, 0, lane);
-                tile_rc<DT, NT>(aq, sm.Dm, LDC, 16 * mt, sm.Ks, LDK, 16 * j, 0, lane);
-                // dK = -dV S_c + E dS_{c+1} + Gs K + Dm^T Q
-                f32x4 ak = zero4();
-                tile_rc<DT, VT>(ak, sm.Rb, LDV, 16 * mt, sm.Sb, LDSK, 16 * j, 0, lane);
-                ak = -ak;
-                if constexpr (G::DBUF)
-                    tile_rr<DT, VT>(ak, sm.Es, LDV, 16 * mt, sm.Db, LDS_, 16 * j, 0, lane);
-                tile_rc<DT, NT>(ak, sm.Gs, LDC, 16 * mt, sm.Ks, LDK, 16 * j, 0, lane);
-                tile_cc<DT, NT>(ak, sm.Dm, LDC, 16 * mt, sm.Qs, LDK, 16 * j, 0, lane);
+        for (int jj = 0; jj < NJW; ++jj) {
+            const int j = NW <= KT ? w + jj * NW : w % KT;
+            typename Frag<DT>::k16 fs[VT], fkc[NT], fqc[NT], fdb[G::DBUF ? VT : 1];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * mt + 4 * g + i;
-                    if (t < len) dq[((tok0 + t) * H + h) * DK + 16 * j + r] = from_f32<DT>(aq[i]);
-                }
-                if constexpr (G::DBUF) {
+            for (int i = 0; i < VT; ++i) frag_cols16(sm.Sb, LDSK, 16 * i, 16 * j, lane, fs[i]);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int t = 16 * mt + 4 * g + i;
-                        if (t < len) dk[((tok0 + t) * H + h) * DK + 16 * j + r] = from_f32<DT>(ak[i]);
+            for (int i = 0; i < NT; ++i) {
+                frag_cols16(sm.Ks, LDK, 16 * i, 16 * j, lane, fkc[i]);
+                frag_cols16(sm.Qs, LDK, 16 * i, 16 * j, lane, fqc[i]);
+            }
+            if constexpr (G::DBUF) {
+#pragma unroll
+                for (int i = 0; i < VT; ++i) frag_rows(sm.Db, LDS_, 16 * j, 16 * i, lane, fdb[i]);
+            }
+#pragma unroll
+            for (int u = 0; u < NMU; ++u) {
+                const int mt = mt0 + u * MS;
+                if (mt < NT) {
+                    typename Frag<DT>::k16 fa[VT], fb[VT], fm[NT];
+                    // dQ = dO S_c + Dm K   (Dm is zero above the diagonal)
+                    f32x4 aq = zero4();
+#pragma unroll
+                    for (int i = 0; i < VT; ++i) frag_rows(sm.Os, LDV, 16 * mt, 16 * i, lane, fa[i]);
+#pragma unroll
+                    for (int i = 0; i < NT; ++i) frag_rows(sm.Dm, LDC, 16 * mt, 16 * i, lane, fm[i]);
+                    mk_n<DT, VT>(aq, fs, fa);
+                    mk_n<DT, NT>(aq, fkc, fm);
+                    // dK = -dV S_c + E dS_{c+1} + Gs K + Dm^T Q
+                    f32x4 an = zero4(), ak = zero4();
+#pragma unroll
+                    for (int i = 0; i < VT; ++i) frag_rows(sm.Rb, LDV, 16 * mt, 16 * i, lane, fb[i]);
+                    mk_n<DT, VT>(an, fs, fb);
+                    if constexpr (G::DBUF) {
+#pragma unroll
+                        for (int i = 0; i < VT; ++i) frag_rows(sm.Es, LDV, 16 * mt, 16 * i, lane, fa[i]);
+                        mk_n<DT, VT>(ak, fdb, fa);
                     }
-                } else {
-                    dKa[u] = ak;
+#pragma unroll
+                    for (int i = 0; i < NT; ++i) frag_rows(sm.Gs, LDC, 16 * mt, 16 * i, lane, fm[i]);
+                    mk_n<DT, NT>(ak, fkc, fm);
+#pragma unroll
+                    for (int i = 0; i < NT; ++i) frag_cols16(sm.Dm, LDC, 16 * i, 16 * mt, lane, fm[i]);
+                    mk_n<DT, NT>(ak, fqc, fm);
+                    ak = ak - an;
+                    if constexpr (DEFER) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            frag_set(pq[jj * NMU + u], i, aq[i]);
+                            if constexpr (G::DBUF) frag_set(pk[jj * NMU + u], i, ak[i]);
+                        }
+                    } else {
+                        const auto rq = chunk_rsrc(dq, c, rowq, DK), rk = chunk_rsrc(dk, c, rowq, DK);
+                        const int voff = ((16 * mt + r) * (int)rowq + 16 * j + 4 * g) * (int)sizeof(DT);
+                        out4 x;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) frag_set(x, i, aq[i]);
+                        store4(x, rq, voff);
+                        if constexpr (G::DBUF) {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) frag_set(x, i, ak[i]);
+                            store4(x, rk, voff);
+                        }
+                    }
+                    if constexpr (!G::DBUF) dKa[jj * NMU + u] = ak;
                 }
             }
         }
@@ -575,21 +745,36 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                     sm.Sb[(v0 + r) * LDSK + 16 * s2 + 4 * g + i] = from_f32<DT>(Dold[s2][i]);
             __syncthreads();
 #pragma unroll
-            for (int u = 0; u < NU; ++u) {
-                const int o = w + u * NW;
-                if (o < NO) {
-                    const int mt = o / KT, j = o % KT;
-                    f32x4 ak = dKa[u];
-                    tile_rc<DT, VT>(ak, sm.Es, LDV, 16 * mt, sm.Sb, LDSK, 16 * j, 0, lane);
+            for (int jj = 0; jj < NJW; ++jj) {
+                const int j = NW <= KT ? w + jj * NW : w % KT;
+                typename Frag<DT>::k16 fs[VT];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int t = 16 * mt + 4 * g + i;
-                        if (t < len) dk[((tok0 + t) * H + h) * DK + 16 * j + r] = from_f32<DT>(ak[i]);
+                for (int i = 0; i < VT; ++i) frag_cols16(sm.Sb, LDSK, 16 * i, 16 * j, lane, fs[i]);
+#pragma unroll
+                for (int u = 0; u < NMU; ++u) {
+                    const int mt = mt0 + u * MS;
+                    if (mt < NT) {
+                        typename Frag<DT>::k16 fa[VT];
+                        f32x4 ak = dKa[jj * NMU + u];
+#pragma unroll
+                        for (int i = 0; i < VT; ++i) frag_rows(sm.Es, LDV, 16 * mt, 16 * i, lane, fa[i]);
+                        mk_n<DT, VT>(ak, fs, fa);
+                        if constexpr (DEFER) {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) frag_set(pk[jj * NMU + u], i, ak[i]);
+                        } else {
+                            const auto rk = chunk_rsrc(dk, c, rowq, DK);
+                            out4 x;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) frag_set(x, i, ak[i]);
+                            store4(x, rk, ((16 * mt + r) * (int)rowq + 16 * j + 4 * g) * (int)sizeof(DT));
+                        }
                     }
                 }
             }
         }
     }
+    if (N > 0) flush(0);
     if (dS0) {
 #pragma unroll
         for (int s = 0; s < KT; ++s)
