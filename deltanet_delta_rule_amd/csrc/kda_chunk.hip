@@ -27,6 +27,8 @@
 // Work split: see kda_pipe_kernel.
 #include "chunk_fwd.hpp"
 
+#include <type_traits>
+
 namespace dr {
 
 namespace {
@@ -139,8 +141,12 @@ __device__ __forceinline__ void kp_prefetch(KdaRegs &x, const KdaSeq &sq, int t0
 }
 
 // v[t0 + 16 I + 4 g + e][vcol] for I < 2, e < 4 (the D layout of X); v ==
-// nullptr loads zeros.
-__device__ __forceinline__ void kp_prefetch_v(unsigned short (&vr)[8], const KdaSeq &sq, int t0,
+// nullptr loads zeros.  With 32-bit elements each value keeps a register of
+// its own: packing two 16-bit loads into one register right after they are
+// issued waits for every load in flight (16-bit elements save the registers
+// where the kernel has none to spare).
+template <typename VT>
+__device__ __forceinline__ void kp_prefetch_v(VT (&vr)[8], const KdaSeq &sq, int t0,
                                               int g, int vcol) {
     const int nv = min(KP_C, sq.len - t0);
     const int sv = sq.H * sq.Dv * 2;
@@ -200,10 +206,13 @@ __global__ __launch_bounds__(512) void kda_pipe_kernel(
                 S[s][hh] = f32x4{x.x, x.y, x.z, x.w};
             }
         }
+    // The chunk loop must not see these loads as pending (it would wait for
+    // every memory operation in flight at their first use, in every chunk).
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
     const int nchunk = (sq.len + KP_C - 1) / KP_C;
     KdaRegs x;
-    unsigned short vr[8];
+    typename std::conditional<L2, unsigned short, unsigned>::type vr[8];
     if (nchunk > 0) {
         if (prep) kp_prefetch(x, sq, 0, wave, p, tid);
         else kp_prefetch_v(vr, sq, 0, g, vcol);
@@ -333,7 +342,7 @@ __global__ __launch_bounds__(512) void kda_pipe_kernel(
                 f32x4 X = Xs[I];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    X[e] -= (float)__builtin_bit_cast(__bf16, vr[4 * I + e]);
+                    X[e] -= (float)__builtin_bit_cast(__bf16, (unsigned short)vr[4 * I + e]);
                 if (I == 1) {
                     bf16x4 fa;
                     load_fragblk(bs.Gb, 0, lane, fa);
@@ -346,7 +355,6 @@ __global__ __launch_bounds__(512) void kda_pipe_kernel(
                 mma_k16(E[I], ft, fy);
                 frag_from_acc16(E[I], fE[I]);
             }
-            if (it + 1 < nchunk) kp_prefetch_v(vr, sq, ts + KP_C, g, vcol);
             const int so = H * Dv * 2;
             const __amdgpu_buffer_rsrc_t ro =
                 make_rsrc(sq.o + sq.row(ts) * Dv, sq.o ? min(KP_C, sq.len - ts) * so : 0);
@@ -363,6 +371,9 @@ __global__ __launch_bounds__(512) void kda_pipe_kernel(
                     buf_store_elem((__bf16)(scale * O[I][e]), ro,
                                    (16 * I + 4 * g + e) * so + 2 * vcol, 0);
             }
+            // after the output stores: the next chunk's wait for these loads
+            // then covers no store issued just before it
+            if (it + 1 < nchunk) kp_prefetch_v(vr, sq, ts + KP_C, g, vcol);
         }
         lds_barrier();
 
