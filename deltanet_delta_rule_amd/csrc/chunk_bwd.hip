@@ -481,10 +481,15 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
         if (c > 0) prefetch(std::integral_constant<int, 1>(), c - 1);
         f32x4 R[NT], E[NT], Z[NT];
         {
-            // R = V - K S_c^T (S_c rows of this wave's columns as B^T)
-            typename Frag<DT>::k16 fs[KT];
+            // R = V - K S_c^T (S_c rows of this wave's columns as B^T) and
+            // dE = P^T dO + K dS^T share the K row fragments
+            typename Frag<DT>::k16 fs[KT], fd[KT];
 #pragma unroll
-            for (int s = 0; s < KT; ++s) frag_rows(sm.Sb, LDSK, v0, 16 * s, lane, fs[s]);
+            for (int s = 0; s < KT; ++s) {
+                frag_rows(sm.Sb, LDSK, v0, 16 * s, lane, fs[s]);
+                cvt4(Dt[s], fd[s]);
+            }
+            f32x4 dE[NT];
 #pragma unroll
             for (int mt = 0; mt < NT; ++mt) {
                 f32x4 x = zero4();
@@ -496,6 +501,20 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                 frag_cols16(sm.Vs, LDV, 16 * mt, v0, lane, fvv);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) R[mt][i] = frag_get(fvv, i) - x[i];
+                dE[mt] = zero4();
+                // P^T is zero above the diagonal: slabs kt < mt are zeros
+                typename Frag<DT>::k16 fa[NT], fo[NT];
+#pragma unroll
+                for (int kt = 0; kt < NT; ++kt) {
+                    if (kt >= mt) {
+                        frag_cols16(sm.Pm, LDC, 16 * kt, 16 * mt, lane, fa[kt]);
+                        frag_cols16(sm.Os, LDV, 16 * kt, v0, lane, fo[kt]);
+                    } else {
+                        fa[kt] = fo[kt] = typename Frag<DT>::k16{};
+                    }
+                }
+                mk_n<DT, NT>(dE[mt], fa, fo);
+                mk_n<DT, KT>(dE[mt], fk, fd);
             }
             // E = Tm diag(beta) R
             typename Frag<DT>::k16 frb[NT];
@@ -516,31 +535,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                     mk<DT>(E[mt], ft, frb[kt]);
                 }
             }
-            // dE = P^T dO + K dS^T, then Z = Tm^T dE
-            typename Frag<DT>::k16 fd[KT];
-#pragma unroll
-            for (int s = 0; s < KT; ++s) cvt4(Dt[s], fd[s]);
-            f32x4 dE[NT];
-#pragma unroll
-            for (int mt = 0; mt < NT; ++mt) {
-                dE[mt] = zero4();
-                // P^T is zero above the diagonal: slabs kt < mt are zeros
-                typename Frag<DT>::k16 fa[NT], fo[NT];
-#pragma unroll
-                for (int kt = 0; kt < NT; ++kt) {
-                    if (kt >= mt) {
-                        frag_cols16(sm.Pm, LDC, 16 * kt, 16 * mt, lane, fa[kt]);
-                        frag_cols16(sm.Os, LDV, 16 * kt, v0, lane, fo[kt]);
-                    } else {
-                        fa[kt] = fo[kt] = typename Frag<DT>::k16{};
-                    }
-                }
-                mk_n<DT, NT>(dE[mt], fa, fo);
-                typename Frag<DT>::k16 fks[KT];
-#pragma unroll
-                for (int s = 0; s < KT; ++s) frag_rows(sm.Ks, LDK, 16 * mt, 16 * s, lane, fks[s]);
-                mk_n<DT, KT>(dE[mt], fks, fd);
-            }
+            // Z = Tm^T dE
             typename Frag<DT>::k16 fde[NT];
 #pragma unroll
             for (int mt = 0; mt < NT; ++mt) cvt4(dE[mt], fde[mt]);
