@@ -824,6 +824,17 @@ __device__ __forceinline__ void state_path(const DT *Ks, const DT *Qs, const DT 
 // backward, which uses them only as DT product operands).
 template <int KSD, int ND, typename DT>
 __device__ __forceinline__ void store_state_row(DT *row, const f32x4 *Sacc, int g) {
+    if constexpr (sizeof(DT) == 2 && KSD == 32) {
+        // tiles 2m, 2m + 1 hold keys 32m + 8g .. 32m + 8g + 7 between them:
+        // one 16-byte store per pair
+#pragma unroll
+        for (int m = 0; m < ND / 2; ++m) {
+            bf16x8 f;
+            frag_from_state(Sacc[2 * m], Sacc[2 * m + 1], g, f);
+            *reinterpret_cast<bf16x8 *>(row + 32 * m + 8 * g) = f;
+        }
+        return;
+    }
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) {
         if constexpr (sizeof(DT) == 4) {
