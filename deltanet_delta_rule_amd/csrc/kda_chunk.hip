@@ -290,7 +290,7 @@ __global__ __launch_bounds__(512) void kda_pipe_kernel(
                     frag_rows(bs.KT, KDA_LD, 16 * I, 32 * s, lane, fk);
                     frag_rows(bs.QT, KDA_LD, 16 * I, 32 * s, lane, fq);
                     mma_k32(Xs[I], fk, fS[s]);
-                    mma_k32(O[I], fq, fS[s]);
+                    mma_k32(O[I], fS[s], fq);  // O transposed (see the stores)
                 }
         }
         lds_barrier();
@@ -364,12 +364,13 @@ __global__ __launch_bounds__(512) void kda_pipe_kernel(
                 for (int Jb = 0; Jb <= I; ++Jb) {
                     bf16x4 fa;
                     load_fragblk(bs.Pb, I * (I + 1) / 2 + Jb, lane, fa);
-                    mma_k16(O[I], fa, fE[Jb]);
+                    mma_k16(O[I], fE[Jb], fa);
                 }
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    buf_store_elem((__bf16)(scale * O[I][e]), ro,
-                                   (16 * I + 4 * g + e) * so + 2 * vcol, 0);
+                // O is computed transposed (operands swapped): lane (g, r)
+                // holds token 16 I + r, value columns vcol - r + 4g .. + 3,
+                // written with one 8-byte store
+                __builtin_amdgcn_raw_buffer_store_b64(pk4_bf16(scale * O[I]), ro,
+                                                      (16 * I + r) * so + 2 * (vcol - r + 4 * g), 0, 0);
             }
             // after the output stores: the next chunk's wait for these loads
             // then covers no store issued just before it
