@@ -246,7 +246,7 @@ def bench_gated_chunk(torch, dr, W, reps=20, name="gated_layer_1p3b", l2=False):
 def bench_kda_sequence(torch, dr, W, reps=10):
     """kda_fwd (chunked kernel) on the layer shape with per-channel decay:
     mean call time with HIP events on the launch stream."""
-    w = W.get("layer_1p3b", gate_amax=1.0, kda=True, chunk=32)
+    w = W.get("layer_1p3b", gate_amax=16.0, kda=True, chunk=32)
     x = W.generate(w)
     dev = torch.device("cuda:0")
     d = {n: (None if t is None else t.to(dev)) for n, t in x.items()}
@@ -269,7 +269,7 @@ def bench_kda_sequence(torch, dr, W, reps=10):
     flops, nbytes = chunk_work(w)
     return {
         "workload": (f"layer_1p3b B{w.B} H{w.H} T{w.T} d{w.Dk} chunk {w.chunk}, bf16 in, "
-                     "per-channel log decay fp32 (A up to 1), fp32 state"),
+                     "per-channel log decay fp32 (A up to 16), fp32 state"),
         "tokens_per_s": w.B * w.T / launch_s,
         "mean_launch_us": round(launch_s * 1e6, 2),
         "hbm_frac": round(nbytes / launch_s / 1e9 / HBM_PEAK_GBS, 4),

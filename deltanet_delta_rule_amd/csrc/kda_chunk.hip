@@ -15,14 +15,23 @@
 // matrix cores, the block below them is a product.
 //
 // The decay ratio exp(b_i - b_j) lives inside the contraction over key
-// channels, so it cannot be applied to a finished Gram tile.  It is split
-// around a reference point m_I per 16-token row block I (the prefix sum at
-// the block's 8th token): rows use k_i exp(b_i - m_I), columns k_j exp(m_I -
-// b_j).  For j in an earlier block the column factor is at most 1; inside the
-// block either factor grows by at most the decay of 8 tokens.  That bounds
-// the domain: the log decay summed over any 8 consecutive tokens of a channel
-// should stay above -40 (per-token gk >= -5 guarantees it); the growing
-// exponents are clamped at 80 so that nothing overflows outside it.
+// channels, so it cannot be applied to a finished Gram tile, and a split into
+// a row factor and a column factor around one reference token per block
+// overflows on one side once a channel decays hard inside the block (an
+// erased channel, gk -> -inf, is the case the digest's KDA section motivates).
+// The pairs (i, j), j < i, of a 32-token chunk are therefore taken by levels:
+// pair (i, j) belongs to level L = the highest bit in which i and j differ, so
+// they sit in the two halves of one aligned segment of 2L tokens, and its
+// reference is the last token of that segment's first half.  Row token i
+// then carries exp(b_i - b_ref) (the decay over ref+1 .. i) and column token
+// j carries exp(b_ref - b_j) (the decay over j+1 .. ref): both are products
+// of per-token factors exp(gk) <= 1, so nothing overflows and the product of
+// the two is exp(b_i - b_j) exactly up to rounding, for every gk <= 0.  Each
+// level is one product over the channels (levels 8, 4, 2, 1 inside the
+// 16-token diagonal blocks, masked to their own pairs; level 16 is the
+// off-diagonal block), and the read weight of a token's own write is q_i . k_i.
+// The state operands k Gamma, q Gamma and k exp(b_last - b) are products of
+// the same factors and stay <= 1 as well.
 //
 // Work split: see kda_pipe_kernel.
 #include "chunk_fwd.hpp"
@@ -37,19 +46,9 @@ constexpr int KDA_DK = 128;      // key channels
 constexpr int KDA_DVW = 64;      // value rows per workgroup
 constexpr int KDA_LD = 136;      // row pitch (bf16) of the token x channel tiles
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr float KDA_EXP2_MAX = 80.f * LOG2E;  // clamp of growing exponents (log2)
+constexpr int KDA_LV = 5;        // levels 16, 8, 4, 2, 1 of the pairs of a 32-token chunk
 
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Column operands of row block I start at row 8 I (I + 1) of KC: block I has
-// the 16 (I + 1) tokens 0 .. 16 I + 15.
-constexpr int kc_base(int I) { return 8 * I * (I + 1); }
-
-// Block pair p = I (I + 1) / 2 + J of the pairs (I, J <= I).
-__device__ __forceinline__ void pair_ij(int p, int &I, int &J) {
-    I = p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0;
-    J = p - I * (I + 1) / 2;
-}
 
 __device__ __forceinline__ unsigned pk2(float a, float b) { return pk_bf16(a, b); }
 
@@ -60,6 +59,22 @@ __device__ __forceinline__ float wave_sum(float v) {
     v += __shfl_xor(v, 32, 64);
     return v;
 }
+__device__ __forceinline__ float2 fmul2(float2 a, float2 b) { return make_float2(a.x * b.x, a.y * b.y); }
+
+// Factor of token s (0..7) of an 8-token quarter at level L <= 4 (its
+// 2L-segment lies inside the quarter): the product of exp(gk) over ref+1 .. s
+// for a row token (second half), over s+1 .. ref for a column token, ref the
+// last token of the segment's first half.  s and L are constants after
+// unrolling, so this folds to a few multiplies.
+__device__ __forceinline__ float2 lvl_factor(const float2 (&e)[8], int s, int L) {
+    const int ref = (s & ~(2 * L - 1)) + L - 1;
+    float2 f = make_float2(1.f, 1.f);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+        if (s > ref ? (u > ref && u <= s) : (u > s && u <= ref)) f = fmul2(f, e[u]);
+    return f;
+}
+
 __device__ __forceinline__ float lo_bf16(unsigned x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float hi_bf16(unsigned x) { return __uint_as_float(x & 0xffff0000u); }
 
@@ -90,11 +105,13 @@ struct KdaSeq {
 // state waves read (K.Gamma, Q.Gamma, KE, the blocks, Gamma_last) is double
 // buffered by chunk parity; at 32 tokens everything fits in LDS.  Each step
 // has three segments separated by workgroup barriers:
-//   1. preparation: prefix sums of its 8 tokens and the operands that need
-//      only in-block differences;  state: X and (Q.Gamma) S^T
-//   2. preparation: the operands that need the other waves' sums;  state:
-//      block substitution, P E, outputs
-//   3. preparation: G and P blocks, inverses;  state: state update
+//   1. preparation: per-token factors exp(gk) of its 8 tokens, their
+//      products and the level operands inside its quarter and block;
+//      state: X and (Q.Gamma) S^T
+//   2. preparation: the operands that need the other quarters' products;
+//      state: block substitution, P E, outputs
+//   3. preparation: G and P blocks level by level, inverses;  state: state
+//      update
 // Step -1 prepares chunk 0 only; the last step only runs the state path.
 // ---------------------------------------------------------------------------
 constexpr int KP_C = 32;
@@ -109,14 +126,26 @@ struct alignas(16) KdaPipeBuf {
     float gamC[KDA_DK];              // Gamma_last
 };
 
+// Level lv (L = 16 >> lv): W holds k_t times its factor at that level (the
+// row factor exp(b_t - b_ref) for a token in the second half of its
+// 2L-segment, the column factor exp(b_ref - b_t) otherwise); QR holds q_t
+// times the row factor (second-half tokens only; the other rows are never
+// selected).
 struct alignas(16) KdaPipeSmem {
-    __bf16 KR[KP_C * KDA_LD];        // k_i exp(b_i - m_I)
-    __bf16 QR[KP_C * KDA_LD];        // q_i exp(b_i - m_I)
-    __bf16 KC[48 * KDA_LD];          // k_j exp(m_I - b_j): I = 0 rows 0..15, I = 1 rows 16..47
+    __bf16 W[KDA_LV][KP_C * KDA_LD];
+    __bf16 QR[KDA_LV][KP_C * KDA_LD];
     KdaPipeBuf buf[2];
     float beta[KP_C];
-    float htot[4][KDA_DK];           // sums of gk over each 8-token quarter (log2)
+    float pdiag[KP_C];               // q_t . k_t: read weight of the token's own write
+    float hq[4][KDA_DK];             // decay over each 8-token quarter (product of exp(gk))
 };
+// Level lv operands of one token (offset o_t, channels 2p, 2p + 1): k times
+// the factor, and q times it for a row token.
+__device__ __forceinline__ void put_level(KdaPipeSmem &sm, int lv, int o_t, float2 kk,
+                                          float2 qq, float2 f, bool row) {
+    *reinterpret_cast<unsigned *>(sm.W[lv] + o_t) = pk2(kk.x * f.x, kk.y * f.y);
+    if (row) *reinterpret_cast<unsigned *>(sm.QR[lv] + o_t) = pk2(qq.x * f.x, qq.y * f.y);
+}
 
 // Raw k, q, gk of tokens 8w .. 8w + 7 and beta of token tid (< 32) of the
 // 32-token chunk at t0, zeros past the sequence's end.
@@ -226,55 +255,52 @@ __global__ __launch_bounds__(512) void kda_pipe_kernel(
         KdaPipeBuf &bs = sm.buf[it & 1];
 
         // ---- segment 1
-        float2 bl[8];
-        float2 ef[8], ifc[8];  // exp(b_t - m_J) and exp(m_J - b_t) of the two channels
+        float2 F[8], Bk[8];    // products of exp(gk) over tokens 0..s and s+1..7 of the quarter
         float nk[8], nq[8];    // inverse norms of k_t and q_t (1 without L2)
         bf16x8 fS[4];
         f32x4 Xs[2], O[2];
         if (pw) {
-            float2 acc = make_float2(0.f, 0.f);
+            float2 e[8];       // exp(gk) of the two channels
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                e[s] = make_float2(exp2_(__uint_as_float(x.g[s][0]) * LOG2E),
+                                   exp2_(__uint_as_float(x.g[s][1]) * LOG2E));
+            F[0] = e[0];
+#pragma unroll
+            for (int s = 1; s < 8; ++s) F[s] = fmul2(F[s - 1], e[s]);
+            Bk[7] = make_float2(1.f, 1.f);
+#pragma unroll
+            for (int s = 6; s >= 0; --s) Bk[s] = fmul2(Bk[s + 1], e[s + 1]);
+            *reinterpret_cast<float2 *>(&sm.hq[wave][2 * p]) = F[7];
+            float pdl = 0.f;
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                acc.x += __uint_as_float(x.g[s][0]) * LOG2E;
-                acc.y += __uint_as_float(x.g[s][1]) * LOG2E;
-                bl[s] = acc;
-            }
-            *reinterpret_cast<float2 *>(&sm.htot[wave][2 * p]) = bl[7];
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
+                const float k0 = lo_bf16(x.k[s]), k1 = hi_bf16(x.k[s]);
+                const float q0 = lo_bf16(x.q[s]), q1 = hi_bf16(x.q[s]);
                 nk[s] = nq[s] = 1.f;
                 if constexpr (L2) {
-                    const float k0 = lo_bf16(x.k[s]), k1 = hi_bf16(x.k[s]);
-                    const float q0 = lo_bf16(x.q[s]), q1 = hi_bf16(x.q[s]);
                     nk[s] = rsqrtf(wave_sum(k0 * k0 + k1 * k1) + 1e-6f);
                     nq[s] = rsqrtf(wave_sum(q0 * q0 + q1 * q1) + 1e-6f);
                 }
+                const float pd = wave_sum(q0 * k0 + q1 * k1) * (nq[s] * nk[s]);
+                pdl = lane == s ? pd : pdl;
             }
-            // everything that needs only in-block differences: b_t - m_J is
-            // the first half's own prefix difference (>= 0, rows grow) or
-            // the second half's own prefix sum (<= 0, columns grow); only the
-            // growing side is clamped.  Rows k e, q e and the block's own
-            // columns k i go to LDS now.
+            if (lane < 8) sm.pdiag[8 * wave + lane] = pdl;
+            // levels 8, 4, 2, 1 lie inside the quarter's 16-token block;
+            // level 16 here for the quarters on either side of the block
+            // boundary (1: columns, 2: rows), the others need a neighbour's
+            // product (segment 2)
             const int col = 2 * p;
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                const int t = 16 * J + 8 * hf + s;
-                if (hf == 0) {
-                    const float d0 = bl[s].x - bl[7].x, d1 = bl[s].y - bl[7].y;
-                    ef[s] = make_float2(exp2_(fminf(d0, KDA_EXP2_MAX)), exp2_(fminf(d1, KDA_EXP2_MAX)));
-                    ifc[s] = make_float2(exp2_(-d0), exp2_(-d1));
-                } else {
-                    const float d0 = bl[s].x, d1 = bl[s].y;
-                    ef[s] = make_float2(exp2_(d0), exp2_(d1));
-                    ifc[s] = make_float2(exp2_(fminf(-d0, KDA_EXP2_MAX)), exp2_(fminf(-d1, KDA_EXP2_MAX)));
-                }
-                const float k0 = lo_bf16(x.k[s]) * nk[s], k1 = hi_bf16(x.k[s]) * nk[s];
-                const float q0 = lo_bf16(x.q[s]) * nq[s], q1 = hi_bf16(x.q[s]) * nq[s];
-                const int o_t = t * KDA_LD + col;
-                *reinterpret_cast<unsigned *>(sm.KR + o_t) = pk2(k0 * ef[s].x, k1 * ef[s].y);
-                *reinterpret_cast<unsigned *>(sm.QR + o_t) = pk2(q0 * ef[s].x, q1 * ef[s].y);
-                *reinterpret_cast<unsigned *>(sm.KC + (kc_base(J) + t) * KDA_LD + col) =
-                    pk2(k0 * ifc[s].x, k1 * ifc[s].y);
+                const int o_t = (8 * wave + s) * KDA_LD + col;
+                const float2 kk = make_float2(lo_bf16(x.k[s]) * nk[s], hi_bf16(x.k[s]) * nk[s]);
+                const float2 qq = make_float2(lo_bf16(x.q[s]) * nq[s], hi_bf16(x.q[s]) * nq[s]);
+                put_level(sm, 1, o_t, kk, qq, hf ? F[s] : Bk[s], hf);
+                put_level(sm, 2, o_t, kk, qq, lvl_factor(e, s, 4), s & 4);
+                put_level(sm, 3, o_t, kk, qq, lvl_factor(e, s, 2), s & 2);
+                put_level(sm, 4, o_t, kk, qq, lvl_factor(e, s, 1), s & 1);
+                if (wave == 1 || wave == 2) put_level(sm, 0, o_t, kk, qq, hf ? Bk[s] : F[s], J);
             }
         }
         if (sw) {
@@ -298,39 +324,33 @@ __global__ __launch_bounds__(512) void kda_pipe_kernel(
         // ---- segment 2
         bf16x4 fE[2];
         if (pw) {
-            float2 mI[2];
-            float2 run = make_float2(0.f, 0.f);
+            float2 Hq[4];
 #pragma unroll
-            for (int I = 0; I < 2; ++I) {
-                const float2 h0 = *reinterpret_cast<const float2 *>(&sm.htot[2 * I][2 * p]);
-                const float2 h1 = *reinterpret_cast<const float2 *>(&sm.htot[2 * I + 1][2 * p]);
-                mI[I] = make_float2(run.x + h0.x, run.y + h0.y);
-                run.x += h0.x + h1.x;
-                run.y += h0.y + h1.y;
-            }
-            if (wave == 0) {
-                bp.gamC[2 * p] = exp2_(run.x);
-                bp.gamC[2 * p + 1] = exp2_(run.y);
-            }
-            const float2 mJ = mI[J];
-            const float2 GJ = make_float2(exp2_(mJ.x), exp2_(mJ.y));
-            const float2 EJ = make_float2(exp2_(run.x - mJ.x), exp2_(run.y - mJ.y));
-            const float2 F1 = make_float2(exp2_(fminf(mI[1].x - mJ.x, 0.f)), exp2_(fminf(mI[1].y - mJ.y, 0.f)));
+            for (int w = 0; w < 4; ++w) Hq[w] = *reinterpret_cast<const float2 *>(&sm.hq[w][2 * p]);
+            // decay over the quarters before and after this one
+            float2 pre = wave > 0 ? Hq[0] : make_float2(1.f, 1.f);
+            pre = wave > 1 ? fmul2(pre, Hq[1]) : pre;
+            pre = wave > 2 ? fmul2(pre, Hq[2]) : pre;
+            float2 post = wave < 3 ? Hq[3] : make_float2(1.f, 1.f);
+            post = wave < 2 ? fmul2(Hq[2], post) : post;
+            post = wave < 1 ? fmul2(Hq[1], post) : post;
+            if (wave == 0)
+                *reinterpret_cast<float2 *>(&bp.gamC[2 * p]) =
+                    fmul2(fmul2(Hq[0], Hq[1]), fmul2(Hq[2], Hq[3]));
+            const float2 h16 = wave == 0 ? Hq[1] : Hq[2];  // level 16 across the neighbour
             const int col = 2 * p;
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                const int t = 16 * J + 8 * hf + s;
-                const float k0 = lo_bf16(x.k[s]) * nk[s], k1 = hi_bf16(x.k[s]) * nk[s];
-                const float q0 = lo_bf16(x.q[s]) * nq[s], q1 = hi_bf16(x.q[s]) * nq[s];
-                const float g0 = ef[s].x * GJ.x, g1 = ef[s].y * GJ.y;   // Gamma_t
-                const float c0 = k0 * ifc[s].x, c1 = k1 * ifc[s].y;     // column operand, block J
-                const int o_t = t * KDA_LD + col;
-                *reinterpret_cast<unsigned *>(bp.KT + o_t) = pk2(k0 * g0, k1 * g1);
-                *reinterpret_cast<unsigned *>(bp.QT + o_t) = pk2(q0 * g0, q1 * g1);
-                *reinterpret_cast<unsigned *>(bp.KE + o_t) = pk2(c0 * EJ.x, c1 * EJ.y);
-                if (J == 0)
-                    *reinterpret_cast<unsigned *>(sm.KC + (kc_base(1) + t) * KDA_LD + col) =
-                        pk2(c0 * F1.x, c1 * F1.y);
+                const int o_t = (8 * wave + s) * KDA_LD + col;
+                const float2 kk = make_float2(lo_bf16(x.k[s]) * nk[s], hi_bf16(x.k[s]) * nk[s]);
+                const float2 qq = make_float2(lo_bf16(x.q[s]) * nq[s], hi_bf16(x.q[s]) * nq[s]);
+                const float2 gm = fmul2(pre, F[s]);     // Gamma_t
+                const float2 ke = fmul2(Bk[s], post);   // exp(b_last - b_t)
+                *reinterpret_cast<unsigned *>(bp.KT + o_t) = pk2(kk.x * gm.x, kk.y * gm.y);
+                *reinterpret_cast<unsigned *>(bp.QT + o_t) = pk2(qq.x * gm.x, qq.y * gm.y);
+                *reinterpret_cast<unsigned *>(bp.KE + o_t) = pk2(kk.x * ke.x, kk.y * ke.y);
+                if (wave == 0 || wave == 3)
+                    put_level(sm, 0, o_t, kk, qq, fmul2(hf ? F[s] : Bk[s], h16), J);
             }
             if (tid < KP_C) sm.beta[tid] = (float)__builtin_bit_cast(__bf16, x.beta);
             if (it + 2 < nchunk) kp_prefetch(x, sq, tp + KP_C, wave, p, tid);
@@ -379,33 +399,63 @@ __global__ __launch_bounds__(512) void kda_pipe_kernel(
         lds_barrier();
 
         // ---- segment 3
-        if (pw && wave < 3) {
-            int I, Jb;
-            pair_ij(wave, I, Jb);
-            f32x4 aG = zero4(), aP = zero4();
+        if (pw) {
+            // waves 0, 1: G of diagonal block I and its inverse; waves 2, 3:
+            // P of diagonal block I, then the level-16 block of G (wave 2)
+            // or P (wave 3).  Each level has its own accumulator; lane (g, r)
+            // element e is pair (i, j) = (r, 4g + e) of the block, which
+            // belongs to the level of the highest bit of i xor j.
+            const int I = wave & 1;
+            f32x4 acc[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                bf16x8 fc, fk, fq;
-                frag_rows(sm.KC, KDA_LD, kc_base(I) + 16 * Jb, 32 * s, lane, fc);
-                frag_rows(sm.KR, KDA_LD, 16 * I, 32 * s, lane, fk);
-                frag_rows(sm.QR, KDA_LD, 16 * I, 32 * s, lane, fq);
-                mma_k32(aG, fc, fk);
-                mma_k32(aP, fc, fq);
-            }
-            if (I == Jb) {
-                const float br = sm.beta[16 * I + r];
-                f32x4 a, pm;
+            for (int l = 0; l < 4; ++l) acc[l] = zero4();
+            if (wave < 2) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    a[e] = r > 4 * g + e ? br * aG[e] : 0.f;
-                    pm[e] = r >= 4 * g + e ? aP[e] : 0.f;
-                }
-                const f32x4 b4 = *reinterpret_cast<const f32x4 *>(sm.beta + 16 * I + 4 * g);
-                diag_inverse(a, b4, bp.Tb, I, lane);
-                store_fragblk(bp.Pb, wave, lane, pm);
+                for (int l = 0; l < 4; ++l)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        bf16x8 f;
+                        frag_rows(sm.W[l + 1], KDA_LD, 16 * I, 32 * s, lane, f);
+                        mma_k32(acc[l], f, f);
+                    }
             } else {
-                store_fragblk(bp.Gb, 0, lane, aG);
-                store_fragblk(bp.Pb, wave, lane, aP);
+#pragma unroll
+                for (int l = 0; l < 4; ++l)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        bf16x8 fc, fr;
+                        frag_rows(sm.W[l + 1], KDA_LD, 16 * I, 32 * s, lane, fc);
+                        frag_rows(sm.QR[l + 1], KDA_LD, 16 * I, 32 * s, lane, fr);
+                        mma_k32(acc[l], fc, fr);
+                    }
+            }
+            f32x4 m;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * g + e, d = r ^ j;
+                const float lv = d >= 8 ? acc[0][e] : d >= 4 ? acc[1][e] : d >= 2 ? acc[2][e] : acc[3][e];
+                m[e] = r > j ? lv : 0.f;
+            }
+            if (wave < 2) {
+                const float br = sm.beta[16 * I + r];
+                const f32x4 b4 = *reinterpret_cast<const f32x4 *>(sm.beta + 16 * I + 4 * g);
+                diag_inverse(br * m, b4, bp.Tb, I, lane);
+            } else {
+                const float pd = sm.pdiag[16 * I + r];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) m[e] = r == 4 * g + e ? pd : m[e];
+                store_fragblk(bp.Pb, 2 * I, lane, m);
+                const __bf16 *rows = wave == 2 ? sm.W[0] : sm.QR[0];
+                f32x4 a16 = zero4();
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    bf16x8 fc, fr;
+                    frag_rows(sm.W[0], KDA_LD, 0, 32 * s, lane, fc);
+                    frag_rows(rows, KDA_LD, 16, 32 * s, lane, fr);
+                    mma_k32(a16, fc, fr);
+                }
+                if (wave == 2) store_fragblk(bp.Gb, 0, lane, a16);
+                else store_fragblk(bp.Pb, 1, lane, a16);
             }
         }
         if (sw) {

@@ -157,13 +157,12 @@ enum {
  *               with Dk = 128 and Dv a multiple of 64, without
  *               DR_FUSED_RECURRENT, run the chunked kernel (32-token
  *               chunks, same digest, "Chunkwise KDA"; the chunk argument is
- *               validated but unused).  Its decay ratios are split around a
- *               reference token per 16-token block, which keeps every factor
- *               finite and accurate while the sum of gk over any 8
- *               consecutive tokens of a channel stays above -40 (gk >= -5
- *               per token guarantees it) and gk <= 0; outside that domain the
- *               results lose accuracy (nothing overflows).  All other cases
- *               run the token-serial schedule, exact for any gk.
+ *               validated but unused).  It forms every decay ratio between
+ *               two tokens of a chunk as a product of per-token factors
+ *               exp(gk) <= 1, so it is exact up to rounding for any gk <= 0,
+ *               down to -inf (a channel erased in one token).  Positive gk
+ *               is computed as given while those products stay finite.  All
+ *               other cases run the token-serial schedule.
  *   workspace, workspace_bytes
  *               device scratch (16-byte aligned, not overlapping any argument)
  *               for the segment-parallel schedule, or NULL.  When the

@@ -1,13 +1,17 @@
 """GPU parity of the chunked KDA forward (``kda_fwd`` on bf16 inputs with
 d_k = 128 and d_v a multiple of 64) against the fp64 KDA oracle.
 
-hada.io digest, section "Chunkwise KDA": per-channel prefix sums of the log
-decay inside each 64-token chunk, decayed couplings and read weights, the
-unit lower-triangular solve, and the end-of-chunk state as one product.
-Seeded inputs go to the HIP path and to ``oracle.kda_ref``; o and S_T must
-satisfy max |gpu - ref| <= 2e-2 * max |ref| (bf16 inputs).  Lengths span one
-to several chunks with ragged tails; decays go from near 1 to the edge of
-the kernel's domain (gk = -5 on every token and channel).
+hada.io digest, section "Chunkwise KDA": per-channel cumulative decays
+inside each 32-token chunk, decayed couplings and read weights, the unit
+lower-triangular solve, and the end-of-chunk state as one product.  Seeded
+inputs go to the HIP path and to ``oracle.kda_ref``; o and S_T must satisfy
+max |gpu - ref| <= 2e-2 * max |ref| (bf16 inputs).  Lengths span one to
+several chunks with ragged tails; decays go from near 1 to erasing a channel
+within one token (the digest's section "Kimi Delta Attention : attenuation
+par canal": per-channel decay lets one channel be wiped while another keeps
+its content): the gated layer's draw with A up to 16, constant gk down to
+-1e4 on every token and channel, half the channels erased while the other
+half keep everything, and channels at gk = -inf.
 """
 from __future__ import annotations
 
@@ -65,25 +69,50 @@ def test_lengths(T):
     _check(_kda("layer_1p3b", B=2, H=2, T=T, seed=10100 + T))
 
 
-@pytest.mark.parametrize("amax", [0.02, 0.3, 1.0])
+@pytest.mark.parametrize("amax", [0.02, 0.3, 1.0, 16.0])
 def test_decay_strengths(amax):
     _check(_kda(H=4, T=200, gate_amax=amax, seed=10200 + int(100 * amax)))
 
 
-def test_domain_edge_constant_decay():
-    # gk = -5 on every token and channel: 8 tokens sum to -40
+@pytest.mark.parametrize("gval", [-5.0, -12.0, -80.0, -1e4])
+def test_constant_strong_decay(gval):
+    # the same gk on every token and channel: a token's write survives the
+    # next token by exp(gval) (from e^-5 down to nothing at all)
     w = _kda(B=1, H=2, T=140, seed=10300)
     x = W.generate(w)
-    x["gk"] = torch.full_like(x["gk"], -5.0)
+    x["gk"] = torch.full_like(x["gk"], gval)
     _check(w, x=x)
 
 
-def test_mixed_channels_some_erased():
-    # half the channels keep everything, the other half forget at rate e^-4
+def test_half_the_channels_erased():
+    # channels 64..127 forget everything at every token (gk = -1e4), channels
+    # 0..63 keep everything (gk = 0)
     w = _kda(B=2, H=2, T=100, seed=10350)
     x = W.generate(w)
     gk = torch.zeros_like(x["gk"])
-    gk[..., 64:] = -4.0
+    gk[..., 64:] = -1e4
+    x["gk"] = gk
+    _check(w, x=x)
+
+
+def test_erasure_mixed_into_the_gate_draw():
+    # the A ~ U(0, 16) draw, with every third token erasing every other
+    # channel and a block of tokens and channels that keeps everything
+    w = _kda(B=2, H=2, T=161, gate_amax=16.0, seed=10360)
+    x = W.generate(w)
+    gk = x["gk"].clone()
+    gk[:, ::3, :, ::2] = -1e4
+    gk[:, 40:75, :, 10:30] = 0.0
+    x["gk"] = gk
+    _check(w, x=x)
+
+
+def test_channels_at_minus_infinity():
+    # exp(-inf) = 0 exactly: a quarter of the channels erased outright
+    w = _kda(B=1, H=2, T=90, gate_amax=16.0, seed=10370)
+    x = W.generate(w)
+    gk = x["gk"].clone()
+    gk[..., 96:] = float("-inf")
     x["gk"] = gk
     _check(w, x=x)
 
@@ -109,8 +138,9 @@ def test_equal_channels_matches_the_gated_chunk_kernel():
     assert rel_err(to_np(s_k), to_np(s_g)) <= 2e-2
 
 
-def test_matches_token_serial_schedule():
-    w = _kda(B=2, H=2, T=333, seed=10600)
+@pytest.mark.parametrize("amax", [1.0, 16.0])
+def test_matches_token_serial_schedule(amax):
+    w = _kda(B=2, H=2, T=333, gate_amax=amax, seed=10600)
     d = to_dev(W.generate(w))
     o_c, s_c = dr.kda_fwd(d["q"], d["k"], d["v"], d["beta"], d["gk"], d["S0"])
     o_r, s_r = dr.kda_fwd(d["q"], d["k"], d["v"], d["beta"], d["gk"], d["S0"],
@@ -150,10 +180,11 @@ def test_output_scale_and_no_initial_state():
     assert rel_err(to_np(st), s_ref) <= 2e-2
 
 
-def test_layer_shape_sampled_heads():
+@pytest.mark.parametrize("amax", [1.0, 16.0])
+def test_layer_shape_sampled_heads(amax):
     # the benchmark's launch: B8 H16 T2048 d128, whole heads sampled
     heads = [(0, 0), (3, 7), (7, 15)]
-    _check(_kda("layer_1p3b", seed=10800), heads=heads)
+    _check(_kda("layer_1p3b", gate_amax=amax, seed=10800), heads=heads)
 
 
 def test_packed_sequences_equal_separate_calls():

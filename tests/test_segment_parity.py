@@ -119,10 +119,16 @@ def test_long_prefill_full_size_sampled_heads():
     assert eo <= 2e-2 and es <= 2e-2
 
 
-def test_kda_long_sequence():
-    # per-key-channel decay: the chunked KDA kernel on the segments
-    w = W.get("long_prefill", H=2, T=6700, gate_amax=1.0, kda=True, seed=12700)
+@pytest.mark.parametrize("case", ["amax1", "amax16_erased"])
+def test_kda_long_sequence(case):
+    # per-key-channel decay: the chunked KDA kernel on the segments, with the
+    # gated layer's draw (A up to 1, or up to 16 with every fifth token
+    # erasing half the channels)
+    amax = 1.0 if case == "amax1" else 16.0
+    w = W.get("long_prefill", H=2, T=6700, gate_amax=amax, kda=True, seed=12700)
     x = W.generate(w)
+    if case != "amax1":
+        x["gk"][:, ::5, :, 64:] = -1e4
     d = to_dev(x)
     need = dr.chunk_fwd_workspace_bytes(w.B, w.T, w.H, w.Dk, w.Dv, 64)
     assert need > 0
