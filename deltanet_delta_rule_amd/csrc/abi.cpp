@@ -82,11 +82,13 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
     if (gated && T > 0 && !g) return DR_ERR_INVALID_ARG;
     if (gk && gated) return DR_ERR_INVALID_ARG;  // one decay kind
     if (ws && (ws_bytes < 0 || !aligned16(ws))) return DR_ERR_INVALID_ARG;
-    // q, k, gk and the states are read in 16-byte vectors; v, beta and o element-wise
-    const void *vec_ptrs[] = {q, k, S0, S_T, gk};
+    // q, k, gk and the states are read in 16-byte vectors and o is written
+    // in 8- or 16-byte vectors (the chunked kernels); v and beta are read
+    // element-wise
+    const void *vec_ptrs[] = {q, k, S0, S_T, gk, o};
     for (const void *p : vec_ptrs)
         if (p && !aligned16(p)) return DR_ERR_INVALID_ARG;
-    const void *elem_ptrs[] = {v, beta, o};
+    const void *elem_ptrs[] = {v, beta};
     for (const void *p : elem_ptrs)
         if (p && !aligned_to(p, esz)) return DR_ERR_INVALID_ARG;
     if (g && !aligned_to(g, 4)) return DR_ERR_INVALID_ARG;
@@ -94,17 +96,17 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
     const Span in[] = {{q, nqk * esz},        {k, nqk * esz},
                        {v, nv * esz},         {beta, nb * esz},
                        {S0, ns * 4},          {gated ? g : nullptr, nb * 4},
-                       {cu, (nseq + 1) * 4},  {gk, nqk * 4},
-                       {ws, ws ? ws_bytes : 0}};
-    const Span so{o, nv * esz}, sst{S_T, ns * 4};
+                       {cu, (nseq + 1) * 4},  {gk, nqk * 4}};
+    // the workspace is written before the inputs are read: an output too
+    const Span so{o, nv * esz}, sst{S_T, ns * 4}, sws{ws, ws ? ws_bytes : 0};
     for (const Span &s : in) {
         if (T > 0 && overlaps(so, s)) return DR_ERR_INVALID_ARG;
         // S_T may be exactly S0 (in-place carry); any other overlap is rejected
         if (overlaps(sst, s) && !(s.p == S0 && S_T == S0)) return DR_ERR_INVALID_ARG;
+        if (overlaps(sws, s)) return DR_ERR_INVALID_ARG;
     }
     if (T > 0 && overlaps(so, sst)) return DR_ERR_INVALID_ARG;
-    if (ws && (overlaps(so, {ws, ws_bytes}) || overlaps(sst, {ws, ws_bytes})))
-        return DR_ERR_INVALID_ARG;
+    if (overlaps(so, sws) || overlaps(sst, sws)) return DR_ERR_INVALID_ARG;
 
     dr::ChunkFwdArgs a{q,       k,        v,       beta,       gated ? g : nullptr,
                        S0,      o,        S_T,     nullptr,    cu,

@@ -38,7 +38,9 @@
  *            32-bit offsets).
  *   Pointers Device pointers (hipMalloc'd or equivalent).  q, k and every
  *            state pointer must be 16-byte aligned (they are read as 16-byte
- *            vectors); v, beta and o need only their element alignment.
+ *            vectors), and so must o of the sequence entry points (the
+ *            chunked kernels write it in 8- or 16-byte vectors); v, beta and
+ *            the decode step's o need only their element alignment.
  *            They are borrowed: the library never allocates, frees or keeps
  *            them beyond the work queued on `stream`.
  *   Stream   `stream` is a hipStream_t passed as void*; NULL is the default
@@ -164,7 +166,8 @@ enum {
  *               is computed as given while those products stay finite.  All
  *               other cases run the token-serial schedule.
  *   workspace, workspace_bytes
- *               device scratch (16-byte aligned, not overlapping any argument)
+ *               device scratch (16-byte aligned, not overlapping any argument;
+ *               an overlap is DR_ERR_INVALID_ARG)
  *               for the segment-parallel schedule, or NULL.  When the
  *               sequences are too few to fill the GPU (say B = 1, H = 16,
  *               T = 32768), the plain and gated rules and the chunked KDA

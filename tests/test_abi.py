@@ -84,6 +84,7 @@ def _step(lib, q=P[0], k=P[1], v=P[2], beta=P[3], S=P[4], o=P[5], B=2, H=2,
     dict(q=None), dict(k=None), dict(v=None), dict(beta=None), dict(o=None),
     dict(q=MISALIGNED), dict(k=MISALIGNED), dict(S0=MISALIGNED),
     dict(S_T=MISALIGNED), dict(v=ODD), dict(beta=ODD), dict(o=ODD),
+    dict(o=MISALIGNED),              # the chunked kernels store o in 8/16-byte vectors
     dict(o=P[0]),                    # output overlaps q
     dict(S_T=P[1]),                  # final state overlaps k
     dict(S0=P[6], S_T=P[4]),         # final state overlaps o
@@ -245,6 +246,8 @@ def test_chunk_options_struct_layout():
     (dict(gk=P[7].value, flags=3), dict(S_T=P[7])),              # S_T overlaps gk
     (dict(workspace=MISALIGNED.value, workspace_bytes=1 << 20), {}),   # workspace misaligned
     (dict(workspace=P[4].value, workspace_bytes=1 << 20), {}),         # workspace overlaps o
+    (dict(workspace=P[1].value, workspace_bytes=1 << 20), {}),         # workspace overlaps k
+    (dict(workspace=P[6].value, workspace_bytes=1 << 20, gk=P[6].value + 4096), {}),  # and gk
     (dict(workspace=P[7].value, workspace_bytes=-1), {}),              # negative size
 ])
 def test_chunk_ex_rejects_invalid(lib, kw, call):
