@@ -304,10 +304,9 @@ def kda_fwd(q, k, v, beta, gk, S0=None, *, output_final_state: bool = True, o=No
     ``delta_rule_chunk_fwd`` plus gk ``[B,T,H,Dk]`` float32, the log decay
     (<= 0) of each key channel at each token (column j of the state is
     multiplied by exp(gk_t[j]) before token t).  bf16 inputs with Dk = 128 and
-    Dv a multiple of 64 run the chunked kernel (32-token chunks; accurate while
-    gk summed over any 8 consecutive tokens of a channel stays above -40, e.g.
-    gk >= -5); everything else, or ``fused_recurrent=True``, runs the
-    token-serial schedule, which has no such limit.  Long sequences that do
+    Dv a multiple of 64 run the chunked kernel (32-token chunks; exact up to
+    rounding for any gk <= 0, down to -inf); everything else, or
+    ``fused_recurrent=True``, runs the token-serial schedule.  Long sequences that do
     not fill the GPU run the chunked kernel segment-parallel (``workspace``
     as in ``delta_rule_chunk_fwd``)."""
     return _chunk_call(False, q, k, v, beta, None, S0, 64, output_final_state, o, S_T, stream,
