@@ -31,6 +31,8 @@ __all__ = [
     "gated_delta_rule_chunk_fwd",
     "gated_delta_rule_recurrent_step",
     "delta_rule_chunk_bwd",
+    "delta_rule_chunk_fwd_noalloc",
+    "DeltaRuleScratchError",
     "kda_recurrent_step",
     "kda_fwd",
     "DR_FUSED_RECURRENT",
@@ -44,7 +46,9 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdeltarule.so")
 
-DR_OK, DR_ERR_INVALID_ARG, DR_ERR_UNSUPPORTED, DR_ERR_HIP = 0, 1, 2, 3
+DR_OK, DR_ERR_INVALID_ARG, DR_ERR_UNSUPPORTED, DR_ERR_HIP, DR_ERR_SCRATCH = 0, 1, 2, 3, 4
+# DR_STATIC_SCRATCH_BYTES of include/deltarule.h
+DR_STATIC_SCRATCH_BYTES = 16 * 1024 * 1024 + 64 * 1024
 DR_F32, DR_BF16 = 0, 1
 
 _lib = None
@@ -68,6 +72,11 @@ class DeltaRuleError(RuntimeError):
     """A HIP runtime failure reported by libdeltarule."""
 
 
+class DeltaRuleScratchError(RuntimeError):
+    """delta_rule_chunk_fwd_noalloc: the shape needs more scratch than the
+    library's static buffer holds (DR_ERR_SCRATCH)."""
+
+
 def load_library():
     """Load libdeltarule.so (built in place by ``deltanet_delta_rule_amd.build``)."""
     global _lib
@@ -89,6 +98,10 @@ def load_library():
     lib.delta_rule_chunk_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp,
                                             i64, i64, i64, i64, i64, i64,
                                             ctypes.POINTER(dr_chunk_opts), i32, vp]
+    lib.delta_rule_chunk_fwd_noalloc.restype = i32
+    lib.delta_rule_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp,
+                                                 i64, i64, i64, i64, i64, i64,
+                                                 ctypes.POINTER(dr_chunk_opts), i32, vp]
     lib.gated_delta_rule_chunk_fwd.restype = i32
     lib.gated_delta_rule_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                                                i64, i64, i64, i64, i64, i64, i32, vp]
@@ -131,6 +144,8 @@ def _check(status: int) -> None:
         raise DeltaRuleError(f"{msg} (hipError {load_library().delta_rule_last_hip_error()})")
     if status == DR_ERR_UNSUPPORTED:
         raise NotImplementedError(msg)
+    if status == DR_ERR_SCRATCH:
+        raise DeltaRuleScratchError(msg)
     raise ValueError(msg)
 
 
@@ -228,9 +243,14 @@ def _chunk_call(gated, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, 
     common = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta))
     tail = (B, T, H, Dk, Dv, int(chunk))
     # segment-parallel schedule for sequences too few to fill the GPU:
-    # workspace=None allocates it when the library asks for one, False never
+    # workspace=None allocates it when the library asks for one, False never,
+    # "static" takes the library's static scratch (delta_rule_chunk_fwd_noalloc)
     ws_ptr, ws_bytes = None, 0
-    if workspace is not False and cu_seqlens is None and not recurrent and T > 0:
+    noalloc = isinstance(workspace, str)
+    if noalloc and workspace != "static":
+        raise ValueError(f"workspace must be a tensor, None, False or 'static', not {workspace!r}")
+    if (not noalloc and workspace is not False and cu_seqlens is None and not recurrent
+            and T > 0):
         if workspace is None:
             need = lib.delta_rule_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, int(chunk),
                                                             _dtype_code(q))
@@ -241,7 +261,7 @@ def _chunk_call(gated, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, 
                 raise ValueError("workspace must be a contiguous tensor on the inputs' GPU")
             ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     if (scale is None and cu_seqlens is None and not l2norm and gk is None and not recurrent
-            and ws_ptr is None):
+            and ws_ptr is None and not noalloc):
         if gated:
             st = lib.gated_delta_rule_chunk_fwd(*common, _ptr(g), _ptr(S0), _ptr(o), _ptr(S_T),
                                                 *tail, _dtype_code(q), _stream(dev, stream))
@@ -257,9 +277,9 @@ def _chunk_call(gated, q, k, v, beta, g, S0, chunk, output_final_state, o, S_T, 
                              | (DR_FUSED_RECURRENT if recurrent else 0),
                              gk=None if gk is None else gk.data_ptr(),
                              workspace=ws_ptr, workspace_bytes=ws_bytes)
-        st = lib.delta_rule_chunk_fwd_ex(*common, _ptr(S0), _ptr(o), _ptr(S_T), *tail,
-                                         ctypes.byref(opts), _dtype_code(q),
-                                         _stream(dev, stream))
+        entry = lib.delta_rule_chunk_fwd_noalloc if noalloc else lib.delta_rule_chunk_fwd_ex
+        st = entry(*common, _ptr(S0), _ptr(o), _ptr(S_T), *tail, ctypes.byref(opts),
+                   _dtype_code(q), _stream(dev, stream))
     _check(st)
     return o, S_T
 
@@ -284,6 +304,26 @@ def delta_rule_chunk_fwd(q, k, v, beta, S0=None, *, chunk: int = 64,
     return _chunk_call(False, q, k, v, beta, None, S0, chunk, output_final_state, o, S_T,
                        stream, scale, cu_seqlens, use_qk_l2norm_in_kernel,
                        recurrent=fused_recurrent, workspace=workspace)
+
+
+def delta_rule_chunk_fwd_noalloc(q, k, v, beta, S0=None, *, g=None, gk=None, chunk: int = 64,
+                                 output_final_state: bool = True, o=None, S_T=None,
+                                 scale=None, cu_seqlens=None, use_qk_l2norm_in_kernel=False,
+                                 fused_recurrent=False, stream=None):
+    """The chunked forward of any rule (plain; gated with ``g``; KDA with
+    ``gk``) with the segment-parallel schedule's scratch taken from the
+    library's static per-GPU buffer instead of a workspace
+    (``delta_rule_chunk_fwd_noalloc``): the library allocates nothing.  Pass
+    ``o`` (and ``S_T``) to allocate nothing here either.  Raises
+    ``DeltaRuleScratchError`` when the shape's schedule needs more than
+    ``DR_STATIC_SCRATCH_BYTES``.  Calls that overlap in time on one GPU race on
+    that buffer."""
+    if g is not None and gk is not None:
+        raise ValueError("g and gk are exclusive")
+    return _chunk_call(g is not None, q, k, v, beta, g, S0, 64 if gk is not None else chunk,
+                       output_final_state, o, S_T, stream, scale, cu_seqlens,
+                       use_qk_l2norm_in_kernel, gk=gk, recurrent=fused_recurrent,
+                       workspace="static")
 
 
 def gated_delta_rule_chunk_fwd(q, k, v, beta, g, S0=None, *, chunk: int = 64,

@@ -56,7 +56,7 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
                     int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t chunk,
                     const int32_t *cu, int64_t nseq, float scale, bool l2, dr_dtype dtype,
                     void *stream, const float *gk = nullptr, bool recurrent = false,
-                    void *ws = nullptr, int64_t ws_bytes = 0) {
+                    void *ws = nullptr, int64_t ws_bytes = 0, bool noalloc = false) {
     if (dtype != DR_F32 && dtype != DR_BF16) return DR_ERR_INVALID_ARG;
     if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0 || chunk < 0) return DR_ERR_INVALID_ARG;
     if (cu && (B != 1 || nseq < 0 || !aligned_to(cu, 4))) return DR_ERR_INVALID_ARG;
@@ -82,6 +82,7 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
     if (gated && T > 0 && !g) return DR_ERR_INVALID_ARG;
     if (gk && gated) return DR_ERR_INVALID_ARG;  // one decay kind
     if (ws && (ws_bytes < 0 || !aligned16(ws))) return DR_ERR_INVALID_ARG;
+    if (noalloc && (ws || ws_bytes != 0)) return DR_ERR_INVALID_ARG;  // scratch is the library's
     // q, k, gk and the states are read in 16-byte vectors and o is written
     // in 8- or 16-byte vectors (the chunked kernels); v and beta are read
     // element-wise
@@ -113,9 +114,17 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
                        ns_count, T,       H,       (int)Dk,    (int)Dv,
                        (int)chunk, scale, l2,     gk,       recurrent};
     // one long sequence per head: the segment-parallel schedule, when the
-    // caller gave it a large enough workspace
-    if (ws && !cu && !recurrent && (!gk || dr::kda_chunk_supported(a, dtype == DR_BF16))) {
+    // caller gave it a large enough workspace (or, without allocation, when
+    // the library's static scratch holds what it needs)
+    if ((ws || noalloc) && !cu && !recurrent &&
+        (!gk || dr::kda_chunk_supported(a, dtype == DR_BF16))) {
         const dr::SegPlan pl = dr::seg_plan(B, T, H, (int)Dk, (int)Dv, (int)chunk);
+        if (noalloc && pl.P > 0) {
+            if (pl.bytes > DR_STATIC_SCRATCH_BYTES) return DR_ERR_SCRATCH;
+            const hipError_t e = dr::static_scratch(&ws);
+            if (e != hipSuccess) return hip_status(e);
+            ws_bytes = DR_STATIC_SCRATCH_BYTES;
+        }
         if (pl.P > 0 && ws_bytes >= pl.bytes)
             return hip_status(dr::launch_chunk_fwd_segmented(
                 a, pl, ws, dtype == DR_BF16, static_cast<hipStream_t>(stream)));
@@ -259,6 +268,22 @@ dr_status delta_rule_chunk_fwd_ex(const void *q, const void *k, const void *v,
                      x.workspace_bytes);
 }
 
+dr_status delta_rule_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                                       const void *beta, const float *S0, void *o, float *S_T,
+                                       int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                       int64_t chunk, const dr_chunk_opts *opts, dr_dtype dtype,
+                                       void *stream) {
+    dr_chunk_opts d{};
+    d.scale = 1.f;
+    const dr_chunk_opts &x = opts ? *opts : d;
+    if (x.flags & ~uint32_t(DR_QK_L2NORM | DR_FUSED_RECURRENT))
+        return DR_ERR_INVALID_ARG;  // unknown flags
+    return chunk_fwd(q, k, v, beta, x.g, x.g != nullptr, S0, o, S_T, B, T, H, Dk, Dv, chunk,
+                     x.cu_seqlens, x.num_seqs, x.scale, (x.flags & DR_QK_L2NORM) != 0, dtype,
+                     stream, x.gk, (x.flags & DR_FUSED_RECURRENT) != 0, x.workspace,
+                     x.workspace_bytes, true);
+}
+
 dr_status delta_rule_recurrent_step(const void *q, const void *k,
                                     const void *v, const void *beta, float *S,
                                     void *o, int64_t B, int64_t H, int64_t Dk,
@@ -319,12 +344,15 @@ const char *delta_rule_status_string(dr_status status) {
     case DR_ERR_INVALID_ARG: return "DR_ERR_INVALID_ARG: invalid argument";
     case DR_ERR_UNSUPPORTED: return "DR_ERR_UNSUPPORTED: unsupported size or shape";
     case DR_ERR_HIP: return "DR_ERR_HIP: HIP runtime error (see delta_rule_last_hip_error)";
+    case DR_ERR_SCRATCH:
+        return "DR_ERR_SCRATCH: the segment-parallel schedule of this shape needs more than "
+               "the static scratch (DR_STATIC_SCRATCH_BYTES); pass a workspace instead";
     default: return "unknown dr_status";
     }
 }
 
 int delta_rule_last_hip_error(void) { return g_last_hip_error; }
 
-int delta_rule_version(void) { return 20700; }
+int delta_rule_version(void) { return 20800; }
 
 }  // extern "C"

@@ -45,6 +45,9 @@ struct SegPlan {
 SegPlan seg_plan(int64_t B, int64_t T, int64_t H, int Dk, int Dv, int chunk);
 hipError_t launch_chunk_fwd_segmented(const ChunkFwdArgs &a, const SegPlan &pl, void *ws,
                                       bool bf16, hipStream_t stream);
+// Device address of the library's static scratch (DR_STATIC_SCRATCH_BYTES)
+// on the current device, resolved on the first call per device.
+hipError_t static_scratch(void **ptr);
 
 // Chunked KDA (per-channel decay): bf16, d_k = 128, d_v a multiple of 64;
 // other cases run the token-serial kernel.

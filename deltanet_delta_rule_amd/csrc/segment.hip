@@ -26,11 +26,39 @@
 // 0.59x the time of the plain schedule; B4 H8 T2048 with 8 segments of 4
 // chunks in 1.45x).
 #include <algorithm>
+#include <mutex>
 
+#include "deltarule.h"
 #include "dr_common.hpp"
 #include "dr_launch.hpp"
 
 namespace dr {
+
+// Scratch of delta_rule_chunk_fwd_noalloc: one copy per GPU, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device array, so kernels get the per-device address resolved below.
+static __device__ __align__(256) unsigned char scratch[DR_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::once_flag g_scratch_once[MAX_DEVICES];
+hipError_t g_scratch_err[MAX_DEVICES];
+void *g_scratch_ptr[MAX_DEVICES];
+}  // namespace
+
+hipError_t static_scratch(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    // first call on this device, with the device current
+    std::call_once(g_scratch_once[dev], [dev] {
+        g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+    });
+    if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 namespace {
 

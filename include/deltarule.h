@@ -69,7 +69,8 @@ typedef enum dr_status {
     DR_OK = 0,
     DR_ERR_INVALID_ARG = 1, /* null/misaligned pointer, negative size, bad enum */
     DR_ERR_UNSUPPORTED = 2, /* valid request outside the supported size set */
-    DR_ERR_HIP = 3          /* a HIP runtime call failed; see last_hip_error */
+    DR_ERR_HIP = 3,         /* a HIP runtime call failed; see last_hip_error */
+    DR_ERR_SCRATCH = 4      /* the call needs more than the static scratch holds */
 } dr_status;
 
 typedef enum dr_dtype {
@@ -218,6 +219,44 @@ dr_status delta_rule_chunk_fwd_ex(const void *q, const void *k, const void *v,
                                   void *stream);
 
 /*
+ * Size of the static device scratch of delta_rule_chunk_fwd_noalloc, per GPU:
+ * 16 MiB + 64 KiB, enough for the segment-parallel schedule of every shape
+ * with Dv = 128 (B = 1, H = 16, T = 32768, d = 128 needs 16 MiB + 256 B).
+ */
+#define DR_STATIC_SCRATCH_BYTES ((int64_t)16 * 1024 * 1024 + 64 * 1024)
+
+/*
+ * delta_rule_chunk_fwd_noalloc -- delta_rule_chunk_fwd_ex for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the segment-parallel schedule takes
+ * its scratch from a static device array of DR_STATIC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends, instead of
+ * from opts->workspace.  Nothing is allocated or freed.
+ *
+ *   Every argument, size, layout and result is that of delta_rule_chunk_fwd_ex
+ *   with a workspace of DR_STATIC_SCRATCH_BYTES, except:
+ *   - opts->workspace must be NULL and opts->workspace_bytes 0
+ *     (DR_ERR_INVALID_ARG otherwise);
+ *   - when the segment-parallel schedule applies to the shape and needs more
+ *     than DR_STATIC_SCRATCH_BYTES (delta_rule_chunk_fwd_workspace_bytes says
+ *     how much), the call returns DR_ERR_SCRATCH and enqueues nothing; use
+ *     delta_rule_chunk_fwd_ex with a workspace for such shapes;
+ *   - the scratch belongs to the current device, which must be the device
+ *     of `stream`.  Every call on a GPU shares that GPU's array (it keeps the
+ *     last call's contents; each call writes everything it reads there before
+ *     reading it), so calls that overlap in time on one GPU -- on different
+ *     streams or from different threads -- race and give wrong results:
+ *     serialise them.
+ *   The first call on a device resolves the array's device address
+ *   (hipGetSymbolAddress); a failure there is DR_ERR_HIP.
+ */
+dr_status delta_rule_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                                       const void *beta, const float *S0, void *o, float *S_T,
+                                       int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                       int64_t chunk, const dr_chunk_opts *opts, dr_dtype dtype,
+                                       void *stream);
+
+/*
  * delta_rule_recurrent_step -- one decode token per sequence, state in place.
  *
  * For every (b,h): reads S, applies the delta-rule write for the token
@@ -357,7 +396,8 @@ int delta_rule_last_hip_error(void);
  * delta_rule_recurrent_step_ex; 2.4.0: delta_rule_chunk_bwd; 2.5.0: per-channel
  * decay (gk) in dr_step_opts; 2.6.0: DR_FUSED_RECURRENT and gk in
  * dr_chunk_opts; 2.7.0: the segment-parallel schedule's workspace in
- * dr_chunk_opts and delta_rule_chunk_fwd_workspace_bytes). */
+ * dr_chunk_opts and delta_rule_chunk_fwd_workspace_bytes; 2.8.0:
+ * delta_rule_chunk_fwd_noalloc and DR_ERR_SCRATCH). */
 int delta_rule_version(void);
 
 #ifdef __cplusplus

@@ -59,7 +59,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    for code in range(4):
+    for code in range(5):
         s = dr.delta_rule_status_string(code)
         assert s.startswith("DR_")
     assert "unknown" in dr.delta_rule_status_string(99)
@@ -354,3 +354,46 @@ def test_chunk_fwd_workspace_bytes(lib):
     assert f(1, 32768, 16, 48, 128, 64, dr.DR_BF16) == -1
     assert f(1, 32768, 16, 128, 128, 100, dr.DR_BF16) == -1
     assert f(1, 32768, 16, 128, 128, 64, 7) == -1
+
+
+# ------------------------------------------------ chunked forward, no allocation
+def _na(lib, opts=None, q=P[0], k=P[1], v=P[2], beta=P[3], S0=None, o=P[4], S_T=P[5],
+        B=1, T=64, H=2, Dk=64, Dv=64, chunk=64, dtype=dr.DR_BF16):
+    return lib.delta_rule_chunk_fwd_noalloc(q, k, v, beta, S0, o, S_T, B, T, H, Dk, Dv, chunk,
+                                            None if opts is None else ctypes.byref(opts),
+                                            dtype, None)
+
+
+@pytest.mark.parametrize("kw, call", [
+    (dict(workspace=P[7].value, workspace_bytes=1 << 20), {}),   # the scratch is the library's
+    (dict(workspace_bytes=1 << 20), {}),
+    (dict(flags=4), {}), (dict(scale=float("nan")), {}),
+    ({}, dict(o=P[0])), ({}, dict(q=MISALIGNED)), ({}, dict(B=-1)),
+])
+def test_noalloc_rejects_invalid(lib, kw, call):
+    assert _na(lib, _opts(**kw), **call) == dr.DR_ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_a_plan_beyond_the_static_scratch(lib):
+    # B1 H4 T65536, d_k 128, d_v 64: 64 segments, H_p 8 MiB + M_p 16 MiB, more
+    # than DR_STATIC_SCRATCH_BYTES; refused before any HIP call (fake
+    # pointers 4 GiB apart)
+    f = lib.delta_rule_chunk_fwd_workspace_bytes
+    need = f(1, 65536, 4, 128, 64, 64, dr.DR_BF16)
+    assert need > dr.DR_STATIC_SCRATCH_BYTES
+    far = [ctypes.c_void_p((1 << 32) * (i + 1)) for i in range(6)]
+    st = _na(lib, None, q=far[0], k=far[1], v=far[2], beta=far[3], o=far[4], S_T=far[5],
+             T=65536, H=4, Dk=128, Dv=64)
+    assert st == dr.DR_ERR_SCRATCH
+    assert "DR_ERR_SCRATCH" in dr.delta_rule_status_string(st)
+    assert lib.delta_rule_last_hip_error() == 0
+
+
+def test_static_scratch_holds_every_plan_with_128_value_rows(lib):
+    # the segment count is capped by the GPU's 256 CUs, so with d_v = 128 the
+    # largest plan (d_k = 128) needs 16 MiB + a few hundred bytes
+    f = lib.delta_rule_chunk_fwd_workspace_bytes
+    worst = max(f(B, T, H, 128, 128, c, dr.DR_BF16)
+                for B in (1, 2, 4) for H in (1, 2, 4, 8, 16)
+                for T in (8192, 32768, 262144) for c in (16, 32, 64))
+    assert 0 < worst <= dr.DR_STATIC_SCRATCH_BYTES
