@@ -13,7 +13,10 @@ JSON line on stdout:
                ridge of ~315 flop/B), from the mean launch time measured with
                HIP events on the launch stream; mfma_frac gives the same time
                against the dense bf16 MFMA peak
-  cpu_baseline the fp64 CPU oracle on the host cores (reported, not a target)
+  cpu_baseline the fp64 CPU oracle on the host cores (reported, not a target),
+               with a single-thread figure on a sample of heads beside it
+  small_model  the small-model config (B4 H8 T2048 d64, SiLU + L2 features),
+               mean launch time and its HBM / MFMA fractions
   parity       the timed run's outputs against that oracle run
   decode       256 back-to-back single-token steps of the decode workload
                (B=128, H=16, d=128), HBM bytes per step and tokens/s
@@ -27,7 +30,7 @@ JSON line on stdout:
                segment-parallel schedule, with the plain schedule beside it
 
 Options: --gpus N (only 1: this build targets one GPU), --steps K,
---warmup W, --no-cpu-baseline, --no-decode, --no-gated, --no-backward,
+--warmup W, --no-cpu-baseline, --no-decode, --no-small-model, --no-gated, --no-backward,
 --no-long-prefill (its segment passes launch the benchmark's kernel on
 other shapes; counter and trace runs of the benchmark line skip it),
 --copy-calib BYTES (also time a
@@ -55,6 +58,10 @@ KERNEL_SOURCES = ["deltanet_delta_rule_amd/csrc/chunk_fwd.hpp",
                   "deltanet_delta_rule_amd/csrc/chunk_fwd.hip",
                   "deltanet_delta_rule_amd/csrc/dr_common.hpp",
                   "deltanet_delta_rule_amd/build.py"]  # compile flags
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "recurrent_step_decode_traffic.txt")
+DECODE_SOURCES = ["deltanet_delta_rule_amd/csrc/recurrent_step.hip",
+                  "deltanet_delta_rule_amd/csrc/dr_common.hpp",
+                  "deltanet_delta_rule_amd/build.py"]
 
 
 def log(*a):
@@ -88,26 +95,26 @@ def decode_bytes(w):
     return bh * (8 * w.Dv * w.Dk + e * (2 * w.Dk + w.Dv + 1) + e * w.Dv + gate)
 
 
-def source_digest():
+def source_digest(sources=KERNEL_SOURCES):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch from the committed counter summary, or None when
+def measured_traffic(path=TRAFFIC_FILE, sources=KERNEL_SOURCES):
+    """HBM bytes per launch from a committed counter summary, or None when
     the kernel sources changed since the counters were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
     kv = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 key, val = line.split(":", 1)
                 kv[key.strip()] = val.strip()
-    if kv.get("kernel_source_sha256") != source_digest():
+    if kv.get("kernel_source_sha256") != source_digest(sources):
         return None
     try:
         return int(float(kv["hbm_bytes_per_launch"]))
@@ -121,6 +128,32 @@ def cpu_threads():
     except AttributeError:  # pragma: no cover
         n = os.cpu_count() or 1
     return max(1, min(16, n))
+
+
+def run_cpu_single_thread(x, w, heads=16):
+    """The fp64 oracle on one host thread over a bounded sample of the
+    workload: the first `heads` (batch, head) pairs at full length."""
+    import numpy as np
+
+    from oracle import delta_rule_ref
+    sel = [(b, h) for b in range(w.B) for h in range(w.H)][:heads]
+    pick = lambda t: np.stack([t[b, :, h].double().numpy() for b, h in sel], axis=1)[None]
+    q, k, v, beta = (pick(x[n]) for n in ("q", "k", "v", "beta"))
+    S0 = None if x["S0"] is None else np.stack([x["S0"][b, h].double().numpy()
+                                                for b, h in sel])[None]
+    t0 = time.perf_counter()
+    delta_rule_ref(q, k, v, beta, S0, nthreads=1)
+    dt = time.perf_counter() - t0
+    # tokens/s of the whole workload at this rate: every (batch, head) pair
+    # costs the same, and a token is all H heads of one batch row
+    return {
+        "value": len(sel) * w.T / w.H / dt,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{len(sel)} of the {w.B * w.H} heads of {w.name}, full T = {w.T}, "
+                  f"{dt:.2f} s, scaled to tokens of all {w.H} heads",
+    }
 
 
 def run_cpu_baseline(x, w, o_gpu, st_gpu):
@@ -154,8 +187,8 @@ def run_cpu_baseline(x, w, o_gpu, st_gpu):
     return base, par
 
 
-def bench_decode(torch, dr, W, reps=3, name="decode"):
-    w = W.get(name)
+def bench_decode(torch, dr, W, reps=3, name="decode", **over):
+    w = W.get(name, **over)
     x = W.generate(w)
     dev = torch.device("cuda:0")
     d = {n: (None if t is None else t.to(dev)) for n, t in x.items()}
@@ -189,7 +222,7 @@ def bench_decode(torch, dr, W, reps=3, name="decode"):
     t = sorted(times)[len(times) // 2]
     per_step = t / w.T
     gbs = decode_bytes(w) / per_step / 1e9
-    return {
+    res = {
         "workload": (f"{w.name} B{w.B} H{w.H} d{w.Dk}, {w.T} steps, bf16 in, fp32 state"
                      + ("" if w.gate_amax <= 0 else
                         ", per-channel log decay fp32" if w.kda else ", log gates fp32")),
@@ -197,7 +230,12 @@ def bench_decode(torch, dr, W, reps=3, name="decode"):
         "us_per_step": per_step * 1e6,
         "hbm_gbs_algorithmic": gbs,
         "hbm_frac": gbs / HBM_PEAK_GBS,
+        "algorithmic_bytes_per_step": decode_bytes(w),
     }
+    traffic = measured_traffic(DECODE_TRAFFIC_FILE, DECODE_SOURCES)
+    if name == "decode" and not over and traffic is not None:
+        res["traffic"] = traffic
+    return res
 
 
 def bench_gated_chunk(torch, dr, W, reps=20, name="gated_layer_1p3b", l2=False):
@@ -232,14 +270,17 @@ def bench_gated_chunk(torch, dr, W, reps=20, name="gated_layer_1p3b", l2=False):
     torch.cuda.synchronize()
     launch_s = sum(a.elapsed_time(b) for a, b in ev) / reps / 1e3
     flops, nbytes = chunk_work(w)
+    what = ("raw q, k normalised in the kernel, fp32 state" if l2 else
+            "fp32 log gates and state" if d["g"] is not None else
+            f"{w.feature} features, fp32 state")
     return {
-        "workload": (f"{w.name} B{w.B} H{w.H} T{w.T} d{w.Dk} chunk {w.chunk}, bf16 in, "
-                     + ("raw q, k normalised in the kernel, fp32 state" if l2 else
-                        "fp32 log gates and state")),
+        "workload": f"{w.name} B{w.B} H{w.H} T{w.T} d{w.Dk} chunk {w.chunk}, {w.dtype} in, {what}",
         "tokens_per_s": w.B * w.T / launch_s,
         "mean_launch_us": round(launch_s * 1e6, 2),
         "hbm_frac": round(nbytes / launch_s / 1e9 / HBM_PEAK_GBS, 4),
         "mfma_frac": round(flops / launch_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "algorithmic_bytes_per_launch": nbytes,
+        "algorithmic_flops_per_launch": flops,
     }
 
 
@@ -369,6 +410,11 @@ def main():
     ap.add_argument("--workload", default="layer_1p3b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-beyond-cache", action="store_true",
+                    help="skip the decode run with a state larger than the Infinity Cache "
+                         "(it launches the decode kernel on another shape)")
+    ap.add_argument("--no-small-model", action="store_true",
+                    help="skip the small-model (B4 H8 T2048 d64) line")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward line")
     ap.add_argument("--no-long-prefill", action="store_true",
@@ -466,9 +512,20 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roof,
     }
+    if not args.no_small_model:
+        log("small model: B4 H8 T2048 d64 chunked forward")
+        out["small_model"] = bench_gated_chunk(torch, dr, W, name="small_model")
+        out["small_model"]["kernel"] = ("chunk_fwd_ws_kernel<bf16, Dk=64, C=64, NW=4> "
+                                        "(4 state + 4 preparation waves)")
     if not args.no_decode:
         log("decode: 256 steps of B128 H16 d128")
         out["decode"] = bench_decode(torch, dr, W)
+        # the 128 MiB state of the decode config fits the 256 MB Infinity
+        # Cache; with 512 sequences (512 MiB) it cannot, so this rate is
+        # bounded by DRAM
+        if not args.no_beyond_cache:
+            log("decode beyond the Infinity Cache: 64 steps of B512 H16 d128")
+            out["decode"]["beyond_infinity_cache"] = bench_decode(torch, dr, W, B=512, T=64)
     if not args.no_gated:
         log("gated rule: layer shape chunked forward, then 256 decode steps")
         out["gated"] = {"chunk": bench_gated_chunk(torch, dr, W)}
@@ -490,9 +547,10 @@ def main():
         out["backward"]["vs_forward_launch"] = round(
             out["backward"]["mean_call_us"] / roof["mean_launch_us"], 2)
     if not args.no_cpu_baseline:
-        log("cpu baseline: fp64 oracle on the whole workload")
+        log("cpu baseline: fp64 oracle on the whole workload, then on one thread")
         torch.cuda.synchronize()
         out["cpu_baseline"], out["parity"] = run_cpu_baseline(x, w, o.cpu(), st.cpu())
+        out["cpu_baseline"]["single_thread"] = run_cpu_single_thread(x, w)
     print(json.dumps(out), flush=True)
 
 
