@@ -6,12 +6,29 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "dr_launch.hpp"
 
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+// A C caller may pass any int where the header says dr_dtype or dr_status.
+// Loading such a value as a C++ enum outside its enumerators' range is
+// undefined, so the entry points read the raw integer and check it before the
+// value is used as an enum.
+template <typename E>
+int raw_enum(const E &e) {
+    static_assert(sizeof(E) == sizeof(int), "the ABI's enums are int-sized");
+    int v;
+    memcpy(&v, &e, sizeof v);
+    return v;
+}
+bool valid_dtype(const dr_dtype &d) {
+    const int v = raw_enum(d);
+    return v == DR_F32 || v == DR_BF16;
+}
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned_to(const void *p, int64_t n) {
@@ -239,13 +256,14 @@ dr_status delta_rule_chunk_fwd(const void *q, const void *k, const void *v,
                                float *S_T, int64_t B, int64_t T, int64_t H,
                                int64_t Dk, int64_t Dv, int64_t chunk,
                                dr_dtype dtype, void *stream) {
+    if (!valid_dtype(dtype)) return DR_ERR_INVALID_ARG;
     return chunk_fwd(q, k, v, beta, nullptr, false, S0, o, S_T, B, T, H, Dk, Dv, chunk, nullptr,
                      0, 1.f, false, dtype, stream);
 }
 
 int64_t delta_rule_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk,
                                              int64_t Dv, int64_t chunk, dr_dtype dtype) {
-    if (dtype != DR_F32 && dtype != DR_BF16) return -1;
+    if (!valid_dtype(dtype)) return -1;
     if (B < 0 || T < 0 || H < 0 || !supported_dim(Dk) || !supported_dim(Dv) ||
         !supported_chunk(chunk))
         return -1;
@@ -257,6 +275,7 @@ dr_status delta_rule_chunk_fwd_ex(const void *q, const void *k, const void *v,
                                   int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
                                   int64_t chunk, const dr_chunk_opts *opts, dr_dtype dtype,
                                   void *stream) {
+    if (!valid_dtype(dtype)) return DR_ERR_INVALID_ARG;
     dr_chunk_opts d{};
     d.scale = 1.f;
     const dr_chunk_opts &x = opts ? *opts : d;
@@ -273,6 +292,7 @@ dr_status delta_rule_chunk_fwd_noalloc(const void *q, const void *k, const void 
                                        int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
                                        int64_t chunk, const dr_chunk_opts *opts, dr_dtype dtype,
                                        void *stream) {
+    if (!valid_dtype(dtype)) return DR_ERR_INVALID_ARG;
     dr_chunk_opts d{};
     d.scale = 1.f;
     const dr_chunk_opts &x = opts ? *opts : d;
@@ -288,6 +308,7 @@ dr_status delta_rule_recurrent_step(const void *q, const void *k,
                                     const void *v, const void *beta, float *S,
                                     void *o, int64_t B, int64_t H, int64_t Dk,
                                     int64_t Dv, dr_dtype dtype, void *stream) {
+    if (!valid_dtype(dtype)) return DR_ERR_INVALID_ARG;
     return recurrent_step(q, k, v, beta, nullptr, false, S, o, B, H, Dk, Dv, 1.f, false, dtype,
                           stream);
 }
@@ -297,6 +318,7 @@ dr_status gated_delta_rule_chunk_fwd(const void *q, const void *k, const void *v
                                      void *o, float *S_T, int64_t B, int64_t T, int64_t H,
                                      int64_t Dk, int64_t Dv, int64_t chunk, dr_dtype dtype,
                                      void *stream) {
+    if (!valid_dtype(dtype)) return DR_ERR_INVALID_ARG;
     return chunk_fwd(q, k, v, beta, g, true, S0, o, S_T, B, T, H, Dk, Dv, chunk, nullptr, 0, 1.f,
                      false, dtype, stream);
 }
@@ -305,6 +327,7 @@ dr_status gated_delta_rule_recurrent_step(const void *q, const void *k, const vo
                                           const void *beta, const float *g, float *S, void *o,
                                           int64_t B, int64_t H, int64_t Dk, int64_t Dv,
                                           dr_dtype dtype, void *stream) {
+    if (!valid_dtype(dtype)) return DR_ERR_INVALID_ARG;
     return recurrent_step(q, k, v, beta, g, true, S, o, B, H, Dk, Dv, 1.f, false, dtype, stream);
 }
 
@@ -312,6 +335,7 @@ dr_status delta_rule_recurrent_step_ex(const void *q, const void *k, const void 
                                        const void *beta, float *S, void *o, int64_t B,
                                        int64_t H, int64_t Dk, int64_t Dv,
                                        const dr_step_opts *opts, dr_dtype dtype, void *stream) {
+    if (!valid_dtype(dtype)) return DR_ERR_INVALID_ARG;
     dr_step_opts d{};
     d.scale = 1.f;
     const dr_step_opts &x = opts ? *opts : d;
@@ -322,6 +346,7 @@ dr_status delta_rule_recurrent_step_ex(const void *q, const void *k, const void 
 
 size_t delta_rule_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk,
                                             int64_t Dv, dr_dtype dtype) {
+    if (!valid_dtype(dtype)) return 0;
     if (B < 0 || T < 0 || H < 0 || !supported_dim(Dk) || !supported_dim(Dv) ||
         (dtype != DR_F32 && dtype != DR_BF16))
         return 0;
@@ -334,12 +359,13 @@ dr_status delta_rule_chunk_bwd(const void *q, const void *k, const void *v, cons
                                void *dk, void *dv, void *dbeta, float *dS0, void *workspace,
                                size_t workspace_bytes, int64_t B, int64_t T, int64_t H,
                                int64_t Dk, int64_t Dv, dr_dtype dtype, void *stream) {
+    if (!valid_dtype(dtype)) return DR_ERR_INVALID_ARG;
     return chunk_bwd(q, k, v, beta, S0, dout, dS_T, dq, dk, dv, dbeta, dS0, workspace,
                      workspace_bytes, B, T, H, Dk, Dv, dtype, stream);
 }
 
 const char *delta_rule_status_string(dr_status status) {
-    switch (status) {
+    switch (raw_enum(status)) {
     case DR_OK: return "DR_OK";
     case DR_ERR_INVALID_ARG: return "DR_ERR_INVALID_ARG: invalid argument";
     case DR_ERR_UNSUPPORTED: return "DR_ERR_UNSUPPORTED: unsupported size or shape";

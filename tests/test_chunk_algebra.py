@@ -10,6 +10,10 @@ any kernel exists.
   la dependance causale") give the same per-token errors: E = U - W S^T.
 * P10: the WY representation (paperlayer summary, section 3) -- the product of
   a chunk's generalized Householder transitions equals I - W^T K.
+* The level split of the chunked KDA kernel (each pair's decay as a row
+  factor times a column factor around the pair's level reference) gives the
+  decay of the tokens between the two, D_{j+1:i} of the hada.io digest's
+  "Chunkwise KDA", for strong decays, erased channels and gk = -inf.
 """
 from __future__ import annotations
 
@@ -83,3 +87,60 @@ def test_chunk_state_is_affine_in_incoming_state():
     _, W, U = ut_transform(K, V, b)
     expect = S @ (np.eye(K.shape[1]) - W.T @ K) + U.T @ K
     assert _rel(S_next, expect) < 1e-12
+
+
+def _level_decays(gk, C):
+    """The decay between every pair of tokens (i, j), j <= i, of a chunk as the
+    chunked KDA kernel forms it: pair (i, j), i > j, belongs to the level of
+    the highest bit in which i and j differ; the reference is the last token
+    of the first half of that level's aligned segment; the row factor is the
+    product of exp(gk) over ref+1 .. i and the column factor over j+1 .. ref.
+    Returns [i, j, d] (zero above the diagonal, one on it)."""
+    e = np.exp(gk)                      # per-token factors, [C, d]
+    out = np.zeros((C, C, gk.shape[1]))
+    for i in range(C):
+        out[i, i] = 1.0
+        for j in range(i):
+            L = 1 << ((i ^ j).bit_length() - 1)
+            ref = (i // (2 * L)) * 2 * L + L - 1
+            row = np.prod(e[ref + 1:i + 1], axis=0)
+            col = np.prod(e[j + 1:ref + 1], axis=0)
+            out[i, j] = row * col
+    return out
+
+
+@pytest.mark.parametrize("case", ["amax16", "erased", "minus_inf", "weak"])
+def test_kda_level_factors_give_the_pairwise_decays(case):
+    # hada.io digest, "Chunkwise KDA": the chunk's couplings and reads carry
+    # D_{j+1:i} = diag(exp(b_i - b_j)) with b the in-chunk prefix sums of gk.
+    # The kernel's level split must give exactly those ratios for any gk <= 0,
+    # including channels erased in one token ("Kimi Delta Attention").
+    r = np.random.default_rng(120)
+    C, d = 32, 8
+    if case == "amax16":
+        gk = -16.0 * r.uniform(size=(1, d)) * np.log1p(np.exp(r.standard_normal((C, d)) + 1))
+    elif case == "erased":
+        gk = np.zeros((C, d))
+        gk[:, d // 2:] = -1e4
+    elif case == "minus_inf":
+        gk = -r.uniform(0, 3, (C, d))
+        gk[::3, 1::2] = -np.inf
+    else:
+        gk = -0.02 * r.uniform(size=(C, d))
+    got = _level_decays(gk, C)
+    # D_{j+1:i}: the decay of tokens j+1 .. i, one product per pair
+    want = np.zeros_like(got)
+    for i in range(C):
+        for j in range(i + 1):
+            want[i, j] = np.prod(np.exp(gk[j + 1:i + 1]), axis=0)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-300)
+    # where the prefix sums are finite, exp(b_i - b_j) is the same ratio
+    if np.all(np.isfinite(gk)):
+        b = np.cumsum(gk, axis=0)
+        with np.errstate(over="ignore"):  # above the diagonal: never used
+            ratio = np.exp(b[:, None, :] - b[None, :, :])
+        mask = np.tril(np.ones((C, C)))[:, :, None] > 0
+        np.testing.assert_allclose(np.where(mask, got, 0), np.where(mask, ratio, 0),
+                                   rtol=1e-9, atol=1e-300)
+    # every factor the kernel multiplies by is at most 1
+    assert np.all(got <= 1.0 + 1e-15)

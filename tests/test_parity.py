@@ -86,9 +86,13 @@ def test_chunk_many_heads_fill_grid():
     _chunk_check(W.get("layer_1p3b", B=8, H=16, T=70), heads=[(0, 0), (3, 7), (7, 15)])
 
 
-def test_chunk_two_wave_launch():
-    # B*H*Dv/32 >= 256 > B*H*Dv/64: the 2-wave launch
-    _chunk_check(W.get("layer_1p3b", B=4, H=16, T=90), heads=[(0, 1), (2, 9), (3, 15)])
+@pytest.mark.parametrize("Dv, waves", [(32, 2), (16, 1)])
+def test_chunk_two_and_one_wave_launches(Dv, waves):
+    # the launch takes 4 state waves (64 value rows) when Dv allows it, else
+    # 2 (Dv = 32) or 1 (Dv = 16): the narrower launches at d_k = 128 with
+    # many heads
+    _chunk_check(W.get("layer_1p3b", B=4, H=16, T=90, Dv=Dv, seed=2100 + waves),
+                 heads=[(0, 1), (2, 9), (3, 15)])
 
 
 # full sizes, exactly the launches the benchmark times (sampled heads)
