@@ -402,6 +402,43 @@ def bench_backward(torch, dr, W, reps=10):
     }
 
 
+def sweep_schedules(torch, dr, W):
+    """Chunked vs token-serial forward over sequence length and head dimension
+    (plain rule, bf16, H = 16, B = max(1, 16384 / T) sequences, chunk 64, no
+    segment schedule): one JSON line per shape with the median call time of
+    each schedule (HIP events on the launch stream) and their ratio."""
+    for d in (64, 128):
+        for T in (16, 64, 256, 1024, 4096, 16384, 32768):
+            B = max(1, 16384 // T)
+            w = W.get("layer_1p3b", B=B, T=T, Dk=d, Dv=d, seed=31000 + T + d)
+            x = W.generate(w)
+            dd = {n: (None if t is None else t.cuda()) for n, t in x.items()}
+            o = torch.empty((w.B, w.T, w.H, w.Dv), dtype=w.torch_dtype, device="cuda")
+            st = torch.empty((w.B, w.H, w.Dv, w.Dk), dtype=torch.float32, device="cuda")
+            res = {}
+            for serial in (False, True):
+                def step():
+                    dr.delta_rule_chunk_fwd(dd["q"], dd["k"], dd["v"], dd["beta"], None,
+                                            chunk=64, o=o, S_T=st, fused_recurrent=serial,
+                                            workspace=False)
+                for _ in range(2):
+                    step()
+                torch.cuda.synchronize()
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(10)]
+                for a, b in ev:
+                    a.record()
+                    step()
+                    b.record()
+                torch.cuda.synchronize()
+                ts = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+                res["serial" if serial else "chunked"] = ts[len(ts) // 2]
+            print(json.dumps({"d": d, "T": T, "B": B, "H": w.H,
+                              "chunked_us": round(res["chunked"], 1),
+                              "serial_us": round(res["serial"], 1),
+                              "speedup": round(res["serial"] / res["chunked"], 2)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -421,6 +458,8 @@ def main():
                     help="skip the long-prefill line")
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the gated-rule lines (chunked layer shape and decode)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only print the chunked vs token-serial sweep over T and d")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="also run a device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -439,6 +478,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.sweep:
+        sweep_schedules(torch, dr, W)
+        return
     dev = torch.device("cuda:0")
     w = W.get(args.workload)
     log(f"generating {w.name}: B{w.B} H{w.H} T{w.T} Dk{w.Dk} Dv{w.Dv} C{w.chunk} {w.dtype}")
