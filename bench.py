@@ -24,7 +24,8 @@ JSON line on stdout:
                (chunked forward) and on the decode workload
   qk_l2norm    the layer shape with raw q, k normalised inside the kernel
   backward     delta_rule_chunk_bwd on the layer shape (checkpointing forward
-               and reverse pass), time per call and ratio to the forward launch
+               and reverse pass), time per call and ratio to the forward launch;
+               with "gated" inside it, gated_delta_rule_chunk_bwd likewise
   kda          per-key-channel decay: decode steps and the chunked forward
   long_prefill the long-prefill config (B1 H16 T32768) through the
                segment-parallel schedule, with the plain schedule beside it
@@ -360,11 +361,12 @@ def bench_long_prefill(torch, dr, W, reps=5):
     }
 
 
-def bench_backward(torch, dr, W, reps=10):
-    """delta_rule_chunk_bwd on the layer shape: the checkpointing forward pass
-    plus the reverse pass, with upstream gradients for o and S_T (mean time per
-    call with HIP events on the launch stream)."""
-    w = W.get("layer_1p3b")
+def bench_backward(torch, dr, W, reps=10, name="layer_1p3b"):
+    """delta_rule_chunk_bwd (gated_delta_rule_chunk_bwd for a gated workload)
+    on the layer shape: the checkpointing forward pass plus the reverse pass,
+    with upstream gradients for o and S_T (mean time per call with HIP events
+    on the launch stream)."""
+    w = W.get(name)
     x = W.generate(w)
     dev = torch.device("cuda:0")
     d = {n: (None if t is None else t.to(dev)) for n, t in x.items()}
@@ -378,8 +380,12 @@ def bench_backward(torch, dr, W, reps=10):
                      dtype=torch.uint8, device=dev)
 
     def step():
-        dr.delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], do, d["S0"], dst,
-                                workspace=ws)
+        if d.get("g") is None:
+            dr.delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], do, d["S0"], dst,
+                                    workspace=ws)
+        else:
+            dr.gated_delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], do,
+                                          d["S0"], dst, workspace=ws)
 
     for _ in range(2):
         step()
@@ -588,6 +594,9 @@ def main():
         out["backward"] = bench_backward(torch, dr, W)
         out["backward"]["vs_forward_launch"] = round(
             out["backward"]["mean_call_us"] / roof["mean_launch_us"], 2)
+        if not args.no_gated:
+            log("backward: gated rule, layer shape")
+            out["backward"]["gated"] = bench_backward(torch, dr, W, name="gated_layer_1p3b")
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle on the whole workload, then on one thread")
         torch.cuda.synchronize()

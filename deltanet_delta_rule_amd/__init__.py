@@ -31,6 +31,7 @@ __all__ = [
     "gated_delta_rule_chunk_fwd",
     "gated_delta_rule_recurrent_step",
     "delta_rule_chunk_bwd",
+    "gated_delta_rule_chunk_bwd",
     "delta_rule_chunk_fwd_noalloc",
     "DeltaRuleScratchError",
     "kda_recurrent_step",
@@ -118,6 +119,9 @@ def load_library():
     lib.delta_rule_chunk_bwd.restype = i32
     lib.delta_rule_chunk_bwd.argtypes = [vp] * 13 + [ctypes.c_size_t, i64, i64, i64, i64, i64,
                                                      i32, vp]
+    lib.gated_delta_rule_chunk_bwd.restype = i32
+    lib.gated_delta_rule_chunk_bwd.argtypes = [vp] * 15 + [ctypes.c_size_t, i64, i64, i64, i64,
+                                                           i64, i32, vp]
     lib.delta_rule_status_string.restype = ctypes.c_char_p
     lib.delta_rule_status_string.argtypes = [i32]
     lib.delta_rule_last_hip_error.restype = i32
@@ -420,6 +424,20 @@ def delta_rule_chunk_bwd(q, k, v, beta, do, S0=None, dS_T=None, *, workspace=Non
     dS0 (float32, or None when ``need_dS0`` is False).  ``workspace`` (a
     uint8 GPU tensor of at least ``delta_rule_chunk_bwd_workspace_bytes``
     bytes) holds the forward checkpoints; it is allocated when not given."""
+    return _bwd_call(q, k, v, beta, None, do, S0, dS_T, workspace, need_dS0, stream)
+
+
+def gated_delta_rule_chunk_bwd(q, k, v, beta, g, do, S0=None, dS_T=None, *, workspace=None,
+                               need_dS0=True, stream=None):
+    """Gradients of ``gated_delta_rule_chunk_fwd``: as ``delta_rule_chunk_bwd``
+    with g ``[B,T,H]`` float32 (the log forget gate) among the inputs; the
+    dict also holds dg (float32 ``[B,T,H]``)."""
+    if g is None:
+        raise ValueError("the gated backward needs g")
+    return _bwd_call(q, k, v, beta, g, do, S0, dS_T, workspace, need_dS0, stream)
+
+
+def _bwd_call(q, k, v, beta, g, do, S0, dS_T, workspace, need_dS0, stream):
     torch = _torch()
     dev = q.device
     if dev.type != "cuda":
@@ -437,6 +455,8 @@ def delta_rule_chunk_bwd(q, k, v, beta, do, S0=None, dS_T=None, *, workspace=Non
         _need(S0, "S0", (B, H, Dv, Dk), torch.float32, dev)
     if dS_T is not None:
         _need(dS_T, "dS_T", (B, H, Dv, Dk), torch.float32, dev)
+    if g is not None:
+        _need(g, "g", (B, T, H), torch.float32, dev)
     lib = load_library()
     nbytes = int(lib.delta_rule_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, code))
     if workspace is None:
@@ -447,11 +467,19 @@ def delta_rule_chunk_bwd(q, k, v, beta, do, S0=None, dS_T=None, *, workspace=Non
            "dbeta": torch.empty_like(beta),
            "dS0": torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
            if need_dS0 else None}
-    st = lib.delta_rule_chunk_bwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(do), _ptr(dS_T),
-        _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
-        _ptr(out["dS0"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        B, T, H, Dk, Dv, code, _stream(dev, stream))
+    nws = workspace.numel() * workspace.element_size()
+    if g is None:
+        st = lib.delta_rule_chunk_bwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(do), _ptr(dS_T),
+            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
+            _ptr(out["dS0"]), _ptr(workspace), nws, B, T, H, Dk, Dv, code, _stream(dev, stream))
+    else:
+        out["dg"] = torch.empty_like(g)
+        st = lib.gated_delta_rule_chunk_bwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(do), _ptr(dS_T),
+            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
+            _ptr(out["dg"]), _ptr(out["dS0"]), _ptr(workspace), nws, B, T, H, Dk, Dv, code,
+            _stream(dev, stream))
     _check(st)
     return out
 

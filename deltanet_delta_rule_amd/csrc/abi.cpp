@@ -195,9 +195,10 @@ int64_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t
 }
 
 dr_status chunk_bwd(const void *q, const void *k, const void *v, const void *beta,
-                    const float *S0, const void *dout, const float *dS_T, void *dq, void *dk,
-                    void *dv, void *dbeta, float *dS0, void *ws, size_t ws_bytes, int64_t B,
-                    int64_t T, int64_t H, int64_t Dk, int64_t Dv, dr_dtype dtype, void *stream) {
+                    const float *g, const float *S0, const void *dout, const float *dS_T,
+                    void *dq, void *dk, void *dv, void *dbeta, float *dg, float *dS0, void *ws,
+                    size_t ws_bytes, int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                    bool gated, dr_dtype dtype, void *stream) {
     if (dtype != DR_F32 && dtype != DR_BF16) return DR_ERR_INVALID_ARG;
     if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0) return DR_ERR_INVALID_ARG;
     if (!supported_dim(Dk) || !supported_dim(Dv)) return DR_ERR_UNSUPPORTED;
@@ -213,6 +214,8 @@ dr_status chunk_bwd(const void *q, const void *k, const void *v, const void *bet
     if (span < 0 || span > INT32_MAX / 2) return DR_ERR_UNSUPPORTED;
     if (T > 0 && (!q || !k || !v || !beta || !dout || !dq || !dk || !dv || !dbeta))
         return DR_ERR_INVALID_ARG;
+    if (gated && T > 0 && (!g || !dg)) return DR_ERR_INVALID_ARG;
+    if (!gated) g = dg = nullptr;
     if (T > 0 && (!ws || (int64_t)ws_bytes < need)) return DR_ERR_INVALID_ARG;
     const void *vec_ptrs[] = {q, k, S0, dS_T, dS0, ws};
     for (const void *p : vec_ptrs)
@@ -220,12 +223,14 @@ dr_status chunk_bwd(const void *q, const void *k, const void *v, const void *bet
     const void *elem_ptrs[] = {v, beta, dout, dq, dk, dv, dbeta};
     for (const void *p : elem_ptrs)
         if (p && !aligned_to(p, esz)) return DR_ERR_INVALID_ARG;
+    if ((g && !aligned_to(g, 4)) || (dg && !aligned_to(dg, 4))) return DR_ERR_INVALID_ARG;
     // outputs must not overlap any input or each other
     const Span in[] = {{q, nqk * esz},  {k, nqk * esz},   {v, nv * esz},
                        {beta, nb * esz}, {S0, ns * 4},    {dout, nv * esz},
-                       {dS_T, ns * 4}};
-    const Span out[] = {{dq, nqk * esz}, {dk, nqk * esz}, {dv, nv * esz},
-                        {dbeta, nb * esz}, {dS0, ns * 4}, {ws, need}};
+                       {dS_T, ns * 4},   {g, nb * 4}};
+    const Span out[] = {{dq, nqk * esz},   {dk, nqk * esz}, {dv, nv * esz},
+                        {dbeta, nb * esz}, {dS0, ns * 4},   {ws, need},
+                        {dg, nb * 4}};
     for (const Span &o : out) {
         for (const Span &s : in)
             if (overlaps(o, s)) return DR_ERR_INVALID_ARG;
@@ -235,15 +240,15 @@ dr_status chunk_bwd(const void *q, const void *k, const void *v, const void *bet
     const hipStream_t st = static_cast<hipStream_t>(stream);
     void *h = ws;
     if (T > 0) {
-        const dr::ChunkFwdArgs f{q,      k,       v,        beta,     nullptr, S0,
+        const dr::ChunkFwdArgs f{q,      k,       v,        beta,     g,       S0,
                                  nullptr, nullptr, h,        nullptr,  B,       T,
                                  H,      (int)Dk, (int)Dv,  dr::chunk_bwd_chunk(bf16),
                                  1.f,    false};
         const hipError_t e = dr::launch_chunk_fwd(f, bf16, st);
         if (e != hipSuccess) return hip_status(e);
     }
-    const dr::ChunkBwdArgs a{q,  k,  v,  beta, dout, dS_T, h,       dq,      dk,
-                             dv, dbeta, dS0, B, T,    H,    (int)Dk, (int)Dv};
+    const dr::ChunkBwdArgs a{q,  k,     v,   beta, dout, dS_T, h,       dq,      dk,
+                             dv, dbeta, dS0, B,    T,    H,    (int)Dk, (int)Dv, g, dg};
     return hip_status(dr::launch_chunk_bwd(a, bf16, st));
 }
 
@@ -360,8 +365,20 @@ dr_status delta_rule_chunk_bwd(const void *q, const void *k, const void *v, cons
                                size_t workspace_bytes, int64_t B, int64_t T, int64_t H,
                                int64_t Dk, int64_t Dv, dr_dtype dtype, void *stream) {
     if (!valid_dtype(dtype)) return DR_ERR_INVALID_ARG;
-    return chunk_bwd(q, k, v, beta, S0, dout, dS_T, dq, dk, dv, dbeta, dS0, workspace,
-                     workspace_bytes, B, T, H, Dk, Dv, dtype, stream);
+    return chunk_bwd(q, k, v, beta, nullptr, S0, dout, dS_T, dq, dk, dv, dbeta, nullptr, dS0,
+                     workspace, workspace_bytes, B, T, H, Dk, Dv, false, dtype, stream);
+}
+
+dr_status gated_delta_rule_chunk_bwd(const void *q, const void *k, const void *v,
+                                     const void *beta, const float *g, const float *S0,
+                                     const void *dout, const float *dS_T, void *dq, void *dk,
+                                     void *dv, void *dbeta, float *dg, float *dS0,
+                                     void *workspace, size_t workspace_bytes, int64_t B,
+                                     int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                     dr_dtype dtype, void *stream) {
+    if (!valid_dtype(dtype)) return DR_ERR_INVALID_ARG;
+    return chunk_bwd(q, k, v, beta, g, S0, dout, dS_T, dq, dk, dv, dbeta, dg, dS0, workspace,
+                     workspace_bytes, B, T, H, Dk, Dv, true, dtype, stream);
 }
 
 const char *delta_rule_status_string(dr_status status) {
@@ -379,6 +396,6 @@ const char *delta_rule_status_string(dr_status status) {
 
 int delta_rule_last_hip_error(void) { return g_last_hip_error; }
 
-int delta_rule_version(void) { return 20800; }
+int delta_rule_version(void) { return 20900; }
 
 }  // extern "C"

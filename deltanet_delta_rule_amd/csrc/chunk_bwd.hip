@@ -66,7 +66,22 @@ struct BwdCfg {
     static constexpr bool DBUF = BASE + (int)sizeof(DT) * DK * LDS_ + 256 <= 160 * 1024;
 };
 
-template <typename DT, int DK, int DV, int C>
+// Gated rule: the chunk's decays and the parts of dL/db, b the in-chunk
+// prefix sums of the log gate (nothing for the plain rule).  The parts are
+// summed into dg at the start of the next chunk (after the loop for the
+// first), so they are only read behind a barrier.
+template <int C, int NW, int NJ, int KT, bool GATED>
+struct BwdGate {
+    float gb[C], gam[C], rto[C];      // b, exp(b), exp(b_last - b)
+    float pdb[KT][C];                 // gamma_t dL/dgamma_t - rho_t dL/drho_t, per key tile
+    float prd[KT][C];                 // rho_t dL/drho_t, per key tile
+    float dgc[NW][4];                 // gamma_last dL/dgamma_last, per wave and row group
+    float wrow[2 * NJ][16], wcol[2 * NJ][16];  // row / column sums of W per C x C tile job
+};
+template <int C, int NW, int NJ, int KT>
+struct BwdGate<C, NW, NJ, KT, false> {};
+
+template <typename DT, int DK, int DV, int C, bool GATED>
 struct BwdSmem {
     typedef BwdCfg<DT, DK, DV, C> G;
     DT Ks[C * G::LDK], Qs[C * G::LDK];
@@ -82,11 +97,12 @@ struct BwdSmem {
     DT Gs[C * G::LDC];                            // dG + dG^T
     float betas[C];
     float dbp[G::NW][C];                          // per-wave parts of dbeta
+    BwdGate<C, G::NW, G::NT * (G::NT + 1) / 2, G::KT, GATED> gt;
 };
 
-template <typename DT, int DK, int DV, int C>
+template <typename DT, int DK, int DV, int C, bool GATED>
 constexpr bool bwd_fits() {
-    return sizeof(BwdSmem<DT, DK, DV, C>) <= 160 * 1024;
+    return sizeof(BwdSmem<DT, DK, DV, C, GATED>) <= 160 * 1024;
 }
 
 // Four consecutive elements of DT to global memory through a buffer resource
@@ -185,6 +201,14 @@ __device__ __forceinline__ void put_tile(DT *M, int ld, int m0, int n0, const f3
     }
 }
 
+// Sum over the 64 lanes of the wave, every lane receiving it.
+__device__ __forceinline__ float wave_sum(float x) {
+    x = group_sum<16>(x);
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
 // Product X Y of two 16x16 matrices held in D layout, given X^T in D layout
 // (the A operand) and Y (the B operand).
 template <typename DT>
@@ -265,14 +289,16 @@ struct ChunkPrefetch {
     RowPrefetch<DT, C, DK, NTHR> k, q;
     RowPrefetch<DT, C, DV, NTHR> v, o;
     RowPrefetch<DT, DV, DK, NTHR> s;
-    DT b;   // beta of token tid (zero past the chunk's valid length)
+    DT b;      // beta of token tid (zero past the chunk's valid length)
+    float gv;  // log gate of token tid (gated rule; zero past the valid length)
     // Part 0: S_c; part 1: K and Q; part 2: V, dO and beta (issued at three
     // points of a chunk, so that no single point floods the vector memory
     // path).
     template <int P>
     __device__ __forceinline__ void load_part(const DT *kk, const DT *qq, const DT *vv,
-                                              const DT *oo, const DT *bb, const DT *sc,
-                                              int64_t tok0, int h, int H, int len, int tid) {
+                                              const DT *oo, const DT *bb, const float *gg,
+                                              const DT *sc, int64_t tok0, int h, int H,
+                                              int len, int tid) {
         const int64_t rk = (int64_t)H * DK, rv = (int64_t)H * DV;
         if constexpr (P == 0) s.load(sc, DK, DV, tid);
         if constexpr (P == 1) {
@@ -286,14 +312,18 @@ struct ChunkPrefetch {
             // waits for this load before the chunk's LDS stores
             const auto rb = make_rsrc(bb + tok0 * H + h, len > 0 ? ((len - 1) * H + 1) * (int)sizeof(DT) : 0);
             b = buf_load_elem<DT>(rb, tid < len ? tid * H * (int)sizeof(DT) : 0x7ffffff0);
+            if (gg && tid < 64) {
+                const auto rg = make_rsrc(gg + tok0 * H + h, len > 0 ? ((len - 1) * H + 1) * 4 : 0);
+                gv = buf_load_elem<float>(rg, tid < len ? tid * H * 4 : 0x7ffffff0);
+            }
         }
     }
     __device__ __forceinline__ void load(const DT *kk, const DT *qq, const DT *vv, const DT *oo,
-                                         const DT *bb, const DT *sc, int64_t tok0, int h, int H,
-                                         int len, int tid) {
-        load_part<0>(kk, qq, vv, oo, bb, sc, tok0, h, H, len, tid);
-        load_part<1>(kk, qq, vv, oo, bb, sc, tok0, h, H, len, tid);
-        load_part<2>(kk, qq, vv, oo, bb, sc, tok0, h, H, len, tid);
+                                         const DT *bb, const float *gg, const DT *sc,
+                                         int64_t tok0, int h, int H, int len, int tid) {
+        load_part<0>(kk, qq, vv, oo, bb, gg, sc, tok0, h, H, len, tid);
+        load_part<1>(kk, qq, vv, oo, bb, gg, sc, tok0, h, H, len, tid);
+        load_part<2>(kk, qq, vv, oo, bb, gg, sc, tok0, h, H, len, tid);
     }
 };
 
@@ -320,16 +350,17 @@ __device__ __forceinline__ void store_rows(DT *dst, int64_t gs, int nvalid, cons
     }
 }
 
-template <typename DT, int DK, int DV, int C>
+template <typename DT, int DK, int DV, int C, bool GATED>
 __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
-    const DT *__restrict__ beta, const DT *__restrict__ dout, const float *__restrict__ dST,
-    const DT *__restrict__ hs, DT *__restrict__ dq, DT *__restrict__ dk, DT *__restrict__ dv,
-    DT *__restrict__ dbeta, float *__restrict__ dS0, int T, int H) {
+    const DT *__restrict__ beta, const float *__restrict__ gl, const DT *__restrict__ dout,
+    const float *__restrict__ dST, const DT *__restrict__ hs, DT *__restrict__ dq,
+    DT *__restrict__ dk, DT *__restrict__ dv, DT *__restrict__ dbeta, float *__restrict__ dg,
+    float *__restrict__ dS0, int T, int H) {
     typedef BwdCfg<DT, DK, DV, C> G;
     constexpr int NW = G::NW, NT = G::NT, KT = G::KT, VT = G::VT;
     constexpr int LDK = G::LDK, LDV = G::LDV, LDS_ = G::LDS_, LDSK = G::LDSK, LDC = G::LDC;
-    __shared__ __attribute__((aligned(16))) BwdSmem<DT, DK, DV, C> sm;
+    __shared__ __attribute__((aligned(16))) BwdSmem<DT, DK, DV, C, GATED> sm;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -396,17 +427,93 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
         }
     };
 
+    // dg of chunk cc from the parts of dL/db (wave 0, lane t = token t):
+    // dL/db_t = gamma_t dL/dgamma_t - rho_t dL/drho_t + (row sums - column
+    // sums of W)_t, plus, at the last token, the terms of b_last (in
+    // gamma_last and every rho_t); then dg_t = sum over s >= t of dL/db_s.
+    auto finalize_dg = [&](int cc) {
+        if constexpr (GATED) {
+            constexpr int NJ = NT * (NT + 1) / 2;
+            float db = 0.f, rd = 0.f;
+            if (lane < C) {
+#pragma unroll
+                for (int j = 0; j < KT; ++j) {
+                    db += sm.gt.pdb[j][lane];
+                    rd += sm.gt.prd[j][lane];
+                }
+                const int tt = lane >> 4, tl = lane & 15;
+#pragma unroll
+                for (int jb = 0; jb < 2 * NJ; ++jb) {
+                    int jj = jb < NJ ? jb : jb - NJ, ti = 0;
+                    while (jj > ti) { jj -= ti + 1; ++ti; }
+                    if (ti == tt) db += sm.gt.wrow[jb][tl];
+                    if (jj == tt) db -= sm.gt.wcol[jb][tl];
+                }
+            }
+            const float srd = wave_sum(rd);
+            if (lane == C - 1) {
+                float gc = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) gc += sm.gt.dgc[ww][e];
+                db += gc + srd;
+            }
+#pragma unroll
+            for (int d = 1; d < C; d <<= 1) {
+                const float y = __shfl_down(db, d, 64);
+                if (lane + d < C) db += y;
+            }
+            const int flen = min(C, T - cc * C);
+            if (lane < flen) dg[(((int64_t)b * T + cc * C) + lane) * H + h] = db;
+        }
+    };
+    // Token 16 mt + r's part of dL/db from the transposed dQ / dK tiles of
+    // key tile j (lane (g, r): keys 16 j + 4 g + i):
+    //   dL/dgamma_t = sum_k Q (.) dO S_c - K (.) dV S_c   (= sum_v dO (.) Q S_c^T - dV (.) K S_c^T)
+    //   dL/drho_t   = sum_k K (.) E dS_{c+1}              (= sum_v E (.) K dS_{c+1}^T)
+    // from aq = (dO S_c)^T, an = (dV S_c)^T and ed = (E dS_{c+1})^T before
+    // their decays.  add: accumulate onto the part written by the first pass.
+    auto gate_part = [&](int j, int mt, const f32x4 &aq, const f32x4 &an, const f32x4 *ed,
+                         bool add) {
+        if constexpr (GATED) {
+            const int t = 16 * mt + r;
+            const typename Frag<DT>::k16 qv =
+                *reinterpret_cast<const typename Frag<DT>::k16 *>(sm.Qs + t * LDK + 16 * j + 4 * g);
+            const typename Frag<DT>::k16 kv =
+                *reinterpret_cast<const typename Frag<DT>::k16 *>(sm.Ks + t * LDK + 16 * j + 4 * g);
+            float sg = 0.f, sr = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sg += frag_get(qv, i) * aq[i] - frag_get(kv, i) * an[i];
+                if (ed) sr += frag_get(kv, i) * (*ed)[i];
+            }
+            sg += __shfl_xor(sg, 16, 64);
+            sg += __shfl_xor(sg, 32, 64);
+            sr += __shfl_xor(sr, 16, 64);
+            sr += __shfl_xor(sr, 32, 64);
+            if (g == 0) {
+                const float pr = sm.gt.rto[t] * sr;
+                float pd = sm.gt.gam[t] * sg - pr;
+                if (add) pd += sm.gt.pdb[j][t];
+                sm.gt.pdb[j][t] = pd;
+                sm.gt.prd[j][t] = pr;
+            }
+        }
+    };
+
     // inputs of the next chunk to process travel in registers one chunk ahead
     ChunkPrefetch<DT, DK, DV, C> pf;
     auto prefetch = [&](auto part, int cn) {
         const int tp = cn * C;
-        pf.template load_part<decltype(part)::value>(k, q, v, dout, beta, hs + (head * N + cn) * DV * DK,
+        pf.template load_part<decltype(part)::value>(k, q, v, dout, beta, GATED ? gl : nullptr,
+                                                     hs + (head * N + cn) * DV * DK,
                                                      (int64_t)b * T + tp, h, H, min(C, T - tp), tid);
     };
     if (N > 0) {
         const int t0 = (N - 1) * C;
-        pf.load(k, q, v, dout, beta, hs + (head * N + N - 1) * DV * DK, (int64_t)b * T + t0, h, H,
-                min(C, T - t0), tid);
+        pf.load(k, q, v, dout, beta, GATED ? gl : nullptr, hs + (head * N + N - 1) * DV * DK,
+                (int64_t)b * T + t0, h, H, min(C, T - t0), tid);
     }
     for (int c = N - 1; c >= 0; --c) {
         const int len = min(C, T - c * C);
@@ -418,9 +525,29 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
         pf.v.store(sm.Vs, LDV, tid);
         pf.o.store(sm.Os, LDV, tid);
         pf.s.store(sm.Sb, LDSK, tid);
+        if (GATED && w == 0 && c + 1 < N) finalize_dg(c + 1);
         {
             const float bt = to_f32(pf.b);  // converted by every lane (see RowPrefetch::store)
             if (tid < C) sm.betas[tid] = bt;
+        }
+        if constexpr (GATED) {
+            // in-chunk prefix sums b of the log gate and the two decays; tokens
+            // past the valid length have g = 0, so b_last is the last valid
+            // token's
+            if (w == 0) {
+                float x = lane < C ? pf.gv : 0.f;
+#pragma unroll
+                for (int d = 1; d < C; d <<= 1) {
+                    const float y = __shfl_up(x, d, 64);
+                    if (lane >= d) x += y;
+                }
+                const float bl = __shfl(x, C - 1, 64);
+                if (lane < C) {
+                    sm.gt.gb[lane] = x;
+                    sm.gt.gam[lane] = __expf(x);
+                    sm.gt.rto[lane] = __expf(bl - x);
+                }
+            }
         }
         __syncthreads();
 
@@ -435,6 +562,15 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
             const int tj = jj;
             f32x4 acc = zero4();
             tile_rr<DT, KT>(acc, isP ? sm.Qs : sm.Ks, LDK, 16 * ti, sm.Ks, LDK, 16 * tj, 0, lane);
+            if constexpr (GATED) {
+                // decay exp(b_hi - b_lo) between the later and the earlier token
+                // (symmetric, as the diagonal blocks below use both triangles)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int x = 16 * ti + 4 * g + i, y = 16 * tj + r;
+                    acc[i] *= __expf(sm.gt.gb[max(x, y)] - sm.gt.gb[min(x, y)]);
+                }
+            }
             if (isP) {
                 put_tile(sm.Pm, LDC, 16 * ti, 16 * tj, acc, lane, [](int x, int y) { return x >= y; });
             } else {
@@ -489,6 +625,16 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                 frag_rows(sm.Sb, LDSK, v0, 16 * s, lane, fs[s]);
                 cvt4(Dt[s], fd[s]);
             }
+            if constexpr (GATED) {
+                // dL/dgamma_last = sum dS_{c+1} (.) S_c over this wave's rows
+                float a = 0.f;
+#pragma unroll
+                for (int s = 0; s < KT; ++s)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) a += Dt[s][i] * frag_get(fs[s], i);
+                a = group_sum<16>(a);
+                if (r == 0) sm.gt.dgc[w][g] = a * sm.gt.gam[C - 1];
+            }
             f32x4 dE[NT];
 #pragma unroll
             for (int mt = 0; mt < NT; ++mt) {
@@ -499,6 +645,11 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                 mk_n<DT, KT>(x, fk, fs);
                 typename Frag<DT>::k16 fvv;
                 frag_cols16(sm.Vs, LDV, 16 * mt, v0, lane, fvv);
+                if constexpr (GATED) {
+                    // R = V - diag(gamma) K S_c^T
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[i] *= sm.gt.gam[16 * mt + 4 * g + i];
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) R[mt][i] = frag_get(fvv, i) - x[i];
                 dE[mt] = zero4();
@@ -514,7 +665,15 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                     }
                 }
                 mk_n<DT, NT>(dE[mt], fa, fo);
-                mk_n<DT, KT>(dE[mt], fk, fd);
+                if constexpr (GATED) {
+                    // dE = P^T dO + diag(rho) K dS^T
+                    f32x4 kd = zero4();
+                    mk_n<DT, KT>(kd, fk, fd);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dE[mt][i] += sm.gt.rto[16 * mt + 4 * g + i] * kd[i];
+                } else {
+                    mk_n<DT, KT>(dE[mt], fk, fd);
+                }
             }
             // E = Tm diag(beta) R
             typename Frag<DT>::k16 frb[NT];
@@ -605,8 +764,24 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
 #pragma unroll
             for (int mt = 0; mt < NT; ++mt) {
                 f32x4 nz = -Z[mt];
-                cvt4(nz, fdv[mt]);
                 frag_cols16(sm.Os, LDV, 16 * mt, v0, lane, fo[mt]);
+                if constexpr (GATED) {
+                    // dS <- gamma_last dS + (diag(gamma) dO)^T Q - (diag(gamma) dV)^T K
+                    f32x4 od;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float gm = sm.gt.gam[16 * mt + 4 * g + i];
+                        nz[i] *= gm;
+                        od[i] = frag_get(fo[mt], i) * gm;
+                    }
+                    cvt4(od, fo[mt]);
+                }
+                cvt4(nz, fdv[mt]);
+            }
+            if constexpr (GATED) {
+                const float gc = sm.gt.gam[C - 1];
+#pragma unroll
+                for (int s = 0; s < KT; ++s) Dt[s] = Dt[s] * gc;
             }
 #pragma unroll
             for (int s = 0; s < KT; ++s) {
@@ -630,6 +805,29 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
             const int tj = jj;
             f32x4 acc = zero4();
             tile_rr<DT, VT>(acc, isD ? sm.Os : sm.Rb, LDV, 16 * ti, sm.Es, LDV, 16 * tj, 0, lane);
+            if constexpr (GATED) {
+                // W = dG (.) tril(K K^T (.) D, -1) + Dm (.) (Q K^T (.) D) off
+                // the diagonal (dL/dD_xy D_xy, D_xy = exp(b_x - b_y)): its row
+                // sums add to dL/db_x, its column sums subtract from dL/db_y.
+                // Dm and dG are stored times D for dQ and dK.
+                f32x4 wv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int x = 16 * ti + 4 * g + i, y = 16 * tj + r;
+                    const float a = isD ? acc[i] : -acc[i];
+                    wv[i] = x > y ? a * to_f32((isD ? sm.Pm : sm.Gl)[x * LDC + y]) : 0.f;
+                    acc[i] = x > y ? acc[i] * __expf(sm.gt.gb[x] - sm.gt.gb[y]) : acc[i];
+                }
+                float cs = wv[0] + wv[1] + wv[2] + wv[3];
+                cs += __shfl_xor(cs, 16, 64);
+                cs += __shfl_xor(cs, 32, 64);
+                if (g == 0) sm.gt.wcol[j][r] = cs;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float rs = group_sum<16>(wv[i]);
+                    if (r == 0) sm.gt.wrow[j][4 * g + i] = rs;
+                }
+            }
             if (isD) {
                 put_tile(sm.Dm, LDC, 16 * ti, 16 * tj, acc, lane, [](int x, int y) { return x >= y; });
             } else {
@@ -689,6 +887,8 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
 #pragma unroll
                     for (int i = 0; i < NT; ++i) frag_rows(sm.Dm, LDC, 16 * mt, 16 * i, lane, fm[i]);
                     mk_n<DT, VT>(aq, fs, fa);
+                    const f32x4 aq0 = aq;
+                    if constexpr (GATED) aq = aq * sm.gt.gam[16 * mt + r];  // token 16 mt + r
                     mk_n<DT, NT>(aq, fkc, fm);
                     // dK = -dV S_c + E dS_{c+1} + Gs K + Dm^T Q
                     f32x4 an = zero4(), ak = zero4();
@@ -699,7 +899,12 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
 #pragma unroll
                         for (int i = 0; i < VT; ++i) frag_rows(sm.Es, LDV, 16 * mt, 16 * i, lane, fa[i]);
                         mk_n<DT, VT>(ak, fdb, fa);
+                        gate_part(j, mt, aq0, an, &ak, false);
+                        if constexpr (GATED) ak = ak * sm.gt.rto[16 * mt + r];
+                    } else {
+                        gate_part(j, mt, aq0, an, nullptr, false);
                     }
+                    if constexpr (GATED) an = an * sm.gt.gam[16 * mt + r];
 #pragma unroll
                     for (int i = 0; i < NT; ++i) frag_rows(sm.Gs, LDC, 16 * mt, 16 * i, lane, fm[i]);
                     mk_n<DT, NT>(ak, fkc, fm);
@@ -753,7 +958,14 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                         f32x4 ak = dKa[jj * NMU + u];
 #pragma unroll
                         for (int i = 0; i < VT; ++i) frag_rows(sm.Es, LDV, 16 * mt, 16 * i, lane, fa[i]);
-                        mk_n<DT, VT>(ak, fs, fa);
+                        if constexpr (GATED) {
+                            f32x4 ed = zero4();
+                            mk_n<DT, VT>(ed, fs, fa);
+                            gate_part(j, mt, zero4(), zero4(), &ed, true);
+                            ak += ed * sm.gt.rto[16 * mt + r];
+                        } else {
+                            mk_n<DT, VT>(ak, fs, fa);
+                        }
                         if constexpr (DEFER) {
 #pragma unroll
                             for (int i = 0; i < 4; ++i) frag_set(pk[jj * NMU + u], i, ak[i]);
@@ -770,6 +982,10 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
         }
     }
     if (N > 0) flush(0);
+    if (GATED && N > 0) {
+        __syncthreads();
+        if (w == 0) finalize_dg(0);
+    }
     if (dS0) {
 #pragma unroll
         for (int s = 0; s < KT; ++s)
@@ -777,21 +993,27 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
     }
 }
 
-template <typename DT, int DK, int DV>
-hipError_t launch_bwd_cfg(const ChunkBwdArgs &a, hipStream_t stream) {
+template <typename DT, int DK, int DV, bool GATED>
+hipError_t launch_bwd_gate(const ChunkBwdArgs &a, hipStream_t stream) {
     constexpr int C = sizeof(DT) == 2 ? 32 : 16;
-    if constexpr (!bwd_fits<DT, DK, DV, C>()) {
+    if constexpr (!bwd_fits<DT, DK, DV, C, GATED>()) {
         return hipErrorInvalidValue;
     } else {
-        hipLaunchKernelGGL((chunk_bwd_kernel<DT, DK, DV, C>), dim3((unsigned)(a.B * a.H)),
+        hipLaunchKernelGGL((chunk_bwd_kernel<DT, DK, DV, C, GATED>), dim3((unsigned)(a.B * a.H)),
                            dim3(DV * 4), 0, stream, static_cast<const DT *>(a.q),
                            static_cast<const DT *>(a.k), static_cast<const DT *>(a.v),
-                           static_cast<const DT *>(a.beta), static_cast<const DT *>(a.dout),
-                           a.dS_T, static_cast<const DT *>(a.h), static_cast<DT *>(a.dq), static_cast<DT *>(a.dk),
-                           static_cast<DT *>(a.dv), static_cast<DT *>(a.dbeta), a.dS0,
-                           (int)a.T, (int)a.H);
+                           static_cast<const DT *>(a.beta), a.g, static_cast<const DT *>(a.dout),
+                           a.dS_T, static_cast<const DT *>(a.h), static_cast<DT *>(a.dq),
+                           static_cast<DT *>(a.dk), static_cast<DT *>(a.dv),
+                           static_cast<DT *>(a.dbeta), a.dg, a.dS0, (int)a.T, (int)a.H);
         return hipGetLastError();
     }
+}
+
+template <typename DT, int DK, int DV>
+hipError_t launch_bwd_cfg(const ChunkBwdArgs &a, hipStream_t stream) {
+    return a.g ? launch_bwd_gate<DT, DK, DV, true>(a, stream)
+               : launch_bwd_gate<DT, DK, DV, false>(a, stream);
 }
 
 template <typename DT, int DK>

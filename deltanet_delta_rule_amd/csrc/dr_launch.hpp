@@ -54,9 +54,10 @@ hipError_t static_scratch(void **ptr);
 bool kda_chunk_supported(const ChunkFwdArgs &a, bool bf16);
 hipError_t launch_kda_chunk(const ChunkFwdArgs &a, hipStream_t stream);
 
-// Arguments of the backward of the chunked forward (plain rule).  h holds the
+// Arguments of the backward of the chunked forward.  h holds the
 // checkpoints the forward kernel wrote with chunk = chunk_bwd_chunk(bf16);
-// dS_T and dS0 may be nullptr.
+// dS_T and dS0 may be nullptr.  g, when set, is the log forget gate [B,T,H]
+// (fp32) of the gated rule, and dg [B,T,H] (fp32) receives its gradient.
 struct ChunkBwdArgs {
     const void *q, *k, *v, *beta, *dout;
     const float *dS_T;
@@ -65,6 +66,8 @@ struct ChunkBwdArgs {
     float *dS0;
     int64_t B, T, H;
     int Dk, Dv;
+    const float *g = nullptr;
+    float *dg = nullptr;
 };
 
 hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, bool bf16, hipStream_t stream);

@@ -384,6 +384,32 @@ dr_status delta_rule_chunk_bwd(const void *q, const void *k, const void *v, cons
                                size_t workspace_bytes, int64_t B, int64_t T, int64_t H,
                                int64_t Dk, int64_t Dv, dr_dtype dtype, void *stream);
 
+/*
+ * gated_delta_rule_chunk_bwd -- gradients of gated_delta_rule_chunk_fwd.
+ *
+ * As delta_rule_chunk_bwd, with the log forget gate g among the inputs and
+ * its gradient among the outputs.  The forward is the gated rule of the
+ * hada.io digest (section "Gated DeltaNet : oublier d'abord l'etat entier",
+ * chunkwise as in "Chunkwise KDA" with a scalar decay), and the gradients are
+ * those of its token recurrence.  Within a chunk the decays are exponentials
+ * of differences of in-chunk prefix sums b of g, so dg is the reverse
+ * in-chunk cumulative sum of dL/db.
+ *
+ *   g       [B,T,H] fp32 log forget gate (required when T > 0, 4-byte
+ *           aligned; values <= 0 as in gated_delta_rule_chunk_fwd)
+ *   dg      [B,T,H] fp32 output dL/dg (required when T > 0, 4-byte aligned)
+ *   workspace  delta_rule_chunk_bwd_workspace_bytes(B,T,H,Dk,Dv,dtype) bytes
+ *   Every other argument, size and error behaves as in delta_rule_chunk_bwd;
+ *   dg must not overlap the inputs, the workspace or the other outputs.
+ */
+dr_status gated_delta_rule_chunk_bwd(const void *q, const void *k, const void *v,
+                                     const void *beta, const float *g, const float *S0,
+                                     const void *dout, const float *dS_T, void *dq, void *dk,
+                                     void *dv, void *dbeta, float *dg, float *dS0,
+                                     void *workspace, size_t workspace_bytes, int64_t B,
+                                     int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                     dr_dtype dtype, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *delta_rule_status_string(dr_status status);
 
@@ -397,7 +423,8 @@ int delta_rule_last_hip_error(void);
  * decay (gk) in dr_step_opts; 2.6.0: DR_FUSED_RECURRENT and gk in
  * dr_chunk_opts; 2.7.0: the segment-parallel schedule's workspace in
  * dr_chunk_opts and delta_rule_chunk_fwd_workspace_bytes; 2.8.0:
- * delta_rule_chunk_fwd_noalloc and DR_ERR_SCRATCH). */
+ * delta_rule_chunk_fwd_noalloc and DR_ERR_SCRATCH; 2.9.0:
+ * gated_delta_rule_chunk_bwd). */
 int delta_rule_version(void);
 
 #ifdef __cplusplus

@@ -334,6 +334,32 @@ def test_backward_rejects_unsupported_and_empty(lib):
     assert _bwd(lib, B=0) == dr.DR_OK
 
 
+def _gbwd(lib, g=ctypes.c_void_p(0x100000 * 12), dg=ctypes.c_void_p(0x100000 * 13), ws=P[7],
+          wsb=1 << 40, q=P[0], k=P[1], v=P[2], beta=P[3], dout=P[4], dq=P[5], dk=P[6],
+          dv=ctypes.c_void_p(0x100000 * 10), dbeta=ctypes.c_void_p(0x100000 * 11), dS0=None,
+          S0=None, dST=None, B=1, T=64, H=2, Dk=64, Dv=64, dtype=dr.DR_BF16):
+    return lib.gated_delta_rule_chunk_bwd(q, k, v, beta, g, S0, dout, dST, dq, dk, dv, dbeta,
+                                          dg, dS0, ws, wsb, B, T, H, Dk, Dv, dtype, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(g=None), dict(dg=None),     # both required when T > 0
+    dict(g=ODD), dict(dg=ctypes.c_void_p(0x100000 * 13 + 2)),   # not 4-byte aligned
+    dict(dg=P[3]),                   # dg overlaps beta
+    dict(dg=P[5]),                   # dg overlaps dq
+    dict(dg=P[7]),                   # dg overlaps the workspace
+    dict(dq=ctypes.c_void_p(0x100000 * 12)),   # an output overlaps g
+    dict(ws=None), dict(dout=None), dict(dtype=7),
+])
+def test_gated_backward_rejects_invalid(lib, kw):
+    assert _gbwd(lib, **kw) == dr.DR_ERR_INVALID_ARG
+
+
+def test_gated_backward_rejects_unsupported_and_empty(lib):
+    assert _gbwd(lib, Dv=40) == dr.DR_ERR_UNSUPPORTED
+    assert _gbwd(lib, H=0) == dr.DR_OK
+
+
 # ------------------------------------------- segment-parallel workspace size
 def test_chunk_fwd_workspace_bytes(lib):
     f = lib.delta_rule_chunk_fwd_workspace_bytes

@@ -1,13 +1,14 @@
-"""GPU parity of the backward (``delta_rule_chunk_bwd``) against the fp64
-backward oracle.
+"""GPU parity of the backward (``delta_rule_chunk_bwd`` and
+``gated_delta_rule_chunk_bwd``) against the fp64 backward oracle.
 
 Seeded inputs and seeded upstream gradients (do, dS_T) go to the HIP path and
-to ``oracle.delta_rule_bwd_ref``; every gradient (dq, dk, dv, dbeta, dS0) must
-satisfy max |gpu - ref| <= tol * max |ref|, tol = 1e-4 for fp32 inputs and
-2e-2 for bf16 inputs, the forward's tolerances.  Cases span several chunks of
-the backward (32 tokens for bf16, 16 for fp32) with ragged tails, every head
-size, beta up to 2, a nonzero incoming state, and the layer shape with whole
-heads sampled.
+to ``oracle.delta_rule_bwd_ref``; every gradient (dq, dk, dv, dbeta, dS0 and,
+for the gated rule, dg) must satisfy max |gpu - ref| <= tol * max |ref|,
+tol = 1e-4 for fp32 inputs and 2e-2 for bf16 inputs, the forward's
+tolerances.  Cases span several chunks of the backward (32 tokens for bf16,
+16 for fp32) with ragged tails, every head size, beta up to 2, a nonzero
+incoming state, gates from weak to strong (per-head A up to 16, so that a
+chunk's decay underflows), and the layer shape with whole heads sampled.
 """
 from __future__ import annotations
 
@@ -41,8 +42,12 @@ def _check(w, seed=7, with_dst=True, heads=None):
     x = W.generate(w)
     do, dst = _upstream(w, seed, with_dst)
     d = to_dev(x)
-    g = dr.delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], do.cuda(), d["S0"],
-                                None if dst is None else dst.cuda())
+    dstd = None if dst is None else dst.cuda()
+    if x.get("g") is None:
+        g = dr.delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], do.cuda(), d["S0"], dstd)
+    else:
+        g = dr.gated_delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], do.cuda(),
+                                          d["S0"], dstd)
     torch.cuda.synchronize()
     if heads is not None:
         pick = lambda t: torch.stack([t[b, :, h] for b, h in heads], dim=1)[None]
@@ -54,9 +59,10 @@ def _check(w, seed=7, with_dst=True, heads=None):
     else:
         xs, do_r, dst_r, got = x, do, dst, g
     ref = delta_rule_bwd_ref(xs["q"], xs["k"], xs["v"], xs["beta"], do_r, xs["S0"], dst_r,
-                             nthreads=threads())
+                             g=xs.get("g"), nthreads=threads())
     tol = TOL[w.torch_dtype]
-    errs = {n: rel_err(to_np(got[n]), ref[n]) for n in ("dq", "dk", "dv", "dbeta", "dS0")}
+    names = ("dq", "dk", "dv", "dbeta", "dS0") + (("dg",) if "dg" in ref else ())
+    errs = {n: rel_err(to_np(got[n]), ref[n]) for n in names}
     print(f"bwd {w.name} B{w.B} H{w.H} T{w.T} Dk{w.Dk} Dv{w.Dv} {w.dtype}: " +
           " ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
     for n, e in errs.items():
@@ -105,5 +111,81 @@ def test_backward_is_deterministic():
     do, dst = _upstream(w, 3)
     a = dr.delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], do.cuda(), None, dst.cuda())
     b = dr.delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], do.cuda(), None, dst.cuda())
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
+
+
+# ----------------------------------------------------------------- gated rule
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("Dk,Dv", [(16, 16), (32, 64), (64, 32), (64, 128), (128, 64),
+                                   (128, 128)])
+def test_gated_backward_shapes(dtype, Dk, Dv):
+    w = W.get("gated_layer_1p3b", B=2, H=2, T=77, Dk=Dk, Dv=Dv, dtype=dtype,
+              seed=7400 + Dk + 3 * Dv)
+    _check(w, seed=Dk + Dv + 1)
+
+
+@pytest.mark.parametrize("T", [1, 16, 31, 32, 33, 100])
+def test_gated_backward_sequence_lengths(T):
+    _check(W.get("gated_layer_1p3b", B=1, H=2, T=T, seed=7500 + T), seed=T + 50)
+
+
+@pytest.mark.parametrize("amax", [0.05, 1.0, 16.0])
+def test_gated_backward_gate_strengths(amax):
+    # weak gates (the decays' derivatives dominate nothing), moderate, and
+    # strong enough that exp(b) underflows within a chunk
+    w = W.get("gated_layer_1p3b", B=2, H=3, T=130, gate_amax=amax, seed=7600)
+    _check(w, seed=11)
+
+
+def test_gated_backward_without_state_gradient_or_initial_state():
+    w = W.get("gated_layer_1p3b", B=2, H=2, T=70, seed=7700)
+    _check(w, with_dst=False)
+
+
+def test_gated_backward_layer_shape_sampled_heads():
+    _check(W.get("gated_layer_1p3b", T=512), heads=[(0, 0), (5, 9), (7, 15)])
+
+
+def test_backward_full_length_sampled_heads():
+    # the layer workload at its full length, both rules, three heads checked
+    _check(W.get("layer_1p3b", B=2, H=16), heads=[(0, 3), (1, 12)])
+    _check(W.get("gated_layer_1p3b", B=2, H=16), heads=[(0, 5), (1, 14)])
+
+
+def test_gated_backward_with_zero_gate_matches_plain():
+    w = W.get("layer_1p3b", B=2, H=2, T=90, seed=7800)
+    d = to_dev(W.generate(w))
+    do, dst = _upstream(w, 5)
+    a = dr.delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], do.cuda(), d["S0"],
+                                dst.cuda())
+    zero = torch.zeros(w.B, w.T, w.H, device="cuda")
+    b = dr.gated_delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], zero, do.cuda(),
+                                      d["S0"], dst.cuda())
+    for n in a:
+        e = rel_err(to_np(b[n]), to_np(a[n]).astype(np.float64))
+        assert e <= TOL[w.torch_dtype], (n, e)
+
+
+def test_gated_backward_empty_sequence_passes_the_state_gradient():
+    w = W.get("gated_layer_1p3b", B=1, H=2, T=0)
+    d = to_dev(W.generate(w))
+    dst = torch.randn(1, 2, 128, 128, device="cuda")
+    do = torch.zeros(1, 0, 2, 128, dtype=torch.bfloat16, device="cuda")
+    g = torch.zeros(1, 0, 2, device="cuda")
+    out = dr.gated_delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], g, do, d["S0"], dst)
+    torch.testing.assert_close(out["dS0"], dst, rtol=0, atol=0)
+    assert out["dg"].numel() == 0
+
+
+def test_gated_backward_is_deterministic():
+    w = W.get("gated_layer_1p3b", B=2, H=4, T=96, seed=7900)
+    d = to_dev(W.generate(w))
+    do, dst = _upstream(w, 3)
+    a = dr.gated_delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], do.cuda(),
+                                      None, dst.cuda())
+    b = dr.gated_delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], do.cuda(),
+                                      None, dst.cuda())
     for n in a:
         assert torch.equal(a[n], b[n]), n
