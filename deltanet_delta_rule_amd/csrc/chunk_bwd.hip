@@ -1,4 +1,4 @@
-// Backward of the chunked delta rule (plain rule, gfx950).
+// Backward of the chunked delta rule (plain and gated rule, gfx950).
 //
 // The forward pass is S_{c+1} = S_c + E^T K and O = Q S_c^T + P E per chunk c
 // (C tokens), with P = Q K^T (.) M, A = diag(beta) tril(K K^T, -1),
@@ -20,6 +20,31 @@
 //
 // and dS0 is dS after the first chunk.  The fp64 oracle (reverse token order)
 // pins all of it.
+//
+// Gated rule (hada.io digest, "Gated DeltaNet" and "Chunkwise KDA" with a
+// scalar decay).  With b the in-chunk prefix sums of the log gate,
+// gamma_t = exp(b_t), rho_t = exp(b_last - b_t) and D_ij = exp(b_i - b_j),
+// the forward uses G (.) D and P (.) D, R = V - diag(gamma) K S_c^T,
+// O = diag(gamma) Q S_c^T + P E and S_{c+1} = gamma_last S_c +
+// E^T diag(rho) K.  The same chain rule gives
+//
+//   dE   = P^T dO + diag(rho) K dS^T
+//   dQ   = diag(gamma) dO S_c + ((dO E^T) (.) M (.) D) K
+//   dK   = -diag(gamma) dV S_c + diag(rho) E dS + (dG' + dG'^T) K
+//          + ((dO E^T) (.) M (.) D)^T Q,            dG' = dG (.) D
+//   dS  <- gamma_last dS + (diag(gamma) dO)^T Q - (diag(gamma) dV)^T K
+//
+// and for b: dL/dgamma_t = sum_k (Q (.) dO S_c - K (.) dV S_c)_tk,
+// dL/drho_t = sum_k (K (.) E dS)_tk, dL/dgamma_last = <dS, S_c>, and
+// W = dG (.) (G (.) D) + (dO E^T) (.) (P (.) D) off the diagonal (dL/dD_ij
+// times D_ij), so that
+//
+//   dL/db_t = gamma_t dL/dgamma_t - rho_t dL/drho_t + sum_j W_tj - sum_i W_it
+//             (+ gamma_last dL/dgamma_last + sum_s rho_s dL/drho_s at the last token)
+//
+// and dg_t is the sum of dL/db_s over s >= t within the chunk.  The sums
+// over k come from the transposed dQ and dK tiles before their decays, so
+// the per-wave phase keeps no extra products.
 //
 // Work split.  One workgroup per (b, h) walks the chunks in reverse.  Wave w
 // owns value columns 16w .. 16w+15: its slices of R, E, dE, Z, dV and the
