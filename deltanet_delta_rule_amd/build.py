@@ -26,11 +26,14 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed fp32 instructions are disabled for all device code.  MFMA results
 # are allocated in ordinary VGPRs (not the accumulator file), so the VALU
-# reads them without v_accvgpr copies.
+# reads them without v_accvgpr copies.  Private arrays are never moved into
+# LDS: in a kernel with LDS to spare the compiler had turned a register
+# prefetch into LDS stores, which wait for the loads right after issuing them.
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    "-mllvm", "-disable-promote-alloca-to-lds",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

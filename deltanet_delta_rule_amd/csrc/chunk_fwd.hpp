@@ -366,10 +366,11 @@ __device__ __forceinline__ float diag_inv_norm(const f32x4 &acc, int lane, bool 
 // wave; a wave loads every K tile its jobs touch once, plus the Q tiles of its
 // P rows, all before its first MFMA, and does its A rows first so that the
 // chain of its diagonal inverse overlaps the products of its P rows.
-template <int NT, int NW, int W>
+template <int NT, int NW, int W, bool NOOUT = false>
 struct GramJobs {
     static constexpr bool a_row(int ti) { return ti % NW == W; }
-    static constexpr bool p_row(int ti) { return (NT - 1 - ti) % NW == W; }
+    // P = Q K^T is needed only for the outputs
+    static constexpr bool p_row(int ti) { return !NOOUT && (NT - 1 - ti) % NW == W; }
     static constexpr int kmax() {
         int m = -1;
         for (int ti = 0; ti < NT; ++ti)
@@ -378,10 +379,10 @@ struct GramJobs {
     }
 };
 
-template <int NT, int NW, int W>
+template <int NT, int NW, int W, bool NOOUT = false>
 constexpr int n_prows() {
     int n = 0;
-    for (int ti = 0; ti < NT; ++ti) n += GramJobs<NT, NW, W>::p_row(ti) ? 1 : 0;
+    for (int ti = 0; ti < NT; ++ti) n += GramJobs<NT, NW, W, NOOUT>::p_row(ti) ? 1 : 0;
     return n;
 }
 
@@ -464,15 +465,15 @@ __device__ __forceinline__ void q_norms(const FD *fq, int ti, NormLds<C> *nl, in
 
 // When the fragments of all the wave's jobs fit in 96 VGPRs they are loaded
 // once, before the first MFMA; otherwise each job loads its own.
-template <typename DT, int DK, int C, int NW, int W, bool GATED, bool L2>
+template <typename DT, int DK, int C, int NW, int W, bool GATED, bool L2, bool NOOUT = false>
 __device__ __forceinline__ void gram_tiles_w(const DT *Ks, const DT *Qs, const float *betas,
                                              const float *bc, DT *Ab, DT *Tb, DT *Ps,
                                              NormLds<C> *nl, int lane) {
     typedef ChunkCfg<DT, DK, C, NW> G;
-    typedef GramJobs<G::NT, NW, W> J;
+    typedef GramJobs<G::NT, NW, W, NOOUT> J;
     constexpr int NT = G::NT, KSD = G::KSD, NSD = DK / KSD, KM = J::kmax();
     typedef typename SlabFrag<KSD == 32, DT>::type FD;
-    constexpr bool ALL = (KM + 1 + n_prows<NT, NW, W>()) * NSD * sizeof(FD) <= 384;
+    constexpr bool ALL = (KM + 1 + n_prows<NT, NW, W, NOOUT>()) * NSD * sizeof(FD) <= 384;
     const int r = lane & 15;
     float brow[NT];
 #pragma unroll
@@ -579,7 +580,8 @@ __device__ __forceinline__ void store_out4_f32(const f32x4 &x, const OutChunk &o
 // Gated rule: X starts at zero, and gate_xy applies the decays and -V after
 // the products (V is then loaded after them, which keeps its fragments out of
 // the products' live range).
-template <typename DT, int DK, int C, int NW, bool GATED, bool L2>
+// NOOUT (no outputs wanted): Y is left at zero and Q is not read.
+template <typename DT, int DK, int C, int NW, bool GATED, bool L2, bool NOOUT = false>
 __device__ __forceinline__ void state_xy(const DT *Ks, const DT *Qs, const f32x4 *Sacc,
                                          const typename Frag<DT>::k16 *fv, f32x4 *X, f32x4 *Y,
                                          int lane) {
@@ -597,15 +599,15 @@ __device__ __forceinline__ void state_xy(const DT *Ks, const DT *Qs, const f32x4
     }
     // All operand fragments are loaded before the first MFMA when they fit in
     // 128 VGPRs; otherwise they are double-buffered one slab ahead.
-    constexpr bool ALL = 2 * NSD * NT * sizeof(FD) <= 512;
+    constexpr bool ALL = (NOOUT ? 1 : 2) * NSD * NT * sizeof(FD) <= 512;
     constexpr int NB = ALL ? NSD : 2;
-    FD fk[NB][NT], fq[NB][NT];
+    FD fk[NB][NT], fq[NOOUT ? 1 : NB][NT];
 #pragma unroll
     for (int s = 0; s < (ALL ? NSD : 1); ++s)
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt) {
             kq_rows<DT, DK, C, NW>(Ks, 16 * mt, s * KSD, lane, fk[s][mt]);
-            kq_rows<DT, DK, C, NW>(Qs, 16 * mt, s * KSD, lane, fq[s][mt]);
+            if constexpr (!NOOUT) kq_rows<DT, DK, C, NW>(Qs, 16 * mt, s * KSD, lane, fq[s][mt]);
         }
 #pragma unroll
     for (int s = 0; s < NSD; ++s) {
@@ -614,7 +616,8 @@ __device__ __forceinline__ void state_xy(const DT *Ks, const DT *Qs, const f32x4
 #pragma unroll
             for (int mt = 0; mt < NT; ++mt) {
                 kq_rows<DT, DK, C, NW>(Ks, 16 * mt, (s + 1) * KSD, lane, fk[cur ^ 1][mt]);
-                kq_rows<DT, DK, C, NW>(Qs, 16 * mt, (s + 1) * KSD, lane, fq[cur ^ 1][mt]);
+                if constexpr (!NOOUT)
+                    kq_rows<DT, DK, C, NW>(Qs, 16 * mt, (s + 1) * KSD, lane, fq[cur ^ 1][mt]);
             }
         }
         FD fb;  // rows of S: B operand of X, A operand of Y
@@ -624,10 +627,10 @@ __device__ __forceinline__ void state_xy(const DT *Ks, const DT *Qs, const f32x4
         for (int mt = 0; mt < NT; ++mt) {
             if constexpr (KSD == 32) {
                 mma_k32(X[mt], fk[cur][mt], fb);
-                mma_k32(Y[mt], fb, fq[cur][mt]);
+                if constexpr (!NOOUT) mma_k32(Y[mt], fb, fq[NOOUT ? 0 : cur][mt]);
             } else {
                 mma_k16(X[mt], fk[cur][mt], fb);
-                mma_k16(Y[mt], fb, fq[cur][mt]);
+                if constexpr (!NOOUT) mma_k16(Y[mt], fb, fq[NOOUT ? 0 : cur][mt]);
             }
         }
     }
@@ -706,7 +709,8 @@ __device__ __forceinline__ void cat16(const f32x4_arr &a, const f32x4_arr &b, f3
 // outputs are unchanged; the state update becomes
 //   S^T <- gam_last S^T + K^T diag(rto) E
 // with its own copy of the E fragments (the outputs need the unscaled E).
-template <typename DT, int DK, int C, int NW, bool GATED, bool L2>
+// NOOUT: the outputs (and the reads of P) are skipped.
+template <typename DT, int DK, int C, int NW, bool GATED, bool L2, bool NOOUT = false>
 __device__ __forceinline__ void state_rest(const ChunkOperands<DT, DK, C, NW> &op,
                                            const DT *Ab, const DT *Tb, const DT *Ps,
                                            const GateLds<C> *ga, const NormLds<C> *nl,
@@ -723,13 +727,15 @@ __device__ __forceinline__ void state_rest(const ChunkOperands<DT, DK, C, NW> &o
     for (int i = 0; i < NT; ++i) load_fragblk(Tb, i, lane, ft[i]);
 #pragma unroll
     for (int i = 0; i < NOFF; ++i) load_fragblk(Ab, i, lane, fa[i]);
-    FC fP[NT][NSC];
+    FC fP[NOOUT ? 1 : NT][NSC];
+    if constexpr (!NOOUT) {
 #pragma unroll
-    for (int mt = 0; mt < NT; ++mt)
+        for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
-        for (int s = 0; s < NSC; ++s)
-            if (s * KSC < 16 * (mt + 1))  // P is lower-triangular
-                p_rows<DT, DK, C, NW>(Ps, 16 * mt, s * KSC, lane, fP[mt][s]);
+            for (int s = 0; s < NSC; ++s)
+                if (s * KSC < 16 * (mt + 1))  // P is lower-triangular
+                    p_rows<DT, DK, C, NW>(Ps, 16 * mt, s * KSC, lane, fP[mt][s]);
+    }
     // block forward substitution
     f32x4 E[NT];
     F16 fe16[NT], fs16[GATED ? NT : 1];
@@ -778,6 +784,7 @@ __device__ __forceinline__ void state_rest(const ChunkOperands<DT, DK, C, NW> &o
             if constexpr (KSC == 32) mma_k32(Sacc[dt], op.fkt[dt][s], fe[s]);
             else mma_k16(Sacc[dt], op.fkt[dt][s], fe[s]);
         }
+    if constexpr (NOOUT) return;
     if constexpr (GATED) slabs(fe16);
     // O^T = S Q^T + E^T P^T.  When the slabs over d_k and over tokens have the
     // same MFMA shape, E^T P^T accumulates onto S Q^T; otherwise it gets its
@@ -791,8 +798,8 @@ __device__ __forceinline__ void state_rest(const ChunkOperands<DT, DK, C, NW> &o
 #pragma unroll
         for (int s = 0; s < NSC; ++s)
             if (s * KSC < 16 * (mt + 1)) {
-                if constexpr (KSC == 32) mma_k32(acc, fe[s], fP[mt][s]);
-                else mma_k16(acc, fe[s], fP[mt][s]);
+                if constexpr (KSC == 32) mma_k32(acc, fe[s], fP[NOOUT ? 0 : mt][s]);
+                else mma_k16(acc, fe[s], fP[NOOUT ? 0 : mt][s]);
             }
         // lane (g, r): token 16mt + r, value columns 4g .. 4g + 3
         f32x4 o4 = (KSC == KSD) ? Y[mt] : Y[mt] + PE;
@@ -1120,7 +1127,7 @@ constexpr bool ws_fits() {
 // loads of chunk c+3 (into the set chunk c has just vacated), computes the
 // Gram tiles and diagonal inverses of chunk c+1, waits for the loads of chunk
 // c+2 and publishes them at the barrier.
-template <typename DT, int DK, int C, int NW, int W, bool GATED, bool L2>
+template <typename DT, int DK, int C, int NW, int W, bool GATED, bool L2, bool NOOUT = false>
 __device__ __forceinline__ void prep_role(PipeSmem<DT, DK, C, NW, GATED, L2> &sm,
                                           const HeadPtrs<DT> &p, int T, int N, int lane) {
     typedef ChunkCfg<DT, DK, C, NW> G;
@@ -1150,7 +1157,7 @@ __device__ __forceinline__ void prep_role(PipeSmem<DT, DK, C, NW, GATED, L2> &sm
     publish(0, t0s);
     lds_barrier();  // chunk 0 staged
     if (N > 0)
-        gram_tiles_w<DT, DK, C, NW, W, GATED, L2>(sm.Ks[0], sm.Qs[0], sm.betas[0], bc_of(0),
+        gram_tiles_w<DT, DK, C, NW, W, GATED, L2, NOOUT>(sm.Ks[0], sm.Qs[0], sm.betas[0], bc_of(0),
                                                   sm.Ab[0], sm.Tb[0], sm.Ps[0], sm.norm.at(0),
                                                   lane);
     wait_vmcnt<D::NVMEM>();  // chunk 1 landed
@@ -1161,7 +1168,7 @@ __device__ __forceinline__ void prep_role(PipeSmem<DT, DK, C, NW, GATED, L2> &sm
         const int s0 = c % 3, s1 = (c + 1) % 3, s2 = (c + 2) % 3;
         dma.issue(p, T, c + 3, sm.Ks[s0], sm.Qs[s0], sm.Vs[s0], tnext, lane);
         if (c + 1 < N)
-            gram_tiles_w<DT, DK, C, NW, W, GATED, L2>(sm.Ks[s1], sm.Qs[s1], sm.betas[s1],
+            gram_tiles_w<DT, DK, C, NW, W, GATED, L2, NOOUT>(sm.Ks[s1], sm.Qs[s1], sm.betas[s1],
                                                       bc_of(s1), sm.Ab[b1p], sm.Tb[b1p],
                                                       sm.Ps[b1p], sm.norm.at(b1p), lane);
         wait_vmcnt<D::NVMEM>();  // chunk c+2 landed
@@ -1197,7 +1204,11 @@ __device__ __forceinline__ void prep_role(PipeSmem<DT, DK, C, NW, GATED, L2> &sm
 //
 // Gated rule (GATED, gl = log gates [B,T,H]): wave 0 of the preparation waves
 // also loads each chunk's gates and publishes their decays with its betas.
-template <typename DT, int DK, int C, int NW, bool GATED, bool L2>
+//
+// NOOUT: a launch without outputs (o == nullptr: the checkpoint pass of the
+// backward, the state passes of the segment-parallel schedule) skips every
+// product that only the outputs need (P = Q K^T, Y = S Q^T, E^T P^T).
+template <typename DT, int DK, int C, int NW, bool GATED, bool L2, bool NOOUT = false>
 __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4 + 1, NW / 4 + 1))) void chunk_fwd_ws_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const float *__restrict__ gl, const float *S0,
@@ -1232,7 +1243,7 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4
         // (L2: V stays in op.fv for the block substitution of that chunk)
         auto xy = [&](int s) {
             if constexpr (!GATED && !L2) op.load_v(sm.Vs[s], wave, lane);
-            state_xy<DT, DK, C, NW, GATED, L2>(sm.Ks[s], sm.Qs[s], Sacc, op.fv, X, Y, lane);
+            state_xy<DT, DK, C, NW, GATED, L2, NOOUT>(sm.Ks[s], sm.Qs[s], Sacc, op.fv, X, Y, lane);
             if constexpr (GATED || L2) op.load_v(sm.Vs[s], wave, lane);
             if constexpr (GATED) gate_xy<DT, C, NT, !L2>(op.fv, sm.gate.at(s)->gam, X, Y, lane);
             op.load_kt(sm.Ks[s], lane);
@@ -1248,8 +1259,9 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4
             const int len = o ? min(C, p.T - t0) : 0;
             out.rsrc = make_rsrc(p.oh + (int64_t)t0 * p.tsv, len * out.row_bytes);
             if (hs) store_state_row<G::KSD, ND>(hs + ((p.head * N + c) * Dv + p.vcol) * DK, Sacc, g);
-            state_rest<DT, DK, C, NW, GATED, L2>(op, sm.Ab[b], sm.Tb[b], sm.Ps[b], sm.gate.at(s0),
-                                                 sm.norm.at(b), Sacc, X, Y, out, lane);
+            state_rest<DT, DK, C, NW, GATED, L2, NOOUT>(op, sm.Ab[b], sm.Tb[b], sm.Ps[b],
+                                                        sm.gate.at(s0), sm.norm.at(b), Sacc, X, Y,
+                                                        out, lane);
             // V first (X starts at -V); the K^T fragments of the next state
             // update only after X and Y have used their operands
             if (c + 1 < N) xy(s1);
@@ -1272,10 +1284,10 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4
             head_ptrs<DT, DK, NW>(q, k, v, beta, gl, o, cu, T, H, Dv, nvt, 0, r);
         const int N = (p.T + C - 1) / C;
         switch (wave - NW) {
-        case 0: prep_role<DT, DK, C, NW, 0, GATED, L2>(sm, p, p.T, N, lane); break;
-        case 1: if constexpr (NW > 1) prep_role<DT, DK, C, NW, 1, GATED, L2>(sm, p, p.T, N, lane); break;
-        case 2: if constexpr (NW > 2) prep_role<DT, DK, C, NW, 2, GATED, L2>(sm, p, p.T, N, lane); break;
-        default: if constexpr (NW > 3) prep_role<DT, DK, C, NW, 3, GATED, L2>(sm, p, p.T, N, lane); break;
+        case 0: prep_role<DT, DK, C, NW, 0, GATED, L2, NOOUT>(sm, p, p.T, N, lane); break;
+        case 1: if constexpr (NW > 1) prep_role<DT, DK, C, NW, 1, GATED, L2, NOOUT>(sm, p, p.T, N, lane); break;
+        case 2: if constexpr (NW > 2) prep_role<DT, DK, C, NW, 2, GATED, L2, NOOUT>(sm, p, p.T, N, lane); break;
+        default: if constexpr (NW > 3) prep_role<DT, DK, C, NW, 3, GATED, L2, NOOUT>(sm, p, p.T, N, lane); break;
         }
     }
 }
@@ -1368,6 +1380,19 @@ hipError_t launch_cfg(const ChunkFwdArgs &a, hipStream_t stream) {
     const DT *q = static_cast<const DT *>(a.q), *k = static_cast<const DT *>(a.k);
     const DT *v = static_cast<const DT *>(a.v), *beta = static_cast<const DT *>(a.beta);
     DT *o = static_cast<DT *>(a.o);
+    // without outputs, the specialisation that skips their products (bf16,
+    // the larger head and chunk sizes: the backward's checkpoints and the
+    // segment passes; other shapes compute the outputs and drop them)
+    constexpr bool HAS_NOOUT = sizeof(DT) == 2 && DK >= 64 && C >= 32 && !L2;
+    if constexpr (HAS_NOOUT && ws_fits<DT, DK, C, NW, GATED, L2>()) {
+        if (!o) {
+            hipLaunchKernelGGL((chunk_fwd_ws_kernel<DT, DK, C, NW, GATED, L2, true>),
+                               dim3((unsigned)grid), dim3(128 * NW), 0, stream, q, k, v, beta, a.g,
+                               a.S0, o, a.S_T, static_cast<DT *>(a.h), a.cu, (int)a.T, (int)a.H,
+                               a.Dv, nvt, a.scale);
+            return hipGetLastError();
+        }
+    }
     if constexpr (ws_fits<DT, DK, C, NW, GATED, L2>()) {
         hipLaunchKernelGGL((chunk_fwd_ws_kernel<DT, DK, C, NW, GATED, L2>), dim3((unsigned)grid),
                            dim3(128 * NW), 0, stream, q, k, v, beta, a.g, a.S0, o, a.S_T,

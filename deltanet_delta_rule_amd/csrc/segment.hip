@@ -85,66 +85,93 @@ __global__ __launch_bounds__(256) void seg_init_kernel(float *M, int *cu, int64_
     }
 }
 
+// M_p (all of it, 16-byte vectors dealt to the 256 threads) and this lane's
+// entries of H_p for the chain step of segment `seg`, into registers.
+template <int DK, int NMV, int TPW, bool MEXACT, bool FULL>
+__device__ __forceinline__ void chain_fetch(f32x4 (&mreg)[NMV], f32x4 (&hreg)[TPW],
+                                            const float *M, const float *Hs, int64_t seg,
+                                            int64_t H, int64_t h, int Dv, int row0, int wave,
+                                            int tid, int g, int r) {
+    constexpr int NT = DK / 16;
+    const int nmv = DK * DK / 4;
+    // native vectors, not float4: copies of HIP's vector struct become memory
+    // copies that keep the array out of registers
+    const f32x4 *mp = reinterpret_cast<const f32x4 *>(M + (seg * H + h) * DK * DK);
+#pragma unroll
+    for (int u = 0; u < NMV; ++u) mreg[u] = mp[MEXACT ? tid + 256 * u : min(tid + 256 * u, nmv - 1)];
+    const float *hp = Hs + ((seg * H + h) * Dv + row0) * DK;
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        const int n = wave + 4 * j;
+        if (FULL || n < NT) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hreg[j][e] = hp[(4 * g + e) * DK + 16 * n + r];
+        }
+    }
+}
+
 // The chain over segments for 16 state rows of one (sequence, head), on the
 // fp32 matrix cores: wave w computes the output columns 16 (w + 4 j) .. of
 // S M_p (16 x 16 tiles, D layout: lane (g, r) holds rows 4g .. 4g + 3 of
 // column r), contracting over d_k four keys at a time with S and M_p staged
 // in LDS.  Hs holds H_p on entry and S_in(p) on exit (each workgroup touches
-// only its own rows).
+// only its own rows).  A step reads all of its operands from LDS into
+// registers before its first product, so that the products issue back to
+// back; the wave index is uniform and, for d_k >= 64, every wave has the same
+// tiles, so nothing in a step branches per lane.
 template <int DK>
 __global__ __launch_bounds__(256) void seg_chain_kernel(float *Hs, const float *M,
                                                         const float *S0, float *S_T, int P,
                                                         int H, int Dv) {
     constexpr int NT = DK / 16;                 // output tiles per row block
     constexpr int TPW = (NT + 3) / 4;           // tiles per wave
+    constexpr bool FULL = NT % 4 == 0;          // every wave has TPW tiles
+    constexpr int NK = DK / 4;                  // k steps of the 16x16x4 products
     constexpr int LDSS = DK + 4;                // S row pitch (floats)
     constexpr int LDM = DK + 16;                // M row pitch: lane groups on distinct banks
     __shared__ __attribute__((aligned(16))) float Ms[DK * LDM];
     __shared__ __attribute__((aligned(16))) float Ss[16 * LDSS];
     const int nrt = Dv / 16;
-    const int rt = blockIdx.x % nrt;
-    const int64_t bh = blockIdx.x / nrt;  // b * H + h
+    // Consecutive workgroup ids go round-robin over the 8 XCDs, each with its
+    // own L2; the row tiles of one head read the same M_p, so remap them onto
+    // one XCD.
+    int wg = blockIdx.x;
+    const int nwg = gridDim.x;
+    if (nwg % 8 == 0) wg = (wg % 8) * (nwg / 8) + wg / 8;
+    const int rt = wg % nrt;
+    const int64_t bh = wg / nrt;  // b * H + h
     const int64_t b = bh / H, h = bh % H;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, r = lane & 15;
     const int row0 = rt * 16;
+    // tile j of this wave covers columns 16 n .., n = wave + 4 j, if n < NT
+    auto has = [&](int j) { return FULL || wave + 4 * j < NT; };
 
-    constexpr int NMV = DK * DK / 4 / 256 > 0 ? DK * DK / 4 / 256 : 1;  // float4 of M per thread
+    constexpr int NMV = DK * DK / 4 / 256 > 0 ? DK * DK / 4 / 256 : 1;  // 16-byte vectors of M per thread
+    constexpr bool MEXACT = NMV * 256 == DK * DK / 4;
     const int nmv = DK * DK / 4;
 
-    // S in D layout: tile j of this wave (if any), lane (g, r): rows 4g + e,
-    // column 16 n + r with n = wave + 4 j
     f32x4 s[TPW];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
         const int n = wave + 4 * j;
+        s[j] = zero4();
+        if (has(j)) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = row0 + 4 * g + e;
-            s[j][e] = (n < NT && S0) ? S0[(bh * Dv + row) * DK + 16 * n + r] : 0.f;
-            if (n < NT) Ss[(4 * g + e) * LDSS + 16 * n + r] = s[j][e];
+            for (int e = 0; e < 4; ++e) {
+                const int row = row0 + 4 * g + e;
+                if (S0) s[j][e] = S0[(bh * Dv + row) * DK + 16 * n + r];
+                Ss[(4 * g + e) * LDSS + 16 * n + r] = s[j][e];
+            }
         }
     }
     // M_p and this lane's H_p entries travel in registers one step ahead
-    float4 mreg[NMV];
+    // (with d_k = 16 some threads hold no part of M: they load a valid
+    // element and do not store it)
+    f32x4 mreg[NMV];
     f32x4 hreg[TPW];
-    auto fetch = [&](int p) {
-        const int64_t seg = b * P + p;
-        const float4 *mp = reinterpret_cast<const float4 *>(M + (seg * H + h) * DK * DK);
-#pragma unroll
-        for (int u = 0; u < NMV; ++u) {
-            const int e = tid + 256 * u;
-            mreg[u] = e < nmv ? mp[e] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        const float *hp = Hs + ((seg * H + h) * Dv + row0) * DK;
-#pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-            const int n = wave + 4 * j;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) hreg[j][e] = n < NT ? hp[(4 * g + e) * DK + 16 * n + r] : 0.f;
-        }
-    };
-    if (P > 0) fetch(0);
+    if (P > 0) chain_fetch<DK, NMV, TPW, MEXACT, FULL>(mreg, hreg, M, Hs, b * P, H, h, Dv, row0, wave, tid, g, r);
     for (int p = 0; p < P; ++p) {
         const int64_t seg = b * P + p;
         float *hp = Hs + ((seg * H + h) * Dv + row0) * DK;
@@ -152,46 +179,52 @@ __global__ __launch_bounds__(256) void seg_chain_kernel(float *Hs, const float *
 #pragma unroll
         for (int u = 0; u < NMV; ++u) {
             const int e = tid + 256 * u;
-            if (e < nmv) {
+            if (MEXACT || e < nmv) {
                 const int row = 4 * e / DK, col = 4 * e % DK;
-                *reinterpret_cast<float4 *>(Ms + row * LDM + col) = mreg[u];
+                *reinterpret_cast<f32x4 *>(Ms + row * LDM + col) = mreg[u];
             }
         }
         f32x4 acc[TPW][2];
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
             const int n = wave + 4 * j;
-            acc[j][0] = hreg[j];
+            acc[j][0] = has(j) ? hreg[j] : zero4();
             acc[j][1] = zero4();
-            if (n < NT) {
+            if (has(j)) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) hp[(4 * g + e) * DK + 16 * n + r] = s[j][e];
             }
         }
-        __syncthreads();
-        if (p + 1 < P) fetch(p + 1);
-        // acc += S M_p: A = S rows (lane (g, r): S[r][k0 + g]), B = M_p
-        // (lane (g, r): M[k0 + g][16 n + r]); two chains per tile
-#pragma unroll 4
-        for (int k0 = 0; k0 < DK; k0 += 8) {
-            const float a0 = Ss[r * LDSS + k0 + g], a1 = Ss[r * LDSS + k0 + 4 + g];
+        // LDS only: the global loads of the next step and the stores of
+        // S_in(p) stay in flight across the barriers (each thread reads and
+        // writes only its own entries of Hs)
+        lds_barrier();
+        if (p + 1 < P)
+            chain_fetch<DK, NMV, TPW, MEXACT, FULL>(mreg, hreg, M, Hs, b * P + p + 1, H, h, Dv, row0,
+                                                    wave, tid, g, r);
+        // acc += S M_p: A = S rows (lane (g, r): S[r][4i + g]), B = M_p
+        // (lane (g, r): M[4i + g][16 n + r]); two chains per tile
+        float a[NK], bm[TPW][NK];
 #pragma unroll
-            for (int j = 0; j < TPW; ++j) {
-                const int n = wave + 4 * j;
-                if (n < NT) {
-                    acc[j][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                        a0, Ms[(k0 + g) * LDM + 16 * n + r], acc[j][0], 0, 0, 0);
-                    acc[j][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                        a1, Ms[(k0 + 4 + g) * LDM + 16 * n + r], acc[j][1], 0, 0, 0);
-                }
-            }
+        for (int i = 0; i < NK; ++i) a[i] = Ss[r * LDSS + 4 * i + g];
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int n = has(j) ? wave + 4 * j : 0;
+#pragma unroll
+            for (int i = 0; i < NK; ++i) bm[j][i] = Ms[(4 * i + g) * LDM + 16 * n + r];
         }
-        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NK; ++i)
+#pragma unroll
+            for (int j = 0; j < TPW; ++j)
+                acc[j][i & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], bm[j][i], acc[j][i & 1],
+                                                                     0, 0, 0);
+        lds_barrier();
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
             const int n = wave + 4 * j;
             s[j] = acc[j][0] + acc[j][1];
-            if (n < NT) {
+            if (has(j)) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) Ss[(4 * g + e) * LDSS + 16 * n + r] = s[j][e];
             }
@@ -201,7 +234,7 @@ __global__ __launch_bounds__(256) void seg_chain_kernel(float *Hs, const float *
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
             const int n = wave + 4 * j;
-            if (n < NT) {
+            if (has(j)) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     S_T[(bh * Dv + row0 + 4 * g + e) * DK + 16 * n + r] = s[j][e];
