@@ -226,14 +226,6 @@ __device__ __forceinline__ void put_tile(DT *M, int ld, int m0, int n0, const f3
     }
 }
 
-// Sum over the 64 lanes of the wave, every lane receiving it.
-__device__ __forceinline__ float wave_sum(float x) {
-    x = group_sum<16>(x);
-    x += __shfl_xor(x, 16, 64);
-    x += __shfl_xor(x, 32, 64);
-    return x;
-}
-
 // Product X Y of two 16x16 matrices held in D layout, given X^T in D layout
 // (the A operand) and Y (the B operand).
 template <typename DT>
@@ -513,10 +505,8 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                 sg += frag_get(qv, i) * aq[i] - frag_get(kv, i) * an[i];
                 if (ed) sr += frag_get(kv, i) * (*ed)[i];
             }
-            sg += __shfl_xor(sg, 16, 64);
-            sg += __shfl_xor(sg, 32, 64);
-            sr += __shfl_xor(sr, 16, 64);
-            sr += __shfl_xor(sr, 32, 64);
+            sg = xor32_sum(xor16_sum(sg));
+            sr = xor32_sum(xor16_sum(sr));
             if (g == 0) {
                 const float pr = sm.gt.rto[t] * sr;
                 float pd = sm.gt.gam[t] * sg - pr;
@@ -844,8 +834,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                     acc[i] = x > y ? acc[i] * __expf(sm.gt.gb[x] - sm.gt.gb[y]) : acc[i];
                 }
                 float cs = wv[0] + wv[1] + wv[2] + wv[3];
-                cs += __shfl_xor(cs, 16, 64);
-                cs += __shfl_xor(cs, 32, 64);
+                cs = xor32_sum(xor16_sum(cs));
                 if (g == 0) sm.gt.wcol[j][r] = cs;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {

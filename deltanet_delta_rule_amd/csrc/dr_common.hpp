@@ -66,6 +66,22 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// x plus its value in lane i xor 16 (xor 32), on the cross-row lane swaps of
+// gfx950: two register-to-register swaps instead of an LDS permute.  Every
+// lane of the wave must be active.
+__device__ __forceinline__ float xor16_sum(float x) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// Sum over the 64 lanes of the wave, every lane receiving it (all lanes
+// active).
+__device__ __forceinline__ float wave_sum(float x) { return xor32_sum(xor16_sum(group_sum<16>(x))); }
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
 

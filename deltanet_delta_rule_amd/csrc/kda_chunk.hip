@@ -52,13 +52,6 @@ __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(
 
 __device__ __forceinline__ unsigned pk2(float a, float b) { return pk_bf16(a, b); }
 
-// Sum over the 64 lanes of the wave, every lane receiving it.
-__device__ __forceinline__ float wave_sum(float v) {
-    v = group_sum<16>(v);
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
-}
 __device__ __forceinline__ float2 fmul2(float2 a, float2 b) { return make_float2(a.x * b.x, a.y * b.y); }
 
 // Factor of token s (0..7) of an 8-token quarter at level L <= 4 (its
