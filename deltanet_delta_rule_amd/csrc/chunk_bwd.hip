@@ -81,14 +81,14 @@ struct BwdCfg {
     static constexpr int PAD = 16 / (int)sizeof(DT);
     static constexpr int LDK = DK + PAD;          // K, Q rows (tokens x d_k)
     static constexpr int LDV = DV + PAD;          // V, dO, E, dV rows (tokens x d_v)
-    static constexpr int LDS_ = DV + PAD;         // dS^T rows (d_k x d_v)
+    static constexpr int LDS_ = DK + PAD;         // dS_{c+1} rows (d_v x d_k, like S_c)
     static constexpr int LDSK = DK + PAD;         // S_c rows (d_v x d_k)
     static constexpr int LDC = C + PAD;           // C x C matrices
     // dS_{c+1}^T gets its own LDS buffer unless that overflows LDS (fp32 with
     // d_k = d_v = 128); then it reuses the S_c^T buffer in a second pass.
-    static constexpr int BASE = (int)sizeof(DT) * (2 * C * LDK + 4 * C * LDV + DV * LDSK + 5 * C * LDC) +
-                                4 * C * (1 + NW);
-    static constexpr bool DBUF = BASE + (int)sizeof(DT) * DK * LDS_ + 256 <= 160 * 1024;
+    static constexpr int BASE = (int)sizeof(DT) * (4 * C * LDK + 4 * C * LDV + DV * LDSK + 6 * C * LDC) +
+                                4 * C * (2 + NW);
+    static constexpr bool DBUF = BASE + (int)sizeof(DT) * DV * LDS_ + 256 <= 160 * 1024;
 };
 
 // Gated rule: the chunk's decays and the parts of dL/db, b the in-chunk
@@ -97,10 +97,10 @@ struct BwdCfg {
 // first), so they are only read behind a barrier.
 template <int C, int NW, int NJ, int KT, bool GATED>
 struct BwdGate {
-    float gb[C], gam[C], rto[C];      // b, exp(b), exp(b_last - b)
+    float gb[2][C], gam[2][C], rto[2][C];  // b, exp(b), exp(b_last - b), by chunk parity
     float pdb[KT][C];                 // gamma_t dL/dgamma_t - rho_t dL/drho_t, per key tile
     float prd[KT][C];                 // rho_t dL/drho_t, per key tile
-    float dgc[NW][4];                 // gamma_last dL/dgamma_last, per wave and row group
+    float dgc[NW];                    // gamma_last dL/dgamma_last, per wave
     float wrow[2 * NJ][16], wcol[2 * NJ][16];  // row / column sums of W per C x C tile job
 };
 template <int C, int NW, int NJ, int KT>
@@ -109,18 +109,19 @@ struct BwdGate<C, NW, NJ, KT, false> {};
 template <typename DT, int DK, int DV, int C, bool GATED>
 struct BwdSmem {
     typedef BwdCfg<DT, DK, DV, C> G;
-    DT Ks[C * G::LDK], Qs[C * G::LDK];
+    DT Ks[2][C * G::LDK], Qs[2][C * G::LDK];     // by chunk parity (the next chunk's
+                                                  // Gram tiles overlap this chunk's dQ, dK)
     DT Vs[C * G::LDV], Os[C * G::LDV];            // V, dO
     DT Es[C * G::LDV], Rb[C * G::LDV];            // E, dV
     DT Sb[DV * G::LDSK];                          // S_c (rows: value index); second
                                                   // pass without DBUF: dS_{c+1}
-    DT Db[G::DBUF ? DK * G::LDS_ : 8];            // dS_{c+1}^T (DBUF)
+    DT Db[G::DBUF ? DV * G::LDS_ : 8];            // dS_{c+1} (DBUF; rows: value index)
     DT Pm[C * G::LDC];                            // Q K^T (.) M
-    DT Gl[C * G::LDC];                            // tril(K K^T, -1)
+    DT Gl[2][C * G::LDC];                         // tril(K K^T, -1), by chunk parity
     DT Tm[C * G::LDC];                            // (I + A)^{-1}
     DT Dm[C * G::LDC];                            // dO E^T (.) M
     DT Gs[C * G::LDC];                            // dG + dG^T
-    float betas[C];
+    float betas[2][C];
     float dbp[G::NW][C];                          // per-wave parts of dbeta
     BwdGate<C, G::NW, G::NT * (G::NT + 1) / 2, G::KT, GATED> gt;
 };
@@ -210,6 +211,13 @@ __device__ __forceinline__ void tile_cc(f32x4 &acc, const DT *At, int lda, int m
         frag_cols16(B, ldb, k0 + 16 * i, n0, lane, fb[i]);
     }
     mk_n<DT, NK>(acc, fa, fb);
+}
+
+// x from the lane N places further in its row of 16 lanes (DPP row shift;
+// zero past the row's end).
+template <int N>
+__device__ __forceinline__ float row_shl(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + N, 0xF, 0xF, true));
 }
 
 // Store a D-layout tile (lane (g, r): rows 4g + i, column r) into a
@@ -308,9 +316,9 @@ struct ChunkPrefetch {
     RowPrefetch<DT, DV, DK, NTHR> s;
     DT b;      // beta of token tid (zero past the chunk's valid length)
     float gv;  // log gate of token tid (gated rule; zero past the valid length)
-    // Part 0: S_c; part 1: K and Q; part 2: V, dO and beta (issued at three
-    // points of a chunk, so that no single point floods the vector memory
-    // path).
+    // Part 0: S_c; part 1: K, Q, beta (and the log gates); part 2: V and dO
+    // (issued at three points of a chunk, so that no single point floods the
+    // vector memory path).
     template <int P>
     __device__ __forceinline__ void load_part(const DT *kk, const DT *qq, const DT *vv,
                                               const DT *oo, const DT *bb, const float *gg,
@@ -321,10 +329,6 @@ struct ChunkPrefetch {
         if constexpr (P == 1) {
             k.load(kk + (tok0 * H + h) * DK, rk, len, tid);
             q.load(qq + (tok0 * H + h) * DK, rk, len, tid);
-        }
-        if constexpr (P == 2) {
-            v.load(vv + (tok0 * H + h) * DV, rv, len, tid);
-            o.load(oo + (tok0 * H + h) * DV, rv, len, tid);
             // through a range-checked resource like the tiles, so that nothing
             // waits for this load before the chunk's LDS stores
             const auto rb = make_rsrc(bb + tok0 * H + h, len > 0 ? ((len - 1) * H + 1) * (int)sizeof(DT) : 0);
@@ -333,6 +337,10 @@ struct ChunkPrefetch {
                 const auto rg = make_rsrc(gg + tok0 * H + h, len > 0 ? ((len - 1) * H + 1) * 4 : 0);
                 gv = buf_load_elem<float>(rg, tid < len ? tid * H * 4 : 0x7ffffff0);
             }
+        }
+        if constexpr (P == 2) {
+            v.load(vv + (tok0 * H + h) * DV, rv, len, tid);
+            o.load(oo + (tok0 * H + h) * DV, rv, len, tid);
         }
     }
     __device__ __forceinline__ void load(const DT *kk, const DT *qq, const DT *vv, const DT *oo,
@@ -390,7 +398,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
 
     // upper tiles of the C x C matrices stay zero
     for (int i = tid; i < C * LDC; i += nthr) {
-        sm.Pm[i] = sm.Gl[i] = sm.Tm[i] = sm.Dm[i] = sm.Gs[i] = from_f32<DT>(0.f);
+        sm.Pm[i] = sm.Gl[0][i] = sm.Gl[1][i] = sm.Tm[i] = sm.Dm[i] = sm.Gs[i] = from_f32<DT>(0.f);
     }
     // dS^T of this wave's value columns: tile s holds dS^T[16s + 4g + i][v0 + r]
     f32x4 Dt[KT];
@@ -467,19 +475,21 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                     if (jj == tt) db -= sm.gt.wcol[jb][tl];
                 }
             }
+            float gc = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) gc += sm.gt.dgc[ww];
             const float srd = wave_sum(rd);
-            if (lane == C - 1) {
-                float gc = 0.f;
-#pragma unroll
-                for (int ww = 0; ww < NW; ++ww)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) gc += sm.gt.dgc[ww][e];
-                db += gc + srd;
-            }
-#pragma unroll
-            for (int d = 1; d < C; d <<= 1) {
-                const float y = __shfl_down(db, d, 64);
-                if (lane + d < C) db += y;
+            if (lane == C - 1) db += gc + srd;
+            // reverse inclusive scan over the chunk's tokens: within each row
+            // of 16 lanes by row shifts (lanes past a row's end add zero),
+            // then rows 0 .. add the totals of the rows after them
+            db += row_shl<1>(db);
+            db += row_shl<2>(db);
+            db += row_shl<4>(db);
+            db += row_shl<8>(db);
+            if constexpr (C > 16) {
+                const float tail = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(db), 16));
+                if (lane < 16) db += tail;
             }
             const int flen = min(C, T - cc * C);
             if (lane < flen) dg[(((int64_t)b * T + cc * C) + lane) * H + h] = db;
@@ -491,14 +501,14 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
     //   dL/drho_t   = sum_k K (.) E dS_{c+1}              (= sum_v E (.) K dS_{c+1}^T)
     // from aq = (dO S_c)^T, an = (dV S_c)^T and ed = (E dS_{c+1})^T before
     // their decays.  add: accumulate onto the part written by the first pass.
-    auto gate_part = [&](int j, int mt, const f32x4 &aq, const f32x4 &an, const f32x4 *ed,
+    auto gate_part = [&](int cb, int j, int mt, const f32x4 &aq, const f32x4 &an, const f32x4 *ed,
                          bool add) {
         if constexpr (GATED) {
             const int t = 16 * mt + r;
             const typename Frag<DT>::k16 qv =
-                *reinterpret_cast<const typename Frag<DT>::k16 *>(sm.Qs + t * LDK + 16 * j + 4 * g);
+                *reinterpret_cast<const typename Frag<DT>::k16 *>(sm.Qs[cb] + t * LDK + 16 * j + 4 * g);
             const typename Frag<DT>::k16 kv =
-                *reinterpret_cast<const typename Frag<DT>::k16 *>(sm.Ks + t * LDK + 16 * j + 4 * g);
+                *reinterpret_cast<const typename Frag<DT>::k16 *>(sm.Ks[cb] + t * LDK + 16 * j + 4 * g);
             float sg = 0.f, sr = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -508,8 +518,8 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
             sg = xor32_sum(xor16_sum(sg));
             sr = xor32_sum(xor16_sum(sr));
             if (g == 0) {
-                const float pr = sm.gt.rto[t] * sr;
-                float pd = sm.gt.gam[t] * sg - pr;
+                const float pr = sm.gt.rto[cb][t] * sr;
+                float pd = sm.gt.gam[cb][t] * sg - pr;
                 if (add) pd += sm.gt.pdb[j][t];
                 sm.gt.pdb[j][t] = pd;
                 sm.gt.prd[j][t] = pr;
@@ -525,26 +535,13 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                                                      hs + (head * N + cn) * DV * DK,
                                                      (int64_t)b * T + tp, h, H, min(C, T - tp), tid);
     };
-    if (N > 0) {
-        const int t0 = (N - 1) * C;
-        pf.load(k, q, v, dout, beta, GATED ? gl : nullptr, hs + (head * N + N - 1) * DV * DK,
-                (int64_t)b * T + t0, h, H, min(C, T - t0), tid);
-    }
-    for (int c = N - 1; c >= 0; --c) {
-        const int len = min(C, T - c * C);
-        const int64_t tok0 = (int64_t)b * T + c * C;
-        __syncthreads();
-        // ---------------------------------------------------------------- load
-        pf.k.store(sm.Ks, LDK, tid);
-        pf.q.store(sm.Qs, LDK, tid);
-        pf.v.store(sm.Vs, LDV, tid);
-        pf.o.store(sm.Os, LDV, tid);
-        pf.s.store(sm.Sb, LDSK, tid);
-        if (GATED && w == 0 && c + 1 < N) finalize_dg(c + 1);
-        {
-            const float bt = to_f32(pf.b);  // converted by every lane (see RowPrefetch::store)
-            if (tid < C) sm.betas[tid] = bt;
-        }
+    // K, Q and beta of chunk cc (and its decays) from the prefetch registers
+    // into buffer set bb; every lane converts beta (see RowPrefetch::store).
+    auto stage_kqb = [&](int bb) {
+        pf.k.store(sm.Ks[bb], LDK, tid);
+        pf.q.store(sm.Qs[bb], LDK, tid);
+        const float bt = to_f32(pf.b);
+        if (tid < C) sm.betas[bb][tid] = bt;
         if constexpr (GATED) {
             // in-chunk prefix sums b of the log gate and the two decays; tokens
             // past the valid length have g = 0, so b_last is the last valid
@@ -558,75 +555,121 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                 }
                 const float bl = __shfl(x, C - 1, 64);
                 if (lane < C) {
-                    sm.gt.gb[lane] = x;
-                    sm.gt.gam[lane] = __expf(x);
-                    sm.gt.rto[lane] = __expf(bl - x);
+                    sm.gt.gb[bb][lane] = x;
+                    sm.gt.gam[bb][lane] = __expf(x);
+                    sm.gt.rto[bb][lane] = __expf(bl - x);
                 }
             }
         }
-        __syncthreads();
+    };
+    // off-diagonal block of the inverse (one wave): T_10 = -T_11 (A_10 T_00),
+    // A_10 = diag(beta_1) G_10
+    auto t10 = [&](int bb) {
+        typename Frag<DT>::k16 fa, fb;
+        f32x4 m1 = zero4();
+        frag_rows(sm.Gl[bb], LDC, 16, 0, lane, fa);
+        {
+            f32x4 tmp;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tmp[i] = frag_get(fa, i) * sm.betas[bb][16 + r];
+            cvt4(tmp, fa);
+        }
+        frag_cols16(sm.Tm, LDC, 0, 0, lane, fb);
+        mk<DT>(m1, fa, fb);
+        f32x4 t10v = zero4();
+        frag_rows(sm.Tm, LDC, 16, 16, lane, fa);
+        cvt4(m1, fb);
+        mk<DT>(t10v, fa, fb);
+        put_tile(sm.Tm, LDC, 16, 0, -t10v, lane, [](int, int) { return true; });
+    };
 
-        // ---------------------------------------------------- Gram and inverse
-        if (c > 0) prefetch(std::integral_constant<int, 0>(), c - 1);
-        // jobs: lower tiles (ti >= tj) of G = K K^T and P = Q K^T
-        constexpr int NJ = NT * (NT + 1) / 2;
-        for (int j = w; j < 2 * NJ; j += NW) {
-            const bool isP = j >= NJ;
-            int jj = isP ? j - NJ : j, ti = 0;
-            while (jj > ti) { jj -= ti + 1; ++ti; }
-            const int tj = jj;
-            f32x4 acc = zero4();
-            tile_rr<DT, KT>(acc, isP ? sm.Qs : sm.Ks, LDK, 16 * ti, sm.Ks, LDK, 16 * tj, 0, lane);
-            if constexpr (GATED) {
-                // decay exp(b_hi - b_lo) between the later and the earlier token
-                // (symmetric, as the diagonal blocks below use both triangles)
+    // Gram tiles of the chunk in buffer set bb (K K^T and Q K^T, lower tiles),
+    // into Gl[bb], Tm and Pm.  One tile, decayed for the gated rule:
+    auto gram_tile = [&](int bb, bool isP, int ti, int tj) {
+        f32x4 acc = zero4();
+        tile_rr<DT, KT>(acc, isP ? sm.Qs[bb] : sm.Ks[bb], LDK, 16 * ti, sm.Ks[bb], LDK, 16 * tj, 0, lane);
+        if constexpr (GATED) {
+            // decay exp(b_hi - b_lo) between the later and the earlier token
+            // (symmetric, as the diagonal blocks use both triangles)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int x = 16 * ti + 4 * g + i, y = 16 * tj + r;
-                    acc[i] *= __expf(sm.gt.gb[max(x, y)] - sm.gt.gb[min(x, y)]);
-                }
+            for (int i = 0; i < 4; ++i) {
+                const int x = 16 * ti + 4 * g + i, y = 16 * tj + r;
+                acc[i] *= __expf(sm.gt.gb[bb][max(x, y)] - sm.gt.gb[bb][min(x, y)]);
             }
+        }
+        return acc;
+    };
+    // diagonal block ti of G and its inverse T_ii = (I + A_ii)^{-1}
+    auto diag_job = [&](int bb, int ti) {
+        const f32x4 acc = gram_tile(bb, false, ti, ti);
+        put_tile(sm.Gl[bb], LDC, 16 * ti, 16 * ti, acc, lane, [](int x, int y) { return x > y; });
+        // A and A^T of the diagonal block: A[x][y] = beta_x G[x][y], x > y
+        f32x4 a, at;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int x = 4 * g + i;
+            a[i] = x > r ? sm.betas[bb][16 * ti + x] * acc[i] : 0.f;
+            at[i] = r > x ? sm.betas[bb][16 * ti + r] * acc[i] : 0.f;  // G symmetric
+        }
+        const f32x4 tinv = inv_unit_lower<DT>(a, at, lane);
+        put_tile(sm.Tm, LDC, 16 * ti, 16 * ti, tinv, lane, [](int x, int y) { return x >= y; });
+    };
+    // the diagonal blocks on the last waves (idle in the C x C phase)
+    auto diag_jobs = [&](int bb) {
+        for (int ti = NW - 1 - w; ti >= 0 && ti < NT; ti += NW) diag_job(bb, ti);
+    };
+    // the other tiles (G below the diagonal, all of P) dealt to waves
+    // 0 .. nwj-1; then T_10 = -T_11 (A_10 T_00), A_10 = diag(beta_1) G_10, on
+    // the wave that formed G_10 (the diagonal inverses are done by then)
+    constexpr int NOFF = NT * (NT - 1) / 2;  // tiles of G below the diagonal
+    constexpr int NJ = NT * (NT + 1) / 2;    // lower tiles of a C x C matrix
+    auto other_jobs = [&](int bb, int nwj) {
+        for (int j = w; j < NOFF + NJ; j += nwj) {
+            const bool isP = j >= NOFF;
+            int jj = isP ? j - NOFF : j, ti = isP ? 0 : 1;
             if (isP) {
-                put_tile(sm.Pm, LDC, 16 * ti, 16 * tj, acc, lane, [](int x, int y) { return x >= y; });
+                while (jj > ti) { jj -= ti + 1; ++ti; }
             } else {
-                put_tile(sm.Gl, LDC, 16 * ti, 16 * tj, acc, lane, [](int x, int y) { return x > y; });
-                if (ti == tj) {
-                    // A and A^T of the diagonal block: A[x][y] = beta_x G[x][y], x > y
-                    f32x4 a, at;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int x = 4 * g + i;
-                        a[i] = x > r ? sm.betas[16 * ti + x] * acc[i] : 0.f;
-                        at[i] = r > x ? sm.betas[16 * ti + r] * acc[i] : 0.f;  // G symmetric
-                    }
-                    const f32x4 tinv = inv_unit_lower<DT>(a, at, lane);
-                    put_tile(sm.Tm, LDC, 16 * ti, 16 * ti, tinv, lane, [](int x, int y) { return x >= y; });
-                }
+                while (jj >= ti) { jj -= ti; ++ti; }
             }
+            const int tj = jj;
+            const f32x4 acc = gram_tile(bb, isP, ti, tj);
+            if (isP) put_tile(sm.Pm, LDC, 16 * ti, 16 * tj, acc, lane, [](int x, int y) { return x >= y; });
+            else put_tile(sm.Gl[bb], LDC, 16 * ti, 16 * tj, acc, lane, [](int x, int y) { return x > y; });
         }
-        __syncthreads();
         if constexpr (NT == 2) {
-            // off-diagonal block: T_10 = -T_11 (A_10 T_00), A_10 = diag(beta_1) G_10
-            if (w == 0) {
-                typename Frag<DT>::k16 fa, fb;
-                f32x4 m1 = zero4();
-                frag_rows(sm.Gl, LDC, 16, 0, lane, fa);
-                {
-                    f32x4 tmp;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) tmp[i] = frag_get(fa, i) * sm.betas[16 + r];
-                    cvt4(tmp, fa);
-                }
-                frag_cols16(sm.Tm, LDC, 0, 0, lane, fb);
-                mk<DT>(m1, fa, fb);
-                f32x4 t10 = zero4();
-                frag_rows(sm.Tm, LDC, 16, 16, lane, fa);
-                cvt4(m1, fb);
-                mk<DT>(t10, fa, fb);
-                put_tile(sm.Tm, LDC, 16, 0, -t10, lane, [](int, int) { return true; });
-            }
-            __syncthreads();
+            if (w == 0) t10(bb);
         }
+    };
+    // The last chunk's inputs, its K, Q, beta staged and its Gram tiles;
+    // inside the loop the next chunk's are staged at the end of the per-wave
+    // phase, its diagonal Gram blocks and their inverses formed by the last
+    // waves during the C x C phase (where they have no tile), and its other
+    // tiles and T_10 by the waves that finish their dQ, dK tiles first (waves
+    // 0 .. 3: the second wave on each SIMD runs behind).
+    if (N > 0) {
+        const int t0 = (N - 1) * C;
+        pf.load(k, q, v, dout, beta, GATED ? gl : nullptr, hs + (head * N + N - 1) * DV * DK,
+                (int64_t)b * T + t0, h, H, min(C, T - t0), tid);
+        stage_kqb((N - 1) & 1);
+        __syncthreads();
+        diag_jobs((N - 1) & 1);
+        __syncthreads();
+        other_jobs((N - 1) & 1, NW);
+    }
+    constexpr int NWJ = NW < 4 ? NW : 4;  // waves that form the next chunk's Gram tiles
+    for (int c = N - 1; c >= 0; --c) {
+        const int len = min(C, T - c * C);
+        const int64_t tok0 = (int64_t)b * T + c * C;
+        const int cb = c & 1;  // buffer set of this chunk's K, Q, beta, decays
+        __syncthreads();
+        // ---------------------------------------------------------------- load
+        pf.v.store(sm.Vs, LDV, tid);
+        pf.o.store(sm.Os, LDV, tid);
+        pf.s.store(sm.Sb, LDSK, tid);
+        if (c > 0) prefetch(std::integral_constant<int, 0>(), c - 1);
+        if (GATED && w == 0 && c + 1 < N) finalize_dg(c + 1);
+        __syncthreads();
 
         // ------------------------------------------- per-wave value columns
         if (c > 0) prefetch(std::integral_constant<int, 1>(), c - 1);
@@ -647,8 +690,8 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                 for (int s = 0; s < KT; ++s)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) a += Dt[s][i] * frag_get(fs[s], i);
-                a = group_sum<16>(a);
-                if (r == 0) sm.gt.dgc[w][g] = a * sm.gt.gam[C - 1];
+                a = wave_sum(a);
+                if (lane == 0) sm.gt.dgc[w] = a * sm.gt.gam[cb][C - 1];
             }
             f32x4 dE[NT];
 #pragma unroll
@@ -656,14 +699,14 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                 f32x4 x = zero4();
                 typename Frag<DT>::k16 fk[KT];
 #pragma unroll
-                for (int s = 0; s < KT; ++s) frag_rows(sm.Ks, LDK, 16 * mt, 16 * s, lane, fk[s]);
+                for (int s = 0; s < KT; ++s) frag_rows(sm.Ks[cb], LDK, 16 * mt, 16 * s, lane, fk[s]);
                 mk_n<DT, KT>(x, fk, fs);
                 typename Frag<DT>::k16 fvv;
                 frag_cols16(sm.Vs, LDV, 16 * mt, v0, lane, fvv);
                 if constexpr (GATED) {
                     // R = V - diag(gamma) K S_c^T
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) x[i] *= sm.gt.gam[16 * mt + 4 * g + i];
+                    for (int i = 0; i < 4; ++i) x[i] *= sm.gt.gam[cb][16 * mt + 4 * g + i];
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) R[mt][i] = frag_get(fvv, i) - x[i];
@@ -685,7 +728,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                     f32x4 kd = zero4();
                     mk_n<DT, KT>(kd, fk, fd);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) dE[mt][i] += sm.gt.rto[16 * mt + 4 * g + i] * kd[i];
+                    for (int i = 0; i < 4; ++i) dE[mt][i] += sm.gt.rto[cb][16 * mt + 4 * g + i] * kd[i];
                 } else {
                     mk_n<DT, KT>(dE[mt], fk, fd);
                 }
@@ -696,7 +739,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
             for (int mt = 0; mt < NT; ++mt) {
                 f32x4 rb;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) rb[i] = sm.betas[16 * mt + 4 * g + i] * R[mt][i];
+                for (int i = 0; i < 4; ++i) rb[i] = sm.betas[cb][16 * mt + 4 * g + i] * R[mt][i];
                 cvt4(rb, frb[mt]);
             }
 #pragma unroll
@@ -735,7 +778,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                 typename Frag<DT>::k16 fa;
 #pragma unroll
                 for (int kt = 0; kt <= mt; ++kt) {
-                    frag_rows(sm.Gl, LDC, 16 * mt, 16 * kt, lane, fa);
+                    frag_rows(sm.Gl[cb], LDC, 16 * mt, 16 * kt, lane, fa);
                     mk<DT>(ge, fa, fe[kt]);
                 }
                 f32x4 zy;
@@ -753,7 +796,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int t = 16 * mt + 4 * g + i;
-                    dvv[i] = sm.betas[t] * Z[mt][i];
+                    dvv[i] = sm.betas[cb][t] * Z[mt][i];
                     sm.Es[t * LDV + v0 + r] = from_f32<DT>(E[mt][i]);
                     sm.Rb[t * LDV + v0 + r] = from_f32<DT>(dvv[i]);
                 }
@@ -768,13 +811,15 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
             for (int s2 = 0; s2 < KT; ++s2) Dold[s2] = Dt[s2];
         }
         {
+            // lane (g, r) holds dS[v0 + r][16 s + 4 g .. + 3]: one vector per tile
+            if constexpr (G::DBUF) {
 #pragma unroll
-            for (int s = 0; s < KT; ++s)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if constexpr (G::DBUF)
-                        sm.Db[(16 * s + 4 * g + i) * LDS_ + v0 + r] = from_f32<DT>(Dt[s][i]);
+                for (int s = 0; s < KT; ++s) {
+                    typename Frag<DT>::k16 x;
+                    cvt4(Dt[s], x);
+                    *reinterpret_cast<typename Frag<DT>::k16 *>(sm.Db + (v0 + r) * LDS_ + 16 * s + 4 * g) = x;
                 }
+            }
             typename Frag<DT>::k16 fdv[NT], fo[NT];
 #pragma unroll
             for (int mt = 0; mt < NT; ++mt) {
@@ -785,7 +830,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                     f32x4 od;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float gm = sm.gt.gam[16 * mt + 4 * g + i];
+                        const float gm = sm.gt.gam[cb][16 * mt + 4 * g + i];
                         nz[i] *= gm;
                         od[i] = frag_get(fo[mt], i) * gm;
                     }
@@ -794,7 +839,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                 cvt4(nz, fdv[mt]);
             }
             if constexpr (GATED) {
-                const float gc = sm.gt.gam[C - 1];
+                const float gc = sm.gt.gam[cb][C - 1];
 #pragma unroll
                 for (int s = 0; s < KT; ++s) Dt[s] = Dt[s] * gc;
             }
@@ -803,16 +848,20 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                 typename Frag<DT>::k16 fa[NT], fb[NT];
 #pragma unroll
                 for (int kt = 0; kt < NT; ++kt) {
-                    frag_cols16(sm.Qs, LDK, 16 * kt, 16 * s, lane, fa[kt]);
-                    frag_cols16(sm.Ks, LDK, 16 * kt, 16 * s, lane, fb[kt]);
+                    frag_cols16(sm.Qs[cb], LDK, 16 * kt, 16 * s, lane, fa[kt]);
+                    frag_cols16(sm.Ks[cb], LDK, 16 * kt, 16 * s, lane, fb[kt]);
                 }
                 mk_n<DT, NT>(Dt[s], fa, fo);
                 mk_n<DT, NT>(Dt[s], fb, fdv);
             }
         }
+        // the next chunk's K, Q, beta (loaded since the start of this phase)
+        if (c > 0) stage_kqb(cb ^ 1);
         __syncthreads();
 
         // ---------------------- C x C products over all value columns, dbeta
+        // (and the next chunk's diagonal Gram blocks and their inverses)
+        if (c > 0) diag_jobs(cb ^ 1);
         for (int j = w; j < 2 * NJ; j += NW) {
             const bool isD = j < NJ;  // dO E^T, else dV E^T
             int jj = isD ? j : j - NJ, ti = 0;
@@ -830,8 +879,8 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                 for (int i = 0; i < 4; ++i) {
                     const int x = 16 * ti + 4 * g + i, y = 16 * tj + r;
                     const float a = isD ? acc[i] : -acc[i];
-                    wv[i] = x > y ? a * to_f32((isD ? sm.Pm : sm.Gl)[x * LDC + y]) : 0.f;
-                    acc[i] = x > y ? acc[i] * __expf(sm.gt.gb[x] - sm.gt.gb[y]) : acc[i];
+                    wv[i] = x > y ? a * to_f32((isD ? sm.Pm : sm.Gl[cb])[x * LDC + y]) : 0.f;
+                    acc[i] = x > y ? acc[i] * __expf(sm.gt.gb[cb][x] - sm.gt.gb[cb][y]) : acc[i];
                 }
                 float cs = wv[0] + wv[1] + wv[2] + wv[3];
                 cs = xor32_sum(xor16_sum(cs));
@@ -882,12 +931,12 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
             for (int i = 0; i < VT; ++i) frag_cols16(sm.Sb, LDSK, 16 * i, 16 * j, lane, fs[i]);
 #pragma unroll
             for (int i = 0; i < NT; ++i) {
-                frag_cols16(sm.Ks, LDK, 16 * i, 16 * j, lane, fkc[i]);
-                frag_cols16(sm.Qs, LDK, 16 * i, 16 * j, lane, fqc[i]);
+                frag_cols16(sm.Ks[cb], LDK, 16 * i, 16 * j, lane, fkc[i]);
+                frag_cols16(sm.Qs[cb], LDK, 16 * i, 16 * j, lane, fqc[i]);
             }
             if constexpr (G::DBUF) {
 #pragma unroll
-                for (int i = 0; i < VT; ++i) frag_rows(sm.Db, LDS_, 16 * j, 16 * i, lane, fdb[i]);
+                for (int i = 0; i < VT; ++i) frag_cols16(sm.Db, LDS_, 16 * i, 16 * j, lane, fdb[i]);
             }
 #pragma unroll
             for (int u = 0; u < NMU; ++u) {
@@ -902,7 +951,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                     for (int i = 0; i < NT; ++i) frag_rows(sm.Dm, LDC, 16 * mt, 16 * i, lane, fm[i]);
                     mk_n<DT, VT>(aq, fs, fa);
                     const f32x4 aq0 = aq;
-                    if constexpr (GATED) aq = aq * sm.gt.gam[16 * mt + r];  // token 16 mt + r
+                    if constexpr (GATED) aq = aq * sm.gt.gam[cb][16 * mt + r];  // token 16 mt + r
                     mk_n<DT, NT>(aq, fkc, fm);
                     // dK = -dV S_c + E dS_{c+1} + Gs K + Dm^T Q
                     f32x4 an = zero4(), ak = zero4();
@@ -913,12 +962,12 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
 #pragma unroll
                         for (int i = 0; i < VT; ++i) frag_rows(sm.Es, LDV, 16 * mt, 16 * i, lane, fa[i]);
                         mk_n<DT, VT>(ak, fdb, fa);
-                        gate_part(j, mt, aq0, an, &ak, false);
-                        if constexpr (GATED) ak = ak * sm.gt.rto[16 * mt + r];
+                        gate_part(cb, j, mt, aq0, an, &ak, false);
+                        if constexpr (GATED) ak = ak * sm.gt.rto[cb][16 * mt + r];
                     } else {
-                        gate_part(j, mt, aq0, an, nullptr, false);
+                        gate_part(cb, j, mt, aq0, an, nullptr, false);
                     }
-                    if constexpr (GATED) an = an * sm.gt.gam[16 * mt + r];
+                    if constexpr (GATED) an = an * sm.gt.gam[cb][16 * mt + r];
 #pragma unroll
                     for (int i = 0; i < NT; ++i) frag_rows(sm.Gs, LDC, 16 * mt, 16 * i, lane, fm[i]);
                     mk_n<DT, NT>(ak, fkc, fm);
@@ -975,8 +1024,8 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                         if constexpr (GATED) {
                             f32x4 ed = zero4();
                             mk_n<DT, VT>(ed, fs, fa);
-                            gate_part(j, mt, zero4(), zero4(), &ed, true);
-                            ak += ed * sm.gt.rto[16 * mt + r];
+                            gate_part(cb, j, mt, zero4(), zero4(), &ed, true);
+                            ak += ed * sm.gt.rto[cb][16 * mt + r];
                         } else {
                             mk_n<DT, VT>(ak, fs, fa);
                         }
@@ -994,6 +1043,8 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                 }
             }
         }
+        // the next chunk's other Gram tiles and T_10
+        if (c > 0 && w < NWJ) other_jobs(cb ^ 1, NWJ);
     }
     if (N > 0) flush(0);
     if (GATED && N > 0) {
