@@ -10,9 +10,10 @@ JSON line on stdout:
   value        tokens/s = B*T*K / wall time of the K steps
   roofline     the fused chunk kernel against HBM bandwidth (its roofline
                bound: arithmetic intensity 170 flop/B is below the MI355X
-               ridge of ~315 flop/B), from the mean launch time measured with
-               HIP events on the launch stream; mfma_frac gives the same time
-               against the dense bf16 MFMA peak
+               ridge of ~315 flop/B), from the mean launch time: one pair of
+               HIP events on the launch stream around the K back-to-back
+               steps, elapsed / K; mfma_frac gives the same time against the
+               dense bf16 MFMA peak
   cpu_baseline the fp64 CPU oracle on the host cores (reported, not a target),
                with a single-thread figure on a sample of heads beside it
   small_model  the small-model config (B4 H8 T2048 d64, SiLU + L2 features),
@@ -67,6 +68,20 @@ DECODE_SOURCES = ["deltanet_delta_rule_amd/csrc/recurrent_step.hip",
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def timed_steps(torch, step, reps):
+    """Seconds per step of `reps` back-to-back steps, from one pair of HIP
+    events on the current stream around all of them (an event pair around
+    every step would put its own gap between the launches)."""
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps / 1e3
 
 
 def chunk_work(w):
@@ -261,15 +276,7 @@ def bench_gated_chunk(torch, dr, W, reps=20, name="gated_layer_1p3b", l2=False):
 
     for _ in range(3):
         step()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
-    torch.cuda.synchronize()
-    for a, b in ev:
-        a.record()
-        step()
-        b.record()
-    torch.cuda.synchronize()
-    launch_s = sum(a.elapsed_time(b) for a, b in ev) / reps / 1e3
+    launch_s = timed_steps(torch, step, reps)
     flops, nbytes = chunk_work(w)
     what = ("raw q, k normalised in the kernel, fp32 state" if l2 else
             "fp32 log gates and state" if d["g"] is not None else
@@ -299,15 +306,7 @@ def bench_kda_sequence(torch, dr, W, reps=10):
         dr.kda_fwd(d["q"], d["k"], d["v"], d["beta"], d["gk"], None, o=o, S_T=st)
 
     step()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
-    torch.cuda.synchronize()
-    for a, b in ev:
-        a.record()
-        step()
-        b.record()
-    torch.cuda.synchronize()
-    launch_s = sum(a.elapsed_time(b) for a, b in ev) / reps / 1e3
+    launch_s = timed_steps(torch, step, reps)
     flops, nbytes = chunk_work(w)
     return {
         "workload": (f"layer_1p3b B{w.B} H{w.H} T{w.T} d{w.Dk} chunk {w.chunk}, bf16 in, "
@@ -389,15 +388,7 @@ def bench_backward(torch, dr, W, reps=10, name="layer_1p3b"):
 
     for _ in range(2):
         step()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
-    torch.cuda.synchronize()
-    for a, b in ev:
-        a.record()
-        step()
-        b.record()
-    torch.cuda.synchronize()
-    t = sum(a.elapsed_time(b) for a, b in ev) / reps / 1e3
+    t = timed_steps(torch, step, reps)
     return {
         "workload": (f"{w.name} B{w.B} H{w.H} T{w.T} d{w.Dk}, bf16 in, fp32 state; "
                      "checkpointing forward + reverse pass (output allocation inside)"),
@@ -513,17 +504,19 @@ def main():
         step()
     torch.cuda.synchronize()
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
+    # the K steps run back to back; one pair of HIP events on the launch
+    # stream (the current one) brackets them, so the mean launch duration is
+    # their elapsed time / K (dispatch gaps between launches included)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record()
     for i in range(K):
-        ev[i][0].record()  # the kernel runs on this same (current) stream
         step()
-        ev[i][1].record()
+    ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_s = sum(a.elapsed_time(b) for a, b in ev) / K / 1e3
+    launch_s = ev0.elapsed_time(ev1) / K / 1e3
     log(f"{K} steps: {wall * 1e3 / K:.3f} ms/step wall, {launch_s * 1e6:.1f} us/launch (events)")
 
     flops, nbytes = chunk_work(w)
