@@ -189,3 +189,42 @@ def test_gated_backward_is_deterministic():
                                       None, dst.cuda())
     for n in a:
         assert torch.equal(a[n], b[n]), n
+
+
+@pytest.mark.parametrize("name", ["layer_1p3b", "gated_layer_1p3b"])
+def test_checkpoints_are_the_prefix_states(name):
+    # The backward's first pass runs the forward kernel without outputs (the
+    # specialisation that skips Q K^T, S Q^T and the output products) and
+    # leaves each 32-token chunk's incoming state in the workspace, in bf16.
+    # Checkpoint c must be the final state of a forward over the first 32 c
+    # tokens with outputs (the same state path), rounded to bf16.
+    w = W.get(name, B=2, H=2, T=150, seed=8100)
+    d = to_dev(W.generate(w))
+    do, dst = _upstream(w, 9)
+    lib = dr.load_library()
+    nbytes = int(lib.delta_rule_chunk_bwd_workspace_bytes(w.B, w.T, w.H, w.Dk, w.Dv, dr.DR_BF16))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    if d.get("g") is None:
+        dr.delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], do.cuda(), d["S0"],
+                                dst.cuda(), workspace=ws)
+    else:
+        dr.gated_delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], do.cuda(),
+                                      d["S0"], dst.cuda(), workspace=ws)
+    torch.cuda.synchronize()
+    n = (w.T + 31) // 32
+    ck = ws.view(torch.bfloat16).view(w.B, w.H, n, w.Dv, w.Dk)
+    for c in range(n):
+        tp = 32 * c
+        if c == 0:
+            ref = torch.zeros(w.B, w.H, w.Dv, w.Dk, device="cuda") if d["S0"] is None else d["S0"]
+        else:
+            sl = lambda t: t[:, :tp].contiguous()
+            if d.get("g") is None:
+                _, ref = dr.delta_rule_chunk_fwd(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["beta"]),
+                                                 d["S0"], chunk=32, workspace=False)
+            else:
+                _, ref = dr.gated_delta_rule_chunk_fwd(sl(d["q"]), sl(d["k"]), sl(d["v"]),
+                                                       sl(d["beta"]), sl(d["g"]), d["S0"],
+                                                       chunk=32, workspace=False)
+        torch.cuda.synchronize()
+        assert torch.equal(ck[:, :, c], ref.to(torch.bfloat16)), f"checkpoint {c}"
