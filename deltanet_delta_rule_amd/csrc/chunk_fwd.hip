@@ -14,4 +14,16 @@ hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, bool bf16, hipStream_t stream
     return a.g ? launch_chunk_fwd_gated(a, bf16, stream) : launch_rule<false, false>(a, bf16, stream);
 }
 
+hipError_t launch_chunk_state_pair(const ChunkFwdArgs &a, float *M, bool bf16,
+                                   hipStream_t stream) {
+    if (!bf16 || a.g || a.gk || a.l2 || a.recurrent || a.h || a.o || a.S0 || a.Dk != 128 ||
+        a.Dv != a.Dk)
+        return hipErrorNotSupported;
+    switch (a.chunk) {
+    case 32: return launch_pair_cfg<__bf16, 128, 32>(a, M, stream);
+    case 64: return launch_pair_cfg<__bf16, 128, 64>(a, M, stream);
+    default: return hipErrorNotSupported;
+    }
+}
+
 }  // namespace dr

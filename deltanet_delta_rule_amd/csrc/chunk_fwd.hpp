@@ -998,7 +998,8 @@ struct ChunkRegs {
 // chunk that ends early loads zeros for its missing tokens.  The K, Q, V
 // instructions of a chunk are dealt round-robin to the NW preparation waves;
 // wave W's share is fixed at compile time, so the number of loads it has in
-// flight is a constant.
+// flight is a constant.  Without outputs (NOQ) no product reads Q, so its
+// tiles are not loaded.
 // Per-token scalars of one chunk in flight to LDS (wave 0 loads them).
 template <typename DT>
 struct TokScalars {
@@ -1006,7 +1007,7 @@ struct TokScalars {
     float g;  // log gate of token lane (gated rule)
 };
 
-template <typename DT, int DK, int C, int NW, int W, bool GATED = false>
+template <typename DT, int DK, int C, int NW, int W, bool GATED = false, bool NOQ = false>
 struct DmaStage {
     typedef ChunkCfg<DT, DK, C, NW> G;
     static constexpr int ESZ = (int)sizeof(DT);
@@ -1014,7 +1015,8 @@ struct DmaStage {
     static constexpr int UPR_K = G::LDK * ESZ / 16, NU_K = C * UPR_K, NI_K = (NU_K + 63) / 64;
     static constexpr int UPR_V = G::LDV * ESZ / 16, NU_V = C * UPR_V, NI_V = (NU_V + 63) / 64;
     static constexpr int KTILE = NI_K * 1024 / ESZ, VTILE = NI_V * 1024 / ESZ;  // buffer sizes
-    static constexpr int NI = 2 * NI_K + NI_V;                // instructions per chunk: K, Q, V
+    static constexpr int NI_Q = NOQ ? 0 : NI_K;               // Q instructions
+    static constexpr int NI = NI_K + NI_Q + NI_V;             // instructions per chunk: K, Q, V
     static constexpr int NMINE = (NI - W + NW - 1) / NW;      // this wave's: j = W, W + NW, ...
     static constexpr int NVMEM = NMINE + (W == 0 ? 1 + GATED : 0);  // + beta, g (wave 0)
     static_assert(G::LDK * ESZ % 16 == 0 && G::LDV * ESZ % 16 == 0, "16-byte units");
@@ -1025,8 +1027,8 @@ struct DmaStage {
 #pragma unroll
         for (int i = 0; i < NMINE; ++i) {
             const int j = W + i * NW;
-            const bool isv = j >= 2 * NI_K;
-            const int jj = isv ? j - 2 * NI_K : (j < NI_K ? j : j - NI_K);
+            const bool isv = j >= NI_K + NI_Q;
+            const int jj = isv ? j - NI_K - NI_Q : (j < NI_K ? j : j - NI_K);
             const int upr = isv ? UPR_V : UPR_K;
             const int u = 64 * jj + lane;
             const int t = u / upr, cu = u % upr;
@@ -1052,8 +1054,8 @@ struct DmaStage {
 #pragma unroll
         for (int i = 0; i < NMINE; ++i) {
             const int j = W + i * NW;
-            const bool isv = j >= 2 * NI_K, isq = !isv && j >= NI_K;
-            const int jj = isv ? j - 2 * NI_K : (isq ? j - NI_K : j);
+            const bool isv = j >= NI_K + NI_Q, isq = !isv && j >= NI_K;
+            const int jj = isv ? j - NI_K - NI_Q : (isq ? j - NI_K : j);
             DT *dst = (isv ? Vs : isq ? Qs : Ks) + jj * (1024 / ESZ);
             const auto &rs = isv ? rv : isq ? rq : rk;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, off[i], 0, 0, 0);
@@ -1131,7 +1133,7 @@ template <typename DT, int DK, int C, int NW, int W, bool GATED, bool L2, bool N
 __device__ __forceinline__ void prep_role(PipeSmem<DT, DK, C, NW, GATED, L2> &sm,
                                           const HeadPtrs<DT> &p, int T, int N, int lane) {
     typedef ChunkCfg<DT, DK, C, NW> G;
-    typedef DmaStage<DT, DK, C, NW, W, GATED> D;
+    typedef DmaStage<DT, DK, C, NW, W, GATED, NOOUT> D;
     D dma;
     dma.init(p, lane);
     const int ptid = 64 * W + lane;
@@ -1208,27 +1210,47 @@ __device__ __forceinline__ void prep_role(PipeSmem<DT, DK, C, NW, GATED, L2> &sm
 // NOOUT: a launch without outputs (o == nullptr: the checkpoint pass of the
 // backward, the state passes of the segment-parallel schedule) skips every
 // product that only the outputs need (P = Q K^T, Y = S Q^T, E^T P^T).
-template <typename DT, int DK, int C, int NW, bool GATED, bool L2, bool NOOUT = false>
-__global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4 + 1, NW / 4 + 1))) void chunk_fwd_ws_kernel(
+//
+// PAIR (with NOOUT, plain rule, d_v = d_k): a second group of NW state waves
+// carries d_k rows of the chunk walk's transition map beside the workgroup's
+// value rows, on the same loaded K and the same Gram tiles and inverses: the
+// map's rows run the same recurrence with v = 0 from the identity, read from
+// and written back to Mst in place (3 NW waves, three per SIMD).
+template <typename DT, int DK, int C, int NW, bool GATED, bool L2, bool NOOUT = false,
+          bool PAIR = false>
+__global__ __launch_bounds__((PAIR ? 192 : 128) * NW) __attribute__((amdgpu_waves_per_eu(PAIR ? 3 : NW / 4 + 1, PAIR ? 3 : NW / 4 + 1))) void chunk_fwd_ws_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const float *__restrict__ gl, const float *S0,
     DT *__restrict__ o, float *S_T, DT *__restrict__ hs, const int *__restrict__ cu, int T,
-    int H, int Dv, int nvt, float scale) {
+    int H, int Dv, int nvt, float scale, float *Mst) {
     typedef ChunkCfg<DT, DK, C, NW> G;
     constexpr int NT = G::NT, ND = G::ND;
+    constexpr int NSW = (PAIR ? 2 : 1) * NW;  // state waves
+    static_assert(!PAIR || (NOOUT && !GATED && !L2), "map rows: plain rule without outputs");
     __shared__ __attribute__((aligned(16))) PipeSmem<DT, DK, C, NW, GATED, L2> sm;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
     const int g = lane >> 4, r = lane & 15;
 
-    if (wave < NW) {
+    if (wave < NSW) {
         // ------------------------------ state waves ------------------------------
+        const bool mrow = PAIR && wave >= NW;  // rows of the transition map
+        const int sw = mrow ? wave - NW : wave;
+        if (mrow) {
+            v = nullptr;
+            S0 = S_T = Mst;
+            Dv = DK;
+        }
         const HeadPtrs<DT> p =
-            head_ptrs<DT, DK, NW>(q, k, v, beta, gl, o, cu, T, H, Dv, nvt, wave, r);
+            head_ptrs<DT, DK, NW>(q, k, v, beta, gl, o, cu, T, H, Dv, nvt, sw, r);
         const int N = (p.T + C - 1) / C;
         f32x4 Sacc[ND], X[NT], Y[NT];
         ChunkOperands<DT, DK, C, NW> op;
+        if (mrow) {
+#pragma unroll
+            for (int mt = 0; mt < NT; ++mt) op.fv[mt] = typename Frag<DT>::k16{};
+        }
         if (S0) {
 #pragma unroll
             for (int dt = 0; dt < ND; ++dt)
@@ -1242,7 +1264,8 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4
         // X, Y and the K^T operands of the chunk in set s
         // (L2: V stays in op.fv for the block substitution of that chunk)
         auto xy = [&](int s) {
-            if constexpr (!GATED && !L2) op.load_v(sm.Vs[s], wave, lane);
+            if constexpr (!GATED && !L2)
+                if (!mrow) op.load_v(sm.Vs[s], sw, lane);
             state_xy<DT, DK, C, NW, GATED, L2, NOOUT>(sm.Ks[s], sm.Qs[s], Sacc, op.fv, X, Y, lane);
             if constexpr (GATED || L2) op.load_v(sm.Vs[s], wave, lane);
             if constexpr (GATED) gate_xy<DT, C, NT, !L2>(op.fv, sm.gate.at(s)->gam, X, Y, lane);
@@ -1283,7 +1306,7 @@ __global__ __launch_bounds__(128 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4
         const HeadPtrs<DT> p =
             head_ptrs<DT, DK, NW>(q, k, v, beta, gl, o, cu, T, H, Dv, nvt, 0, r);
         const int N = (p.T + C - 1) / C;
-        switch (wave - NW) {
+        switch (wave - NSW) {
         case 0: prep_role<DT, DK, C, NW, 0, GATED, L2, NOOUT>(sm, p, p.T, N, lane); break;
         case 1: if constexpr (NW > 1) prep_role<DT, DK, C, NW, 1, GATED, L2, NOOUT>(sm, p, p.T, N, lane); break;
         case 2: if constexpr (NW > 2) prep_role<DT, DK, C, NW, 2, GATED, L2, NOOUT>(sm, p, p.T, N, lane); break;
@@ -1389,7 +1412,7 @@ hipError_t launch_cfg(const ChunkFwdArgs &a, hipStream_t stream) {
             hipLaunchKernelGGL((chunk_fwd_ws_kernel<DT, DK, C, NW, GATED, L2, true>),
                                dim3((unsigned)grid), dim3(128 * NW), 0, stream, q, k, v, beta, a.g,
                                a.S0, o, a.S_T, static_cast<DT *>(a.h), a.cu, (int)a.T, (int)a.H,
-                               a.Dv, nvt, a.scale);
+                               a.Dv, nvt, a.scale, nullptr);
             return hipGetLastError();
         }
     }
@@ -1397,13 +1420,30 @@ hipError_t launch_cfg(const ChunkFwdArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL((chunk_fwd_ws_kernel<DT, DK, C, NW, GATED, L2>), dim3((unsigned)grid),
                            dim3(128 * NW), 0, stream, q, k, v, beta, a.g, a.S0, o, a.S_T,
                            static_cast<DT *>(a.h), a.cu,
-                           (int)a.T, (int)a.H, a.Dv, nvt, a.scale);
+                           (int)a.T, (int)a.H, a.Dv, nvt, a.scale, nullptr);
     } else {
         hipLaunchKernelGGL((chunk_fwd_serial_kernel<DT, DK, C, NW, GATED, L2>), dim3((unsigned)grid),
                            dim3(64 * NW), 0, stream, q, k, v, beta, a.g, a.S0, o, a.S_T,
                            static_cast<DT *>(a.h), a.cu,
                            (int)a.T, (int)a.H, a.Dv, nvt, a.scale);
     }
+    return hipGetLastError();
+}
+
+// The zero-state pass and the transition-map pass of the segment-parallel
+// schedule in one launch (PAIR): value rows from zero states into a.S_T and
+// the d_k rows of each segment's map in M (identity in, map out, in place).
+template <typename DT, int DK, int C>
+hipError_t launch_pair_cfg(const ChunkFwdArgs &a, float *M, hipStream_t stream) {
+    constexpr int NW = 4;
+    const int nvt = DK / (16 * NW);
+    const int64_t grid = a.B * a.H * nvt;
+    hipLaunchKernelGGL((chunk_fwd_ws_kernel<DT, DK, C, NW, false, false, true, true>),
+                       dim3((unsigned)grid), dim3(192 * NW), 0, stream,
+                       static_cast<const DT *>(a.q), static_cast<const DT *>(a.k),
+                       static_cast<const DT *>(a.v), static_cast<const DT *>(a.beta), nullptr,
+                       nullptr, nullptr, a.S_T, nullptr, a.cu, (int)a.T, (int)a.H, a.Dv, nvt,
+                       a.scale, M);
     return hipGetLastError();
 }
 

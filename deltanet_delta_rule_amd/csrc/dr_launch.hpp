@@ -34,6 +34,12 @@ struct ChunkFwdArgs {
 };
 
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
+// a without outputs or initial state (value rows from zero states into
+// a.S_T) and, in the same launch, the d_k x d_k transition map of each
+// sequence in M (read as the incoming map, written back); plain rule, bf16,
+// d_k = d_v = 128, chunks of 32 or 64, else hipErrorNotSupported.
+hipError_t launch_chunk_state_pair(const ChunkFwdArgs &a, float *M, bool bf16,
+                                   hipStream_t stream);
 hipError_t launch_fused_recurrent(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
 // Segment-parallel schedule of the chunked forward (plain or gated rule, no
 // packed sequences): P segments of L tokens (a multiple of the chunk), and

@@ -65,6 +65,7 @@ namespace {
 constexpr int SEG_CUS = 256;      // compute units of one MI355X
 constexpr int SEG_MIN = 6;        // fewest segments worth three passes
 constexpr int SEG_MIN_CHUNKS = 16;  // shortest segment, in chunks
+constexpr int SEG_PAIR_CHUNK = 32;  // chunk of the combined state-and-map pass
 
 // Identity initial state of the M pass (one float4 per thread) and the
 // segment offsets (one packed row of B * T tokens; segment p of sequence b
@@ -299,14 +300,22 @@ hipError_t launch_chunk_fwd_segmented(const ChunkFwdArgs &a, const SegPlan &pl, 
     s.S0 = nullptr;
     s.o = nullptr;
     s.S_T = Hs;
-    if ((e = launch_chunk_fwd(s, bf16, stream)) != hipSuccess) return e;
-    // 2. M_p: v = 0, S = I in place, d_k value rows
-    ChunkFwdArgs m = s;
-    m.v = nullptr;
-    m.Dv = a.Dk;
-    m.S0 = M;
-    m.S_T = M;
-    if ((e = launch_chunk_fwd(m, bf16, stream)) != hipSuccess) return e;
+    // 2. M_p: v = 0, S = I in place, d_k value rows.  Where the shape allows,
+    // 1 and 2 are one launch that shares each chunk's loads, Gram tiles and
+    // inverses between the value rows and the map rows.
+    ChunkFwdArgs pr = s;
+    pr.chunk = SEG_PAIR_CHUNK;
+    e = launch_chunk_state_pair(pr, M, bf16, stream);
+    if (e == hipErrorNotSupported) {
+        if ((e = launch_chunk_fwd(s, bf16, stream)) != hipSuccess) return e;
+        ChunkFwdArgs m = s;
+        m.v = nullptr;
+        m.Dv = a.Dk;
+        m.S0 = M;
+        m.S_T = M;
+        e = launch_chunk_fwd(m, bf16, stream);
+    }
+    if (e != hipSuccess) return e;
     // 3. the chain: S_in(p) into Hs, and the final state
     switch (a.Dk) {
     case 16: e = launch_chain<16>(Hs, M, a.S0, a.S_T, a.B, pl.P, a.H, a.Dv, stream); break;
