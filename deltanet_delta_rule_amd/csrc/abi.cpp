@@ -187,11 +187,27 @@ dr_status recurrent_step(const void *q, const void *k, const void *v, const void
         dr::launch_recurrent_step(a, dtype == DR_BF16, static_cast<hipStream_t>(stream)));
 }
 
-// Checkpoint workspace of the backward: every chunk's incoming state.
-int64_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, bool bf16) {
+// Workspace of the backward: every chunk's incoming state (the forward
+// checkpoints), then the gradient of every chunk's state and the solve's Z
+// ([B,T,H,Dv]) for the two-pass schedule; each part 256-byte aligned.
+struct BwdWs {
+    int64_t ckpt, dsz, total;  // bytes of the checkpoints and of Z; all parts
+};
+BwdWs bwd_workspace(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, bool bf16) {
     const int64_t cb = dr::chunk_bwd_chunk(bf16);
     const int64_t N = (T + cb - 1) / cb;
-    return mul_checked({B, H, N, Dv, Dk, bf16 ? 2 : 4});
+    const int64_t esz = bf16 ? 2 : 4;
+    BwdWs w;
+    w.ckpt = mul_checked({B, H, N, Dv, Dk, esz});
+    w.dsz = mul_checked({B, T, H, Dv, esz});
+    const auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
+    w.total = w.ckpt < 0 || w.dsz < 0 || w.ckpt > INT64_MAX / 4 || w.dsz > INT64_MAX / 4
+                  ? -1
+                  : 2 * al(w.ckpt) + al(w.dsz);
+    return w;
+}
+int64_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, bool bf16) {
+    return bwd_workspace(B, T, H, Dk, Dv, bf16).total;
 }
 
 dr_status chunk_bwd(const void *q, const void *k, const void *v, const void *beta,
@@ -247,8 +263,14 @@ dr_status chunk_bwd(const void *q, const void *k, const void *v, const void *bet
         const hipError_t e = dr::launch_chunk_fwd(f, bf16, st);
         if (e != hipSuccess) return hip_status(e);
     }
-    const dr::ChunkBwdArgs a{q,  k,     v,   beta, dout, dS_T, h,       dq,      dk,
-                             dv, dbeta, dS0, B,    T,    H,    (int)Dk, (int)Dv, g, dg};
+    dr::ChunkBwdArgs a{q,  k,     v,   beta, dout, dS_T, h,       dq,      dk,
+                       dv, dbeta, dS0, B,    T,    H,    (int)Dk, (int)Dv, g, dg};
+    if (T > 0) {
+        const BwdWs wl = bwd_workspace(B, T, H, Dk, Dv, bf16);
+        const int64_t ck = (wl.ckpt + 255) / 256 * 256;
+        a.dsb = static_cast<char *>(ws) + ck;
+        a.dsz = static_cast<char *>(ws) + 2 * ck;
+    }
     return hip_status(dr::launch_chunk_bwd(a, bf16, st));
 }
 

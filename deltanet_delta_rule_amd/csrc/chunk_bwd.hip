@@ -314,18 +314,23 @@ struct ChunkPrefetch {
     RowPrefetch<DT, C, DK, NTHR> k, q;
     RowPrefetch<DT, C, DV, NTHR> v, o;
     RowPrefetch<DT, DV, DK, NTHR> s;
+    RowPrefetch<DT, DV, DK, NTHR> ds;  // dS_{c+1} checkpoint (products-only mode)
+    RowPrefetch<DT, C, DV, NTHR> z;    // Z (products-only mode)
     DT b;      // beta of token tid (zero past the chunk's valid length)
     float gv;  // log gate of token tid (gated rule; zero past the valid length)
     // Part 0: S_c; part 1: K, Q, beta (and the log gates); part 2: V and dO
     // (issued at three points of a chunk, so that no single point floods the
-    // vector memory path).
-    template <int P>
+    // vector memory path).  MODE 1 (recursion only) loads no S_c and no V;
+    // MODE 2 (products only) also loads the dS_{c+1} checkpoint (part 0) and
+    // Z (part 2).
+    template <int P, int MODE>
     __device__ __forceinline__ void load_part(const DT *kk, const DT *qq, const DT *vv,
                                               const DT *oo, const DT *bb, const float *gg,
-                                              const DT *sc, int64_t tok0, int h, int H,
-                                              int len, int tid) {
+                                              const DT *sc, const DT *dsc, const DT *zz,
+                                              int64_t tok0, int h, int H, int len, int tid) {
         const int64_t rk = (int64_t)H * DK, rv = (int64_t)H * DV;
-        if constexpr (P == 0) s.load(sc, DK, DV, tid);
+        if constexpr (P == 0 && MODE != 1) s.load(sc, DK, DV, tid);
+        if constexpr (P == 0 && MODE == 2) ds.load(dsc, DK, DV, tid);
         if constexpr (P == 1) {
             k.load(kk + (tok0 * H + h) * DK, rk, len, tid);
             q.load(qq + (tok0 * H + h) * DK, rk, len, tid);
@@ -339,16 +344,10 @@ struct ChunkPrefetch {
             }
         }
         if constexpr (P == 2) {
-            v.load(vv + (tok0 * H + h) * DV, rv, len, tid);
+            if constexpr (MODE != 1) v.load(vv + (tok0 * H + h) * DV, rv, len, tid);
             o.load(oo + (tok0 * H + h) * DV, rv, len, tid);
+            if constexpr (MODE == 2) z.load(zz + (tok0 * H + h) * DV, rv, len, tid);
         }
-    }
-    __device__ __forceinline__ void load(const DT *kk, const DT *qq, const DT *vv, const DT *oo,
-                                         const DT *bb, const float *gg, const DT *sc,
-                                         int64_t tok0, int h, int H, int len, int tid) {
-        load_part<0>(kk, qq, vv, oo, bb, gg, sc, tok0, h, H, len, tid);
-        load_part<1>(kk, qq, vv, oo, bb, gg, sc, tok0, h, H, len, tid);
-        load_part<2>(kk, qq, vv, oo, bb, gg, sc, tok0, h, H, len, tid);
     }
 };
 
@@ -375,35 +374,53 @@ __device__ __forceinline__ void store_rows(DT *dst, int64_t gs, int nvalid, cons
     }
 }
 
-template <typename DT, int DK, int DV, int C, bool GATED>
+// MODE 0: the whole backward in one reverse walk per (b, h).  MODE 1
+// (recursion only): dE, Z, dV and the dS recursion, one workgroup per (b, h);
+// it writes dV, dS0, Z (dsz, [B,T,H,d_v]) and every chunk's dS_{c+1}
+// (dsb, [B,H,N,d_v,d_k], like the forward checkpoints).  MODE 2 (products
+// only): R, E, dbeta, dQ, dK (and dg) from those, with nsplit workgroups per
+// (b, h), each over its own run of chunks, so that the chunks of a head run
+// in parallel.
+template <typename DT, int DK, int DV, int C, bool GATED, int MODE>
 __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const float *__restrict__ gl, const DT *__restrict__ dout,
     const float *__restrict__ dST, const DT *__restrict__ hs, DT *__restrict__ dq,
     DT *__restrict__ dk, DT *__restrict__ dv, DT *__restrict__ dbeta, float *__restrict__ dg,
-    float *__restrict__ dS0, int T, int H) {
+    float *__restrict__ dS0, DT *__restrict__ dsb, DT *__restrict__ dsz, int T, int H,
+    int nsplit) {
     typedef BwdCfg<DT, DK, DV, C> G;
     constexpr int NW = G::NW, NT = G::NT, KT = G::KT, VT = G::VT;
     constexpr int LDK = G::LDK, LDV = G::LDV, LDS_ = G::LDS_, LDSK = G::LDSK, LDC = G::LDC;
+    constexpr bool PROD = MODE != 1;   // R, E, dbeta and the products over all value columns
+    constexpr bool RECUR = MODE != 2;  // dE, Z and the dS recursion
+    static_assert(MODE == 0 || G::DBUF, "split modes keep dS_{c+1} in its own LDS buffer");
     __shared__ __attribute__((aligned(16))) BwdSmem<DT, DK, DV, C, GATED> sm;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, r = lane & 15;
     const int v0 = 16 * w;
-    const int64_t head = blockIdx.x;
+    const int64_t head = MODE == 2 ? blockIdx.x / nsplit : blockIdx.x;
     const int b = (int)(head / H), h = (int)(head % H);
     const int N = (T + C - 1) / C;
     const int nthr = 64 * NW;
+    // chunks [c_lo, c_hi) of this workgroup, walked in reverse
+    int c_lo = 0, c_hi = N;
+    if constexpr (MODE == 2) {
+        const int per = (N + nsplit - 1) / nsplit, part = (int)(blockIdx.x % nsplit);
+        c_lo = min(N, part * per);
+        c_hi = min(N, c_lo + per);
+    }
 
     // upper tiles of the C x C matrices stay zero
     for (int i = tid; i < C * LDC; i += nthr) {
         sm.Pm[i] = sm.Gl[0][i] = sm.Gl[1][i] = sm.Tm[i] = sm.Dm[i] = sm.Gs[i] = from_f32<DT>(0.f);
     }
     // dS^T of this wave's value columns: tile s holds dS^T[16s + 4g + i][v0 + r]
-    f32x4 Dt[KT];
+    f32x4 Dt[RECUR ? KT : 1];
 #pragma unroll
-    for (int s = 0; s < KT; ++s) {
+    for (int s = 0; s < (RECUR ? KT : 0); ++s) {
         Dt[s] = dST ? *reinterpret_cast<const f32x4 *>(dST + (head * DV + v0 + r) * DK + 16 * s + 4 * g)
                     : zero4();
     }
@@ -531,9 +548,9 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
     ChunkPrefetch<DT, DK, DV, C> pf;
     auto prefetch = [&](auto part, int cn) {
         const int tp = cn * C;
-        pf.template load_part<decltype(part)::value>(k, q, v, dout, beta, GATED ? gl : nullptr,
-                                                     hs + (head * N + cn) * DV * DK,
-                                                     (int64_t)b * T + tp, h, H, min(C, T - tp), tid);
+        pf.template load_part<decltype(part)::value, MODE>(
+            k, q, v, dout, beta, GATED ? gl : nullptr, hs + (head * N + cn) * DV * DK,
+            dsb + (head * N + cn) * DV * DK, dsz, (int64_t)b * T + tp, h, H, min(C, T - tp), tid);
     };
     // K, Q and beta of chunk cc (and its decays) from the prefetch registers
     // into buffer set bb; every lane converts beta (see RowPrefetch::store).
@@ -647,32 +664,38 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
     // waves during the C x C phase (where they have no tile), and its other
     // tiles and T_10 by the waves that finish their dQ, dK tiles first (waves
     // 0 .. 3: the second wave on each SIMD runs behind).
-    if (N > 0) {
-        const int t0 = (N - 1) * C;
-        pf.load(k, q, v, dout, beta, GATED ? gl : nullptr, hs + (head * N + N - 1) * DV * DK,
-                (int64_t)b * T + t0, h, H, min(C, T - t0), tid);
-        stage_kqb((N - 1) & 1);
+    if (c_hi > c_lo) {
+        prefetch(std::integral_constant<int, 0>(), c_hi - 1);
+        prefetch(std::integral_constant<int, 1>(), c_hi - 1);
+        prefetch(std::integral_constant<int, 2>(), c_hi - 1);
+        stage_kqb((c_hi - 1) & 1);
         __syncthreads();
-        diag_jobs((N - 1) & 1);
+        diag_jobs((c_hi - 1) & 1);
         __syncthreads();
-        other_jobs((N - 1) & 1, NW);
+        other_jobs((c_hi - 1) & 1, NW);
     }
     constexpr int NWJ = NW < 4 ? NW : 4;  // waves that form the next chunk's Gram tiles
-    for (int c = N - 1; c >= 0; --c) {
+    for (int c = c_hi - 1; c >= c_lo; --c) {
         const int len = min(C, T - c * C);
         const int64_t tok0 = (int64_t)b * T + c * C;
         const int cb = c & 1;  // buffer set of this chunk's K, Q, beta, decays
         __syncthreads();
         // ---------------------------------------------------------------- load
-        pf.v.store(sm.Vs, LDV, tid);
+        if constexpr (PROD) pf.v.store(sm.Vs, LDV, tid);
         pf.o.store(sm.Os, LDV, tid);
-        pf.s.store(sm.Sb, LDSK, tid);
-        if (c > 0) prefetch(std::integral_constant<int, 0>(), c - 1);
-        if (GATED && w == 0 && c + 1 < N) finalize_dg(c + 1);
+        if constexpr (PROD) pf.s.store(sm.Sb, LDSK, tid);
+        if constexpr (MODE == 2) {
+            pf.ds.store(sm.Db, LDS_, tid);
+            pf.z.store(sm.Rb, LDV, tid);  // Z; each wave turns its columns into dV
+        }
+        if (c > c_lo) prefetch(std::integral_constant<int, 0>(), c - 1);
+        if constexpr (MODE == 1)
+            if (c > c_lo) prefetch(std::integral_constant<int, 2>(), c - 1);
+        if (PROD && GATED && w == 0 && c + 1 < c_hi) finalize_dg(c + 1);
         __syncthreads();
 
         // ------------------------------------------- per-wave value columns
-        if (c > 0) prefetch(std::integral_constant<int, 1>(), c - 1);
+        if (c > c_lo) prefetch(std::integral_constant<int, 1>(), c - 1);
         f32x4 R[NT], E[NT], Z[NT];
         {
             // R = V - K S_c^T (S_c rows of this wave's columns as B^T) and
@@ -680,95 +703,136 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
             typename Frag<DT>::k16 fs[KT], fd[KT];
 #pragma unroll
             for (int s = 0; s < KT; ++s) {
-                frag_rows(sm.Sb, LDSK, v0, 16 * s, lane, fs[s]);
-                cvt4(Dt[s], fd[s]);
+                if constexpr (PROD) frag_rows(sm.Sb, LDSK, v0, 16 * s, lane, fs[s]);
+                if constexpr (RECUR) cvt4(Dt[s], fd[s]);
             }
-            if constexpr (GATED) {
+            if constexpr (GATED && PROD) {
                 // dL/dgamma_last = sum dS_{c+1} (.) S_c over this wave's rows
                 float a = 0.f;
 #pragma unroll
-                for (int s = 0; s < KT; ++s)
+                for (int s = 0; s < KT; ++s) {
+                    if constexpr (RECUR) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) a += Dt[s][i] * frag_get(fs[s], i);
+                        for (int i = 0; i < 4; ++i) a += Dt[s][i] * frag_get(fs[s], i);
+                    } else {
+                        typename Frag<DT>::k16 fdd;
+                        frag_rows(sm.Db, LDS_, v0, 16 * s, lane, fdd);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) a += frag_get(fdd, i) * frag_get(fs[s], i);
+                    }
+                }
                 a = wave_sum(a);
                 if (lane == 0) sm.gt.dgc[w] = a * sm.gt.gam[cb][C - 1];
             }
             f32x4 dE[NT];
 #pragma unroll
             for (int mt = 0; mt < NT; ++mt) {
-                f32x4 x = zero4();
                 typename Frag<DT>::k16 fk[KT];
 #pragma unroll
                 for (int s = 0; s < KT; ++s) frag_rows(sm.Ks[cb], LDK, 16 * mt, 16 * s, lane, fk[s]);
-                mk_n<DT, KT>(x, fk, fs);
-                typename Frag<DT>::k16 fvv;
-                frag_cols16(sm.Vs, LDV, 16 * mt, v0, lane, fvv);
-                if constexpr (GATED) {
-                    // R = V - diag(gamma) K S_c^T
+                if constexpr (PROD) {
+                    f32x4 x = zero4();
+                    mk_n<DT, KT>(x, fk, fs);
+                    typename Frag<DT>::k16 fvv;
+                    frag_cols16(sm.Vs, LDV, 16 * mt, v0, lane, fvv);
+                    if constexpr (GATED) {
+                        // R = V - diag(gamma) K S_c^T
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) x[i] *= sm.gt.gam[cb][16 * mt + 4 * g + i];
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) R[mt][i] = frag_get(fvv, i) - x[i];
-                dE[mt] = zero4();
-                // P^T is zero above the diagonal: slabs kt < mt are zeros
-                typename Frag<DT>::k16 fa[NT], fo[NT];
-#pragma unroll
-                for (int kt = 0; kt < NT; ++kt) {
-                    if (kt >= mt) {
-                        frag_cols16(sm.Pm, LDC, 16 * kt, 16 * mt, lane, fa[kt]);
-                        frag_cols16(sm.Os, LDV, 16 * kt, v0, lane, fo[kt]);
-                    } else {
-                        fa[kt] = fo[kt] = typename Frag<DT>::k16{};
+                        for (int i = 0; i < 4; ++i) x[i] *= sm.gt.gam[cb][16 * mt + 4 * g + i];
                     }
-                }
-                mk_n<DT, NT>(dE[mt], fa, fo);
-                if constexpr (GATED) {
-                    // dE = P^T dO + diag(rho) K dS^T
-                    f32x4 kd = zero4();
-                    mk_n<DT, KT>(kd, fk, fd);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) dE[mt][i] += sm.gt.rto[cb][16 * mt + 4 * g + i] * kd[i];
-                } else {
-                    mk_n<DT, KT>(dE[mt], fk, fd);
+                    for (int i = 0; i < 4; ++i) R[mt][i] = frag_get(fvv, i) - x[i];
+                }
+                if constexpr (RECUR) {
+                    dE[mt] = zero4();
+                    // P^T is zero above the diagonal: slabs kt < mt are zeros
+                    typename Frag<DT>::k16 fa[NT], fo[NT];
+#pragma unroll
+                    for (int kt = 0; kt < NT; ++kt) {
+                        if (kt >= mt) {
+                            frag_cols16(sm.Pm, LDC, 16 * kt, 16 * mt, lane, fa[kt]);
+                            frag_cols16(sm.Os, LDV, 16 * kt, v0, lane, fo[kt]);
+                        } else {
+                            fa[kt] = fo[kt] = typename Frag<DT>::k16{};
+                        }
+                    }
+                    mk_n<DT, NT>(dE[mt], fa, fo);
+                    if constexpr (GATED) {
+                        // dE = P^T dO + diag(rho) K dS^T
+                        f32x4 kd = zero4();
+                        mk_n<DT, KT>(kd, fk, fd);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) dE[mt][i] += sm.gt.rto[cb][16 * mt + 4 * g + i] * kd[i];
+                    } else {
+                        mk_n<DT, KT>(dE[mt], fk, fd);
+                    }
                 }
             }
             // E = Tm diag(beta) R
-            typename Frag<DT>::k16 frb[NT];
+            if constexpr (PROD) {
+                typename Frag<DT>::k16 frb[NT];
 #pragma unroll
-            for (int mt = 0; mt < NT; ++mt) {
-                f32x4 rb;
+                for (int mt = 0; mt < NT; ++mt) {
+                    f32x4 rb;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) rb[i] = sm.betas[cb][16 * mt + 4 * g + i] * R[mt][i];
-                cvt4(rb, frb[mt]);
-            }
+                    for (int i = 0; i < 4; ++i) rb[i] = sm.betas[cb][16 * mt + 4 * g + i] * R[mt][i];
+                    cvt4(rb, frb[mt]);
+                }
 #pragma unroll
-            for (int mt = 0; mt < NT; ++mt) {
-                E[mt] = zero4();
-                typename Frag<DT>::k16 ft;
+                for (int mt = 0; mt < NT; ++mt) {
+                    E[mt] = zero4();
+                    typename Frag<DT>::k16 ft;
 #pragma unroll
-                for (int kt = 0; kt <= mt; ++kt) {
-                    frag_rows(sm.Tm, LDC, 16 * mt, 16 * kt, lane, ft);
-                    mk<DT>(E[mt], ft, frb[kt]);
+                    for (int kt = 0; kt <= mt; ++kt) {
+                        frag_rows(sm.Tm, LDC, 16 * mt, 16 * kt, lane, ft);
+                        mk<DT>(E[mt], ft, frb[kt]);
+                    }
                 }
             }
-            // Z = Tm^T dE
-            typename Frag<DT>::k16 fde[NT];
+            if constexpr (RECUR) {
+                // Z = Tm^T dE
+                typename Frag<DT>::k16 fde[NT];
 #pragma unroll
-            for (int mt = 0; mt < NT; ++mt) cvt4(dE[mt], fde[mt]);
+                for (int mt = 0; mt < NT; ++mt) cvt4(dE[mt], fde[mt]);
 #pragma unroll
-            for (int mt = 0; mt < NT; ++mt) {
-                Z[mt] = zero4();
-                typename Frag<DT>::k16 fa;
+                for (int mt = 0; mt < NT; ++mt) {
+                    Z[mt] = zero4();
+                    typename Frag<DT>::k16 fa;
 #pragma unroll
-                for (int kt = mt; kt < NT; ++kt) {
-                    frag_cols16(sm.Tm, LDC, 16 * kt, 16 * mt, lane, fa);
-                    mk<DT>(Z[mt], fa, fde[kt]);
+                    for (int kt = mt; kt < NT; ++kt) {
+                        frag_cols16(sm.Tm, LDC, 16 * kt, 16 * mt, lane, fa);
+                        mk<DT>(Z[mt], fa, fde[kt]);
+                    }
+                }
+            } else {
+                // Z of this wave's columns, from the recursion pass
+#pragma unroll
+                for (int mt = 0; mt < NT; ++mt) {
+                    typename Frag<DT>::k16 fz;
+                    frag_cols16(sm.Rb, LDV, 16 * mt, v0, lane, fz);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Z[mt][i] = to_f32(frag_get(fz, i));
                 }
             }
         }
+        // recursion only: dV = diag(beta) Z and Z itself, published for the
+        // stores of this chunk
+        if constexpr (!PROD) {
+#pragma unroll
+            for (int mt = 0; mt < NT; ++mt) {
+                f32x4 dvv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * mt + 4 * g + i;
+                    dvv[i] = sm.betas[cb][t] * Z[mt][i];
+                    sm.Es[t * LDV + v0 + r] = from_f32<DT>(Z[mt][i]);
+                    sm.Rb[t * LDV + v0 + r] = from_f32<DT>(dvv[i]);
+                }
+                Z[mt] = dvv;
+            }
+        }
         // Y = R - tril(G, -1) E; dbeta parts; dV; publish E and dV
-        {
+        if constexpr (PROD) {
             typename Frag<DT>::k16 fe[NT];
 #pragma unroll
             for (int mt = 0; mt < NT; ++mt) cvt4(E[mt], fe[mt]);
@@ -810,7 +874,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
 #pragma unroll
             for (int s2 = 0; s2 < KT; ++s2) Dold[s2] = Dt[s2];
         }
-        {
+        if constexpr (RECUR) {
             // lane (g, r) holds dS[v0 + r][16 s + 4 g .. + 3]: one vector per tile
             if constexpr (G::DBUF) {
 #pragma unroll
@@ -856,13 +920,13 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
             }
         }
         // the next chunk's K, Q, beta (loaded since the start of this phase)
-        if (c > 0) stage_kqb(cb ^ 1);
+        if (c > c_lo) stage_kqb(cb ^ 1);
         __syncthreads();
 
         // ---------------------- C x C products over all value columns, dbeta
         // (and the next chunk's diagonal Gram blocks and their inverses)
-        if (c > 0) diag_jobs(cb ^ 1);
-        for (int j = w; j < 2 * NJ; j += NW) {
+        if (c > c_lo) diag_jobs(cb ^ 1);
+        for (int j = w; PROD && j < 2 * NJ; j += NW) {
             const bool isD = j < NJ;  // dO E^T, else dV E^T
             int jj = isD ? j : j - NJ, ti = 0;
             while (jj > ti) { jj -= ti + 1; ++ti; }
@@ -906,7 +970,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                 }
             }
         }
-        for (int t = tid; t < len; t += nthr) {
+        for (int t = tid; PROD && t < len; t += nthr) {
             float sb = 0.f;
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww) sb += sm.dbp[ww][t];
@@ -915,8 +979,19 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
         __syncthreads();
 
         // ------------------------------------------------------- dQ and dK
-        if (c > 0) prefetch(std::integral_constant<int, 2>(), c - 1);
-        if (c + 1 < N) flush(c + 1);
+        if constexpr (MODE == 1) {
+            // recursion only: dV, Z and the dS_{c+1} checkpoint leave from LDS
+            store_rows<DT, C, DV, 64 * NW>(dv + (tok0 * H + h) * DV, (int64_t)H * DV, len, sm.Rb,
+                                           LDV, tid);
+            store_rows<DT, C, DV, 64 * NW>(dsz + (tok0 * H + h) * DV, (int64_t)H * DV, len, sm.Es,
+                                           LDV, tid);
+            store_rows<DT, DV, DK, 64 * NW>(dsb + (head * N + c) * DV * DK, DK, DV, sm.Db, LDS_,
+                                            tid);
+            if (c > c_lo && w < NWJ) other_jobs(cb ^ 1, NWJ);
+            continue;
+        }
+        if (c > c_lo) prefetch(std::integral_constant<int, 2>(), c - 1);
+        if (c + 1 < c_hi) flush(c + 1);
         // dV of all value columns, from its LDS copy, 16 bytes per store
         store_rows<DT, C, DV, 64 * NW>(dv + (tok0 * H + h) * DV, (int64_t)H * DV, len, sm.Rb, LDV, tid);
         // The operands along d_k (columns of S_c, K and Q, rows of
@@ -1044,34 +1119,62 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
             }
         }
         // the next chunk's other Gram tiles and T_10
-        if (c > 0 && w < NWJ) other_jobs(cb ^ 1, NWJ);
+        if (c > c_lo && w < NWJ) other_jobs(cb ^ 1, NWJ);
     }
-    if (N > 0) flush(0);
-    if (GATED && N > 0) {
+    if (PROD && c_hi > c_lo) flush(c_lo);
+    if (PROD && GATED && c_hi > c_lo) {
         __syncthreads();
-        if (w == 0) finalize_dg(0);
+        if (w == 0) finalize_dg(c_lo);
     }
-    if (dS0) {
+    if (RECUR && dS0) {
 #pragma unroll
         for (int s = 0; s < KT; ++s)
             *reinterpret_cast<f32x4 *>(dS0 + (head * DV + v0 + r) * DK + 16 * s + 4 * g) = Dt[s];
     }
 }
 
+// Workgroups per (b, h) of the products-only pass: as many as fill the
+// compute units once.  Fewer than 4 means the single-pass kernel: per chunk
+// the recursion pass takes about half the single pass's time and the
+// products pass about as long as the single pass (the clock drops with
+// every compute unit busy), so two workgroups per (b, h) lose.
+inline int bwd_nsplit(int64_t BH, int N) {
+    const int64_t n = 256 / (BH > 0 ? BH : 1);
+    const int ns = (int)(n < N ? n : N);
+    return ns >= 4 ? ns : 1;
+}
+
+template <typename DT, int DK, int DV, bool GATED, int MODE>
+hipError_t launch_bwd_mode(const ChunkBwdArgs &a, int nsplit, hipStream_t stream) {
+    hipLaunchKernelGGL((chunk_bwd_kernel<DT, DK, DV, sizeof(DT) == 2 ? 32 : 16, GATED, MODE>),
+                       dim3((unsigned)(a.B * a.H * (MODE == 2 ? nsplit : 1))), dim3(DV * 4), 0,
+                       stream, static_cast<const DT *>(a.q), static_cast<const DT *>(a.k),
+                       static_cast<const DT *>(a.v), static_cast<const DT *>(a.beta), a.g,
+                       static_cast<const DT *>(a.dout), a.dS_T, static_cast<const DT *>(a.h),
+                       static_cast<DT *>(a.dq), static_cast<DT *>(a.dk), static_cast<DT *>(a.dv),
+                       static_cast<DT *>(a.dbeta), a.dg, a.dS0, static_cast<DT *>(a.dsb),
+                       static_cast<DT *>(a.dsz), (int)a.T, (int)a.H, nsplit);
+    return hipGetLastError();
+}
+
+// One reverse pass per (b, h), or, where that leaves compute units idle and
+// the caller gave the scratch (dsb, dsz), the recursion pass then the
+// products pass over nsplit runs of chunks per (b, h).
 template <typename DT, int DK, int DV, bool GATED>
 hipError_t launch_bwd_gate(const ChunkBwdArgs &a, hipStream_t stream) {
     constexpr int C = sizeof(DT) == 2 ? 32 : 16;
     if constexpr (!bwd_fits<DT, DK, DV, C, GATED>()) {
         return hipErrorInvalidValue;
     } else {
-        hipLaunchKernelGGL((chunk_bwd_kernel<DT, DK, DV, C, GATED>), dim3((unsigned)(a.B * a.H)),
-                           dim3(DV * 4), 0, stream, static_cast<const DT *>(a.q),
-                           static_cast<const DT *>(a.k), static_cast<const DT *>(a.v),
-                           static_cast<const DT *>(a.beta), a.g, static_cast<const DT *>(a.dout),
-                           a.dS_T, static_cast<const DT *>(a.h), static_cast<DT *>(a.dq),
-                           static_cast<DT *>(a.dk), static_cast<DT *>(a.dv),
-                           static_cast<DT *>(a.dbeta), a.dg, a.dS0, (int)a.T, (int)a.H);
-        return hipGetLastError();
+        if constexpr (BwdCfg<DT, DK, DV, C>::DBUF) {
+            const int ns = bwd_nsplit(a.B * a.H, (int)((a.T + C - 1) / C));
+            if (a.dsb && a.dsz && ns >= 2) {
+                const hipError_t e = launch_bwd_mode<DT, DK, DV, GATED, 1>(a, 1, stream);
+                if (e != hipSuccess) return e;
+                return launch_bwd_mode<DT, DK, DV, GATED, 2>(a, ns, stream);
+            }
+        }
+        return launch_bwd_mode<DT, DK, DV, GATED, 0>(a, 1, stream);
     }
 }
 

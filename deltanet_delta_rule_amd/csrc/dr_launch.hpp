@@ -64,6 +64,9 @@ hipError_t launch_kda_chunk(const ChunkFwdArgs &a, hipStream_t stream);
 // checkpoints the forward kernel wrote with chunk = chunk_bwd_chunk(bf16);
 // dS_T and dS0 may be nullptr.  g, when set, is the log forget gate [B,T,H]
 // (fp32) of the gated rule, and dg [B,T,H] (fp32) receives its gradient.
+// dsb (like h) and dsz ([B,T,H,Dv], input dtype), when both are set, are
+// scratch for the two-pass schedule (the gradient of every chunk's state,
+// and the solve's Z).
 struct ChunkBwdArgs {
     const void *q, *k, *v, *beta, *dout;
     const float *dS_T;
@@ -74,6 +77,7 @@ struct ChunkBwdArgs {
     int Dk, Dv;
     const float *g = nullptr;
     float *dg = nullptr;
+    void *dsb = nullptr, *dsz = nullptr;
 };
 
 hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, bool bf16, hipStream_t stream);

@@ -303,9 +303,13 @@ def test_step_ex_unsupported_and_empty(lib):
 def test_backward_workspace_size(lib):
     f = lib.delta_rule_chunk_bwd_workspace_bytes
     # bf16: 32-token chunks, bf16 states; fp32: 16-token chunks, fp32 states;
-    # one state per chunk and head
-    assert f(2, 100, 3, 64, 32, dr.DR_BF16) == 2 * 3 * 4 * 32 * 64 * 2
-    assert f(2, 100, 3, 64, 32, dr.DR_F32) == 2 * 3 * 7 * 32 * 64 * 4
+    # one state per chunk and head (the forward checkpoints), as much again
+    # for the gradients of the chunk states, and one [B,T,H,Dv] tensor of the
+    # input dtype (the solve's Z), each part rounded up to 256 bytes
+    al = lambda x: (x + 255) // 256 * 256
+    assert f(2, 100, 3, 64, 32, dr.DR_BF16) == 2 * al(2 * 3 * 4 * 32 * 64 * 2) + al(2 * 100 * 3 * 32 * 2)
+    assert f(2, 100, 3, 64, 32, dr.DR_F32) == 2 * al(2 * 3 * 7 * 32 * 64 * 4) + al(2 * 100 * 3 * 32 * 4)
+    assert f(1, 3, 1, 16, 16, dr.DR_BF16) == 2 * al(16 * 16 * 2) + al(3 * 16 * 2)
     assert f(1, 0, 1, 16, 16, dr.DR_BF16) == 0
     assert f(1, 10, 1, 24, 16, dr.DR_BF16) == 0   # unsupported size
     assert f(-1, 10, 1, 16, 16, dr.DR_BF16) == 0

@@ -96,6 +96,24 @@ def test_backward_layer_shape_sampled_heads():
     _check(W.get("layer_1p3b", T=512), heads=[(0, 0), (3, 7), (7, 15)])
 
 
+@pytest.mark.parametrize("gated", [False, True])
+def test_backward_single_pass_schedule(gated):
+    # more (b, h) than half the compute units: one reverse pass per (b, h)
+    w = W.get("layer_1p3b", B=9, H=16, T=80, Dk=64, Dv=64, gate_amax=4.0 if gated else 0.0,
+              seed=7400)
+    _check(w, heads=[(0, 0), (4, 9), (8, 15)])
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_backward_chunk_runs_with_empty_workgroups(gated):
+    # 40 (b, h): the recursion pass, then six workgroups per (b, h) over 8
+    # chunks in runs of two, the last two workgroups without chunks (the
+    # sampled-heads layer test covers the single pass at 128 (b, h))
+    w = W.get("layer_1p3b", B=5, H=8, T=250, Dk=64, Dv=64, gate_amax=4.0 if gated else 0.0,
+              seed=7500)
+    _check(w, heads=[(0, 0), (2, 5), (4, 7)])
+
+
 def test_backward_empty_sequence_passes_the_state_gradient():
     w = W.get("long_prefill", H=2, T=0)
     d = to_dev(W.generate(w))
@@ -212,7 +230,7 @@ def test_checkpoints_are_the_prefix_states(name):
                                       d["S0"], dst.cuda(), workspace=ws)
     torch.cuda.synchronize()
     n = (w.T + 31) // 32
-    ck = ws.view(torch.bfloat16).view(w.B, w.H, n, w.Dv, w.Dk)
+    ck = ws[: w.B * w.H * n * w.Dv * w.Dk * 2].view(torch.bfloat16).view(w.B, w.H, n, w.Dv, w.Dk)
     for c in range(n):
         tp = 32 * c
         if c == 0:
