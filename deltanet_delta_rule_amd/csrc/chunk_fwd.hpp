@@ -870,11 +870,14 @@ struct HeadPtrs {
 // Packed variable-length input (cu != nullptr): sequence b spans tokens
 // cu[b] .. cu[b+1] of the single batch row of T tokens; the bounds are
 // clamped into [0, T] so that no access leaves the buffers whatever cu holds.
+// Sequence b of the launch: batch row b (tokens b T ..), packed sequence b
+// (cu), or, with segL > 0, segment b % segP of batch row b / segP (tokens
+// (b % segP) segL .. of that row, at most segL of them).
 template <typename DT, int DK, int NW>
 __device__ __forceinline__ HeadPtrs<DT> head_ptrs(const DT *q, const DT *k, const DT *v,
                                                   const DT *beta, const float *gl, DT *o,
                                                   const int *cu, int T, int H, int Dv, int nvt,
-                                                  int wave, int r) {
+                                                  int wave, int r, int segP = 0, int segL = 0) {
     // Consecutive workgroup ids are dispatched round-robin over the 8 XCDs
     // (each with its own L2).  Remap so that the value tiles of one head,
     // which read the same K and Q, run on the same XCD.
@@ -890,6 +893,10 @@ __device__ __forceinline__ HeadPtrs<DT> head_ptrs(const DT *q, const DT *k, cons
         const int lo = min(max(cu[b], 0), T);
         const int hi = min(max(cu[b + 1], lo), T);
         t0 = lo;
+        p.T = hi - lo;
+    } else if (segL > 0) {
+        const int lo = min((b % segP) * segL, T), hi = min(lo + segL, T);
+        t0 = (int64_t)(b / segP) * T + lo;
         p.T = hi - lo;
     }
     p.vcol = vt * 16 * NW + wave * 16 + r;
@@ -1222,7 +1229,7 @@ __global__ __launch_bounds__((PAIR ? 192 : 128) * NW) __attribute__((amdgpu_wave
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const float *__restrict__ gl, const float *S0,
     DT *__restrict__ o, float *S_T, DT *__restrict__ hs, const int *__restrict__ cu, int T,
-    int H, int Dv, int nvt, float scale, float *Mst) {
+    int H, int Dv, int nvt, float scale, float *Mst, int segP, int segL) {
     typedef ChunkCfg<DT, DK, C, NW> G;
     constexpr int NT = G::NT, ND = G::ND;
     constexpr int NSW = (PAIR ? 2 : 1) * NW;  // state waves
@@ -1239,19 +1246,26 @@ __global__ __launch_bounds__((PAIR ? 192 : 128) * NW) __attribute__((amdgpu_wave
         const int sw = mrow ? wave - NW : wave;
         if (mrow) {
             v = nullptr;
-            S0 = S_T = Mst;
+            S0 = nullptr;
+            S_T = Mst;
             Dv = DK;
         }
         const HeadPtrs<DT> p =
-            head_ptrs<DT, DK, NW>(q, k, v, beta, gl, o, cu, T, H, Dv, nvt, sw, r);
+            head_ptrs<DT, DK, NW>(q, k, v, beta, gl, o, cu, T, H, Dv, nvt, sw, r, segP, segL);
         const int N = (p.T + C - 1) / C;
         f32x4 Sacc[ND], X[NT], Y[NT];
         ChunkOperands<DT, DK, C, NW> op;
         if (mrow) {
 #pragma unroll
             for (int mt = 0; mt < NT; ++mt) op.fv[mt] = typename Frag<DT>::k16{};
-        }
-        if (S0) {
+            // the map starts as the identity: row vcol of this lane
+            const int row = p.vcol;
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    Sacc[dt][i] = state_col<G::KSD>(dt, g) + i == row ? 1.f : 0.f;
+        } else if (S0) {
 #pragma unroll
             for (int dt = 0; dt < ND; ++dt)
                 Sacc[dt] = *reinterpret_cast<const f32x4 *>(S0 + p.sbase + state_col<G::KSD>(dt, g));
@@ -1304,7 +1318,7 @@ __global__ __launch_bounds__((PAIR ? 192 : 128) * NW) __attribute__((amdgpu_wave
         // --------------------------- preparation waves ---------------------------
         __builtin_amdgcn_s_setprio(3);
         const HeadPtrs<DT> p =
-            head_ptrs<DT, DK, NW>(q, k, v, beta, gl, o, cu, T, H, Dv, nvt, 0, r);
+            head_ptrs<DT, DK, NW>(q, k, v, beta, gl, o, cu, T, H, Dv, nvt, 0, r, segP, segL);
         const int N = (p.T + C - 1) / C;
         switch (wave - NSW) {
         case 0: prep_role<DT, DK, C, NW, 0, GATED, L2, NOOUT>(sm, p, p.T, N, lane); break;
@@ -1338,7 +1352,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const float *__restrict__ gl, const float *S0,
     DT *__restrict__ o, float *S_T, DT *__restrict__ hs, const int *__restrict__ cu, int T,
-    int H, int Dv, int nvt, float scale) {
+    int H, int Dv, int nvt, float scale, int segP, int segL) {
     typedef ChunkCfg<DT, DK, C, NW> G;
     constexpr int ND = G::ND;
     __shared__ __attribute__((aligned(16))) SerialSmem<DT, DK, C, NW, GATED, L2> sm;
@@ -1346,7 +1360,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
     const int g = lane >> 4, r = lane & 15;
-    const HeadPtrs<DT> p = head_ptrs<DT, DK, NW>(q, k, v, beta, gl, o, cu, T, H, Dv, nvt, wave, r);
+    const HeadPtrs<DT> p =
+        head_ptrs<DT, DK, NW>(q, k, v, beta, gl, o, cu, T, H, Dv, nvt, wave, r, segP, segL);
 
     f32x4 Sacc[ND];
     if (S0) {
@@ -1412,7 +1427,7 @@ hipError_t launch_cfg(const ChunkFwdArgs &a, hipStream_t stream) {
             hipLaunchKernelGGL((chunk_fwd_ws_kernel<DT, DK, C, NW, GATED, L2, true>),
                                dim3((unsigned)grid), dim3(128 * NW), 0, stream, q, k, v, beta, a.g,
                                a.S0, o, a.S_T, static_cast<DT *>(a.h), a.cu, (int)a.T, (int)a.H,
-                               a.Dv, nvt, a.scale, nullptr);
+                               a.Dv, nvt, a.scale, nullptr, a.segP, a.segL);
             return hipGetLastError();
         }
     }
@@ -1420,19 +1435,19 @@ hipError_t launch_cfg(const ChunkFwdArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL((chunk_fwd_ws_kernel<DT, DK, C, NW, GATED, L2>), dim3((unsigned)grid),
                            dim3(128 * NW), 0, stream, q, k, v, beta, a.g, a.S0, o, a.S_T,
                            static_cast<DT *>(a.h), a.cu,
-                           (int)a.T, (int)a.H, a.Dv, nvt, a.scale, nullptr);
+                           (int)a.T, (int)a.H, a.Dv, nvt, a.scale, nullptr, a.segP, a.segL);
     } else {
         hipLaunchKernelGGL((chunk_fwd_serial_kernel<DT, DK, C, NW, GATED, L2>), dim3((unsigned)grid),
                            dim3(64 * NW), 0, stream, q, k, v, beta, a.g, a.S0, o, a.S_T,
                            static_cast<DT *>(a.h), a.cu,
-                           (int)a.T, (int)a.H, a.Dv, nvt, a.scale);
+                           (int)a.T, (int)a.H, a.Dv, nvt, a.scale, a.segP, a.segL);
     }
     return hipGetLastError();
 }
 
 // The zero-state pass and the transition-map pass of the segment-parallel
 // schedule in one launch (PAIR): value rows from zero states into a.S_T and
-// the d_k rows of each segment's map in M (identity in, map out, in place).
+// the d_k rows of each segment's map (from the identity) into M.
 template <typename DT, int DK, int C>
 hipError_t launch_pair_cfg(const ChunkFwdArgs &a, float *M, hipStream_t stream) {
     constexpr int NW = 4;
@@ -1443,7 +1458,7 @@ hipError_t launch_pair_cfg(const ChunkFwdArgs &a, float *M, hipStream_t stream) 
                        static_cast<const DT *>(a.q), static_cast<const DT *>(a.k),
                        static_cast<const DT *>(a.v), static_cast<const DT *>(a.beta), nullptr,
                        nullptr, nullptr, a.S_T, nullptr, a.cu, (int)a.T, (int)a.H, a.Dv, nvt,
-                       a.scale, M);
+                       a.scale, M, a.segP, a.segL);
     return hipGetLastError();
 }
 

@@ -31,13 +31,17 @@ struct ChunkFwdArgs {
     bool l2;
     const float *gk = nullptr;
     bool recurrent = false;
+    // segment view (cu unset, chunked kernels of the plain and gated rule):
+    // sequence b is segment b % segP of batch row b / segP, tokens
+    // (b % segP) segL .. + segL of that row (B counts segments, T the row)
+    int segP = 0, segL = 0;
 };
 
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
 // a without outputs or initial state (value rows from zero states into
 // a.S_T) and, in the same launch, the d_k x d_k transition map of each
-// sequence in M (read as the incoming map, written back); plain rule, bf16,
-// d_k = d_v = 128, chunks of 32 or 64, else hipErrorNotSupported.
+// sequence (from the identity) into M; plain rule, bf16, d_k = d_v = 128,
+// chunks of 32 or 64, else hipErrorNotSupported (before any launch).
 hipError_t launch_chunk_state_pair(const ChunkFwdArgs &a, float *M, bool bf16,
                                    hipStream_t stream);
 hipError_t launch_fused_recurrent(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);

@@ -284,29 +284,34 @@ hipError_t launch_chunk_fwd_segmented(const ChunkFwdArgs &a, const SegPlan &pl, 
     float *M = reinterpret_cast<float *>(base + align256(nseg * a.H * (int64_t)a.Dv * a.Dk * 4));
     int *cu = reinterpret_cast<int *>(reinterpret_cast<char *>(M) +
                                       align256(nseg * a.H * (int64_t)a.Dk * a.Dk * 4));
-    const int64_t nmat = nseg * a.H;
-    const int64_t n_init = std::max<int64_t>(nmat * a.Dk * a.Dk / 4, nseg + 1);
-    hipLaunchKernelGGL(seg_init_kernel, dim3((unsigned)((n_init + 255) / 256)), dim3(256), 0,
-                       stream, M, cu, nmat, a.Dk, (int)a.B, pl.P, (int)a.T, pl.L);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-
-    ChunkFwdArgs s = a;  // the segments as packed sequences of one row of B*T tokens
-    s.cu = cu;
+    ChunkFwdArgs s = a;
     s.B = nseg;
-    s.T = a.B * a.T;
     s.h = nullptr;
     // 1. H_p from zero states, no outputs
     s.S0 = nullptr;
     s.o = nullptr;
     s.S_T = Hs;
-    // 2. M_p: v = 0, S = I in place, d_k value rows.  Where the shape allows,
-    // 1 and 2 are one launch that shares each chunk's loads, Gram tiles and
-    // inverses between the value rows and the map rows.
+    // 2. M_p: v = 0 from S = I, d_k value rows.  Where the shape allows, 1
+    // and 2 are one launch that shares each chunk's loads, Gram tiles and
+    // inverses between the value rows and the map rows, and the kernels find
+    // each segment's tokens themselves (segment view: no offsets array, no
+    // set-up launch).
+    s.segP = pl.P;
+    s.segL = pl.L;
     ChunkFwdArgs pr = s;
     pr.chunk = SEG_PAIR_CHUNK;
-    e = launch_chunk_state_pair(pr, M, bf16, stream);
+    hipError_t e = launch_chunk_state_pair(pr, M, bf16, stream);
     if (e == hipErrorNotSupported) {
+        // otherwise the segments as packed sequences of one row of B*T
+        // tokens, and M starts as stored identities
+        const int64_t nmat = nseg * a.H;
+        const int64_t n_init = std::max<int64_t>(nmat * a.Dk * a.Dk / 4, nseg + 1);
+        hipLaunchKernelGGL(seg_init_kernel, dim3((unsigned)((n_init + 255) / 256)), dim3(256), 0,
+                           stream, M, cu, nmat, a.Dk, (int)a.B, pl.P, (int)a.T, pl.L);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        s.segP = s.segL = 0;
+        s.cu = cu;
+        s.T = a.B * a.T;
         if ((e = launch_chunk_fwd(s, bf16, stream)) != hipSuccess) return e;
         ChunkFwdArgs m = s;
         m.v = nullptr;
