@@ -362,13 +362,18 @@ dr_status delta_rule_recurrent_step_ex(const void *q, const void *k, const void 
  * states of every chunk are kept and the chunk-internal quantities
  * recomputed).  The call first reruns the forward pass to store each chunk's
  * incoming state in `workspace` (in `dtype`, the precision the backward's
- * products use it in), then walks the chunks in reverse.
+ * products use it in), then walks the chunks in reverse (when B*H is small:
+ * a reverse pass over the state-gradient recursion alone, then the
+ * gradients of the chunks formed in parallel from its results).
  *
  *   q, k, v, beta, S0   the forward inputs, as in delta_rule_chunk_fwd
  *   workspace           device memory of at least
  *                       delta_rule_chunk_bwd_workspace_bytes(B,T,H,Dk,Dv,dtype)
  *                       bytes (16-byte aligned; contents on return: the
- *                       forward checkpoints); may be NULL when T == 0
+ *                       forward checkpoints, [B,H,N,Dv,Dk] in the input
+ *                       dtype at its start, then scratch of the two-pass
+ *                       schedule that runs when B*H is small); may be NULL
+ *                       when T == 0
  *   Outputs must not overlap the inputs, the workspace or each other.
  * Sizes as delta_rule_chunk_fwd (Dk, Dv in {16,32,64,128}); the chunk length
  * is chosen by the library (32 tokens for bf16, 16 for fp32).  Errors as
@@ -424,7 +429,8 @@ int delta_rule_last_hip_error(void);
  * dr_chunk_opts; 2.7.0: the segment-parallel schedule's workspace in
  * dr_chunk_opts and delta_rule_chunk_fwd_workspace_bytes; 2.8.0:
  * delta_rule_chunk_fwd_noalloc and DR_ERR_SCRATCH; 2.9.0:
- * gated_delta_rule_chunk_bwd). */
+ * gated_delta_rule_chunk_bwd; 2.10.0: the backward's workspace also holds
+ * the scratch of its two-pass schedule). */
 int delta_rule_version(void);
 
 #ifdef __cplusplus
