@@ -68,6 +68,36 @@ __device__ __forceinline__ float2 lvl_factor(const float2 (&e)[8], int s, int L)
     return f;
 }
 
+// Eight sums over the 64 lanes at once: lane l receives the sum of v[l >> 3]
+// (lanes 8s .. 8s + 7 hold token s's).  Each exchange step halves the values
+// a lane keeps -- lane xor 32 (the wave halves swap by permlane32), xor 16
+// (rows by permlane16), xor 8 (a DPP rotation by 8 within each row) -- and
+// sums the half it keeps with its partner's copy of it; three DPP steps then
+// sum the 8-lane groups.  Ten exchanges in a dependent chain six deep, where
+// eight separate sums take 48 in eight chains of six.
+__device__ __forceinline__ float batch_sum8(const float (&v)[8], int lane) {
+    float u[4], w[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // lower half keeps token i, upper half token 4 + i
+        const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]),
+                                                        __float_as_uint(v[4 + i]), false, false);
+        u[i] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        // row r (16 lanes) keeps token 2 r + i
+        const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(u[i]),
+                                                        __float_as_uint(u[2 + i]), false, false);
+        w[i] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    }
+    // lanes 0-7 of a row keep token 2 r, lanes 8-15 token 2 r + 1
+    const bool upper = lane & 8;
+    const float send = upper ? w[0] : w[1];
+    const float keep = upper ? w[1] : w[0];
+    return group_sum<8>(keep + dpp_move<0x128>(send));  // row_ror:8
+}
+
 __device__ __forceinline__ float lo_bf16(unsigned x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float hi_bf16(unsigned x) { return __uint_as_float(x & 0xffff0000u); }
 
@@ -265,20 +295,33 @@ __global__ __launch_bounds__(512) void kda_pipe_kernel(
 #pragma unroll
             for (int s = 6; s >= 0; --s) Bk[s] = fmul2(Bk[s + 1], e[s + 1]);
             *reinterpret_cast<float2 *>(&sm.hq[wave][2 * p]) = F[7];
-            float pdl = 0.f;
+            // q_t . k_t (and with L2 |k_t|^2, |q_t|^2) of the quarter's 8
+            // tokens, each summed over the 64 lanes' channel pairs at once
+            float qk[8];
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                const float k0 = lo_bf16(x.k[s]), k1 = hi_bf16(x.k[s]);
-                const float q0 = lo_bf16(x.q[s]), q1 = hi_bf16(x.q[s]);
+                qk[s] = lo_bf16(x.q[s]) * lo_bf16(x.k[s]) + hi_bf16(x.q[s]) * hi_bf16(x.k[s]);
                 nk[s] = nq[s] = 1.f;
-                if constexpr (L2) {
-                    nk[s] = rsqrtf(wave_sum(k0 * k0 + k1 * k1) + 1e-6f);
-                    nq[s] = rsqrtf(wave_sum(q0 * q0 + q1 * q1) + 1e-6f);
-                }
-                const float pd = wave_sum(q0 * k0 + q1 * k1) * (nq[s] * nk[s]);
-                pdl = lane == s ? pd : pdl;
             }
-            if (lane < 8) sm.pdiag[8 * wave + lane] = pdl;
+            float pd = batch_sum8(qk, lane);  // token lane >> 3
+            if constexpr (L2) {
+                float kk[8], qq[8];
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const float k0 = lo_bf16(x.k[s]), k1 = hi_bf16(x.k[s]);
+                    const float q0 = lo_bf16(x.q[s]), q1 = hi_bf16(x.q[s]);
+                    kk[s] = k0 * k0 + k1 * k1;
+                    qq[s] = q0 * q0 + q1 * q1;
+                }
+                const float tk = batch_sum8(kk, lane), tq = batch_sum8(qq, lane);
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    nk[s] = rsqrtf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(tk), 8 * s)) + 1e-6f);
+                    nq[s] = rsqrtf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(tq), 8 * s)) + 1e-6f);
+                }
+                pd *= rsqrtf(tk + 1e-6f) * rsqrtf(tq + 1e-6f);
+            }
+            if ((lane & 7) == 0) sm.pdiag[8 * wave + (lane >> 3)] = pd;
             // levels 8, 4, 2, 1 lie inside the quarter's 16-token block;
             // level 16 here for the quarters on either side of the block
             // boundary (1: columns, 2: rows), the others need a neighbour's
