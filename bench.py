@@ -264,15 +264,19 @@ def bench_gated_chunk(torch, dr, W, reps=20, name="gated_layer_1p3b", l2=False):
     d = {n: (None if t is None else t.to(dev)) for n, t in x.items()}
     o = torch.empty((w.B, w.T, w.H, w.Dv), dtype=w.torch_dtype, device=dev)
     st = torch.empty((w.B, w.H, w.Dv, w.Dk), dtype=torch.float32, device=dev)
+    # the segment-parallel schedule's workspace (where the shape has a plan:
+    # the small model), allocated once, before timing
+    need = dr.chunk_fwd_workspace_bytes(w.B, w.T, w.H, w.Dk, w.Dv, w.chunk, w.torch_dtype)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else False
 
     def step():
         if d["g"] is None:
             dr.delta_rule_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["S0"], chunk=w.chunk,
-                                    o=o, S_T=st, use_qk_l2norm_in_kernel=l2)
+                                    o=o, S_T=st, use_qk_l2norm_in_kernel=l2, workspace=ws)
         else:
             dr.gated_delta_rule_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["S0"],
                                           chunk=w.chunk, o=o, S_T=st,
-                                          use_qk_l2norm_in_kernel=l2)
+                                          use_qk_l2norm_in_kernel=l2, workspace=ws)
 
     for _ in range(3):
         step()
@@ -556,8 +560,10 @@ def main():
     if not args.no_small_model:
         log("small model: B4 H8 T2048 d64 chunked forward")
         out["small_model"] = bench_gated_chunk(torch, dr, W, name="small_model")
-        out["small_model"]["kernel"] = ("chunk_fwd_ws_kernel<bf16, Dk=64, C=64, NW=4> "
-                                        "(4 state + 4 preparation waves)")
+        out["small_model"]["kernel"] = (
+            "segment-parallel schedule, 8 segments of 256 tokens per sequence: "
+            "chunk_fwd_ws_kernel<bf16, Dk=64, C=32, NW=4> with map rows (12 waves), "
+            "seg_chain_kernel<64>, chunk_fwd_ws_kernel<bf16, Dk=64, C=64, NW=4>")
     if not args.no_decode:
         log("decode: 256 steps of B128 H16 d128")
         out["decode"] = bench_decode(torch, dr, W)

@@ -135,7 +135,9 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
     // the library's static scratch holds what it needs)
     if ((ws || noalloc) && !cu && !recurrent &&
         (!gk || dr::kda_chunk_supported(a, dtype == DR_BF16))) {
-        const dr::SegPlan pl = dr::seg_plan(B, T, H, (int)Dk, (int)Dv, (int)chunk);
+        const dr::SegPlan pl =
+            dr::seg_plan(B, T, H, (int)Dk, (int)Dv, (int)chunk,
+                         dr::chunk_state_pair_supported(a, dtype == DR_BF16));
         if (noalloc && pl.P > 0) {
             if (pl.bytes > DR_STATIC_SCRATCH_BYTES) return DR_ERR_SCRATCH;
             const hipError_t e = dr::static_scratch(&ws);
@@ -294,7 +296,9 @@ int64_t delta_rule_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, in
     if (B < 0 || T < 0 || H < 0 || !supported_dim(Dk) || !supported_dim(Dv) ||
         !supported_chunk(chunk))
         return -1;
-    return dr::seg_plan(B, T, H, (int)Dk, (int)Dv, (int)chunk).bytes;
+    // the largest plan any rule takes for these sizes (the combined pass
+    // allows the most segments)
+    return dr::seg_plan(B, T, H, (int)Dk, (int)Dv, (int)chunk, true).bytes;
 }
 
 dr_status delta_rule_chunk_fwd_ex(const void *q, const void *k, const void *v,

@@ -14,11 +14,16 @@ hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, bool bf16, hipStream_t stream
     return a.g ? launch_chunk_fwd_gated(a, bf16, stream) : launch_rule<false, false>(a, bf16, stream);
 }
 
+bool chunk_state_pair_supported(const ChunkFwdArgs &a, bool bf16) {
+    return bf16 && !a.g && !a.gk && !a.l2 && !a.recurrent && (a.Dk == 64 || a.Dk == 128) &&
+           a.Dv == a.Dk;
+}
+
 hipError_t launch_chunk_state_pair(const ChunkFwdArgs &a, float *M, bool bf16,
                                    hipStream_t stream) {
-    if (!bf16 || a.g || a.gk || a.l2 || a.recurrent || a.h || a.o || a.S0 || a.Dk != 128 ||
-        a.Dv != a.Dk)
-        return hipErrorNotSupported;
+    if (!chunk_state_pair_supported(a, bf16) || a.h || a.o || a.S0) return hipErrorNotSupported;
+    if (a.Dk == 64)
+        return a.chunk == 32 ? launch_pair_cfg<__bf16, 64, 32>(a, M, stream) : hipErrorNotSupported;
     switch (a.chunk) {
     case 32: return launch_pair_cfg<__bf16, 128, 32>(a, M, stream);
     case 64: return launch_pair_cfg<__bf16, 128, 64>(a, M, stream);

@@ -40,19 +40,24 @@ struct ChunkFwdArgs {
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
 // a without outputs or initial state (value rows from zero states into
 // a.S_T) and, in the same launch, the d_k x d_k transition map of each
-// sequence (from the identity) into M; plain rule, bf16, d_k = d_v = 128,
-// chunks of 32 or 64, else hipErrorNotSupported (before any launch).
+// sequence (from the identity) into M; plain rule, bf16, d_k = d_v in
+// {64, 128} (chunks of 32, or 64 at d_k = 128), else hipErrorNotSupported
+// (before any launch).  chunk_state_pair_supported tells whether a's rule,
+// dtype and sizes allow it.
+bool chunk_state_pair_supported(const ChunkFwdArgs &a, bool bf16);
 hipError_t launch_chunk_state_pair(const ChunkFwdArgs &a, float *M, bool bf16,
                                    hipStream_t stream);
 hipError_t launch_fused_recurrent(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
 // Segment-parallel schedule of the chunked forward (plain or gated rule, no
 // packed sequences): P segments of L tokens (a multiple of the chunk), and
 // the workspace it needs; P = 0 when the plain schedule fills the GPU anyway.
+// combined: the call runs the combined state-and-map pass, which allows
+// shorter segments at d_k <= 64 (never a larger workspace without it).
 struct SegPlan {
     int P, L;
     int64_t bytes;
 };
-SegPlan seg_plan(int64_t B, int64_t T, int64_t H, int Dk, int Dv, int chunk);
+SegPlan seg_plan(int64_t B, int64_t T, int64_t H, int Dk, int Dv, int chunk, bool combined);
 hipError_t launch_chunk_fwd_segmented(const ChunkFwdArgs &a, const SegPlan &pl, void *ws,
                                       bool bf16, hipStream_t stream);
 // Device address of the library's static scratch (DR_STATIC_SCRATCH_BYTES)

@@ -64,7 +64,13 @@ namespace {
 
 constexpr int SEG_CUS = 256;      // compute units of one MI355X
 constexpr int SEG_MIN = 6;        // fewest segments worth three passes
-constexpr int SEG_MIN_CHUNKS = 16;  // shortest segment, in chunks
+// Shortest segment, in chunks: each chain step multiplies by a d_k x d_k
+// map and each pass pays a pipeline fill, so short segments pay only where
+// d_k is small and the state passes are one launch (measured on the small
+// model, B4 H8 T2048 d64: 30 us with segments of 4 chunks against 39 us
+// unsegmented, and 44.5 us when the two state passes were separate
+// launches; at d_k = 128 segments of 4 chunks do not beat the plain walk)
+constexpr int SEG_MIN_CHUNKS = 16, SEG_MIN_CHUNKS_SMALL_DK = 4;
 constexpr int SEG_PAIR_CHUNK = 32;  // chunk of the combined state-and-map pass
 
 // Identity initial state of the M pass (one float4 per thread) and the
@@ -257,12 +263,13 @@ int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
 
-SegPlan seg_plan(int64_t B, int64_t T, int64_t H, int Dk, int Dv, int chunk) {
+SegPlan seg_plan(int64_t B, int64_t T, int64_t H, int Dk, int Dv, int chunk, bool combined) {
     SegPlan pl{0, 0, 0};
     if (B <= 0 || T <= 0 || H <= 0 || chunk <= 0 || B * T > INT32_MAX) return pl;
     const int64_t units = B * H * std::max(1, Dv / 64);  // workgroups of the plain schedule
+    const int min_chunks = combined && Dk <= 64 ? SEG_MIN_CHUNKS_SMALL_DK : SEG_MIN_CHUNKS;
     int64_t P = std::min<int64_t>(SEG_CUS / std::max<int64_t>(units, 1),
-                                  T / (SEG_MIN_CHUNKS * chunk));
+                                  T / (min_chunks * chunk));
     if (P < SEG_MIN) return pl;
     const int64_t L = ((T + P - 1) / P + chunk - 1) / chunk * chunk;
     P = (T + L - 1) / L;

@@ -377,8 +377,12 @@ def test_chunk_fwd_workspace_bytes(lib):
     assert f(8, 2048, 16, 128, 128, 64, dr.DR_BF16) == 0
     # too short to cut into six segments of sixteen chunks
     assert f(1, 6000, 2, 128, 128, 64, dr.DR_BF16) == 0
-    # a batch of small sequences: more segments would not pay for three passes
-    assert f(4, 2048, 8, 64, 64, 64, dr.DR_BF16) == 0
+    # the small-model shape (B4 H8 T2048 d64): with d_k <= 64 segments may be
+    # as short as 4 chunks, so 8 segments of 256 tokens
+    seg64 = 4 * 8 * 8 * 64 * 64 * 4
+    assert f(4, 2048, 8, 64, 64, 64, dr.DR_BF16) == 2 * seg64 + 256
+    # ... but not shorter: 2 chunks per segment would be needed here
+    assert f(4, 1024, 8, 64, 64, 64, dr.DR_BF16) == 0
     assert f(1, 0, 16, 128, 128, 64, dr.DR_BF16) == 0
     # invalid arguments
     assert f(1, 32768, 16, 48, 128, 64, dr.DR_BF16) == -1

@@ -37,15 +37,18 @@ def _run(d, gated, ws, **kw):
                                    **kw)
 
 
-def _check(w, gated=False, x=None, **kw):
+def _check(w, gated=False, x=None, segmented=True, **kw):
     x = W.generate(w) if x is None else x
     d = to_dev(x)
     need = dr.chunk_fwd_workspace_bytes(w.B, w.T, w.H, w.Dk, w.Dv, w.chunk, w.torch_dtype)
-    assert need > 0, "the shape should take the segment-parallel schedule"
+    assert need > 0, "the shape should have a segment plan"
     ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda")
     o, st = _run(d, gated, ws, chunk=w.chunk, **kw)
     torch.cuda.synchronize()
-    assert not torch.isnan(ws[:16]).any(), "workspace untouched: segment schedule not used"
+    if segmented:
+        assert not torch.isnan(ws[:16]).any(), "workspace untouched: segment schedule not used"
+    else:
+        assert torch.isnan(ws).all(), "the plain schedule should have run"
     o_p, st_p = _run(d, gated, False, chunk=w.chunk, **kw)
     ref_x = x
     if kw.get("use_qk_l2norm_in_kernel"):
@@ -70,8 +73,15 @@ def test_one_long_sequence(gated):
 
 @pytest.mark.parametrize("gated", [False, True])
 def test_batch_of_two_flattened(gated):
+    # d = 64: the plain rule takes 21 segments of 5 chunks (the combined
+    # state-and-map pass), the gated rule 6 segments of 17 chunks
     _check(W.get("small_model", B=2, H=2, T=6500, gate_amax=0.5 if gated else 0.0,
                  seed=12100), gated)
+
+
+def test_small_model_config_segments():
+    # the small-model config (B4 H8 T2048 d64): 8 segments of 4 chunks
+    _check(W.get("small_model", seed=12150))
 
 
 def test_fp32_inputs():
