@@ -10,21 +10,26 @@
 // (hada.io digest, sections "Chunkwise KDA" and "Transition diagonale-bas
 // rang": the state update is a product of transitions plus rank-one writes;
 // paperlayer summary of arXiv:2406.06484, section 5: associative
-// matrix-valued state updates; the composition of segments follows).  The sequence is cut into P
-// segments of whole chunks and, with the existing chunk kernel on the
-// segments as packed sequences:
+// matrix-valued state updates; the composition of segments follows).  The
+// sequence is cut into P segments of whole chunks and, with the chunk kernel
+// on the segments:
 //   1. H_p: each segment from a zero state, no outputs;
 //   2. M_p: each segment with v = 0 from S = I (d_k value rows), no outputs;
 //   3. a short chain per (sequence, head, 16 state rows):
 //      S_in(p) = S_in(p-1) M_{p-1} + H_{p-1} in fp32, which also gives S_T;
 //   4. each segment from its true S_in, writing the outputs.
-// Steps 1, 2 and 4 run P times as many workgroups as the plain schedule; the
-// total work is about three plain passes, and a chunk step costs more when
-// the whole GPU shares HBM (~2.4 us against ~1.7 us for a few workgroups at
-// d = 128), so the schedule is used only with at least six segments of at
-// least sixteen chunks each (measured: B1 H16 T32768 with 8 segments runs in
-// 0.59x the time of the plain schedule; B4 H8 T2048 with 8 segments of 4
-// chunks in 1.45x).
+// For the plain rule in bf16 with d_k = d_v in {64, 128}, 1 and 2 are one
+// launch of the chunk kernel's map-rows specialisation (value rows and map
+// rows on the same staged K, Gram tiles and inverses), and the kernels find
+// each segment's tokens from (P, L) themselves; otherwise the segments run
+// as packed sequences after a set-up kernel that writes the identities and
+// the offsets.  Steps 1, 2 and 4 run P times as many workgroups as the plain
+// schedule, and a chunk step costs more when the whole GPU shares HBM, so
+// the schedule needs at least six segments of at least sixteen chunks, or
+// of four chunks at d_k <= 64 with the combined pass (measured: B1 H16
+// T32768 d128, 8 segments: 303 us against 880 us for the plain schedule;
+// B4 H8 T2048 d64, 8 segments of 4 chunks: 31 us against 39 us, and 44.5 us
+// when 1 and 2 were separate launches).
 #include <algorithm>
 #include <mutex>
 

@@ -178,10 +178,13 @@ enum {
  *               each segment's affine state map S_out = S_in M + H, chain the
  *               maps in fp32, and run the segments again from their true
  *               incoming states for the outputs (about three passes of work
- *               on P times as many workgroups).  Used only when
- *               workspace_bytes >= delta_rule_chunk_fwd_workspace_bytes(...)
- *               > 0; otherwise the plain schedule runs and the workspace is
- *               not touched.  Results agree with the plain schedule up to
+ *               on P times as many workgroups; the first two are one launch
+ *               for the plain rule in bf16 with Dk = Dv in {64, 128}).  Used
+ *               only when workspace_bytes >=
+ *               delta_rule_chunk_fwd_workspace_bytes(...) > 0 (the call may
+ *               plan fewer segments, and use less of it, for other rules);
+ *               otherwise the plain schedule runs and the workspace is not
+ *               touched.  Results agree with the plain schedule up to
  *               rounding.
  */
 typedef struct dr_chunk_opts {
@@ -197,9 +200,10 @@ typedef struct dr_chunk_opts {
 
 /*
  * Bytes of workspace for the segment-parallel schedule of
- * delta_rule_chunk_fwd_ex on this shape (B sequences of T tokens), or 0 when
- * the plain schedule already fills the GPU (the schedule is then never used);
- * -1 for an unsupported dtype, dimension or chunk.  Pure host arithmetic.
+ * delta_rule_chunk_fwd_ex on this shape (B sequences of T tokens; enough for
+ * every rule and dtype), or 0 when the plain schedule already fills the GPU
+ * (the schedule is then never used); -1 for an unsupported dtype, dimension
+ * or chunk.  Pure host arithmetic.
  */
 int64_t delta_rule_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk,
                                              int64_t Dv, int64_t chunk, dr_dtype dtype);
