@@ -417,6 +417,12 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
     for (int i = tid; i < C * LDC; i += nthr) {
         sm.Pm[i] = sm.Gl[0][i] = sm.Gl[1][i] = sm.Tm[i] = sm.Dm[i] = sm.Gs[i] = from_f32<DT>(0.f);
     }
+    // Tm, Pm and dO by chunk parity: mode 1 keeps two of each (the second in
+    // the LDS its unused products would take: Dm, Gs, Vs), so that the next
+    // chunk's Gram tiles and inverses form while this chunk's are read
+    auto tm_buf = [&](int bb) -> DT * { return MODE == 1 && bb ? sm.Dm : sm.Tm; };
+    auto pm_buf = [&](int bb) -> DT * { return MODE == 1 && bb ? sm.Gs : sm.Pm; };
+    auto os_buf = [&](int bb) -> DT * { return MODE == 1 && bb ? sm.Vs : sm.Os; };
     // dS^T of this wave's value columns: tile s holds dS^T[16s + 4g + i][v0 + r]
     f32x4 Dt[RECUR ? KT : 1];
 #pragma unroll
@@ -591,13 +597,13 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
             for (int i = 0; i < 4; ++i) tmp[i] = frag_get(fa, i) * sm.betas[bb][16 + r];
             cvt4(tmp, fa);
         }
-        frag_cols16(sm.Tm, LDC, 0, 0, lane, fb);
+        frag_cols16(tm_buf(bb), LDC, 0, 0, lane, fb);
         mk<DT>(m1, fa, fb);
         f32x4 t10v = zero4();
-        frag_rows(sm.Tm, LDC, 16, 16, lane, fa);
+        frag_rows(tm_buf(bb), LDC, 16, 16, lane, fa);
         cvt4(m1, fb);
         mk<DT>(t10v, fa, fb);
-        put_tile(sm.Tm, LDC, 16, 0, -t10v, lane, [](int, int) { return true; });
+        put_tile(tm_buf(bb), LDC, 16, 0, -t10v, lane, [](int, int) { return true; });
     };
 
     // Gram tiles of the chunk in buffer set bb (K K^T and Q K^T, lower tiles),
@@ -629,7 +635,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
             at[i] = r > x ? sm.betas[bb][16 * ti + r] * acc[i] : 0.f;  // G symmetric
         }
         const f32x4 tinv = inv_unit_lower<DT>(a, at, lane);
-        put_tile(sm.Tm, LDC, 16 * ti, 16 * ti, tinv, lane, [](int x, int y) { return x >= y; });
+        put_tile(tm_buf(bb), LDC, 16 * ti, 16 * ti, tinv, lane, [](int x, int y) { return x >= y; });
     };
     // the diagonal blocks on the last waves (idle in the C x C phase)
     auto diag_jobs = [&](int bb) {
@@ -640,7 +646,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
     // the wave that formed G_10 (the diagonal inverses are done by then)
     constexpr int NOFF = NT * (NT - 1) / 2;  // tiles of G below the diagonal
     constexpr int NJ = NT * (NT + 1) / 2;    // lower tiles of a C x C matrix
-    auto other_jobs = [&](int bb, int nwj) {
+    auto other_jobs = [&](int bb, int nwj, bool with_t10 = true) {
         for (int j = w; j < NOFF + NJ; j += nwj) {
             const bool isP = j >= NOFF;
             int jj = isP ? j - NOFF : j, ti = isP ? 0 : 1;
@@ -651,11 +657,11 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
             }
             const int tj = jj;
             const f32x4 acc = gram_tile(bb, isP, ti, tj);
-            if (isP) put_tile(sm.Pm, LDC, 16 * ti, 16 * tj, acc, lane, [](int x, int y) { return x >= y; });
+            if (isP) put_tile(pm_buf(bb), LDC, 16 * ti, 16 * tj, acc, lane, [](int x, int y) { return x >= y; });
             else put_tile(sm.Gl[bb], LDC, 16 * ti, 16 * tj, acc, lane, [](int x, int y) { return x > y; });
         }
         if constexpr (NT == 2) {
-            if (w == 0) t10(bb);
+            if (with_t10 && w == 0) t10(bb);
         }
     };
     // The last chunk's inputs, its K, Q, beta staged and its Gram tiles;
@@ -674,28 +680,11 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
         __syncthreads();
         other_jobs((c_hi - 1) & 1, NW);
     }
-    constexpr int NWJ = NW < 4 ? NW : 4;  // waves that form the next chunk's Gram tiles
-    for (int c = c_hi - 1; c >= c_lo; --c) {
-        const int len = min(C, T - c * C);
-        const int64_t tok0 = (int64_t)b * T + c * C;
-        const int cb = c & 1;  // buffer set of this chunk's K, Q, beta, decays
-        __syncthreads();
-        // ---------------------------------------------------------------- load
-        if constexpr (PROD) pf.v.store(sm.Vs, LDV, tid);
-        pf.o.store(sm.Os, LDV, tid);
-        if constexpr (PROD) pf.s.store(sm.Sb, LDSK, tid);
-        if constexpr (MODE == 2) {
-            pf.ds.store(sm.Db, LDS_, tid);
-            pf.z.store(sm.Rb, LDV, tid);  // Z; each wave turns its columns into dV
-        }
-        if (c > c_lo) prefetch(std::integral_constant<int, 0>(), c - 1);
-        if constexpr (MODE == 1)
-            if (c > c_lo) prefetch(std::integral_constant<int, 2>(), c - 1);
-        if (PROD && GATED && w == 0 && c + 1 < c_hi) finalize_dg(c + 1);
-        __syncthreads();
-
-        // ------------------------------------------- per-wave value columns
-        if (c > c_lo) prefetch(std::integral_constant<int, 1>(), c - 1);
+    // The column work of chunk (parity cb) for this wave's 16 value columns:
+    // R and E (products modes), dE, Z, dV and the dS update (recursion
+    // modes), publishing E, dV (or Z), dS_{c+1} and the dbeta parts in LDS.
+    f32x4 Dold[G::DBUF ? 1 : KT];  // dS_{c+1} kept for the second dK pass (no DBUF)
+    auto per_wave = [&](int cb) {
         f32x4 R[NT], E[NT], Z[NT];
         {
             // R = V - K S_c^T (S_c rows of this wave's columns as B^T) and
@@ -750,8 +739,8 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
 #pragma unroll
                     for (int kt = 0; kt < NT; ++kt) {
                         if (kt >= mt) {
-                            frag_cols16(sm.Pm, LDC, 16 * kt, 16 * mt, lane, fa[kt]);
-                            frag_cols16(sm.Os, LDV, 16 * kt, v0, lane, fo[kt]);
+                            frag_cols16(pm_buf(cb), LDC, 16 * kt, 16 * mt, lane, fa[kt]);
+                            frag_cols16(os_buf(cb), LDV, 16 * kt, v0, lane, fo[kt]);
                         } else {
                             fa[kt] = fo[kt] = typename Frag<DT>::k16{};
                         }
@@ -784,7 +773,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                     typename Frag<DT>::k16 ft;
 #pragma unroll
                     for (int kt = 0; kt <= mt; ++kt) {
-                        frag_rows(sm.Tm, LDC, 16 * mt, 16 * kt, lane, ft);
+                        frag_rows(tm_buf(cb), LDC, 16 * mt, 16 * kt, lane, ft);
                         mk<DT>(E[mt], ft, frb[kt]);
                     }
                 }
@@ -800,7 +789,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                     typename Frag<DT>::k16 fa;
 #pragma unroll
                     for (int kt = mt; kt < NT; ++kt) {
-                        frag_cols16(sm.Tm, LDC, 16 * kt, 16 * mt, lane, fa);
+                        frag_cols16(tm_buf(cb), LDC, 16 * kt, 16 * mt, lane, fa);
                         mk<DT>(Z[mt], fa, fde[kt]);
                     }
                 }
@@ -869,7 +858,6 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
         }
         // publish S_c^T and dS_{c+1}^T (this wave's columns) for dQ, dK; then
         // the dS update
-        f32x4 Dold[G::DBUF ? 1 : KT];
         if constexpr (!G::DBUF) {
 #pragma unroll
             for (int s2 = 0; s2 < KT; ++s2) Dold[s2] = Dt[s2];
@@ -888,7 +876,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
 #pragma unroll
             for (int mt = 0; mt < NT; ++mt) {
                 f32x4 nz = -Z[mt];
-                frag_cols16(sm.Os, LDV, 16 * mt, v0, lane, fo[mt]);
+                frag_cols16(os_buf(cb), LDV, 16 * mt, v0, lane, fo[mt]);
                 if constexpr (GATED) {
                     // dS <- gamma_last dS + (diag(gamma) dO)^T Q - (diag(gamma) dV)^T K
                     f32x4 od;
@@ -919,207 +907,264 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
                 mk_n<DT, NT>(Dt[s], fb, fdv);
             }
         }
-        // the next chunk's K, Q, beta (loaded since the start of this phase)
-        if (c > c_lo) stage_kqb(cb ^ 1);
-        __syncthreads();
+    };
 
-        // ---------------------- C x C products over all value columns, dbeta
-        // (and the next chunk's diagonal Gram blocks and their inverses)
-        if (c > c_lo) diag_jobs(cb ^ 1);
-        for (int j = w; PROD && j < 2 * NJ; j += NW) {
-            const bool isD = j < NJ;  // dO E^T, else dV E^T
-            int jj = isD ? j : j - NJ, ti = 0;
-            while (jj > ti) { jj -= ti + 1; ++ti; }
-            const int tj = jj;
-            f32x4 acc = zero4();
-            tile_rr<DT, VT>(acc, isD ? sm.Os : sm.Rb, LDV, 16 * ti, sm.Es, LDV, 16 * tj, 0, lane);
-            if constexpr (GATED) {
-                // W = dG (.) tril(K K^T (.) D, -1) + Dm (.) (Q K^T (.) D) off
-                // the diagonal (dL/dD_xy D_xy, D_xy = exp(b_x - b_y)): its row
-                // sums add to dL/db_x, its column sums subtract from dL/db_y.
-                // Dm and dG are stored times D for dQ and dK.
-                f32x4 wv;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int x = 16 * ti + 4 * g + i, y = 16 * tj + r;
-                    const float a = isD ? acc[i] : -acc[i];
-                    wv[i] = x > y ? a * to_f32((isD ? sm.Pm : sm.Gl[cb])[x * LDC + y]) : 0.f;
-                    acc[i] = x > y ? acc[i] * __expf(sm.gt.gb[cb][x] - sm.gt.gb[cb][y]) : acc[i];
-                }
-                float cs = wv[0] + wv[1] + wv[2] + wv[3];
-                cs = xor32_sum(xor16_sum(cs));
-                if (g == 0) sm.gt.wcol[j][r] = cs;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float rs = group_sum<16>(wv[i]);
-                    if (r == 0) sm.gt.wrow[j][4 * g + i] = rs;
-                }
-            }
-            if (isD) {
-                put_tile(sm.Dm, LDC, 16 * ti, 16 * tj, acc, lane, [](int x, int y) { return x >= y; });
-            } else {
-                // dG = -tril(dV E^T, -1), stored with its transpose
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int x = 16 * ti + 4 * g + i, y = 16 * tj + r;
-                    const DT val = from_f32<DT>(x > y ? -acc[i] : 0.f);
-                    if (x >= y) {
-                        sm.Gs[x * LDC + y] = val;
-                        sm.Gs[y * LDC + x] = val;
-                    }
-                }
-            }
-        }
-        for (int t = tid; PROD && t < len; t += nthr) {
-            float sb = 0.f;
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) sb += sm.dbp[ww][t];
-            dbeta[(tok0 + t) * H + h] = from_f32<DT>(sb);
+    constexpr int NWJ = NW < 4 ? NW : 4;  // waves that form the next chunk's Gram tiles
+    if constexpr (MODE == 1) {
+        // Recursion only, two barriers per chunk.  Chunk c's K, Q, beta, dO,
+        // Tm and Pm sit in the buffers of parity c & 1.  With its column work
+        // the waves form chunk c-1's Gram tiles and diagonal inverses (its
+        // inputs were staged one chunk earlier); after the barrier, T_10 of
+        // chunk c-1, the stores of chunk c (dV, Z, dS_{c+1}) and the staging
+        // of chunk c-2 (loaded during the column work).
+        if (N > 0) pf.o.store(os_buf((N - 1) & 1), LDV, tid);
+        if (N > 1) {
+            prefetch(std::integral_constant<int, 1>(), N - 2);
+            prefetch(std::integral_constant<int, 2>(), N - 2);
+            stage_kqb((N - 2) & 1);
+            pf.o.store(os_buf((N - 2) & 1), LDV, tid);
         }
         __syncthreads();
-
-        // ------------------------------------------------------- dQ and dK
-        if constexpr (MODE == 1) {
-            // recursion only: dV, Z and the dS_{c+1} checkpoint leave from LDS
+        for (int c = N - 1; c >= 0; --c) {
+            const int len = min(C, T - c * C);
+            const int64_t tok0 = (int64_t)b * T + c * C;
+            const int cb = c & 1;
+            if (c > 1) {
+                prefetch(std::integral_constant<int, 1>(), c - 2);
+                prefetch(std::integral_constant<int, 2>(), c - 2);
+            }
+            per_wave(cb);
+            if (c > 0) {
+                diag_jobs(cb ^ 1);
+                if (w < NWJ) other_jobs(cb ^ 1, NWJ, false);
+            }
+            __syncthreads();
+            if constexpr (NT == 2)
+                if (c > 0 && w == 0) t10(cb ^ 1);
             store_rows<DT, C, DV, 64 * NW>(dv + (tok0 * H + h) * DV, (int64_t)H * DV, len, sm.Rb,
                                            LDV, tid);
             store_rows<DT, C, DV, 64 * NW>(dsz + (tok0 * H + h) * DV, (int64_t)H * DV, len, sm.Es,
                                            LDV, tid);
             store_rows<DT, DV, DK, 64 * NW>(dsb + (head * N + c) * DV * DK, DK, DV, sm.Db, LDS_,
                                             tid);
-            if (c > c_lo && w < NWJ) other_jobs(cb ^ 1, NWJ);
-            continue;
+            if (c > 1) {
+                stage_kqb(cb);
+                pf.o.store(os_buf(cb), LDV, tid);
+            }
+            __syncthreads();
         }
-        if (c > c_lo) prefetch(std::integral_constant<int, 2>(), c - 1);
-        if (c + 1 < c_hi) flush(c + 1);
-        // dV of all value columns, from its LDS copy, 16 bytes per store
-        store_rows<DT, C, DV, 64 * NW>(dv + (tok0 * H + h) * DV, (int64_t)H * DV, len, sm.Rb, LDV, tid);
-        // The operands along d_k (columns of S_c, K and Q, rows of
-        // dS_{c+1}^T) are read once per key tile and serve all of the wave's
-        // token tiles.
-        f32x4 dKa[G::DBUF ? 1 : NJW * NMU];
-#pragma unroll
-        for (int jj = 0; jj < NJW; ++jj) {
-            const int j = NW <= KT ? w + jj * NW : w % KT;
-            typename Frag<DT>::k16 fs[VT], fkc[NT], fqc[NT], fdb[G::DBUF ? VT : 1];
-#pragma unroll
-            for (int i = 0; i < VT; ++i) frag_cols16(sm.Sb, LDSK, 16 * i, 16 * j, lane, fs[i]);
-#pragma unroll
-            for (int i = 0; i < NT; ++i) {
-                frag_cols16(sm.Ks[cb], LDK, 16 * i, 16 * j, lane, fkc[i]);
-                frag_cols16(sm.Qs[cb], LDK, 16 * i, 16 * j, lane, fqc[i]);
+    } else {
+        for (int c = c_hi - 1; c >= c_lo; --c) {
+            const int len = min(C, T - c * C);
+            const int64_t tok0 = (int64_t)b * T + c * C;
+            const int cb = c & 1;  // buffer set of this chunk's K, Q, beta, decays
+            __syncthreads();
+            // ---------------------------------------------------------------- load
+            if constexpr (PROD) pf.v.store(sm.Vs, LDV, tid);
+            pf.o.store(sm.Os, LDV, tid);
+            if constexpr (PROD) pf.s.store(sm.Sb, LDSK, tid);
+            if constexpr (MODE == 2) {
+                pf.ds.store(sm.Db, LDS_, tid);
+                pf.z.store(sm.Rb, LDV, tid);  // Z; each wave turns its columns into dV
             }
-            if constexpr (G::DBUF) {
+            if (c > c_lo) prefetch(std::integral_constant<int, 0>(), c - 1);
+            if (GATED && w == 0 && c + 1 < c_hi) finalize_dg(c + 1);
+            __syncthreads();
+
+            // ------------------------------------------- per-wave value columns
+            if (c > c_lo) prefetch(std::integral_constant<int, 1>(), c - 1);
+            per_wave(cb);
+            // the next chunk's K, Q, beta (loaded since the start of this phase)
+            if (c > c_lo) stage_kqb(cb ^ 1);
+            __syncthreads();
+
+            // ---------------------- C x C products over all value columns, dbeta
+            // (and the next chunk's diagonal Gram blocks and their inverses)
+            if (c > c_lo) diag_jobs(cb ^ 1);
+            for (int j = w; PROD && j < 2 * NJ; j += NW) {
+                const bool isD = j < NJ;  // dO E^T, else dV E^T
+                int jj = isD ? j : j - NJ, ti = 0;
+                while (jj > ti) { jj -= ti + 1; ++ti; }
+                const int tj = jj;
+                f32x4 acc = zero4();
+                tile_rr<DT, VT>(acc, isD ? sm.Os : sm.Rb, LDV, 16 * ti, sm.Es, LDV, 16 * tj, 0, lane);
+                if constexpr (GATED) {
+                    // W = dG (.) tril(K K^T (.) D, -1) + Dm (.) (Q K^T (.) D) off
+                    // the diagonal (dL/dD_xy D_xy, D_xy = exp(b_x - b_y)): its row
+                    // sums add to dL/db_x, its column sums subtract from dL/db_y.
+                    // Dm and dG are stored times D for dQ and dK.
+                    f32x4 wv;
 #pragma unroll
-                for (int i = 0; i < VT; ++i) frag_cols16(sm.Db, LDS_, 16 * i, 16 * j, lane, fdb[i]);
-            }
-#pragma unroll
-            for (int u = 0; u < NMU; ++u) {
-                const int mt = mt0 + u * MS;
-                if (mt < NT) {
-                    typename Frag<DT>::k16 fa[VT], fb[VT], fm[NT];
-                    // dQ = dO S_c + Dm K   (Dm is zero above the diagonal)
-                    f32x4 aq = zero4();
-#pragma unroll
-                    for (int i = 0; i < VT; ++i) frag_rows(sm.Os, LDV, 16 * mt, 16 * i, lane, fa[i]);
-#pragma unroll
-                    for (int i = 0; i < NT; ++i) frag_rows(sm.Dm, LDC, 16 * mt, 16 * i, lane, fm[i]);
-                    mk_n<DT, VT>(aq, fs, fa);
-                    const f32x4 aq0 = aq;
-                    if constexpr (GATED) aq = aq * sm.gt.gam[cb][16 * mt + r];  // token 16 mt + r
-                    mk_n<DT, NT>(aq, fkc, fm);
-                    // dK = -dV S_c + E dS_{c+1} + Gs K + Dm^T Q
-                    f32x4 an = zero4(), ak = zero4();
-#pragma unroll
-                    for (int i = 0; i < VT; ++i) frag_rows(sm.Rb, LDV, 16 * mt, 16 * i, lane, fb[i]);
-                    mk_n<DT, VT>(an, fs, fb);
-                    if constexpr (G::DBUF) {
-#pragma unroll
-                        for (int i = 0; i < VT; ++i) frag_rows(sm.Es, LDV, 16 * mt, 16 * i, lane, fa[i]);
-                        mk_n<DT, VT>(ak, fdb, fa);
-                        gate_part(cb, j, mt, aq0, an, &ak, false);
-                        if constexpr (GATED) ak = ak * sm.gt.rto[cb][16 * mt + r];
-                    } else {
-                        gate_part(cb, j, mt, aq0, an, nullptr, false);
+                    for (int i = 0; i < 4; ++i) {
+                        const int x = 16 * ti + 4 * g + i, y = 16 * tj + r;
+                        const float a = isD ? acc[i] : -acc[i];
+                        wv[i] = x > y ? a * to_f32((isD ? sm.Pm : sm.Gl[cb])[x * LDC + y]) : 0.f;
+                        acc[i] = x > y ? acc[i] * __expf(sm.gt.gb[cb][x] - sm.gt.gb[cb][y]) : acc[i];
                     }
-                    if constexpr (GATED) an = an * sm.gt.gam[cb][16 * mt + r];
+                    float cs = wv[0] + wv[1] + wv[2] + wv[3];
+                    cs = xor32_sum(xor16_sum(cs));
+                    if (g == 0) sm.gt.wcol[j][r] = cs;
 #pragma unroll
-                    for (int i = 0; i < NT; ++i) frag_rows(sm.Gs, LDC, 16 * mt, 16 * i, lane, fm[i]);
-                    mk_n<DT, NT>(ak, fkc, fm);
+                    for (int i = 0; i < 4; ++i) {
+                        const float rs = group_sum<16>(wv[i]);
+                        if (r == 0) sm.gt.wrow[j][4 * g + i] = rs;
+                    }
+                }
+                if (isD) {
+                    put_tile(sm.Dm, LDC, 16 * ti, 16 * tj, acc, lane, [](int x, int y) { return x >= y; });
+                } else {
+                    // dG = -tril(dV E^T, -1), stored with its transpose
 #pragma unroll
-                    for (int i = 0; i < NT; ++i) frag_cols16(sm.Dm, LDC, 16 * i, 16 * mt, lane, fm[i]);
-                    mk_n<DT, NT>(ak, fqc, fm);
-                    ak = ak - an;
-                    if constexpr (DEFER) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            frag_set(pq[jj * NMU + u], i, aq[i]);
-                            if constexpr (G::DBUF) frag_set(pk[jj * NMU + u], i, ak[i]);
-                        }
-                    } else {
-                        const auto rq = chunk_rsrc(dq, c, rowq, DK), rk = chunk_rsrc(dk, c, rowq, DK);
-                        const int voff = ((16 * mt + r) * (int)rowq + 16 * j + 4 * g) * (int)sizeof(DT);
-                        out4 x;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) frag_set(x, i, aq[i]);
-                        store4(x, rq, voff);
-                        if constexpr (G::DBUF) {
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) frag_set(x, i, ak[i]);
-                            store4(x, rk, voff);
+                    for (int i = 0; i < 4; ++i) {
+                        const int x = 16 * ti + 4 * g + i, y = 16 * tj + r;
+                        const DT val = from_f32<DT>(x > y ? -acc[i] : 0.f);
+                        if (x >= y) {
+                            sm.Gs[x * LDC + y] = val;
+                            sm.Gs[y * LDC + x] = val;
                         }
                     }
-                    if constexpr (!G::DBUF) dKa[jj * NMU + u] = ak;
                 }
             }
-        }
-        if constexpr (!G::DBUF) {
-            // second pass: dS_{c+1} replaces S_c, then dK += E dS_{c+1}
-            __syncthreads();
+            for (int t = tid; PROD && t < len; t += nthr) {
+                float sb = 0.f;
 #pragma unroll
-            for (int s2 = 0; s2 < KT; ++s2)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sm.Sb[(v0 + r) * LDSK + 16 * s2 + 4 * g + i] = from_f32<DT>(Dold[s2][i]);
+                for (int ww = 0; ww < NW; ++ww) sb += sm.dbp[ww][t];
+                dbeta[(tok0 + t) * H + h] = from_f32<DT>(sb);
+            }
             __syncthreads();
+
+            // ------------------------------------------------------- dQ and dK
+            if (c > c_lo) prefetch(std::integral_constant<int, 2>(), c - 1);
+            if (c + 1 < c_hi) flush(c + 1);
+            // dV of all value columns, from its LDS copy, 16 bytes per store
+            store_rows<DT, C, DV, 64 * NW>(dv + (tok0 * H + h) * DV, (int64_t)H * DV, len, sm.Rb, LDV, tid);
+            // The operands along d_k (columns of S_c, K and Q, rows of
+            // dS_{c+1}^T) are read once per key tile and serve all of the wave's
+            // token tiles.
+            f32x4 dKa[G::DBUF ? 1 : NJW * NMU];
 #pragma unroll
             for (int jj = 0; jj < NJW; ++jj) {
                 const int j = NW <= KT ? w + jj * NW : w % KT;
-                typename Frag<DT>::k16 fs[VT];
+                typename Frag<DT>::k16 fs[VT], fkc[NT], fqc[NT], fdb[G::DBUF ? VT : 1];
 #pragma unroll
                 for (int i = 0; i < VT; ++i) frag_cols16(sm.Sb, LDSK, 16 * i, 16 * j, lane, fs[i]);
+#pragma unroll
+                for (int i = 0; i < NT; ++i) {
+                    frag_cols16(sm.Ks[cb], LDK, 16 * i, 16 * j, lane, fkc[i]);
+                    frag_cols16(sm.Qs[cb], LDK, 16 * i, 16 * j, lane, fqc[i]);
+                }
+                if constexpr (G::DBUF) {
+#pragma unroll
+                    for (int i = 0; i < VT; ++i) frag_cols16(sm.Db, LDS_, 16 * i, 16 * j, lane, fdb[i]);
+                }
 #pragma unroll
                 for (int u = 0; u < NMU; ++u) {
                     const int mt = mt0 + u * MS;
                     if (mt < NT) {
-                        typename Frag<DT>::k16 fa[VT];
-                        f32x4 ak = dKa[jj * NMU + u];
+                        typename Frag<DT>::k16 fa[VT], fb[VT], fm[NT];
+                        // dQ = dO S_c + Dm K   (Dm is zero above the diagonal)
+                        f32x4 aq = zero4();
 #pragma unroll
-                        for (int i = 0; i < VT; ++i) frag_rows(sm.Es, LDV, 16 * mt, 16 * i, lane, fa[i]);
-                        if constexpr (GATED) {
-                            f32x4 ed = zero4();
-                            mk_n<DT, VT>(ed, fs, fa);
-                            gate_part(cb, j, mt, zero4(), zero4(), &ed, true);
-                            ak += ed * sm.gt.rto[cb][16 * mt + r];
+                        for (int i = 0; i < VT; ++i) frag_rows(sm.Os, LDV, 16 * mt, 16 * i, lane, fa[i]);
+#pragma unroll
+                        for (int i = 0; i < NT; ++i) frag_rows(sm.Dm, LDC, 16 * mt, 16 * i, lane, fm[i]);
+                        mk_n<DT, VT>(aq, fs, fa);
+                        const f32x4 aq0 = aq;
+                        if constexpr (GATED) aq = aq * sm.gt.gam[cb][16 * mt + r];  // token 16 mt + r
+                        mk_n<DT, NT>(aq, fkc, fm);
+                        // dK = -dV S_c + E dS_{c+1} + Gs K + Dm^T Q
+                        f32x4 an = zero4(), ak = zero4();
+#pragma unroll
+                        for (int i = 0; i < VT; ++i) frag_rows(sm.Rb, LDV, 16 * mt, 16 * i, lane, fb[i]);
+                        mk_n<DT, VT>(an, fs, fb);
+                        if constexpr (G::DBUF) {
+#pragma unroll
+                            for (int i = 0; i < VT; ++i) frag_rows(sm.Es, LDV, 16 * mt, 16 * i, lane, fa[i]);
+                            mk_n<DT, VT>(ak, fdb, fa);
+                            gate_part(cb, j, mt, aq0, an, &ak, false);
+                            if constexpr (GATED) ak = ak * sm.gt.rto[cb][16 * mt + r];
                         } else {
-                            mk_n<DT, VT>(ak, fs, fa);
+                            gate_part(cb, j, mt, aq0, an, nullptr, false);
                         }
+                        if constexpr (GATED) an = an * sm.gt.gam[cb][16 * mt + r];
+#pragma unroll
+                        for (int i = 0; i < NT; ++i) frag_rows(sm.Gs, LDC, 16 * mt, 16 * i, lane, fm[i]);
+                        mk_n<DT, NT>(ak, fkc, fm);
+#pragma unroll
+                        for (int i = 0; i < NT; ++i) frag_cols16(sm.Dm, LDC, 16 * i, 16 * mt, lane, fm[i]);
+                        mk_n<DT, NT>(ak, fqc, fm);
+                        ak = ak - an;
                         if constexpr (DEFER) {
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) frag_set(pk[jj * NMU + u], i, ak[i]);
+                            for (int i = 0; i < 4; ++i) {
+                                frag_set(pq[jj * NMU + u], i, aq[i]);
+                                if constexpr (G::DBUF) frag_set(pk[jj * NMU + u], i, ak[i]);
+                            }
                         } else {
-                            const auto rk = chunk_rsrc(dk, c, rowq, DK);
+                            const auto rq = chunk_rsrc(dq, c, rowq, DK), rk = chunk_rsrc(dk, c, rowq, DK);
+                            const int voff = ((16 * mt + r) * (int)rowq + 16 * j + 4 * g) * (int)sizeof(DT);
                             out4 x;
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) frag_set(x, i, ak[i]);
-                            store4(x, rk, ((16 * mt + r) * (int)rowq + 16 * j + 4 * g) * (int)sizeof(DT));
+                            for (int i = 0; i < 4; ++i) frag_set(x, i, aq[i]);
+                            store4(x, rq, voff);
+                            if constexpr (G::DBUF) {
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) frag_set(x, i, ak[i]);
+                                store4(x, rk, voff);
+                            }
+                        }
+                        if constexpr (!G::DBUF) dKa[jj * NMU + u] = ak;
+                    }
+                }
+            }
+            if constexpr (!G::DBUF) {
+                // second pass: dS_{c+1} replaces S_c, then dK += E dS_{c+1}
+                __syncthreads();
+#pragma unroll
+                for (int s2 = 0; s2 < KT; ++s2)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        sm.Sb[(v0 + r) * LDSK + 16 * s2 + 4 * g + i] = from_f32<DT>(Dold[s2][i]);
+                __syncthreads();
+#pragma unroll
+                for (int jj = 0; jj < NJW; ++jj) {
+                    const int j = NW <= KT ? w + jj * NW : w % KT;
+                    typename Frag<DT>::k16 fs[VT];
+#pragma unroll
+                    for (int i = 0; i < VT; ++i) frag_cols16(sm.Sb, LDSK, 16 * i, 16 * j, lane, fs[i]);
+#pragma unroll
+                    for (int u = 0; u < NMU; ++u) {
+                        const int mt = mt0 + u * MS;
+                        if (mt < NT) {
+                            typename Frag<DT>::k16 fa[VT];
+                            f32x4 ak = dKa[jj * NMU + u];
+#pragma unroll
+                            for (int i = 0; i < VT; ++i) frag_rows(sm.Es, LDV, 16 * mt, 16 * i, lane, fa[i]);
+                            if constexpr (GATED) {
+                                f32x4 ed = zero4();
+                                mk_n<DT, VT>(ed, fs, fa);
+                                gate_part(cb, j, mt, zero4(), zero4(), &ed, true);
+                                ak += ed * sm.gt.rto[cb][16 * mt + r];
+                            } else {
+                                mk_n<DT, VT>(ak, fs, fa);
+                            }
+                            if constexpr (DEFER) {
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) frag_set(pk[jj * NMU + u], i, ak[i]);
+                            } else {
+                                const auto rk = chunk_rsrc(dk, c, rowq, DK);
+                                out4 x;
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) frag_set(x, i, ak[i]);
+                                store4(x, rk, ((16 * mt + r) * (int)rowq + 16 * j + 4 * g) * (int)sizeof(DT));
+                            }
                         }
                     }
                 }
             }
+            // the next chunk's other Gram tiles and T_10
+            if (c > c_lo && w < NWJ) other_jobs(cb ^ 1, NWJ);
         }
-        // the next chunk's other Gram tiles and T_10
-        if (c > c_lo && w < NWJ) other_jobs(cb ^ 1, NWJ);
     }
     if (PROD && c_hi > c_lo) flush(c_lo);
     if (PROD && GATED && c_hi > c_lo) {
