@@ -26,12 +26,14 @@ JSON line on stdout:
   qk_l2norm    the layer shape with raw q, k normalised inside the kernel
   backward     delta_rule_chunk_bwd on the layer shape (checkpointing forward
                and reverse pass), time per call and ratio to the forward launch;
-               with "gated" inside it, gated_delta_rule_chunk_bwd likewise
+               with "gated" inside it, gated_delta_rule_chunk_bwd likewise, and
+               "one_sequence", one sequence of the layer shape (B = 1, the
+               two-pass reverse schedule for few heads)
   kda          per-key-channel decay: decode steps and the chunked forward
   long_prefill the long-prefill config (B1 H16 T32768) through the
                segment-parallel schedule, with the plain schedule beside it
 
-Options: --gpus N (only 1: this build targets one GPU), --steps K,
+Options: --gpus N (only 1: the library runs on one GPU), --steps K,
 --warmup W, --no-cpu-baseline, --no-decode, --no-small-model, --no-gated, --no-backward,
 --no-long-prefill (its segment passes launch the benchmark's kernel on
 other shapes; counter and trace runs of the benchmark line skip it),
@@ -364,12 +366,12 @@ def bench_long_prefill(torch, dr, W, reps=5):
     }
 
 
-def bench_backward(torch, dr, W, reps=10, name="layer_1p3b"):
+def bench_backward(torch, dr, W, reps=10, name="layer_1p3b", B=None):
     """delta_rule_chunk_bwd (gated_delta_rule_chunk_bwd for a gated workload)
-    on the layer shape: the checkpointing forward pass plus the reverse pass,
-    with upstream gradients for o and S_T (mean time per call with HIP events
-    on the launch stream)."""
-    w = W.get(name)
+    on the layer shape (or B of its sequences): the checkpointing forward pass
+    plus the reverse pass, with upstream gradients for o and S_T (mean time
+    per call with HIP events on the launch stream)."""
+    w = W.get(name) if B is None else W.get(name, B=B)
     x = W.generate(w)
     dev = torch.device("cuda:0")
     d = {n: (None if t is None else t.to(dev)) for n, t in x.items()}
@@ -395,7 +397,9 @@ def bench_backward(torch, dr, W, reps=10, name="layer_1p3b"):
     t = timed_steps(torch, step, reps)
     return {
         "workload": (f"{w.name} B{w.B} H{w.H} T{w.T} d{w.Dk}, bf16 in, fp32 state; "
-                     "checkpointing forward + reverse pass (output allocation inside)"),
+                     "checkpointing forward + reverse pass (output allocation inside)"
+                     + ("; reverse pass as the recursion pass then the products pass over "
+                        "runs of chunks (few heads)" if w.B * w.H <= 64 else "")),
         "tokens_per_s": w.B * w.T / t,
         "mean_call_us": round(t * 1e6, 2),
         "vs_forward_launch": None,
@@ -467,7 +471,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the delta-rule kernels shard by "
-              "(batch, head) with no communication, and this build runs on a "
+              "(batch, head) with no communication, and the library runs on a "
               "single MI355X. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
@@ -596,6 +600,8 @@ def main():
         if not args.no_gated:
             log("backward: gated rule, layer shape")
             out["backward"]["gated"] = bench_backward(torch, dr, W, name="gated_layer_1p3b")
+        log("backward: one sequence of the layer shape (two-pass schedule)")
+        out["backward"]["one_sequence"] = bench_backward(torch, dr, W, B=1)
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle on the whole workload, then on one thread")
         torch.cuda.synchronize()
