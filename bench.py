@@ -148,6 +148,18 @@ def cpu_threads():
     return max(1, min(16, n))
 
 
+def repeat_timed(fn, min_s=10.0, max_runs=200):
+    """Run fn() back to back until min_s seconds of it have been timed (at
+    least once); returns (mean seconds per run, runs, total seconds)."""
+    total, runs = 0.0, 0
+    while runs == 0 or (total < min_s and runs < max_runs):
+        t0 = time.perf_counter()
+        fn()
+        total += time.perf_counter() - t0
+        runs += 1
+    return total / runs, runs, total
+
+
 def run_cpu_single_thread(x, w, heads=16):
     """The fp64 oracle on one host thread over a bounded sample of the
     workload: the first `heads` (batch, head) pairs at full length."""
@@ -159,9 +171,7 @@ def run_cpu_single_thread(x, w, heads=16):
     q, k, v, beta = (pick(x[n]) for n in ("q", "k", "v", "beta"))
     S0 = None if x["S0"] is None else np.stack([x["S0"][b, h].double().numpy()
                                                 for b, h in sel])[None]
-    t0 = time.perf_counter()
-    delta_rule_ref(q, k, v, beta, S0, nthreads=1)
-    dt = time.perf_counter() - t0
+    dt, runs, total = repeat_timed(lambda: delta_rule_ref(q, k, v, beta, S0, nthreads=1))
     # tokens/s of the whole workload at this rate: every (batch, head) pair
     # costs the same, and a token is all H heads of one batch row
     return {
@@ -170,22 +180,22 @@ def run_cpu_single_thread(x, w, heads=16):
         "cores": 1,
         "kind": "oracle",
         "sample": f"{len(sel)} of the {w.B * w.H} heads of {w.name}, full T = {w.T}, "
-                  f"{dt:.2f} s, scaled to tokens of all {w.H} heads",
+                  f"{runs} runs in {total:.1f} s, scaled to tokens of all {w.H} heads",
     }
 
 
 def run_cpu_baseline(x, w, o_gpu, st_gpu):
     """The fp64 oracle on the whole workload (all heads, full T), timed
-    around the oracle call only with inputs already widened to fp64."""
+    around the oracle call only with inputs already widened to fp64, repeated
+    for about ten seconds (the first call's outputs give the parity)."""
     import numpy as np
 
     from oracle import delta_rule_ref
     q, k, v, beta = (x[n].double().numpy() for n in ("q", "k", "v", "beta"))
     S0 = None if x["S0"] is None else x["S0"].double().numpy()
     nt = cpu_threads()
-    t0 = time.perf_counter()
     o_ref, s_ref = delta_rule_ref(q, k, v, beta, S0, nthreads=nt)
-    dt = time.perf_counter() - t0
+    dt, runs, total = repeat_timed(lambda: delta_rule_ref(q, k, v, beta, S0, nthreads=nt))
     og = o_gpu.double().cpu().numpy()
     sg = st_gpu.double().cpu().numpy()
     par = {
@@ -200,7 +210,7 @@ def run_cpu_baseline(x, w, o_gpu, st_gpu):
         "cores": nt,
         "kind": "oracle",
         "sample": (f"whole {w.name} workload ({w.B * w.H} heads x {w.T} tokens), "
-                   f"{dt:.2f} s"),
+                   f"{runs} runs in {total:.1f} s"),
     }
     return base, par
 
