@@ -15,20 +15,14 @@ hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, bool bf16, hipStream_t stream
 }
 
 bool chunk_state_pair_supported(const ChunkFwdArgs &a, bool bf16) {
-    return bf16 && !a.g && !a.gk && !a.l2 && !a.recurrent && (a.Dk == 64 || a.Dk == 128) &&
+    return bf16 && !a.gk && !a.l2 && !a.recurrent && (a.Dk == 64 || a.Dk == 128) &&
            a.Dv == a.Dk;
 }
 
 hipError_t launch_chunk_state_pair(const ChunkFwdArgs &a, float *M, bool bf16,
                                    hipStream_t stream) {
     if (!chunk_state_pair_supported(a, bf16) || a.h || a.o || a.S0) return hipErrorNotSupported;
-    if (a.Dk == 64)
-        return a.chunk == 32 ? launch_pair_cfg<__bf16, 64, 32>(a, M, stream) : hipErrorNotSupported;
-    switch (a.chunk) {
-    case 32: return launch_pair_cfg<__bf16, 128, 32>(a, M, stream);
-    case 64: return launch_pair_cfg<__bf16, 128, 64>(a, M, stream);
-    default: return hipErrorNotSupported;
-    }
+    return a.g ? launch_chunk_state_pair_gated(a, M, stream) : launch_pair_rule<false>(a, M, stream);
 }
 
 }  // namespace dr

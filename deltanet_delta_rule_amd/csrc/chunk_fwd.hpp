@@ -1218,11 +1218,11 @@ __device__ __forceinline__ void prep_role(PipeSmem<DT, DK, C, NW, GATED, L2> &sm
 // backward, the state passes of the segment-parallel schedule) skips every
 // product that only the outputs need (P = Q K^T, Y = S Q^T, E^T P^T).
 //
-// PAIR (with NOOUT, plain rule, d_v = d_k): a second group of NW state waves
-// carries d_k rows of the chunk walk's transition map beside the workgroup's
-// value rows, on the same loaded K and the same Gram tiles and inverses: the
-// map's rows run the same recurrence with v = 0 from the identity, read from
-// and written back to Mst in place (3 NW waves, three per SIMD).
+// PAIR (with NOOUT, plain or gated rule, d_v = d_k): a second group of NW
+// state waves carries d_k rows of the chunk walk's transition map beside the
+// workgroup's value rows, on the same loaded K, gates, Gram tiles and
+// inverses: the map's rows run the same recurrence with v = 0 from the
+// identity and are written to Mst (3 NW waves, three per SIMD).
 template <typename DT, int DK, int C, int NW, bool GATED, bool L2, bool NOOUT = false,
           bool PAIR = false>
 __global__ __launch_bounds__((PAIR ? 192 : 128) * NW) __attribute__((amdgpu_waves_per_eu(PAIR ? 3 : NW / 4 + 1, PAIR ? 3 : NW / 4 + 1))) void chunk_fwd_ws_kernel(
@@ -1233,7 +1233,7 @@ __global__ __launch_bounds__((PAIR ? 192 : 128) * NW) __attribute__((amdgpu_wave
     typedef ChunkCfg<DT, DK, C, NW> G;
     constexpr int NT = G::NT, ND = G::ND;
     constexpr int NSW = (PAIR ? 2 : 1) * NW;  // state waves
-    static_assert(!PAIR || (NOOUT && !GATED && !L2), "map rows: plain rule without outputs");
+    static_assert(!PAIR || (NOOUT && !L2), "map rows: no outputs, no in-kernel norm");
     __shared__ __attribute__((aligned(16))) PipeSmem<DT, DK, C, NW, GATED, L2> sm;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1281,7 +1281,8 @@ __global__ __launch_bounds__((PAIR ? 192 : 128) * NW) __attribute__((amdgpu_wave
             if constexpr (!GATED && !L2)
                 if (!mrow) op.load_v(sm.Vs[s], sw, lane);
             state_xy<DT, DK, C, NW, GATED, L2, NOOUT>(sm.Ks[s], sm.Qs[s], Sacc, op.fv, X, Y, lane);
-            if constexpr (GATED || L2) op.load_v(sm.Vs[s], wave, lane);
+            if constexpr (GATED || L2)
+                if (!mrow) op.load_v(sm.Vs[s], sw, lane);
             if constexpr (GATED) gate_xy<DT, C, NT, !L2>(op.fv, sm.gate.at(s)->gam, X, Y, lane);
             op.load_kt(sm.Ks[s], lane);
         };
@@ -1448,18 +1449,32 @@ hipError_t launch_cfg(const ChunkFwdArgs &a, hipStream_t stream) {
 // The zero-state pass and the transition-map pass of the segment-parallel
 // schedule in one launch (PAIR): value rows from zero states into a.S_T and
 // the d_k rows of each segment's map (from the identity) into M.
-template <typename DT, int DK, int C>
+template <typename DT, int DK, int C, bool GATED>
 hipError_t launch_pair_cfg(const ChunkFwdArgs &a, float *M, hipStream_t stream) {
     constexpr int NW = 4;
     const int nvt = DK / (16 * NW);
     const int64_t grid = a.B * a.H * nvt;
-    hipLaunchKernelGGL((chunk_fwd_ws_kernel<DT, DK, C, NW, false, false, true, true>),
+    hipLaunchKernelGGL((chunk_fwd_ws_kernel<DT, DK, C, NW, GATED, false, true, true>),
                        dim3((unsigned)grid), dim3(192 * NW), 0, stream,
                        static_cast<const DT *>(a.q), static_cast<const DT *>(a.k),
-                       static_cast<const DT *>(a.v), static_cast<const DT *>(a.beta), nullptr,
+                       static_cast<const DT *>(a.v), static_cast<const DT *>(a.beta), a.g,
                        nullptr, nullptr, a.S_T, nullptr, a.cu, (int)a.T, (int)a.H, a.Dv, nvt,
                        a.scale, M, a.segP, a.segL);
     return hipGetLastError();
+}
+
+// The combined pass for one rule: d_k = d_v = 64 at chunks of 32, 128 at 32
+// or 64.
+template <bool GATED>
+hipError_t launch_pair_rule(const ChunkFwdArgs &a, float *M, hipStream_t stream) {
+    if (a.Dk == 64)
+        return a.chunk == 32 ? launch_pair_cfg<__bf16, 64, 32, GATED>(a, M, stream)
+                             : hipErrorNotSupported;
+    switch (a.chunk) {
+    case 32: return launch_pair_cfg<__bf16, 128, 32, GATED>(a, M, stream);
+    case 64: return launch_pair_cfg<__bf16, 128, 64, GATED>(a, M, stream);
+    default: return hipErrorNotSupported;
+    }
 }
 
 // Waves per workgroup.  The chunk walk is sequential, so the time per chunk
@@ -1513,6 +1528,7 @@ hipError_t launch_rule(const ChunkFwdArgs &a, bool bf16, hipStream_t stream) {
 // The gated and the L2-normalising instantiations live in translation units
 // of their own.
 hipError_t launch_chunk_fwd_gated(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
+hipError_t launch_chunk_state_pair_gated(const ChunkFwdArgs &a, float *M, hipStream_t stream);
 hipError_t launch_chunk_fwd_l2(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
 hipError_t launch_chunk_fwd_gated_l2(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
 

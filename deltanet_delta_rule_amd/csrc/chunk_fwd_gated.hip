@@ -8,4 +8,8 @@ hipError_t launch_chunk_fwd_gated(const ChunkFwdArgs &a, bool bf16, hipStream_t 
     return launch_rule<true, false>(a, bf16, stream);
 }
 
+hipError_t launch_chunk_state_pair_gated(const ChunkFwdArgs &a, float *M, hipStream_t stream) {
+    return launch_pair_rule<true>(a, M, stream);
+}
+
 }  // namespace dr

@@ -40,8 +40,8 @@ struct ChunkFwdArgs {
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, bool bf16, hipStream_t stream);
 // a without outputs or initial state (value rows from zero states into
 // a.S_T) and, in the same launch, the d_k x d_k transition map of each
-// sequence (from the identity) into M; plain rule, bf16, d_k = d_v in
-// {64, 128} (chunks of 32, or 64 at d_k = 128), else hipErrorNotSupported
+// sequence (from the identity) into M; plain or gated rule, bf16, d_k = d_v
+// in {64, 128} (chunks of 32, or 64 at d_k = 128), else hipErrorNotSupported
 // (before any launch).  chunk_state_pair_supported tells whether a's rule,
 // dtype and sizes allow it.
 bool chunk_state_pair_supported(const ChunkFwdArgs &a, bool bf16);

@@ -18,9 +18,10 @@
 //   3. a short chain per (sequence, head, 16 state rows):
 //      S_in(p) = S_in(p-1) M_{p-1} + H_{p-1} in fp32, which also gives S_T;
 //   4. each segment from its true S_in, writing the outputs.
-// For the plain rule in bf16 with d_k = d_v in {64, 128}, 1 and 2 are one
-// launch of the chunk kernel's map-rows specialisation (value rows and map
-// rows on the same staged K, Gram tiles and inverses), and the kernels find
+// For the plain and the gated rule in bf16 with d_k = d_v in {64, 128}, 1
+// and 2 are one launch of the chunk kernel's map-rows specialisation (value
+// rows and map rows on the same staged K, gates, Gram tiles and inverses),
+// and the kernels find
 // each segment's tokens from (P, L) themselves; otherwise the segments run
 // as packed sequences after a set-up kernel that writes the identities and
 // the offsets.  Steps 1, 2 and 4 run P times as many workgroups as the plain

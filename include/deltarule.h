@@ -179,7 +179,8 @@ enum {
  *               maps in fp32, and run the segments again from their true
  *               incoming states for the outputs (about three passes of work
  *               on P times as many workgroups; the first two are one launch
- *               for the plain rule in bf16 with Dk = Dv in {64, 128}).  Used
+ *               for the plain and gated rules in bf16 with Dk = Dv in
+ *               {64, 128}).  Used
  *               only when workspace_bytes >=
  *               delta_rule_chunk_fwd_workspace_bytes(...) > 0 (the call may
  *               plan fewer segments, and use less of it, for other rules);

@@ -73,8 +73,8 @@ def test_one_long_sequence(gated):
 
 @pytest.mark.parametrize("gated", [False, True])
 def test_batch_of_two_flattened(gated):
-    # d = 64: the plain rule takes 21 segments of 5 chunks (the combined
-    # state-and-map pass), the gated rule 6 segments of 17 chunks
+    # d = 64: 21 segments of 5 chunks (the combined state-and-map pass, plain
+    # and gated rule)
     _check(W.get("small_model", B=2, H=2, T=6500, gate_amax=0.5 if gated else 0.0,
                  seed=12100), gated)
 
@@ -82,6 +82,24 @@ def test_batch_of_two_flattened(gated):
 def test_small_model_config_segments():
     # the small-model config (B4 H8 T2048 d64): 8 segments of 4 chunks
     _check(W.get("small_model", seed=12150))
+
+
+def test_gated_long_prefill_full_size_sampled_heads():
+    # the long-prefill shape with the gated layer's gate draw (A up to 16),
+    # through the combined pass of the gated rule; whole heads sampled
+    from tests.parity_utils import gather_heads, oracle_heads
+    w = W.get("long_prefill", gate_amax=16.0, seed=12160)
+    x = W.generate(w)
+    d = to_dev(x)
+    assert dr.chunk_fwd_workspace_bytes(w.B, w.T, w.H, w.Dk, w.Dv, w.chunk) > 0
+    o, st = dr.gated_delta_rule_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["S0"])
+    torch.cuda.synchronize()
+    heads = [(0, 3), (0, 12)]
+    o_ref, s_ref = oracle_heads(x, heads)
+    o_got, s_got = gather_heads(o, st, heads)
+    eo, es = rel_err(o_got, o_ref), rel_err(s_got, s_ref)
+    print(f"segments gated long_prefill full size: o err {eo:.3e} S_T err {es:.3e}", flush=True)
+    assert eo <= 2e-2 and es <= 2e-2
 
 
 def test_fp32_inputs():
