@@ -334,7 +334,7 @@ def bench_kda_sequence(torch, dr, W, reps=10):
     }
 
 
-def bench_long_prefill(torch, dr, W, reps=5):
+def bench_long_prefill(torch, dr, W, reps=20):
     """delta_rule_chunk_fwd on the long-prefill config (B1 H16 T32768, beta in
     (0,2), S0 != 0): the segment-parallel schedule the binding picks for it,
     and the plain schedule (workspace=False) for comparison; mean call time

@@ -98,52 +98,64 @@ __global__ __launch_bounds__(256) void seg_init_kernel(float *M, int *cu, int64_
     }
 }
 
-// M_p (all of it, 16-byte vectors dealt to the 256 threads) and this lane's
-// entries of H_p for the chain step of segment `seg`, into registers.
-template <int DK, int NMV, int TPW, bool MEXACT, bool FULL>
-__device__ __forceinline__ void chain_fetch(f32x4 (&mreg)[NMV], f32x4 (&hreg)[TPW],
-                                            const float *M, const float *Hs, int64_t seg,
-                                            int64_t H, int64_t h, int Dv, int row0, int wave,
-                                            int tid, int g, int r) {
-    constexpr int NT = DK / 16;
+// Launch shape of the chain: waves per workgroup (each with the same number
+// of 16-column output tiles where d_k allows), the steps whose M_p and H_p
+// travel in registers ahead of use, and the accumulation chains per tile.
+template <int DK> struct ChainCfg {
+    static constexpr int NWV = DK >= 128 ? 8 : 4;
+    static constexpr int PD = DK >= 128 ? 3 : 4;
+    static constexpr int NACC = 2;
+    static constexpr int NTH = 64 * NWV;
+};
+
+// The operands of the chain step of segment `seg`, 16-byte vectors dealt to
+// the workgroup's threads: all of M_p, and the workgroup's 16 rows of H_p
+// (one vector per thread; with d_k = 16 or 32 some threads hold no part of
+// them: they load a valid vector and do not store it).
+template <int DK, int NMV, bool MEXACT>
+__device__ __forceinline__ void chain_fetch(f32x4 (&mreg)[NMV], f32x4 &hreg, const float *M,
+                                            const float *Hs, int64_t seg, int64_t H, int64_t h,
+                                            int Dv, int row0, int tid) {
+    using CF = ChainCfg<DK>;
     const int nmv = DK * DK / 4;
     // native vectors, not float4: copies of HIP's vector struct become memory
     // copies that keep the array out of registers
     const f32x4 *mp = reinterpret_cast<const f32x4 *>(M + (seg * H + h) * DK * DK);
 #pragma unroll
-    for (int u = 0; u < NMV; ++u) mreg[u] = mp[MEXACT ? tid + 256 * u : min(tid + 256 * u, nmv - 1)];
-    const float *hp = Hs + ((seg * H + h) * Dv + row0) * DK;
-#pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-        const int n = wave + 4 * j;
-        if (FULL || n < NT) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) hreg[j][e] = hp[(4 * g + e) * DK + 16 * n + r];
-        }
-    }
+    for (int u = 0; u < NMV; ++u)
+        mreg[u] = mp[MEXACT ? tid + CF::NTH * u : min(tid + CF::NTH * u, nmv - 1)];
+    const f32x4 *hp = reinterpret_cast<const f32x4 *>(Hs + ((seg * H + h) * Dv + row0) * DK);
+    hreg = hp[4 * DK >= CF::NTH ? tid : min(tid, 4 * DK - 1)];
 }
 
 // The chain over segments for 16 state rows of one (sequence, head), on the
-// fp32 matrix cores: wave w computes the output columns 16 (w + 4 j) .. of
+// fp32 matrix cores: wave w computes the output columns 16 (w + NWV j) .. of
 // S M_p (16 x 16 tiles, D layout: lane (g, r) holds rows 4g .. 4g + 3 of
-// column r), contracting over d_k four keys at a time with S and M_p staged
-// in LDS.  Hs holds H_p on entry and S_in(p) on exit (each workgroup touches
-// only its own rows).  A step reads all of its operands from LDS into
-// registers before its first product, so that the products issue back to
-// back; the wave index is uniform and, for d_k >= 64, every wave has the same
-// tiles, so nothing in a step branches per lane.
+// column r), contracting over d_k four keys at a time with S, M_p and H_p
+// staged in LDS.  Hs holds H_p on entry and S_in(p) on exit (each workgroup
+// touches only its own rows).  The maps are independent of the chain, so
+// each thread keeps its share of the next PD steps' M_p and H_p in flight in
+// a register ring: a step waits only for its own operands, issued PD steps
+// earlier, instead of one fetch latency per step.  A step reads all of its
+// operands from LDS into registers before its first product, so that the
+// products issue back to back; the wave index is uniform and, for d_k >= 64,
+// every wave has the same tiles, so nothing in a step branches per lane.
 template <int DK>
-__global__ __launch_bounds__(256) void seg_chain_kernel(float *Hs, const float *M,
-                                                        const float *S0, float *S_T, int P,
-                                                        int H, int Dv) {
+__global__ __launch_bounds__(ChainCfg<DK>::NTH) void seg_chain_kernel(float *Hs, const float *M,
+                                                                     const float *S0,
+                                                                     float *S_T, int P, int H,
+                                                                     int Dv) {
+    using CF = ChainCfg<DK>;
+    constexpr int NWV = CF::NWV, PD = CF::PD, NACC = CF::NACC, NTH = CF::NTH;
     constexpr int NT = DK / 16;                 // output tiles per row block
-    constexpr int TPW = (NT + 3) / 4;           // tiles per wave
-    constexpr bool FULL = NT % 4 == 0;          // every wave has TPW tiles
+    constexpr int TPW = (NT + NWV - 1) / NWV;   // tiles per wave
+    constexpr bool FULL = NT % NWV == 0;        // every wave has TPW tiles
     constexpr int NK = DK / 4;                  // k steps of the 16x16x4 products
-    constexpr int LDSS = DK + 4;                // S row pitch (floats)
+    constexpr int LDSS = DK + 4;                // S and H row pitch (floats)
     constexpr int LDM = DK + 16;                // M row pitch: lane groups on distinct banks
     __shared__ __attribute__((aligned(16))) float Ms[DK * LDM];
     __shared__ __attribute__((aligned(16))) float Ss[16 * LDSS];
+    __shared__ __attribute__((aligned(16))) float Hl[16 * LDSS];
     const int nrt = Dv / 16;
     // Consecutive workgroup ids go round-robin over the 8 XCDs, each with its
     // own L2; the row tiles of one head read the same M_p, so remap them onto
@@ -158,17 +170,17 @@ __global__ __launch_bounds__(256) void seg_chain_kernel(float *Hs, const float *
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, r = lane & 15;
     const int row0 = rt * 16;
-    // tile j of this wave covers columns 16 n .., n = wave + 4 j, if n < NT
-    auto has = [&](int j) { return FULL || wave + 4 * j < NT; };
+    // tile j of this wave covers columns 16 n .., n = wave + NWV j, if n < NT
+    auto has = [&](int j) { return FULL || wave + NWV * j < NT; };
 
-    constexpr int NMV = DK * DK / 4 / 256 > 0 ? DK * DK / 4 / 256 : 1;  // 16-byte vectors of M per thread
-    constexpr bool MEXACT = NMV * 256 == DK * DK / 4;
+    constexpr int NMV = DK * DK / 4 / NTH > 0 ? DK * DK / 4 / NTH : 1;  // 16-byte vectors of M per thread
+    constexpr bool MEXACT = NMV * NTH == DK * DK / 4;
     const int nmv = DK * DK / 4;
 
     f32x4 s[TPW];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
-        const int n = wave + 4 * j;
+        const int n = wave + NWV * j;
         s[j] = zero4();
         if (has(j)) {
 #pragma unroll
@@ -179,50 +191,63 @@ __global__ __launch_bounds__(256) void seg_chain_kernel(float *Hs, const float *
             }
         }
     }
-    // M_p and this lane's H_p entries travel in registers one step ahead
-    // (with d_k = 16 some threads hold no part of M: they load a valid
-    // element and do not store it)
-    f32x4 mreg[NMV];
-    f32x4 hreg[TPW];
-    if (P > 0) chain_fetch<DK, NMV, TPW, MEXACT, FULL>(mreg, hreg, M, Hs, b * P, H, h, Dv, row0, wave, tid, g, r);
-    for (int p = 0; p < P; ++p) {
+    // Ring slot k holds the operands of the steps p with p % PD == k.  Every
+    // fetch is issued unconditionally (past the last step it reloads the last
+    // segment and nothing reads it), and all of them are 16-byte vectors, so
+    // that no branch merges a loaded register with an old value and the
+    // slots keep their registers around the loop: a register copied at a
+    // merge or at the loop's back edge waits for every load in flight.
+    f32x4 mreg[PD][NMV];
+    f32x4 hreg[PD];
+    auto fetch = [&](int p, f32x4(&mr)[NMV], f32x4 &hr) {
+        chain_fetch<DK, NMV, MEXACT>(mr, hr, M, Hs, b * P + min(p, P - 1), H, h, Dv, row0, tid);
+    };
+    // one chain step: S_in(p) -> S_in(p + 1); refill the slot with step p + PD
+    auto step = [&](int p, f32x4(&mr)[NMV], f32x4 &hr, bool refill) {
         const int64_t seg = b * P + p;
         float *hp = Hs + ((seg * H + h) * Dv + row0) * DK;
-        // M_p into LDS, S_in(p) over H_p, accumulators start at H_p
+        // M_p and H_p into LDS
 #pragma unroll
         for (int u = 0; u < NMV; ++u) {
-            const int e = tid + 256 * u;
+            const int e = tid + NTH * u;
             if (MEXACT || e < nmv) {
                 const int row = 4 * e / DK, col = 4 * e % DK;
-                *reinterpret_cast<f32x4 *>(Ms + row * LDM + col) = mreg[u];
+                *reinterpret_cast<f32x4 *>(Ms + row * LDM + col) = mr[u];
             }
         }
-        f32x4 acc[TPW][2];
+        if (4 * DK >= NTH || tid < 4 * DK)
+            *reinterpret_cast<f32x4 *>(Hl + (4 * tid / DK) * LDSS + 4 * tid % DK) = hr;
+        // LDS only: the global loads of later steps and the stores of S_in(p)
+        // stay in flight across the barriers
+        lds_barrier();
+        // S_in(p) over H_p: every thread's load of H_p has returned (its
+        // value went to LDS before the barrier)
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
-            const int n = wave + 4 * j;
-            acc[j][0] = has(j) ? hreg[j] : zero4();
-            acc[j][1] = zero4();
+            const int n = wave + NWV * j;
             if (has(j)) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) hp[(4 * g + e) * DK + 16 * n + r] = s[j][e];
             }
         }
-        // LDS only: the global loads of the next step and the stores of
-        // S_in(p) stay in flight across the barriers (each thread reads and
-        // writes only its own entries of Hs)
-        lds_barrier();
-        if (p + 1 < P)
-            chain_fetch<DK, NMV, TPW, MEXACT, FULL>(mreg, hreg, M, Hs, b * P + p + 1, H, h, Dv, row0,
-                                                    wave, tid, g, r);
-        // acc += S M_p: A = S rows (lane (g, r): S[r][4i + g]), B = M_p
-        // (lane (g, r): M[4i + g][16 n + r]); two chains per tile
+        if (refill) fetch(p + PD, mr, hr);
+        // acc = H_p + S M_p: A = S rows (lane (g, r): S[r][4i + g]), B = M_p
+        // (lane (g, r): M[4i + g][16 n + r]); NACC chains per tile
+        f32x4 acc[TPW][NACC];
         float a[NK], bm[TPW][NK];
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int n = has(j) ? wave + NWV * j : 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[j][0][e] = Hl[(4 * g + e) * LDSS + 16 * n + r];
+#pragma unroll
+            for (int c = 1; c < NACC; ++c) acc[j][c] = zero4();
+        }
 #pragma unroll
         for (int i = 0; i < NK; ++i) a[i] = Ss[r * LDSS + 4 * i + g];
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
-            const int n = has(j) ? wave + 4 * j : 0;
+            const int n = has(j) ? wave + NWV * j : 0;
 #pragma unroll
             for (int i = 0; i < NK; ++i) bm[j][i] = Ms[(4 * i + g) * LDM + 16 * n + r];
         }
@@ -230,23 +255,38 @@ __global__ __launch_bounds__(256) void seg_chain_kernel(float *Hs, const float *
         for (int i = 0; i < NK; ++i)
 #pragma unroll
             for (int j = 0; j < TPW; ++j)
-                acc[j][i & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], bm[j][i], acc[j][i & 1],
-                                                                     0, 0, 0);
+                acc[j][i % NACC] =
+                    __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], bm[j][i], acc[j][i % NACC], 0, 0, 0);
         lds_barrier();
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
-            const int n = wave + 4 * j;
-            s[j] = acc[j][0] + acc[j][1];
+            const int n = wave + NWV * j;
+            s[j] = acc[j][0];
+#pragma unroll
+            for (int c = 1; c < NACC; ++c) s[j] += acc[j][c];
             if (has(j)) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) Ss[(4 * g + e) * LDSS + 16 * n + r] = s[j][e];
             }
         }
+    };
+    if (P > 0) {
+#pragma unroll
+        for (int k = 0; k < PD; ++k) fetch(k, mreg[k], hreg[k]);
+        // whole rounds of PD steps, each refilling its slot, then the rest
+        int p0 = 0;
+        for (; p0 + PD <= P; p0 += PD) {
+#pragma unroll
+            for (int k = 0; k < PD; ++k) step(p0 + k, mreg[k], hreg[k], true);
+        }
+#pragma unroll
+        for (int k = 0; k < PD - 1; ++k)
+            if (p0 + k < P) step(p0 + k, mreg[k], hreg[k], false);
     }
     if (S_T) {
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
-            const int n = wave + 4 * j;
+            const int n = wave + NWV * j;
             if (has(j)) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -260,8 +300,8 @@ template <int DK>
 hipError_t launch_chain(float *Hs, const float *M, const float *S0, float *S_T, int64_t B, int P,
                         int64_t H, int Dv, hipStream_t stream) {
     const int64_t grid = B * H * (Dv / 16);
-    hipLaunchKernelGGL((seg_chain_kernel<DK>), dim3((unsigned)grid), dim3(256), 0, stream, Hs,
-                       M, S0, S_T, P, (int)H, Dv);
+    hipLaunchKernelGGL((seg_chain_kernel<DK>), dim3((unsigned)grid), dim3(ChainCfg<DK>::NTH), 0,
+                       stream, Hs, M, S0, S_T, P, (int)H, Dv);
     return hipGetLastError();
 }
 
