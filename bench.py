@@ -4,8 +4,13 @@
 One step = one ``delta_rule_chunk_fwd`` over the 1.3B-scale layer shape
 (B=8, H=16, T=2048, d_k=d_v=128, chunk 64, bf16 inputs, fp32 state, final
 state returned) with inputs already resident in HBM.  W untimed warm-up
-steps, then K timed steps between two device synchronisations.  Prints ONE
-JSON line on stdout:
+steps, then K timed steps between two device synchronisations.  The GPU
+raises its clock over the first tens of milliseconds of sustained work (the
+benchmark step takes ~84 us per launch in the first 8 ms and settles at
+~71 us after ~20 ms), so the default W = 1500 (~0.1 s) and every other line
+below runs its step back to back for 0.1 s before its timed region: each
+figure is the steady-state rate, not the ramp's.  Prints ONE JSON line on
+stdout:
 
   value        tokens/s = B*T*K / wall time of the K steps
   roofline     the fused chunk kernel against HBM bandwidth (its roofline
@@ -84,6 +89,25 @@ def timed_steps(torch, step, reps):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / reps / 1e3
+
+
+SETTLE_S = 0.1  # seconds of back-to-back work before a timed region
+
+
+def settle(torch, step, seconds=SETTLE_S):
+    """Run `step` back to back for about `seconds` so that the timed region
+    that follows starts at the GPU's steady clock; returns the number of runs.
+    Batches of 8 runs end in a synchronisation, so that the host never queues
+    far ahead of the device."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            step()
+        n += 8
+        torch.cuda.synchronize()
+    return n
 
 
 def chunk_work(w):
@@ -236,7 +260,7 @@ def bench_decode(torch, dr, W, reps=3, name="decode", **over):
                 dr.gated_delta_rule_recurrent_step(d["q"][t], d["k"][t], d["v"][t],
                                                    d["beta"][t], d["g"][t], S, o=outs[t])
 
-    run()  # warm-up
+    settle(torch, run)  # the state resets before every timed run
     times = []
     for _ in range(reps):
         S.copy_(d["S0"])  # reset outside the timed region
@@ -290,8 +314,7 @@ def bench_gated_chunk(torch, dr, W, reps=20, name="gated_layer_1p3b", l2=False):
                                           chunk=w.chunk, o=o, S_T=st,
                                           use_qk_l2norm_in_kernel=l2, workspace=ws)
 
-    for _ in range(3):
-        step()
+    settle(torch, step)
     launch_s = timed_steps(torch, step, reps)
     flops, nbytes = chunk_work(w)
     what = ("raw q, k normalised in the kernel, fp32 state" if l2 else
@@ -321,7 +344,7 @@ def bench_kda_sequence(torch, dr, W, reps=10):
     def step():
         dr.kda_fwd(d["q"], d["k"], d["v"], d["beta"], d["gk"], None, o=o, S_T=st)
 
-    step()
+    settle(torch, step)
     launch_s = timed_steps(torch, step, reps)
     flops, nbytes = chunk_work(w)
     return {
@@ -353,7 +376,7 @@ def bench_long_prefill(torch, dr, W, reps=20):
         def step():
             dr.delta_rule_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["S0"], chunk=w.chunk,
                                     o=o, S_T=st, workspace=workspace)
-        step()
+        settle(torch, step)
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         s.record()
@@ -402,8 +425,7 @@ def bench_backward(torch, dr, W, reps=10, name="layer_1p3b", B=None):
             dr.gated_delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], do,
                                           d["S0"], dst, workspace=ws)
 
-    for _ in range(2):
-        step()
+    settle(torch, step)
     t = timed_steps(torch, step, reps)
     return {
         "workload": (f"{w.name} B{w.B} H{w.H} T{w.T} d{w.Dk}, bf16 in, fp32 state; "
@@ -458,7 +480,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1500,
+                    help="untimed steps before the K timed ones (the default is ~0.1 s "
+                         "of work, enough for the clock to settle)")
     ap.add_argument("--workload", default="layer_1p3b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
