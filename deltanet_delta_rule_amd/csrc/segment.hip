@@ -177,20 +177,6 @@ __global__ __launch_bounds__(ChainCfg<DK>::NTH) void seg_chain_kernel(float *Hs,
     constexpr bool MEXACT = NMV * NTH == DK * DK / 4;
     const int nmv = DK * DK / 4;
 
-    f32x4 s[TPW];
-#pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-        const int n = wave + NWV * j;
-        s[j] = zero4();
-        if (has(j)) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = row0 + 4 * g + e;
-                if (S0) s[j][e] = S0[(bh * Dv + row) * DK + 16 * n + r];
-                Ss[(4 * g + e) * LDSS + 16 * n + r] = s[j][e];
-            }
-        }
-    }
     // Ring slot k holds the operands of the steps p with p % PD == k.  Every
     // fetch is issued unconditionally (past the last step it reloads the last
     // segment and nothing reads it), and all of them are 16-byte vectors, so
@@ -202,6 +188,31 @@ __global__ __launch_bounds__(ChainCfg<DK>::NTH) void seg_chain_kernel(float *Hs,
     auto fetch = [&](int p, f32x4(&mr)[NMV], f32x4 &hr) {
         chain_fetch<DK, NMV, MEXACT>(mr, hr, M, Hs, b * P + min(p, P - 1), H, h, Dv, row0, tid);
     };
+    // S_in(0) = S0 (or zero): its loads go out first, then the ring's, and
+    // only then is S0 waited for, so the two latencies overlap (the loads
+    // return in order).  The S0 loads are unconditional (from Hs when S0 is
+    // null, then replaced by zeros) so that no branch merges them.
+    if (P <= 0) return;  // the schedule always has segments; nothing to chain
+    const float *s0p = S0 ? S0 : Hs;
+    f32x4 s[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        const int n = has(j) ? wave + NWV * j : 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[j][e] = s0p[(bh * Dv + row0 + 4 * g + e) * DK + 16 * n + r];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the S0 loads ahead of the ring's
+#pragma unroll
+    for (int k = 0; k < PD; ++k) fetch(k, mreg[k], hreg[k]);
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        const int n = wave + NWV * j;
+        if (!S0) s[j] = zero4();
+        if (has(j)) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Ss[(4 * g + e) * LDSS + 16 * n + r] = s[j][e];
+        }
+    }
     // one chain step: S_in(p) -> S_in(p + 1); refill the slot with step p + PD
     auto step = [&](int p, f32x4(&mr)[NMV], f32x4 &hr, bool refill) {
         const int64_t seg = b * P + p;
@@ -270,19 +281,15 @@ __global__ __launch_bounds__(ChainCfg<DK>::NTH) void seg_chain_kernel(float *Hs,
             }
         }
     };
-    if (P > 0) {
+    // whole rounds of PD steps, each refilling its slot, then the rest
+    int p0 = 0;
+    for (; p0 + PD <= P; p0 += PD) {
 #pragma unroll
-        for (int k = 0; k < PD; ++k) fetch(k, mreg[k], hreg[k]);
-        // whole rounds of PD steps, each refilling its slot, then the rest
-        int p0 = 0;
-        for (; p0 + PD <= P; p0 += PD) {
-#pragma unroll
-            for (int k = 0; k < PD; ++k) step(p0 + k, mreg[k], hreg[k], true);
-        }
-#pragma unroll
-        for (int k = 0; k < PD - 1; ++k)
-            if (p0 + k < P) step(p0 + k, mreg[k], hreg[k], false);
+        for (int k = 0; k < PD; ++k) step(p0 + k, mreg[k], hreg[k], true);
     }
+#pragma unroll
+    for (int k = 0; k < PD - 1; ++k)
+        if (p0 + k < P) step(p0 + k, mreg[k], hreg[k], false);
     if (S_T) {
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
