@@ -601,7 +601,7 @@ def main():
         out["small_model"]["kernel"] = (
             "segment-parallel schedule, 8 segments of 256 tokens per sequence: "
             "chunk_fwd_ws_kernel<bf16, Dk=64, C=32, NW=4> with map rows (12 waves), "
-            "seg_chain_kernel<64>, chunk_fwd_ws_kernel<bf16, Dk=64, C=64, NW=4>")
+            "seg_chain_kernel<64>, chunk_fwd_ws_kernel<bf16, Dk=64, C=32, NW=4> (outputs)")
     if not args.no_decode:
         log("decode: 256 steps of B128 H16 d128")
         out["decode"] = bench_decode(torch, dr, W)

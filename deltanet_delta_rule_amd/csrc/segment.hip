@@ -390,10 +390,13 @@ hipError_t launch_chunk_fwd_segmented(const ChunkFwdArgs &a, const SegPlan &pl, 
     default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
-    // 4. outputs from the true incoming states
+    // 4. outputs from the true incoming states (with d_k <= 64 in 32-token
+    // chunks: the segments are short there, and the shorter chunk's period
+    // and pipeline fill measured shorter)
     s.S0 = Hs;
     s.S_T = nullptr;
     s.o = a.o;
+    if (a.Dk <= 64 && s.chunk == 64) s.chunk = 32;
     return launch_chunk_fwd(s, bf16, stream);
 }
 
