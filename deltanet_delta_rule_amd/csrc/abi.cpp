@@ -422,6 +422,6 @@ const char *delta_rule_status_string(dr_status status) {
 
 int delta_rule_last_hip_error(void) { return g_last_hip_error; }
 
-int delta_rule_version(void) { return 21000; }
+int delta_rule_version(void) { return 21100; }
 
 }  // extern "C"

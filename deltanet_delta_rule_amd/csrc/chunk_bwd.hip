@@ -66,6 +66,8 @@
 #include "dr_common.hpp"
 #include "dr_launch.hpp"
 
+#include <climits>
+#include <mutex>
 #include <type_traits>
 
 namespace dr {
@@ -374,13 +376,16 @@ __device__ __forceinline__ void store_rows(DT *dst, int64_t gs, int nvalid, cons
     }
 }
 
-// MODE 0: the whole backward in one reverse walk per (b, h).  MODE 1
-// (recursion only): dE, Z, dV and the dS recursion, one workgroup per (b, h);
-// it writes dV, dS0, Z (dsz, [B,T,H,d_v]) and every chunk's dS_{c+1}
-// (dsb, [B,H,N,d_v,d_k], like the forward checkpoints).  MODE 2 (products
-// only): R, E, dbeta, dQ, dK (and dg) from those, with nsplit workgroups per
-// (b, h), each over its own run of chunks, so that the chunks of a head run
-// in parallel.
+// MODE 0: the whole backward in one reverse walk per (b, h), over chunks
+// [c_beg, c_end) from dS = dST at the end of c_end - 1 (dS0 gets dS at the
+// start of c_beg).  MODE 1 (recursion only): dE, Z, dV and the dS recursion,
+// one workgroup per (b, h); it writes dV, dS0, Z (dsz, [B,T,H,d_v]) and every
+// chunk's dS_{c+1} (dsb, [B,H,N,d_v,d_k], like the forward checkpoints).
+// MODE 2 (products only): R, E, dbeta, dQ, dK (and dg) from those, with
+// nsplit workgroups per (b, h), each over its own run of chunks, so that the
+// chunks of a head run in parallel.  MODE 3: the recursion of MODE 1 over
+// chunks [c_beg, c_end), writing nothing but dS at the start of c_beg (into
+// dS0): the incoming dS of a MODE 0 walk over the chunks before c_beg.
 template <typename DT, int DK, int DV, int C, bool GATED, int MODE>
 __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
@@ -388,11 +393,12 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
     const float *__restrict__ dST, const DT *__restrict__ hs, DT *__restrict__ dq,
     DT *__restrict__ dk, DT *__restrict__ dv, DT *__restrict__ dbeta, float *__restrict__ dg,
     float *__restrict__ dS0, DT *__restrict__ dsb, DT *__restrict__ dsz, int T, int H,
-    int nsplit) {
+    int nsplit, int c_beg, int c_end) {
     typedef BwdCfg<DT, DK, DV, C> G;
     constexpr int NW = G::NW, NT = G::NT, KT = G::KT, VT = G::VT;
     constexpr int LDK = G::LDK, LDV = G::LDV, LDS_ = G::LDS_, LDSK = G::LDSK, LDC = G::LDC;
-    constexpr bool PROD = MODE != 1;   // R, E, dbeta and the products over all value columns
+    constexpr bool RONLY = MODE == 1 || MODE == 3;  // the recursion alone
+    constexpr bool PROD = !RONLY;      // R, E, dbeta and the products over all value columns
     constexpr bool RECUR = MODE != 2;  // dE, Z and the dS recursion
     static_assert(MODE == 0 || G::DBUF, "split modes keep dS_{c+1} in its own LDS buffer");
     __shared__ __attribute__((aligned(16))) BwdSmem<DT, DK, DV, C, GATED> sm;
@@ -407,6 +413,10 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
     const int nthr = 64 * NW;
     // chunks [c_lo, c_hi) of this workgroup, walked in reverse
     int c_lo = 0, c_hi = N;
+    if constexpr (MODE == 0 || MODE == 3) {
+        c_lo = max(0, c_beg);
+        c_hi = min(N, c_end);
+    }
     if constexpr (MODE == 2) {
         const int per = (N + nsplit - 1) / nsplit, part = (int)(blockIdx.x % nsplit);
         c_lo = min(N, part * per);
@@ -420,9 +430,9 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
     // Tm, Pm and dO by chunk parity: mode 1 keeps two of each (the second in
     // the LDS its unused products would take: Dm, Gs, Vs), so that the next
     // chunk's Gram tiles and inverses form while this chunk's are read
-    auto tm_buf = [&](int bb) -> DT * { return MODE == 1 && bb ? sm.Dm : sm.Tm; };
-    auto pm_buf = [&](int bb) -> DT * { return MODE == 1 && bb ? sm.Gs : sm.Pm; };
-    auto os_buf = [&](int bb) -> DT * { return MODE == 1 && bb ? sm.Vs : sm.Os; };
+    auto tm_buf = [&](int bb) -> DT * { return RONLY && bb ? sm.Dm : sm.Tm; };
+    auto pm_buf = [&](int bb) -> DT * { return RONLY && bb ? sm.Gs : sm.Pm; };
+    auto os_buf = [&](int bb) -> DT * { return RONLY && bb ? sm.Vs : sm.Os; };
     // dS^T of this wave's value columns: tile s holds dS^T[16s + 4g + i][v0 + r]
     f32x4 Dt[RECUR ? KT : 1];
 #pragma unroll
@@ -554,7 +564,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
     ChunkPrefetch<DT, DK, DV, C> pf;
     auto prefetch = [&](auto part, int cn) {
         const int tp = cn * C;
-        pf.template load_part<decltype(part)::value, MODE>(
+        pf.template load_part<decltype(part)::value, RONLY ? 1 : MODE>(
             k, q, v, dout, beta, GATED ? gl : nullptr, hs + (head * N + cn) * DV * DK,
             dsb + (head * N + cn) * DV * DK, dsz, (int64_t)b * T + tp, h, H, min(C, T - tp), tid);
     };
@@ -910,44 +920,46 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
     };
 
     constexpr int NWJ = NW < 4 ? NW : 4;  // waves that form the next chunk's Gram tiles
-    if constexpr (MODE == 1) {
+    if constexpr (RONLY) {
         // Recursion only, two barriers per chunk.  Chunk c's K, Q, beta, dO,
         // Tm and Pm sit in the buffers of parity c & 1.  With its column work
         // the waves form chunk c-1's Gram tiles and diagonal inverses (its
         // inputs were staged one chunk earlier); after the barrier, T_10 of
-        // chunk c-1, the stores of chunk c (dV, Z, dS_{c+1}) and the staging
-        // of chunk c-2 (loaded during the column work).
-        if (N > 0) pf.o.store(os_buf((N - 1) & 1), LDV, tid);
-        if (N > 1) {
-            prefetch(std::integral_constant<int, 1>(), N - 2);
-            prefetch(std::integral_constant<int, 2>(), N - 2);
-            stage_kqb((N - 2) & 1);
-            pf.o.store(os_buf((N - 2) & 1), LDV, tid);
+        // chunk c-1, the stores of chunk c (dV, Z, dS_{c+1}; MODE 1 only) and
+        // the staging of chunk c-2 (loaded during the column work).
+        if (c_hi > c_lo) pf.o.store(os_buf((c_hi - 1) & 1), LDV, tid);
+        if (c_hi - c_lo > 1) {
+            prefetch(std::integral_constant<int, 1>(), c_hi - 2);
+            prefetch(std::integral_constant<int, 2>(), c_hi - 2);
+            stage_kqb((c_hi - 2) & 1);
+            pf.o.store(os_buf((c_hi - 2) & 1), LDV, tid);
         }
         __syncthreads();
-        for (int c = N - 1; c >= 0; --c) {
+        for (int c = c_hi - 1; c >= c_lo; --c) {
             const int len = min(C, T - c * C);
             const int64_t tok0 = (int64_t)b * T + c * C;
             const int cb = c & 1;
-            if (c > 1) {
+            if (c > c_lo + 1) {
                 prefetch(std::integral_constant<int, 1>(), c - 2);
                 prefetch(std::integral_constant<int, 2>(), c - 2);
             }
             per_wave(cb);
-            if (c > 0) {
+            if (c > c_lo) {
                 diag_jobs(cb ^ 1);
                 if (w < NWJ) other_jobs(cb ^ 1, NWJ, false);
             }
             __syncthreads();
             if constexpr (NT == 2)
-                if (c > 0 && w == 0) t10(cb ^ 1);
-            store_rows<DT, C, DV, 64 * NW>(dv + (tok0 * H + h) * DV, (int64_t)H * DV, len, sm.Rb,
-                                           LDV, tid);
-            store_rows<DT, C, DV, 64 * NW>(dsz + (tok0 * H + h) * DV, (int64_t)H * DV, len, sm.Es,
-                                           LDV, tid);
-            store_rows<DT, DV, DK, 64 * NW>(dsb + (head * N + c) * DV * DK, DK, DV, sm.Db, LDS_,
-                                            tid);
-            if (c > 1) {
+                if (c > c_lo && w == 0) t10(cb ^ 1);
+            if constexpr (MODE == 1) {
+                store_rows<DT, C, DV, 64 * NW>(dv + (tok0 * H + h) * DV, (int64_t)H * DV, len,
+                                               sm.Rb, LDV, tid);
+                store_rows<DT, C, DV, 64 * NW>(dsz + (tok0 * H + h) * DV, (int64_t)H * DV, len,
+                                               sm.Es, LDV, tid);
+                store_rows<DT, DV, DK, 64 * NW>(dsb + (head * N + c) * DV * DK, DK, DV, sm.Db,
+                                                LDS_, tid);
+            }
+            if (c > c_lo + 1) {
                 stage_kqb(cb);
                 pf.o.store(os_buf(cb), LDV, tid);
             }
@@ -1190,7 +1202,8 @@ inline int bwd_nsplit(int64_t BH, int N) {
 }
 
 template <typename DT, int DK, int DV, bool GATED, int MODE>
-hipError_t launch_bwd_mode(const ChunkBwdArgs &a, int nsplit, hipStream_t stream) {
+hipError_t launch_bwd_mode(const ChunkBwdArgs &a, int nsplit, hipStream_t stream, int c_beg = 0,
+                           int c_end = INT_MAX) {
     hipLaunchKernelGGL((chunk_bwd_kernel<DT, DK, DV, sizeof(DT) == 2 ? 32 : 16, GATED, MODE>),
                        dim3((unsigned)(a.B * a.H * (MODE == 2 ? nsplit : 1))), dim3(DV * 4), 0,
                        stream, static_cast<const DT *>(a.q), static_cast<const DT *>(a.k),
@@ -1198,13 +1211,80 @@ hipError_t launch_bwd_mode(const ChunkBwdArgs &a, int nsplit, hipStream_t stream
                        static_cast<const DT *>(a.dout), a.dS_T, static_cast<const DT *>(a.h),
                        static_cast<DT *>(a.dq), static_cast<DT *>(a.dk), static_cast<DT *>(a.dv),
                        static_cast<DT *>(a.dbeta), a.dg, a.dS0, static_cast<DT *>(a.dsb),
-                       static_cast<DT *>(a.dsz), (int)a.T, (int)a.H, nsplit);
+                       static_cast<DT *>(a.dsz), (int)a.T, (int)a.H, nsplit, c_beg, c_end);
     return hipGetLastError();
 }
 
-// One reverse pass per (b, h), or, where that leaves compute units idle and
-// the caller gave the scratch (dsb, dsz), the recursion pass then the
-// products pass over nsplit runs of chunks per (b, h).
+// A second stream per device, with a fork and a join event, for the split
+// reverse walk below.  Created on first use with the device current (default
+// priority); a mutex per device keeps each call's record / wait / launch
+// sequence whole, so calls from several host threads stay ordered.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    hipError_t err = hipSuccess;
+    std::mutex mu;
+};
+constexpr int BWD_MAX_DEVICES = 64;
+std::once_flag g_side_once[BWD_MAX_DEVICES];
+SideStream g_side[BWD_MAX_DEVICES];
+
+hipError_t side_stream(SideStream **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= BWD_MAX_DEVICES) return hipErrorInvalidDevice;
+    SideStream &ss = g_side[dev];
+    std::call_once(g_side_once[dev], [&ss] {
+        ss.err = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking);
+        if (ss.err == hipSuccess) ss.err = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming);
+        if (ss.err == hipSuccess) ss.err = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming);
+    });
+    if (ss.err != hipSuccess) return ss.err;
+    *out = &ss;
+    return hipSuccess;
+}
+
+// Reverse walk in two pieces for B*H <= 128 (one workgroup per (b, h)
+// leaves half the compute units idle): on the caller's stream the recursion
+// alone (MODE 3, about half a single-pass chunk step) walks chunks [m, N)
+// from dS_T to give dS at chunk m, and then the single pass over chunks
+// [0, m) starts from it; meanwhile, on the side stream, the single pass over
+// chunks [m, N) runs from dS_T.  The caller's stream, which holds the
+// critical path, waits for nothing but the join at the end (a stream that
+// waits on an event starts its next kernel several microseconds late).  The
+// two sides take about as long when m is ~11/32 of the chunks (measured:
+// 8/32, 13/32 and 15/32 were slower).  dS at chunk m (fp32, [B,H,Dv,Dk])
+// goes to the workspace's scratch region (dsb).
+constexpr int BWD_SPLIT_NUM = 11, BWD_SPLIT_DEN = 32;
+constexpr int BWD_SPLIT_MIN_CHUNKS = 8;
+
+template <typename DT, int DK, int DV, bool GATED>
+hipError_t launch_bwd_split(const ChunkBwdArgs &a, int N, hipStream_t stream) {
+    SideStream *ss = nullptr;
+    hipError_t e = side_stream(&ss);
+    if (e != hipSuccess) return e;
+    const int m = N * BWD_SPLIT_NUM / BWD_SPLIT_DEN;
+    float *mid = static_cast<float *>(a.dsb);
+    ChunkBwdArgs tail = a, rec = a, head = a;
+    tail.dS0 = nullptr;                 // [m, N) from dS_T; dS0 comes from the head piece
+    rec.dS0 = mid;                      // dS at chunk m
+    rec.dsb = rec.dsz = nullptr;
+    head.dS_T = mid;                    // [0, m) from dS at chunk m
+    std::lock_guard<std::mutex> lock(ss->mu);
+    if ((e = hipEventRecord(ss->fork, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return e;
+    if ((e = launch_bwd_mode<DT, DK, DV, GATED, 0>(tail, 1, ss->s, m, N)) != hipSuccess) return e;
+    if ((e = launch_bwd_mode<DT, DK, DV, GATED, 3>(rec, 1, stream, m, N)) != hipSuccess) return e;
+    if ((e = launch_bwd_mode<DT, DK, DV, GATED, 0>(head, 1, stream, 0, m)) != hipSuccess) return e;
+    if ((e = hipEventRecord(ss->join, ss->s)) != hipSuccess) return e;
+    return hipStreamWaitEvent(stream, ss->join, 0);
+}
+
+// One reverse pass per (b, h); where that leaves compute units idle and the
+// caller gave the scratch (dsb, dsz), either the recursion pass then the
+// products pass over nsplit runs of chunks per (b, h) (few heads), or the
+// reverse walk in two pieces on two streams (up to 128 heads).
 template <typename DT, int DK, int DV, bool GATED>
 hipError_t launch_bwd_gate(const ChunkBwdArgs &a, hipStream_t stream) {
     constexpr int C = sizeof(DT) == 2 ? 32 : 16;
@@ -1212,12 +1292,15 @@ hipError_t launch_bwd_gate(const ChunkBwdArgs &a, hipStream_t stream) {
         return hipErrorInvalidValue;
     } else {
         if constexpr (BwdCfg<DT, DK, DV, C>::DBUF) {
-            const int ns = bwd_nsplit(a.B * a.H, (int)((a.T + C - 1) / C));
+            const int N = (int)((a.T + C - 1) / C);
+            const int ns = bwd_nsplit(a.B * a.H, N);
             if (a.dsb && a.dsz && ns >= 2) {
                 const hipError_t e = launch_bwd_mode<DT, DK, DV, GATED, 1>(a, 1, stream);
                 if (e != hipSuccess) return e;
                 return launch_bwd_mode<DT, DK, DV, GATED, 2>(a, ns, stream);
             }
+            if (a.dsb && a.B * a.H <= 128 && N >= BWD_SPLIT_MIN_CHUNKS)
+                return launch_bwd_split<DT, DK, DV, GATED>(a, N, stream);
         }
         return launch_bwd_mode<DT, DK, DV, GATED, 0>(a, 1, stream);
     }

@@ -45,15 +45,24 @@
  *            them beyond the work queued on `stream`.
  *   Stream   `stream` is a hipStream_t passed as void*; NULL is the default
  *            stream.  Calls only enqueue work: they never synchronise the
- *            device and never block on the GPU.
+ *            device and never block on the GPU.  The backward may run part
+ *            of its work on a second stream of the library's (see
+ *            delta_rule_chunk_bwd); that work starts after the work queued
+ *            on `stream` before the call, and work queued on `stream` after
+ *            the call starts after it.
  *   Errors   Every entry point returns a dr_status.  Arguments are validated
  *            on the host before any HIP call; on DR_ERR_INVALID_ARG or
  *            DR_ERR_UNSUPPORTED nothing was enqueued.  DR_ERR_HIP means a HIP
  *            launch reported an error; the hipError_t value is then available
  *            from delta_rule_last_hip_error() on the calling thread.
- *   Threads  No global mutable state besides that thread-local error code:
- *            concurrent calls on different streams are safe.  Calls on one
- *            stream run in order.
+ *   Threads  Global state: that thread-local error code; per GPU, the
+ *            array of delta_rule_chunk_fwd_noalloc and, from the first
+ *            backward call that splits its reverse walk, a second stream
+ *            and two events (default priority), held until the process
+ *            ends.  A call's fork, launches and join on that stream are
+ *            enqueued under a per-GPU mutex.  Concurrent calls on different
+ *            streams are safe (the noalloc entry point excepted, see
+ *            there); calls on one stream run in order.
  */
 #ifndef DELTARULE_H
 #define DELTARULE_H
@@ -367,9 +376,14 @@ dr_status delta_rule_recurrent_step_ex(const void *q, const void *k, const void 
  * states of every chunk are kept and the chunk-internal quantities
  * recomputed).  The call first reruns the forward pass to store each chunk's
  * incoming state in `workspace` (in `dtype`, the precision the backward's
- * products use it in), then walks the chunks in reverse (when B*H is small:
- * a reverse pass over the state-gradient recursion alone, then the
- * gradients of the chunks formed in parallel from its results).
+ * products use it in), then walks the chunks in reverse.  With B*H <= 64
+ * the walk is a reverse pass over the state-gradient recursion alone, then
+ * the gradients of the chunks formed in parallel from its results.  With
+ * 64 < B*H <= 128 (one workgroup per (b, h) would leave half the GPU idle)
+ * and at least 8 chunks it goes in two pieces: the last ~21/32 of the
+ * chunks run from dS_T on the library's second stream while `stream` runs
+ * the recursion alone over those chunks, then the first ~11/32 from the
+ * state gradient that gives.
  *
  *   q, k, v, beta, S0   the forward inputs, as in delta_rule_chunk_fwd
  *   workspace           device memory of at least
@@ -377,8 +391,8 @@ dr_status delta_rule_recurrent_step_ex(const void *q, const void *k, const void 
  *                       bytes (16-byte aligned; contents on return: the
  *                       forward checkpoints, [B,H,N,Dv,Dk] in the input
  *                       dtype at its start, then scratch of the two-pass
- *                       schedule that runs when B*H is small); may be NULL
- *                       when T == 0
+ *                       schedule or the split walk's state gradient);
+ *                       may be NULL when T == 0
  *   Outputs must not overlap the inputs, the workspace or each other.
  * Sizes as delta_rule_chunk_fwd (Dk, Dv in {16,32,64,128}); the chunk length
  * is chosen by the library (32 tokens for bf16, 16 for fp32).  Errors as
@@ -435,7 +449,8 @@ int delta_rule_last_hip_error(void);
  * dr_chunk_opts and delta_rule_chunk_fwd_workspace_bytes; 2.8.0:
  * delta_rule_chunk_fwd_noalloc and DR_ERR_SCRATCH; 2.9.0:
  * gated_delta_rule_chunk_bwd; 2.10.0: the backward's workspace also holds
- * the scratch of its two-pass schedule). */
+ * the scratch of its two-pass schedule; 2.11.0: the backward's split
+ * reverse walk on a second stream). */
 int delta_rule_version(void);
 
 #ifdef __cplusplus

@@ -107,11 +107,39 @@ def test_backward_single_pass_schedule(gated):
 @pytest.mark.parametrize("gated", [False, True])
 def test_backward_chunk_runs_with_empty_workgroups(gated):
     # 40 (b, h): the recursion pass, then six workgroups per (b, h) over 8
-    # chunks in runs of two, the last two workgroups without chunks (the
-    # sampled-heads layer test covers the single pass at 128 (b, h))
+    # chunks in runs of two, the last two workgroups without chunks
     w = W.get("layer_1p3b", B=5, H=8, T=250, Dk=64, Dv=64, gate_amax=4.0 if gated else 0.0,
               seed=7500)
     _check(w, heads=[(0, 0), (2, 5), (4, 7)])
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_backward_split_reverse_walk(gated):
+    # 80 (b, h) and 10 chunks with a ragged tail: the reverse walk in two
+    # pieces on two streams (the single pass over chunks 3..9 from dS_T; the
+    # recursion alone over the same chunks for dS at chunk 3, then the single
+    # pass over chunks 0..2 from it)
+    w = W.get("layer_1p3b", B=5, H=16, T=300, Dk=64, Dv=64, gate_amax=4.0 if gated else 0.0,
+              seed=7450)
+    _check(w, heads=[(0, 0), (2, 7), (4, 15)])
+
+
+def test_backward_full_size_sampled_heads():
+    # the benchmark's configuration and launch: B8 H16 T2048 d128, 64 chunks,
+    # the split reverse walk (every head computed, two checked)
+    _check(W.get("layer_1p3b"), heads=[(0, 1), (7, 14)])
+    _check(W.get("gated_layer_1p3b"), heads=[(3, 2), (6, 11)])
+
+
+def test_backward_split_walk_is_deterministic():
+    w = W.get("gated_layer_1p3b", B=5, H=16, T=300, Dk=64, Dv=64, seed=7460)
+    d = to_dev(W.generate(w))
+    do, dst = _upstream(w, 5)
+    run = lambda: dr.gated_delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"],
+                                                do.cuda(), d["S0"], dst.cuda())
+    a, b = run(), run()
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
 
 
 def test_backward_empty_sequence_passes_the_state_gradient():
