@@ -431,7 +431,10 @@ def bench_backward(torch, dr, W, reps=10, name="layer_1p3b", B=None):
         "workload": (f"{w.name} B{w.B} H{w.H} T{w.T} d{w.Dk}, bf16 in, fp32 state; "
                      "checkpointing forward + reverse pass (output allocation inside)"
                      + ("; reverse pass as the recursion pass then the products pass over "
-                        "runs of chunks (few heads)" if w.B * w.H <= 64 else "")),
+                        "runs of chunks (few heads)" if w.B * w.H <= 64 else
+                        "; reverse walk split over two streams (recursion over the last "
+                        "21/32 of the chunks, then the first 11/32, beside the single pass "
+                        "over the last 21/32)" if w.B * w.H <= 128 else "")),
         "tokens_per_s": w.B * w.T / t,
         "mean_call_us": round(t * 1e6, 2),
         "vs_forward_launch": None,
