@@ -191,9 +191,10 @@ dr_status recurrent_step(const void *q, const void *k, const void *v, const void
 
 // Workspace of the backward: every chunk's incoming state (the forward
 // checkpoints), then the gradient of every chunk's state and the solve's Z
-// ([B,T,H,Dv]) for the two-pass schedule; each part 256-byte aligned.
+// ([B,T,H,Dv]) for the two-pass schedule, then (few heads) the segments'
+// maps of the state-gradient recursion; each part 256-byte aligned.
 struct BwdWs {
-    int64_t ckpt, dsz, total;  // bytes of the checkpoints and of Z; all parts
+    int64_t ckpt, dsz, seg, total;  // bytes of the checkpoints, of Z, of the maps; all parts
 };
 BwdWs bwd_workspace(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, bool bf16) {
     const int64_t cb = dr::chunk_bwd_chunk(bf16);
@@ -202,10 +203,12 @@ BwdWs bwd_workspace(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, boo
     BwdWs w;
     w.ckpt = mul_checked({B, H, N, Dv, Dk, esz});
     w.dsz = mul_checked({B, T, H, Dv, esz});
+    w.seg = w.ckpt < 0 ? -1 : dr::bwd_seg_bytes(B, H, N, Dk, Dv);
     const auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
-    w.total = w.ckpt < 0 || w.dsz < 0 || w.ckpt > INT64_MAX / 4 || w.dsz > INT64_MAX / 4
+    w.total = w.ckpt < 0 || w.dsz < 0 || w.seg < 0 || w.ckpt > INT64_MAX / 4 ||
+                      w.dsz > INT64_MAX / 4 || w.seg > INT64_MAX / 4
                   ? -1
-                  : 2 * al(w.ckpt) + al(w.dsz);
+                  : 2 * al(w.ckpt) + al(w.dsz) + w.seg;
     return w;
 }
 int64_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, bool bf16) {
@@ -272,6 +275,7 @@ dr_status chunk_bwd(const void *q, const void *k, const void *v, const void *bet
         const int64_t ck = (wl.ckpt + 255) / 256 * 256;
         a.dsb = static_cast<char *>(ws) + ck;
         a.dsz = static_cast<char *>(ws) + 2 * ck;
+        if (wl.seg > 0) a.segws = static_cast<char *>(ws) + 2 * ck + (wl.dsz + 255) / 256 * 256;
     }
     return hip_status(dr::launch_chunk_bwd(a, bf16, st));
 }
@@ -422,6 +426,6 @@ const char *delta_rule_status_string(dr_status status) {
 
 int delta_rule_last_hip_error(void) { return g_last_hip_error; }
 
-int delta_rule_version(void) { return 21100; }
+int delta_rule_version(void) { return 21200; }
 
 }  // extern "C"

@@ -66,6 +66,7 @@
 #include "dr_common.hpp"
 #include "dr_launch.hpp"
 
+#include <algorithm>
 #include <climits>
 #include <mutex>
 #include <type_traits>
@@ -347,7 +348,7 @@ struct ChunkPrefetch {
         }
         if constexpr (P == 2) {
             if constexpr (MODE != 1) v.load(vv + (tok0 * H + h) * DV, rv, len, tid);
-            o.load(oo + (tok0 * H + h) * DV, rv, len, tid);
+            o.load(oo ? oo + (tok0 * H + h) * DV : oo, rv, oo ? len : 0, tid);  // null: dO = 0
             if constexpr (MODE == 2) z.load(zz + (tok0 * H + h) * DV, rv, len, tid);
         }
     }
@@ -386,6 +387,12 @@ __device__ __forceinline__ void store_rows(DT *dst, int64_t gs, int nvalid, cons
 // chunks of a head run in parallel.  MODE 3: the recursion of MODE 1 over
 // chunks [c_beg, c_end), writing nothing but dS at the start of c_beg (into
 // dS0): the incoming dS of a MODE 0 walk over the chunks before c_beg.
+// Segmented launches of MODES 1 and 3 (segP > 1): segP workgroups per (b, h),
+// workgroup part p over chunks [p segL, (p + 1) segL); their dS_T and (MODE
+// 3) dS0 arrays are per segment, [(b segP + p) H + h][d_v][d_k], and MODE 1
+// writes dS0 from segment 0 only.  ident starts dS from the identity (d_v =
+// d_k), and a null dout reads dO as zero: with both, MODE 3 gives the
+// segment's linear map of dS.
 template <typename DT, int DK, int DV, int C, bool GATED, int MODE>
 __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
@@ -393,7 +400,7 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
     const float *__restrict__ dST, const DT *__restrict__ hs, DT *__restrict__ dq,
     DT *__restrict__ dk, DT *__restrict__ dv, DT *__restrict__ dbeta, float *__restrict__ dg,
     float *__restrict__ dS0, DT *__restrict__ dsb, DT *__restrict__ dsz, int T, int H,
-    int nsplit, int c_beg, int c_end) {
+    int nsplit, int c_beg, int c_end, int segP, int segL, int ident) {
     typedef BwdCfg<DT, DK, DV, C> G;
     constexpr int NW = G::NW, NT = G::NT, KT = G::KT, VT = G::VT;
     constexpr int LDK = G::LDK, LDV = G::LDV, LDS_ = G::LDS_, LDSK = G::LDSK, LDC = G::LDC;
@@ -407,21 +414,30 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, r = lane & 15;
     const int v0 = 16 * w;
-    const int64_t head = MODE == 2 ? blockIdx.x / nsplit : blockIdx.x;
+    const bool segd = (MODE == 1 || MODE == 3) && segP > 1;  // segmented launch
+    const int nper = MODE == 2 ? nsplit : segd ? segP : 1;      // workgroups per (b, h)
+    const int64_t head = blockIdx.x / nper;
+    const int part = (int)(blockIdx.x % nper);
     const int b = (int)(head / H), h = (int)(head % H);
     const int N = (T + C - 1) / C;
     const int nthr = 64 * NW;
     // chunks [c_lo, c_hi) of this workgroup, walked in reverse
     int c_lo = 0, c_hi = N;
-    if constexpr (MODE == 0 || MODE == 3) {
+    if constexpr (MODE == 0 || MODE == 1 || MODE == 3) {
         c_lo = max(0, c_beg);
         c_hi = min(N, c_end);
     }
+    if (segd) {
+        c_lo = min(N, part * segL);
+        c_hi = min(N, c_lo + segL);
+    }
     if constexpr (MODE == 2) {
-        const int per = (N + nsplit - 1) / nsplit, part = (int)(blockIdx.x % nsplit);
+        const int per = (N + nsplit - 1) / nsplit;
         c_lo = min(N, part * per);
         c_hi = min(N, c_lo + per);
     }
+    // row of the per-segment state arrays of a segmented launch
+    const int64_t sidx = segd ? ((int64_t)b * segP + part) * H + h : head;
 
     // upper tiles of the C x C matrices stay zero
     for (int i = tid; i < C * LDC; i += nthr) {
@@ -437,8 +453,13 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
     f32x4 Dt[RECUR ? KT : 1];
 #pragma unroll
     for (int s = 0; s < (RECUR ? KT : 0); ++s) {
-        Dt[s] = dST ? *reinterpret_cast<const f32x4 *>(dST + (head * DV + v0 + r) * DK + 16 * s + 4 * g)
-                    : zero4();
+        if (ident) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Dt[s][i] = 16 * s + 4 * g + i == v0 + r ? 1.f : 0.f;
+        } else {
+            Dt[s] = dST ? *reinterpret_cast<const f32x4 *>(dST + (sidx * DV + v0 + r) * DK + 16 * s + 4 * g)
+                        : zero4();
+        }
     }
     // The in-loop code must not see these loads as pending (it would wait for
     // every memory operation in flight at their first use, in every chunk).
@@ -1183,10 +1204,11 @@ __global__ __launch_bounds__(DV * 4) void chunk_bwd_kernel(
         __syncthreads();
         if (w == 0) finalize_dg(c_lo);
     }
-    if (RECUR && dS0) {
+    if (RECUR && dS0 && (MODE == 3 || !segd || part == 0)) {
+        const int64_t oidx = MODE == 3 ? sidx : head;
 #pragma unroll
         for (int s = 0; s < KT; ++s)
-            *reinterpret_cast<f32x4 *>(dS0 + (head * DV + v0 + r) * DK + 16 * s + 4 * g) = Dt[s];
+            *reinterpret_cast<f32x4 *>(dS0 + (oidx * DV + v0 + r) * DK + 16 * s + 4 * g) = Dt[s];
     }
 }
 
@@ -1201,17 +1223,21 @@ inline int bwd_nsplit(int64_t BH, int N) {
     return ns >= 4 ? ns : 1;
 }
 
+// nsplit: workgroups per (b, h) of MODE 2; segP, segL: segments per (b, h)
+// and chunks per segment of a segmented MODE 1 / MODE 3 launch.
 template <typename DT, int DK, int DV, bool GATED, int MODE>
 hipError_t launch_bwd_mode(const ChunkBwdArgs &a, int nsplit, hipStream_t stream, int c_beg = 0,
-                           int c_end = INT_MAX) {
+                           int c_end = INT_MAX, int segP = 1, int segL = 0, bool ident = false) {
+    const int nper = MODE == 2 ? nsplit : (MODE == 1 || MODE == 3) && segP > 1 ? segP : 1;
     hipLaunchKernelGGL((chunk_bwd_kernel<DT, DK, DV, sizeof(DT) == 2 ? 32 : 16, GATED, MODE>),
-                       dim3((unsigned)(a.B * a.H * (MODE == 2 ? nsplit : 1))), dim3(DV * 4), 0,
+                       dim3((unsigned)(a.B * a.H * nper)), dim3(DV * 4), 0,
                        stream, static_cast<const DT *>(a.q), static_cast<const DT *>(a.k),
                        static_cast<const DT *>(a.v), static_cast<const DT *>(a.beta), a.g,
                        static_cast<const DT *>(a.dout), a.dS_T, static_cast<const DT *>(a.h),
                        static_cast<DT *>(a.dq), static_cast<DT *>(a.dk), static_cast<DT *>(a.dv),
                        static_cast<DT *>(a.dbeta), a.dg, a.dS0, static_cast<DT *>(a.dsb),
-                       static_cast<DT *>(a.dsz), (int)a.T, (int)a.H, nsplit, c_beg, c_end);
+                       static_cast<DT *>(a.dsz), (int)a.T, (int)a.H, nsplit, c_beg, c_end,
+                       segP, segL, ident ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -1281,10 +1307,68 @@ hipError_t launch_bwd_split(const ChunkBwdArgs &a, int N, hipStream_t stream) {
     return hipStreamWaitEvent(stream, ss->join, 0);
 }
 
+// Segmented recursion for few (b, h) (B*H <= 32, at least 4 segments of at
+// least 4 chunks).  The dS recursion over a segment is affine in the dS that
+// enters it (every chunk maps dS -> dS A_c + B_c, rows independently), so
+//   dS_start(p) = dS_end(p) A_p + B_p,  dS_end(p) = dS_start(p + 1),
+// with A_p the segment's map (the recursion from the identity with dO = 0:
+// MODE 3, ident, null dout, d_v := d_k) and B_p its response to dO from zero
+// (MODE 3).  Both run over all segments at once, the map on the side stream;
+// the chain (segment.hip, last segment first) then turns them into every
+// segment's entering dS, the recursion pass (MODE 1) runs over all segments
+// at once from those, and the products pass follows as before.
+constexpr int BWD_SEG_MAX_HEADS = 32, BWD_SEG_MIN = 4, BWD_SEG_MAX = 16;
+constexpr int BWD_SEG_MIN_CHUNKS = 4;
+
+int64_t al256(int64_t x) { return (x + 255) / 256 * 256; }
+
+template <typename DT, int DK, int DV, bool GATED>
+hipError_t launch_bwd_segmented(const ChunkBwdArgs &a, const BwdSegPlan &sp, int ns,
+                                hipStream_t stream) {
+    SideStream *ss = nullptr;
+    hipError_t e = side_stream(&ss);
+    if (e != hipSuccess) return e;
+    float *Bs = static_cast<float *>(a.segws);  // B_p, then each segment's entering dS
+    float *As = reinterpret_cast<float *>(static_cast<char *>(a.segws) +
+                                          al256(a.B * sp.P * a.H * (int64_t)DV * DK * 4));
+    ChunkBwdArgs aff = a, map = a, rec = a;
+    aff.dS_T = nullptr;
+    aff.dS0 = Bs;
+    aff.dsb = aff.dsz = nullptr;
+    map.Dv = DK;
+    map.v = map.dout = nullptr;
+    map.dv = nullptr;
+    map.dS_T = nullptr;
+    map.dS0 = As;
+    map.dsb = map.dsz = nullptr;
+    rec.dS_T = Bs;
+    {
+        std::lock_guard<std::mutex> lock(ss->mu);
+        if ((e = hipEventRecord(ss->fork, stream)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return e;
+        if ((e = launch_bwd_mode<DT, DK, DK, GATED, 3>(map, 1, ss->s, 0, INT_MAX, sp.P, sp.L,
+                                                       true)) != hipSuccess)
+            return e;
+        if ((e = launch_bwd_mode<DT, DK, DV, GATED, 3>(aff, 1, stream, 0, INT_MAX, sp.P, sp.L,
+                                                       false)) != hipSuccess)
+            return e;
+        if ((e = hipEventRecord(ss->join, ss->s)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(stream, ss->join, 0)) != hipSuccess) return e;
+    }
+    if ((e = launch_seg_chain(Bs, As, a.dS_T, nullptr, a.B, sp.P, a.H, DK, DV, true, stream)) !=
+        hipSuccess)
+        return e;
+    if ((e = launch_bwd_mode<DT, DK, DV, GATED, 1>(rec, 1, stream, 0, INT_MAX, sp.P, sp.L)) !=
+        hipSuccess)
+        return e;
+    return launch_bwd_mode<DT, DK, DV, GATED, 2>(a, ns, stream);
+}
+
 // One reverse pass per (b, h); where that leaves compute units idle and the
-// caller gave the scratch (dsb, dsz), either the recursion pass then the
-// products pass over nsplit runs of chunks per (b, h) (few heads), or the
-// reverse walk in two pieces on two streams (up to 128 heads).
+// caller gave the scratch (dsb, dsz), either the recursion pass (segmented
+// for few heads, above) then the products pass over nsplit runs of chunks
+// per (b, h) (up to 64 heads), or the reverse walk in two pieces on two
+// streams (up to 128 heads).
 template <typename DT, int DK, int DV, bool GATED>
 hipError_t launch_bwd_gate(const ChunkBwdArgs &a, hipStream_t stream) {
     constexpr int C = sizeof(DT) == 2 ? 32 : 16;
@@ -1295,6 +1379,11 @@ hipError_t launch_bwd_gate(const ChunkBwdArgs &a, hipStream_t stream) {
             const int N = (int)((a.T + C - 1) / C);
             const int ns = bwd_nsplit(a.B * a.H, N);
             if (a.dsb && a.dsz && ns >= 2) {
+                if constexpr (bwd_fits<DT, DK, DK, C, GATED>() && BwdCfg<DT, DK, DK, C>::DBUF) {
+                    const BwdSegPlan sp = bwd_seg_plan(a.B, a.H, N);
+                    if (a.segws && sp.P > 0)
+                        return launch_bwd_segmented<DT, DK, DV, GATED>(a, sp, ns, stream);
+                }
                 const hipError_t e = launch_bwd_mode<DT, DK, DV, GATED, 1>(a, 1, stream);
                 if (e != hipSuccess) return e;
                 return launch_bwd_mode<DT, DK, DV, GATED, 2>(a, ns, stream);
@@ -1337,6 +1426,26 @@ hipError_t bwd_dk(const ChunkBwdArgs &a, hipStream_t stream) {
 }  // namespace
 
 int chunk_bwd_chunk(bool bf16) { return bf16 ? 32 : 16; }
+
+BwdSegPlan bwd_seg_plan(int64_t B, int64_t H, int64_t N) {
+    BwdSegPlan pl{0, 0};
+    const int64_t BH = B * H;
+    if (BH <= 0 || BH > BWD_SEG_MAX_HEADS || N <= 0) return pl;
+    int64_t P = std::min<int64_t>(std::min<int64_t>(128 / BH, N / BWD_SEG_MIN_CHUNKS), BWD_SEG_MAX);
+    if (P < BWD_SEG_MIN) return pl;
+    const int64_t L = (N + P - 1) / P;
+    P = (N + L - 1) / L;
+    if (P < BWD_SEG_MIN) return pl;
+    pl.P = (int)P;
+    pl.L = (int)L;
+    return pl;
+}
+
+int64_t bwd_seg_bytes(int64_t B, int64_t H, int64_t N, int64_t Dk, int64_t Dv) {
+    const BwdSegPlan pl = bwd_seg_plan(B, H, N);
+    if (pl.P == 0) return 0;
+    return al256(B * pl.P * H * Dv * Dk * 4) + al256(B * pl.P * H * Dk * Dk * 4);
+}
 
 hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, bool bf16, hipStream_t stream) {
     return bf16 ? bwd_dk<__bf16>(a, stream) : bwd_dk<float>(a, stream);

@@ -87,11 +87,24 @@ struct ChunkBwdArgs {
     const float *g = nullptr;
     float *dg = nullptr;
     void *dsb = nullptr, *dsz = nullptr;
+    void *segws = nullptr;  // per-segment maps of the segmented recursion
 };
 
 hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, bool bf16, hipStream_t stream);
+// Chain over P segments per (b, h): S <- S M_p + H_p in fp32, segments first
+// to last (rev: last to first); Hs holds H_p on entry and each step's
+// incoming S on exit; S0 (or zero) enters, S_T (if set) gets the result.
+hipError_t launch_seg_chain(float *Hs, const float *M, const float *S0, float *S_T, int64_t B,
+                            int P, int64_t H, int Dk, int Dv, bool rev, hipStream_t stream);
 // Tokens per chunk of the backward (and of its forward checkpoints).
 int chunk_bwd_chunk(bool bf16);
+// Segments of the backward's state-gradient recursion for few (b, h): P
+// segments of L chunks (P = 0: no segments), and the bytes of their maps.
+struct BwdSegPlan {
+    int P, L;
+};
+BwdSegPlan bwd_seg_plan(int64_t B, int64_t H, int64_t N);
+int64_t bwd_seg_bytes(int64_t B, int64_t H, int64_t N, int64_t Dk, int64_t Dv);
 
 // Arguments of the single-token decode step (state updated in place).  g is
 // the log forget gate [B,H] (fp32) of the gated rule, or nullptr; scale

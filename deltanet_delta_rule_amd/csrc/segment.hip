@@ -133,7 +133,9 @@ __device__ __forceinline__ void chain_fetch(f32x4 (&mreg)[NMV], f32x4 &hreg, con
 // S M_p (16 x 16 tiles, D layout: lane (g, r) holds rows 4g .. 4g + 3 of
 // column r), contracting over d_k four keys at a time with S, M_p and H_p
 // staged in LDS.  Hs holds H_p on entry and S_in(p) on exit (each workgroup
-// touches only its own rows).  The maps are independent of the chain, so
+// touches only its own rows).  With rev the segments are taken last to
+// first (the backward's chain of state gradients, whose maps compose in
+// reverse).  The maps are independent of the chain, so
 // each thread keeps its share of the next PD steps' M_p and H_p in flight in
 // a register ring: a step waits only for its own operands, issued PD steps
 // earlier, instead of one fetch latency per step.  A step reads all of its
@@ -144,7 +146,7 @@ template <int DK>
 __global__ __launch_bounds__(ChainCfg<DK>::NTH) void seg_chain_kernel(float *Hs, const float *M,
                                                                      const float *S0,
                                                                      float *S_T, int P, int H,
-                                                                     int Dv) {
+                                                                     int Dv, int rev) {
     using CF = ChainCfg<DK>;
     constexpr int NWV = CF::NWV, PD = CF::PD, NACC = CF::NACC, NTH = CF::NTH;
     constexpr int NT = DK / 16;                 // output tiles per row block
@@ -185,8 +187,11 @@ __global__ __launch_bounds__(ChainCfg<DK>::NTH) void seg_chain_kernel(float *Hs,
     // merge or at the loop's back edge waits for every load in flight.
     f32x4 mreg[PD][NMV];
     f32x4 hreg[PD];
+    // segment of chain step p
+    auto segof = [&](int p) { return rev ? P - 1 - p : p; };
     auto fetch = [&](int p, f32x4(&mr)[NMV], f32x4 &hr) {
-        chain_fetch<DK, NMV, MEXACT>(mr, hr, M, Hs, b * P + min(p, P - 1), H, h, Dv, row0, tid);
+        chain_fetch<DK, NMV, MEXACT>(mr, hr, M, Hs, b * P + segof(min(p, P - 1)), H, h, Dv, row0,
+                                     tid);
     };
     // S_in(0) = S0 (or zero): its loads go out first, then the ring's, and
     // only then is S0 waited for, so the two latencies overlap (the loads
@@ -215,7 +220,7 @@ __global__ __launch_bounds__(ChainCfg<DK>::NTH) void seg_chain_kernel(float *Hs,
     }
     // one chain step: S_in(p) -> S_in(p + 1); refill the slot with step p + PD
     auto step = [&](int p, f32x4(&mr)[NMV], f32x4 &hr, bool refill) {
-        const int64_t seg = b * P + p;
+        const int64_t seg = b * P + segof(p);
         float *hp = Hs + ((seg * H + h) * Dv + row0) * DK;
         // M_p and H_p into LDS
 #pragma unroll
@@ -305,16 +310,27 @@ __global__ __launch_bounds__(ChainCfg<DK>::NTH) void seg_chain_kernel(float *Hs,
 
 template <int DK>
 hipError_t launch_chain(float *Hs, const float *M, const float *S0, float *S_T, int64_t B, int P,
-                        int64_t H, int Dv, hipStream_t stream) {
+                        int64_t H, int Dv, hipStream_t stream, bool rev = false) {
     const int64_t grid = B * H * (Dv / 16);
     hipLaunchKernelGGL((seg_chain_kernel<DK>), dim3((unsigned)grid), dim3(ChainCfg<DK>::NTH), 0,
-                       stream, Hs, M, S0, S_T, P, (int)H, Dv);
+                       stream, Hs, M, S0, S_T, P, (int)H, Dv, rev ? 1 : 0);
     return hipGetLastError();
 }
 
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
+
+hipError_t launch_seg_chain(float *Hs, const float *M, const float *S0, float *S_T, int64_t B,
+                            int P, int64_t H, int Dk, int Dv, bool rev, hipStream_t stream) {
+    switch (Dk) {
+    case 16: return launch_chain<16>(Hs, M, S0, S_T, B, P, H, Dv, stream, rev);
+    case 32: return launch_chain<32>(Hs, M, S0, S_T, B, P, H, Dv, stream, rev);
+    case 64: return launch_chain<64>(Hs, M, S0, S_T, B, P, H, Dv, stream, rev);
+    case 128: return launch_chain<128>(Hs, M, S0, S_T, B, P, H, Dv, stream, rev);
+    default: return hipErrorInvalidValue;
+    }
+}
 
 SegPlan seg_plan(int64_t B, int64_t T, int64_t H, int Dk, int Dv, int chunk, bool combined) {
     SegPlan pl{0, 0, 0};

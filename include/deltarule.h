@@ -378,7 +378,11 @@ dr_status delta_rule_recurrent_step_ex(const void *q, const void *k, const void 
  * incoming state in `workspace` (in `dtype`, the precision the backward's
  * products use it in), then walks the chunks in reverse.  With B*H <= 64
  * the walk is a reverse pass over the state-gradient recursion alone, then
- * the gradients of the chunks formed in parallel from its results.  With
+ * the gradients of the chunks formed in parallel from its results; with
+ * B*H <= 32 and at least 16 chunks that recursion itself runs in segments:
+ * each segment's linear map and its response to dout are formed at once,
+ * chained from the last segment, and the segments then run side by side
+ * from their incoming state gradients.  With
  * 64 < B*H <= 128 (one workgroup per (b, h) would leave half the GPU idle)
  * and at least 8 chunks it goes in two pieces: the last ~21/32 of the
  * chunks run from dS_T on the library's second stream while `stream` runs
@@ -391,7 +395,8 @@ dr_status delta_rule_recurrent_step_ex(const void *q, const void *k, const void 
  *                       bytes (16-byte aligned; contents on return: the
  *                       forward checkpoints, [B,H,N,Dv,Dk] in the input
  *                       dtype at its start, then scratch of the two-pass
- *                       schedule or the split walk's state gradient);
+ *                       schedule or the split walk's state gradient, and
+ *                       of the segments' maps);
  *                       may be NULL when T == 0
  *   Outputs must not overlap the inputs, the workspace or each other.
  * Sizes as delta_rule_chunk_fwd (Dk, Dv in {16,32,64,128}); the chunk length
@@ -450,7 +455,8 @@ int delta_rule_last_hip_error(void);
  * delta_rule_chunk_fwd_noalloc and DR_ERR_SCRATCH; 2.9.0:
  * gated_delta_rule_chunk_bwd; 2.10.0: the backward's workspace also holds
  * the scratch of its two-pass schedule; 2.11.0: the backward's split
- * reverse walk on a second stream). */
+ * reverse walk on a second stream; 2.12.0: the segmented state-gradient
+ * recursion for few heads, its maps in the workspace). */
 int delta_rule_version(void);
 
 #ifdef __cplusplus

@@ -311,6 +311,20 @@ def test_backward_workspace_size(lib):
     assert f(2, 100, 3, 64, 32, dr.DR_F32) == 2 * al(2 * 3 * 7 * 32 * 64 * 4) + al(2 * 100 * 3 * 32 * 4)
     assert f(1, 3, 1, 16, 16, dr.DR_BF16) == 2 * al(16 * 16 * 2) + al(3 * 16 * 2)
     assert f(1, 0, 1, 16, 16, dr.DR_BF16) == 0
+    # few (b, h) and enough chunks: the segments' maps of the state-gradient
+    # recursion follow, P segments of fp32 [Dv,Dk] responses and [Dk,Dk] maps
+    # per (b, h): 128 / (B H) segments, at most 16 and of at least 4 chunks,
+    # used from 4 segments and up to 32 (b, h)
+    base = lambda B, T, H, Dk, Dv: (2 * al(B * H * (T // 32) * Dv * Dk * 2) +
+                                    al(B * T * H * Dv * 2))
+    assert f(1, 2048, 16, 128, 128, dr.DR_BF16) == base(1, 2048, 16, 128, 128) + \
+        2 * al(8 * 16 * 128 * 128 * 4)                          # 8 segments of 8 chunks
+    assert f(1, 512, 16, 128, 64, dr.DR_BF16) == base(1, 512, 16, 128, 64) + \
+        al(4 * 16 * 64 * 128 * 4) + al(4 * 16 * 128 * 128 * 4)  # 4 segments of 4 chunks
+    assert f(2, 2048, 16, 64, 64, dr.DR_BF16) == base(2, 2048, 16, 64, 64) + \
+        2 * al(2 * 4 * 16 * 64 * 64 * 4)                        # 32 (b, h): 4 segments
+    assert f(4, 2048, 16, 64, 64, dr.DR_BF16) == base(4, 2048, 16, 64, 64)   # 64 (b, h): none
+    assert f(1, 448, 16, 64, 64, dr.DR_BF16) == base(1, 448, 16, 64, 64)     # 14 chunks: 3 segments
     assert f(1, 10, 1, 24, 16, dr.DR_BF16) == 0   # unsupported size
     assert f(-1, 10, 1, 16, 16, dr.DR_BF16) == 0
 

@@ -124,6 +124,25 @@ def test_backward_split_reverse_walk(gated):
     _check(w, heads=[(0, 0), (2, 7), (4, 15)])
 
 
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("dtype,Dk,Dv", [("bf16", 64, 128), ("bf16", 128, 64), ("bf16", 32, 32),
+                                         ("f32", 64, 64)])
+def test_backward_segmented_recursion(gated, dtype, Dk, Dv):
+    # 4 (b, h), 1000 tokens: the state-gradient recursion in segments (bf16:
+    # 32 chunks in 8 segments of 4, the last chunk 8 tokens long), each
+    # segment's map and response to dO formed at once, then chained
+    w = W.get("layer_1p3b", B=1, H=4, T=1000, Dk=Dk, Dv=Dv, dtype=dtype,
+              gate_amax=4.0 if gated else 0.0, beta_scale=2.0, s0_std=0.02, seed=7470)
+    _check(w, seed=9)
+
+
+def test_backward_one_sequence_full_size_sampled_heads():
+    # the benchmark's one-sequence backward: B1 H16 T2048 d128, 64 chunks in
+    # 8 segments (every head computed, three checked)
+    _check(W.get("layer_1p3b", B=1), heads=[(0, 0), (0, 9), (0, 15)])
+    _check(W.get("gated_layer_1p3b", B=1), heads=[(0, 3), (0, 12)])
+
+
 def test_backward_full_size_sampled_heads():
     # the benchmark's configuration and launch: B8 H16 T2048 d128, 64 chunks,
     # the split reverse walk (every head computed, two checked)
