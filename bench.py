@@ -430,8 +430,9 @@ def bench_backward(torch, dr, W, reps=10, name="layer_1p3b", B=None):
     return {
         "workload": (f"{w.name} B{w.B} H{w.H} T{w.T} d{w.Dk}, bf16 in, fp32 state; "
                      "checkpointing forward + reverse pass (output allocation inside)"
-                     + ("; reverse pass as the recursion pass then the products pass over "
-                        "runs of chunks (few heads)" if w.B * w.H <= 64 else
+                     + ("; reverse pass as the recursion pass (in segments whose maps are "
+                        "chained, for at most 32 (b, h)) then the products pass over runs of "
+                        "chunks (few heads)" if w.B * w.H <= 64 else
                         "; reverse walk split over two streams (recursion over the last "
                         "21/32 of the chunks, then the first 11/32, beside the single pass "
                         "over the last 21/32)" if w.B * w.H <= 128 else "")),
@@ -440,6 +441,63 @@ def bench_backward(torch, dr, W, reps=10, name="layer_1p3b", B=None):
         "vs_forward_launch": None,
         "workspace_bytes": int(ws.numel()),
     }
+
+
+def bench_training_step(torch, dr, W, reps=10, name="layer_1p3b"):
+    """The chunked work of a training step on the layer shape: the forward
+    (chunk 64) then the backward that forms its own checkpoints, against the
+    forward that keeps the checkpoints in the backward's workspace (chunk 32,
+    delta_rule_chunk_fwd_checkpointed) then the backward that reuses them
+    (DR_BWD_CHECKPOINTS_READY); mean time per step and per call with HIP
+    events on the launch stream, upstream gradients for o and S_T."""
+    w = W.get(name)
+    x = W.generate(w)
+    dev = torch.device("cuda:0")
+    d = {n: (None if t is None else t.to(dev)) for n, t in x.items()}
+    gen = torch.Generator(device="cpu").manual_seed(11)
+    do = torch.randn(w.B, w.T, w.H, w.Dv, generator=gen).to(w.torch_dtype).to(dev)
+    dst = torch.randn(w.B, w.H, w.Dv, w.Dk, generator=gen).to(dev)
+    lib = dr.load_library()
+    ws = torch.empty(int(lib.delta_rule_chunk_bwd_workspace_bytes(w.B, w.T, w.H, w.Dk, w.Dv,
+                                                                  dr.DR_BF16)),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty((w.B, w.T, w.H, w.Dv), dtype=w.torch_dtype, device=dev)
+    st = torch.empty((w.B, w.H, w.Dv, w.Dk), dtype=torch.float32, device=dev)
+    args = (d["q"], d["k"], d["v"], d["beta"])
+
+    def fwd():
+        dr.delta_rule_chunk_fwd(*args, d["S0"], chunk=w.chunk, o=o, S_T=st, workspace=False)
+
+    def bwd():
+        dr.delta_rule_chunk_bwd(*args, do, d["S0"], dst, workspace=ws)
+
+    def fwd_ck():
+        dr.delta_rule_chunk_fwd_checkpointed(*args, d["S0"], o=o, S_T=st, workspace=ws)
+
+    def bwd_reuse():
+        dr.delta_rule_chunk_bwd(*args, do, d["S0"], dst, workspace=ws, checkpoints_ready=True)
+
+    def plain_step():
+        fwd()
+        bwd()
+
+    def ck_step():
+        fwd_ck()
+        bwd_reuse()
+
+    res = {}
+    for key, fn in (("forward_then_backward_us", plain_step),
+                    ("checkpointed_forward_then_backward_us", ck_step),
+                    ("checkpointed_forward_us", fwd_ck)):
+        settle(torch, fn)
+        res[key] = round(timed_steps(torch, fn, reps) * 1e6, 2)
+    fwd_ck()  # the checkpoints of these inputs, then the backward alone on them
+    settle(torch, bwd_reuse)
+    res["backward_reusing_checkpoints_us"] = round(timed_steps(torch, bwd_reuse, reps) * 1e6, 2)
+    res["workload"] = (f"{w.name} B{w.B} H{w.H} T{w.T} d{w.Dk}, bf16 in, fp32 state; "
+                       "forward (chunk 64) + backward, against the checkpointing forward "
+                       "(chunk 32) + the backward on its checkpoints")
+    return res
 
 
 def sweep_schedules(torch, dr, W):
@@ -639,6 +697,11 @@ def main():
             out["backward"]["gated"] = bench_backward(torch, dr, W, name="gated_layer_1p3b")
         log("backward: one sequence of the layer shape (two-pass schedule)")
         out["backward"]["one_sequence"] = bench_backward(torch, dr, W, B=1)
+        log("training step: forward + backward, with and without reused checkpoints")
+        out["backward"]["training_step"] = bench_training_step(torch, dr, W)
+        ts = out["backward"]["training_step"]
+        ts["backward_reusing_vs_forward_launch"] = round(
+            ts["backward_reusing_checkpoints_us"] / roof["mean_launch_us"], 2)
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle on the whole workload, then on one thread")
         torch.cuda.synchronize()

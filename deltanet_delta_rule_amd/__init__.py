@@ -32,6 +32,7 @@ __all__ = [
     "gated_delta_rule_recurrent_step",
     "delta_rule_chunk_bwd",
     "gated_delta_rule_chunk_bwd",
+    "delta_rule_chunk_fwd_checkpointed",
     "delta_rule_chunk_fwd_noalloc",
     "DeltaRuleScratchError",
     "kda_recurrent_step",
@@ -51,6 +52,7 @@ DR_OK, DR_ERR_INVALID_ARG, DR_ERR_UNSUPPORTED, DR_ERR_HIP, DR_ERR_SCRATCH = 0, 1
 # DR_STATIC_SCRATCH_BYTES of include/deltarule.h
 DR_STATIC_SCRATCH_BYTES = 16 * 1024 * 1024 + 64 * 1024
 DR_F32, DR_BF16 = 0, 1
+DR_BWD_CHECKPOINTS_READY = 1
 
 _lib = None
 
@@ -122,6 +124,12 @@ def load_library():
     lib.gated_delta_rule_chunk_bwd.restype = i32
     lib.gated_delta_rule_chunk_bwd.argtypes = [vp] * 15 + [ctypes.c_size_t, i64, i64, i64, i64,
                                                            i64, i32, vp]
+    lib.delta_rule_chunk_fwd_checkpointed.restype = i32
+    lib.delta_rule_chunk_fwd_checkpointed.argtypes = [vp] * 9 + [ctypes.c_size_t, i64, i64, i64,
+                                                                 i64, i64, i32, vp]
+    lib.delta_rule_chunk_bwd_ex.restype = i32
+    lib.delta_rule_chunk_bwd_ex.argtypes = [vp] * 15 + [ctypes.c_size_t, i64, i64, i64, i64, i64,
+                                                        ctypes.c_uint32, i32, vp]
     lib.delta_rule_status_string.restype = ctypes.c_char_p
     lib.delta_rule_status_string.argtypes = [i32]
     lib.delta_rule_last_hip_error.restype = i32
@@ -417,27 +425,80 @@ def gated_delta_rule_recurrent_step(q, k, v, beta, g, S, *, o=None, scale=None,
 
 
 def delta_rule_chunk_bwd(q, k, v, beta, do, S0=None, dS_T=None, *, workspace=None,
-                         need_dS0=True, stream=None):
+                         need_dS0=True, checkpoints_ready=False, stream=None):
     """Gradients of ``delta_rule_chunk_fwd`` (plain rule) for upstream
     gradients ``do`` ``[B,T,H,Dv]`` (dtype of q) and ``dS_T`` ``[B,H,Dv,Dk]``
     float32 or None.  Returns a dict with dq, dk, dv, dbeta (dtype of q) and
     dS0 (float32, or None when ``need_dS0`` is False).  ``workspace`` (a
     uint8 GPU tensor of at least ``delta_rule_chunk_bwd_workspace_bytes``
-    bytes) holds the forward checkpoints; it is allocated when not given."""
-    return _bwd_call(q, k, v, beta, None, do, S0, dS_T, workspace, need_dS0, stream)
+    bytes) holds the forward checkpoints; it is allocated when not given.
+    ``checkpoints_ready``: the workspace already holds them, written by
+    ``delta_rule_chunk_fwd_checkpointed`` for these same inputs, so the
+    checkpointing forward pass is skipped."""
+    return _bwd_call(q, k, v, beta, None, do, S0, dS_T, workspace, need_dS0, stream,
+                     checkpoints_ready)
 
 
 def gated_delta_rule_chunk_bwd(q, k, v, beta, g, do, S0=None, dS_T=None, *, workspace=None,
-                               need_dS0=True, stream=None):
+                               need_dS0=True, checkpoints_ready=False, stream=None):
     """Gradients of ``gated_delta_rule_chunk_fwd``: as ``delta_rule_chunk_bwd``
     with g ``[B,T,H]`` float32 (the log forget gate) among the inputs; the
     dict also holds dg (float32 ``[B,T,H]``)."""
     if g is None:
         raise ValueError("the gated backward needs g")
-    return _bwd_call(q, k, v, beta, g, do, S0, dS_T, workspace, need_dS0, stream)
+    return _bwd_call(q, k, v, beta, g, do, S0, dS_T, workspace, need_dS0, stream,
+                     checkpoints_ready)
 
 
-def _bwd_call(q, k, v, beta, g, do, S0, dS_T, workspace, need_dS0, stream):
+def delta_rule_chunk_fwd_checkpointed(q, k, v, beta, S0=None, *, g=None,
+                                      output_final_state=True, o=None, S_T=None,
+                                      workspace=None, stream=None):
+    """The forward of the plain rule (or, with ``g``, the gated rule) that
+    also writes every chunk's incoming state into the backward's
+    ``workspace`` (allocated when None), at the backward's chunk length (32
+    tokens for bfloat16, 16 for float32).  Returns ``(o, S_T, workspace)``;
+    pass that workspace with ``checkpoints_ready=True`` to the backward of the
+    same inputs, which then skips its checkpointing forward pass."""
+    torch = _torch()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("the chunked forward needs GPU tensors")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    code = _dtype_code(q)
+    _need(q, "q", (B, T, H, Dk), dt, dev)
+    _need(k, "k", (B, T, H, Dk), dt, dev)
+    _need(v, "v", (B, T, H, Dv), dt, dev)
+    _need(beta, "beta", (B, T, H), dt, dev)
+    if S0 is not None:
+        _need(S0, "S0", (B, H, Dv, Dk), torch.float32, dev)
+    if g is not None:
+        _need(g, "g", (B, T, H), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=dt, device=dev)
+    else:
+        _need(o, "o", (B, T, H, Dv), dt, dev)
+    if output_final_state and S_T is None:
+        S_T = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+    elif S_T is not None:
+        _need(S_T, "S_T", (B, H, Dv, Dk), torch.float32, dev)
+    lib = load_library()
+    nbytes = int(lib.delta_rule_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, code))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace must be a GPU tensor of at least {nbytes} bytes")
+    nws = workspace.numel() * workspace.element_size()
+    st = lib.delta_rule_chunk_fwd_checkpointed(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(o), _ptr(S_T),
+        _ptr(workspace), nws, B, T, H, Dk, Dv, code, _stream(dev, stream))
+    _check(st)
+    return o, S_T, workspace
+
+
+def _bwd_call(q, k, v, beta, g, do, S0, dS_T, workspace, need_dS0, stream,
+              checkpoints_ready=False):
     torch = _torch()
     dev = q.device
     if dev.type != "cuda":
@@ -468,7 +529,15 @@ def _bwd_call(q, k, v, beta, g, do, S0, dS_T, workspace, need_dS0, stream):
            "dS0": torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
            if need_dS0 else None}
     nws = workspace.numel() * workspace.element_size()
-    if g is None:
+    if checkpoints_ready:
+        if g is not None:
+            out["dg"] = torch.empty_like(g)
+        st = lib.delta_rule_chunk_bwd_ex(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(do), _ptr(dS_T),
+            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
+            _ptr(out.get("dg")), _ptr(out["dS0"]), _ptr(workspace), nws, B, T, H, Dk, Dv,
+            DR_BWD_CHECKPOINTS_READY, code, _stream(dev, stream))
+    elif g is None:
         st = lib.delta_rule_chunk_bwd(
             _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(S0), _ptr(do), _ptr(dS_T),
             _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),

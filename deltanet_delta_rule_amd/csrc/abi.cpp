@@ -73,7 +73,8 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
                     int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t chunk,
                     const int32_t *cu, int64_t nseq, float scale, bool l2, dr_dtype dtype,
                     void *stream, const float *gk = nullptr, bool recurrent = false,
-                    void *ws = nullptr, int64_t ws_bytes = 0, bool noalloc = false) {
+                    void *ws = nullptr, int64_t ws_bytes = 0, bool noalloc = false,
+                    void *ckpt = nullptr, int64_t ckpt_bytes = 0) {
     if (dtype != DR_F32 && dtype != DR_BF16) return DR_ERR_INVALID_ARG;
     if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0 || chunk < 0) return DR_ERR_INVALID_ARG;
     if (cu && (B != 1 || nseq < 0 || !aligned_to(cu, 4))) return DR_ERR_INVALID_ARG;
@@ -100,6 +101,10 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
     if (gk && gated) return DR_ERR_INVALID_ARG;  // one decay kind
     if (ws && (ws_bytes < 0 || !aligned16(ws))) return DR_ERR_INVALID_ARG;
     if (noalloc && (ws || ws_bytes != 0)) return DR_ERR_INVALID_ARG;  // scratch is the library's
+    // checkpoints for the backward: its chunk, the forward it differentiates
+    if (ckpt && (cu || gk || recurrent || l2 || scale != 1.f || ws || noalloc ||
+                 chunk != dr::chunk_bwd_chunk(dtype == DR_BF16) || !aligned16(ckpt)))
+        return DR_ERR_INVALID_ARG;
     // q, k, gk and the states are read in 16-byte vectors and o is written
     // in 8- or 16-byte vectors (the chunked kernels); v and beta are read
     // element-wise
@@ -117,23 +122,25 @@ dr_status chunk_fwd(const void *q, const void *k, const void *v, const void *bet
                        {cu, (nseq + 1) * 4},  {gk, nqk * 4}};
     // the workspace is written before the inputs are read: an output too
     const Span so{o, nv * esz}, sst{S_T, ns * 4}, sws{ws, ws ? ws_bytes : 0};
+    const Span sck{ckpt, ckpt ? ckpt_bytes : 0};
     for (const Span &s : in) {
         if (T > 0 && overlaps(so, s)) return DR_ERR_INVALID_ARG;
         // S_T may be exactly S0 (in-place carry); any other overlap is rejected
         if (overlaps(sst, s) && !(s.p == S0 && S_T == S0)) return DR_ERR_INVALID_ARG;
-        if (overlaps(sws, s)) return DR_ERR_INVALID_ARG;
+        if (overlaps(sws, s) || overlaps(sck, s)) return DR_ERR_INVALID_ARG;
     }
     if (T > 0 && overlaps(so, sst)) return DR_ERR_INVALID_ARG;
     if (overlaps(so, sws) || overlaps(sst, sws)) return DR_ERR_INVALID_ARG;
+    if ((T > 0 && overlaps(so, sck)) || overlaps(sst, sck)) return DR_ERR_INVALID_ARG;
 
     dr::ChunkFwdArgs a{q,       k,        v,       beta,       gated ? g : nullptr,
-                       S0,      o,        S_T,     nullptr,    cu,
+                       S0,      o,        S_T,     ckpt,       cu,
                        ns_count, T,       H,       (int)Dk,    (int)Dv,
                        (int)chunk, scale, l2,     gk,       recurrent};
     // one long sequence per head: the segment-parallel schedule, when the
     // caller gave it a large enough workspace (or, without allocation, when
     // the library's static scratch holds what it needs)
-    if ((ws || noalloc) && !cu && !recurrent &&
+    if ((ws || noalloc) && !cu && !recurrent && !ckpt &&
         (!gk || dr::kda_chunk_supported(a, dtype == DR_BF16))) {
         const dr::SegPlan pl =
             dr::seg_plan(B, T, H, (int)Dk, (int)Dv, (int)chunk,
@@ -219,7 +226,7 @@ dr_status chunk_bwd(const void *q, const void *k, const void *v, const void *bet
                     const float *g, const float *S0, const void *dout, const float *dS_T,
                     void *dq, void *dk, void *dv, void *dbeta, float *dg, float *dS0, void *ws,
                     size_t ws_bytes, int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
-                    bool gated, dr_dtype dtype, void *stream) {
+                    bool gated, dr_dtype dtype, void *stream, bool ckpt_ready = false) {
     if (dtype != DR_F32 && dtype != DR_BF16) return DR_ERR_INVALID_ARG;
     if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0) return DR_ERR_INVALID_ARG;
     if (!supported_dim(Dk) || !supported_dim(Dv)) return DR_ERR_UNSUPPORTED;
@@ -260,7 +267,7 @@ dr_status chunk_bwd(const void *q, const void *k, const void *v, const void *bet
     }
     const hipStream_t st = static_cast<hipStream_t>(stream);
     void *h = ws;
-    if (T > 0) {
+    if (T > 0 && !ckpt_ready) {
         const dr::ChunkFwdArgs f{q,      k,       v,        beta,     g,       S0,
                                  nullptr, nullptr, h,        nullptr,  B,       T,
                                  H,      (int)Dk, (int)Dv,  dr::chunk_bwd_chunk(bf16),
@@ -411,6 +418,39 @@ dr_status gated_delta_rule_chunk_bwd(const void *q, const void *k, const void *v
                      workspace_bytes, B, T, H, Dk, Dv, true, dtype, stream);
 }
 
+dr_status delta_rule_chunk_fwd_checkpointed(const void *q, const void *k, const void *v,
+                                            const void *beta, const float *g, const float *S0,
+                                            void *o, float *S_T, void *workspace,
+                                            size_t workspace_bytes, int64_t B, int64_t T,
+                                            int64_t H, int64_t Dk, int64_t Dv, dr_dtype dtype,
+                                            void *stream) {
+    if (!valid_dtype(dtype) || (dtype != DR_F32 && dtype != DR_BF16)) return DR_ERR_INVALID_ARG;
+    if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0) return DR_ERR_INVALID_ARG;
+    if (!supported_dim(Dk) || !supported_dim(Dv)) return DR_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0) return DR_OK;
+    const bool bf16 = dtype == DR_BF16;
+    const int64_t need = bwd_workspace_bytes(B, T, H, Dk, Dv, bf16);
+    if (need < 0) return DR_ERR_UNSUPPORTED;
+    if (T > 0 && (!workspace || (int64_t)workspace_bytes < need)) return DR_ERR_INVALID_ARG;
+    return chunk_fwd(q, k, v, beta, g, g != nullptr, S0, o, S_T, B, T, H, Dk, Dv,
+                     dr::chunk_bwd_chunk(bf16), nullptr, 0, 1.f, false, dtype, stream, nullptr,
+                     false, nullptr, 0, false, T > 0 ? workspace : nullptr,
+                     bwd_workspace(B, T, H, Dk, Dv, bf16).ckpt);
+}
+
+dr_status delta_rule_chunk_bwd_ex(const void *q, const void *k, const void *v, const void *beta,
+                                  const float *g, const float *S0, const void *dout,
+                                  const float *dS_T, void *dq, void *dk, void *dv, void *dbeta,
+                                  float *dg, float *dS0, void *workspace, size_t workspace_bytes,
+                                  int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                  uint32_t flags, dr_dtype dtype, void *stream) {
+    if (!valid_dtype(dtype)) return DR_ERR_INVALID_ARG;
+    if (flags & ~(uint32_t)DR_BWD_CHECKPOINTS_READY) return DR_ERR_INVALID_ARG;
+    return chunk_bwd(q, k, v, beta, g, S0, dout, dS_T, dq, dk, dv, dbeta, g ? dg : nullptr, dS0,
+                     workspace, workspace_bytes, B, T, H, Dk, Dv, g != nullptr, dtype, stream,
+                     (flags & DR_BWD_CHECKPOINTS_READY) != 0);
+}
+
 const char *delta_rule_status_string(dr_status status) {
     switch (raw_enum(status)) {
     case DR_OK: return "DR_OK";
@@ -426,6 +466,6 @@ const char *delta_rule_status_string(dr_status status) {
 
 int delta_rule_last_hip_error(void) { return g_last_hip_error; }
 
-int delta_rule_version(void) { return 21200; }
+int delta_rule_version(void) { return 21300; }
 
 }  // extern "C"

@@ -442,6 +442,55 @@ dr_status gated_delta_rule_chunk_bwd(const void *q, const void *k, const void *v
 /* Static, human-readable name of a status code (never NULL). */
 const char *delta_rule_status_string(dr_status status);
 
+/* Flags of delta_rule_chunk_bwd_ex. */
+enum {
+    /* The workspace already holds the forward checkpoints of these very
+     * inputs (written by delta_rule_chunk_fwd_checkpointed into the same
+     * workspace, and not changed since): the backward skips its
+     * checkpointing forward pass.  Nothing checks that the inputs match. */
+    DR_BWD_CHECKPOINTS_READY = 1u
+};
+
+/*
+ * delta_rule_chunk_fwd_checkpointed -- the forward of the plain rule (g ==
+ * NULL) or the gated rule (g: [B,T,H] fp32 log forget gate) that also keeps
+ * what the backward needs: o and S_T as delta_rule_chunk_fwd /
+ * gated_delta_rule_chunk_fwd with the backward's chunk length (32 tokens for
+ * bf16, 16 for fp32; output scale 1, no in-kernel norm, no packed
+ * sequences), and every chunk's incoming state written to the start of
+ * `workspace` in the layout the backward keeps there.  A training step then
+ * runs this forward and delta_rule_chunk_bwd_ex with
+ * DR_BWD_CHECKPOINTS_READY on the same workspace, so the states are formed
+ * once (the training strategy of the paperlayer summary of arXiv:2406.06484,
+ * section 3: the forward keeps the chunk states for the backward).
+ *
+ *   workspace   at least delta_rule_chunk_bwd_workspace_bytes(B,T,H,Dk,Dv,
+ *               dtype) bytes, 16-byte aligned, not overlapping any argument;
+ *               may be NULL when T == 0
+ * Other arguments, sizes, layouts and errors as delta_rule_chunk_fwd (S_T
+ * may be NULL; S_T may equal S0).  Results equal delta_rule_chunk_fwd's with
+ * chunk = that length.
+ */
+dr_status delta_rule_chunk_fwd_checkpointed(const void *q, const void *k, const void *v,
+                                            const void *beta, const float *g, const float *S0,
+                                            void *o, float *S_T, void *workspace,
+                                            size_t workspace_bytes, int64_t B, int64_t T,
+                                            int64_t H, int64_t Dk, int64_t Dv, dr_dtype dtype,
+                                            void *stream);
+
+/*
+ * delta_rule_chunk_bwd_ex -- delta_rule_chunk_bwd (g == NULL, dg ignored) or
+ * gated_delta_rule_chunk_bwd (g and dg set) with flags: 0 or
+ * DR_BWD_CHECKPOINTS_READY.  Arguments, sizes and errors as those entry
+ * points; unknown flag bits are DR_ERR_INVALID_ARG.
+ */
+dr_status delta_rule_chunk_bwd_ex(const void *q, const void *k, const void *v, const void *beta,
+                                  const float *g, const float *S0, const void *dout,
+                                  const float *dS_T, void *dq, void *dk, void *dv, void *dbeta,
+                                  float *dg, float *dS0, void *workspace, size_t workspace_bytes,
+                                  int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                  uint32_t flags, dr_dtype dtype, void *stream);
+
 /* The hipError_t value of the last DR_ERR_HIP returned on this thread
  * (0 if none). */
 int delta_rule_last_hip_error(void);
@@ -456,7 +505,8 @@ int delta_rule_last_hip_error(void);
  * gated_delta_rule_chunk_bwd; 2.10.0: the backward's workspace also holds
  * the scratch of its two-pass schedule; 2.11.0: the backward's split
  * reverse walk on a second stream; 2.12.0: the segmented state-gradient
- * recursion for few heads, its maps in the workspace). */
+ * recursion for few heads, its maps in the workspace; 2.13.0:
+ * delta_rule_chunk_fwd_checkpointed and delta_rule_chunk_bwd_ex). */
 int delta_rule_version(void);
 
 #ifdef __cplusplus

@@ -347,6 +347,48 @@ def test_backward_rejects_invalid(lib, kw):
     assert _bwd(lib, **kw) == dr.DR_ERR_INVALID_ARG
 
 
+def _fwdck(lib, ws=P[7], wsb=1 << 40, q=P[0], k=P[1], v=P[2], beta=P[3], g=None, S0=None,
+           o=P[5], ST=None, B=1, T=64, H=2, Dk=64, Dv=64, dtype=dr.DR_BF16):
+    return lib.delta_rule_chunk_fwd_checkpointed(q, k, v, beta, g, S0, o, ST, ws, wsb, B, T, H,
+                                                 Dk, Dv, dtype, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(ws=None), dict(wsb=16), dict(ws=MISALIGNED), dict(o=None), dict(q=None),
+    dict(o=P[0]),                    # output overlaps q
+    dict(ws=P[1]),                   # checkpoints over k
+    dict(ws=P[5]),                   # checkpoints over o
+    dict(ST=P[7]),                   # final state over the checkpoints
+    dict(B=-1), dict(dtype=5),
+])
+def test_checkpointed_forward_rejects_invalid(lib, kw):
+    assert _fwdck(lib, **kw) == dr.DR_ERR_INVALID_ARG
+
+
+def test_checkpointed_forward_rejects_unsupported_and_empty(lib):
+    assert _fwdck(lib, Dk=48) == dr.DR_ERR_UNSUPPORTED
+    assert _fwdck(lib, B=0) == dr.DR_OK
+    assert _fwdck(lib, H=0) == dr.DR_OK
+
+
+def _bwdx(lib, flags=1, g=None, dg=None, ws=P[7], wsb=1 << 40, q=P[0], k=P[1], v=P[2],
+          beta=P[3], dout=P[4], dq=P[5], dk=P[6], dv=ctypes.c_void_p(0x100000 * 10),
+          dbeta=ctypes.c_void_p(0x100000 * 11), dS0=None, S0=None, dST=None, B=1, T=64, H=2,
+          Dk=64, Dv=64, dtype=dr.DR_BF16):
+    return lib.delta_rule_chunk_bwd_ex(q, k, v, beta, g, S0, dout, dST, dq, dk, dv, dbeta, dg,
+                                       dS0, ws, wsb, B, T, H, Dk, Dv, flags, dtype, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(flags=2), dict(flags=0xffffffff),          # unknown flag bits
+    dict(ws=None), dict(wsb=16), dict(dq=P[0]),
+    dict(g=ctypes.c_void_p(0x100000 * 12)),          # gated without dg
+    dict(dtype=5),
+])
+def test_backward_ex_rejects_invalid(lib, kw):
+    assert _bwdx(lib, **kw) == dr.DR_ERR_INVALID_ARG
+
+
 def test_backward_rejects_unsupported_and_empty(lib):
     assert _bwd(lib, Dk=48) == dr.DR_ERR_UNSUPPORTED
     assert _bwd(lib, B=0) == dr.DR_OK

@@ -143,6 +143,40 @@ def test_backward_one_sequence_full_size_sampled_heads():
     _check(W.get("gated_layer_1p3b", B=1), heads=[(0, 3), (0, 12)])
 
 
+@pytest.mark.parametrize("name,B,T", [("layer_1p3b", 8, 512), ("gated_layer_1p3b", 8, 300),
+                                      ("layer_1p3b", 1, 1000), ("gated_layer_1p3b", 2, 130)])
+def test_backward_reuses_forward_checkpoints(name, B, T):
+    # the checkpointing forward (outputs and every chunk's incoming state in
+    # the backward's workspace), then the backward on those checkpoints:
+    # equal, bit for bit, to the forward at the backward's chunk and to the
+    # backward that forms the checkpoints itself (split walk at 128 (b, h),
+    # segmented recursion at 4, two-pass at 32)
+    w = W.get(name, B=B, T=T, seed=7480)
+    d = to_dev(W.generate(w))
+    do, dst = _upstream(w, 13)
+    do, dst = do.cuda(), dst.cuda()
+    g = d.get("g")
+    o, st, ws = dr.delta_rule_chunk_fwd_checkpointed(d["q"], d["k"], d["v"], d["beta"], d["S0"],
+                                                     g=g)
+    if g is None:
+        o2, st2 = dr.delta_rule_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["S0"], chunk=32,
+                                          workspace=False)
+        ref = dr.delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], do, d["S0"], dst)
+        got = dr.delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], do, d["S0"], dst,
+                                      workspace=ws, checkpoints_ready=True)
+    else:
+        o2, st2 = dr.gated_delta_rule_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], g, d["S0"],
+                                                chunk=32, workspace=False)
+        ref = dr.gated_delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], g, do, d["S0"],
+                                            dst)
+        got = dr.gated_delta_rule_chunk_bwd(d["q"], d["k"], d["v"], d["beta"], g, do, d["S0"],
+                                            dst, workspace=ws, checkpoints_ready=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(st, st2)
+    for n in ref:
+        assert torch.equal(ref[n], got[n]), n
+
+
 def test_backward_full_size_sampled_heads():
     # the benchmark's configuration and launch: B8 H16 T2048 d128, 64 chunks,
     # the split reverse walk (every head computed, two checked)
