@@ -144,6 +144,7 @@ struct alignas(16) KdaPipeBuf {
     __bf16 QT[KP_C * KDA_LD];        // q_t Gamma_t
     __bf16 KE[KP_C * KDA_LD];        // k_t exp(b_last - b_t)
     __bf16 Gb[1 * FRAG_ELEMS];       // G_10
+    __bf16 Gd[2 * FRAG_ELEMS];       // diag(beta_I) G_II (strictly lower)
     __bf16 Tb[2 * FRAG_ELEMS];       // -T_II diag(beta_I)
     __bf16 Pb[3 * FRAG_ELEMS];       // P_00, P_10, P_11
     float gamC[KDA_DK];              // Gamma_last
@@ -270,6 +271,20 @@ __global__ __launch_bounds__(512) void kda_pipe_kernel(
         else kp_prefetch_v(vr, sq, 0, g, vcol);
     }
 
+    // G_10 (G) or P_10 of a chunk from its level-16 operands into buffer b
+    auto level16 = [&](bool G, KdaPipeBuf &b) {
+        const __bf16 *rows = G ? sm.W[0] : sm.QR[0];
+        f32x4 a16 = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bf16x8 fc, fr;
+            frag_rows(sm.W[0], KDA_LD, 0, 32 * s, lane, fc);
+            frag_rows(rows, KDA_LD, 16, 32 * s, lane, fr);
+            mma_k32(a16, fc, fr);
+        }
+        if (G) store_fragblk(b.Gb, 0, lane, a16);
+        else store_fragblk(b.Pb, 1, lane, a16);
+    };
     for (int it = -1; it < nchunk; ++it) {
         const bool pw = prep && it + 1 < nchunk;   // prepare chunk it + 1
         const bool sw = !prep && it >= 0;          // state path of chunk it
@@ -340,6 +355,17 @@ __global__ __launch_bounds__(512) void kda_pipe_kernel(
             }
         }
         if (sw) {
+            // waves 4, 5: the inverse of diagonal block vt of this chunk (its
+            // G block was formed by the preparation waves one step earlier)
+            if (vt < 2) {
+                bf16x4 fg;
+                load_fragblk(bs.Gd, vt, lane, fg);
+                f32x4 a;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[e] = (float)fg[e];
+                const f32x4 b4 = *reinterpret_cast<const f32x4 *>(sm.beta + 16 * vt + 4 * g);
+                diag_inverse(a, b4, bs.Tb, vt, lane);
+            }
 #pragma unroll
             for (int s = 0; s < 4; ++s) cvt8(S[s][0], S[s][1], fS[s]);
 #pragma unroll
@@ -473,27 +499,18 @@ __global__ __launch_bounds__(512) void kda_pipe_kernel(
                 m[e] = r > j ? lv : 0.f;
             }
             if (wave < 2) {
-                const float br = sm.beta[16 * I + r];
-                const f32x4 b4 = *reinterpret_cast<const f32x4 *>(sm.beta + 16 * I + 4 * g);
-                diag_inverse(br * m, b4, bp.Tb, I, lane);
+                // inverted by state waves 4, 5 in the next step's first segment
+                store_fragblk(bp.Gd, I, lane, sm.beta[16 * I + r] * m);
             } else {
                 const float pd = sm.pdiag[16 * I + r];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) m[e] = r == 4 * g + e ? pd : m[e];
                 store_fragblk(bp.Pb, 2 * I, lane, m);
-                const __bf16 *rows = wave == 2 ? sm.W[0] : sm.QR[0];
-                f32x4 a16 = zero4();
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    bf16x8 fc, fr;
-                    frag_rows(sm.W[0], KDA_LD, 0, 32 * s, lane, fc);
-                    frag_rows(rows, KDA_LD, 16, 32 * s, lane, fr);
-                    mma_k32(a16, fc, fr);
-                }
-                if (wave == 2) store_fragblk(bp.Gb, 0, lane, a16);
-                else store_fragblk(bp.Pb, 1, lane, a16);
+                if (it < 0) level16(wave == 2, bp);  // chunk 0: no state path yet
             }
         }
+        // the level-16 block of the next chunk's G (wave 6) and P (wave 7)
+        if (!prep && it >= 0 && it + 1 < nchunk && vt >= 2) level16(vt == 2, bp);
         if (sw) {
             const bf16x8 fE32 = __builtin_shufflevector(fE[0], fE[1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
