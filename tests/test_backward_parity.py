@@ -177,6 +177,21 @@ def test_backward_reuses_forward_checkpoints(name, B, T):
         assert torch.equal(ref[n], got[n]), n
 
 
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("B,H,T", [
+    (8, 16, 256),    # split walk, 128 (b, h), its fewest chunks: 8 (pieces 2 + 6)
+    (5, 13, 257),    # split walk, 65 (b, h), 9 chunks, a one-token tail
+    (2, 16, 512),    # segmented recursion, 32 (b, h): 4 segments of 4 chunks
+    (1, 1, 4096),    # segmented recursion, one (b, h): 16 segments of 8 chunks
+    (2, 8, 480),     # 16 (b, h), 15 chunks: too few for 4 segments, two-pass
+])
+def test_backward_schedule_boundaries(gated, B, H, T):
+    w = W.get("layer_1p3b", B=B, H=H, T=T, Dk=64, Dv=64, gate_amax=4.0 if gated else 0.0,
+              beta_scale=2.0, s0_std=0.02, seed=7490 + T)
+    heads = None if B * H <= 2 else [(0, 0), (B // 2, H // 2), (B - 1, H - 1)]
+    _check(w, seed=17, heads=heads)
+
+
 def test_backward_full_size_sampled_heads():
     # the benchmark's configuration and launch: B8 H16 T2048 d128, 64 chunks,
     # the split reverse walk (every head computed, two checked)
