@@ -192,6 +192,54 @@ def test_backward_schedule_boundaries(gated, B, H, T):
     _check(w, seed=17, heads=heads)
 
 
+@pytest.mark.parametrize("dtype,T,gated", [("f32", 77, False), ("f32", 40, True),
+                                          ("bf16", 33, True), ("bf16", 1, False)])
+def test_checkpointed_forward_edge_cases(dtype, T, gated):
+    # fp32 (16-token chunks) and bf16, ragged and one-token sequences, S_T
+    # carried in place over S0: outputs equal the chunked forward at the
+    # backward's chunk, and the backward on the kept checkpoints equals the
+    # one that forms them (and the oracle)
+    w = W.get("layer_1p3b", B=2, H=3, T=T, Dk=32, Dv=64, dtype=dtype,
+              gate_amax=4.0 if gated else 0.0, s0_std=0.02, seed=7510 + T)
+    d = to_dev(W.generate(w))
+    do, dst = _upstream(w, 21)
+    do, dst = do.cuda(), dst.cuda()
+    g = d.get("g")
+    c = 16 if dtype == "f32" else 32
+    S0 = d["S0"].clone()
+    carry = d["S0"].clone()
+    o, st, ws = dr.delta_rule_chunk_fwd_checkpointed(d["q"], d["k"], d["v"], d["beta"], carry,
+                                                     g=g, S_T=carry)
+    assert st.data_ptr() == carry.data_ptr()
+    fwd = dr.delta_rule_chunk_fwd if g is None else \
+        (lambda *a, **kw: dr.gated_delta_rule_chunk_fwd(*a[:4], g, *a[4:], **kw))
+    o2, st2 = fwd(d["q"], d["k"], d["v"], d["beta"], S0, chunk=c, workspace=False)
+    bwd = dr.delta_rule_chunk_bwd if g is None else \
+        (lambda *a, **kw: dr.gated_delta_rule_chunk_bwd(*a[:4], g, *a[4:], **kw))
+    ref = bwd(d["q"], d["k"], d["v"], d["beta"], do, S0, dst)
+    got = bwd(d["q"], d["k"], d["v"], d["beta"], do, S0, dst, workspace=ws,
+              checkpoints_ready=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(st, st2)
+    for n in ref:
+        assert torch.equal(ref[n], got[n]), n
+
+
+def test_checkpointed_forward_without_final_state_and_empty():
+    w = W.get("layer_1p3b", B=1, H=2, T=64, Dk=64, Dv=64, seed=7520)
+    d = to_dev(W.generate(w))
+    o, st, ws = dr.delta_rule_chunk_fwd_checkpointed(d["q"], d["k"], d["v"], d["beta"],
+                                                     output_final_state=False)
+    o2, _ = dr.delta_rule_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], chunk=32,
+                                    workspace=False)
+    assert st is None and torch.equal(o, o2)
+    e = W.get("layer_1p3b", B=1, H=2, T=0, Dk=64, Dv=64, seed=7521)
+    de = to_dev(W.generate(e))
+    S0 = torch.randn(1, 2, 64, 64, device="cuda")
+    o, st, ws = dr.delta_rule_chunk_fwd_checkpointed(de["q"], de["k"], de["v"], de["beta"], S0)
+    assert o.shape == (1, 0, 2, 64) and torch.equal(st, S0)
+
+
 def test_backward_full_size_sampled_heads():
     # the benchmark's configuration and launch: B8 H16 T2048 d128, 64 chunks,
     # the split reverse walk (every head computed, two checked)
