@@ -81,3 +81,20 @@ def gather_heads(o_gpu, st_gpu, heads):
 
 def to_dev(x, device="cuda"):
     return {n: (None if t is None else t.to(device)) for n, t in x.items()}
+
+
+def grad_errors(got: dict, ref: dict) -> dict:
+    """Relative errors of the backward's gradients, each against max |ref| of
+    that gradient, except dg: the gate gradient of a token is a difference of
+    products of the chunk's operands (the same products whose row sums make
+    dbeta), so where the gates have decayed everything it cancels to a value
+    far below those products and their fp32 rounding.  Its error is measured
+    against max(max |dg|, max |dbeta|)."""
+    errs = {n: rel_err(to_np(got[n]), ref[n]) for n in ref}
+    if "dg" in ref:
+        scale = max(float(np.max(np.abs(ref["dg"]))) if ref["dg"].size else 0.0,
+                    float(np.max(np.abs(ref["dbeta"]))) if ref["dbeta"].size else 0.0)
+        diff = np.abs(to_np(got["dg"]) - np.asarray(ref["dg"], dtype=np.float64))
+        errs["dg"] = float(np.max(diff) / scale) if diff.size and scale > 0 else errs["dg"]
+    return errs
+
