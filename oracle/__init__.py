@@ -22,6 +22,8 @@ Contents
     Gradients with respect to q, k, v, beta, S0 (and g for the gated rule)
     by the chain rule through the recurrence in reverse token order, in fp64
     (C, ``ref_delta_rule_bwd.c``).
+``kda_bwd_ref``
+    The same gradients for the per-key-channel decay, with dgk.
 ``l2norm_rows``
     x / sqrt(sum x^2 + eps) along the last axis in fp64: the in-kernel
     normalisation option applied to q and k before either oracle.
@@ -79,6 +81,8 @@ def _load():
                                 i64, i64, i64, i64, i64, ctypes.c_int]
     lib.ref_delta_rule_bwd_f64.restype = ctypes.c_int
     lib.ref_delta_rule_bwd_f64.argtypes = [dp] * 14 + [i64, i64, i64, i64, i64, ctypes.c_int]
+    lib.ref_kda_bwd_f64.restype = ctypes.c_int
+    lib.ref_kda_bwd_f64.argtypes = [dp] * 14 + [i64, i64, i64, i64, i64, ctypes.c_int]
     lib.ref_gated_delta_rule_f64.restype = ctypes.c_int
     lib.ref_gated_delta_rule_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp,
                                              i64, i64, i64, i64, i64, ctypes.c_int]
@@ -211,6 +215,36 @@ def delta_rule_bwd_ref(q, k, v, beta, do, S0=None, dS_T=None, g=None, nthreads: 
     return out
 
 
+def kda_bwd_ref(q, k, v, beta, gk, do, S0=None, dS_T=None, nthreads: int = 1):
+    """Gradients of L = sum <do, o> + <dS_T, S_T> through the per-channel-decay
+    recurrence of ``kda_ref`` in fp64 on the CPU (``ref_delta_rule_bwd.c``,
+    ``ref_kda_bwd_f64``).  gk is ``[B,T,H,Dk]``; the rest as
+    ``delta_rule_bwd_ref``.  Returns a dict with dq, dk, dv, dbeta, dgk
+    ([B,T,H,Dk]) and dS0."""
+    q, k, v, beta, s0, (B, T, H, Dk, Dv) = _check(q, k, v, beta, S0)
+    gk = _as_f64(gk)
+    if gk.shape != (B, T, H, Dk):
+        raise ValueError(f"gk must be [B,T,H,Dk]={B, T, H, Dk}, got {gk.shape}")
+    do = _as_f64(do)
+    if do.shape != (B, T, H, Dv):
+        raise ValueError(f"do must be [B,T,H,Dv]={B, T, H, Dv}, got {do.shape}")
+    dst = None
+    if dS_T is not None:
+        dst = _as_f64(dS_T)
+        if dst.shape != (B, H, Dv, Dk):
+            raise ValueError(f"dS_T must be [B,H,Dv,Dk]={B, H, Dv, Dk}, got {dst.shape}")
+    out = {"dq": np.zeros((B, T, H, Dk)), "dk": np.zeros((B, T, H, Dk)),
+           "dv": np.zeros((B, T, H, Dv)), "dbeta": np.zeros((B, T, H)),
+           "dgk": np.zeros((B, T, H, Dk)), "dS0": np.zeros((B, H, Dv, Dk))}
+    rc = _load().ref_kda_bwd_f64(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gk), _ptr(s0), _ptr(do), _ptr(dst),
+        _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
+        _ptr(out["dgk"]), _ptr(out["dS0"]), B, T, H, Dk, Dv, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle failed with code {rc}")
+    return out
+
+
 def l2norm_rows(x, eps: float = 1e-6):
     """Each row (last axis) of x divided by sqrt(sum of its squares + eps),
     in fp64: the l2norm helper of the gated layer on houmin.site
@@ -221,4 +255,4 @@ def l2norm_rows(x, eps: float = 1e-6):
 
 
 __all__ = ["build", "delta_rule_ref", "gated_delta_rule_ref", "kda_ref", "delta_rule_bwd_ref",
-           "l2norm_rows"]
+           "kda_bwd_ref", "l2norm_rows"]

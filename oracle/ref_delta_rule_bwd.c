@@ -27,7 +27,18 @@
  *   dg_t     = <dP, P_t>                        P_t = exp(g_t) S_{t-1}
  *   D       <- a_t dP                           gradient with respect to S_{t-1}
  *
- * and finally dS0 = D.  These are derived here from the update as the pages
+ * and finally dS0 = D.
+ *
+ * Per-channel decay (ref_kda_bwd_f64, Kimi Delta Attention): gk_t [d_k]
+ * scales column j of the state by a_t[j] = exp(gk_t[j]) (hada.io digest,
+ * section "Kimi Delta Attention : attenuation par canal": the decay S_{t-1}
+ * D_t with D_t = Diag(alpha_t) comes before the prediction), so
+ *
+ *   P_t     = S_{t-1} Diag(a_t)
+ *   dgk_t[j] = sum_i dP_ij (P_t)_ij             column j of <dP, P_t>
+ *   D       <- dP Diag(a_t)
+ *
+ * and every other line above is unchanged.  These are derived here from the update as the pages
  * state it (the pages give the strategy of recomputing states in the
  * backward -- paperlayer summary of arXiv:2406.06484, section 3 -- but not
  * the equations); the tests pin them with central finite differences and
@@ -48,8 +59,8 @@
 #include <string.h>
 
 typedef struct {
-    const double *q, *k, *v, *beta, *g, *S0, *dout, *dST;
-    double *dq, *dk, *dv, *dbeta, *dg, *dS0;
+    const double *q, *k, *v, *beta, *g, *gk, *S0, *dout, *dST;
+    double *dq, *dk, *dv, *dbeta, *dg, *dgk, *dS0;
     int64_t B, T, H, Dk, Dv;
     int64_t next;
     int failed;
@@ -61,6 +72,15 @@ typedef struct {
     double *D;   /* Dv x Dk */
     double *u, *w;
 } bwd_scratch;
+
+/* Decay of element (i, j) of the state before token `row`: exp(g) for the
+ * gated rule, exp(gk[j]) per key channel, 1 for the plain rule. */
+static double decay(const bwd_job *J, int64_t row, int64_t j)
+{
+    if (J->gk)
+        return exp(J->gk[row * J->Dk + j]);
+    return J->g ? exp(J->g[row]) : 1.0;
+}
 
 static void one_head_bwd(const bwd_job *J, int64_t b, int64_t h, bwd_scratch *W)
 {
@@ -77,11 +97,11 @@ static void one_head_bwd(const bwd_job *J, int64_t b, int64_t h, bwd_scratch *W)
         const int64_t row = (b * T + t) * H + h;
         const double *kt = J->k + row * Dk, *vt = J->v + row * Dv;
         const double bt = J->beta[row];
-        const double at = J->g ? exp(J->g[row]) : 1.0;
         const double *Sp = S + t * M;
         double *Sn = S + (t + 1) * M;
-        for (int64_t i = 0; i < M; ++i)
-            P[i] = at * Sp[i];
+        for (int64_t i = 0; i < Dv; ++i)
+            for (int64_t j = 0; j < Dk; ++j)
+                P[i * Dk + j] = decay(J, row, j) * Sp[i * Dk + j];
         for (int64_t i = 0; i < Dv; ++i) {
             double p = 0.0;
             for (int64_t j = 0; j < Dk; ++j)
@@ -103,7 +123,6 @@ static void one_head_bwd(const bwd_job *J, int64_t b, int64_t h, bwd_scratch *W)
         const double *qt = J->q + row * Dk, *kt = J->k + row * Dk, *vt = J->v + row * Dv;
         const double *dot = J->dout + row * Dv;
         const double bt = J->beta[row];
-        const double at = J->g ? exp(J->g[row]) : 1.0;
         const double *Sp = S + t * M, *Sn = S + (t + 1) * M;
         double *dqt = J->dq + row * Dk, *dkt = J->dk + row * Dk, *dvt = J->dv + row * Dv;
 
@@ -118,8 +137,9 @@ static void one_head_bwd(const bwd_job *J, int64_t b, int64_t h, bwd_scratch *W)
             dqt[j] = acc;
         }
         /* recompute P_t and u_t */
-        for (int64_t i = 0; i < M; ++i)
-            P[i] = at * Sp[i];
+        for (int64_t i = 0; i < Dv; ++i)
+            for (int64_t j = 0; j < Dk; ++j)
+                P[i * Dk + j] = decay(J, row, j) * Sp[i * Dk + j];
         for (int64_t i = 0; i < Dv; ++i) {
             double p = 0.0;
             for (int64_t j = 0; j < Dk; ++j)
@@ -157,8 +177,17 @@ static void one_head_bwd(const bwd_job *J, int64_t b, int64_t h, bwd_scratch *W)
                 acc += D[i] * P[i];
             J->dg[row] = acc;
         }
-        for (int64_t i = 0; i < M; ++i)
-            D[i] = at * D[i];
+        if (J->gk && J->dgk) {
+            for (int64_t j = 0; j < Dk; ++j) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < Dv; ++i)
+                    acc += D[i * Dk + j] * P[i * Dk + j];
+                J->dgk[row * Dk + j] = acc;
+            }
+        }
+        for (int64_t i = 0; i < Dv; ++i)
+            for (int64_t j = 0; j < Dk; ++j)
+                D[i * Dk + j] = decay(J, row, j) * D[i * Dk + j];
     }
     memcpy(J->dS0 + sh, D, (size_t)M * sizeof(double));
 }
@@ -191,6 +220,30 @@ static void *bwd_worker(void *arg)
     return NULL;
 }
 
+static int run_bwd(bwd_job *J, int nthreads)
+{
+    if (J->B * J->H == 0)
+        return 0;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > J->B * J->H)
+        nthreads = (int)(J->B * J->H);
+    pthread_t *tid = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!tid)
+        return -2;
+    int started = 0;
+    for (int i = 1; i < nthreads; ++i) {
+        if (pthread_create(&tid[i], NULL, bwd_worker, J) != 0)
+            break;
+        ++started;
+    }
+    bwd_worker(J);
+    for (int i = 1; i <= started; ++i)
+        pthread_join(tid[i], NULL);
+    free(tid);
+    return J->failed ? -2 : 0;
+}
+
 /*
  * Gradients of L = sum_t <do_t, o_t> + <dS_T, S_T> with respect to q, k, v,
  * beta, g (gated rule only) and S0.  Threads split (b,h) pairs only; the
@@ -206,26 +259,24 @@ int ref_delta_rule_bwd_f64(const double *q, const double *k, const double *v,
     if (!q || !k || !v || !beta || !dout || !dq || !dk || !dv || !dbeta || !dS0 || B < 0 ||
         T < 0 || H < 0 || Dk < 1 || Dv < 1)
         return -1;
-    if (B * H == 0)
-        return 0;
-    if (nthreads < 1)
-        nthreads = 1;
-    if (nthreads > B * H)
-        nthreads = (int)(B * H);
-    bwd_job J = {q,  k,  v,     beta, g,   S0, dout, dST, dq, dk, dv,
-                 dbeta, dg, dS0, B, T, H, Dk, Dv, 0, 0};
-    pthread_t *tid = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
-    if (!tid)
-        return -2;
-    int started = 0;
-    for (int i = 1; i < nthreads; ++i) {
-        if (pthread_create(&tid[i], NULL, bwd_worker, &J) != 0)
-            break;
-        ++started;
-    }
-    bwd_worker(&J);
-    for (int i = 1; i <= started; ++i)
-        pthread_join(tid[i], NULL);
-    free(tid);
-    return J.failed ? -2 : 0;
+    bwd_job J = {q,  k,  v,     beta, g,    NULL, S0, dout, dST, dq, dk, dv,
+                 dbeta, dg, NULL, dS0, B, T, H, Dk, Dv, 0, 0};
+    return run_bwd(&J, nthreads);
+}
+
+/*
+ * The same gradients for the per-key-channel decay (gk [B,T,H,Dk] in, dgk
+ * [B,T,H,Dk] out).  Same return codes.
+ */
+int ref_kda_bwd_f64(const double *q, const double *k, const double *v, const double *beta,
+                    const double *gk, const double *S0, const double *dout, const double *dST,
+                    double *dq, double *dk, double *dv, double *dbeta, double *dgk, double *dS0,
+                    int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int nthreads)
+{
+    if (!q || !k || !v || !beta || !gk || !dout || !dq || !dk || !dv || !dbeta || !dgk ||
+        !dS0 || B < 0 || T < 0 || H < 0 || Dk < 1 || Dv < 1)
+        return -1;
+    bwd_job J = {q,  k,  v,     beta, NULL, gk, S0, dout, dST, dq, dk, dv,
+                 dbeta, NULL, dgk, dS0, B, T, H, Dk, Dv, 0, 0};
+    return run_bwd(&J, nthreads);
 }
