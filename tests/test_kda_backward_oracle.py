@@ -138,8 +138,8 @@ def test_erased_channel_blocks_the_state_gradient():
     x2["gk"][:, 3, :, 2] = -1e4
     g2 = _bwd(x2, up)
     assert np.any(g2["dS0"][..., 2] != 0)
-    # cutting at the erasing token: tokens 0..2 alone with dS_T's column 2
-    # zeroed, and the rest fed back, give the same dS0 column
+    # the tokens from 3 on, run alone from the state after token 2, give that
+    # incoming state's column 2 no gradient
     x3 = {n: (a if n == "S0" else a[:, :3]) for n, a in x2.items()}
     _, s_mid = kda_ref(x3["q"], x3["k"], x3["v"], x3["beta"], x3["gk"], x3["S0"])
     x4 = {n: (s_mid if n == "S0" else a[:, 3:]) for n, a in x2.items()}
