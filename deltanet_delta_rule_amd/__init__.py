@@ -37,6 +37,8 @@ __all__ = [
     "DeltaRuleScratchError",
     "kda_recurrent_step",
     "kda_fwd",
+    "kda_bwd",
+    "kda_bwd_workspace_bytes",
     "DR_FUSED_RECURRENT",
     "chunk_fwd_workspace_bytes",
     "delta_rule_status_string",
@@ -130,6 +132,11 @@ def load_library():
     lib.delta_rule_chunk_bwd_ex.restype = i32
     lib.delta_rule_chunk_bwd_ex.argtypes = [vp] * 15 + [ctypes.c_size_t, i64, i64, i64, i64, i64,
                                                         ctypes.c_uint32, i32, vp]
+    lib.kda_bwd_workspace_bytes.restype = i64
+    lib.kda_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64]
+    lib.kda_bwd.restype = i32
+    lib.kda_bwd.argtypes = [vp] * 15 + [i64, ctypes.c_float, vp, ctypes.c_size_t,
+                                        i64, i64, i64, i64, i64, i32, vp]
     lib.delta_rule_status_string.restype = ctypes.c_char_p
     lib.delta_rule_status_string.argtypes = [i32]
     lib.delta_rule_last_hip_error.restype = i32
@@ -549,6 +556,78 @@ def _bwd_call(q, k, v, beta, g, do, S0, dS_T, workspace, need_dS0, stream,
             _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
             _ptr(out["dg"]), _ptr(out["dS0"]), _ptr(workspace), nws, B, T, H, Dk, Dv, code,
             _stream(dev, stream))
+    _check(st)
+    return out
+
+
+def kda_bwd_workspace_bytes(B, T, H, Dk, Dv, num_seqs=None):
+    """Bytes of device workspace ``kda_bwd`` needs (``num_seqs``: the number
+    of packed sequences, or None for B sequences of T tokens)."""
+    n = B if num_seqs is None else num_seqs
+    return int(load_library().kda_bwd_workspace_bytes(B, T, H, Dk, Dv, n))
+
+
+def kda_bwd(q, k, v, beta, gk, do, S0=None, dS_T=None, *, scale=None, cu_seqlens=None,
+            workspace=None, need_dS0=True, stream=None):
+    """Gradients of ``kda_fwd`` (without the in-kernel L2 norm) for upstream
+    gradients ``do`` ``[B,T,H,Dv]`` (dtype of q) and ``dS_T`` float32 or
+    None, for any log decay gk, erased channels included (``kda_bwd``).
+    ``scale`` and ``cu_seqlens`` as in the forward.  Returns a dict with dq,
+    dk, dv, dbeta (dtype of q), dgk (float32 ``[B,T,H,Dk]``) and dS0 (float32,
+    or None when ``need_dS0`` is False).  ``workspace``: a uint8 GPU tensor of
+    at least ``kda_bwd_workspace_bytes`` bytes, allocated when None.  With
+    ``cu_seqlens``, tokens outside every sequence get zero gradients."""
+    torch = _torch()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("the backward needs GPU tensors")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    code = _dtype_code(q)
+    _need(q, "q", (B, T, H, Dk), dt, dev)
+    _need(k, "k", (B, T, H, Dk), dt, dev)
+    _need(v, "v", (B, T, H, Dv), dt, dev)
+    _need(beta, "beta", (B, T, H), dt, dev)
+    _need(gk, "gk", (B, T, H, Dk), torch.float32, dev)
+    _need(do, "do", (B, T, H, Dv), dt, dev)
+    nseq = B
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError("packed sequences (cu_seqlens) need a batch of 1")
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+            raise ValueError("cu_seqlens must be a 1-D tensor of num_seqs + 1 offsets")
+        if cu_seqlens.dtype != torch.int32:
+            cu_seqlens = cu_seqlens.to(torch.int32)
+        nseq = cu_seqlens.numel() - 1
+        _need(cu_seqlens, "cu_seqlens", (nseq + 1,), torch.int32, dev)
+    if S0 is not None:
+        _need(S0, "S0", (nseq, H, Dv, Dk), torch.float32, dev)
+    if dS_T is not None:
+        _need(dS_T, "dS_T", (nseq, H, Dv, Dk), torch.float32, dev)
+    lib = load_library()
+    nbytes = int(lib.kda_bwd_workspace_bytes(B, T, H, Dk, Dv, nseq))
+    if nbytes < 0:
+        raise NotImplementedError(f"kda_bwd does not support Dk={Dk}, Dv={Dv}")
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace must be a GPU tensor of at least {nbytes} bytes")
+    alloc = torch.zeros if cu_seqlens is not None else torch.empty
+    out = {"dq": alloc(q.shape, dtype=dt, device=dev), "dk": alloc(k.shape, dtype=dt, device=dev),
+           "dv": alloc(v.shape, dtype=dt, device=dev),
+           "dbeta": alloc(beta.shape, dtype=dt, device=dev),
+           "dgk": alloc(gk.shape, dtype=torch.float32, device=dev),
+           "dS0": torch.empty((nseq, H, Dv, Dk), dtype=torch.float32, device=dev)
+           if need_dS0 else None}
+    st = lib.kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gk), _ptr(S0), _ptr(do),
+                     _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                     _ptr(out["dbeta"]), _ptr(out["dgk"]), _ptr(out["dS0"]),
+                     None if cu_seqlens is None else ctypes.c_void_p(cu_seqlens.data_ptr()),
+                     nseq if cu_seqlens is not None else 0,
+                     1.0 if scale is None else float(scale), _ptr(workspace),
+                     workspace.numel() * workspace.element_size(), B, T, H, Dk, Dv, code,
+                     _stream(dev, stream))
     _check(st)
     return out
 

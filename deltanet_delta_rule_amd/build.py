@@ -20,7 +20,7 @@ OBJDIR = os.path.join(PKG, "_build")
 
 SOURCES = ["abi.cpp", "chunk_fwd.hip", "chunk_fwd_gated.hip", "chunk_fwd_l2.hip",
            "chunk_fwd_gated_l2.hip", "chunk_bwd.hip", "recurrent_step.hip",
-           "fused_recurrent.hip", "kda_chunk.hip", "segment.hip"]
+           "fused_recurrent.hip", "kda_chunk.hip", "segment.hip", "kda_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -287,6 +287,62 @@ dr_status chunk_bwd(const void *q, const void *k, const void *v, const void *bet
     return hip_status(dr::launch_chunk_bwd(a, bf16, st));
 }
 
+// Validation and dispatch of the token-serial backward of the per-channel
+// decay rule (packed sequences as in chunk_fwd).
+dr_status kda_bwd_impl(const void *q, const void *k, const void *v, const void *beta,
+                       const float *gk, const float *S0, const void *dout, const float *dS_T,
+                       void *dq, void *dk, void *dv, void *dbeta, float *dgk, float *dS0,
+                       const int32_t *cu, int64_t nseq, float scale, void *ws, size_t ws_bytes,
+                       int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, dr_dtype dtype,
+                       void *stream) {
+    if (dtype != DR_F32 && dtype != DR_BF16) return DR_ERR_INVALID_ARG;
+    if (B < 0 || T < 0 || H < 0 || Dk < 0 || Dv < 0) return DR_ERR_INVALID_ARG;
+    if (cu && (B != 1 || nseq < 0 || !aligned_to(cu, 4))) return DR_ERR_INVALID_ARG;
+    if (!(scale == scale) || scale - scale != 0.f) return DR_ERR_INVALID_ARG;  // NaN or inf
+    if (!supported_dim(Dk) || !supported_dim(Dv)) return DR_ERR_UNSUPPORTED;
+    const int64_t ns_count = cu ? nseq : B;
+    if (ns_count == 0 || H == 0) return DR_OK;
+    const bool bf16 = dtype == DR_BF16;
+    const int64_t esz = bf16 ? 2 : 4;
+    const int64_t nqk = mul_checked({B, T, H, Dk}), nv = mul_checked({B, T, H, Dv});
+    const int64_t nb = mul_checked({B, T, H}), ns = mul_checked({ns_count, H, Dv, Dk});
+    const int64_t ntok = mul_checked({B, T});
+    if (nqk < 0 || nv < 0 || nb < 0 || ns < 0 || ntok < 0) return DR_ERR_UNSUPPORTED;
+    const int64_t need = dr::kda_bwd_workspace_bytes(ntok, ns_count, H, (int)Dk, (int)Dv);
+    if (need < 0) return DR_ERR_UNSUPPORTED;
+    // grid = sequences * H * row tiles (at most Dv / 16) and token offsets in 32 bits
+    if (T > INT32_MAX || H > INT32_MAX || mul_checked({ns_count, H, Dv / 16}) > INT32_MAX ||
+        mul_checked({ns_count, 2048}) > INT32_MAX)
+        return DR_ERR_UNSUPPORTED;
+    if (T > 0 && (!q || !k || !v || !beta || !gk || !dout || !dq || !dk || !dv || !dbeta ||
+                  !dgk))
+        return DR_ERR_INVALID_ARG;
+    if (T > 0 && (!ws || (int64_t)ws_bytes < need)) return DR_ERR_INVALID_ARG;
+    if (T == 0) ws = nullptr;
+    const void *vec_ptrs[] = {q, k, gk, S0, dS_T, dS0, dgk, ws};
+    for (const void *p : vec_ptrs)
+        if (p && !aligned16(p)) return DR_ERR_INVALID_ARG;
+    const void *elem_ptrs[] = {v, beta, dout, dq, dk, dv, dbeta};
+    for (const void *p : elem_ptrs)
+        if (p && !aligned_to(p, esz)) return DR_ERR_INVALID_ARG;
+    const Span in[] = {{q, nqk * esz},    {k, nqk * esz},   {v, nv * esz},
+                       {beta, nb * esz},  {gk, nqk * 4},    {S0, ns * 4},
+                       {dout, nv * esz},  {dS_T, ns * 4},   {cu, cu ? (nseq + 1) * 4 : 0}};
+    const Span out[] = {{dq, nqk * esz},   {dk, nqk * esz}, {dv, nv * esz},
+                        {dbeta, nb * esz}, {dgk, nqk * 4},  {dS0, ns * 4},
+                        {ws, ws ? need : 0}};
+    for (const Span &o : out) {
+        for (const Span &s : in)
+            if (overlaps(o, s)) return DR_ERR_INVALID_ARG;
+        for (const Span &o2 : out)
+            if (&o2 != &o && overlaps(o, o2)) return DR_ERR_INVALID_ARG;
+    }
+    dr::KdaBwdArgs a{q,   k,    v,     beta, gk,       S0,      dout,    dS_T,
+                     dq,  dk,   dv,    dbeta, dgk,     dS0,     ws,      cu,
+                     ns_count, T, H,   (int)Dk, (int)Dv, scale};
+    return hip_status(dr::launch_kda_bwd(a, bf16, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -451,6 +507,27 @@ dr_status delta_rule_chunk_bwd_ex(const void *q, const void *k, const void *v, c
                      (flags & DR_BWD_CHECKPOINTS_READY) != 0);
 }
 
+int64_t kda_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                int64_t num_seqs) {
+    if (B < 0 || T < 0 || H < 0 || num_seqs < 0) return -1;
+    if (!supported_dim(Dk) || !supported_dim(Dv)) return -1;
+    const int64_t ntok = mul_checked({B, T});
+    if (ntok < 0 || mul_checked({ntok + num_seqs, H, Dv, Dk, 16}) < 0) return -1;
+    return dr::kda_bwd_workspace_bytes(ntok, num_seqs, H, (int)Dk, (int)Dv);
+}
+
+dr_status kda_bwd(const void *q, const void *k, const void *v, const void *beta,
+                  const float *gk, const float *S0, const void *dout, const float *dS_T,
+                  void *dq, void *dk, void *dv, void *dbeta, float *dgk, float *dS0,
+                  const int32_t *cu_seqlens, int64_t num_seqs, float scale, void *workspace,
+                  size_t workspace_bytes, int64_t B, int64_t T, int64_t H, int64_t Dk,
+                  int64_t Dv, dr_dtype dtype, void *stream) {
+    if (!valid_dtype(dtype)) return DR_ERR_INVALID_ARG;
+    return kda_bwd_impl(q, k, v, beta, gk, S0, dout, dS_T, dq, dk, dv, dbeta, dgk, dS0,
+                        cu_seqlens, num_seqs, scale, workspace, workspace_bytes, B, T, H, Dk,
+                        Dv, dtype, stream);
+}
+
 const char *delta_rule_status_string(dr_status status) {
     switch (raw_enum(status)) {
     case DR_OK: return "DR_OK";
@@ -466,6 +543,6 @@ const char *delta_rule_status_string(dr_status status) {
 
 int delta_rule_last_hip_error(void) { return g_last_hip_error; }
 
-int delta_rule_version(void) { return 21300; }
+int delta_rule_version(void) { return 21400; }
 
 }  // extern "C"

@@ -106,6 +106,28 @@ struct BwdSegPlan {
 BwdSegPlan bwd_seg_plan(int64_t B, int64_t H, int64_t N);
 int64_t bwd_seg_bytes(int64_t B, int64_t H, int64_t N, int64_t Dk, int64_t Dv);
 
+// Arguments of the token-serial backward of the per-key-channel decay rule.
+// Without cu the nseq = B sequences are T tokens each; with cu, nseq packed
+// sequences share one row of T tokens.  ws holds kda_bwd_workspace_bytes.
+struct KdaBwdArgs {
+    const void *q, *k, *v, *beta;
+    const float *gk, *S0;
+    const void *dout;
+    const float *dS_T;
+    void *dq, *dk, *dv, *dbeta;
+    float *dgk, *dS0;
+    void *ws;
+    const int *cu;
+    int64_t nseq, T, H;
+    int Dk, Dv;
+    float scale;
+};
+
+hipError_t launch_kda_bwd(const KdaBwdArgs &a, bool bf16, hipStream_t stream);
+// Workspace bytes for ntok tokens in total (B*T, or T when packed) in nseq
+// sequences; -1 for an unsupported d_k.
+int64_t kda_bwd_workspace_bytes(int64_t ntok, int64_t nseq, int64_t H, int Dk, int Dv);
+
 // Arguments of the single-token decode step (state updated in place).  g is
 // the log forget gate [B,H] (fp32) of the gated rule, or nullptr; scale
 // multiplies the outputs; l2 normalises q and k in the kernel; gk, when set

@@ -1,0 +1,581 @@
+// Backward of the per-key-channel decay rule (Kimi Delta Attention), token
+// by token, exact for any log decay gk <= 0 (a channel erased in one token
+// included).
+//
+// The forward (hada.io digest, section "Kimi Delta Attention : attenuation
+// par canal": decay the state's key columns, predict, correct, write, read),
+// per (sequence, head) with a_t[j] = exp(gk_t[j]):
+//
+//   P_t = S_{t-1} Diag(a_t);  e_t = v_t - P_t k_t;  S_t = P_t + beta_t e_t k_t^T;
+//   o_t = scale S_t q_t.
+//
+// Its gradients, token by token in reverse with D = dL/dS_t (dS_T at the end):
+//
+//   D += scale do_t q_t^T;     dq_t = scale S_t^T do_t;     w = D k_t;
+//   dv_t = beta_t w;           dbeta_t = e_t . w;
+//   dk_t = beta_t (D^T e_t - P_t^T w);
+//   D -= beta_t w k_t^T;       dgk_t[j] = sum_i D_ij (P_t)_ij;    D <- D Diag(a_t)
+//
+// and dS0 = D.  The pages give the strategy of recomputing states in the
+// backward (paper summary of "Parallelizing Linear Transformers with the Delta
+// Rule over Sequence Length", section 3) and these equations follow from the
+// chain rule through one token.
+//
+// Work split.  Row i of the state depends only on row i before it, in both
+// directions, so a workgroup owns RW rows of one (sequence, head) state and
+// needs no other workgroup: LPR = d_k / 8 lanes per row, each holding 8
+// consecutive columns (as the token-serial forward).  Only dq, dk, dgk and
+// dbeta are sums over all rows: each workgroup adds up its own rows' terms
+// (lane swaps inside a wave, then across its waves in LDS, two tokens per
+// barrier) and writes one partial per row tile to the workspace; a second
+// kernel adds the tiles' partials and converts them.
+//
+// Phases of the main kernel:
+//   1. the forward over the sequence, storing the state at the start of every
+//      16-token block to the workspace (each lane its own 8 values, read back
+//      by the same lane);
+//   2. blocks last to first: the block's starting state reloaded, its tokens
+//      recomputed forward with every pre-token state S_{t-1} kept in
+//      registers, then walked in reverse.
+// The inputs of a block (k, q, exp(gk), the workgroup's rows of v and do,
+// beta) are staged in LDS in fp32 and double-buffered: the next block's
+// global loads are in flight while the current one is processed.
+#include <algorithm>
+
+#include "dr_common.hpp"
+#include "dr_launch.hpp"
+
+namespace dr {
+
+namespace {
+
+// Lanes per workgroup: 128 rows of d_k / 8 lanes, at most 512.
+template <int DK>
+struct KbLanes {
+    static constexpr int value = DK / 8 * 128 < 512 ? DK / 8 * 128 : 512;
+};
+
+template <typename DT, int DK>
+struct KbCfg {
+    static constexpr int ESZ = sizeof(DT);
+    static constexpr int LPR = DK / 8;                          // lanes per state row
+    static constexpr int NTH = KbLanes<DK>::value;
+    static constexpr int RW = NTH / LPR;                        // state rows per workgroup
+    static constexpr int NWV = NTH / 64;
+    static constexpr int TB = 16;                               // tokens per block
+    static constexpr int G = 2;                                 // tokens per cross-wave sum
+    static constexpr int NRED = 3 * DK + 4;                     // dq, dk, dgk, dbeta (+ pad)
+    static constexpr int VPR = DK * ESZ / 16;                   // 16-byte vectors per k row
+    static constexpr int KV = TB * VPR;
+    static constexpr int GV = TB * DK / 4;                      // float4 of gk per block
+    static constexpr int NK = (KV + NTH - 1) / NTH;
+    static constexpr int NG = (GV + NTH - 1) / NTH;
+    static constexpr int NV = (TB * RW + NTH - 1) / NTH;
+    // byte offsets in one staging buffer (all fp32)
+    static constexpr int OFF_K = 0;
+    static constexpr int OFF_Q = TB * DK * 4;
+    static constexpr int OFF_A = 2 * TB * DK * 4;
+    static constexpr int OFF_V = 3 * TB * DK * 4;
+    static constexpr int OFF_D = OFF_V + TB * RW * 4;
+    static constexpr int OFF_B = OFF_D + TB * RW * 4;
+    static constexpr int BUF = OFF_B + TB * 4;
+    static constexpr int RED = 2 * G * NWV * NRED;              // floats, two parities
+};
+
+template <typename DT, int DK>
+struct KbStage {
+    typedef KbCfg<DT, DK> C;
+    uint4 k[C::NK], q[C::NK];
+    float4 g[C::NG];
+    DT v[C::NV], d[C::NV];
+    DT b;
+};
+
+// Token row of one (sequence, head): token t is row (base + t) * H + h of the
+// [*, H, d] arrays.
+struct KbRows {
+    int64_t base, H, h;
+    __device__ __forceinline__ int64_t row(int t) const { return (base + t) * H + h; }
+};
+
+template <typename DT, int DK>
+__device__ __forceinline__ void kb_load(KbStage<DT, DK> &st, const DT *__restrict__ q,
+                                        const DT *__restrict__ k, const DT *__restrict__ v,
+                                        const DT *__restrict__ beta, const float *__restrict__ gk,
+                                        const DT *__restrict__ dout, const KbRows &sr, int t0,
+                                        int nt, int row0, int Dv, bool want_qd) {
+    typedef KbCfg<DT, DK> C;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int n = 0; n < C::NK; ++n) {
+        const int u = tid + C::NTH * n;
+        const int i = u / C::VPR, c = u % C::VPR;
+        st.k[n] = st.q[n] = make_uint4(0, 0, 0, 0);
+        if (u < C::KV && i < nt) {
+            const int64_t off = sr.row(t0 + i) * DK + c * (16 / C::ESZ);
+            st.k[n] = *reinterpret_cast<const uint4 *>(k + off);
+            if (want_qd) st.q[n] = *reinterpret_cast<const uint4 *>(q + off);
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < C::NG; ++n) {
+        const int u = tid + C::NTH * n;
+        const int i = u / (DK / 4), c = u % (DK / 4);
+        st.g[n] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (u < C::GV && i < nt)
+            st.g[n] = *reinterpret_cast<const float4 *>(gk + sr.row(t0 + i) * DK + 4 * c);
+    }
+#pragma unroll
+    for (int n = 0; n < C::NV; ++n) {
+        const int u = tid + C::NTH * n;
+        const int i = u / C::RW, r = row0 + u % C::RW;
+        st.v[n] = st.d[n] = DT(0.f);
+        if (u < C::TB * C::RW && i < nt && r < Dv) {
+            st.v[n] = v[sr.row(t0 + i) * Dv + r];
+            if (want_qd) st.d[n] = dout[sr.row(t0 + i) * Dv + r];
+        }
+    }
+    st.b = DT(0.f);
+    if (tid < nt) st.b = beta[sr.row(t0 + tid)];
+}
+
+__device__ __forceinline__ void kb_put(float *dst, const uint4 &x, float) {
+    *reinterpret_cast<uint4 *>(dst) = x;
+}
+__device__ __forceinline__ void kb_put(float *dst, const uint4 &x, __bf16) {
+    const bf16x8 h = __builtin_bit_cast(bf16x8, x);
+    reinterpret_cast<float4 *>(dst)[0] = make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
+    reinterpret_cast<float4 *>(dst)[1] = make_float4((float)h[4], (float)h[5], (float)h[6], (float)h[7]);
+}
+
+template <typename DT, int DK>
+__device__ __forceinline__ void kb_store(const KbStage<DT, DK> &st, char *buf) {
+    typedef KbCfg<DT, DK> C;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int n = 0; n < C::NK; ++n) {
+        const int u = tid + C::NTH * n;
+        if (u < C::KV) {
+            kb_put(reinterpret_cast<float *>(buf + C::OFF_K) + u * (16 / C::ESZ), st.k[n], DT{});
+            kb_put(reinterpret_cast<float *>(buf + C::OFF_Q) + u * (16 / C::ESZ), st.q[n], DT{});
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < C::NG; ++n) {
+        const int u = tid + C::NTH * n;
+        if (u < C::GV) {
+            const float4 x = st.g[n];
+            reinterpret_cast<float4 *>(buf + C::OFF_A)[u] =
+                make_float4(__expf(x.x), __expf(x.y), __expf(x.z), __expf(x.w));
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < C::NV; ++n) {
+        const int u = tid + C::NTH * n;
+        if (u < C::TB * C::RW) {
+            reinterpret_cast<float *>(buf + C::OFF_V)[u] = to_f32(st.v[n]);
+            reinterpret_cast<float *>(buf + C::OFF_D)[u] = to_f32(st.d[n]);
+        }
+    }
+    if (tid < C::TB) reinterpret_cast<float *>(buf + C::OFF_B)[tid] = to_f32(st.b);
+}
+
+__device__ __forceinline__ void kb_lds8(const char *p, float (&x)[8]) {
+    const float4 a = reinterpret_cast<const float4 *>(p)[0];
+    const float4 b = reinterpret_cast<const float4 *>(p)[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// Sum over the rows of the wave at the same column position: the rows sit
+// LPR lanes apart, so rotations of the 16-lane DPP row by LPR, 2 LPR, ...
+// and then the cross-row lane swaps (xor 16, xor 32) keep every lane's
+// column and leave it the total.  Every lane of the wave must be active.
+template <int LPR>
+__device__ __forceinline__ float kb_rows_sum(float x) {
+    if constexpr (LPR <= 1) x += dpp_move<0x121>(x);  // row_ror:1
+    if constexpr (LPR <= 2) x += dpp_move<0x122>(x);  // row_ror:2
+    if constexpr (LPR <= 4) x += dpp_move<0x124>(x);  // row_ror:4
+    if constexpr (LPR <= 8) x += dpp_move<0x128>(x);  // row_ror:8
+    return xor32_sum(xor16_sum(x));
+}
+
+// Grid: (sequence, head, row tile) flattened, tile fastest.  cu (packed
+// sequences in one batch row of T tokens) or the batch index picks the token
+// range; offsets are clamped into [0, T].  Checkpoint slots of a sequence
+// start at block base / 16 + n (disjoint between sequences, in bounds for
+// any offsets).
+template <typename DT, int DK>
+__global__ __launch_bounds__(KbLanes<DK>::value) void kda_bwd_kernel(
+    const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
+    const DT *__restrict__ beta, const float *__restrict__ gk, const float *__restrict__ S0,
+    const DT *__restrict__ dout, const float *__restrict__ dS_T, DT *__restrict__ dv,
+    float *__restrict__ dS0, float *__restrict__ ckpt, float *__restrict__ part,
+    float *__restrict__ partb, const int *__restrict__ cu, int T, int H, int Dv, int R,
+    int64_t rows_total, float scale) {
+    typedef KbCfg<DT, DK> C;
+    constexpr int LPR = C::LPR, TB = C::TB, G = C::G;
+    __shared__ __attribute__((aligned(16))) char smem[2 * C::BUF];
+    __shared__ __attribute__((aligned(16))) float red[C::RED];
+
+    const int tile = blockIdx.x % R;
+    const int64_t seqhead = blockIdx.x / R;   // n * H + h
+    const int64_t n = seqhead / H;
+    const int h = (int)(seqhead % H);
+    int lo = 0, hi = T;
+    int64_t batch = n;
+    if (cu) {
+        lo = min(max(cu[n], 0), T);
+        hi = min(max(cu[n + 1], lo), T);
+        batch = 0;
+    }
+    const KbRows sr{batch * T + lo, H, h};
+    const int len = hi - lo;
+    const int nblk = (len + TB - 1) / TB;
+    const int64_t blk0 = sr.base / TB + n;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int sub = tid % LPR, rloc = tid / LPR;
+    const int row0 = tile * C::RW, row = row0 + rloc;
+    const bool live = row < Dv;
+    const int64_t srow = (seqhead * Dv + row) * DK + 8 * sub;
+    auto ck_at = [&](int j) {
+        return ckpt + (((blk0 + j) * H + h) * (int64_t)(R * C::RW) + row) * DK + 8 * sub;
+    };
+
+    // ---- phase 1: forward, the state at every block start to the workspace
+    float s[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = 0.f;
+    if (S0 && live) {
+        const float4 a0 = reinterpret_cast<const float4 *>(S0 + srow)[0];
+        const float4 a1 = reinterpret_cast<const float4 *>(S0 + srow)[1];
+        s[0] = a0.x; s[1] = a0.y; s[2] = a0.z; s[3] = a0.w;
+        s[4] = a1.x; s[5] = a1.y; s[6] = a1.z; s[7] = a1.w;
+    }
+    KbStage<DT, DK> st;
+    if (nblk > 0) {
+        kb_load<DT, DK>(st, q, k, v, beta, gk, dout, sr, 0, min(TB, len), row0, Dv, false);
+        kb_store<DT, DK>(st, smem);
+    }
+    lds_barrier();
+    for (int j = 0; j < nblk; ++j) {
+        const int t0 = j * TB, nt = min(TB, len - t0);
+        const bool more = j + 1 < nblk;
+        if (more)
+            kb_load<DT, DK>(st, q, k, v, beta, gk, dout, sr, t0 + TB, min(TB, len - t0 - TB),
+                            row0, Dv, false);
+        float4 *cp = reinterpret_cast<float4 *>(ck_at(j));
+        cp[0] = make_float4(s[0], s[1], s[2], s[3]);
+        cp[1] = make_float4(s[4], s[5], s[6], s[7]);
+        const char *buf = smem + (j & 1) * C::BUF;
+        for (int i = 0; i < nt; ++i) {
+            float kk[8], aa[8];
+            kb_lds8(buf + C::OFF_K + (i * DK + 8 * sub) * 4, kk);
+            kb_lds8(buf + C::OFF_A + (i * DK + 8 * sub) * 4, aa);
+            const float vv = reinterpret_cast<const float *>(buf + C::OFF_V)[i * C::RW + rloc];
+            const float bb = reinterpret_cast<const float *>(buf + C::OFF_B)[i];
+            float pk = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                s[e] *= aa[e];
+                pk += s[e] * kk[e];
+            }
+            const float bu = bb * (vv - group_sum<LPR>(pk));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s[e] += bu * kk[e];
+        }
+        if (more) kb_store<DT, DK>(st, smem + ((j + 1) & 1) * C::BUF);
+        lds_barrier();
+    }
+    // the checkpoint stores complete before phase 2 reads them back
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+    // ---- phase 2: blocks last to first
+    float D[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) D[e] = 0.f;
+    if (dS_T && live) {
+        const float4 a0 = reinterpret_cast<const float4 *>(dS_T + srow)[0];
+        const float4 a1 = reinterpret_cast<const float4 *>(dS_T + srow)[1];
+        D[0] = a0.x; D[1] = a0.y; D[2] = a0.z; D[3] = a0.w;
+        D[4] = a1.x; D[5] = a1.y; D[6] = a1.z; D[7] = a1.w;
+    }
+    if (nblk > 0) {
+        const int t0 = (nblk - 1) * TB;
+        kb_load<DT, DK>(st, q, k, v, beta, gk, dout, sr, t0, len - t0, row0, Dv, true);
+        kb_store<DT, DK>(st, smem + ((nblk - 1) & 1) * C::BUF);
+    }
+    lds_barrier();
+    for (int j = nblk - 1; j >= 0; --j) {
+        const int t0 = j * TB, nt = min(TB, len - t0);
+        if (j > 0)
+            kb_load<DT, DK>(st, q, k, v, beta, gk, dout, sr, t0 - TB, TB, row0, Dv, true);
+        const char *buf = smem + (j & 1) * C::BUF;
+        {
+            const float4 *cp = reinterpret_cast<const float4 *>(ck_at(j));
+            const float4 a0 = cp[0], a1 = cp[1];
+            s[0] = a0.x; s[1] = a0.y; s[2] = a0.z; s[3] = a0.w;
+            s[4] = a1.x; s[5] = a1.y; s[6] = a1.z; s[7] = a1.w;
+        }
+        // recompute: sp[i] = the state before token i
+        float sp[TB][8];
+#pragma unroll
+        for (int i = 0; i < TB; ++i) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sp[i][e] = s[e];
+            if (i < nt) {
+                float kk[8], aa[8];
+                kb_lds8(buf + C::OFF_K + (i * DK + 8 * sub) * 4, kk);
+                kb_lds8(buf + C::OFF_A + (i * DK + 8 * sub) * 4, aa);
+                const float vv = reinterpret_cast<const float *>(buf + C::OFF_V)[i * C::RW + rloc];
+                const float bb = reinterpret_cast<const float *>(buf + C::OFF_B)[i];
+                float pk = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    s[e] *= aa[e];
+                    pk += s[e] * kk[e];
+                }
+                const float bu = bb * (vv - group_sum<LPR>(pk));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s[e] += bu * kk[e];
+            }
+        }
+        // reverse
+#pragma unroll
+        for (int i = TB - 1; i >= 0; --i) {
+            const int par = (i / G) & 1;
+            if (i < nt) {
+                float kk[8], qq[8], aa[8], P[8], xq[8], xk[8], xg[8];
+                kb_lds8(buf + C::OFF_K + (i * DK + 8 * sub) * 4, kk);
+                kb_lds8(buf + C::OFF_Q + (i * DK + 8 * sub) * 4, qq);
+                kb_lds8(buf + C::OFF_A + (i * DK + 8 * sub) * 4, aa);
+                const float vv = reinterpret_cast<const float *>(buf + C::OFF_V)[i * C::RW + rloc];
+                const float sd = scale * reinterpret_cast<const float *>(buf + C::OFF_D)[i * C::RW + rloc];
+                const float bb = reinterpret_cast<const float *>(buf + C::OFF_B)[i];
+                float pk = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    P[e] = sp[i][e] * aa[e];
+                    pk += P[e] * kk[e];
+                }
+                const float err = vv - group_sum<LPR>(pk);    // e_t for this row
+                const float bu = bb * err;
+                float wk = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    xq[e] = (P[e] + bu * kk[e]) * sd;          // S_t^T do (this row's term)
+                    D[e] += sd * qq[e];
+                    wk += D[e] * kk[e];
+                }
+                const float w = group_sum<LPR>(wk);
+                if (live && sub == 0) dv[sr.row(t0 + i) * Dv + row] = from_f32<DT>(bb * w);
+                const float bw = bb * w;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    xk[e] = bb * (D[e] * err - P[e] * w);
+                    D[e] -= bw * kk[e];
+                    xg[e] = D[e] * P[e];
+                    D[e] *= aa[e];
+                }
+                float xb = err * w;
+                // this wave's rows summed; lanes 0 .. LPR-1 hold the sums
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    xq[e] = kb_rows_sum<LPR>(xq[e]);
+                    xk[e] = kb_rows_sum<LPR>(xk[e]);
+                    xg[e] = kb_rows_sum<LPR>(xg[e]);
+                }
+                xb = kb_rows_sum<LPR>(xb);
+                float *rw = red + ((par * G + i % G) * C::NWV + wave) * C::NRED;
+                if (lane < LPR) {
+                    float4 *d4 = reinterpret_cast<float4 *>(rw + 8 * sub);
+                    d4[0] = make_float4(xq[0], xq[1], xq[2], xq[3]);
+                    d4[1] = make_float4(xq[4], xq[5], xq[6], xq[7]);
+                    d4 = reinterpret_cast<float4 *>(rw + DK + 8 * sub);
+                    d4[0] = make_float4(xk[0], xk[1], xk[2], xk[3]);
+                    d4[1] = make_float4(xk[4], xk[5], xk[6], xk[7]);
+                    d4 = reinterpret_cast<float4 *>(rw + 2 * DK + 8 * sub);
+                    d4[0] = make_float4(xg[0], xg[1], xg[2], xg[3]);
+                    d4[1] = make_float4(xg[4], xg[5], xg[6], xg[7]);
+                    if (lane == 0) rw[3 * DK] = xb;
+                }
+            }
+            if (i % G == 0) {
+                // tokens i .. i+G-1 of the block: the waves' sums added up and
+                // written as this row tile's partials
+                lds_barrier();
+                constexpr int NV1 = 3 * DK + 1;
+                for (int u = tid; u < G * NV1; u += C::NTH) {
+                    const int tk = u / NV1, e = u % NV1;
+                    if (i + tk < nt) {
+                        const float *rr = red + (par * G + tk) * C::NWV * C::NRED + e;
+                        float acc = 0.f;
+#pragma unroll
+                        for (int wv = 0; wv < C::NWV; ++wv) acc += rr[wv * C::NRED];
+                        const int64_t grow = sr.row(t0 + i + tk);
+                        if (e < 3 * DK)
+                            part[((int64_t)((e / DK) * R + tile) * rows_total + grow) * DK +
+                                 e % DK] = acc;
+                        else
+                            partb[(int64_t)tile * rows_total + grow] = acc;
+                    }
+                }
+            }
+        }
+        if (j > 0) kb_store<DT, DK>(st, smem + ((j - 1) & 1) * C::BUF);
+        lds_barrier();
+    }
+    if (dS0 && live) {
+        float4 *dst = reinterpret_cast<float4 *>(dS0 + srow);
+        dst[0] = make_float4(D[0], D[1], D[2], D[3]);
+        dst[1] = make_float4(D[4], D[5], D[6], D[7]);
+    }
+}
+
+// dq, dk, dgk, dbeta of every covered token: the row tiles' partials added
+// (tile order fixed, so results do not depend on scheduling) and converted.
+// Grid: (sequence, split); split s takes tokens s, s + nsplit, ... of the
+// sequence.
+template <typename DT, int DK>
+__global__ __launch_bounds__(256) void kda_bwd_reduce_kernel(
+    const float *__restrict__ part, const float *__restrict__ partb, DT *__restrict__ dq,
+    DT *__restrict__ dk, float *__restrict__ dgk, DT *__restrict__ dbeta,
+    const int *__restrict__ cu, int T, int H, int R, int64_t rows_total, int nsplit) {
+    const int64_t n = blockIdx.x / nsplit;
+    const int sp = blockIdx.x % nsplit;
+    int lo = 0, hi = T;
+    int64_t batch = n;
+    if (cu) {
+        lo = min(max(cu[n], 0), T);
+        hi = min(max(cu[n + 1], lo), T);
+        batch = 0;
+    }
+    const int64_t base = batch * T + lo;
+    const int len = hi - lo;
+    const int nvec = H * (DK / 4);
+    for (int t = sp; t < len; t += nsplit) {
+        const int64_t r0 = (base + t) * H;
+        for (int u = threadIdx.x; u < nvec; u += 256) {
+            const int64_t grow = r0 + u / (DK / 4);
+            const int c = 4 * (u % (DK / 4));
+#pragma unroll
+            for (int qty = 0; qty < 3; ++qty) {
+                float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+                for (int tl = 0; tl < R; ++tl) {
+                    const float4 x = *reinterpret_cast<const float4 *>(
+                        part + ((int64_t)(qty * R + tl) * rows_total + grow) * DK + c);
+                    acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+                }
+                if (qty == 2) {
+                    *reinterpret_cast<float4 *>(dgk + grow * DK + c) = acc;
+                } else {
+                    DT *dst = (qty == 0 ? dq : dk) + grow * DK + c;
+                    dst[0] = from_f32<DT>(acc.x);
+                    dst[1] = from_f32<DT>(acc.y);
+                    dst[2] = from_f32<DT>(acc.z);
+                    dst[3] = from_f32<DT>(acc.w);
+                }
+            }
+        }
+        for (int u = threadIdx.x; u < H; u += 256) {
+            float acc = 0.f;
+            for (int tl = 0; tl < R; ++tl) acc += partb[(int64_t)tl * rows_total + r0 + u];
+            dbeta[r0 + u] = from_f32<DT>(acc);
+        }
+    }
+}
+
+template <int DK>
+int kb_rows_per_wg() {
+    return KbCfg<float, DK>::RW;
+}
+
+int kb_rw(int Dk) {
+    switch (Dk) {
+    case 16: return kb_rows_per_wg<16>();
+    case 32: return kb_rows_per_wg<32>();
+    case 64: return kb_rows_per_wg<64>();
+    case 128: return kb_rows_per_wg<128>();
+    default: return 0;
+    }
+}
+
+struct KbLayout {
+    int R;               // row tiles per (sequence, head)
+    int64_t ckpt, part, partb, total;  // float offsets: checkpoints, partials; total bytes
+};
+
+KbLayout kb_layout(int64_t ntok, int64_t nseq, int64_t H, int Dk, int Dv) {
+    KbLayout l{0, 0, 0, 0, -1};
+    const int rw = kb_rw(Dk);
+    if (rw == 0 || ntok < 0 || nseq < 0 || H < 0) return l;
+    l.R = (Dv + rw - 1) / rw;
+    const auto al = [](int64_t x) { return (x + 63) / 64 * 64; };  // 256-byte parts
+    const int64_t nck = (ntok / KbCfg<float, 16>::TB + nseq) * H * l.R * rw * Dk;
+    const int64_t npart = 3 * (int64_t)l.R * ntok * H * Dk;
+    const int64_t npb = (int64_t)l.R * ntok * H;
+    l.ckpt = 0;
+    l.part = al(nck);
+    l.partb = l.part + al(npart);
+    l.total = (l.partb + al(npb)) * 4;
+    return l;
+}
+
+template <typename DT, int DK>
+hipError_t launch_kb(const KdaBwdArgs &a, const KbLayout &l, hipStream_t stream) {
+    float *ws = static_cast<float *>(a.ws);
+    const int64_t ntok = a.cu ? a.T : a.nseq * a.T;
+    const int64_t rows_total = ntok * a.H;
+    const int64_t grid = a.nseq * a.H * l.R;
+    if (grid > 0) {
+        hipLaunchKernelGGL((kda_bwd_kernel<DT, DK>), dim3((unsigned)grid),
+                           dim3(KbCfg<DT, DK>::NTH), 0, stream, static_cast<const DT *>(a.q),
+                           static_cast<const DT *>(a.k), static_cast<const DT *>(a.v),
+                           static_cast<const DT *>(a.beta), a.gk, a.S0,
+                           static_cast<const DT *>(a.dout), a.dS_T, static_cast<DT *>(a.dv),
+                           a.dS0, ws + l.ckpt, ws + l.part, ws + l.partb, a.cu, (int)a.T,
+                           (int)a.H, a.Dv, l.R, rows_total, a.scale);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // enough reduce workgroups to fill the GPU whatever the number of sequences
+    const int64_t nsplit = std::max<int64_t>(1, std::min<int64_t>(std::max<int64_t>(a.T, 1),
+                                                                  (2048 + a.nseq - 1) / std::max<int64_t>(a.nseq, 1)));
+    const int64_t rgrid = a.nseq * nsplit;
+    if (rgrid > 0 && a.T > 0) {
+        hipLaunchKernelGGL((kda_bwd_reduce_kernel<DT, DK>), dim3((unsigned)rgrid), dim3(256), 0,
+                           stream, ws + l.part, ws + l.partb, static_cast<DT *>(a.dq),
+                           static_cast<DT *>(a.dk), a.dgk, static_cast<DT *>(a.dbeta), a.cu,
+                           (int)a.T, (int)a.H, l.R, rows_total, (int)nsplit);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+template <typename DT>
+hipError_t kb_dk(const KdaBwdArgs &a, const KbLayout &l, hipStream_t stream) {
+    switch (a.Dk) {
+    case 16: return launch_kb<DT, 16>(a, l, stream);
+    case 32: return launch_kb<DT, 32>(a, l, stream);
+    case 64: return launch_kb<DT, 64>(a, l, stream);
+    case 128: return launch_kb<DT, 128>(a, l, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int64_t kda_bwd_workspace_bytes(int64_t ntok, int64_t nseq, int64_t H, int Dk, int Dv) {
+    return kb_layout(ntok, nseq, H, Dk, Dv).total;
+}
+
+hipError_t launch_kda_bwd(const KdaBwdArgs &a, bool bf16, hipStream_t stream) {
+    if (a.nseq == 0 || a.H == 0) return hipSuccess;
+    const int64_t ntok = a.cu ? a.T : a.nseq * a.T;
+    const KbLayout l = kb_layout(ntok, a.nseq, a.H, a.Dk, a.Dv);
+    if (l.total < 0) return hipErrorInvalidValue;
+    return bf16 ? kb_dk<__bf16>(a, l, stream) : kb_dk<float>(a, l, stream);
+}
+
+}  // namespace dr

@@ -491,6 +491,53 @@ dr_status delta_rule_chunk_bwd_ex(const void *q, const void *k, const void *v, c
                                   int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
                                   uint32_t flags, dr_dtype dtype, void *stream);
 
+/*
+ * kda_bwd -- gradients of the per-key-channel decay rule (Kimi Delta
+ * Attention; hada.io digest, section "Kimi Delta Attention : attenuation par
+ * canal") for any log decay, erased channels (gk = -inf or very negative)
+ * included: the forward it differentiates is delta_rule_chunk_fwd_ex with
+ * opts.gk (either schedule; they agree up to rounding), optionally with
+ * opts.cu_seqlens and opts.scale, without DR_QK_L2NORM.  With a_t[j] =
+ * exp(gk_t[j]): P_t = S_{t-1} Diag(a_t), e_t = v_t - P_t k_t, S_t = P_t +
+ * beta_t e_t k_t^T, o_t = scale S_t q_t; the gradients are those of the
+ * loss L = sum_t <do_t, o_t> + <dS_T, S_T> through that recurrence (the
+ * backward with recomputed states of the paper summary of "Parallelizing
+ * Linear Transformers with the Delta Rule over Sequence Length", section 3).
+ *
+ * Token-serial: one workgroup per (sequence, head, tile of state rows) walks
+ * the sequence forward, storing the state every 16 tokens in the workspace,
+ * then walks it backward block by block, recomputing each block's states.
+ *
+ *   q, k, v, beta, S0, dout, dS_T  as delta_rule_chunk_bwd (S0, dS_T may be
+ *               NULL: zero); gk [B,T,H,Dk] fp32, 16-byte aligned
+ *   cu_seqlens, num_seqs  packed sequences as in dr_chunk_opts (B must be 1;
+ *               S0, dS_T and dS0 are then [num_seqs,H,Dv,Dk]), or NULL
+ *   scale       finite output scale of the forward
+ *   dq, dk      [B,T,H,Dk] in the input dtype
+ *   dv          [B,T,H,Dv] in the input dtype
+ *   dbeta       [B,T,H] in the input dtype
+ *   dgk         [B,T,H,Dk] fp32, 16-byte aligned
+ *   dS0         [B,H,Dv,Dk] fp32 or NULL (not written)
+ *   workspace   kda_bwd_workspace_bytes(B,T,H,Dk,Dv,num_seqs) bytes (num_seqs
+ *               = B without packing), 16-byte aligned; may be NULL when
+ *               T == 0.  Contents on return: scratch.
+ *   Tokens covered by no packed sequence get no gradient (left untouched).
+ *   Outputs must not overlap the inputs, the workspace or each other.
+ * Sizes: Dk, Dv in {16,32,64,128}, else DR_ERR_UNSUPPORTED.  Other errors as
+ * delta_rule_chunk_bwd; a missing or too small workspace, a non-finite
+ * scale or cu_seqlens with B != 1 is DR_ERR_INVALID_ARG.  Asynchronous on
+ * `stream`; allocates nothing.
+ */
+int64_t kda_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                int64_t num_seqs);
+
+dr_status kda_bwd(const void *q, const void *k, const void *v, const void *beta,
+                  const float *gk, const float *S0, const void *dout, const float *dS_T,
+                  void *dq, void *dk, void *dv, void *dbeta, float *dgk, float *dS0,
+                  const int32_t *cu_seqlens, int64_t num_seqs, float scale, void *workspace,
+                  size_t workspace_bytes, int64_t B, int64_t T, int64_t H, int64_t Dk,
+                  int64_t Dv, dr_dtype dtype, void *stream);
+
 /* The hipError_t value of the last DR_ERR_HIP returned on this thread
  * (0 if none). */
 int delta_rule_last_hip_error(void);
@@ -506,7 +553,8 @@ int delta_rule_last_hip_error(void);
  * the scratch of its two-pass schedule; 2.11.0: the backward's split
  * reverse walk on a second stream; 2.12.0: the segmented state-gradient
  * recursion for few heads, its maps in the workspace; 2.13.0:
- * delta_rule_chunk_fwd_checkpointed and delta_rule_chunk_bwd_ex). */
+ * delta_rule_chunk_fwd_checkpointed and delta_rule_chunk_bwd_ex; 2.14.0:
+ * kda_bwd). */
 int delta_rule_version(void);
 
 #ifdef __cplusplus

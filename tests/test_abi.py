@@ -420,6 +420,66 @@ def test_gated_backward_rejects_unsupported_and_empty(lib):
     assert _gbwd(lib, H=0) == dr.DR_OK
 
 
+# ------------------------------------------ per-channel-decay backward
+def test_kda_backward_workspace_size(lib):
+    f = lib.kda_bwd_workspace_bytes
+    f.restype = ctypes.c_int64
+    f.argtypes = [ctypes.c_int64] * 6
+    # the state of every row tile at every 16-token block start of every
+    # sequence (B*T/16 + sequences blocks), then fp32 partials of dq, dk, dgk
+    # ([tiles, B*T*H, Dk] each) and of dbeta; rows per tile = 512 lanes /
+    # (Dk / 8) lanes per row, at most 128 rows (Dk 128: 32, 64: 64, 32 and
+    # 16: 128); each part rounded up to 256 bytes
+    al = lambda x: (x + 255) // 256 * 256
+
+    def want(B, T, H, Dk, Dv, n):
+        rw = {128: 32, 64: 64, 32: 128, 16: 128}[Dk]
+        R = -(-Dv // rw)
+        ck = (B * T // 16 + n) * H * R * rw * Dk * 4
+        return al(ck) + al(3 * R * B * T * H * Dk * 4) + al(R * B * T * H * 4)
+
+    assert f(8, 2048, 16, 128, 128, 8) == want(8, 2048, 16, 128, 128, 8)
+    assert f(2, 77, 3, 64, 32, 2) == want(2, 77, 3, 64, 32, 2)
+    assert f(1, 300, 2, 16, 64, 5) == want(1, 300, 2, 16, 64, 5)
+    assert f(1, 0, 2, 32, 32, 1) == want(1, 0, 2, 32, 32, 1)
+    assert f(1, 10, 1, 24, 16, 1) == -1      # unsupported size
+    assert f(-1, 10, 1, 16, 16, 1) == -1
+
+
+def _kbwd(lib, gk=ctypes.c_void_p(0x100000 * 12), dgk=ctypes.c_void_p(0x100000 * 13), ws=P[7],
+          wsb=1 << 40, q=P[0], k=P[1], v=P[2], beta=P[3], dout=P[4], dq=P[5], dk=P[6],
+          dv=ctypes.c_void_p(0x100000 * 10), dbeta=ctypes.c_void_p(0x100000 * 11), dS0=None,
+          S0=None, dST=None, cu=None, nseq=0, scale=1.0, B=1, T=64, H=2, Dk=64, Dv=64,
+          dtype=dr.DR_BF16):
+    return lib.kda_bwd(q, k, v, beta, gk, S0, dout, dST, dq, dk, dv, dbeta, dgk, dS0, cu, nseq,
+                       scale, ws, wsb, B, T, H, Dk, Dv, dtype, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(gk=None), dict(dgk=None),   # both required when T > 0
+    dict(gk=MISALIGNED), dict(dgk=ctypes.c_void_p(0x100000 * 13 + 4)),  # 16-byte vectors
+    dict(dgk=P[1]),                  # dgk overlaps k
+    dict(dgk=P[7]),                  # dgk overlaps the workspace
+    dict(dq=ctypes.c_void_p(0x100000 * 12)),   # an output overlaps gk
+    dict(ws=None), dict(wsb=16), dict(dout=None), dict(dv=None),
+    dict(scale=float("nan")), dict(scale=float("inf")),
+    dict(cu=P[7], nseq=2, B=2),      # packed sequences need B = 1
+    dict(cu=ctypes.c_void_p(0x100000 * 14 + 2), nseq=2),   # misaligned offsets
+    dict(cu=P[5], nseq=2),           # offsets overlap an output
+    dict(B=-1), dict(dtype=3),
+])
+def test_kda_backward_rejects_invalid(lib, kw):
+    assert _kbwd(lib, **kw) == dr.DR_ERR_INVALID_ARG
+
+
+def test_kda_backward_rejects_unsupported_and_empty(lib):
+    assert _kbwd(lib, Dk=48) == dr.DR_ERR_UNSUPPORTED
+    assert _kbwd(lib, Dv=24) == dr.DR_ERR_UNSUPPORTED
+    assert _kbwd(lib, B=0) == dr.DR_OK
+    assert _kbwd(lib, H=0) == dr.DR_OK
+    assert _kbwd(lib, cu=ctypes.c_void_p(0x100000 * 14), nseq=0) == dr.DR_OK
+
+
 # ------------------------------------------- segment-parallel workspace size
 def test_chunk_fwd_workspace_bytes(lib):
     f = lib.delta_rule_chunk_fwd_workspace_bytes
