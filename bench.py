@@ -33,7 +33,8 @@ stdout:
                and reverse pass), time per call and ratio to the forward launch;
                with "gated" inside it, gated_delta_rule_chunk_bwd likewise, and
                "one_sequence", one sequence of the layer shape (B = 1, the
-               two-pass reverse schedule for few heads)
+               two-pass reverse schedule for few heads), "training_step", and
+               "kda", kda_bwd on the layer shape with per-channel decay
   kda          per-key-channel decay: decode steps and the chunked forward
   long_prefill the long-prefill config (B1 H16 T32768) through the
                segment-parallel schedule, with the plain schedule beside it
@@ -443,6 +444,37 @@ def bench_backward(torch, dr, W, reps=10, name="layer_1p3b", B=None):
     }
 
 
+def bench_kda_backward(torch, dr, W, reps=5):
+    """kda_bwd on the layer shape with per-channel decay drawn with A up to 16
+    (the kda_fwd line's inputs), upstream gradients for o and S_T: mean time
+    per call with HIP events on the launch stream (outputs allocated inside)."""
+    w = W.get("layer_1p3b", gate_amax=16.0, kda=True, chunk=32)
+    x = W.generate(w)
+    dev = torch.device("cuda:0")
+    d = {n: (None if t is None else t.to(dev)) for n, t in x.items()}
+    gen = torch.Generator(device="cpu").manual_seed(11)
+    do = torch.randn(w.B, w.T, w.H, w.Dv, generator=gen).to(w.torch_dtype).to(dev)
+    dst = torch.randn(w.B, w.H, w.Dv, w.Dk, generator=gen).to(dev)
+    ws = torch.empty(dr.kda_bwd_workspace_bytes(w.B, w.T, w.H, w.Dk, w.Dv), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        dr.kda_bwd(d["q"], d["k"], d["v"], d["beta"], d["gk"], do, d["S0"], dst, workspace=ws)
+
+    settle(torch, step)
+    t = timed_steps(torch, step, reps)
+    return {
+        "workload": (f"layer_1p3b B{w.B} H{w.H} T{w.T} d{w.Dk}, bf16 in, per-channel log decay "
+                     "fp32 (A up to 16), fp32 state; token-serial: forward with a checkpoint "
+                     "every 16 tokens, then blocks in reverse with their states recomputed, "
+                     "and a reduce over the row tiles"),
+        "tokens_per_s": w.B * w.T / t,
+        "mean_call_us": round(t * 1e6, 2),
+        "vs_kda_forward": None,
+        "workspace_bytes": int(ws.numel()),
+    }
+
+
 def bench_training_step(torch, dr, W, reps=10, name="layer_1p3b"):
     """The chunked work of a training step on the layer shape: the forward
     (chunk 64) then the backward that forms its own checkpoints, against the
@@ -702,6 +734,12 @@ def main():
         ts = out["backward"]["training_step"]
         ts["backward_reusing_vs_forward_launch"] = round(
             ts["backward_reusing_checkpoints_us"] / roof["mean_launch_us"], 2)
+        if not args.no_gated:
+            log("backward: KDA, layer shape (token-serial)")
+            kb = out["backward"]["kda"] = bench_kda_backward(torch, dr, W)
+            kf = out.get("kda", {}).get("sequence")
+            if kf:
+                kb["vs_kda_forward"] = round(kb["mean_call_us"] / kf["mean_launch_us"], 2)
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle on the whole workload, then on one thread")
         torch.cuda.synchronize()

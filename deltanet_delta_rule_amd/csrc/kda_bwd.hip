@@ -26,8 +26,8 @@
 // needs no other workgroup: LPR = d_k / 8 lanes per row, each holding 8
 // consecutive columns (as the token-serial forward).  Only dq, dk, dgk and
 // dbeta are sums over all rows: each workgroup adds up its own rows' terms
-// (lane swaps inside a wave, then across its waves in LDS, two tokens per
-// barrier) and writes one partial per row tile to the workspace; a second
+// (a reduce-scatter on lane swaps inside a wave, then across its waves in
+// LDS, two tokens per barrier) and writes one partial per row tile to the workspace; a second
 // kernel adds the tiles' partials and converts them.
 //
 // Phases of the main kernel:
@@ -189,15 +189,42 @@ __device__ __forceinline__ void kb_lds8(const char *p, float (&x)[8]) {
 
 // Sum over the rows of the wave at the same column position: the rows sit
 // LPR lanes apart, so rotations of the 16-lane DPP row by LPR, 2 LPR, ...
-// and then the cross-row lane swaps (xor 16, xor 32) keep every lane's
-// column and leave it the total.  Every lane of the wave must be active.
+// keep every lane's column and leave it the sum over the rows in its DPP row.
 template <int LPR>
-__device__ __forceinline__ float kb_rows_sum(float x) {
+__device__ __forceinline__ float kb_dpp_rows_sum(float x) {
     if constexpr (LPR <= 1) x += dpp_move<0x121>(x);  // row_ror:1
     if constexpr (LPR <= 2) x += dpp_move<0x122>(x);  // row_ror:2
     if constexpr (LPR <= 4) x += dpp_move<0x124>(x);  // row_ror:4
     if constexpr (LPR <= 8) x += dpp_move<0x128>(x);  // row_ror:8
-    return xor32_sum(xor16_sum(x));
+    return x;
+}
+
+// a + b after swapping the upper 32 lanes of a with the lower 32 of b: the
+// lower half then holds a's two halves added, the upper half b's.
+__device__ __forceinline__ float kb_fold32(float a, float b) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+// a + b after swapping the odd 16-lane rows of a with the even rows of b:
+// rows 0 and 2 then hold a's row pairs added, rows 1 and 3 b's.
+__device__ __forceinline__ float kb_fold16(float a, float b) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// Reduce-scatter of 24 per-lane values over the 4 DPP rows of the wave
+// (after kb_dpp_rows_sum): value x[e + 6 r] summed over the wave's rows ends
+// in z[e] of the lanes of DPP row r (e < 6).  Two halvings of the values
+// (upper with lower half of the wave, then odd with even rows), 18 lane
+// swaps instead of 48 for a sum in every lane.
+__device__ __forceinline__ void kb_scatter24(const float (&x)[24], float (&z)[6]) {
+    float y[12];
+#pragma unroll
+    for (int e = 0; e < 12; ++e) y[e] = kb_fold32(x[e], x[e + 12]);
+    // lower half: x[e] (rows 0,1), upper half: x[e + 12] (rows 2,3)
+#pragma unroll
+    for (int e = 0; e < 6; ++e) z[e] = kb_fold16(y[e], y[e + 6]);
+    // row 0: x[e], row 1: x[e + 6], row 2: x[e + 12], row 3: x[e + 18]
 }
 
 // Grid: (sequence, head, row tile) flattened, tile fastest.  cu (packed
@@ -309,15 +336,17 @@ __global__ __launch_bounds__(KbLanes<DK>::value) void kda_bwd_kernel(
     lds_barrier();
     for (int j = nblk - 1; j >= 0; --j) {
         const int t0 = j * TB, nt = min(TB, len - t0);
-        if (j > 0)
-            kb_load<DT, DK>(st, q, k, v, beta, gk, dout, sr, t0 - TB, TB, row0, Dv, true);
-        const char *buf = smem + (j & 1) * C::BUF;
+        // the block's state first, so that waiting for it does not wait for
+        // the next block's loads
         {
             const float4 *cp = reinterpret_cast<const float4 *>(ck_at(j));
             const float4 a0 = cp[0], a1 = cp[1];
             s[0] = a0.x; s[1] = a0.y; s[2] = a0.z; s[3] = a0.w;
             s[4] = a1.x; s[5] = a1.y; s[6] = a1.z; s[7] = a1.w;
         }
+        if (j > 0)
+            kb_load<DT, DK>(st, q, k, v, beta, gk, dout, sr, t0 - TB, TB, row0, Dv, true);
+        const char *buf = smem + (j & 1) * C::BUF;
         // recompute: sp[i] = the state before token i
         float sp[TB][8];
 #pragma unroll
@@ -378,26 +407,25 @@ __global__ __launch_bounds__(KbLanes<DK>::value) void kda_bwd_kernel(
                     xg[e] = D[e] * P[e];
                     D[e] *= aa[e];
                 }
-                float xb = err * w;
-                // this wave's rows summed; lanes 0 .. LPR-1 hold the sums
+                // this wave's rows summed: lane (DPP row r, column group sub)
+                // ends with values 6r .. 6r+5 of (xq, xk, xg) for its columns
+                float x24[24], z[6];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    xq[e] = kb_rows_sum<LPR>(xq[e]);
-                    xk[e] = kb_rows_sum<LPR>(xk[e]);
-                    xg[e] = kb_rows_sum<LPR>(xg[e]);
+                    x24[e] = kb_dpp_rows_sum<LPR>(xq[e]);
+                    x24[8 + e] = kb_dpp_rows_sum<LPR>(xk[e]);
+                    x24[16 + e] = kb_dpp_rows_sum<LPR>(xg[e]);
                 }
-                xb = kb_rows_sum<LPR>(xb);
+                kb_scatter24(x24, z);
+                const float xb = xor32_sum(xor16_sum(kb_dpp_rows_sum<LPR>(err * w)));
                 float *rw = red + ((par * G + i % G) * C::NWV + wave) * C::NRED;
-                if (lane < LPR) {
-                    float4 *d4 = reinterpret_cast<float4 *>(rw + 8 * sub);
-                    d4[0] = make_float4(xq[0], xq[1], xq[2], xq[3]);
-                    d4[1] = make_float4(xq[4], xq[5], xq[6], xq[7]);
-                    d4 = reinterpret_cast<float4 *>(rw + DK + 8 * sub);
-                    d4[0] = make_float4(xk[0], xk[1], xk[2], xk[3]);
-                    d4[1] = make_float4(xk[4], xk[5], xk[6], xk[7]);
-                    d4 = reinterpret_cast<float4 *>(rw + 2 * DK + 8 * sub);
-                    d4[0] = make_float4(xg[0], xg[1], xg[2], xg[3]);
-                    d4[1] = make_float4(xg[4], xg[5], xg[6], xg[7]);
+                if ((lane & 15) < LPR) {
+                    const int r4 = lane >> 4;
+#pragma unroll
+                    for (int e = 0; e < 6; ++e) {
+                        const int x = 6 * r4 + e;   // quantity x / 8, column 8 sub + x % 8
+                        rw[(x >> 3) * DK + 8 * sub + (x & 7)] = z[e];
+                    }
                     if (lane == 0) rw[3 * DK] = xb;
                 }
             }
