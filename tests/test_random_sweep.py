@@ -1,6 +1,7 @@
 """Seeded random sweep of the GPU paths against the fp64 oracle.
 
-Forty forward cases and sixteen backward cases, drawn once from a fixed seed
+Forty forward cases, sixteen backward cases and ten cases of the KDA
+backward (with an output scale drawn half the time), drawn once from fixed seeds
 over the supported space -- the rule (plain, gated with per-head A up to 16,
 KDA with per-channel decay), the dtype, d_k and d_v in {16, 32, 64, 128}, the
 chunk, batch, heads, sequence length (ragged tails included), beta in (0, 1)
@@ -18,8 +19,8 @@ import torch
 
 import deltanet_delta_rule_amd as dr
 from deltanet_delta_rule_amd import workloads as W
-from oracle import (delta_rule_bwd_ref, delta_rule_ref, gated_delta_rule_ref, kda_ref,
-                    l2norm_rows)
+from oracle import (delta_rule_bwd_ref, delta_rule_ref, gated_delta_rule_ref, kda_bwd_ref,
+                    kda_ref, l2norm_rows)
 from tests.parity_utils import TOL, grad_errors, rel_err, threads, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
@@ -53,6 +54,23 @@ def _draw(n, seed, backward=False):
 
 FWD = _draw(40, 123)
 BWD = _draw(16, 456, backward=True)
+
+
+def _draw_kda_bwd(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        cases.append(dict(
+            rule="kda", dtype=str(rng.choice(["bf16", "bf16", "f32"])),
+            Dk=int(rng.choice(DIMS)), Dv=int(rng.choice(DIMS)), chunk=32,
+            B=int(rng.integers(1, 4)), H=int(rng.integers(1, 5)), T=int(rng.integers(1, 301)),
+            beta_scale=float(rng.choice([1.0, 2.0])), s0_std=float(rng.choice([0.0, 0.02])),
+            scale=None if rng.random() < 0.5 else float(rng.uniform(0.1, 2.0)),
+            seed=40000 + 97 * i))
+    return cases
+
+
+KBWD = _draw_kda_bwd(10, 789)
 
 
 def _id(c):
@@ -131,6 +149,28 @@ def test_backward_random_case(c):
                              g=x.get("g"), nthreads=threads())
     tol = TOL[w.torch_dtype]
     errs = grad_errors(got, ref)
+    print(f"{_id(c)}: " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e <= tol, (n, e)
+
+
+@pytest.mark.parametrize("c", KBWD, ids=_id)
+def test_kda_backward_random_case(c):
+    w = _workload(c)
+    x = W.generate(w)
+    d = to_dev(x)
+    gen = torch.Generator().manual_seed(c["seed"] + 1)
+    do = torch.randn(w.B, w.T, w.H, w.Dv, generator=gen).to(w.torch_dtype)
+    dst = torch.randn(w.B, w.H, w.Dv, w.Dk, generator=gen)
+    got = dr.kda_bwd(d["q"], d["k"], d["v"], d["beta"], d["gk"], do.cuda(), d["S0"], dst.cuda(),
+                     scale=c["scale"])
+    torch.cuda.synchronize()
+    # <do, scale S q> = <scale do, S q>: the oracle takes the scaled upstream gradient
+    do_o = do.double() * (1.0 if c["scale"] is None else c["scale"])
+    ref = kda_bwd_ref(x["q"], x["k"], x["v"], x["beta"], x["gk"], do_o, x["S0"], dst,
+                      nthreads=threads())
+    tol = TOL[w.torch_dtype]
+    errs = {n: rel_err(to_np(got[n]), ref[n]) for n in ref}
     print(f"{_id(c)}: " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
     for n, e in errs.items():
         assert e <= tol, (n, e)
