@@ -24,19 +24,23 @@
 // Work split.  Row i of the state depends only on row i before it, in both
 // directions, so a workgroup owns RW rows of one (sequence, head) state and
 // needs no other workgroup: LPR = d_k / 8 lanes per row, each holding 8
-// consecutive columns (as the token-serial forward).  Only dq, dk, dgk and
-// dbeta are sums over all rows: each workgroup adds up its own rows' terms
-// (a reduce-scatter on lane swaps inside a wave, then across its waves in
-// LDS, two tokens per barrier) and writes one partial per row tile to the workspace; a second
-// kernel adds the tiles' partials and converts them.
+// consecutive columns (as the token-serial forward), and at d_k >= 64 two
+// rows per lane (RL rows apart), which fills the GPU in one round at the
+// layer shape and halves the cross-row sums per row.  Only dq, dk, dgk and
+// dbeta are sums over all rows: each lane first adds its own rows' terms,
+// then each workgroup adds up its rows (a reduce-scatter on lane swaps
+// inside a wave, then across its waves in LDS, two tokens per barrier) and
+// writes one partial per row tile to the workspace; a second kernel adds the
+// tiles' partials and converts them.
 //
 // Phases of the main kernel:
 //   1. the forward over the sequence, storing the state at the start of every
-//      16-token block to the workspace (each lane its own 8 values, read back
+//      16-token block to the workspace (each lane its own values, read back
 //      by the same lane);
-//   2. blocks last to first: the block's starting state reloaded, its tokens
-//      recomputed forward with every pre-token state S_{t-1} kept in
-//      registers, then walked in reverse.
+//   2. blocks last to first, each in two halves of 8 tokens (the second half
+//      first): the block's starting state reloaded and advanced to the half,
+//      the half's tokens recomputed with every pre-token state S_{t-1} kept
+//      in registers, then walked in reverse.
 // The inputs of a block (k, q, exp(gk), the workgroup's rows of v and do,
 // beta) are staged in LDS in fp32 and double-buffered: the next block's
 // global loads are in flight while the current one is processed.
@@ -55,12 +59,15 @@ struct KbLanes {
     static constexpr int value = DK / 8 * 128 < 512 ? DK / 8 * 128 : 512;
 };
 
-template <typename DT, int DK>
+template <typename DT, int DK, int RPL_ = 1>
 struct KbCfg {
     static constexpr int ESZ = sizeof(DT);
     static constexpr int LPR = DK / 8;                          // lanes per state row
     static constexpr int NTH = KbLanes<DK>::value;
-    static constexpr int RW = NTH / LPR;                        // state rows per workgroup
+    static constexpr int RPL = RPL_;                            // state rows per lane
+    static constexpr int RL = NTH / LPR;                        // rows of one lane layer
+    static constexpr int RW = RPL * RL;                         // state rows per workgroup
+    static constexpr int HB = 8;                                // tokens of a half block
     static constexpr int NWV = NTH / 64;
     static constexpr int TB = 16;                               // tokens per block
     static constexpr int G = 2;                                 // tokens per cross-wave sum
@@ -82,9 +89,9 @@ struct KbCfg {
     static constexpr int RED = 2 * G * NWV * NRED;              // floats, two parities
 };
 
-template <typename DT, int DK>
+template <typename DT, int DK, int RPL>
 struct KbStage {
-    typedef KbCfg<DT, DK> C;
+    typedef KbCfg<DT, DK, RPL> C;
     uint4 k[C::NK], q[C::NK];
     float4 g[C::NG];
     DT v[C::NV], d[C::NV];
@@ -98,13 +105,13 @@ struct KbRows {
     __device__ __forceinline__ int64_t row(int t) const { return (base + t) * H + h; }
 };
 
-template <typename DT, int DK>
-__device__ __forceinline__ void kb_load(KbStage<DT, DK> &st, const DT *__restrict__ q,
+template <typename DT, int DK, int RPL>
+__device__ __forceinline__ void kb_load(KbStage<DT, DK, RPL> &st, const DT *__restrict__ q,
                                         const DT *__restrict__ k, const DT *__restrict__ v,
                                         const DT *__restrict__ beta, const float *__restrict__ gk,
                                         const DT *__restrict__ dout, const KbRows &sr, int t0,
                                         int nt, int row0, int Dv, bool want_qd) {
-    typedef KbCfg<DT, DK> C;
+    typedef KbCfg<DT, DK, RPL> C;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int n = 0; n < C::NK; ++n) {
@@ -148,9 +155,9 @@ __device__ __forceinline__ void kb_put(float *dst, const uint4 &x, __bf16) {
     reinterpret_cast<float4 *>(dst)[1] = make_float4((float)h[4], (float)h[5], (float)h[6], (float)h[7]);
 }
 
-template <typename DT, int DK>
-__device__ __forceinline__ void kb_store(const KbStage<DT, DK> &st, char *buf) {
-    typedef KbCfg<DT, DK> C;
+template <typename DT, int DK, int RPL>
+__device__ __forceinline__ void kb_store(const KbStage<DT, DK, RPL> &st, char *buf) {
+    typedef KbCfg<DT, DK, RPL> C;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int n = 0; n < C::NK; ++n) {
@@ -227,12 +234,31 @@ __device__ __forceinline__ void kb_scatter24(const float (&x)[24], float (&z)[6]
     // row 0: x[e], row 1: x[e + 6], row 2: x[e + 12], row 3: x[e + 18]
 }
 
+// One token forward on a lane's rows: decay, predict, correct, write.
+template <int LPR, int RPL>
+__device__ __forceinline__ void kb_fwd_token(float (&s)[RPL][8], const float (&kk)[8],
+                                             const float (&aa)[8], const float (&vv)[RPL],
+                                             float bb) {
+#pragma unroll
+    for (int u = 0; u < RPL; ++u) {
+        float pk = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            s[u][e] *= aa[e];
+            pk += s[u][e] * kk[e];
+        }
+        const float bu = bb * (vv[u] - group_sum<LPR>(pk));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[u][e] += bu * kk[e];
+    }
+}
+
 // Grid: (sequence, head, row tile) flattened, tile fastest.  cu (packed
 // sequences in one batch row of T tokens) or the batch index picks the token
 // range; offsets are clamped into [0, T].  Checkpoint slots of a sequence
 // start at block base / 16 + n (disjoint between sequences, in bounds for
-// any offsets).
-template <typename DT, int DK>
+// any offsets).  A lane holds RPL rows, RL rows apart, and 8 columns of each.
+template <typename DT, int DK, int RPL_>
 __global__ __launch_bounds__(KbLanes<DK>::value) void kda_bwd_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const float *__restrict__ gk, const float *__restrict__ S0,
@@ -240,8 +266,9 @@ __global__ __launch_bounds__(KbLanes<DK>::value) void kda_bwd_kernel(
     float *__restrict__ dS0, float *__restrict__ ckpt, float *__restrict__ part,
     float *__restrict__ partb, const int *__restrict__ cu, int T, int H, int Dv, int R,
     int64_t rows_total, float scale) {
-    typedef KbCfg<DT, DK> C;
-    constexpr int LPR = C::LPR, TB = C::TB, G = C::G;
+    typedef KbCfg<DT, DK, RPL_> C;
+    constexpr int LPR = C::LPR, TB = C::TB, G = C::G, RPL = C::RPL, RL = C::RL, HB = C::HB;
+    static_assert(HB % G == 0 && TB == 2 * HB, "flush groups inside half blocks");
     __shared__ __attribute__((aligned(16))) char smem[2 * C::BUF];
     __shared__ __attribute__((aligned(16))) float red[C::RED];
 
@@ -263,201 +290,230 @@ __global__ __launch_bounds__(KbLanes<DK>::value) void kda_bwd_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int sub = tid % LPR, rloc = tid / LPR;
-    const int row0 = tile * C::RW, row = row0 + rloc;
-    const bool live = row < Dv;
-    const int64_t srow = (seqhead * Dv + row) * DK + 8 * sub;
-    auto ck_at = [&](int j) {
-        return ckpt + (((blk0 + j) * H + h) * (int64_t)(R * C::RW) + row) * DK + 8 * sub;
+    const int row0 = tile * C::RW;
+    int row[RPL];
+    bool live[RPL];
+#pragma unroll
+    for (int u = 0; u < RPL; ++u) {
+        row[u] = row0 + rloc + u * RL;
+        live[u] = row[u] < Dv;
+    }
+    auto srow = [&](int u) { return (seqhead * Dv + row[u]) * DK + 8 * sub; };
+    auto ck_at = [&](int j, int u) {
+        return ckpt + (((blk0 + j) * H + h) * (int64_t)(R * C::RW) + row[u]) * DK + 8 * sub;
+    };
+    auto lds_v = [&](const char *buf, int off, int i, float (&x)[RPL]) {
+#pragma unroll
+        for (int u = 0; u < RPL; ++u)
+            x[u] = reinterpret_cast<const float *>(buf + off)[i * C::RW + rloc + u * RL];
+    };
+    auto load8 = [&](const float *p, float (&x)[8]) {
+        const float4 a0 = reinterpret_cast<const float4 *>(p)[0];
+        const float4 a1 = reinterpret_cast<const float4 *>(p)[1];
+        x[0] = a0.x; x[1] = a0.y; x[2] = a0.z; x[3] = a0.w;
+        x[4] = a1.x; x[5] = a1.y; x[6] = a1.z; x[7] = a1.w;
     };
 
     // ---- phase 1: forward, the state at every block start to the workspace
-    float s[8];
+    float s[RPL][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] = 0.f;
-    if (S0 && live) {
-        const float4 a0 = reinterpret_cast<const float4 *>(S0 + srow)[0];
-        const float4 a1 = reinterpret_cast<const float4 *>(S0 + srow)[1];
-        s[0] = a0.x; s[1] = a0.y; s[2] = a0.z; s[3] = a0.w;
-        s[4] = a1.x; s[5] = a1.y; s[6] = a1.z; s[7] = a1.w;
+    for (int u = 0; u < RPL; ++u) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[u][e] = 0.f;
+        if (S0 && live[u]) load8(S0 + srow(u), s[u]);
     }
-    KbStage<DT, DK> st;
+    KbStage<DT, DK, RPL> st;
     if (nblk > 0) {
-        kb_load<DT, DK>(st, q, k, v, beta, gk, dout, sr, 0, min(TB, len), row0, Dv, false);
-        kb_store<DT, DK>(st, smem);
+        kb_load<DT, DK, RPL>(st, q, k, v, beta, gk, dout, sr, 0, min(TB, len), row0, Dv, false);
+        kb_store<DT, DK, RPL>(st, smem);
     }
     lds_barrier();
     for (int j = 0; j < nblk; ++j) {
         const int t0 = j * TB, nt = min(TB, len - t0);
         const bool more = j + 1 < nblk;
         if (more)
-            kb_load<DT, DK>(st, q, k, v, beta, gk, dout, sr, t0 + TB, min(TB, len - t0 - TB),
+            kb_load<DT, DK, RPL>(st, q, k, v, beta, gk, dout, sr, t0 + TB, min(TB, len - t0 - TB),
                             row0, Dv, false);
-        float4 *cp = reinterpret_cast<float4 *>(ck_at(j));
-        cp[0] = make_float4(s[0], s[1], s[2], s[3]);
-        cp[1] = make_float4(s[4], s[5], s[6], s[7]);
+#pragma unroll
+        for (int u = 0; u < RPL; ++u) {
+            float4 *cp = reinterpret_cast<float4 *>(ck_at(j, u));
+            cp[0] = make_float4(s[u][0], s[u][1], s[u][2], s[u][3]);
+            cp[1] = make_float4(s[u][4], s[u][5], s[u][6], s[u][7]);
+        }
         const char *buf = smem + (j & 1) * C::BUF;
         for (int i = 0; i < nt; ++i) {
-            float kk[8], aa[8];
+            float kk[8], aa[8], vv[RPL];
             kb_lds8(buf + C::OFF_K + (i * DK + 8 * sub) * 4, kk);
             kb_lds8(buf + C::OFF_A + (i * DK + 8 * sub) * 4, aa);
-            const float vv = reinterpret_cast<const float *>(buf + C::OFF_V)[i * C::RW + rloc];
-            const float bb = reinterpret_cast<const float *>(buf + C::OFF_B)[i];
-            float pk = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                s[e] *= aa[e];
-                pk += s[e] * kk[e];
-            }
-            const float bu = bb * (vv - group_sum<LPR>(pk));
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s[e] += bu * kk[e];
+            lds_v(buf, C::OFF_V, i, vv);
+            kb_fwd_token<LPR, RPL>(s, kk, aa, vv, reinterpret_cast<const float *>(buf + C::OFF_B)[i]);
         }
-        if (more) kb_store<DT, DK>(st, smem + ((j + 1) & 1) * C::BUF);
+        if (more) kb_store<DT, DK, RPL>(st, smem + ((j + 1) & 1) * C::BUF);
         lds_barrier();
     }
     // the checkpoint stores complete before phase 2 reads them back
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-    // ---- phase 2: blocks last to first
-    float D[8];
+    // ---- phase 2: blocks last to first, each in two halves of HB tokens
+    float D[RPL][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) D[e] = 0.f;
-    if (dS_T && live) {
-        const float4 a0 = reinterpret_cast<const float4 *>(dS_T + srow)[0];
-        const float4 a1 = reinterpret_cast<const float4 *>(dS_T + srow)[1];
-        D[0] = a0.x; D[1] = a0.y; D[2] = a0.z; D[3] = a0.w;
-        D[4] = a1.x; D[5] = a1.y; D[6] = a1.z; D[7] = a1.w;
+    for (int u = 0; u < RPL; ++u) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) D[u][e] = 0.f;
+        if (dS_T && live[u]) load8(dS_T + srow(u), D[u]);
     }
     if (nblk > 0) {
         const int t0 = (nblk - 1) * TB;
-        kb_load<DT, DK>(st, q, k, v, beta, gk, dout, sr, t0, len - t0, row0, Dv, true);
-        kb_store<DT, DK>(st, smem + ((nblk - 1) & 1) * C::BUF);
+        kb_load<DT, DK, RPL>(st, q, k, v, beta, gk, dout, sr, t0, len - t0, row0, Dv, true);
+        kb_store<DT, DK, RPL>(st, smem + ((nblk - 1) & 1) * C::BUF);
     }
     lds_barrier();
     for (int j = nblk - 1; j >= 0; --j) {
         const int t0 = j * TB, nt = min(TB, len - t0);
         // the block's state first, so that waiting for it does not wait for
         // the next block's loads
-        {
-            const float4 *cp = reinterpret_cast<const float4 *>(ck_at(j));
-            const float4 a0 = cp[0], a1 = cp[1];
-            s[0] = a0.x; s[1] = a0.y; s[2] = a0.z; s[3] = a0.w;
-            s[4] = a1.x; s[5] = a1.y; s[6] = a1.z; s[7] = a1.w;
-        }
+        float c0[RPL][8];
+#pragma unroll
+        for (int u = 0; u < RPL; ++u) load8(ck_at(j, u), c0[u]);
         if (j > 0)
-            kb_load<DT, DK>(st, q, k, v, beta, gk, dout, sr, t0 - TB, TB, row0, Dv, true);
+            kb_load<DT, DK, RPL>(st, q, k, v, beta, gk, dout, sr, t0 - TB, TB, row0, Dv, true);
         const char *buf = smem + (j & 1) * C::BUF;
-        // recompute: sp[i] = the state before token i
-        float sp[TB][8];
+#pragma unroll 1
+        for (int hb = 1; hb >= 0; --hb) {
+            const int i0 = hb * HB;   // first token of the half
+            if (i0 >= nt) continue;   // uniform; an even number of flush groups skipped
 #pragma unroll
-        for (int i = 0; i < TB; ++i) {
+            for (int u = 0; u < RPL; ++u)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sp[i][e] = s[e];
-            if (i < nt) {
-                float kk[8], aa[8];
+                for (int e = 0; e < 8; ++e) s[u][e] = c0[u][e];
+            // the second half starts from the state after the first
+            for (int i = 0; i < i0 && i < nt; ++i) {
+                float kk[8], aa[8], vv[RPL];
                 kb_lds8(buf + C::OFF_K + (i * DK + 8 * sub) * 4, kk);
                 kb_lds8(buf + C::OFF_A + (i * DK + 8 * sub) * 4, aa);
-                const float vv = reinterpret_cast<const float *>(buf + C::OFF_V)[i * C::RW + rloc];
-                const float bb = reinterpret_cast<const float *>(buf + C::OFF_B)[i];
-                float pk = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    s[e] *= aa[e];
-                    pk += s[e] * kk[e];
-                }
-                const float bu = bb * (vv - group_sum<LPR>(pk));
-#pragma unroll
-                for (int e = 0; e < 8; ++e) s[e] += bu * kk[e];
+                lds_v(buf, C::OFF_V, i, vv);
+                kb_fwd_token<LPR, RPL>(s, kk, aa, vv, reinterpret_cast<const float *>(buf + C::OFF_B)[i]);
             }
-        }
-        // reverse
+            // recompute: sp[i] = the state before token i0 + i
+            float sp[HB][RPL][8];
 #pragma unroll
-        for (int i = TB - 1; i >= 0; --i) {
-            const int par = (i / G) & 1;
-            if (i < nt) {
-                float kk[8], qq[8], aa[8], P[8], xq[8], xk[8], xg[8];
-                kb_lds8(buf + C::OFF_K + (i * DK + 8 * sub) * 4, kk);
-                kb_lds8(buf + C::OFF_Q + (i * DK + 8 * sub) * 4, qq);
-                kb_lds8(buf + C::OFF_A + (i * DK + 8 * sub) * 4, aa);
-                const float vv = reinterpret_cast<const float *>(buf + C::OFF_V)[i * C::RW + rloc];
-                const float sd = scale * reinterpret_cast<const float *>(buf + C::OFF_D)[i * C::RW + rloc];
-                const float bb = reinterpret_cast<const float *>(buf + C::OFF_B)[i];
-                float pk = 0.f;
+            for (int i = 0; i < HB; ++i) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    P[e] = sp[i][e] * aa[e];
-                    pk += P[e] * kk[e];
+                for (int u = 0; u < RPL; ++u)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) sp[i][u][e] = s[u][e];
+                if (i0 + i < nt) {
+                    float kk[8], aa[8], vv[RPL];
+                    kb_lds8(buf + C::OFF_K + ((i0 + i) * DK + 8 * sub) * 4, kk);
+                    kb_lds8(buf + C::OFF_A + ((i0 + i) * DK + 8 * sub) * 4, aa);
+                    lds_v(buf, C::OFF_V, i0 + i, vv);
+                    kb_fwd_token<LPR, RPL>(s, kk, aa, vv,
+                                           reinterpret_cast<const float *>(buf + C::OFF_B)[i0 + i]);
                 }
-                const float err = vv - group_sum<LPR>(pk);    // e_t for this row
-                const float bu = bb * err;
-                float wk = 0.f;
+            }
+            // reverse
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    xq[e] = (P[e] + bu * kk[e]) * sd;          // S_t^T do (this row's term)
-                    D[e] += sd * qq[e];
-                    wk += D[e] * kk[e];
-                }
-                const float w = group_sum<LPR>(wk);
-                if (live && sub == 0) dv[sr.row(t0 + i) * Dv + row] = from_f32<DT>(bb * w);
-                const float bw = bb * w;
+            for (int i = HB - 1; i >= 0; --i) {
+                const int ti = i0 + i;
+                const int par = (i / G) & 1;   // HB is a multiple of 2 G
+                if (ti < nt) {
+                    float kk[8], qq[8], aa[8], vv[RPL], sd[RPL];
+                    kb_lds8(buf + C::OFF_K + (ti * DK + 8 * sub) * 4, kk);
+                    kb_lds8(buf + C::OFF_Q + (ti * DK + 8 * sub) * 4, qq);
+                    kb_lds8(buf + C::OFF_A + (ti * DK + 8 * sub) * 4, aa);
+                    lds_v(buf, C::OFF_V, ti, vv);
+                    lds_v(buf, C::OFF_D, ti, sd);
+                    const float bb = reinterpret_cast<const float *>(buf + C::OFF_B)[ti];
+                    // the lane's rows' terms, added over its rows in the lane
+                    float xq[8], xk[8], xg[8], xb = 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    xk[e] = bb * (D[e] * err - P[e] * w);
-                    D[e] -= bw * kk[e];
-                    xg[e] = D[e] * P[e];
-                    D[e] *= aa[e];
-                }
-                // this wave's rows summed: lane (DPP row r, column group sub)
-                // ends with values 6r .. 6r+5 of (xq, xk, xg) for its columns
-                float x24[24], z[6];
+                    for (int e = 0; e < 8; ++e) xq[e] = xk[e] = xg[e] = 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    x24[e] = kb_dpp_rows_sum<LPR>(xq[e]);
-                    x24[8 + e] = kb_dpp_rows_sum<LPR>(xk[e]);
-                    x24[16 + e] = kb_dpp_rows_sum<LPR>(xg[e]);
-                }
-                kb_scatter24(x24, z);
-                const float xb = xor32_sum(xor16_sum(kb_dpp_rows_sum<LPR>(err * w)));
-                float *rw = red + ((par * G + i % G) * C::NWV + wave) * C::NRED;
-                if ((lane & 15) < LPR) {
-                    const int r4 = lane >> 4;
+                    for (int u = 0; u < RPL; ++u) {
+                        float P[8], pk = 0.f;
+                        const float sdu = scale * sd[u];
 #pragma unroll
-                    for (int e = 0; e < 6; ++e) {
-                        const int x = 6 * r4 + e;   // quantity x / 8, column 8 sub + x % 8
-                        rw[(x >> 3) * DK + 8 * sub + (x & 7)] = z[e];
+                        for (int e = 0; e < 8; ++e) {
+                            P[e] = sp[i][u][e] * aa[e];
+                            pk += P[e] * kk[e];
+                        }
+                        const float err = vv[u] - group_sum<LPR>(pk);   // e_t for this row
+                        const float bu = bb * err;
+                        float wk = 0.f;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            xq[e] += (P[e] + bu * kk[e]) * sdu;       // S_t^T do (this row's term)
+                            D[u][e] += sdu * qq[e];
+                            wk += D[u][e] * kk[e];
+                        }
+                        const float w = group_sum<LPR>(wk);
+                        if (live[u] && sub == 0)
+                            dv[sr.row(t0 + ti) * Dv + row[u]] = from_f32<DT>(bb * w);
+                        const float bw = bb * w;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            xk[e] += bb * (D[u][e] * err - P[e] * w);
+                            D[u][e] -= bw * kk[e];
+                            xg[e] += D[u][e] * P[e];
+                            D[u][e] *= aa[e];
+                        }
+                        xb += err * w;
                     }
-                    if (lane == 0) rw[3 * DK] = xb;
-                }
-            }
-            if (i % G == 0) {
-                // tokens i .. i+G-1 of the block: the waves' sums added up and
-                // written as this row tile's partials
-                lds_barrier();
-                constexpr int NV1 = 3 * DK + 1;
-                for (int u = tid; u < G * NV1; u += C::NTH) {
-                    const int tk = u / NV1, e = u % NV1;
-                    if (i + tk < nt) {
-                        const float *rr = red + (par * G + tk) * C::NWV * C::NRED + e;
-                        float acc = 0.f;
+                    // this wave's rows summed: lane (DPP row r, column group sub)
+                    // ends with values 6r .. 6r+5 of (xq, xk, xg) for its columns
+                    float x24[24], z[6];
 #pragma unroll
-                        for (int wv = 0; wv < C::NWV; ++wv) acc += rr[wv * C::NRED];
-                        const int64_t grow = sr.row(t0 + i + tk);
-                        if (e < 3 * DK)
-                            part[((int64_t)((e / DK) * R + tile) * rows_total + grow) * DK +
-                                 e % DK] = acc;
-                        else
-                            partb[(int64_t)tile * rows_total + grow] = acc;
+                    for (int e = 0; e < 8; ++e) {
+                        x24[e] = kb_dpp_rows_sum<LPR>(xq[e]);
+                        x24[8 + e] = kb_dpp_rows_sum<LPR>(xk[e]);
+                        x24[16 + e] = kb_dpp_rows_sum<LPR>(xg[e]);
+                    }
+                    kb_scatter24(x24, z);
+                    xb = xor32_sum(xor16_sum(kb_dpp_rows_sum<LPR>(xb)));
+                    float *rw = red + ((par * G + i % G) * C::NWV + wave) * C::NRED;
+                    if ((lane & 15) < LPR) {
+                        const int r4 = lane >> 4;
+#pragma unroll
+                        for (int e = 0; e < 6; ++e) {
+                            const int x = 6 * r4 + e;   // quantity x / 8, column 8 sub + x % 8
+                            rw[(x >> 3) * DK + 8 * sub + (x & 7)] = z[e];
+                        }
+                        if (lane == 0) rw[3 * DK] = xb;
                     }
                 }
+                if (i % G == 0) {
+                    // tokens ti .. ti+G-1 of the block: the waves' sums added
+                    // up and written as this row tile's partials
+                    lds_barrier();
+                    constexpr int NV1 = 3 * DK + 1;
+                    for (int u = tid; u < G * NV1; u += C::NTH) {
+                        const int tk = u / NV1, e = u % NV1;
+                        if (ti + tk < nt) {
+                            const float *rr = red + (par * G + tk) * C::NWV * C::NRED + e;
+                            float acc = 0.f;
+#pragma unroll
+                            for (int wv = 0; wv < C::NWV; ++wv) acc += rr[wv * C::NRED];
+                            const int64_t grow = sr.row(t0 + ti + tk);
+                            if (e < 3 * DK)
+                                part[((int64_t)((e / DK) * R + tile) * rows_total + grow) * DK +
+                                     e % DK] = acc;
+                            else
+                                partb[(int64_t)tile * rows_total + grow] = acc;
+                        }
+                    }
+                }
             }
         }
-        if (j > 0) kb_store<DT, DK>(st, smem + ((j - 1) & 1) * C::BUF);
+        if (j > 0) kb_store<DT, DK, RPL>(st, smem + ((j - 1) & 1) * C::BUF);
         lds_barrier();
     }
-    if (dS0 && live) {
-        float4 *dst = reinterpret_cast<float4 *>(dS0 + srow);
-        dst[0] = make_float4(D[0], D[1], D[2], D[3]);
-        dst[1] = make_float4(D[4], D[5], D[6], D[7]);
+#pragma unroll
+    for (int u = 0; u < RPL; ++u) {
+        if (dS0 && live[u]) {
+            float4 *dst = reinterpret_cast<float4 *>(dS0 + srow(u));
+            dst[0] = make_float4(D[u][0], D[u][1], D[u][2], D[u][3]);
+            dst[1] = make_float4(D[u][4], D[u][5], D[u][6], D[u][7]);
+        }
     }
 }
 
@@ -514,51 +570,63 @@ __global__ __launch_bounds__(256) void kda_bwd_reduce_kernel(
     }
 }
 
-template <int DK>
-int kb_rows_per_wg() {
-    return KbCfg<float, DK>::RW;
-}
+// Rows per lane: two from d_k = 64 when one row per lane would need more
+// workgroups than the GPU has CUs (the layer shape: one round instead of
+// two, and half the cross-row sums per row); one otherwise, where more,
+// shorter workgroups finish sooner.
+constexpr int64_t KB_CUS = 256;
 
-int kb_rw(int Dk) {
-    switch (Dk) {
-    case 16: return kb_rows_per_wg<16>();
-    case 32: return kb_rows_per_wg<32>();
-    case 64: return kb_rows_per_wg<64>();
-    case 128: return kb_rows_per_wg<128>();
-    default: return 0;
+template <int DK>
+int kb_rpl(int64_t nseq, int64_t H, int Dv) {
+    if constexpr (DK < 64) {
+        return 1;
+    } else {
+        const int rl = KbCfg<float, DK, 1>::RL;
+        return nseq * H * ((Dv + rl - 1) / rl) > KB_CUS ? 2 : 1;
     }
 }
 
 struct KbLayout {
-    int R;               // row tiles per (sequence, head)
+    int rpl, R;          // rows per lane, row tiles per (sequence, head)
     int64_t ckpt, part, partb, total;  // float offsets: checkpoints, partials; total bytes
 };
 
-KbLayout kb_layout(int64_t ntok, int64_t nseq, int64_t H, int Dk, int Dv) {
-    KbLayout l{0, 0, 0, 0, -1};
-    const int rw = kb_rw(Dk);
-    if (rw == 0 || ntok < 0 || nseq < 0 || H < 0) return l;
+template <int DK>
+KbLayout kb_layout_dk(int64_t ntok, int64_t nseq, int64_t H, int Dv) {
+    KbLayout l{0, 0, 0, 0, 0, -1};
+    if (ntok < 0 || nseq < 0 || H < 0) return l;
+    l.rpl = kb_rpl<DK>(nseq, H, Dv);
+    const int rw = KbCfg<float, DK, 1>::RL * l.rpl;
     l.R = (Dv + rw - 1) / rw;
     const auto al = [](int64_t x) { return (x + 63) / 64 * 64; };  // 256-byte parts
-    const int64_t nck = (ntok / KbCfg<float, 16>::TB + nseq) * H * l.R * rw * Dk;
-    const int64_t npart = 3 * (int64_t)l.R * ntok * H * Dk;
+    const int64_t nck = (ntok / KbCfg<float, DK, 1>::TB + nseq) * H * l.R * rw * DK;
+    const int64_t npart = 3 * (int64_t)l.R * ntok * H * DK;
     const int64_t npb = (int64_t)l.R * ntok * H;
-    l.ckpt = 0;
     l.part = al(nck);
     l.partb = l.part + al(npart);
     l.total = (l.partb + al(npb)) * 4;
     return l;
 }
 
-template <typename DT, int DK>
+KbLayout kb_layout(int64_t ntok, int64_t nseq, int64_t H, int Dk, int Dv) {
+    switch (Dk) {
+    case 16: return kb_layout_dk<16>(ntok, nseq, H, Dv);
+    case 32: return kb_layout_dk<32>(ntok, nseq, H, Dv);
+    case 64: return kb_layout_dk<64>(ntok, nseq, H, Dv);
+    case 128: return kb_layout_dk<128>(ntok, nseq, H, Dv);
+    default: return KbLayout{0, 0, 0, 0, 0, -1};
+    }
+}
+
+template <typename DT, int DK, int RPL>
 hipError_t launch_kb(const KdaBwdArgs &a, const KbLayout &l, hipStream_t stream) {
     float *ws = static_cast<float *>(a.ws);
     const int64_t ntok = a.cu ? a.T : a.nseq * a.T;
     const int64_t rows_total = ntok * a.H;
     const int64_t grid = a.nseq * a.H * l.R;
     if (grid > 0) {
-        hipLaunchKernelGGL((kda_bwd_kernel<DT, DK>), dim3((unsigned)grid),
-                           dim3(KbCfg<DT, DK>::NTH), 0, stream, static_cast<const DT *>(a.q),
+        hipLaunchKernelGGL((kda_bwd_kernel<DT, DK, RPL>), dim3((unsigned)grid),
+                           dim3(KbLanes<DK>::value), 0, stream, static_cast<const DT *>(a.q),
                            static_cast<const DT *>(a.k), static_cast<const DT *>(a.v),
                            static_cast<const DT *>(a.beta), a.gk, a.S0,
                            static_cast<const DT *>(a.dout), a.dS_T, static_cast<DT *>(a.dv),
@@ -581,13 +649,21 @@ hipError_t launch_kb(const KdaBwdArgs &a, const KbLayout &l, hipStream_t stream)
     return hipSuccess;
 }
 
+template <typename DT, int DK>
+hipError_t launch_kb_rpl(const KdaBwdArgs &a, const KbLayout &l, hipStream_t stream) {
+    if constexpr (DK >= 64) {
+        if (l.rpl == 2) return launch_kb<DT, DK, 2>(a, l, stream);
+    }
+    return launch_kb<DT, DK, 1>(a, l, stream);
+}
+
 template <typename DT>
 hipError_t kb_dk(const KdaBwdArgs &a, const KbLayout &l, hipStream_t stream) {
     switch (a.Dk) {
-    case 16: return launch_kb<DT, 16>(a, l, stream);
-    case 32: return launch_kb<DT, 32>(a, l, stream);
-    case 64: return launch_kb<DT, 64>(a, l, stream);
-    case 128: return launch_kb<DT, 128>(a, l, stream);
+    case 16: return launch_kb_rpl<DT, 16>(a, l, stream);
+    case 32: return launch_kb_rpl<DT, 32>(a, l, stream);
+    case 64: return launch_kb_rpl<DT, 64>(a, l, stream);
+    case 128: return launch_kb_rpl<DT, 128>(a, l, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -427,13 +427,15 @@ def test_kda_backward_workspace_size(lib):
     f.argtypes = [ctypes.c_int64] * 6
     # the state of every row tile at every 16-token block start of every
     # sequence (B*T/16 + sequences blocks), then fp32 partials of dq, dk, dgk
-    # ([tiles, B*T*H, Dk] each) and of dbeta; rows per tile = 512 lanes /
-    # (Dk / 8) lanes per row, at most 128 rows (Dk 128: 32, 64: 64, 32 and
-    # 16: 128); each part rounded up to 256 bytes
+    # ([tiles, B*T*H, Dk] each) and of dbeta; rows per tile = lanes (at most
+    # 512, 128 rows' worth) / (Dk / 8) lanes per row (Dk 128: 32, 64: 64, 32
+    # and 16: 128), times two rows per lane from Dk = 64 when one would need
+    # more than 256 workgroups; each part rounded up to 256 bytes
     al = lambda x: (x + 255) // 256 * 256
 
     def want(B, T, H, Dk, Dv, n):
-        rw = {128: 32, 64: 64, 32: 128, 16: 128}[Dk]
+        rl = {128: 32, 64: 64, 32: 128, 16: 128}[Dk]
+        rw = rl * (2 if Dk >= 64 and n * H * -(-Dv // rl) > 256 else 1)
         R = -(-Dv // rw)
         ck = (B * T // 16 + n) * H * R * rw * Dk * 4
         return al(ck) + al(3 * R * B * T * H * Dk * 4) + al(R * B * T * H * 4)
@@ -441,6 +443,9 @@ def test_kda_backward_workspace_size(lib):
     assert f(8, 2048, 16, 128, 128, 8) == want(8, 2048, 16, 128, 128, 8)
     assert f(2, 77, 3, 64, 32, 2) == want(2, 77, 3, 64, 32, 2)
     assert f(1, 300, 2, 16, 64, 5) == want(1, 300, 2, 16, 64, 5)
+    assert f(2, 40, 130, 64, 64, 2) == want(2, 40, 130, 64, 64, 2)    # two rows per lane
+    assert f(1, 40, 70, 128, 128, 1) == want(1, 40, 70, 128, 128, 1)  # two rows per lane
+    assert f(1, 40, 64, 128, 128, 1) == want(1, 40, 64, 128, 128, 1)  # one: 256 workgroups
     assert f(1, 0, 2, 32, 32, 1) == want(1, 0, 2, 32, 32, 1)
     assert f(1, 10, 1, 24, 16, 1) == -1      # unsupported size
     assert f(-1, 10, 1, 16, 16, 1) == -1

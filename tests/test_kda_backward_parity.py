@@ -102,6 +102,15 @@ def test_decay_strengths(amax, dtype):
     _check(_kda(H=3, T=90, gate_amax=amax, dtype=dtype, seed=20200 + int(100 * amax)))
 
 
+@pytest.mark.parametrize("dtype,Dk,Dv,B,H", [("f32", 64, 64, 2, 130), ("bf16", 128, 128, 1, 70),
+                                              ("f32", 128, 64, 1, 130)])
+def test_many_heads(dtype, Dk, Dv, B, H):
+    # more (sequence, head, row tile) than the GPU has CUs at one row per
+    # lane: the kernel with two rows per lane
+    _check(_kda(B=B, H=H, T=40, Dk=Dk, Dv=Dv, dtype=dtype, gate_amax=16.0,
+                seed=21000 + H + Dk), seed=H)
+
+
 def test_erased_channels():
     # a third of the tokens erase every other channel; a quarter of the
     # channels are erased outright at one token (exp(-inf) = 0)
