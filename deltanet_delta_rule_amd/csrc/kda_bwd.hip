@@ -59,11 +59,11 @@ struct KbLanes {
     static constexpr int value = DK / 8 * 128 < 512 ? DK / 8 * 128 : 512;
 };
 
-template <typename DT, int DK, int RPL_ = 1>
+template <typename DT, int DK, int RPL_ = 1, int NTH_ = KbLanes<DK>::value>
 struct KbCfg {
     static constexpr int ESZ = sizeof(DT);
     static constexpr int LPR = DK / 8;                          // lanes per state row
-    static constexpr int NTH = KbLanes<DK>::value;
+    static constexpr int NTH = NTH_;
     static constexpr int RPL = RPL_;                            // state rows per lane
     static constexpr int RL = NTH / LPR;                        // rows of one lane layer
     static constexpr int RW = RPL * RL;                         // state rows per workgroup
@@ -89,9 +89,9 @@ struct KbCfg {
     static constexpr int RED = 2 * G * NWV * NRED;              // floats, two parities
 };
 
-template <typename DT, int DK, int RPL>
+template <typename DT, int DK, int RPL, int NTH>
 struct KbStage {
-    typedef KbCfg<DT, DK, RPL> C;
+    typedef KbCfg<DT, DK, RPL, NTH> C;
     uint4 k[C::NK], q[C::NK];
     float4 g[C::NG];
     DT v[C::NV], d[C::NV];
@@ -105,13 +105,13 @@ struct KbRows {
     __device__ __forceinline__ int64_t row(int t) const { return (base + t) * H + h; }
 };
 
-template <typename DT, int DK, int RPL>
-__device__ __forceinline__ void kb_load(KbStage<DT, DK, RPL> &st, const DT *__restrict__ q,
+template <typename DT, int DK, int RPL, int NTH>
+__device__ __forceinline__ void kb_load(KbStage<DT, DK, RPL, NTH> &st, const DT *__restrict__ q,
                                         const DT *__restrict__ k, const DT *__restrict__ v,
                                         const DT *__restrict__ beta, const float *__restrict__ gk,
                                         const DT *__restrict__ dout, const KbRows &sr, int t0,
                                         int nt, int row0, int Dv, bool want_qd) {
-    typedef KbCfg<DT, DK, RPL> C;
+    typedef KbCfg<DT, DK, RPL, NTH> C;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int n = 0; n < C::NK; ++n) {
@@ -155,9 +155,9 @@ __device__ __forceinline__ void kb_put(float *dst, const uint4 &x, __bf16) {
     reinterpret_cast<float4 *>(dst)[1] = make_float4((float)h[4], (float)h[5], (float)h[6], (float)h[7]);
 }
 
-template <typename DT, int DK, int RPL>
-__device__ __forceinline__ void kb_store(const KbStage<DT, DK, RPL> &st, char *buf) {
-    typedef KbCfg<DT, DK, RPL> C;
+template <typename DT, int DK, int RPL, int NTH>
+__device__ __forceinline__ void kb_store(const KbStage<DT, DK, RPL, NTH> &st, char *buf) {
+    typedef KbCfg<DT, DK, RPL, NTH> C;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int n = 0; n < C::NK; ++n) {
@@ -258,15 +258,15 @@ __device__ __forceinline__ void kb_fwd_token(float (&s)[RPL][8], const float (&k
 // range; offsets are clamped into [0, T].  Checkpoint slots of a sequence
 // start at block base / 16 + n (disjoint between sequences, in bounds for
 // any offsets).  A lane holds RPL rows, RL rows apart, and 8 columns of each.
-template <typename DT, int DK, int RPL_>
-__global__ __launch_bounds__(KbLanes<DK>::value) void kda_bwd_kernel(
+template <typename DT, int DK, int RPL_, int NTH_>
+__global__ __launch_bounds__(NTH_) void kda_bwd_kernel(
     const DT *__restrict__ q, const DT *__restrict__ k, const DT *__restrict__ v,
     const DT *__restrict__ beta, const float *__restrict__ gk, const float *__restrict__ S0,
     const DT *__restrict__ dout, const float *__restrict__ dS_T, DT *__restrict__ dv,
     float *__restrict__ dS0, float *__restrict__ ckpt, float *__restrict__ part,
     float *__restrict__ partb, const int *__restrict__ cu, int T, int H, int Dv, int R,
     int64_t rows_total, float scale) {
-    typedef KbCfg<DT, DK, RPL_> C;
+    typedef KbCfg<DT, DK, RPL_, NTH_> C;
     constexpr int LPR = C::LPR, TB = C::TB, G = C::G, RPL = C::RPL, RL = C::RL, HB = C::HB;
     static_assert(HB % G == 0 && TB == 2 * HB, "flush groups inside half blocks");
     __shared__ __attribute__((aligned(16))) char smem[2 * C::BUF];
@@ -322,17 +322,17 @@ __global__ __launch_bounds__(KbLanes<DK>::value) void kda_bwd_kernel(
         for (int e = 0; e < 8; ++e) s[u][e] = 0.f;
         if (S0 && live[u]) load8(S0 + srow(u), s[u]);
     }
-    KbStage<DT, DK, RPL> st;
+    KbStage<DT, DK, RPL, NTH_> st;
     if (nblk > 0) {
-        kb_load<DT, DK, RPL>(st, q, k, v, beta, gk, dout, sr, 0, min(TB, len), row0, Dv, false);
-        kb_store<DT, DK, RPL>(st, smem);
+        kb_load<DT, DK, RPL, NTH_>(st, q, k, v, beta, gk, dout, sr, 0, min(TB, len), row0, Dv, false);
+        kb_store<DT, DK, RPL, NTH_>(st, smem);
     }
     lds_barrier();
     for (int j = 0; j < nblk; ++j) {
         const int t0 = j * TB, nt = min(TB, len - t0);
         const bool more = j + 1 < nblk;
         if (more)
-            kb_load<DT, DK, RPL>(st, q, k, v, beta, gk, dout, sr, t0 + TB, min(TB, len - t0 - TB),
+            kb_load<DT, DK, RPL, NTH_>(st, q, k, v, beta, gk, dout, sr, t0 + TB, min(TB, len - t0 - TB),
                             row0, Dv, false);
 #pragma unroll
         for (int u = 0; u < RPL; ++u) {
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(KbLanes<DK>::value) void kda_bwd_kernel(
             lds_v(buf, C::OFF_V, i, vv);
             kb_fwd_token<LPR, RPL>(s, kk, aa, vv, reinterpret_cast<const float *>(buf + C::OFF_B)[i]);
         }
-        if (more) kb_store<DT, DK, RPL>(st, smem + ((j + 1) & 1) * C::BUF);
+        if (more) kb_store<DT, DK, RPL, NTH_>(st, smem + ((j + 1) & 1) * C::BUF);
         lds_barrier();
     }
     // the checkpoint stores complete before phase 2 reads them back
@@ -364,8 +364,8 @@ __global__ __launch_bounds__(KbLanes<DK>::value) void kda_bwd_kernel(
     }
     if (nblk > 0) {
         const int t0 = (nblk - 1) * TB;
-        kb_load<DT, DK, RPL>(st, q, k, v, beta, gk, dout, sr, t0, len - t0, row0, Dv, true);
-        kb_store<DT, DK, RPL>(st, smem + ((nblk - 1) & 1) * C::BUF);
+        kb_load<DT, DK, RPL, NTH_>(st, q, k, v, beta, gk, dout, sr, t0, len - t0, row0, Dv, true);
+        kb_store<DT, DK, RPL, NTH_>(st, smem + ((nblk - 1) & 1) * C::BUF);
     }
     lds_barrier();
     for (int j = nblk - 1; j >= 0; --j) {
@@ -376,7 +376,7 @@ __global__ __launch_bounds__(KbLanes<DK>::value) void kda_bwd_kernel(
 #pragma unroll
         for (int u = 0; u < RPL; ++u) load8(ck_at(j, u), c0[u]);
         if (j > 0)
-            kb_load<DT, DK, RPL>(st, q, k, v, beta, gk, dout, sr, t0 - TB, TB, row0, Dv, true);
+            kb_load<DT, DK, RPL, NTH_>(st, q, k, v, beta, gk, dout, sr, t0 - TB, TB, row0, Dv, true);
         const char *buf = smem + (j & 1) * C::BUF;
 #pragma unroll 1
         for (int hb = 1; hb >= 0; --hb) {
@@ -504,7 +504,7 @@ __global__ __launch_bounds__(KbLanes<DK>::value) void kda_bwd_kernel(
                 }
             }
         }
-        if (j > 0) kb_store<DT, DK, RPL>(st, smem + ((j - 1) & 1) * C::BUF);
+        if (j > 0) kb_store<DT, DK, RPL, NTH_>(st, smem + ((j - 1) & 1) * C::BUF);
         lds_barrier();
     }
 #pragma unroll
@@ -570,36 +570,46 @@ __global__ __launch_bounds__(256) void kda_bwd_reduce_kernel(
     }
 }
 
-// Rows per lane: two from d_k = 64 when one row per lane would need more
-// workgroups than the GPU has CUs (the layer shape: one round instead of
-// two, and half the cross-row sums per row); one otherwise, where more,
-// shorter workgroups finish sooner.
+// Workgroup shape from d_k = 64: two state rows per lane when one would need
+// more workgroups than the GPU has CUs (the layer shape: one round instead
+// of two, and half the cross-row sums per row); half the lanes (256) when
+// even that would leave half the CUs idle (few heads: twice the workgroups,
+// half the issue per SIMD); else one row per lane on 512 lanes.
 constexpr int64_t KB_CUS = 256;
 
+struct KbShape {
+    int rpl, nth;
+};
+
 template <int DK>
-int kb_rpl(int64_t nseq, int64_t H, int Dv) {
+KbShape kb_shape(int64_t nseq, int64_t H, int Dv) {
+    constexpr int full = KbLanes<DK>::value;
     if constexpr (DK < 64) {
-        return 1;
+        return {1, full};
     } else {
-        const int rl = KbCfg<float, DK, 1>::RL;
-        return nseq * H * ((Dv + rl - 1) / rl) > KB_CUS ? 2 : 1;
+        const int rl = KbCfg<float, DK, 1, full>::RL;
+        const int64_t wg = nseq * H * ((Dv + rl - 1) / rl);
+        if (wg > KB_CUS) return {2, full};
+        if (2 * wg <= KB_CUS) return {1, full / 2};
+        return {1, full};
     }
 }
 
 struct KbLayout {
-    int rpl, R;          // rows per lane, row tiles per (sequence, head)
+    KbShape shape;
+    int R;               // row tiles per (sequence, head)
     int64_t ckpt, part, partb, total;  // float offsets: checkpoints, partials; total bytes
 };
 
 template <int DK>
 KbLayout kb_layout_dk(int64_t ntok, int64_t nseq, int64_t H, int Dv) {
-    KbLayout l{0, 0, 0, 0, 0, -1};
+    KbLayout l{{0, 0}, 0, 0, 0, 0, -1};
     if (ntok < 0 || nseq < 0 || H < 0) return l;
-    l.rpl = kb_rpl<DK>(nseq, H, Dv);
-    const int rw = KbCfg<float, DK, 1>::RL * l.rpl;
+    l.shape = kb_shape<DK>(nseq, H, Dv);
+    const int rw = l.shape.nth / (DK / 8) * l.shape.rpl;
     l.R = (Dv + rw - 1) / rw;
     const auto al = [](int64_t x) { return (x + 63) / 64 * 64; };  // 256-byte parts
-    const int64_t nck = (ntok / KbCfg<float, DK, 1>::TB + nseq) * H * l.R * rw * DK;
+    const int64_t nck = (ntok / KbCfg<float, DK>::TB + nseq) * H * l.R * rw * DK;
     const int64_t npart = 3 * (int64_t)l.R * ntok * H * DK;
     const int64_t npb = (int64_t)l.R * ntok * H;
     l.part = al(nck);
@@ -614,19 +624,19 @@ KbLayout kb_layout(int64_t ntok, int64_t nseq, int64_t H, int Dk, int Dv) {
     case 32: return kb_layout_dk<32>(ntok, nseq, H, Dv);
     case 64: return kb_layout_dk<64>(ntok, nseq, H, Dv);
     case 128: return kb_layout_dk<128>(ntok, nseq, H, Dv);
-    default: return KbLayout{0, 0, 0, 0, 0, -1};
+    default: return KbLayout{{0, 0}, 0, 0, 0, 0, -1};
     }
 }
 
-template <typename DT, int DK, int RPL>
+template <typename DT, int DK, int RPL, int NTH>
 hipError_t launch_kb(const KdaBwdArgs &a, const KbLayout &l, hipStream_t stream) {
     float *ws = static_cast<float *>(a.ws);
     const int64_t ntok = a.cu ? a.T : a.nseq * a.T;
     const int64_t rows_total = ntok * a.H;
     const int64_t grid = a.nseq * a.H * l.R;
     if (grid > 0) {
-        hipLaunchKernelGGL((kda_bwd_kernel<DT, DK, RPL>), dim3((unsigned)grid),
-                           dim3(KbLanes<DK>::value), 0, stream, static_cast<const DT *>(a.q),
+        hipLaunchKernelGGL((kda_bwd_kernel<DT, DK, RPL, NTH>), dim3((unsigned)grid),
+                           dim3(NTH), 0, stream, static_cast<const DT *>(a.q),
                            static_cast<const DT *>(a.k), static_cast<const DT *>(a.v),
                            static_cast<const DT *>(a.beta), a.gk, a.S0,
                            static_cast<const DT *>(a.dout), a.dS_T, static_cast<DT *>(a.dv),
@@ -650,20 +660,22 @@ hipError_t launch_kb(const KdaBwdArgs &a, const KbLayout &l, hipStream_t stream)
 }
 
 template <typename DT, int DK>
-hipError_t launch_kb_rpl(const KdaBwdArgs &a, const KbLayout &l, hipStream_t stream) {
+hipError_t launch_kb_shape(const KdaBwdArgs &a, const KbLayout &l, hipStream_t stream) {
+    constexpr int full = KbLanes<DK>::value;
     if constexpr (DK >= 64) {
-        if (l.rpl == 2) return launch_kb<DT, DK, 2>(a, l, stream);
+        if (l.shape.rpl == 2) return launch_kb<DT, DK, 2, full>(a, l, stream);
+        if (l.shape.nth == full / 2) return launch_kb<DT, DK, 1, full / 2>(a, l, stream);
     }
-    return launch_kb<DT, DK, 1>(a, l, stream);
+    return launch_kb<DT, DK, 1, full>(a, l, stream);
 }
 
 template <typename DT>
 hipError_t kb_dk(const KdaBwdArgs &a, const KbLayout &l, hipStream_t stream) {
     switch (a.Dk) {
-    case 16: return launch_kb_rpl<DT, 16>(a, l, stream);
-    case 32: return launch_kb_rpl<DT, 32>(a, l, stream);
-    case 64: return launch_kb_rpl<DT, 64>(a, l, stream);
-    case 128: return launch_kb_rpl<DT, 128>(a, l, stream);
+    case 16: return launch_kb_shape<DT, 16>(a, l, stream);
+    case 32: return launch_kb_shape<DT, 32>(a, l, stream);
+    case 64: return launch_kb_shape<DT, 64>(a, l, stream);
+    case 128: return launch_kb_shape<DT, 128>(a, l, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -429,13 +429,15 @@ def test_kda_backward_workspace_size(lib):
     # sequence (B*T/16 + sequences blocks), then fp32 partials of dq, dk, dgk
     # ([tiles, B*T*H, Dk] each) and of dbeta; rows per tile = lanes (at most
     # 512, 128 rows' worth) / (Dk / 8) lanes per row (Dk 128: 32, 64: 64, 32
-    # and 16: 128), times two rows per lane from Dk = 64 when one would need
-    # more than 256 workgroups; each part rounded up to 256 bytes
+    # and 16: 128); from Dk = 64, twice that (two rows per lane) when one
+    # would need more than 256 workgroups, half (half the lanes) when it
+    # would need at most 128; each part rounded up to 256 bytes
     al = lambda x: (x + 255) // 256 * 256
 
     def want(B, T, H, Dk, Dv, n):
         rl = {128: 32, 64: 64, 32: 128, 16: 128}[Dk]
-        rw = rl * (2 if Dk >= 64 and n * H * -(-Dv // rl) > 256 else 1)
+        wg = n * H * -(-Dv // rl)
+        rw = rl if Dk < 64 else 2 * rl if wg > 256 else rl // 2 if 2 * wg <= 256 else rl
         R = -(-Dv // rw)
         ck = (B * T // 16 + n) * H * R * rw * Dk * 4
         return al(ck) + al(3 * R * B * T * H * Dk * 4) + al(R * B * T * H * 4)
@@ -446,6 +448,8 @@ def test_kda_backward_workspace_size(lib):
     assert f(2, 40, 130, 64, 64, 2) == want(2, 40, 130, 64, 64, 2)    # two rows per lane
     assert f(1, 40, 70, 128, 128, 1) == want(1, 40, 70, 128, 128, 1)  # two rows per lane
     assert f(1, 40, 64, 128, 128, 1) == want(1, 40, 64, 128, 128, 1)  # one: 256 workgroups
+    assert f(1, 40, 40, 128, 128, 1) == want(1, 40, 40, 128, 128, 1)  # 160: full width
+    assert f(1, 2048, 16, 128, 128, 1) == want(1, 2048, 16, 128, 128, 1)  # 64: half width
     assert f(1, 0, 2, 32, 32, 1) == want(1, 0, 2, 32, 32, 1)
     assert f(1, 10, 1, 24, 16, 1) == -1      # unsupported size
     assert f(-1, 10, 1, 16, 16, 1) == -1

@@ -103,10 +103,13 @@ def test_decay_strengths(amax, dtype):
 
 
 @pytest.mark.parametrize("dtype,Dk,Dv,B,H", [("f32", 64, 64, 2, 130), ("bf16", 128, 128, 1, 70),
-                                              ("f32", 128, 64, 1, 130)])
+                                              ("f32", 128, 64, 1, 130), ("bf16", 128, 128, 1, 40),
+                                              ("f32", 64, 128, 1, 70)])
 def test_many_heads(dtype, Dk, Dv, B, H):
-    # more (sequence, head, row tile) than the GPU has CUs at one row per
-    # lane: the kernel with two rows per lane
+    # the workgroup shapes by count: more (sequence, head, row tile) than the
+    # GPU has CUs at one row per lane takes two rows per lane (the first
+    # three cases); 129 .. 256 one row on 512 lanes (the last two); fewer,
+    # as in the other tests, one row on 256 lanes
     _check(_kda(B=B, H=H, T=40, Dk=Dk, Dv=Dv, dtype=dtype, gate_amax=16.0,
                 seed=21000 + H + Dk), seed=H)
 
