@@ -37,10 +37,11 @@
 //   1. the forward over the sequence, storing the state at the start of every
 //      16-token block to the workspace (each lane its own values, read back
 //      by the same lane);
-//   2. blocks last to first, each in two halves of 8 tokens (the second half
-//      first): the block's starting state reloaded and advanced to the half,
-//      the half's tokens recomputed with every pre-token state S_{t-1} kept
-//      in registers, then walked in reverse.
+//   2. blocks last to first (with two rows per lane, in two halves of 8
+//      tokens, the second half first): the block's starting state reloaded
+//      and advanced to the sub-block, its tokens recomputed with every
+//      decayed pre-token state P_t kept in registers, then walked in
+//      reverse.
 // The inputs of a block (k, q, exp(gk), the workgroup's rows of v and do,
 // beta) are staged in LDS in fp32 and double-buffered: the next block's
 // global loads are in flight while the current one is processed.
@@ -67,9 +68,9 @@ struct KbCfg {
     static constexpr int RPL = RPL_;                            // state rows per lane
     static constexpr int RL = NTH / LPR;                        // rows of one lane layer
     static constexpr int RW = RPL * RL;                         // state rows per workgroup
-    static constexpr int HB = 8;                                // tokens of a half block
     static constexpr int NWV = NTH / 64;
     static constexpr int TB = 16;                               // tokens per block
+    static constexpr int HB = TB / RPL;                         // tokens of a sub-block
     static constexpr int G = 2;                                 // tokens per cross-wave sum
     static constexpr int NRED = 3 * DK + 4;                     // dq, dk, dgk, dbeta (+ pad)
     static constexpr int VPR = DK * ESZ / 16;                   // 16-byte vectors per k row
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(NTH_) void kda_bwd_kernel(
     int64_t rows_total, float scale) {
     typedef KbCfg<DT, DK, RPL_, NTH_> C;
     constexpr int LPR = C::LPR, TB = C::TB, G = C::G, RPL = C::RPL, RL = C::RL, HB = C::HB;
-    static_assert(HB % G == 0 && TB == 2 * HB, "flush groups inside half blocks");
+    static_assert(HB % (2 * G) == 0 && TB == RPL * HB, "whole flush-group pairs per sub-block");
     __shared__ __attribute__((aligned(16))) char smem[2 * C::BUF];
     __shared__ __attribute__((aligned(16))) float red[C::RED];
 
@@ -354,7 +355,8 @@ __global__ __launch_bounds__(NTH_) void kda_bwd_kernel(
     // the checkpoint stores complete before phase 2 reads them back
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-    // ---- phase 2: blocks last to first, each in two halves of HB tokens
+    // ---- phase 2: blocks last to first, each in RPL sub-blocks of HB tokens
+    // (the registers hold HB x RPL pre-token states)
     float D[RPL][8];
 #pragma unroll
     for (int u = 0; u < RPL; ++u) {
@@ -379,14 +381,14 @@ __global__ __launch_bounds__(NTH_) void kda_bwd_kernel(
             kb_load<DT, DK, RPL, NTH_>(st, q, k, v, beta, gk, dout, sr, t0 - TB, TB, row0, Dv, true);
         const char *buf = smem + (j & 1) * C::BUF;
 #pragma unroll 1
-        for (int hb = 1; hb >= 0; --hb) {
-            const int i0 = hb * HB;   // first token of the half
+        for (int hb = RPL - 1; hb >= 0; --hb) {
+            const int i0 = hb * HB;   // first token of the sub-block
             if (i0 >= nt) continue;   // uniform; an even number of flush groups skipped
 #pragma unroll
             for (int u = 0; u < RPL; ++u)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) s[u][e] = c0[u][e];
-            // the second half starts from the state after the first
+            // a later sub-block starts from the state after the earlier ones
             for (int i = 0; i < i0 && i < nt; ++i) {
                 float kk[8], aa[8], vv[RPL];
                 kb_lds8(buf + C::OFF_K + (i * DK + 8 * sub) * 4, kk);
@@ -394,21 +396,38 @@ __global__ __launch_bounds__(NTH_) void kda_bwd_kernel(
                 lds_v(buf, C::OFF_V, i, vv);
                 kb_fwd_token<LPR, RPL>(s, kk, aa, vv, reinterpret_cast<const float *>(buf + C::OFF_B)[i]);
             }
-            // recompute: sp[i] = the state before token i0 + i
+            // recompute: sp[i] = P of token i0 + i, the decayed state before
+            // its write (read below only for tokens of the sequence)
             float sp[HB][RPL][8];
 #pragma unroll
             for (int i = 0; i < HB; ++i) {
+                if constexpr (RPL > 1) {
+                    // defined on every path: with two rows per lane the
+                    // partly defined states cost the allocator spills
 #pragma unroll
-                for (int u = 0; u < RPL; ++u)
+                    for (int u = 0; u < RPL; ++u)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) sp[i][u][e] = s[u][e];
+                        for (int e = 0; e < 8; ++e) sp[i][u][e] = 0.f;
+                }
                 if (i0 + i < nt) {
                     float kk[8], aa[8], vv[RPL];
                     kb_lds8(buf + C::OFF_K + ((i0 + i) * DK + 8 * sub) * 4, kk);
                     kb_lds8(buf + C::OFF_A + ((i0 + i) * DK + 8 * sub) * 4, aa);
                     lds_v(buf, C::OFF_V, i0 + i, vv);
-                    kb_fwd_token<LPR, RPL>(s, kk, aa, vv,
-                                           reinterpret_cast<const float *>(buf + C::OFF_B)[i0 + i]);
+                    const float bb = reinterpret_cast<const float *>(buf + C::OFF_B)[i0 + i];
+#pragma unroll
+                    for (int u = 0; u < RPL; ++u) {
+                        float pk = 0.f;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            s[u][e] *= aa[e];
+                            sp[i][u][e] = s[u][e];
+                            pk += s[u][e] * kk[e];
+                        }
+                        const float bu = bb * (vv[u] - group_sum<LPR>(pk));
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) s[u][e] += bu * kk[e];
+                    }
                 }
             }
             // reverse
@@ -430,13 +449,11 @@ __global__ __launch_bounds__(NTH_) void kda_bwd_kernel(
                     for (int e = 0; e < 8; ++e) xq[e] = xk[e] = xg[e] = 0.f;
 #pragma unroll
                     for (int u = 0; u < RPL; ++u) {
-                        float P[8], pk = 0.f;
+                        const float(&P)[8] = sp[i][u];
+                        float pk = 0.f;
                         const float sdu = scale * sd[u];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            P[e] = sp[i][u][e] * aa[e];
-                            pk += P[e] * kk[e];
-                        }
+                        for (int e = 0; e < 8; ++e) pk += P[e] * kk[e];
                         const float err = vv[u] - group_sum<LPR>(pk);   // e_t for this row
                         const float bu = bb * err;
                         float wk = 0.f;
@@ -452,7 +469,12 @@ __global__ __launch_bounds__(NTH_) void kda_bwd_kernel(
                         const float bw = bb * w;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            xk[e] += bb * (D[u][e] * err - P[e] * w);
+                            // (the two forms round alike; the second
+                            // keeps fewer values live with two rows a lane)
+                            if constexpr (RPL == 1)
+                                xk[e] += D[u][e] * bu - P[e] * bw;
+                            else
+                                xk[e] += bb * (D[u][e] * err - P[e] * w);
                             D[u][e] -= bw * kk[e];
                             xg[e] += D[u][e] * P[e];
                             D[u][e] *= aa[e];
