@@ -66,6 +66,7 @@ BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published (256 CU x 2.4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_layer_1p3b_traffic.txt")
 KERNEL_SOURCES = ["deltanet_delta_rule_amd/csrc/chunk_fwd.hpp",
                   "deltanet_delta_rule_amd/csrc/chunk_fwd.hip",
+                  "deltanet_delta_rule_amd/csrc/chunk_fwd_d128_c64.hip",
                   "deltanet_delta_rule_amd/csrc/dr_common.hpp",
                   "deltanet_delta_rule_amd/build.py"]  # compile flags
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "recurrent_step_decode_traffic.txt")

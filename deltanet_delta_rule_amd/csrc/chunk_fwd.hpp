@@ -1496,12 +1496,25 @@ hipError_t dispatch_nw(const ChunkFwdArgs &a, hipStream_t stream) {
     }
 }
 
+}  // namespace
+
+// The plain rule's bf16 kernels at d_k = 128 and 64-token chunks (the layer
+// shape's launch) live in a translation unit of their own, built with another
+// instruction-scheduling strategy.
+hipError_t launch_chunk_fwd_plain_d128_c64(const ChunkFwdArgs &a, hipStream_t stream);
+
+namespace {
+
 template <typename DT, int DK, bool GATED, bool L2>
 hipError_t dispatch_c(const ChunkFwdArgs &a, hipStream_t stream) {
     switch (a.chunk) {
     case 16: return dispatch_nw<DT, DK, 16, GATED, L2>(a, stream);
     case 32: return dispatch_nw<DT, DK, 32, GATED, L2>(a, stream);
-    case 64: return dispatch_nw<DT, DK, 64, GATED, L2>(a, stream);
+    case 64:
+        if constexpr (sizeof(DT) == 2 && DK == 128 && !GATED && !L2)
+            return launch_chunk_fwd_plain_d128_c64(a, stream);
+        else
+            return dispatch_nw<DT, DK, 64, GATED, L2>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
