@@ -199,6 +199,21 @@ def test_empty_sequence():
     assert torch.equal(g["dS0"].cpu(), dst)
 
 
+def test_without_the_state_gradient_output():
+    # dS0 not requested: nothing written for it, the other gradients the same
+    w = _kda(B=1, H=2, T=40, Dk=128, Dv=128, dtype="bf16", seed=20950)
+    x = W.generate(w)
+    d = to_dev(x)
+    do, dst = _upstream(w.B, w.T, w.H, w.Dk, w.Dv, w.torch_dtype, 9)
+    a = dr.kda_bwd(d["q"], d["k"], d["v"], d["beta"], d["gk"], do.cuda(), d["S0"], dst.cuda())
+    b = dr.kda_bwd(d["q"], d["k"], d["v"], d["beta"], d["gk"], do.cuda(), d["S0"], dst.cuda(),
+                   need_dS0=False)
+    torch.cuda.synchronize()
+    assert b["dS0"] is None
+    for n in ("dq", "dk", "dv", "dbeta", "dgk"):
+        assert torch.equal(a[n], b[n]), n
+
+
 def test_repeated_calls_are_bit_identical():
     w = _kda(B=2, H=3, T=45, Dk=128, Dv=128, dtype="bf16", seed=20900)
     x = W.generate(w)
